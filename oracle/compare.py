@@ -1,0 +1,46 @@
+"""Error measures for parity checks.  Test infrastructure only.
+
+The rel-L2 measure and the first-mismatch report follow the verification
+discipline of "Day 79: Tile programming with cuTile" (compare against a
+float64 reference over the identical rounded inputs; report the first failing
+index with both values; look at whether errors come in tile-sized bands).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def rel_l2(out, ref):
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.linalg.norm(ref.ravel())
+    num = np.linalg.norm((out - ref).ravel())
+    if den == 0.0:
+        return float(num)
+    return float(num / den)
+
+
+def first_mismatch(out, ref, rtol, atol):
+    """Index, got, expected of the first element with |d| > atol + rtol |ref|,
+    or None.  NaN anywhere in ``out`` where ``ref`` is finite counts."""
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    bad = ~(np.abs(out - ref) <= atol + rtol * np.abs(ref))
+    if not bad.any():
+        return None
+    idx = np.unravel_index(int(np.argmax(bad)), bad.shape)
+    return tuple(int(i) for i in idx), float(out[idx]), float(ref[idx])
+
+
+def band_report(out, ref, tile, axis=1):
+    """rel-L2 over the first and the last ``tile`` positions along ``axis``, so
+    a tail or tile-band error cannot hide inside a global norm."""
+    out = np.asarray(out, np.float64)
+    ref = np.asarray(ref, np.float64)
+    n = out.shape[axis]
+    head = [slice(None)] * out.ndim
+    tail = [slice(None)] * out.ndim
+    head[axis] = slice(0, min(tile, n))
+    tail[axis] = slice(max(n - tile, 0), n)
+    return (rel_l2(out[tuple(head)], ref[tuple(head)]),
+            rel_l2(out[tuple(tail)], ref[tuple(tail)]))

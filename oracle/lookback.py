@@ -1,0 +1,121 @@
+"""Float64 simulator of the single-pass decoupled look-back scan protocol.
+Test infrastructure only.
+
+Follows "Selective-scan CUDA kernels", sections "The problem" (the affine
+combine is associative but not commutative) and "The five kernels" (each tile
+publishes its local aggregate under flag A, walks back until it meets a
+predecessor's inclusive prefix under flag P, then publishes its own P; tiles
+are claimed in order from a counter so a waiting tile's predecessors are
+always already claimed; the warp variant inspects a window of predecessors at
+once).
+
+The simulator runs the protocol with any element type and combine, under a
+seeded random interleaving of the tiles' steps, so a reordered or swapped
+combine shows up as a wrong answer.  A tile whose predecessors never publish
+is reported as a deadlock after a step bound instead of spinning forever.
+"""
+from __future__ import annotations
+
+import random
+
+EMPTY, AGG, INC = 0, 1, 2
+
+
+class Deadlock(RuntimeError):
+    pass
+
+
+def lookback_scan(elements, combine, identity, tile, window=64, seed=0,
+                  resident=8, max_steps=10_000_000, swap_combine=False,
+                  never_publish=None):
+    """Inclusive scan of ``elements`` (one chain) through simulated tiles.
+
+    ``combine(first, second)`` composes two elements, ``first`` earlier in the
+    sequence.  Returns the list of inclusive prefixes.  ``swap_combine`` runs
+    the deliberately broken variant that calls combine(later, earlier) in the
+    look-back and in the final apply; ``never_publish`` names a tile that
+    stalls, to exercise the deadlock bound.
+    """
+    def comb(first, second):
+        return combine(second, first) if swap_combine else combine(first, second)
+
+    rng = random.Random(seed)
+    n = len(elements)
+    ntiles = -(-n // tile)
+    status = [EMPTY] * ntiles
+    agg = [None] * ntiles
+    inc = [None] * ntiles
+    out = [None] * n
+    next_claim = 0
+    active = {}  # tile -> state dict
+    steps = 0
+    done = 0
+
+    def local_scan(t):
+        lo, hi = t * tile, min((t + 1) * tile, n)
+        acc = None
+        pref = []
+        for i in range(lo, hi):
+            acc = elements[i] if acc is None else combine(acc, elements[i])
+            pref.append(acc)
+        return pref
+
+    while done < ntiles:
+        steps += 1
+        if steps > max_steps:
+            raise Deadlock(f"no progress after {max_steps} steps; waiting tiles {sorted(active)}")
+        while len(active) < resident and next_claim < ntiles:
+            active[next_claim] = {"phase": 0}
+            next_claim += 1
+        t = rng.choice(sorted(active))
+        st = active[t]
+        if st["phase"] == 0:
+            st["local"] = local_scan(t)
+            if t == never_publish:
+                st["phase"] = 9
+                continue
+            if t == 0:
+                inc[0] = st["local"][-1]
+                status[0] = INC
+                st["prefix"] = None
+                st["phase"] = 2
+            else:
+                agg[t] = st["local"][-1]
+                status[t] = AGG
+                st["phase"] = 1
+                st["look"] = t - 1
+                st["acc"] = None  # combination of AGGs already walked, earliest first
+        elif st["phase"] == 1:
+            # inspect up to `window` predecessors at once, nearest first
+            lo = max(st["look"] - window + 1, 0)
+            view = list(range(st["look"], lo - 1, -1))
+            flags = [status[p] for p in view]
+            resolved = False
+            acc = st["acc"]
+            for p, f in zip(view, flags):
+                if f == EMPTY:
+                    break  # a predecessor has not published yet: retry later
+                if f == INC:
+                    prefix = inc[p] if acc is None else comb(inc[p], acc)
+                    resolved = True
+                    break
+                acc = agg[p] if acc is None else comb(agg[p], acc)
+            else:
+                # the whole window held aggregates: keep them and walk further back
+                st["acc"] = acc
+                st["look"] = lo - 1
+                continue
+            if resolved:
+                st["prefix"] = prefix
+                inc[t] = comb(prefix, st["local"][-1])
+                status[t] = INC
+                st["phase"] = 2
+        elif st["phase"] == 2:
+            lo = t * tile
+            for k, v in enumerate(st["local"]):
+                out[lo + k] = v if st["prefix"] is None else comb(st["prefix"], v)
+            del active[t]
+            done += 1
+        else:  # stalled tile
+            continue
+    return out

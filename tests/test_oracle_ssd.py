@@ -1,0 +1,155 @@
+"""Pins for the float64 SSD oracle (CPU only).
+
+Each test ties ``oracle.ssd.ssd_loop`` to something other than itself: a
+hand-worked fixture, the brute-force unrolled sum, the decay-free
+linear-attention closed form, the dt = 0 identity, chunk-size invariance of the
+independent chunked formulation, state carry across calls, the scalar-scan
+special case, and mutants (h_{t-1} output, strict mask, swapped groups) that
+must be caught.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import chunked, scan, ssd
+
+
+def rand_case(seed, Bt=2, L=23, H=4, P=3, S=5, G=2, h0=True, D=True, dt_shift=-2.0):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((Bt, L, H, P))
+    B = rng.standard_normal((Bt, L, G, S))
+    C = rng.standard_normal((Bt, L, G, S))
+    dt = np.log1p(np.exp(rng.standard_normal((Bt, L, H)) + dt_shift))
+    A = -np.exp(rng.uniform(0.0, math.log(16.0), H))
+    Dv = rng.standard_normal(H) if D else None
+    hv = 0.3 * rng.standard_normal((Bt, H, P, S)) if h0 else None
+    return x, dt, A, B, C, Dv, hv
+
+
+def load_hand(golden_dir):
+    with open(os.path.join(golden_dir, "ssd_hand_L2.json")) as f:
+        g = json.load(f)
+    A = np.array([-math.log(2.0)])
+    arr = {k: np.array(g[k], dtype=np.float64) for k in ("dt", "x", "B", "C", "D", "h0_PxS")}
+    return g, arr["x"], arr["dt"], A, arr["B"], arr["C"], arr["D"], arr["h0_PxS"]
+
+
+def test_hand_worked_fixture(golden_dir):
+    g, x, dt, A, B, C, D, h0 = load_hand(golden_dir)
+    y, hf = ssd.ssd_loop(x, dt, A, B, C, D, h0)
+    np.testing.assert_allclose(y, np.array(g["y"]), rtol=0, atol=1e-12)
+    np.testing.assert_allclose(hf, np.array(g["h_final_PxS"]), rtol=0, atol=1e-12)
+
+
+def test_previous_state_output_mutant_is_caught(golden_dir):
+    g, x, dt, A, B, C, D, h0 = load_hand(golden_dir)
+    y_prev, _ = ssd.ssd_loop(x, dt, A, B, C, D, h0, y_uses_previous_state=True)
+    np.testing.assert_allclose(y_prev, np.array(g["y_if_output_used_previous_state"]), atol=1e-12)
+    assert np.abs(y_prev - np.array(g["y"])).max() > 0.5
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_bruteforce_unrolled_sum(seed):
+    case = rand_case(seed, Bt=1, L=17, H=2, P=3, S=4, G=1 + seed % 2)
+    y, hf = ssd.ssd_loop(*case)
+    yb, hb = ssd.ssd_bruteforce(*case)
+    assert np.abs(y - yb).max() < 1e-12 * max(1.0, np.abs(yb).max())
+    assert np.abs(hf - hb).max() < 1e-12 * max(1.0, np.abs(hb).max())
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_decay_free_is_linear_attention(seed):
+    x, dt, A, B, C, D, h0 = rand_case(seed, L=19)
+    y, _ = ssd.ssd_loop(x, dt, np.zeros_like(A), B, C, D, h0)
+    yl = ssd.ssd_linear_attention(x, dt, B, C, D, h0)
+    assert np.abs(y - yl).max() < 1e-11
+
+
+def test_zero_timestep_keeps_state():
+    x, dt, A, B, C, D, h0 = rand_case(5)
+    dt0 = np.zeros_like(dt)
+    y, hf = ssd.ssd_loop(x, dt0, A, B, C, D, h0)
+    np.testing.assert_allclose(hf, h0, rtol=0, atol=0)
+    H = x.shape[2]
+    grp = np.arange(H) // (H // B.shape[2])
+    expect = np.einsum("blhs,bhps->blhp", C[:, :, grp, :], h0) + D[None, None, :, None] * x
+    assert np.abs(y - expect).max() < 1e-12
+
+
+def test_single_token_by_hand_formula():
+    x, dt, A, B, C, D, h0 = rand_case(6, Bt=1, L=1, H=1, G=1)
+    y, hf = ssd.ssd_loop(x, dt, A, B, C, D, h0)
+    a0 = A[0] * dt[0, 0, 0]
+    h_S_by_P = math.exp(a0) * h0[0, 0].T + dt[0, 0, 0] * np.outer(B[0, 0, 0], x[0, 0, 0])
+    expect = C[0, 0, 0] @ h_S_by_P + D[0] * x[0, 0, 0]
+    assert np.abs(y[0, 0, 0] - expect).max() < 1e-13
+    assert np.abs(hf[0, 0] - h_S_by_P.T).max() < 1e-13
+
+
+@pytest.mark.parametrize("chunk", [1, 2, 4, 7, 8, 16, 23, 64])
+def test_chunked_formulation_matches_loop(chunk):
+    case = rand_case(7, L=23)
+    y, hf = ssd.ssd_loop(*case)
+    yc, hc = chunked.ssd_chunked(*case, chunk=chunk)
+    assert np.abs(y - yc).max() < 1e-11
+    assert np.abs(hf - hc).max() < 1e-11
+
+
+def test_strict_mask_mutant_is_caught():
+    case = rand_case(8, L=16)
+    y, _ = ssd.ssd_loop(*case)
+    ym, _ = chunked.ssd_chunked(*case, chunk=8, keep_diagonal=False)
+    assert np.abs(y - ym).max() > 1e-2
+
+
+def test_chained_calls_carry_state():
+    x, dt, A, B, C, D, h0 = rand_case(9, L=30)
+    y, hf = ssd.ssd_loop(x, dt, A, B, C, D, h0)
+    L1 = 11
+    y1, h1 = ssd.ssd_loop(x[:, :L1], dt[:, :L1], A, B[:, :L1], C[:, :L1], D, h0)
+    y2, h2 = ssd.ssd_loop(x[:, L1:], dt[:, L1:], A, B[:, L1:], C[:, L1:], D, h1)
+    assert np.abs(np.concatenate([y1, y2], axis=1) - y).max() < 1e-12
+    assert np.abs(h2 - hf).max() < 1e-12
+
+
+def test_one_state_one_channel_is_the_scalar_scan():
+    rng = np.random.default_rng(10)
+    Bt, L, H = 2, 40, 3
+    x = rng.standard_normal((Bt, L, H, 1))
+    B = rng.standard_normal((Bt, L, 1, 1))
+    C = np.ones((Bt, L, 1, 1))
+    dt = np.log1p(np.exp(rng.standard_normal((Bt, L, H)) - 2))
+    A = -np.exp(rng.uniform(0, math.log(16), H))
+    y, _ = ssd.ssd_loop(x, dt, A, B, C, None, None)
+    for b in range(Bt):
+        a_rows = np.exp(A[None, :] * dt[b]).T                     # [H, L]
+        b_rows = (dt[b] * B[b, :, 0, 0][:, None] * x[b, :, :, 0]).T
+        h = scan.scan_loop(a_rows, b_rows)
+        assert np.abs(y[b, :, :, 0].T - h).max() < 1e-12
+
+
+def test_group_mapping_is_contiguous_head_blocks():
+    x, dt, A, B, C, D, h0 = rand_case(11, H=4, G=2)
+    y, _ = ssd.ssd_loop(x, dt, A, B, C, D, h0)
+    B2, C2 = B.copy(), C.copy()
+    B2[:, :, 1] += 1.0
+    C2[:, :, 1] -= 0.5
+    y2, _ = ssd.ssd_loop(x, dt, A, B2, C2, D, h0)
+    # heads 0,1 read group 0 and are unchanged; heads 2,3 read group 1
+    assert np.abs(y2[:, :, :2] - y[:, :, :2]).max() == 0.0
+    assert np.abs(y2[:, :, 2:] - y[:, :, 2:]).max() > 1e-3
+
+
+def test_identical_heads_in_a_group_agree():
+    x, dt, A, B, C, D, h0 = rand_case(12, H=4, G=1, h0=False)
+    for h in range(1, 4):
+        x[:, :, h] = x[:, :, 0]
+        dt[:, :, h] = dt[:, :, 0]
+    A[:] = A[0]
+    D[:] = D[0]
+    y, _ = ssd.ssd_loop(x, dt, A, B, C, D, None)
+    for h in range(1, 4):
+        assert np.array_equal(y[:, :, h], y[:, :, 0])
