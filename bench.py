@@ -1,0 +1,289 @@
+"""Throughput benchmark of the SSD forward pass and the linear scan on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ssd_large]
+
+One step is one ``ssd_fwd`` call (segment sums, CB, intra-chunk products,
+chunk states, inter-chunk recurrence and outputs) over one batch of the named
+workload, with inputs already resident in HBM.  K steps are timed with HIP
+events on the launch stream, bracketed by device synchronisation.  Input and
+output buffers rotate over enough copies that the footprint exceeds 1 GiB, so
+the 256 MB Infinity Cache cannot serve repeated steps.  The linear scan is
+timed the same way in its own loop and reported in the ``linear_scan`` object
+of the same JSON line.
+
+The CPU baseline is the float64 oracle, unmodified, run on a bounded sample
+of the same workload (a few whole (batch, head) sequences, one per worker
+process) and scaled to the metric's unit.
+
+Prints exactly one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+FP32_PEAK_TFLOPS = 157.3
+METRIC = "SSD fwd tokens/sec (B·L) + % of HBM/MFMA roofline; linear-scan GB/s"
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
+def ssd_alg_bytes(inp, shape):
+    """Compulsory HBM bytes of one forward pass: every input read once and
+    every output written once (x, dt, A, B, C, D, optional h0, y, h_final)."""
+    b = sum(_nbytes(inp[k]) for k in ("x", "dt", "A", "B", "C", "D", "h0"))
+    b += _nbytes(inp["x"])                                            # y
+    b += shape.batch * shape.nheads * shape.headdim * shape.dstate * 4  # h_final
+    return b
+
+
+def ssd_alg_flops(shape):
+    """Causal-triangle MFMA flops: C B^T once per (batch, chunk, group) plus,
+    per (batch, chunk, head), the masked product, the chunk state and C h^T."""
+    T = shape.chunk
+    nc = shape.nchunks
+    cb = shape.batch * nc * shape.ngroups * T * (T + 1) * shape.dstate
+    per_head = T * (T + 1) * shape.headdim + 4 * T * shape.dstate * shape.headdim
+    return cb + shape.batch * nc * shape.nheads * per_head
+
+
+def source_digest(names):
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "chunked_linear_scan_amd", "csrc")
+    for n in sorted(names):
+        with open(os.path.join(csrc, n), "rb") as f:
+            h.update(n.encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_key, sources, launches_per_step=1):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, only if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            db = json.load(f)
+    except (OSError, ValueError):
+        return None
+    rec = db.get(kernel_key)
+    if not rec or rec.get("source_digest") != source_digest(sources):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def time_loop(fn, nsets, steps, warmup, stream):
+    import torch
+    for i in range(warmup):
+        fn(i % nsets)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        fn(i % nsets)
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / 1e3 / steps  # seconds per step
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle on a bounded sample, one (batch, head) per process
+# ---------------------------------------------------------------------------
+def _oracle_ssd_job(args):
+    import numpy as np
+    from oracle import ssd as ossd
+    x, dt, A, B, C, D, h0 = args
+    t0 = time.perf_counter()
+    ossd.ssd_loop(x, dt, A, B, C, D, h0)
+    return time.perf_counter() - t0
+
+
+def cpu_baseline_ssd(inp, shape, budget_s=20.0):
+    import multiprocessing as mp
+    import numpy as np
+    cores = len(os.sched_getaffinity(0))
+    H, G = shape.nheads, shape.ngroups
+    np64 = lambda t: None if t is None else t.to(dtype=__import__("torch").float64).numpy()
+    # one whole sequence per worker: (batch 0, head k) for k spread over groups
+    heads = [int(round(k * (H - 1) / max(cores - 1, 1))) for k in range(cores)]
+    jobs = []
+    for h in heads:
+        g = h // (H // G)
+        jobs.append((np64(inp["x"][:1, :, h:h + 1]), np64(inp["dt"][:1, :, h:h + 1]),
+                     np64(inp["A"][h:h + 1]), np64(inp["B"][:1, :, g:g + 1]),
+                     np64(inp["C"][:1, :, g:g + 1]), np64(inp["D"][h:h + 1]),
+                     None if inp["h0"] is None else np64(inp["h0"][:1, h:h + 1])))
+    # bound the sample: shorten the sequences if one would take too long
+    L = shape.seqlen
+    probe = min(L, 512)
+    t_probe = _oracle_ssd_job(tuple(v if v is None or v.ndim < 2 else v[:, :probe] for v in jobs[0]))
+    est = t_probe * L / probe
+    Ls = L if est <= budget_s else max(probe, int(L * budget_s / est))
+    jobs = [tuple(v if v is None or v.ndim < 2 else v[:, :Ls] for v in j) for j in jobs]
+    env_threads = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
+    for k in env_threads:
+        os.environ[k] = "1"
+    t0 = time.perf_counter()
+    with mp.get_context("spawn").Pool(cores) as pool:
+        pool.map(_oracle_ssd_job, jobs)
+    wall = time.perf_counter() - t0
+    for k, v in env_threads.items():
+        if v is None:
+            os.environ.pop(k, None)
+        else:
+            os.environ[k] = v
+    # tokens/s counts a token once all H heads of its batch row are done
+    tok_equiv = Ls * len(jobs) / H
+    return {"value": tok_equiv / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{len(jobs)} whole (batch 0, head) sequences of {Ls} tokens, one per "
+                      f"process ({len(jobs)}/{H} of one batch row), wall {wall:.1f}s"}
+
+
+def cpu_baseline_scan(inp):
+    from oracle import scan as oscan
+    t0 = time.perf_counter()
+    oscan.scan_loop(inp["a"].numpy(), inp["b"].numpy())
+    wall = time.perf_counter() - t0
+    nbytes = 12 * inp["a"].numel()
+    return {"value": nbytes / wall / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole workload ({tuple(inp['a'].shape)}), wall {wall:.2f}s"}
+
+
+# ---------------------------------------------------------------------------
+def bench_ssd(name, steps, warmup, want_cpu):
+    import torch
+    import chunked_linear_scan_amd as cls
+    from chunked_linear_scan_amd import workloads
+    shape, seed = workloads.SSD_WORKLOADS[name]
+    inp = workloads.make_ssd_inputs(shape, seed)
+    alg_bytes = ssd_alg_bytes(inp, shape)
+    nsets = max(1, math.ceil((1 << 30) / alg_bytes))
+    dev = torch.device("cuda:0")
+    sets = []
+    for _ in range(nsets):
+        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+        d["y"] = torch.empty_like(d["x"])
+        d["hf"] = torch.empty(shape.batch, shape.nheads, shape.headdim, shape.dstate,
+                              dtype=torch.float32, device=dev)
+        sets.append(d)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        d = sets[i]
+        cls.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=shape.chunk,
+                    out=d["y"])
+
+    t = time_loop(step, nsets, steps, warmup, stream)
+    tokens = shape.batch * shape.seqlen
+    flops = ssd_alg_flops(shape)
+    gbs = alg_bytes / t / 1e9
+    tflops = flops / t / 1e12
+    srcs = ["ssd_bf16.hpp", "common.hpp", "ssd_kernels.hpp"]
+    res = {
+        "t": t, "tokens_per_s": tokens / t, "alg_bytes": alg_bytes, "alg_flops": flops,
+        "gbs": gbs, "tflops": tflops, "nsets": nsets,
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("ssd_fwd:" + name, srcs),
+                     "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                     "kernels": "ssd_cb_kernel + ssd_chunk_kernel, timed together per call"},
+        "shape": shape,
+    }
+    if want_cpu:
+        res["cpu_baseline"] = cpu_baseline_ssd(inp, shape)
+    return res
+
+
+def bench_scan(name, steps, warmup, want_cpu):
+    import torch
+    import chunked_linear_scan_amd as cls
+    from chunked_linear_scan_amd import workloads
+    inp = workloads.scan_workload(name)
+    rows, L = inp["a"].shape
+    nbytes = 12 * rows * L
+    nsets = max(1, math.ceil((1 << 30) / nbytes))
+    dev = torch.device("cuda:0")
+    sets = [(inp["a"].to(dev), inp["b"].to(dev), torch.empty(rows, L, device=dev)) for _ in range(nsets)]
+    stream = torch.cuda.current_stream(dev)
+    ws = torch.zeros(cls.load_library().linear_scan_workspace_size(rows, L), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        a, b, h = sets[i]
+        cls.linear_scan(a, b, out=h, workspace=ws)
+
+    t = time_loop(step, nsets, steps, warmup, stream)
+    gbs = nbytes / t / 1e9
+    res = {"workload": f"{name}: {rows} rows x {L} fp32", "value": round(gbs, 1), "unit": "GB/s",
+           "us_per_call": round(t * 1e6, 2), "nsets": nsets,
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "traffic": measured_traffic("linear_scan:" + name, ["linear_scan.hip", "common.hpp"])}}
+    if want_cpu:
+        res["cpu_baseline"] = cpu_baseline_scan(inp)
+    return res
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=30)
+    ap.add_argument("--workload", default="ssd_large",
+                    choices=["ssd_small", "ssd_large", "ssd_long", "ssd_tiny"])
+    ap.add_argument("--scan-workload", default="scan", choices=["scan", "scan_ragged"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-scan", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); run it with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    want_cpu = not args.no_cpu_baseline
+    ssd = bench_ssd(args.workload, args.steps, args.warmup, want_cpu)
+    shape = ssd["shape"]
+    line = {
+        "metric": METRIC,
+        "value": round(ssd["tokens_per_s"], 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ssd["t"] * 1e3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if shape.dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; shapes and distributions of the named workload)",
+        "config": {"workload": f"{args.workload}: batch {shape.batch}, L={shape.seqlen}, "
+                               f"{shape.nheads} heads, P={shape.headdim}, S={shape.dstate}, "
+                               f"{shape.ngroups} group(s), chunk {shape.chunk}, {shape.dtype}",
+                   "global_batch": shape.batch, "seq_len": shape.seqlen, "parallelism": "single GPU",
+                   "buffer_sets": ssd["nsets"]},
+        "roofline": ssd["roofline"],
+    }
+    if "cpu_baseline" in ssd:
+        line["cpu_baseline"] = ssd["cpu_baseline"]
+    if not args.no_scan:
+        line["linear_scan"] = bench_scan(args.scan_workload, args.steps, args.warmup, want_cpu)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

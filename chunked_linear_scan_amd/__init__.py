@@ -1,0 +1,179 @@
+"""Python binding of the gfx950 ``libchunked_linear_scan.so`` C ABI.
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, outputs and the workspace are allocated with torch on the device,
+and the C entry points of ``include/chunked_linear_scan.h`` are called with
+raw pointers on torch's current stream.  Every step of the computation runs in
+the library's HIP kernels; there is no fallback path.  If the shared library
+has not been built, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libchunked_linear_scan.so")
+
+SSD_OK = 0
+SSD_F32 = 0
+SSD_BF16 = 1
+_DTYPE_CODE = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+class SSDError(RuntimeError):
+    """A negative status returned by the library."""
+
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({strerror(status)})")
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) and return the shared library; raise if it is missing."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`"
+                " (there is no non-HIP fallback)")
+        lib = ctypes.CDLL(path)
+        i64, sz, vp, fp = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_void_p
+        lib.ssd_strerror.argtypes = [ctypes.c_int]
+        lib.ssd_strerror.restype = ctypes.c_char_p
+        lib.linear_scan_workspace_size.argtypes = [i64, i64]
+        lib.linear_scan_workspace_size.restype = sz
+        lib.linear_scan.argtypes = [fp, fp, fp, i64, i64, vp, sz, vp]
+        lib.linear_scan.restype = ctypes.c_int
+        lib.ssd_fwd_workspace_size.argtypes = [i64] * 7 + [ctypes.c_int]
+        lib.ssd_fwd_workspace_size.restype = sz
+        lib.ssd_fwd.argtypes = [vp, fp, fp, vp, vp, fp, fp] + [i64] * 7 + [ctypes.c_int, vp, fp, vp, sz, vp]
+        lib.ssd_fwd.restype = ctypes.c_int
+        _lib = lib
+        return lib
+
+
+def strerror(status: int) -> str:
+    try:
+        return load_library().ssd_strerror(int(status)).decode()
+    except RuntimeError:
+        return "library not loaded"
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+class _Workspace:
+    """Per-device cached workspace.  It is zero-filled when (re)allocated; the
+    kernels leave their flags and counters at zero, so it is reused as is."""
+
+    def __init__(self):
+        self._buf = {}
+        self._lock = threading.Lock()
+
+    def get(self, device: torch.device, nbytes: int) -> torch.Tensor:
+        key = (device.type, device.index)
+        with self._lock:
+            buf = self._buf.get(key)
+            if buf is None or buf.numel() < nbytes:
+                size = max(nbytes, 4096)
+                buf = torch.zeros(size, dtype=torch.uint8, device=device)
+                self._buf[key] = buf
+            return buf
+
+
+_scan_ws = _Workspace()
+_ssd_ws = _Workspace()
+
+
+def _check_cuda(name, t, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (got {t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def linear_scan(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """h[r, t] = a[r, t] h[r, t-1] + b[r, t] with h[r, -1] = 0, fp32 [rows, L]."""
+    lib = load_library()
+    _check_cuda("a", a, torch.float32)
+    if a.dim() != 2:
+        raise ValueError("a must be [rows, L]")
+    _check_cuda("b", b, torch.float32, a.shape)
+    rows, length = a.shape
+    h = torch.empty_like(a) if out is None else out
+    _check_cuda("out", h, torch.float32, a.shape)
+    need = lib.linear_scan_workspace_size(rows, length)
+    if need == 0:
+        raise SSDError(-2, "linear_scan_workspace_size")
+    ws = _scan_ws.get(a.device, need) if workspace is None else workspace
+    st = lib.linear_scan(_ptr(a), _ptr(b), _ptr(h), rows, length, _ptr(ws), ws.numel(),
+                         _stream_handle(a.device))
+    if st != SSD_OK:
+        raise SSDError(st, "linear_scan")
+    return h
+
+
+def ssd_fwd(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, want_final_state: bool = True,
+            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Mamba-2 SSD chunked forward pass.  Returns (y, h_final or None).
+
+    x [Bt,L,H,P] and B, C [Bt,L,G,S] in fp32 or bf16 (same dtype); dt
+    [Bt,L,H], A [H], D [H] (optional) and h0 [Bt,H,P,S] (optional) in fp32.
+    """
+    lib = load_library()
+    if x.dtype not in _DTYPE_CODE:
+        raise TypeError("x must be float32 or bfloat16")
+    _check_cuda("x", x, x.dtype)
+    if x.dim() != 4:
+        raise ValueError("x must be [batch, seqlen, nheads, headdim]")
+    Bt, L, H, P = x.shape
+    _check_cuda("B", B, x.dtype)
+    if B.dim() != 4 or B.shape[0] != Bt or B.shape[1] != L:
+        raise ValueError("B must be [batch, seqlen, ngroups, dstate]")
+    G, S = B.shape[2], B.shape[3]
+    _check_cuda("C", C, x.dtype, B.shape)
+    _check_cuda("dt", dt, torch.float32, (Bt, L, H))
+    _check_cuda("A", A, torch.float32, (H,))
+    if D is not None:
+        _check_cuda("D", D, torch.float32, (H,))
+    if h0 is not None:
+        _check_cuda("h0", h0, torch.float32, (Bt, H, P, S))
+    y = torch.empty_like(x) if out is None else out
+    _check_cuda("out", y, x.dtype, x.shape)
+    hf = torch.empty((Bt, H, P, S), dtype=torch.float32, device=x.device) if want_final_state else None
+    code = _DTYPE_CODE[x.dtype]
+    need = lib.ssd_fwd_workspace_size(Bt, L, H, P, S, G, chunk, code)
+    ws = workspace
+    if ws is None:
+        ws = _ssd_ws.get(x.device, max(need, 1))
+    st = lib.ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
+                     Bt, L, H, P, S, G, int(chunk), code, _ptr(y), _ptr(hf), _ptr(ws), ws.numel(),
+                     _stream_handle(x.device))
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_fwd")
+    return y, hf
+
+
+__all__ = ["linear_scan", "ssd_fwd", "load_library", "strerror", "SSDError", "LIB_PATH",
+           "SSD_F32", "SSD_BF16"]

@@ -1,0 +1,122 @@
+// C ABI of the library: host-side validation, workspace sizing and dispatch.
+// Every argument is checked before anything is enqueued; kernels are
+// launched on the caller's stream and nothing here synchronises.
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/chunked_linear_scan.h"
+#include "launch.hpp"
+
+namespace {
+
+constexpr int64_t kLsTile = 4096;  // elements per linear-scan tile
+constexpr size_t kHeader = 256;    // bytes: error word and padding
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+struct ScanPlan {
+    bool segmented;
+    int64_t tiles_per_row;
+    int64_t rows_per_tile;
+    int64_t ntiles;
+    size_t claim_off, done_off, status_off, bytes;
+};
+
+ScanPlan plan_scan(int64_t rows, int64_t L) {
+    ScanPlan p{};
+    p.segmented = L <= kLsTile - 6;
+    if (p.segmented) {
+        p.rows_per_tile = (kLsTile - 6) / L;
+        p.tiles_per_row = 1;
+        p.ntiles = (rows + p.rows_per_tile - 1) / p.rows_per_tile;
+        p.claim_off = p.done_off = p.status_off = kHeader;
+        p.bytes = kHeader;
+    } else {
+        p.rows_per_tile = 1;
+        p.tiles_per_row = (L + 3 + kLsTile - 1) / kLsTile;
+        p.ntiles = rows * p.tiles_per_row;
+        p.claim_off = kHeader;
+        p.done_off = p.claim_off + round_up(size_t(rows) * 4, 256);
+        p.status_off = p.done_off + round_up(size_t(rows) * 4, 256);
+        p.bytes = p.status_off + size_t(rows) * size_t(p.tiles_per_row) * 32;
+    }
+    return p;
+}
+
+bool scan_sizes_ok(int64_t rows, int64_t L) {
+    if (rows <= 0 || L <= 0) return false;
+    if (L > (int64_t(1) << 40) || rows > (int64_t(1) << 40)) return false;
+    const ScanPlan p = plan_scan(rows, L);
+    // grid x times 256 work-items must stay below 2^32
+    return p.ntiles <= (int64_t(1) << 23) && p.tiles_per_row < (int64_t(1) << 30);
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ssd_strerror(int status) {
+    switch (status) {
+        case SSD_OK: return "ok";
+        case SSD_ERR_NULL: return "a required pointer is NULL";
+        case SSD_ERR_SHAPE: return "invalid shape (a size <= 0, too large, or heads % groups != 0)";
+        case SSD_ERR_DTYPE: return "dtype must be SSD_F32 or SSD_BF16";
+        case SSD_ERR_CHUNK: return "chunk must be 16, 32, 64, 128 or 256";
+        case SSD_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case SSD_ERR_WORKSPACE: return "workspace is NULL or smaller than required";
+        case SSD_ERR_HIP: return "a HIP kernel launch failed";
+        case SSD_ERR_UNSUPPORTED: return "head dim / state size not supported by this dtype's kernels";
+        default: return "unknown status";
+    }
+}
+
+size_t linear_scan_workspace_size(int64_t rows, int64_t length) {
+    if (!scan_sizes_ok(rows, length)) return 0;
+    return plan_scan(rows, length).bytes;
+}
+
+int linear_scan(const float* a, const float* b, float* h, int64_t rows, int64_t length,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    if (!a || !b || !h || !workspace) return SSD_ERR_NULL;
+    if (!scan_sizes_ok(rows, length)) return SSD_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(h) || !aligned16(workspace)) return SSD_ERR_ALIGN;
+    const ScanPlan p = plan_scan(rows, length);
+    if (workspace_bytes < p.bytes) return SSD_ERR_WORKSPACE;
+    char* ws = static_cast<char*>(workspace);
+    return cls_launch_linear_scan(a, b, h, rows, length, p.segmented ? 1 : 0, int(p.tiles_per_row),
+                                  int(p.rows_per_tile), p.ntiles,
+                                  reinterpret_cast<uint32_t*>(ws + p.claim_off),
+                                  reinterpret_cast<uint32_t*>(ws + p.done_off), ws + p.status_off,
+                                  reinterpret_cast<uint32_t*>(ws), static_cast<hipStream_t>(stream));
+}
+
+size_t ssd_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                              int64_t dstate, int64_t ngroups, int64_t chunk, int dtype) {
+    SsdShape s{batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype};
+    if (cls_ssd_check(s) != SSD_OK) return 0;
+    return cls_ssd_workspace_bytes(s);
+}
+
+int ssd_fwd(const void* x, const float* dt, const float* A, const void* B, const void* C,
+            const float* D, const float* h0, int64_t batch, int64_t seqlen, int64_t nheads,
+            int64_t headdim, int64_t dstate, int64_t ngroups, int64_t chunk, int dtype, void* y,
+            float* h_final, void* workspace, size_t workspace_bytes, void* stream) {
+    if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
+    SsdShape s{batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype};
+    const int st = cls_ssd_check(s);
+    if (st != SSD_OK) return st;
+    const size_t need = cls_ssd_workspace_bytes(s);
+    if (need > 0 && !workspace) return SSD_ERR_NULL;
+    if (workspace_bytes < need) return SSD_ERR_WORKSPACE;
+    const void* ptrs[] = {x, dt, A, B, C, D, h0, y, h_final, workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    SsdArgs args{x, dt, A, B, C, D, h0, y, h_final, workspace};
+    return cls_ssd_launch(s, args, static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,38 @@
+// Internal launch interface between the C ABI (api.cpp) and the kernel
+// translation units.  Not part of the public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+struct SsdShape {
+    int64_t batch, seqlen, nheads, headdim, dstate, ngroups, chunk;
+    int dtype;
+};
+
+struct SsdArgs {
+    const void* x;
+    const float* dt;
+    const float* A;
+    const void* B;
+    const void* C;
+    const float* D;
+    const float* h0;
+    void* y;
+    float* h_final;
+    void* workspace;
+};
+
+extern "C" {
+int cls_launch_linear_scan(const float* a, const float* b, float* h, int64_t rows, int64_t L,
+                           int segmented, int tiles_per_row, int rows_per_tile, int64_t ntiles,
+                           uint32_t* claim, uint32_t* done, void* status, uint32_t* err,
+                           hipStream_t stream);
+
+// Shape/dtype/chunk validation shared by sizing and launching (SSD_OK or a
+// negative status).
+int cls_ssd_check(const SsdShape& s);
+size_t cls_ssd_workspace_bytes(const SsdShape& s);
+int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t stream);
+}

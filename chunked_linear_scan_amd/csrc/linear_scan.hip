@@ -1,0 +1,314 @@
+// Scalar linear recurrence h[t] = a[t] h[t-1] + b[t] on gfx950.
+//
+// The recurrence and its affine combine follow "Selective-scan CUDA kernels",
+// section "The problem"; the single-pass scheme (tiles claimed in order from a
+// counter, local aggregate published under flag A, look-back over a window of
+// predecessors until an inclusive prefix P is found, items scanned serially
+// in registers) follows its section "The five kernels" (levels 3b and 3c).
+//
+// MI355X choices:
+//   * a tile is 256 threads x 16 items = 4096 elements, loaded as 16-byte
+//     vectors from a 16-byte aligned window, so rows that start misaligned
+//     (ragged lengths) still use full vector loads; elements outside the row
+//     are the identity (a = 1, b = 0);
+//   * the in-tile scan is a 16-item serial scan per thread, a 64-lane wave
+//     scan and a 4-wave combine through LDS;
+//   * one 64-lane wave inspects 64 predecessors per look-back step and folds
+//     every aggregate between the tile and the nearest inclusive prefix with a
+//     6-step order-preserving tree reduction;
+//   * rows are independent chains: tiles are claimed from one counter per row,
+//     so claims never contend across rows and a row's chain never waits on
+//     another row;
+//   * the last tile of a row to finish clears the row's status words and
+//     counters, so the workspace is all-zero again after every call;
+//   * rows no longer than a tile are packed whole into tiles and scanned with a
+//     row-start reset flag, with no look-back at all.
+#include "common.hpp"
+
+namespace cls {
+
+constexpr int kLsThreads = 256;
+constexpr int kLsItems = 16;
+constexpr int kLsTile = kLsThreads * kLsItems;   // 4096 elements
+constexpr int kLsWaves = kLsThreads / 64;
+// Each look-back poll sleeps ~64 clocks; 2^24 polls is several seconds, far
+// beyond any legitimate wait, so a corrupted workspace ends the kernel instead
+// of hanging it (the error word is raised and the tile treats the missing
+// predecessors as the identity).
+constexpr uint32_t kLsSpinLimit = 1u << 24;
+
+// An affine step h -> a h + b.  In segmented (packed-rows) mode `f` marks a
+// run that contains a row start: such a run ignores whatever precedes it, so
+// a NaN/Inf at the end of one row cannot leak into the next.
+struct Pair {
+    float a, b;
+    int f;
+};
+
+// (first, then second): h -> s.a (f.a h + f.b) + s.b
+__device__ __forceinline__ Pair combine(Pair f, Pair s) {
+    if (s.f) return s;
+    return Pair{f.a * s.a, fmaf(s.a, f.b, s.b), f.f};
+}
+
+__device__ __forceinline__ void load16(const float* __restrict__ p, int64_t t0, int64_t lo,
+                                       int64_t hi, float ident, float (&v)[kLsItems]) {
+#pragma unroll
+    for (int q = 0; q < kLsItems / 4; ++q) {
+        const int64_t i = t0 + 4 * q;
+        if (i >= lo && i + 4 <= hi) {
+            const float4 w = *reinterpret_cast<const float4*>(p + i);
+            v[4 * q + 0] = w.x;
+            v[4 * q + 1] = w.y;
+            v[4 * q + 2] = w.z;
+            v[4 * q + 3] = w.w;
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int64_t e = i + k;
+                v[4 * q + k] = (e >= lo && e < hi) ? p[e] : ident;
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ void store16(float* __restrict__ p, int64_t t0, int64_t lo, int64_t hi,
+                                        const float (&v)[kLsItems]) {
+#pragma unroll
+    for (int q = 0; q < kLsItems / 4; ++q) {
+        const int64_t i = t0 + 4 * q;
+        if (i >= lo && i + 4 <= hi) {
+            *reinterpret_cast<float4*>(p + i) =
+                make_float4(v[4 * q + 0], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
+        } else {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int64_t e = i + k;
+                if (e >= lo && e < hi) p[e] = v[4 * q + k];
+            }
+        }
+    }
+}
+
+__device__ __forceinline__ u32x4 pack_status(Pair v) {
+    return u32x4{1u, as_uint(v.a), as_uint(v.b), 0u};
+}
+
+// Exclusive prefix of tile j of a row: the ordered combination of tiles
+// 0..j-1.  Runs on one full wave; every lane returns the same value.
+// status_row holds [tile][2] 16-byte words: [0] aggregate, [1] inclusive.
+__device__ Pair lookback(const u32x4* status_row, int j, uint32_t* err) {
+    const int lane = lane_id();
+    Pair acc{1.0f, 0.0f, 0};  // combination of the predecessors already folded
+    int base = j - 1;         // tile inspected by lane 0
+    uint32_t spins = 0;
+    while (true) {
+        const int p = base - lane;
+        int kind;  // 2 inclusive, 1 aggregate, 0 not yet published
+        Pair v{1.0f, 0.0f, 0};
+        if (p < 0) {
+            kind = 2;  // before the row start the state is 0: identity prefix
+        } else {
+            const u32x4 inc = load_coherent_b128(status_row + 2 * p + 1);
+            if (inc[0]) {
+                kind = 2;
+                v.a = as_float(inc[1]);
+                v.b = as_float(inc[2]);
+            } else {
+                const u32x4 ag = load_coherent_b128(status_row + 2 * p);
+                kind = ag[0] ? 1 : 0;
+                v.a = as_float(ag[1]);
+                v.b = as_float(ag[2]);
+            }
+        }
+        const uint64_t incm = __ballot(kind == 2);
+        const uint64_t notready = __ballot(kind == 0);
+        const int kp = incm ? int(__builtin_ctzll(incm)) : 64;
+        const uint64_t below = (kp >= 64) ? ~0ull : ((1ull << kp) - 1ull);
+        if (notready & below) {
+            if (++spins > kLsSpinLimit) {
+                if (lane == 0) atomic_add_u32(err, 1u);
+                return acc;
+            }
+            __builtin_amdgcn_s_sleep(1);
+            continue;
+        }
+        if (lane > kp) v = Pair{1.0f, 0.0f, 0};
+        // Ordered tree reduction: lane k ends up holding lanes [k, k+2d) with
+        // the higher lane (the earlier tile) applied first.
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            Pair o{shfl_down(v.a, d), shfl_down(v.b, d), 0};
+            if (lane + d >= 64) o = Pair{1.0f, 0.0f, 0};
+            v = combine(o, v);
+        }
+        const Pair win{bcast_lane0(v.a), bcast_lane0(v.b), 0};
+        acc = combine(win, acc);
+        if (kp < 64) return acc;
+        base -= 64;
+    }
+}
+
+// One tile per workgroup.  SEGMENTED: tiles hold whole rows and reset at each
+// row start (rows no longer than a tile); otherwise each tile belongs to one
+// row and the row's tiles chain through the look-back.
+template <bool SEGMENTED>
+__global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
+    const float* __restrict__ a, const float* __restrict__ b, float* __restrict__ h,
+    int64_t rows, int64_t L, int tiles_per_row, int rows_per_tile,
+    uint32_t* __restrict__ claim, uint32_t* __restrict__ done, u32x4* __restrict__ status,
+    uint32_t* __restrict__ err) {
+    __shared__ int s_tile;
+    __shared__ float s_wa[kLsWaves], s_wb[kLsWaves];
+    __shared__ int s_wf[kLsWaves];
+    __shared__ float s_pa, s_pb;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+
+    int64_t lo, hi, row = 0;
+    int j = 0;
+    if (SEGMENTED) {
+        const int64_t r0 = int64_t(blockIdx.x) * rows_per_tile;
+        const int64_t r1 = (r0 + rows_per_tile < rows) ? r0 + rows_per_tile : rows;
+        lo = r0 * L;
+        hi = r1 * L;
+    } else {
+        row = blockIdx.x / tiles_per_row;
+        if (tid == 0) s_tile = int(atomic_add_u32(&claim[row], 1u));
+        __syncthreads();
+        j = s_tile;
+        lo = row * L;
+        hi = lo + L;
+    }
+    const int64_t abase = (lo & ~int64_t(3)) + int64_t(j) * kLsTile;
+    const int64_t t0 = abase + int64_t(tid) * kLsItems;
+    const bool empty_tile = !SEGMENTED && abase >= hi;
+
+    // LS1: load 16 items and scan them serially in registers.  av/bv become
+    // the thread-local inclusive (A, B); rmask bit k says the run up to item k
+    // holds a row start (SEGMENTED only).
+    float av[kLsItems], bv[kLsItems];
+    uint32_t rmask = 0;
+    if (!empty_tile) {
+        load16(a, t0, lo, hi, 1.0f, av);
+        load16(b, t0, lo, hi, 0.0f, bv);
+        int64_t ns = 0;
+        if (SEGMENTED) ns = ((t0 + L - 1) / L) * L;  // first row start >= t0
+        int f = 0;
+#pragma unroll
+        for (int k = 0; k < kLsItems; ++k) {
+            bool reset = false;
+            if (SEGMENTED && t0 + k == ns && ns < hi) {
+                reset = true;
+                ns += L;
+            }
+            if (k > 0 && !reset) {
+                bv[k] = fmaf(av[k], bv[k - 1], bv[k]);
+                av[k] = av[k - 1] * av[k];
+            }
+            f |= reset ? 1 : 0;
+            rmask |= uint32_t(f) << k;
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < kLsItems; ++k) {
+            av[k] = 1.0f;
+            bv[k] = 0.0f;
+        }
+    }
+
+    // LS2: 64-lane inclusive scan of the thread aggregates, then the waves.
+    Pair w{av[kLsItems - 1], bv[kLsItems - 1], int(rmask >> (kLsItems - 1))};
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        Pair o{shfl_up(w.a, d), shfl_up(w.b, d), SEGMENTED ? shfl_up_i(w.f, d) : 0};
+        if (lane >= d) w = combine(o, w);
+    }
+    Pair lane_excl{shfl_up(w.a, 1), shfl_up(w.b, 1), SEGMENTED ? shfl_up_i(w.f, 1) : 0};
+    if (lane == 0) lane_excl = Pair{1.0f, 0.0f, 0};
+    if (lane == 63) {
+        s_wa[wave] = w.a;
+        s_wb[wave] = w.b;
+        s_wf[wave] = w.f;
+    }
+    __syncthreads();
+    Pair wave_excl{1.0f, 0.0f, 0};
+    Pair tile_agg{1.0f, 0.0f, 0};
+#pragma unroll
+    for (int q = 0; q < kLsWaves; ++q) {
+        const Pair s{s_wa[q], s_wb[q], s_wf[q]};
+        if (q < wave) wave_excl = combine(wave_excl, s);
+        tile_agg = combine(tile_agg, s);
+    }
+
+    // LS3: publish the aggregate, look back, publish the inclusive prefix.
+    if (!SEGMENTED) {
+        if (wave == 0) {
+            u32x4* srow = status + row * int64_t(tiles_per_row) * 2;
+            Pair prefix{1.0f, 0.0f, 0};
+            if (!empty_tile) {
+                if (j > 0) {
+                    if (lane == 0) store_coherent_b128(srow + 2 * j, pack_status(tile_agg));
+                    prefix = lookback(srow, j, err);
+                }
+                if (lane == 0) store_coherent_b128(srow + 2 * j + 1, pack_status(combine(prefix, tile_agg)));
+            }
+            if (lane == 0) {
+                s_pa = prefix.a;
+                s_pb = prefix.b;
+            }
+            // The row's last finisher clears its status words and counters;
+            // by then every tile of the row has finished reading them.
+            uint32_t last = 0;
+            if (lane == 0) last = (atomic_add_u32(&done[row], 1u) == uint32_t(tiles_per_row - 1)) ? 1u : 0u;
+            last = __builtin_amdgcn_readfirstlane(last);
+            if (last) {
+                for (int q = lane; q < 2 * tiles_per_row; q += 64)
+                    store_coherent_b128(srow + q, u32x4{0u, 0u, 0u, 0u});
+                if (lane == 0) {
+                    store_coherent_u32(&claim[row], 0u);
+                    store_coherent_u32(&done[row], 0u);
+                }
+            }
+        }
+        __syncthreads();
+        if (empty_tile) return;
+    }
+
+    // LS4: apply the prefix and store.  The state before this thread's first
+    // item is the b-part of the full prefix (the state before a row is 0);
+    // items whose run already holds a row start do not see it.
+    Pair pre = combine(wave_excl, lane_excl);
+    if (!SEGMENTED) pre = combine(Pair{s_pa, s_pb, 0}, pre);
+    const float hin = pre.b;
+#pragma unroll
+    for (int k = 0; k < kLsItems; ++k) {
+        const bool own = SEGMENTED && ((rmask >> k) & 1u);
+        bv[k] = own ? bv[k] : fmaf(av[k], hin, bv[k]);
+    }
+    store16(h, t0, lo, hi, bv);
+}
+
+}  // namespace cls
+
+extern "C" int cls_launch_linear_scan(const float* a, const float* b, float* h, int64_t rows,
+                                      int64_t L, int segmented, int tiles_per_row,
+                                      int rows_per_tile, int64_t ntiles, uint32_t* claim,
+                                      uint32_t* done, void* status, uint32_t* err,
+                                      hipStream_t stream) {
+    using namespace cls;
+    const dim3 grid{uint32_t(ntiles), 1u, 1u};
+    const dim3 block{uint32_t(kLsThreads), 1u, 1u};
+    if (segmented) {
+        hipLaunchKernelGGL(linear_scan_kernel<true>, grid, block, 0, stream, a, b, h, rows, L,
+                           tiles_per_row, rows_per_tile, claim, done,
+                           reinterpret_cast<u32x4*>(status), err);
+    } else {
+        hipLaunchKernelGGL(linear_scan_kernel<false>, grid, block, 0, stream, a, b, h, rows, L,
+                           tiles_per_row, rows_per_tile, claim, done,
+                           reinterpret_cast<u32x4*>(status), err);
+    }
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+}

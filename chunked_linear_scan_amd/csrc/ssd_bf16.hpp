@@ -1,0 +1,319 @@
+// bf16 SSD chunked forward pass on gfx950: MFMA contractions with fp32
+// accumulation and an fp32 state.
+//
+// Follows "Accelerating Mamba-2 with high-performance forward pass kernels in
+// NVIDIA cuTile".  Per chunk of T tokens and per (batch, head):
+//   S1  G = inclusive cumulative sum of A dt (kept in log2 units so every
+//       exponential is one exp2), section "Kernel 1";
+//   S2a CB = C B^T for the chunk, computed once per (batch, chunk, group) by
+//       ssd_cb_kernel and shared by all heads of the group (the page's output
+//       kernel recomputes it per head);
+//   S2b the decay-masked product (CB . exp(G_i - G_j) . dt_j . [i >= j]) X, with
+//       the skip term D x folded into the diagonal;
+//   S2c/S3 the state jump h <- exp(G_last) h + X^T (dt exp(G_last - G) . B),
+//       section "Kernel 2", with h carried in registers across chunks;
+//   S4  y = exp(G_i) (C_i h^T) + intra term, section "Kernel 3".
+// Positive exponents (j > i) are never kept: the masked entries are selected
+// away, not multiplied by zero.
+//
+// MFMA: v_mfma_f32_16x16x32_bf16.  Lane l holds A[l%16][8(l/16)..+7],
+// B[8(l/16)..+7][l%16] and D[4(l/16)..+3][l%16].  Every product is arranged
+// so its output columns are tokens or head-dim channels that a lane can store
+// or reuse without a register transpose:
+//   y^T[p][i]   = H[p][s] C[i][s]^T  +  X^T[p][j] W[i][j]^T     (k = s, then j)
+//   h^T[s][p]  += (B^T[s][t] w_t) X[t][p]                        (k = t)
+//   CB^T[j][i]  = B[j][s] C[i][s]^T                              (k = s)
+// The token-major operands (X and B for k = t) are transposed once per chunk
+// into LDS with an in-register 8x8 transpose.
+#pragma once
+
+#include "common.hpp"
+#include "ssd_kernels.hpp"
+
+namespace cls {
+
+constexpr int kBfThreads = 256;
+
+__device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
+    return *reinterpret_cast<const u32x4*>(p);
+}
+
+// ---------------------------------------------------------------------------
+// S2a: CB[b, c, g][i][j] = sum_s C[i][s] B[j][s] for the 32-token blocks with
+// block(j) <= block(i).  One workgroup per (batch, chunk, group).
+// ---------------------------------------------------------------------------
+template <int TT, int S>
+__global__ __launch_bounds__(kBfThreads) void ssd_cb_kernel(SsdBf16Params p) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, kg = lane >> 4;
+    const int64_t bcg = blockIdx.x;
+    const int g = int(bcg % p.G);
+    const int64_t c = (bcg / p.G) % p.nchunks;
+    const int64_t b = bcg / (int64_t(p.G) * p.nchunks);
+    const int64_t tok0 = c * p.chunk;
+    const int n = int((p.L - tok0 < p.chunk) ? (p.L - tok0) : p.chunk);
+    uint16_t* out = p.cb + bcg * (TT * TT);
+    const int64_t rowstride = int64_t(p.G) * S;
+    const uint16_t* Cbase = p.C + ((b * p.L + tok0) * p.G + g) * S;
+    const uint16_t* Bbase = p.B + ((b * p.L + tok0) * p.G + g) * S;
+
+    for (int it = wave; it < TT / 16; it += 4) {
+        const int i = 16 * it + l16;
+        u32x4 cf[S / 32];
+#pragma unroll
+        for (int ks = 0; ks < S / 32; ++ks)
+            cf[ks] = (i < n) ? ldg16(Cbase + i * rowstride + 32 * ks + 8 * kg) : u32x4{0, 0, 0, 0};
+        const int jt_end = (it | 1);
+        for (int jt = 0; jt <= jt_end; ++jt) {
+            const int j = 16 * jt + l16;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < S / 32; ++ks) {
+                const u32x4 bf = (j < n) ? ldg16(Bbase + j * rowstride + 32 * ks + 8 * kg) : u32x4{0, 0, 0, 0};
+                acc = mfma16x16x32(bf, cf[ks], acc);
+            }
+            // lane holds CB[i][16 jt + 4 kg + r], r = 0..3
+            u32x2 v;
+            v[0] = pack_bf16x2(acc[0], acc[1]);
+            v[1] = pack_bf16x2(acc[2], acc[3]);
+            *reinterpret_cast<u32x2*>(out + i * TT + 16 * jt + 4 * kg) = v;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// S1, S2b, S2c, S3, S4 for one (batch, head): chunks in order, state in
+// registers (fp32) and in LDS as the bf16 MFMA operand.
+// ---------------------------------------------------------------------------
+template <int TT, int P, int S>
+__global__ __launch_bounds__(kBfThreads) void ssd_chunk_kernel(SsdBf16Params p) {
+    constexpr int XP = TT + 8;         // LDS pitch (elements) of X^T and B^T rows
+    constexpr int HP = S + 8;          // LDS pitch of the bf16 state rows
+    constexpr int NPT = P / 16;        // head-dim tiles
+    constexpr int NST = S / 16;        // state tiles
+    constexpr int KS = (NST + 3) / 4;  // state tiles per wave
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
+    uint16_t* Xt = reinterpret_cast<uint16_t*>(smem_raw);   // [P][XP]
+    uint16_t* Bt = Xt + P * XP;                              // [S][XP]
+    uint16_t* Hs = Bt + S * XP;                              // [P][HP]
+    float* Gs = reinterpret_cast<float*>(Hs + P * HP);       // [TT]
+    float* dts = Gs + TT;                                    // [TT]
+    float* ws = dts + TT;                                    // [TT]
+    float* scratch = ws + TT;                                // [4]
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, kg = lane >> 4;
+    const int64_t bh = blockIdx.x;
+    const int64_t b = bh / p.H;
+    const int h = int(bh % p.H);
+    const int g = h / (p.H / p.G);
+    const float A2 = p.A[h] * kLog2e;
+    const float Dh = p.D ? p.D[h] : 0.0f;
+    const int64_t L = p.L;
+
+    // state h^T tiles owned by this wave: s-tiles st = wave + 4k, all p-tiles
+    f32x4 hacc[KS][NPT];
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        const int st = wave + 4 * k;
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) {
+            f32x4 v = {0.f, 0.f, 0.f, 0.f};
+            if (st < NST && p.h0) {
+                const float* src = p.h0 + (bh * P + 16 * pt + l16) * S + 16 * st + 4 * kg;
+                v = *reinterpret_cast<const f32x4*>(src);
+            }
+            hacc[k][pt] = v;
+            if (st < NST) {
+                u32x2 w;
+                w[0] = pack_bf16x2(v[0], v[1]);
+                w[1] = pack_bf16x2(v[2], v[3]);
+                *reinterpret_cast<u32x2*>(Hs + (16 * pt + l16) * HP + 16 * st + 4 * kg) = w;
+            }
+        }
+    }
+
+    for (int c = 0; c < p.nchunks; ++c) {
+        const int64_t tok0 = int64_t(c) * p.chunk;
+        const int n = int((L - tok0 < p.chunk) ? (L - tok0) : p.chunk);
+
+        // S1: cumulative sum of a_t (log2 units) inside the chunk
+        float dtv = 0.0f;
+        if (tid < n) dtv = p.dt[(b * L + tok0 + tid) * p.H + h];
+        const float G = block_inclusive_sum_256(A2 * dtv, scratch);
+        if (tid < TT) {
+            Gs[tid] = G;
+            dts[tid] = dtv;
+        }
+
+        // stage X^T [p][t] and B^T [s][t] (bf16) through an 8x8 register transpose
+        for (int q = tid; q < (TT / 8) * (P / 8); q += kBfThreads) {
+            const int tb = q / (P / 8), pb = q % (P / 8);
+            u32x4 r[8], o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int t = 8 * tb + e;
+                r[e] = (t < n) ? ldg16(p.x + ((b * L + tok0 + t) * p.H + h) * P + 8 * pb) : u32x4{0, 0, 0, 0};
+            }
+            transpose8x8_b16(r, o);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4*>(Xt + (8 * pb + e) * XP + 8 * tb) = o[e];
+        }
+        for (int q = tid; q < (TT / 8) * (S / 8); q += kBfThreads) {
+            const int tb = q / (S / 8), sb = q % (S / 8);
+            u32x4 r[8], o[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int t = 8 * tb + e;
+                r[e] = (t < n) ? ldg16(p.B + ((b * L + tok0 + t) * p.G + g) * S + 8 * sb) : u32x4{0, 0, 0, 0};
+            }
+            transpose8x8_b16(r, o);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4*>(Bt + (8 * sb + e) * XP + 8 * tb) = o[e];
+        }
+        __syncthreads();
+        const float Glast = Gs[TT - 1];  // padded positions add 0: G at the last real token
+        if (tid < TT) ws[tid] = dts[tid] * fexp2(Glast - Gs[tid]);
+
+        // S2b + S4: y^T tiles, 16 tokens per tile, tiles spread over the waves
+        const uint16_t* cbase = p.cb + ((b * p.nchunks + c) * p.G + g) * (TT * TT);
+        const uint16_t* Cbase = p.C + ((b * L + tok0) * p.G + g) * S;
+        const int ntile = (n + 15) / 16;
+        for (int it = wave; it < ntile; it += 4) {
+            const int i = 16 * it + l16;
+            const bool vi = i < n;
+            const float gi = Gs[i];
+            f32x4 acc[NPT];
+#pragma unroll
+            for (int pt = 0; pt < NPT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < S / 32; ++ks) {
+                const u32x4 cf = vi ? ldg16(Cbase + int64_t(i) * p.G * S + 32 * ks + 8 * kg) : u32x4{0, 0, 0, 0};
+#pragma unroll
+                for (int pt = 0; pt < NPT; ++pt) {
+                    const u32x4 hf = *reinterpret_cast<const u32x4*>(Hs + (16 * pt + l16) * HP + 32 * ks + 8 * kg);
+                    acc[pt] = mfma16x16x32(hf, cf, acc[pt]);
+                }
+            }
+            const float sc = fexp2(gi);
+#pragma unroll
+            for (int pt = 0; pt < NPT; ++pt) acc[pt] *= sc;
+            const int jb_end = (16 * it + 15) / 32;
+            for (int jb = 0; jb <= jb_end; ++jb) {
+                const int j0 = 32 * jb + 8 * kg;
+                const u32x4 cbw = ldg16(cbase + i * TT + j0);
+                float wv[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const uint32_t word = cbw[e >> 1];
+                    const float cbv = (e & 1) ? bf16_hi(word) : bf16_lo(word);
+                    const int j = j0 + e;
+                    float w = cbv * fexp2(gi - Gs[j]) * dts[j];
+                    w = (j <= i) ? w : 0.0f;
+                    w += (j == i) ? Dh : 0.0f;
+                    wv[e] = w;
+                }
+                u32x4 wf;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) wf[e] = pack_bf16x2(wv[2 * e], wv[2 * e + 1]);
+#pragma unroll
+                for (int pt = 0; pt < NPT; ++pt) {
+                    const u32x4 xf = *reinterpret_cast<const u32x4*>(Xt + (16 * pt + l16) * XP + 32 * jb + 8 * kg);
+                    acc[pt] = mfma16x16x32(xf, wf, acc[pt]);
+                }
+            }
+            if (vi) {
+                uint16_t* dst = p.y + ((b * L + tok0 + i) * p.H + h) * P + 4 * kg;
+#pragma unroll
+                for (int pt = 0; pt < NPT; ++pt) {
+                    u32x2 v;
+                    v[0] = pack_bf16x2(acc[pt][0], acc[pt][1]);
+                    v[1] = pack_bf16x2(acc[pt][2], acc[pt][3]);
+                    *reinterpret_cast<u32x2*>(dst + 16 * pt) = v;
+                }
+            }
+        }
+        __syncthreads();
+
+        // S2c + S3: h^T <- exp(G_last) h^T + (B^T w) X
+        const float alpha = fexp2(Glast);
+        const int ntb = (n + 31) / 32;
+#pragma unroll
+        for (int k = 0; k < KS; ++k)
+#pragma unroll
+            for (int pt = 0; pt < NPT; ++pt) hacc[k][pt] *= alpha;
+        for (int tb = 0; tb < ntb; ++tb) {
+            const int t0 = 32 * tb + 8 * kg;
+            float wt[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) wt[e] = ws[t0 + e];
+            u32x4 xf[NPT];
+#pragma unroll
+            for (int pt = 0; pt < NPT; ++pt)
+                xf[pt] = *reinterpret_cast<const u32x4*>(Xt + (16 * pt + l16) * XP + t0);
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                const int st = wave + 4 * k;
+                if (st >= NST) continue;
+                const u32x4 braw = *reinterpret_cast<const u32x4*>(Bt + (16 * st + l16) * XP + t0);
+                u32x4 af;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    af[e] = pack_bf16x2(bf16_lo(braw[e]) * wt[2 * e], bf16_hi(braw[e]) * wt[2 * e + 1]);
+#pragma unroll
+                for (int pt = 0; pt < NPT; ++pt) hacc[k][pt] = mfma16x16x32(af, xf[pt], hacc[k][pt]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            const int st = wave + 4 * k;
+            if (st >= NST) continue;
+#pragma unroll
+            for (int pt = 0; pt < NPT; ++pt) {
+                u32x2 w;
+                w[0] = pack_bf16x2(hacc[k][pt][0], hacc[k][pt][1]);
+                w[1] = pack_bf16x2(hacc[k][pt][2], hacc[k][pt][3]);
+                *reinterpret_cast<u32x2*>(Hs + (16 * pt + l16) * HP + 16 * st + 4 * kg) = w;
+            }
+        }
+        __syncthreads();
+    }
+
+    if (p.h_final) {
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            const int st = wave + 4 * k;
+            if (st >= NST) continue;
+#pragma unroll
+            for (int pt = 0; pt < NPT; ++pt) {
+                float* dst = p.h_final + (bh * P + 16 * pt + l16) * S + 16 * st + 4 * kg;
+                *reinterpret_cast<f32x4*>(dst) = hacc[k][pt];
+            }
+        }
+    }
+}
+
+template <int TT, int P, int S>
+int launch_ssd_bf16_tpl(const SsdBf16Params& prm, hipStream_t stream) {
+    const size_t lds = ssd_bf16_lds_bytes(TT, P, S);
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_chunk_kernel<TT, P, S>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
+            return -7;
+        attr_set = true;
+    }
+    const dim3 block{uint32_t(kBfThreads), 1u, 1u};
+    const dim3 gcb{uint32_t(prm.batch * prm.nchunks * prm.G), 1u, 1u};
+    hipLaunchKernelGGL((ssd_cb_kernel<TT, S>), gcb, block, 0, stream, prm);
+    const dim3 gmain{uint32_t(prm.batch * prm.H), 1u, 1u};
+    hipLaunchKernelGGL((ssd_chunk_kernel<TT, P, S>), gmain, block, lds, stream, prm);
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+}  // namespace cls

@@ -1,0 +1,114 @@
+/*
+ * chunked_linear_scan — MI355X (gfx950) Mamba-2 SSD chunked forward pass and
+ * scalar linear scan behind a plain C ABI.
+ *
+ * Every entry point takes plain pointers and sizes.  Device pointers are HIP
+ * device memory on the current device; `stream` is a hipStream_t passed as
+ * void* (NULL = the default stream).  All work is enqueued on that stream and
+ * nothing synchronises the host.  The library never allocates or frees device
+ * memory: the caller owns every buffer, including the workspace.
+ *
+ * Errors: arguments are validated on the host before anything is launched.
+ * A negative status means nothing was enqueued (except SSD_ERR_HIP, which is
+ * returned when a launch itself fails).  No exceptions cross this boundary.
+ *
+ * Workspace contract: size it with the matching *_workspace_size call, fill it
+ * with zero bytes once before its first use, and keep it for later calls; the
+ * kernels leave every flag and counter they use back at zero when they finish.
+ * Calls that share a workspace must be ordered on one stream.  After a call
+ * that returned an error from a launch, zero the workspace again.
+ */
+#ifndef CHUNKED_LINEAR_SCAN_H
+#define CHUNKED_LINEAR_SCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+enum {
+    SSD_OK = 0,
+    SSD_ERR_NULL = -1,        /* a required pointer is NULL                      */
+    SSD_ERR_SHAPE = -2,       /* a size is <= 0, or heads % groups != 0          */
+    SSD_ERR_DTYPE = -3,       /* dtype is not SSD_F32 or SSD_BF16                */
+    SSD_ERR_CHUNK = -4,       /* chunk is not one of 16, 32, 64, 128, 256        */
+    SSD_ERR_ALIGN = -5,       /* a pointer is not 16-byte aligned                */
+    SSD_ERR_WORKSPACE = -6,   /* workspace NULL or smaller than required         */
+    SSD_ERR_HIP = -7,         /* a HIP launch failed                             */
+    SSD_ERR_UNSUPPORTED = -8  /* head dim / state size outside the kernel's set  */
+};
+
+/* Element types of x, B, C and y.  dt, A, D and both states are always fp32. */
+enum { SSD_F32 = 0, SSD_BF16 = 1 };
+
+/*
+ * Mamba-2 SSD (state-space duality) chunked forward pass.
+ *
+ * Computes, per batch b and head h, the recurrence of "Accelerating Mamba-2
+ * with high-performance forward pass kernels in NVIDIA cuTile", section
+ * "Mamba-2 architecture":
+ *     h_t = exp(A[h] dt_t) h_{t-1} + dt_t B_t x_t^T,   y_t = c_t^T h_t + D[h] x_t
+ * with h_{-1} = h0, evaluated chunk by chunk as in that page's three kernel
+ * sections (cumulative sum of A dt inside each chunk, the state at each chunk
+ * start, the per-chunk output).  The output uses the token's own updated
+ * state (causal mask that keeps the diagonal).  Head h reads B/C group
+ * h / (nheads / ngroups).
+ *
+ * Layouts (row-major, contiguous, 16-byte aligned):
+ *   x, y      [batch, seqlen, nheads, headdim]   dtype
+ *   dt        [batch, seqlen, nheads]            fp32
+ *   A, D      [nheads]                           fp32  (D may be NULL = 0)
+ *   B, C      [batch, seqlen, ngroups, dstate]   dtype
+ *   h0        [batch, nheads, headdim, dstate]   fp32  (may be NULL = zeros)
+ *   h_final   [batch, nheads, headdim, dstate]   fp32  (may be NULL = not written)
+ *
+ * chunk: 16, 32, 64, 128 or 256 tokens; seqlen need not be a multiple of it.
+ * The decay exponents A[h] dt_t are expected to be <= 0 (decays in (0, 1]);
+ * the kernels rely on that to never keep a positive exponent.
+ *
+ * SSD_BF16 runs the MFMA path (bf16 operands, fp32 accumulation and fp32
+ * state); it supports headdim in {16, 32, 64, 128} and dstate in
+ * {16, 32, 64, 128, 256}.  SSD_F32 runs an fp32 path for any shape with
+ * headdim * dstate <= 16384.
+ *
+ * Outputs must not alias inputs.  Returns SSD_OK or a negative status.
+ */
+size_t ssd_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                              int64_t headdim, int64_t dstate, int64_t ngroups,
+                              int64_t chunk, int dtype);
+
+int ssd_fwd(const void* x, const float* dt, const float* A, const void* B,
+            const void* C, const float* D, const float* h0,
+            int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+            int64_t dstate, int64_t ngroups, int64_t chunk, int dtype,
+            void* y, float* h_final, void* workspace, size_t workspace_bytes,
+            void* stream);
+
+/*
+ * Scalar linear recurrence of "Selective-scan CUDA kernels", section "The
+ * problem":  h[r, t] = a[r, t] h[r, t-1] + b[r, t],  h[r, -1] = 0,
+ * independently for each of `rows` rows of `length` elements.
+ *
+ * Layout: a, b, h are [rows, length] fp32, row-major, contiguous, 16-byte
+ * aligned at the base (rows need not be aligned).  One single-pass kernel:
+ * each row is split into tiles that publish their aggregate and look back
+ * over up to 64 predecessors at a time (decoupled look-back).  The result is
+ * bit-identical from run to run.  h must not alias a or b.
+ */
+size_t linear_scan_workspace_size(int64_t rows, int64_t length);
+
+int linear_scan(const float* a, const float* b, float* h, int64_t rows,
+                int64_t length, void* workspace, size_t workspace_bytes,
+                void* stream);
+
+/* Human-readable text for a status code (static storage). */
+const char* ssd_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CHUNKED_LINEAR_SCAN_H */

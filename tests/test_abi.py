@@ -1,0 +1,98 @@
+"""C-ABI tests that need no GPU: the library loads, exports every function the
+public header declares, and rejects bad arguments on the host before any
+launch (validation runs before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunked_linear_scan_amd as cls
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "chunked_linear_scan.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(cls.LIB_PATH),
+                                reason="library not built (run __graft_entry__.build())")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)
+    skip = {"if", "sizeof", "defined"}
+    return sorted({n for n in names if n not in skip})
+
+
+def test_header_lists_expected_entry_points():
+    assert set(header_functions()) == {
+        "ssd_fwd_workspace_size", "ssd_fwd", "linear_scan_workspace_size", "linear_scan",
+        "ssd_strerror"}
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(cls.LIB_PATH)
+    for name in header_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_covers_every_status():
+    for st in range(0, -9, -1):
+        txt = cls.strerror(st)
+        assert txt and txt != "unknown status"
+    assert cls.strerror(-99) == "unknown status"
+
+
+FAKE = ctypes.c_void_p(0x10000)  # 16-byte aligned, never dereferenced on error paths
+
+
+def test_linear_scan_rejects_bad_arguments():
+    lib = cls.load_library()
+    ws = lib.linear_scan_workspace_size(4, 100)
+    assert ws > 0
+    assert lib.linear_scan(None, FAKE, FAKE, 4, 100, FAKE, ws, None) == -1
+    assert lib.linear_scan(FAKE, FAKE, FAKE, 0, 100, FAKE, ws, None) == -2
+    assert lib.linear_scan(FAKE, FAKE, FAKE, 4, -1, FAKE, ws, None) == -2
+    assert lib.linear_scan(FAKE, ctypes.c_void_p(0x10004), FAKE, 4, 100, FAKE, ws, None) == -5
+    assert lib.linear_scan(FAKE, FAKE, FAKE, 4, 100, FAKE, 0, None) == -6
+    assert lib.linear_scan(FAKE, FAKE, FAKE, 4, 100, None, ws, None) == -1
+
+
+def test_linear_scan_workspace_size_is_monotone_and_row_scaled():
+    lib = cls.load_library()
+    assert lib.linear_scan_workspace_size(0, 10) == 0
+    short = lib.linear_scan_workspace_size(1000, 100)      # packed rows: header only
+    long1 = lib.linear_scan_workspace_size(1, 65536)
+    long384 = lib.linear_scan_workspace_size(384, 65536)
+    assert short > 0 and long1 > 0
+    assert long384 > long1
+    assert long384 >= 384 * 16 * 32  # two 16-byte status words per tile
+
+
+def test_ssd_rejects_bad_arguments():
+    lib = cls.load_library()
+    args_ok = dict(Bt=1, L=64, H=2, P=16, S=32, G=1, T=32, dt=cls.SSD_BF16)
+
+    def call(x=FAKE, dtp=FAKE, A=FAKE, B=FAKE, C=FAKE, y=FAKE, ws=FAKE, ws_bytes=1 << 30, **kw):
+        a = dict(args_ok)
+        a.update(kw)
+        return lib.ssd_fwd(x, dtp, A, B, C, None, None, a["Bt"], a["L"], a["H"], a["P"], a["S"],
+                           a["G"], a["T"], a["dt"], y, None, ws, ws_bytes, None)
+
+    assert call(x=None) == -1
+    assert call(y=None) == -1
+    assert call(Bt=0) == -2
+    assert call(L=-5) == -2
+    assert call(H=3, G=2) == -2
+    assert call(dt=7) == -3
+    assert call(T=48) == -4
+    assert call(T=512) == -4
+    assert call(B=ctypes.c_void_p(0x10008)) == -5
+    assert call(ws_bytes=0) in (-6, -8)
+    assert call(P=24) in (-8, -2)
+
+
+def test_ssd_workspace_size_zero_for_invalid_shapes():
+    lib = cls.load_library()
+    assert lib.ssd_fwd_workspace_size(1, 64, 3, 16, 32, 2, 32, 1) == 0
+    assert lib.ssd_fwd_workspace_size(1, 64, 2, 16, 32, 1, 33, 1) == 0

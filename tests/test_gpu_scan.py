@@ -1,0 +1,125 @@
+"""GPU parity tests for linear_scan (HIP path through the C ABI) against the
+float64 oracle, at full workload sizes and at edge sizes, plus determinism and
+workspace hygiene.  Tolerance: rel-L2 <= 1e-5 for fp32 inputs."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_linear_scan_amd as cls
+from chunked_linear_scan_amd import workloads
+from oracle import compare, scan as oscan
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+def run(a, b):
+    h = cls.linear_scan(a.cuda(), b.cuda())
+    torch.cuda.synchronize()
+    return h.cpu().numpy()
+
+
+def check(a, b, tol=TOL, label=""):
+    print(f"[scan] {label} rows={a.shape[0]} L={a.shape[1]}", flush=True)
+    sys.stdout.flush()
+    got = run(a, b)
+    ref = oscan.scan_loop(a.numpy(), b.numpy())
+    err = compare.rel_l2(got, ref)
+    mm = compare.first_mismatch(got, ref, rtol=1e-4, atol=1e-5)
+    row_err = max(compare.rel_l2(got[r], ref[r]) for r in range(a.shape[0]))
+    assert err <= tol, (label, err, mm)
+    assert row_err <= 10 * tol, (label, row_err, mm)
+    return got, ref
+
+
+@pytest.mark.parametrize("name", ["scan", "scan_ragged"])
+def test_full_workload(name):
+    w = workloads.scan_workload(name)
+    got, ref = check(w["a"], w["b"], label=name)
+    head, tail = compare.band_report(got, ref, 4096, axis=1)
+    assert head <= TOL and tail <= TOL
+
+
+@pytest.mark.parametrize("rows,L", [
+    (1, 1), (3, 1), (5, 2), (7, 3), (2, 4), (4, 5), (3, 31), (3, 32), (3, 33), (1, 4089), (2, 4090),
+    (2, 4091), (2, 4093), (2, 4096), (2, 4097), (3, 8191), (3, 8192), (3, 8193), (1, 65533),
+    (5, 12345), (1000, 7), (257, 129)])
+def test_edge_sizes(rows, L):
+    w = workloads.make_scan_inputs(rows, L, seed=rows * 7919 + L)
+    check(w["a"], w["b"], label="edge")
+
+
+def test_very_long_row():
+    L = 1 << 22
+    w = workloads.make_scan_inputs(2, L, seed=11)
+    check(w["a"], w["b"], label="2^22")
+
+
+def test_long_lookback_chain():
+    # 1024 tiles in one row: the 64-lane window walks back many times
+    L = 4096 * 1024
+    a = torch.full((1, L), 0.999, dtype=torch.float32)
+    b = torch.randn(1, L, generator=torch.Generator().manual_seed(3))
+    check(a, b, label="chain")
+
+
+def test_special_cases():
+    g = torch.Generator().manual_seed(5)
+    b = torch.randn(4, 20000, generator=g)
+    got = run(torch.zeros_like(b), b)
+    assert np.array_equal(got, b.numpy())
+    got = run(torch.ones(4, 3000), b[:, :3000].contiguous())
+    ref = np.cumsum(b[:, :3000].numpy().astype(np.float64), axis=1)
+    assert compare.rel_l2(got, ref) < TOL
+
+
+def test_rows_do_not_leak_nonfinite_values():
+    # short rows are packed into one tile: an overflow in row 0 must not reach row 1
+    a = torch.full((3, 50), 10.0)
+    a[1] = 0.5
+    a[2] = 0.9
+    b = torch.ones(3, 50)
+    got = run(a, b)
+    assert np.isinf(got[0, -1])
+    ref = oscan.scan_loop(a[1:].numpy(), b[1:].numpy())
+    assert compare.rel_l2(got[1:], ref) < TOL
+    # long rows chain through the look-back: same check across rows
+    a = torch.full((2, 9000), 1.5)
+    a[1] = 0.95
+    b = torch.ones(2, 9000)
+    got = run(a, b)
+    ref = oscan.scan_loop(a[1:].numpy(), b[1:].numpy())
+    assert compare.rel_l2(got[1:], ref) < TOL
+
+
+def test_deterministic_and_workspace_clean():
+    w = workloads.scan_workload("scan_ragged")
+    a, b = w["a"].cuda(), w["b"].cuda()
+    lib = cls.load_library()
+    need = lib.linear_scan_workspace_size(*a.shape)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    first = cls.linear_scan(a, b, workspace=ws)
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0, "workspace must be all zero after a call"
+    for _ in range(100):
+        again = cls.linear_scan(a, b, workspace=ws)
+        assert torch.equal(again, first)
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0
+
+
+def test_workspace_reused_across_shapes():
+    lib = cls.load_library()
+    shapes = [(384, 65536), (7, 100000), (1000, 33), (3, 9000), (384, 65533)]
+    need = max(lib.linear_scan_workspace_size(r, L) for r, L in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, (r, L) in enumerate(shapes):
+        w = workloads.make_scan_inputs(r, L, seed=100 + i)
+        got = cls.linear_scan(w["a"].cuda(), w["b"].cuda(), workspace=ws).cpu().numpy()
+        ref = oscan.scan_loop(w["a"].numpy(), w["b"].numpy())
+        assert compare.rel_l2(got, ref) <= TOL, (r, L)
+    torch.cuda.synchronize()
+    assert int(ws.count_nonzero()) == 0
