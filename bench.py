@@ -111,45 +111,42 @@ def _oracle_ssd_job(args):
     return time.perf_counter() - t0
 
 
-def cpu_baseline_ssd(inp, shape, budget_s=20.0):
+def cpu_baseline_ssd(inp, shape, budget_s=15.0):
+    """Oracle wall time on as many whole (batch, head) sequences as fit the
+    budget (all of them when they do), one sequence per job, one job per core."""
     import multiprocessing as mp
-    import numpy as np
+    import torch
     cores = len(os.sched_getaffinity(0))
     H, G = shape.nheads, shape.ngroups
-    np64 = lambda t: None if t is None else t.to(dtype=__import__("torch").float64).numpy()
-    # one whole sequence per worker: (batch 0, head k) for k spread over groups
-    heads = [int(round(k * (H - 1) / max(cores - 1, 1))) for k in range(cores)]
-    jobs = []
-    for h in heads:
+    np64 = lambda t: None if t is None else t.to(dtype=torch.float64).numpy()
+
+    def job(bb, h, n=None):
         g = h // (H // G)
-        jobs.append((np64(inp["x"][:1, :, h:h + 1]), np64(inp["dt"][:1, :, h:h + 1]),
-                     np64(inp["A"][h:h + 1]), np64(inp["B"][:1, :, g:g + 1]),
-                     np64(inp["C"][:1, :, g:g + 1]), np64(inp["D"][h:h + 1]),
-                     None if inp["h0"] is None else np64(inp["h0"][:1, h:h + 1])))
-    # bound the sample: shorten the sequences if one would take too long
+        sl = slice(None) if n is None else slice(0, n)
+        return (np64(inp["x"][bb:bb + 1, sl, h:h + 1]), np64(inp["dt"][bb:bb + 1, sl, h:h + 1]),
+                np64(inp["A"][h:h + 1]), np64(inp["B"][bb:bb + 1, sl, g:g + 1]),
+                np64(inp["C"][bb:bb + 1, sl, g:g + 1]), np64(inp["D"][h:h + 1]),
+                None if inp["h0"] is None else np64(inp["h0"][bb:bb + 1, h:h + 1]))
+
     L = shape.seqlen
-    probe = min(L, 512)
-    t_probe = _oracle_ssd_job(tuple(v if v is None or v.ndim < 2 else v[:, :probe] for v in jobs[0]))
-    est = t_probe * L / probe
-    Ls = L if est <= budget_s else max(probe, int(L * budget_s / est))
-    jobs = [tuple(v if v is None or v.ndim < 2 else v[:, :Ls] for v in j) for j in jobs]
-    env_threads = {k: os.environ.get(k) for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS")}
-    for k in env_threads:
+    probe = min(L, 1024)
+    t_job = _oracle_ssd_job(job(0, 0, probe)) * L / probe
+    total = shape.batch * H
+    njobs = max(1, min(total, int(budget_s * cores / max(t_job, 1e-6))))
+    # spread the sampled sequences over batches and heads
+    pairs = [(k % shape.batch, (k * 7919) % H) for k in range(total)][:njobs] if njobs < total \
+        else [(bb, h) for bb in range(shape.batch) for h in range(H)]
+    for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
         os.environ[k] = "1"
+    jobs = [job(bb, h) for bb, h in pairs]
     t0 = time.perf_counter()
     with mp.get_context("spawn").Pool(cores) as pool:
-        pool.map(_oracle_ssd_job, jobs)
+        pool.map(_oracle_ssd_job, jobs, chunksize=1)
     wall = time.perf_counter() - t0
-    for k, v in env_threads.items():
-        if v is None:
-            os.environ.pop(k, None)
-        else:
-            os.environ[k] = v
-    # tokens/s counts a token once all H heads of its batch row are done
-    tok_equiv = Ls * len(jobs) / H
+    tok_equiv = L * len(jobs) / H  # a token counts once all H heads of its row are done
     return {"value": tok_equiv / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(jobs)} whole (batch 0, head) sequences of {Ls} tokens, one per "
-                      f"process ({len(jobs)}/{H} of one batch row), wall {wall:.1f}s"}
+            "sample": f"{len(jobs)} of {total} whole (batch, head) sequences of {L} tokens, "
+                      f"one per job on {cores} processes, wall {wall:.1f}s"}
 
 
 def cpu_baseline_scan(inp):
