@@ -36,14 +36,31 @@ __device__ __forceinline__ void store_coherent_b128(void* p, u32x4 v) {
                  : : "v"(p), "v"(v) : "memory");
 }
 
-// Store without waiting; pair with wait_vmem() before announcing a flag.
-__device__ __forceinline__ void store_coherent_b128_nowait(void* p, u32x4 v) {
-    asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+// Payloads larger than a status word are written and read with compiler-
+// generated relaxed agent-scope 64-bit atomics (sc1, device coherent).  They
+// must not be written with inline-asm stores that leave the store in flight:
+// the compiler cannot see that such an instruction still reads its data
+// registers and may overwrite them before the hardware has read the last
+// dwords.  Publish with wait_vmem() + a barrier before the flag store.
+__device__ __forceinline__ void store_payload(float* p, f32x4 v) {
+    const uint64_t lo = uint64_t(__builtin_bit_cast(uint32_t, float(v.x))) |
+                        (uint64_t(__builtin_bit_cast(uint32_t, float(v.y))) << 32);
+    const uint64_t hi = uint64_t(__builtin_bit_cast(uint32_t, float(v.z))) |
+                        (uint64_t(__builtin_bit_cast(uint32_t, float(v.w))) << 32);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p), lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(p) + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ u32x4 load_coherent_b128_nowait(const void* p) {
-    u32x4 v;
-    asm volatile("global_load_dwordx4 %0, %1, off sc1" : "=v"(v) : "v"(p) : "memory");
+__device__ __forceinline__ f32x4 load_payload(const float* p) {
+    const uint64_t lo = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(reinterpret_cast<const uint64_t*>(p) + 1, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+    f32x4 v;
+    v.x = __builtin_bit_cast(float, uint32_t(lo));
+    v.y = __builtin_bit_cast(float, uint32_t(lo >> 32));
+    v.z = __builtin_bit_cast(float, uint32_t(hi));
+    v.w = __builtin_bit_cast(float, uint32_t(hi >> 32));
     return v;
 }
 
@@ -99,6 +116,8 @@ __device__ __forceinline__ float bf16_lo(uint32_t w) { return __builtin_bit_cast
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
 __device__ __forceinline__ float fexp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ u32x4 ldg_b128(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // Inclusive sum over the first 256 threads of a 256-thread block (one value
 // per thread).  `scratch` holds 4 floats of LDS.  Ends with a barrier.

@@ -7,20 +7,28 @@
 // in registers) follows its section "The five kernels" (levels 3b and 3c).
 //
 // MI355X choices:
-//   * a tile is 256 threads x 16 items = 4096 elements, loaded as 16-byte
-//     vectors from a 16-byte aligned window, so rows that start misaligned
-//     (ragged lengths) still use full vector loads; elements outside the row
-//     are the identity (a = 1, b = 0);
-//   * the in-tile scan is a 16-item serial scan per thread, a 64-lane wave
-//     scan and a 4-wave combine through LDS;
+//   * a tile is 4 waves x 1024 elements; each wave owns a contiguous run and
+//     loads it as 16-byte vectors with lanes 16 bytes apart, so every
+//     wave-wide load covers 1 KB of consecutive memory; a 16-byte aligned
+//     window makes rows that start misaligned (ragged lengths) use the same
+//     vector loads; positions outside the row are the identity (a = 1, b = 0);
+//   * the in-tile scan is a 4-item serial scan per lane, a 64-lane wave scan
+//     per 256-element step with the step carry kept wave-uniform, and a
+//     4-wave combine through LDS;
 //   * one 64-lane wave inspects 64 predecessors per look-back step and folds
 //     every aggregate between the tile and the nearest inclusive prefix with a
 //     6-step order-preserving tree reduction;
 //   * rows are independent chains: tiles are claimed from one counter per row,
 //     so claims never contend across rows and a row's chain never waits on
 //     another row;
-//   * the last tile of a row to finish clears the row's status words and
-//     counters, so the workspace is all-zero again after every call;
+//   * the last tile of a row to finish (a per-row done counter, bumped after
+//     the tile's stores) clears the row's status words and counters, so the
+//     workspace is all-zero after every call and any later call, whatever its
+//     shape and workspace layout, starts clean;
+//   * a claimed index outside the row is treated as an empty tile, so even a
+//     corrupted workspace can only produce wrong values and bounded waits,
+//     never an out-of-range address;
+//   * the output is written with non-temporal stores (it is never re-read);
 //   * rows no longer than a tile are packed whole into tiles and scanned with a
 //     row-start reset flag, with no look-back at all.
 #include "common.hpp"
@@ -28,9 +36,10 @@
 namespace cls {
 
 constexpr int kLsThreads = 256;
-constexpr int kLsItems = 16;
-constexpr int kLsTile = kLsThreads * kLsItems;   // 4096 elements
 constexpr int kLsWaves = kLsThreads / 64;
+constexpr int kLsSteps = 4;                      // 256-element steps per wave
+constexpr int kLsWaveRun = kLsSteps * 256;       // 1024 elements per wave
+constexpr int kLsTile = kLsWaves * kLsWaveRun;   // 4096 elements per tile
 // Each look-back poll sleeps ~64 clocks; 2^24 polls is several seconds, far
 // beyond any legitimate wait, so a corrupted workspace ends the kernel instead
 // of hanging it (the error word is raised and the tile treats the missing
@@ -51,45 +60,31 @@ __device__ __forceinline__ Pair combine(Pair f, Pair s) {
     return Pair{f.a * s.a, fmaf(s.a, f.b, s.b), f.f};
 }
 
-__device__ __forceinline__ void load16(const float* __restrict__ p, int64_t t0, int64_t lo,
-                                       int64_t hi, float ident, float (&v)[kLsItems]) {
+__device__ __forceinline__ f32x4 load4(const float* __restrict__ p, int64_t i, int64_t lo, int64_t hi,
+                                       float ident) {
+    if (i >= lo && i + 4 <= hi) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + i));
+    f32x4 v;
 #pragma unroll
-    for (int q = 0; q < kLsItems / 4; ++q) {
-        const int64_t i = t0 + 4 * q;
-        if (i >= lo && i + 4 <= hi) {
-            const float4 w = *reinterpret_cast<const float4*>(p + i);
-            v[4 * q + 0] = w.x;
-            v[4 * q + 1] = w.y;
-            v[4 * q + 2] = w.z;
-            v[4 * q + 3] = w.w;
-        } else {
+    for (int k = 0; k < 4; ++k) {
+        const int64_t e = i + k;
+        v[k] = (e >= lo && e < hi) ? p[e] : ident;
+    }
+    return v;
+}
+
+__device__ __forceinline__ void store4(float* __restrict__ p, int64_t i, int64_t lo, int64_t hi, f32x4 v) {
+    if (i >= lo && i + 4 <= hi) {
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p + i));
+        return;
+    }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int64_t e = i + k;
-                v[4 * q + k] = (e >= lo && e < hi) ? p[e] : ident;
-            }
-        }
+    for (int k = 0; k < 4; ++k) {
+        const int64_t e = i + k;
+        if (e >= lo && e < hi) p[e] = v[k];
     }
 }
 
-__device__ __forceinline__ void store16(float* __restrict__ p, int64_t t0, int64_t lo, int64_t hi,
-                                        const float (&v)[kLsItems]) {
-#pragma unroll
-    for (int q = 0; q < kLsItems / 4; ++q) {
-        const int64_t i = t0 + 4 * q;
-        if (i >= lo && i + 4 <= hi) {
-            *reinterpret_cast<float4*>(p + i) =
-                make_float4(v[4 * q + 0], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const int64_t e = i + k;
-                if (e >= lo && e < hi) p[e] = v[4 * q + k];
-            }
-        }
-    }
-}
-
+// Status word: {1, alpha, beta, 0}; all-zero means not yet published.
 __device__ __forceinline__ u32x4 pack_status(Pair v) {
     return u32x4{1u, as_uint(v.a), as_uint(v.b), 0u};
 }
@@ -104,7 +99,7 @@ __device__ Pair lookback(const u32x4* status_row, int j, uint32_t* err) {
     uint32_t spins = 0;
     while (true) {
         const int p = base - lane;
-        int kind;  // 2 inclusive, 1 aggregate, 0 not yet published
+        int kind;  // 2 inclusive, 1 aggregate, 0 not yet published in this call
         Pair v{1.0f, 0.0f, 0};
         if (p < 0) {
             kind = 2;  // before the row start the state is 0: identity prefix
@@ -158,7 +153,7 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
     int64_t rows, int64_t L, int tiles_per_row, int rows_per_tile,
     uint32_t* __restrict__ claim, uint32_t* __restrict__ done, u32x4* __restrict__ status,
     uint32_t* __restrict__ err) {
-    __shared__ int s_tile;
+    __shared__ uint32_t s_claim;
     __shared__ float s_wa[kLsWaves], s_wb[kLsWaves];
     __shared__ int s_wf[kLsWaves];
     __shared__ float s_pa, s_pb;
@@ -168,7 +163,7 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
     const int wave = tid >> 6;
 
     int64_t lo, hi, row = 0;
-    int j = 0;
+    uint32_t cnt = 0;
     if (SEGMENTED) {
         const int64_t r0 = int64_t(blockIdx.x) * rows_per_tile;
         const int64_t r1 = (r0 + rows_per_tile < rows) ? r0 + rows_per_tile : rows;
@@ -176,62 +171,79 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
         hi = r1 * L;
     } else {
         row = blockIdx.x / tiles_per_row;
-        if (tid == 0) s_tile = int(atomic_add_u32(&claim[row], 1u));
+        if (tid == 0) s_claim = atomic_add_u32(&claim[row], 1u);
         __syncthreads();
-        j = s_tile;
+        cnt = s_claim;
         lo = row * L;
         hi = lo + L;
     }
+    const bool in_range = SEGMENTED || cnt < uint32_t(tiles_per_row);
+    const int j = in_range ? int(cnt) : 0;
     const int64_t abase = (lo & ~int64_t(3)) + int64_t(j) * kLsTile;
-    const int64_t t0 = abase + int64_t(tid) * kLsItems;
-    const bool empty_tile = !SEGMENTED && abase >= hi;
+    const bool empty_tile = !SEGMENTED && (!in_range || abase >= hi);
+    const int64_t wbase = abase + int64_t(wave) * kLsWaveRun + 4 * lane;  // + 256 q
 
-    // LS1: load 16 items and scan them serially in registers.  av/bv become
-    // the thread-local inclusive (A, B); rmask bit k says the run up to item k
-    // holds a row start (SEGMENTED only).
-    float av[kLsItems], bv[kLsItems];
-    uint32_t rmask = 0;
+    // LS1: load 4 steps of 4 items; scan the 4 items of each step serially.
+    f32x4 av[kLsSteps], bv[kLsSteps];
+    uint32_t rmask = 0;  // bit 4q+k: the run up to item k of step q holds a row start
     if (!empty_tile) {
-        load16(a, t0, lo, hi, 1.0f, av);
-        load16(b, t0, lo, hi, 0.0f, bv);
-        int64_t ns = 0;
-        if (SEGMENTED) ns = ((t0 + L - 1) / L) * L;  // first row start >= t0
-        int f = 0;
 #pragma unroll
-        for (int k = 0; k < kLsItems; ++k) {
-            bool reset = false;
-            if (SEGMENTED && t0 + k == ns && ns < hi) {
-                reset = true;
-                ns += L;
+        for (int q = 0; q < kLsSteps; ++q) {
+            av[q] = load4(a, wbase + 256 * q, lo, hi, 1.0f);
+            bv[q] = load4(b, wbase + 256 * q, lo, hi, 0.0f);
+        }
+#pragma unroll
+        for (int q = 0; q < kLsSteps; ++q) {
+            const int64_t t0 = wbase + 256 * q;
+            int64_t ns = 0;
+            if (SEGMENTED) ns = ((t0 + L - 1) / L) * L;  // first row start >= t0
+            int f = 0;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                bool reset = false;
+                if (SEGMENTED && t0 + k == ns && ns < hi) {
+                    reset = true;
+                    ns += L;
+                }
+                if (k > 0 && !reset) {
+                    bv[q][k] = fmaf(av[q][k], bv[q][k - 1], bv[q][k]);
+                    av[q][k] = av[q][k - 1] * av[q][k];
+                }
+                f |= reset ? 1 : 0;
+                rmask |= uint32_t(f) << (4 * q + k);
             }
-            if (k > 0 && !reset) {
-                bv[k] = fmaf(av[k], bv[k - 1], bv[k]);
-                av[k] = av[k - 1] * av[k];
-            }
-            f |= reset ? 1 : 0;
-            rmask |= uint32_t(f) << k;
         }
     } else {
 #pragma unroll
-        for (int k = 0; k < kLsItems; ++k) {
-            av[k] = 1.0f;
-            bv[k] = 0.0f;
+        for (int q = 0; q < kLsSteps; ++q) {
+            av[q] = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
+            bv[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
     }
 
-    // LS2: 64-lane inclusive scan of the thread aggregates, then the waves.
-    Pair w{av[kLsItems - 1], bv[kLsItems - 1], int(rmask >> (kLsItems - 1))};
+    // LS2: per step, a 64-lane scan of the lane aggregates; the steps chain
+    // through a wave-uniform carry.  pre[q] is the wave-local prefix in front
+    // of this lane's items of step q.
+    Pair pre[kLsSteps];
+    Pair carry{1.0f, 0.0f, 0};
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        Pair o{shfl_up(w.a, d), shfl_up(w.b, d), SEGMENTED ? shfl_up_i(w.f, d) : 0};
-        if (lane >= d) w = combine(o, w);
+    for (int q = 0; q < kLsSteps; ++q) {
+        Pair w{av[q][3], bv[q][3], int((rmask >> (4 * q + 3)) & 1u)};
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            Pair o{shfl_up(w.a, d), shfl_up(w.b, d), SEGMENTED ? shfl_up_i(w.f, d) : 0};
+            if (lane >= d) w = combine(o, w);
+        }
+        Pair ex{shfl_up(w.a, 1), shfl_up(w.b, 1), SEGMENTED ? shfl_up_i(w.f, 1) : 0};
+        if (lane == 0) ex = Pair{1.0f, 0.0f, 0};
+        pre[q] = combine(carry, ex);
+        const Pair tot{__shfl(w.a, 63, 64), __shfl(w.b, 63, 64), SEGMENTED ? __shfl(w.f, 63, 64) : 0};
+        carry = combine(carry, tot);
     }
-    Pair lane_excl{shfl_up(w.a, 1), shfl_up(w.b, 1), SEGMENTED ? shfl_up_i(w.f, 1) : 0};
-    if (lane == 0) lane_excl = Pair{1.0f, 0.0f, 0};
-    if (lane == 63) {
-        s_wa[wave] = w.a;
-        s_wb[wave] = w.b;
-        s_wf[wave] = w.f;
+    if (lane == 0) {
+        s_wa[wave] = carry.a;
+        s_wb[wave] = carry.b;
+        s_wf[wave] = carry.f;
     }
     __syncthreads();
     Pair wave_excl{1.0f, 0.0f, 0};
@@ -244,9 +256,9 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
     }
 
     // LS3: publish the aggregate, look back, publish the inclusive prefix.
+    u32x4* srow = status + row * int64_t(tiles_per_row) * 2;
     if (!SEGMENTED) {
         if (wave == 0) {
-            u32x4* srow = status + row * int64_t(tiles_per_row) * 2;
             Pair prefix{1.0f, 0.0f, 0};
             if (!empty_tile) {
                 if (j > 0) {
@@ -259,36 +271,43 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
                 s_pa = prefix.a;
                 s_pb = prefix.b;
             }
-            // The row's last finisher clears its status words and counters;
-            // by then every tile of the row has finished reading them.
-            uint32_t last = 0;
-            if (lane == 0) last = (atomic_add_u32(&done[row], 1u) == uint32_t(tiles_per_row - 1)) ? 1u : 0u;
-            last = __builtin_amdgcn_readfirstlane(last);
-            if (last) {
-                for (int q = lane; q < 2 * tiles_per_row; q += 64)
-                    store_coherent_b128(srow + q, u32x4{0u, 0u, 0u, 0u});
-                if (lane == 0) {
-                    store_coherent_u32(&claim[row], 0u);
-                    store_coherent_u32(&done[row], 0u);
-                }
-            }
         }
         __syncthreads();
-        if (empty_tile) return;
     }
 
-    // LS4: apply the prefix and store.  The state before this thread's first
-    // item is the b-part of the full prefix (the state before a row is 0);
-    // items whose run already holds a row start do not see it.
-    Pair pre = combine(wave_excl, lane_excl);
-    if (!SEGMENTED) pre = combine(Pair{s_pa, s_pb, 0}, pre);
-    const float hin = pre.b;
+    // LS4: apply the prefix and store.  The state in front of a lane's items
+    // is the b-part of the full prefix (the state before a row is 0); items
+    // whose run already holds a row start do not see it.
+    if (!empty_tile) {
+        Pair tp = wave_excl;
+        if (!SEGMENTED) tp = combine(Pair{s_pa, s_pb, 0}, tp);
 #pragma unroll
-    for (int k = 0; k < kLsItems; ++k) {
-        const bool own = SEGMENTED && ((rmask >> k) & 1u);
-        bv[k] = own ? bv[k] : fmaf(av[k], hin, bv[k]);
+        for (int q = 0; q < kLsSteps; ++q) {
+            const float hin = combine(tp, pre[q]).b;
+            f32x4 out;
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const bool own = SEGMENTED && ((rmask >> (4 * q + k)) & 1u);
+                out[k] = own ? bv[q][k] : fmaf(av[q][k], hin, bv[q][k]);
+            }
+            store4(h, wbase + 256 * q, lo, hi, out);
+        }
     }
-    store16(h, t0, lo, hi, bv);
+
+    // The row's last finisher clears its status words and counters; every
+    // tile of the row has finished its look-back before it counts itself done.
+    if (!SEGMENTED && wave == 0) {
+        uint32_t last = 0;
+        if (lane == 0) last = (atomic_add_u32(&done[row], 1u) == uint32_t(tiles_per_row - 1)) ? 1u : 0u;
+        last = __builtin_amdgcn_readfirstlane(last);
+        if (last) {
+            for (int q = lane; q < 2 * tiles_per_row; q += 64) store_coherent_b128(srow + q, u32x4{0u, 0u, 0u, 0u});
+            if (lane == 0) {
+                store_coherent_u32(&claim[row], 0u);
+                store_coherent_u32(&done[row], 0u);
+            }
+        }
+    }
 }
 
 }  // namespace cls
@@ -303,12 +322,10 @@ extern "C" int cls_launch_linear_scan(const float* a, const float* b, float* h, 
     const dim3 block{uint32_t(kLsThreads), 1u, 1u};
     if (segmented) {
         hipLaunchKernelGGL(linear_scan_kernel<true>, grid, block, 0, stream, a, b, h, rows, L,
-                           tiles_per_row, rows_per_tile, claim, done,
-                           reinterpret_cast<u32x4*>(status), err);
+                           tiles_per_row, rows_per_tile, claim, done, reinterpret_cast<u32x4*>(status), err);
     } else {
         hipLaunchKernelGGL(linear_scan_kernel<false>, grid, block, 0, stream, a, b, h, rows, L,
-                           tiles_per_row, rows_per_tile, claim, done,
-                           reinterpret_cast<u32x4*>(status), err);
+                           tiles_per_row, rows_per_tile, claim, done, reinterpret_cast<u32x4*>(status), err);
     }
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }

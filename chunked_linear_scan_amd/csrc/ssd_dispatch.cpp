@@ -26,7 +26,63 @@ int ssd_bf16_launch(int TT, int P, int S, const SsdBf16Params& prm, hipStream_t 
     }
 }
 
+// Segments per sequence for the fused kernel: one when there are at least as
+// many sequences as compute units, else enough to give every CU about two
+// workgroups, at most 64 (the look-back window) and at most one per chunk.
+static int g_segments_override = 0;
+static int g_force_path = 0;  // 0 auto, 1 the per-(batch, head) chunk kernel, 2 the fused kernel
+
+SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
+                            int64_t chunk, int dtype) {
+    SsdFusedPlan pl{};
+    const int TT = bf16_tile_tokens(int(chunk));
+    pl.use = dtype == 1 && P == 64 && (S == 64 || S == 128) && ssd_fused_lds_bytes(TT, int(S)) > 0 &&
+             ssd_fused_lds_bytes(TT, int(S)) <= 160 * 1024 && g_force_path != 1;
+    if (!pl.use) return pl;
+    const int64_t nc = (L + chunk - 1) / chunk;
+    const int64_t nchains = batch * H;
+    int64_t nsegs;
+    if (g_segments_override > 0) {
+        nsegs = g_segments_override;
+    } else if (nchains >= 256) {
+        nsegs = 1;
+    } else {
+        nsegs = (512 + nchains - 1) / nchains;
+    }
+    if (nsegs > 64) nsegs = 64;
+    if (nsegs > nc) nsegs = nc;
+    if (nsegs < 1) nsegs = 1;
+    const int64_t k = (nc + nsegs - 1) / nsegs;
+    nsegs = (nc + k - 1) / k;
+    const int64_t ntiles = nsegs * nchains;
+    if (ntiles >= (int64_t(1) << 24)) {
+        pl.use = false;
+        return pl;
+    }
+    pl.TT = TT;
+    pl.nsegs = int(nsegs);
+    pl.seg_chunks = int(k);
+    pl.nchains = int(nchains);
+    pl.ntiles = int(ntiles);
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    pl.status_off = 256;
+    pl.payload_off = pl.status_off + up(size_t(ntiles) * 16);
+    const size_t pay = nsegs > 1 ? size_t(ntiles) * 2 * 256 * ssd_fused_state_floats(int(S)) * 4 : 0;
+    pl.cb_off = pl.payload_off + up(pay);
+    pl.bytes = pl.cb_off + size_t(batch) * size_t(nc) * size_t(G) * size_t(TT) * TT * 2;
+    return pl;
+}
+
 }  // namespace cls
+
+// Tuning hook (not part of the public header): force the number of segments
+// per sequence of the fused SSD kernel (0 restores the heuristic).
+extern "C" void cls_ssd_set_segments(int nsegs) { cls::g_segments_override = nsegs < 0 ? 0 : nsegs; }
+
+// Validation hook (not part of the public header): 1 forces the per-(batch,
+// head) chunk kernel for bf16 shapes the fused kernel also covers, 0 restores
+// the automatic choice.
+extern "C" void cls_ssd_force_path(int path) { cls::g_force_path = path; }
 
 namespace {
 
@@ -59,6 +115,9 @@ extern "C" int cls_ssd_check(const SsdShape& s) {
 
 extern "C" size_t cls_ssd_workspace_bytes(const SsdShape& s) {
     if (s.dtype == SSD_F32) return 0;
+    const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
+                                                     s.ngroups, s.chunk, s.dtype);
+    if (pl.use) return pl.bytes;
     const int64_t TT = cls::bf16_tile_tokens(int(s.chunk));
     return size_t(s.batch) * size_t(nchunks(s)) * size_t(s.ngroups) * size_t(TT * TT) * 2 + 256;
 }
@@ -86,6 +145,42 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
     p.G = int(s.ngroups);
     p.chunk = int(s.chunk);
     p.nchunks = int(nchunks(s));
+    const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
+                                                     s.ngroups, s.chunk, s.dtype);
+    if (pl.use) {
+        char* ws = static_cast<char*>(a.workspace);
+        p.cb = reinterpret_cast<uint16_t*>(ws + pl.cb_off);
+        p.claim = reinterpret_cast<uint32_t*>(ws + 64);
+        p.status = ws + pl.status_off;
+        p.zero_count = pl.ntiles;
+        cls::SsdFusedParams f{};
+        f.x = p.x;
+        f.dt = p.dt;
+        f.A = p.A;
+        f.B = p.B;
+        f.C = p.C;
+        f.D = p.D;
+        f.h0 = p.h0;
+        f.y = p.y;
+        f.h_final = p.h_final;
+        f.cb = p.cb;
+        f.claim = p.claim;
+        f.status = reinterpret_cast<cls::u32x4_t*>(ws + pl.status_off);
+        f.payload = reinterpret_cast<float*>(ws + pl.payload_off);
+        f.err = reinterpret_cast<uint32_t*>(ws);
+        f.batch = s.batch;
+        f.L = s.seqlen;
+        f.H = int(s.nheads);
+        f.G = int(s.ngroups);
+        f.chunk = int(s.chunk);
+        f.nchunks = p.nchunks;
+        f.seg_chunks = pl.seg_chunks;
+        f.nsegs = pl.nsegs;
+        f.nchains = pl.nchains;
+        const int st = cls::ssd_fused_launch(pl.TT, int(s.dstate), p, f, pl.ntiles, stream);
+        if (st == -8) return SSD_ERR_UNSUPPORTED;
+        return st == 0 ? SSD_OK : SSD_ERR_HIP;
+    }
     const int TT = cls::bf16_tile_tokens(int(s.chunk));
     const int st = cls::ssd_bf16_launch(TT, int(s.headdim), int(s.dstate), p, stream);
     if (st == -8) return SSD_ERR_UNSUPPORTED;

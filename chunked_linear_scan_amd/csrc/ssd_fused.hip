@@ -1,0 +1,58 @@
+// Launchers of the fused head-dim-64 SSD kernel (see ssd_fused.hpp) and of
+// the CB pass that precedes it.
+#include "ssd_bf16.hpp"
+#include "ssd_fused.hpp"
+
+namespace cls {
+
+template <int TT, int S>
+static int launch_fused_tpl(const SsdBf16Params& cbp, const SsdFusedParams& fp, int ntiles,
+                            hipStream_t stream) {
+    using Lay = FuLayout<TT, S>;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_kernel<TT, S>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, Lay::BYTES) != hipSuccess)
+            return -7;
+        attr_set = true;
+    }
+    const dim3 block{256u, 1u, 1u};
+    const dim3 gcb{uint32_t(cbp.batch * cbp.nchunks * cbp.G), 1u, 1u};
+    hipLaunchKernelGGL((ssd_cb_kernel<TT, S>), gcb, block, 0, stream, cbp);
+    const dim3 gmain{uint32_t(ntiles), 1u, 1u};
+    hipLaunchKernelGGL((ssd_fused_kernel<TT, S>), gmain, block, Lay::BYTES, stream, fp);
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+size_t ssd_fused_lds_bytes(int TT, int S) {
+    switch (TT * 1000 + S) {
+        case 32064: return FuLayout<32, 64>::BYTES;
+        case 32128: return FuLayout<32, 128>::BYTES;
+        case 64064: return FuLayout<64, 64>::BYTES;
+        case 64128: return FuLayout<64, 128>::BYTES;
+        case 128064: return FuLayout<128, 64>::BYTES;
+        case 128128: return FuLayout<128, 128>::BYTES;
+        case 256064: return FuLayout<256, 64>::BYTES;
+        case 256128: return FuLayout<256, 128>::BYTES;
+        default: return 0;
+    }
+}
+
+int ssd_fused_state_floats(int S) { return (S / 64) * 16; }
+
+int ssd_fused_launch(int TT, int S, const SsdBf16Params& cbp, const SsdFusedParams& fp, int ntiles,
+                     hipStream_t stream) {
+    switch (TT * 1000 + S) {
+        case 32064: return launch_fused_tpl<32, 64>(cbp, fp, ntiles, stream);
+        case 32128: return launch_fused_tpl<32, 128>(cbp, fp, ntiles, stream);
+        case 64064: return launch_fused_tpl<64, 64>(cbp, fp, ntiles, stream);
+        case 64128: return launch_fused_tpl<64, 128>(cbp, fp, ntiles, stream);
+        case 128064: return launch_fused_tpl<128, 64>(cbp, fp, ntiles, stream);
+        case 128128: return launch_fused_tpl<128, 128>(cbp, fp, ntiles, stream);
+        case 256064: return launch_fused_tpl<256, 64>(cbp, fp, ntiles, stream);
+        case 256128: return launch_fused_tpl<256, 128>(cbp, fp, ntiles, stream);
+        default: return -8;
+    }
+}
+
+}  // namespace cls

@@ -7,6 +7,8 @@
 
 namespace cls {
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
 struct SsdF32Params {
     const void* x;
     const float* dt;
@@ -37,6 +39,36 @@ struct SsdBf16Params {
     uint16_t* cb;        // workspace: bf16 [Bt, Nc, G, TT, TT]
     int64_t batch, L;
     int H, G, chunk, nchunks;
+    // look-back bookkeeping the CB pass resets for the fused kernel
+    uint32_t* claim;     // tile claim counter
+    void* status;        // [zero_count] 16-byte status words
+    int zero_count;
+};
+
+struct SsdFusedParams {
+    const uint16_t* x;
+    const float* dt;
+    const float* A;
+    const uint16_t* B;
+    const uint16_t* C;
+    const float* D;
+    const float* h0;
+    uint16_t* y;
+    float* h_final;
+    const uint16_t* cb;
+    uint32_t* claim;
+    u32x4_t* status;     // [ntiles] {flag, alpha, 0, 0}
+    float* payload;      // [ntiles][2][256][state floats per lane]
+    uint32_t* err;
+    int64_t batch, L;
+    int H, G, chunk, nchunks, seg_chunks, nsegs, nchains;
+};
+
+// Plan of the fused head-dim-64 path for one shape (also sizes its workspace).
+struct SsdFusedPlan {
+    bool use;
+    int TT, nsegs, seg_chunks, nchains, ntiles;
+    size_t status_off, payload_off, cb_off, bytes;
 };
 
 // Tile sizes of the bf16 path: the chunk is padded to a multiple of 32 tokens.
@@ -54,6 +86,13 @@ constexpr bool ssd_bf16_lds_fits(int TT, int P, int S) {
 }
 
 bool ssd_bf16_supported(int TT, int P, int S);
+
+size_t ssd_fused_lds_bytes(int TT, int S);
+int ssd_fused_state_floats(int S);
+int ssd_fused_launch(int TT, int S, const SsdBf16Params& cbp, const SsdFusedParams& fp, int ntiles,
+                     hipStream_t stream);
+SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
+                            int64_t chunk, int dtype);
 int ssd_bf16_launch(int TT, int P, int S, const SsdBf16Params& prm, hipStream_t stream);
 
 }  // namespace cls

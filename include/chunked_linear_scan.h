@@ -13,10 +13,12 @@
  * returned when a launch itself fails).  No exceptions cross this boundary.
  *
  * Workspace contract: size it with the matching *_workspace_size call, fill it
- * with zero bytes once before its first use, and keep it for later calls; the
- * kernels leave every flag and counter they use back at zero when they finish.
- * Calls that share a workspace must be ordered on one stream.  After a call
- * that returned an error from a launch, zero the workspace again.
+ * with zero bytes once before its first use, and keep it for later calls of
+ * any shape that fits it: the kernels keep it consistent from call to call
+ * (per-call epochs and counters the kernels themselves advance or reset), so
+ * it is never cleared again.  Calls that share a workspace must be ordered on
+ * one stream.  After a call that returned an error from a launch, zero the
+ * workspace again.
  */
 #ifndef CHUNKED_LINEAR_SCAN_H
 #define CHUNKED_LINEAR_SCAN_H
@@ -71,8 +73,10 @@ enum { SSD_F32 = 0, SSD_BF16 = 1 };
  *
  * SSD_BF16 runs the MFMA path (bf16 operands, fp32 accumulation and fp32
  * state); it supports headdim in {16, 32, 64, 128} and dstate in
- * {16, 32, 64, 128, 256}.  SSD_F32 runs an fp32 path for any shape with
- * headdim * dstate <= 16384.
+ * {32, 64, 128, 256} where the chunk's tiles fit the 160 KB of LDS
+ * (SSD_ERR_UNSUPPORTED otherwise; ssd_fwd_workspace_size returns 0 then).
+ * SSD_F32 runs an fp32 path for any shape with headdim * dstate <= 16384 and
+ * headdim, dstate multiples of 4.
  *
  * Outputs must not alias inputs.  Returns SSD_OK or a negative status.
  */

@@ -216,3 +216,22 @@ def test_full_workloads_sampled(name, bsel, hsel):
             T = inp["chunk"]
             assert compare.rel_l2(gy[bi, -T:, hi], ry[bi, -T:, hi]) <= TOL_BF16
     assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("nsegs", [1, 2, 3, 7, 64])
+def test_segment_lookback_forced(nsegs):
+    """The fused kernel splits each sequence into segments chained by a
+    decoupled look-back over state aggregates; force the segment count so the
+    protocol runs with one-chunk segments, uneven segments and the 64-segment
+    window."""
+    lib = cls.load_library()
+    lib.cls_ssd_set_segments.argtypes = [__import__("ctypes").c_int]
+    inp = small_case(20 + nsegs, 2, 64 * 40 + 17, 3, 64, 128, 1, torch.bfloat16, dt_shift=-4.0)
+    lib.cls_ssd_set_segments(nsegs)
+    try:
+        y, hf = gpu_run(inp, chunk=32)
+    finally:
+        lib.cls_ssd_set_segments(0)
+    ry, rh, _, _ = oracle_run(inp)
+    assert_close(y, ry, TOL_BF16, f"y nsegs={nsegs}")
+    assert_close(hf, rh, TOL_BF16, f"h nsegs={nsegs}")
