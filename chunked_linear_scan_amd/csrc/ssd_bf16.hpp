@@ -45,10 +45,21 @@ __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
 
 // ---------------------------------------------------------------------------
 // S2a: CB[b, c, g][i][j] = sum_s C[i][s] B[j][s] for the 32-token blocks with
-// block(j) <= block(i).  One workgroup per (batch, chunk, group).
+// block(j) <= block(i), and, when p.bt is set, B^T[b, c, g][s][t] (the
+// token-contiguous copy of B that the fused kernel reads as an MFMA operand).
+// Padded rows and columns (token >= chunk length) are written as zeros.
+// One workgroup per (batch, chunk, group, 32-row block ib): wave w computes
+// the 16-row tile 2 ib + (w & 1) against the 16-column tiles (w >> 1) + 2 q.
 // ---------------------------------------------------------------------------
+template <int TT>
+inline uint32_t cb_grid(const SsdBf16Params& prm) {
+    return uint32_t(prm.batch * prm.nchunks * prm.G * (TT / 32));
+}
+
 template <int TT, int S>
 __global__ __launch_bounds__(kBfThreads) void ssd_cb_kernel(SsdBf16Params p) {
+    constexpr int KS = S / 32;
+    constexpr int NIB = TT / 32;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kg = lane >> 4;
     // reset the fused kernel's look-back bookkeeping (it runs after this pass)
@@ -59,7 +70,8 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cb_kernel(SsdBf16Params p) {
             st[q] = u32x4{0u, 0u, 0u, 0u};
         if (blockIdx.x == 0 && tid == 0) *p.claim = 0u;
     }
-    const int64_t bcg = blockIdx.x;
+    const int ib = int(blockIdx.x % NIB);
+    const int64_t bcg = blockIdx.x / NIB;
     const int g = int(bcg % p.G);
     const int64_t c = (bcg / p.G) % p.nchunks;
     const int64_t b = bcg / (int64_t(p.G) * p.nchunks);
@@ -70,26 +82,50 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cb_kernel(SsdBf16Params p) {
     const uint16_t* Cbase = p.C + ((b * p.L + tok0) * p.G + g) * S;
     const uint16_t* Bbase = p.B + ((b * p.L + tok0) * p.G + g) * S;
 
-    for (int it = wave; it < TT / 16; it += 4) {
-        const int i = 16 * it + l16;
-        u32x4 cf[S / 32];
+    const int it = 2 * ib + (wave & 1);
+    const int i = 16 * it + l16;
+    u32x4 cf[KS];
 #pragma unroll
-        for (int ks = 0; ks < S / 32; ++ks)
-            cf[ks] = (i < n) ? ldg16(Cbase + i * rowstride + 32 * ks + 8 * kg) : u32x4{0, 0, 0, 0};
-        const int jt_end = (it | 1);
-        for (int jt = 0; jt <= jt_end; ++jt) {
-            const int j = 16 * jt + l16;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KS; ++ks)
+        cf[ks] = (i < n) ? ldg16(Cbase + i * rowstride + 32 * ks + 8 * kg) : u32x4{0, 0, 0, 0};
+    auto load_b = [&](int jt, u32x4 (&dst)[KS]) {
+        const int j = 16 * jt + l16;
 #pragma unroll
-            for (int ks = 0; ks < S / 32; ++ks) {
-                const u32x4 bf = (j < n) ? ldg16(Bbase + j * rowstride + 32 * ks + 8 * kg) : u32x4{0, 0, 0, 0};
-                acc = mfma16x16x32(bf, cf[ks], acc);
+        for (int ks = 0; ks < KS; ++ks)
+            dst[ks] = (j < n) ? ldg16(Bbase + j * rowstride + 32 * ks + 8 * kg) : u32x4{0, 0, 0, 0};
+    };
+    u32x4 bcur[KS], bnxt[KS];
+    int jt = wave >> 1;
+    load_b(jt, bcur);
+    for (int q = 0; q <= ib; ++q) {
+        if (q < ib) load_b(jt + 2, bnxt);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(bcur[ks], cf[ks], acc);
+        // lane holds CB[i][16 jt + 4 kg + r], r = 0..3
+        u32x2 v;
+        v[0] = pack_bf16x2(acc[0], acc[1]);
+        v[1] = pack_bf16x2(acc[2], acc[3]);
+        *reinterpret_cast<u32x2*>(out + i * TT + 16 * jt + 4 * kg) = v;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) bcur[ks] = bnxt[ks];
+        jt += 2;
+    }
+    if (p.bt) {
+        // B^T[s][t] for the block's 32 tokens: thread item (s, 8-token group)
+        uint16_t* bt = p.bt + bcg * (int64_t(S) * TT);
+        for (int u = tid; u < S * 4; u += kBfThreads) {
+            const int s = u % S;
+            const int t0 = 32 * ib + 8 * (u / S);
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int ta = t0 + 2 * e, tb = ta + 1;
+                const uint32_t lo = ta < n ? Bbase[ta * rowstride + s] : 0u;
+                const uint32_t hi = tb < n ? Bbase[tb * rowstride + s] : 0u;
+                w[e] = lo | (hi << 16);
             }
-            // lane holds CB[i][16 jt + 4 kg + r], r = 0..3
-            u32x2 v;
-            v[0] = pack_bf16x2(acc[0], acc[1]);
-            v[1] = pack_bf16x2(acc[2], acc[3]);
-            *reinterpret_cast<u32x2*>(out + i * TT + 16 * jt + 4 * kg) = v;
+            *reinterpret_cast<u32x4*>(bt + s * TT + t0) = u32x4{w[0], w[1], w[2], w[3]};
         }
     }
 }
@@ -317,7 +353,7 @@ int launch_ssd_bf16_tpl(const SsdBf16Params& prm, hipStream_t stream) {
         attr_set = true;
     }
     const dim3 block{uint32_t(kBfThreads), 1u, 1u};
-    const dim3 gcb{uint32_t(prm.batch * prm.nchunks * prm.G), 1u, 1u};
+    const dim3 gcb{cb_grid<TT>(prm), 1u, 1u};
     hipLaunchKernelGGL((ssd_cb_kernel<TT, S>), gcb, block, 0, stream, prm);
     const dim3 gmain{uint32_t(prm.batch * prm.H), 1u, 1u};
     hipLaunchKernelGGL((ssd_chunk_kernel<TT, P, S>), gmain, block, lds, stream, prm);

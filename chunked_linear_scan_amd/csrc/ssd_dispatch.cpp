@@ -67,9 +67,10 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     pl.status_off = 256;
     pl.payload_off = pl.status_off + up(size_t(ntiles) * 16);
-    const size_t pay = nsegs > 1 ? size_t(ntiles) * 2 * 256 * ssd_fused_state_floats(int(S)) * 4 : 0;
+    const size_t pay = nsegs > 1 ? size_t(ntiles) * 2 * ssd_fused_state_floats(int(S)) * 4 : 0;
     pl.cb_off = pl.payload_off + up(pay);
-    pl.bytes = pl.cb_off + size_t(batch) * size_t(nc) * size_t(G) * size_t(TT) * TT * 2;
+    pl.bt_off = pl.cb_off + up(size_t(batch) * size_t(nc) * size_t(G) * size_t(TT) * TT * 2);
+    pl.bytes = pl.bt_off + size_t(batch) * size_t(nc) * size_t(G) * size_t(S) * TT * 2;
     return pl;
 }
 
@@ -150,6 +151,7 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
     if (pl.use) {
         char* ws = static_cast<char*>(a.workspace);
         p.cb = reinterpret_cast<uint16_t*>(ws + pl.cb_off);
+        p.bt = reinterpret_cast<uint16_t*>(ws + pl.bt_off);
         p.claim = reinterpret_cast<uint32_t*>(ws + 64);
         p.status = ws + pl.status_off;
         p.zero_count = pl.ntiles;
@@ -164,6 +166,7 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
         f.y = p.y;
         f.h_final = p.h_final;
         f.cb = p.cb;
+        f.bt = p.bt;
         f.claim = p.claim;
         f.status = reinterpret_cast<cls::u32x4_t*>(ws + pl.status_off);
         f.payload = reinterpret_cast<float*>(ws + pl.payload_off);

@@ -16,11 +16,12 @@ static int launch_fused_tpl(const SsdBf16Params& cbp, const SsdFusedParams& fp, 
             return -7;
         attr_set = true;
     }
-    const dim3 block{256u, 1u, 1u};
-    const dim3 gcb{uint32_t(cbp.batch * cbp.nchunks * cbp.G), 1u, 1u};
-    hipLaunchKernelGGL((ssd_cb_kernel<TT, S>), gcb, block, 0, stream, cbp);
+    const dim3 gcb{cb_grid<TT>(cbp), 1u, 1u};
+    const dim3 bcb{uint32_t(kBfThreads), 1u, 1u};
+    hipLaunchKernelGGL((ssd_cb_kernel<TT, S>), gcb, bcb, 0, stream, cbp);
     const dim3 gmain{uint32_t(ntiles), 1u, 1u};
-    hipLaunchKernelGGL((ssd_fused_kernel<TT, S>), gmain, block, Lay::BYTES, stream, fp);
+    const dim3 bmain{uint32_t(kFuThreads), 1u, 1u};
+    hipLaunchKernelGGL((ssd_fused_kernel<TT, S>), gmain, bmain, Lay::BYTES, stream, fp);
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
@@ -38,7 +39,7 @@ size_t ssd_fused_lds_bytes(int TT, int S) {
     }
 }
 
-int ssd_fused_state_floats(int S) { return (S / 64) * 16; }
+int ssd_fused_state_floats(int S) { return kFuP * S; }
 
 int ssd_fused_launch(int TT, int S, const SsdBf16Params& cbp, const SsdFusedParams& fp, int ntiles,
                      hipStream_t stream) {

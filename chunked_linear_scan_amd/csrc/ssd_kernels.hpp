@@ -37,6 +37,7 @@ struct SsdBf16Params {
     uint16_t* y;         // bf16 [Bt, L, H, P]
     float* h_final;      // [Bt, H, P, S] or null
     uint16_t* cb;        // workspace: bf16 [Bt, Nc, G, TT, TT]
+    uint16_t* bt;        // workspace: bf16 [Bt, Nc, G, S, TT] (B^T), or null when not needed
     int64_t batch, L;
     int H, G, chunk, nchunks;
     // look-back bookkeeping the CB pass resets for the fused kernel
@@ -56,9 +57,10 @@ struct SsdFusedParams {
     uint16_t* y;
     float* h_final;
     const uint16_t* cb;
+    const uint16_t* bt;
     uint32_t* claim;
     u32x4_t* status;     // [ntiles] {flag, alpha, 0, 0}
-    float* payload;      // [ntiles][2][256][state floats per lane]
+    float* payload;      // [ntiles][2][threads][state floats per lane]
     uint32_t* err;
     int64_t batch, L;
     int H, G, chunk, nchunks, seg_chunks, nsegs, nchains;
@@ -68,7 +70,7 @@ struct SsdFusedParams {
 struct SsdFusedPlan {
     bool use;
     int TT, nsegs, seg_chunks, nchains, ntiles;
-    size_t status_off, payload_off, cb_off, bytes;
+    size_t status_off, payload_off, cb_off, bt_off, bytes;
 };
 
 // Tile sizes of the bf16 path: the chunk is padded to a multiple of 32 tokens.
@@ -88,7 +90,7 @@ constexpr bool ssd_bf16_lds_fits(int TT, int P, int S) {
 bool ssd_bf16_supported(int TT, int P, int S);
 
 size_t ssd_fused_lds_bytes(int TT, int S);
-int ssd_fused_state_floats(int S);
+int ssd_fused_state_floats(int S);  // floats of one [64, S] state
 int ssd_fused_launch(int TT, int S, const SsdBf16Params& cbp, const SsdFusedParams& fp, int ntiles,
                      hipStream_t stream);
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
