@@ -2,14 +2,17 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ssd_large]
 
-One step is one ``ssd_fwd`` call (segment sums, CB, intra-chunk products,
-chunk states, inter-chunk recurrence and outputs) over one batch of the named
-workload, with inputs already resident in HBM.  K steps are timed with HIP
-events on the launch stream, bracketed by device synchronisation.  Input and
-output buffers rotate over enough copies that the footprint exceeds 1 GiB, so
-the 256 MB Infinity Cache cannot serve repeated steps.  The linear scan is
-timed the same way in its own loop and reported in the ``linear_scan`` object
-of the same JSON line.
+One step is one ``ssd_fwd`` call over one batch of the named workload, with
+inputs already resident in HBM: the CB pass (C B^T per (batch, chunk, group)
+and the token-contiguous copy of B) and the fused kernel (segment sums,
+intra-chunk products, chunk states, the inter-chunk recurrence and outputs).
+K steps are timed with HIP events on the launch stream, bracketed by device
+synchronisation; during the same steps the library records events around
+each of its two kernels, which gives the fused kernel's own time for the
+roofline.  Input and output buffers rotate over enough copies that the
+footprint exceeds 1 GiB, so the 256 MB Infinity Cache cannot serve repeated
+steps.  The linear scan (one kernel) is timed the same way in its own loop and
+reported in the ``linear_scan`` object of the same JSON line.
 
 The CPU baseline is the float64 oracle, unmodified, run on a bounded sample
 of the same workload (a few whole (batch, head) sequences, one per worker
@@ -84,11 +87,13 @@ def measured_traffic(kernel_key, sources, launches_per_step=1):
     return rec.get("hbm_bytes_per_launch")
 
 
-def time_loop(fn, nsets, steps, warmup, stream):
+def time_loop(fn, nsets, steps, warmup, stream, before_timed=None):
     import torch
     for i in range(warmup):
         fn(i % nsets)
     torch.cuda.synchronize()
+    if before_timed is not None:
+        before_timed()
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     start.record(stream)
@@ -183,20 +188,41 @@ def bench_ssd(name, steps, warmup, want_cpu):
         cls.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=shape.chunk,
                     out=d["y"])
 
-    t = time_loop(step, nsets, steps, warmup, stream)
+    lib = cls.load_library()
+    import ctypes
+    lib.cls_ssd_profile.argtypes = [ctypes.c_int]
+    lib.cls_ssd_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double)] * 2 + [ctypes.POINTER(ctypes.c_int)]
+    if lib.cls_ssd_profile(1) != 0:  # creates the events
+        raise RuntimeError("could not create the profiling events")
+    lib.cls_ssd_profile(0)
+    t = time_loop(step, nsets, steps, warmup, stream, before_timed=lambda: lib.cls_ssd_profile(1))
+    cb_ms, fu_ms, ncalls = ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
+    if lib.cls_ssd_profile_read(ctypes.byref(cb_ms), ctypes.byref(fu_ms), ctypes.byref(ncalls)) != 0:
+        raise RuntimeError("reading the profiling events failed")
+    lib.cls_ssd_profile(0)
+    n = max(ncalls.value, 1)
+    t_fused = fu_ms.value / 1e3 / n if ncalls.value else None
+    t_cb = cb_ms.value / 1e3 / n if ncalls.value else None
     tokens = shape.batch * shape.seqlen
     flops = ssd_alg_flops(shape)
-    gbs = alg_bytes / t / 1e9
-    tflops = flops / t / 1e12
-    srcs = ["ssd_bf16.hpp", "common.hpp", "ssd_kernels.hpp"]
+    t_kernel = t_fused if t_fused else t
+    gbs = alg_bytes / t_kernel / 1e9
+    tflops = flops / t_kernel / 1e12
+    t_roof = max(alg_bytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12))
+    srcs = ["ssd_fused.hpp", "ssd_fused.hip", "common.hpp", "ssd_kernels.hpp"]
     res = {
         "t": t, "tokens_per_s": tokens / t, "alg_bytes": alg_bytes, "alg_flops": flops,
         "gbs": gbs, "tflops": tflops, "nsets": nsets,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("ssd_fwd:" + name, srcs),
+                     "traffic": measured_traffic("ssd_fused_kernel:" + name, srcs),
+                     "kernel": "ssd_fused_kernel" if t_fused else "whole ssd_fwd call",
+                     "kernel_us": round(t_kernel * 1e6, 2),
+                     "cb_pass_us": None if t_cb is None else round(t_cb * 1e6, 2),
+                     "call_us": round(t * 1e6, 2),
+                     "alg_bytes": alg_bytes, "alg_flops": flops,
                      "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                     "kernels": "ssd_cb_kernel + ssd_chunk_kernel, timed together per call"},
+                     "call_frac_of_roofline": round(t_roof / t, 4)},
         "shape": shape,
     }
     if want_cpu:
@@ -243,6 +269,9 @@ def main():
     ap.add_argument("--scan-workload", default="scan", choices=["scan", "scan_ragged"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-scan", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run three plain 1 GiB device copies (the known-size reference that "
+                         "scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); run it with --gpus 1",
@@ -252,6 +281,13 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_probe:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     want_cpu = not args.no_cpu_baseline
     ssd = bench_ssd(args.workload, args.steps, args.warmup, want_cpu)
     shape = ssd["shape"]

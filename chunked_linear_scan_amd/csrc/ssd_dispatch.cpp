@@ -1,4 +1,6 @@
 // SSD validation, workspace sizing and dispatch to the fp32 or bf16 path.
+#include <vector>
+
 #include "../../include/chunked_linear_scan.h"
 #include "launch.hpp"
 #include "ssd_kernels.hpp"
@@ -75,6 +77,65 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
 }
 
 }  // namespace cls
+
+// Measurement hook (not part of the public header).  While enabled, every
+// fused-path ssd_fwd call records three events on its stream: before the CB
+// pass, between the CB pass and the fused kernel, and after the fused kernel.
+// Up to kProfCalls calls are kept (later calls reuse the slots round robin).
+namespace {
+constexpr int kProfCalls = 1024;
+struct ProfRecord {
+    bool on = false;
+    int calls = 0;
+    std::vector<hipEvent_t> ev;  // 3 per call
+};
+ProfRecord g_prof;
+}  // namespace
+
+namespace cls {
+hipEvent_t* ssd_profile_events() {
+    if (!g_prof.on) return nullptr;
+    hipEvent_t* e = g_prof.ev.data() + 3 * (g_prof.calls % kProfCalls);
+    ++g_prof.calls;
+    return e;
+}
+}  // namespace cls
+
+// enable != 0: start a new record (creating the events once); 0: stop.
+// Returns 0, or SSD_ERR_HIP when the events cannot be created.
+extern "C" int cls_ssd_profile(int enable) {
+    if (enable && g_prof.ev.empty()) {
+        g_prof.ev.resize(3 * kProfCalls);
+        for (auto& e : g_prof.ev)
+            if (hipEventCreate(&e) != hipSuccess) {
+                g_prof.ev.clear();
+                return SSD_ERR_HIP;
+            }
+    }
+    g_prof.on = enable != 0;
+    if (enable) g_prof.calls = 0;
+    return SSD_OK;
+}
+
+// Waits for the recorded calls and returns the summed CB-pass and fused-kernel
+// times in milliseconds and the number of calls summed.
+extern "C" int cls_ssd_profile_read(double* cb_ms, double* fused_ms, int* calls) {
+    double a = 0.0, b = 0.0;
+    const int n = g_prof.calls < kProfCalls ? g_prof.calls : kProfCalls;
+    for (int i = 0; i < n; ++i) {
+        hipEvent_t* e = g_prof.ev.data() + 3 * i;
+        float t0 = 0.f, t1 = 0.f;
+        if (hipEventSynchronize(e[2]) != hipSuccess || hipEventElapsedTime(&t0, e[0], e[1]) != hipSuccess ||
+            hipEventElapsedTime(&t1, e[1], e[2]) != hipSuccess)
+            return SSD_ERR_HIP;
+        a += t0;
+        b += t1;
+    }
+    if (cb_ms) *cb_ms = a;
+    if (fused_ms) *fused_ms = b;
+    if (calls) *calls = n;
+    return SSD_OK;
+}
 
 // Tuning hook (not part of the public header): force the number of segments
 // per sequence of the fused SSD kernel (0 restores the heuristic).
@@ -180,7 +241,7 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
         f.seg_chunks = pl.seg_chunks;
         f.nsegs = pl.nsegs;
         f.nchains = pl.nchains;
-        const int st = cls::ssd_fused_launch(pl.TT, int(s.dstate), p, f, pl.ntiles, stream);
+        const int st = cls::ssd_fused_launch(pl.TT, int(s.dstate), p, f, pl.ntiles, stream, cls::ssd_profile_events());
         if (st == -8) return SSD_ERR_UNSUPPORTED;
         return st == 0 ? SSD_OK : SSD_ERR_HIP;
     }

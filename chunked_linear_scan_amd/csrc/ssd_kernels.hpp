@@ -91,8 +91,10 @@ bool ssd_bf16_supported(int TT, int P, int S);
 
 size_t ssd_fused_lds_bytes(int TT, int S);
 int ssd_fused_state_floats(int S);  // floats of one [64, S] state
+// ev: null, or three events recorded before the CB pass, between the passes
+// and after the fused kernel (measurement hook)
 int ssd_fused_launch(int TT, int S, const SsdBf16Params& cbp, const SsdFusedParams& fp, int ntiles,
-                     hipStream_t stream);
+                     hipStream_t stream, hipEvent_t* ev);
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
                             int64_t chunk, int dtype);
 int ssd_bf16_launch(int TT, int P, int S, const SsdBf16Params& prm, hipStream_t stream);
