@@ -28,25 +28,33 @@ int ssd_bf16_launch(int TT, int P, int S, const SsdBf16Params& prm, hipStream_t 
     }
 }
 
-// Segments per sequence for the fused kernel: one when there are at least as
-// many sequences as compute units, else enough to give every CU about two
-// workgroups, at most 64 (the look-back window) and at most one per chunk.
+// Segments per sequence for the fused kernel: one when there are at least 128
+// sequences (a segment after the first re-runs its chunks once for the state
+// aggregate, which costs more than idle compute units), else enough for about
+// 512 workgroups, at most 64 (the look-back window) and at most one per chunk.
 static int g_segments_override = 0;
 static int g_force_path = 0;  // 0 auto, 1 the per-(batch, head) chunk kernel, 2 the fused kernel
 
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
                             int64_t chunk, int dtype) {
     SsdFusedPlan pl{};
+    // The kernel's quadratic block is at most 128 tokens: a longer chunk is run
+    // as sub-chunks of 128 with the state passed between them, which changes the
+    // result only by rounding (the chunked form equals the recurrence for every
+    // chunk length).
+    chunk = chunk > kFusedMaxChunk ? kFusedMaxChunk : chunk;
     const int TT = bf16_tile_tokens(int(chunk));
     pl.use = dtype == 1 && P == 64 && (S == 64 || S == 128) && ssd_fused_lds_bytes(TT, int(S)) > 0 &&
              ssd_fused_lds_bytes(TT, int(S)) <= 160 * 1024 && g_force_path != 1;
+    // the kernel's per-chunk buffer ranges and lane offsets are 32-bit
+    if (H * 64 * 2 * TT >= (int64_t(1) << 31) || G * S * 2 * TT >= (int64_t(1) << 31)) pl.use = false;
     if (!pl.use) return pl;
     const int64_t nc = (L + chunk - 1) / chunk;
     const int64_t nchains = batch * H;
     int64_t nsegs;
     if (g_segments_override > 0) {
         nsegs = g_segments_override;
-    } else if (nchains >= 256) {
+    } else if (nchains >= 128) {
         nsegs = 1;
     } else {
         nsegs = (512 + nchains - 1) / nchains;
@@ -62,6 +70,7 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
         return pl;
     }
     pl.TT = TT;
+    pl.chunk = int(chunk);
     pl.nsegs = int(nsegs);
     pl.seg_chunks = int(k);
     pl.nchains = int(nchains);
@@ -210,6 +219,8 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
     const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
                                                      s.ngroups, s.chunk, s.dtype);
     if (pl.use) {
+        p.chunk = pl.chunk;
+        p.nchunks = int((s.seqlen + pl.chunk - 1) / pl.chunk);
         char* ws = static_cast<char*>(a.workspace);
         p.cb = reinterpret_cast<uint16_t*>(ws + pl.cb_off);
         p.bt = reinterpret_cast<uint16_t*>(ws + pl.bt_off);
@@ -236,7 +247,7 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
         f.L = s.seqlen;
         f.H = int(s.nheads);
         f.G = int(s.ngroups);
-        f.chunk = int(s.chunk);
+        f.chunk = p.chunk;
         f.nchunks = p.nchunks;
         f.seg_chunks = pl.seg_chunks;
         f.nsegs = pl.nsegs;

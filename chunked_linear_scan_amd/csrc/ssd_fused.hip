@@ -36,8 +36,6 @@ size_t ssd_fused_lds_bytes(int TT, int S) {
         case 64128: return FuLayout<64, 128>::BYTES;
         case 128064: return FuLayout<128, 64>::BYTES;
         case 128128: return FuLayout<128, 128>::BYTES;
-        case 256064: return FuLayout<256, 64>::BYTES;
-        case 256128: return FuLayout<256, 128>::BYTES;
         default: return 0;
     }
 }
@@ -53,8 +51,6 @@ int ssd_fused_launch(int TT, int S, const SsdBf16Params& cbp, const SsdFusedPara
         case 64128: return launch_fused_tpl<64, 128>(cbp, fp, ntiles, stream, ev);
         case 128064: return launch_fused_tpl<128, 64>(cbp, fp, ntiles, stream, ev);
         case 128128: return launch_fused_tpl<128, 128>(cbp, fp, ntiles, stream, ev);
-        case 256064: return launch_fused_tpl<256, 64>(cbp, fp, ntiles, stream, ev);
-        case 256128: return launch_fused_tpl<256, 128>(cbp, fp, ntiles, stream, ev);
         default: return -8;
     }
 }

@@ -13,8 +13,8 @@
 // matrix-valued state and run as a single-pass decoupled look-back (section
 // "The five kernels") over segments of chunks.
 //
-// Work unit (one workgroup, 8 waves): segment `seg` of chain (b, h), i.e.
-// chunks [seg K, seg K + K).  A sequence split into several segments runs
+// Work unit (one workgroup): segment `seg` of chain (b, h), i.e. chunks
+// [seg K, seg K + K).  A sequence split into several segments runs
 //   phase 1: the segment's own aggregate S_seg (zero initial state) and its
 //            decay alpha_seg = exp2(sum of the chunks' G_last);
 //   publish: the aggregate (flag 1), or for segment 0 the inclusive state
@@ -27,17 +27,23 @@
 // counter in segment-major order, so a waiting segment's predecessors are
 // always claimed already.
 //
+// Wave roles.  Eight compute waves do every MFMA; four loader waves own the
+// HBM stream.  Vector memory operations of a wave complete in issue order, so
+// if the compute waves fetched X themselves, every wait for an L2-resident
+// operand issued after an X load would also wait out the HBM latency of that
+// load.  The loaders instead fetch the NEXT chunk's X while the current one
+// computes and prepare it; compute waves only issue L2-resident operand loads
+// and the y stores.  The two roles meet at two barriers per chunk (after the
+// state term, at the end).
+//
 // A chunk (TT tokens, padded to a multiple of 32) is handled as 32-token
-// blocks; wave b prepares block b of the NEXT chunk at the end of the current
-// one, so no wave waits on another while a chunk computes except at two
-// barriers (after the state term, at the end).  With GL the cumulative sum of
-// a_t inside its block (log2 units, <= 0) and every exponent formed <= 0
-// unless guarded:
-//   * prep: the block's X arrives straight from global memory into a double
-//     LDS buffer (global_load_lds_dwordx4), the wave scans GL, stores the
-//     per-token tables and the block decay Q = exp2(GL_end), and writes
-//     X~[t] = dt_t exp2(GL_end - GL_t) X[t] (a factor <= dt_t) to a second
-//     double buffer;
+// blocks.  With GL the cumulative sum of a_t inside its block (log2 units,
+// <= 0) and every exponent formed <= 0 unless guarded:
+//   * prep (loader waves, block by block): X arrives straight from global
+//     memory into a double LDS buffer (global_load_lds_dwordx4); the wave scans
+//     GL, stores the per-token tables and the block decay Q = exp2(GL_end),
+//     and writes X~[t] = dt_t exp2(GL_end - GL_t) X[t] (a factor <= dt_t) to a
+//     second double buffer;
 //   * one pass over the blocks does the state jump (wave = state tile) and the
 //     intra product of two 16-token output tiles per wave, paired (i, NIT-1-i)
 //     so every wave has the same causal work.  Both use the X~ fragments of
@@ -51,8 +57,11 @@
 //     per-token factors and one per-row scale are needed; stronger decay takes
 //     the element-wise form.
 //   * B^T comes ready-made from the CB pass; B^T, CB and C fragments are fetched
-//     a little ahead into small register rings; y leaves as 16-byte pieces
-//     assembled across lane rows with v_permlane16_swap.
+//     ahead into register rings.  Every ring slot is refilled at every block
+//     (the address, not the load, depends on the wave's causal extent), so no
+//     ring register is merged across branches, which would force the load to
+//     complete on the spot; y leaves as 16-byte pieces assembled across lane
+//     rows with v_permlane16_swap.
 #pragma once
 
 #include <type_traits>
@@ -62,8 +71,10 @@
 
 namespace cls {
 
-constexpr int kFuThreads = 512;
-constexpr int kFuWaves = kFuThreads / 64;
+constexpr int kFuCompute = 512;                              // compute threads (8 waves)
+constexpr int kFuWaves = kFuCompute / 64;                    // compute waves
+constexpr int kFuLoaders = 4;                                // loader waves
+constexpr int kFuThreads = kFuCompute + 64 * kFuLoaders;     // workgroup size
 constexpr int kFuP = 64;  // head dim of this kernel
 constexpr uint32_t kFuSpinLimit = 1u << 24;
 constexpr float kFuSplitMin = 7.8886091e-31f;  // 2^-100: weakest block decay of the split diagonal form
@@ -94,10 +105,8 @@ __device__ __forceinline__ void lds_barrier() {
 // 16 bytes per lane from global memory straight into LDS at lds_wave + 16 lane
 // (global_load_lds_dwordx4 with the wave-uniform LDS base in M0, which is
 // restored afterwards).  Issued from inline assembly so the compiler does not
-// make every later LDS read wait for it: readers wait with wait_vmcnt.  The
-// compiler's own waits for loads issued before or after it stay correct, as
-// vector memory operations complete in issue order (an unseen one only makes
-// them wait longer).
+// make every later LDS read wait for it; only loader waves issue it, and they
+// wait for it with wait_vmcnt before touching the data.
 __device__ __forceinline__ void load_to_lds(const void* src, unsigned char* lds_wave) {
     const uint32_t la = uint32_t(uintptr_t((__attribute__((address_space(3))) unsigned char*)lds_wave));
     uint32_t saved;
@@ -127,10 +136,34 @@ __device__ __forceinline__ void fu_static_switch(int v, F& f) {
     }
 }
 
+// f(std::integral_constant<int, k>) for k = K .. N - 1, in order.
+template <int K, int N, typename F>
+__device__ __forceinline__ void fu_static_for(F&& f) {
+    if constexpr (K < N) {
+        f(std::integral_constant<int, K>{});
+        fu_static_for<K + 1, N>(f);
+    }
+}
+
+// v from the lane N below inside its 16-lane row, 0 for the first N lanes of
+// the row (DPP row_shr).
+template <int N>
+__device__ __forceinline__ float fu_dpp_shr(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x110 + N, 0xf, 0xf,
+                                                                 false));
+}
+
+// lane 15 of each even row into every lane of the following row, 0 elsewhere
+// (DPP row_bcast:15 on rows 1 and 3).
+__device__ __forceinline__ float fu_dpp_bcast15(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x142, 0xa, 0xf,
+                                                                 false));
+}
+
 template <int TT, int S>
 struct FuLayout {
     static_assert(S == 64 || S == 128, "state size of the fused kernel");
-    static_assert(TT >= 32 && TT <= 256 && TT % 32 == 0, "tile tokens");
+    static_assert(TT >= 32 && TT <= 128 && TT % 32 == 0, "tile tokens");
     static constexpr int NST = S / 16;                    // state tiles (16 wide)
     static constexpr int NPW = (4 * NST) / kFuWaves;      // state head-dim tiles per wave
     static constexpr int NACC = NPW * 4;                  // state floats per lane
@@ -138,17 +171,23 @@ struct FuLayout {
     static constexpr int NPAIR = NIT / 2;                 // output tile pairs
     static constexpr int WPP = kFuWaves / NPAIR;          // waves per pair
     static constexpr int NPTW = WPP >= 4 ? 1 : 4 / WPP;   // output head-dim tiles per wave
-    static constexpr int NB = TT / 32;                    // 32-token blocks (wave b prepares block b)
-    static constexpr int XBYTES = TT * 128;               // one X buffer [TT][64] bf16
+    static constexpr int NB = TT / 32;                    // 32-token blocks
+    static constexpr int NBL = (NB + kFuLoaders - 1) / kFuLoaders;  // blocks per loader wave (<= 2)
+    static_assert(NBL <= 2, "a loader wave scans at most two blocks at once");
+    static constexpr int NCL = TT * S / 2048;             // 16-byte C loads per loader lane
+    static constexpr int CROWS = 512 / S;                 // C rows per 1 KB wave load
+    static constexpr int XBYTES = TT * 128;               // X buffer [TT][64] bf16
     static constexpr int HP = S + 8;                      // bf16 pitch of the state rows
+    static constexpr int CP = S + 8;                      // bf16 pitch of the C rows
     // per-chunk tables (floats): block-local cumulative decay GL, dt, the split
     // factors U = dt exp2(-GL) and VD = D exp2(-GL), and the block decays Q
     static constexpr int T_GL = 0, T_DT = TT, T_U = 2 * TT, T_VD = 3 * TT, T_Q = 4 * TT;
     static constexpr int TFLOATS = 4 * TT + 16;
     static constexpr int X_OFF = 0;                       // 2 x raw X [TT][64] bf16, swizzled
     static constexpr int XT_OFF = X_OFF + 2 * XBYTES;     // 2 x X~, same layout
-    static constexpr int H_OFF = XT_OFF + 2 * XBYTES;     // [64][HP] bf16
-    static constexpr int TB_OFF = H_OFF + kFuP * HP * 2;  // 2 x tables
+    static constexpr int H_OFF = XT_OFF + 2 * XBYTES;     // [64][HP] bf16 chunk-start state
+    static constexpr int C_OFF = H_OFF + kFuP * HP * 2;   // [TT][CP] bf16 C of the chunk
+    static constexpr int TB_OFF = C_OFF + TT * CP * 2;    // 2 x tables
     static constexpr int MISC_OFF = TB_OFF + 2 * TFLOATS * 4;  // ints [4]
     static constexpr int ALPHA_OFF = MISC_OFF + 64;            // look-back decays [64]
     static constexpr int BYTES = ALPHA_OFF + 64 * 4;
@@ -185,21 +224,23 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
     extern __shared__ __attribute__((aligned(16))) unsigned char sm[];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches and bases
+    const bool loader = wave >= kFuWaves;
+    const int lw = wave - kFuWaves;                               // loader index (loader waves)
     const int l16 = lane & 15, kg = lane >> 4;
     uint16_t* Hs = reinterpret_cast<uint16_t*>(sm + Lay::H_OFF);
+    unsigned char* Cs = sm + Lay::C_OFF;
     int* lb_int = reinterpret_cast<int*>(sm + Lay::MISC_OFF);
     float* lb_alpha = reinterpret_cast<float*>(sm + Lay::ALPHA_OFF);
-    auto tables = [&](int buf) { return reinterpret_cast<float*>(sm + Lay::TB_OFF) + buf * Lay::TFLOATS; };
 
     // state tile of this wave: s-tile st, head-dim tiles pt0 .. pt0 + NPW - 1
     const int st = wave % Lay::NST;
-    const int pt0 = (wave / Lay::NST) * NPW;
+    const int pt0 = ((wave % kFuWaves) / Lay::NST) * NPW;
     // output tiles of this wave: 16-token tiles itA, itB, head-dim tiles ptb ..
     const int pair = wave % Lay::NPAIR;
-    const int ptb = (wave / Lay::NPAIR) * NPTW;
+    const int ptb = ((wave % kFuWaves) / Lay::NPAIR) * NPTW;
     const bool has_out = ptb < 4;
     const int itA = pair, itB = Lay::NIT - 1 - pair;
-    const int jdA = itA >> 1, jdB = itB >> 1;
+    const int jdA_w = itA >> 1, jdB_w = itB >> 1;
 
     // ---- claim a segment (segment-major order) ----
     if (tid == 0) lb_int[0] = int(atomic_add_u32(p.claim, 1u));
@@ -229,7 +270,7 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
             dst[j] = v;
         }
     };
-    auto store_hs = [&]() {
+    auto store_hs = [&](int l16, int kg) {
 #pragma unroll
         for (int j = 0; j < NPW; ++j) {
             u32x2 w;
@@ -239,74 +280,151 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
         }
     };
 
-    // ---- per-chunk operand fetches ----
     auto chunk_rows = [&](int c) {
         const int64_t tok0 = int64_t(c) * p.chunk;
         return int((L - tok0 < p.chunk) ? (L - tok0) : p.chunk);
     };
-    // X rows of this wave's block of chunk c into raw buffer `buf` (waves < NB):
-    // 4 pieces of 8 rows; lane i of a piece fills LDS bytes 16 i .. 16 i + 15,
-    // so it loads the 16 bytes of the logical row and column that the swizzle
-    // places there.  Rows past the chunk load a real row of it (finite values;
-    // their weights are zero).
-    auto issue_x = [&](int c, int buf) {
-        const int64_t tok0 = int64_t(c) * p.chunk;
-        const int n = chunk_rows(c);
-        const char* base = reinterpret_cast<const char*>(p.x + ((b * L + tok0) * p.H + h) * kFuP);
-        unsigned char* xb = sm + Lay::X_OFF + buf * Lay::XBYTES;
+
+    // =======================================================================
+    // Loader waves.  Loader lw owns the 32-token block lw of every chunk (scan
+    // lane = row of the block); its X lanes hold 8-row pieces of the block.
+    // All loader loads are buffer loads whose range ends at the chunk's last
+    // real row, so rows past a ragged end read as zeros.  They prepare chunk
+    // c + 1 into the other half of the double-buffered X, X~ and tables while
+    // the compute waves work on chunk c.
+    // =======================================================================
+    static_assert(Lay::NBL == 1, "one block per loader wave");
+    const bool lblk = lw < NB;                       // this loader has a block
+    const int lrow = 32 * lw + 8 * 0 + (lane >> 3);  // row of X piece m = 0 (+ 8 m)
+    const uint32_t xrow_bytes = uint32_t(p.H * kFuP * 2);
+    const uint32_t kNoRow = 0x7ffffff0u;             // offset past any range: reads zeros
+    uint32_t xoff[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int piece = 4 * wave + m;
-            const int t = 8 * piece + (lane >> 3);
-            const int pc = lane & 7;                                    // 16-byte slot in the row
-            const int cc = (((pc >> 1) ^ (t & 3)) << 1) | (pc & 1);     // logical 16-byte column
-            const int tr = t < n ? t : n - 1;
-            load_to_lds(base + uint32_t(tr) * uint32_t(p.H * kFuP * 2) + uint32_t(cc * 16), xb + piece * 1024);
-        }
-    };
-    // dt of this wave's block of chunk c: lane l holds row 32 wave + l / 2
-    auto fetch_dt = [&](int c) {
+    for (int m = 0; m < 4; ++m)
+        xoff[m] = lblk ? uint32_t(lrow + 8 * m) * xrow_bytes + uint32_t((lane & 7) * 16) : kNoRow;
+    const uint32_t dtoff = (lblk && lane < 32) ? uint32_t(32 * lw + lane) * uint32_t(p.H * 4) : kNoRow;
+    uint32_t coff[Lay::NCL];
+#pragma unroll
+    for (int k = 0; k < Lay::NCL; ++k) {
+        const int r = Lay::CROWS * (kFuLoaders * k + lw) + lane / (S / 8);
+        coff[k] = uint32_t(r) * uint32_t(p.G * S * 2) + uint32_t((lane % (S / 8)) * 16);
+    }
+    u32x4 xreg[4];
+    u32x4 creg[Lay::NCL];
+    float dtv = 0.0f;
+    // X and dt of chunk c into registers
+    auto issue_x = [&](int c) {
         const int64_t tok0 = int64_t(c) * p.chunk;
         const int n = chunk_rows(c);
-        const int t = 32 * wave + (lane >> 1);
-        return t < n ? p.dt[(b * L + tok0 + t) * p.H + h] : 0.0f;
+        const auto rx = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(p.x + ((b * L + tok0) * p.H + h) * kFuP), 0, int(uint32_t(n) * xrow_bytes), 0x00020000);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) xreg[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, int(xoff[m]), 0, 0);
+        const auto rd = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.dt + (b * L + tok0) * p.H + h), 0,
+                                                          n * p.H * 4, 0x00020000);
+        dtv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, int(dtoff), 0, 0));
     };
-    // Block preparation (wave b < NB, block b of chunk c): GL scan, tables, X~.
-    auto prep = [&](float dtv, int buf) {
-        const int r = lane >> 1;                       // row in the block
-        const int t = 32 * wave + r;                   // row in the chunk
+    // GL scan, tables, raw X and X~ of the loader's block into buffers `buf`
+    auto prep = [&](int buf) {
+        float* T = reinterpret_cast<float*>(sm + Lay::TB_OFF) + buf * Lay::TFLOATS;
+        unsigned char* Xr = sm + Lay::X_OFF + buf * Lay::XBYTES;
+        unsigned char* Xt = sm + Lay::XT_OFF + buf * Lay::XBYTES;
+        const int t = 32 * lw + (lane & 31);
+        // inclusive scan over the 32 rows (lanes 0-31; lanes 32-63 carry zeros):
+        // row shifts inside 16-lane rows, then lane 15 of row 0 into row 1
         float v = A2 * dtv;
-#pragma unroll
-        for (int d = 2; d < 64; d <<= 1) {             // inclusive scan over rows (lane pairs)
-            const float o = __shfl_up(v, d, 64);
-            if (lane >= d) v += o;
-        }
-        const float gl = v;                            // GL_t <= 0
-        const float ge = __shfl(v, 63, 64);            // GL at the block end
-        const float cf = dtv * fexp2(ge - gl);         // X~ factor, <= dt
-        float* T = tables(buf);
-        if ((lane & 1) == 0) {
+        v += fu_dpp_shr<1>(v);
+        v += fu_dpp_shr<2>(v);
+        v += fu_dpp_shr<4>(v);
+        v += fu_dpp_shr<8>(v);
+        v += fu_dpp_bcast15(v);
+        const float gl = v;                                  // GL_t <= 0
+        const float ge = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+        const float cf = dtv * fexp2(ge - gl);               // X~ factor, <= dt
+        if (lblk && lane < 32) {
             const float e = fexp2(fminf(-gl, 126.0f));  // used only when the block decay is <= 2^100
             T[Lay::T_GL + t] = gl;
             T[Lay::T_DT + t] = dtv;
             T[Lay::T_U + t] = dtv * e;
             T[Lay::T_VD + t] = Dh * e;
+            if (lane == 0) T[Lay::T_Q + lw] = fexp2(ge);
         }
-        if (lane == 0) T[Lay::T_Q + wave] = fexp2(ge);
-        const unsigned char* xr = sm + Lay::X_OFF + buf * Lay::XBYTES;
-        unsigned char* xt = sm + Lay::XT_OFF + buf * Lay::XBYTES;
+        float f[4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const int cc = 4 * (lane & 1) + m;
-            const uint32_t off = x_off(t, cc >> 1, (cc & 1) * 16);
-            const u32x4 xv = *reinterpret_cast<const u32x4*>(xr + off);
-            u32x4 w;
+        for (int m = 0; m < 4; ++m) f[m] = __shfl(cf, 8 * m + (lane >> 3), 64);
+        if (lblk) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(bf16_lo(xv[e]) * cf, bf16_hi(xv[e]) * cf);
-            *reinterpret_cast<u32x4*>(xt + off) = w;
+            for (int m = 0; m < 4; ++m) {
+                const int tr = lrow + 8 * m;
+                const int cc = lane & 7;
+                const uint32_t off = x_off(tr, cc >> 1, (cc & 1) * 16);
+                const u32x4 xv = xreg[m];
+                u32x4 w;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t word = xv[e];
+                    w[e] = pack_bf16x2(bf16_lo(word) * f[m], bf16_hi(word) * f[m]);
+                }
+                *reinterpret_cast<u32x4*>(Xr + off) = xv;
+                *reinterpret_cast<u32x4*>(Xt + off) = w;
+            }
         }
     };
-    // operands shared by the heads of a group live per (b, chunk, g); lane offsets are 32-bit
+    // C of chunk c into registers, and from there into the LDS copy
+    auto issue_c = [&](int c) {
+        const int n = chunk_rows(c);
+        const auto rc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t*>(p.C + ((b * L + int64_t(c) * p.chunk) * p.G + g) * S), 0, n * p.G * S * 2,
+            0x00020000);
+#pragma unroll
+        for (int k = 0; k < Lay::NCL; ++k) creg[k] = __builtin_amdgcn_raw_buffer_load_b128(rc, int(coff[k]), 0, 0);
+    };
+    auto store_c = [&]() {
+#pragma unroll
+        for (int k = 0; k < Lay::NCL; ++k) {
+            const int r = Lay::CROWS * (kFuLoaders * k + lw) + lane / (S / 8);
+            *reinterpret_cast<u32x4*>(Cs + r * (Lay::CP * 2) + (lane % (S / 8)) * 16) = creg[k];
+        }
+    };
+    // The loader waves' share of a phase, with the same barriers as the compute
+    // waves.  Each register set is consumed before it is refilled, with the
+    // scheduler kept from hoisting the refill: a load issued while the old
+    // value is live would land in other registers and be copied back at the
+    // loop edge, which waits for the load to complete.  Loads are issued
+    // unconditionally (past the last chunk the last one is reloaded and
+    // prepared into the free buffer half) so no register is merged across
+    // branches.
+    auto run_loader = [&](auto out_tag) {
+        constexpr bool OUT = decltype(out_tag)::value;
+        if (c_begin >= c_end) return;
+        const int last = c_end - 1;
+        auto clampc = [&](int c) { return c <= last ? c : last; };
+        issue_x(c_begin);
+        if constexpr (OUT) issue_c(c_begin);
+        prep(c_begin & 1);
+        if constexpr (OUT) store_c();
+        __builtin_amdgcn_sched_barrier(0);
+        issue_x(clampc(c_begin + 1));
+        if constexpr (OUT) issue_c(clampc(c_begin + 1));
+        lds_barrier();
+        for (int c = c_begin; c < c_end; ++c) {
+            prep((c + 1) & 1);  // chunk c + 1 into the half chunk c - 1 used
+            __builtin_amdgcn_sched_barrier(0);
+            issue_x(clampc(c + 2));
+            lds_barrier();  // barrier 1: the compute waves have read C and H of chunk c
+            if constexpr (OUT) {
+                store_c();  // C of chunk c + 1
+                __builtin_amdgcn_sched_barrier(0);
+                issue_c(clampc(c + 2));
+            }
+            lds_barrier();  // barrier 2
+        }
+    };
+
+    // =======================================================================
+    // Compute waves: operands shared by the heads of a group live per
+    // (b, chunk, g); lane offsets are 32-bit.
+    // =======================================================================
     const int64_t bcg0 = b * p.nchunks * p.G + g;  // (b, chunk 0, g)
     auto cb_base = [&](int c) {
         return reinterpret_cast<const char*>(p.cb + (bcg0 + int64_t(c) * p.G) * (int64_t(TT) * TT));
@@ -317,24 +435,16 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
     const uint32_t bt_lane = uint32_t(((16 * st + l16) * TT + 8 * kg) * 2);
     const uint32_t cbA_lane = uint32_t(((16 * itA + l16) * TT + 8 * kg) * 2);
     const uint32_t cbB_lane = uint32_t(((16 * itB + l16) * TT + 8 * kg) * 2);
-    auto fetch_c = [&](int c, int it, u32x4 (&dst)[KS]) {
-        const int n = chunk_rows(c);
-        const int i = 16 * it + l16;
-        const int ir = i < n ? i : n - 1;  // rows past the sequence: any finite row (outputs not stored)
-        const char* base = reinterpret_cast<const char*>(p.C + ((b * L + int64_t(c) * p.chunk) * p.G + g) * S);
-        const uint32_t off = uint32_t(ir) * uint32_t(p.G * S * 2) + uint32_t(16 * kg);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) dst[ks] = ldg_b128(base + off + 64 * ks);
-    };
 
-    // Rings of kRing fragments (the block loop is unrolled, so slots are static
-    // registers): block k of a chunk sits in slot k % kRing.  When
-    // block k is consumed its slot is refilled with block k + kRing of the same
-    // chunk or, past the tile's last block jd, with block k % kRing of the next.
-    constexpr int kRing = 3;
-    u32x4 btr[kRing];              // B^T fragments (state product)
-    u32x4 rA[kRing], rB[kRing];    // CB fragments of the two output tiles
-    u32x4 cA[KS], cB[KS];          // C fragments of the two output tiles
+    // Operand rings (the block loop is unrolled, so slots are static registers):
+    // slot k holds block k of the current chunk.  When block k is consumed its
+    // slot is refilled, always, with block k of the next chunk (of the same
+    // chunk after the last one: a harmless reload), so every fragment is
+    // fetched a whole chunk ahead.  A slot beyond the wave's causal extent is
+    // reloaded every chunk and never read.
+    constexpr int RA = ((Lay::NPAIR - 1) >> 1) + 1;  // blocks tile A can reach
+    u32x4 btr[NB];                 // B^T fragments (state product)
+    u32x4 rA[RA], rB[NB];          // CB fragments of the two output tiles
     float sumG = 0.0f;
 
     auto run_chunks = [&](auto out_tag, auto pt0_c, auto ptb_c) {
@@ -342,53 +452,43 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
         constexpr int PT0 = decltype(pt0_c)::value * NPW;
         constexpr int PTB = decltype(ptb_c)::value * NPTW;
         if (c_begin >= c_end) return;
-        // prologue: the first chunk's blocks, then the operand rings
-        float dtn = 0.0f;
-        if (wave < NB) {
-            issue_x(c_begin, c_begin & 1);
-            dtn = fetch_dt(c_begin);
-        }
+        // prologue: the first chunk's operand rings (the loaders prepare its X and C)
 #pragma unroll
-        for (int k = 0; k < kRing; ++k)
-            if (k < NB) btr[k] = ldg_b128(bt_base(c_begin) + bt_lane + 64 * k);
+        for (int k = 0; k < NB; ++k) btr[k] = ldg_b128(bt_base(c_begin) + bt_lane + 64 * k);
         if (OUT && has_out) {
-            fetch_c(c_begin, itA, cA);
-            fetch_c(c_begin, itB, cB);
 #pragma unroll
-            for (int k = 0; k < kRing; ++k) {
-                if (k <= jdA) rA[k] = ldg_b128(cb_base(c_begin) + cbA_lane + 64 * k);
-                if (k <= jdB) rB[k] = ldg_b128(cb_base(c_begin) + cbB_lane + 64 * k);
-            }
-        }
-        if (wave < NB) {
-            wait_vmcnt<0>();
-            prep(dtn, c_begin & 1);
+            for (int k = 0; k < RA; ++k) rA[k] = ldg_b128(cb_base(c_begin) + cbA_lane + 64 * k);
+#pragma unroll
+            for (int k = 0; k < NB; ++k) rB[k] = ldg_b128(cb_base(c_begin) + cbB_lane + 64 * k);
         }
         lds_barrier();
 
         for (int c = c_begin; c < c_end; ++c) {
+            // Lane-dependent offsets are rebuilt every chunk from an opaque copy of
+            // the lane id: hoisted out of the chunk loop they would each hold a
+            // register for the whole loop.
+            int lane_c = lane;
+            asm volatile("" : "+v"(lane_c));
+            const int l16 = lane_c & 15, kg = lane_c >> 4;
+            // likewise the wave's causal extents, so the per-block branch
+            // conditions are formed where they are used
+            int jdA = jdA_w, jdB = jdB_w;
+            asm volatile("" : "+s"(jdA), "+s"(jdB));
+            const uint32_t bt_lane = uint32_t(((16 * st + l16) * TT + 8 * kg) * 2);
+            const uint32_t cbA_lane = uint32_t(((16 * itA + l16) * TT + 8 * kg) * 2);
+            const uint32_t cbB_lane = uint32_t(((16 * itB + l16) * TT + 8 * kg) * 2);
             const int64_t tok0 = int64_t(c) * p.chunk;
             const int n = chunk_rows(c);
-            const bool more = c + 1 < c_end;
-            const int cn = c + 1;
-            const int cur = c & 1, nxt = cur ^ 1;
-            const char* cbc = cb_base(c);
-            const char* cbn = cb_base(cn);
-            const char* btc = bt_base(c);
-            const char* btn = bt_base(cn);
-            const unsigned char* Xr = sm + Lay::X_OFF + cur * Lay::XBYTES;
-            const unsigned char* Xt = sm + Lay::XT_OFF + cur * Lay::XBYTES;
-            const float* T = tables(cur);
-            // next chunk's blocks: X straight into the other raw buffer (last read in
-            // the previous chunk), dt into a register
-            if (more && wave < NB) {
-                issue_x(cn, nxt);
-                dtn = fetch_dt(cn);
-            }
-#pragma unroll
-            for (int bb = 0; bb < NB; ++bb) sumG += T[Lay::T_GL + 32 * bb + 31];  // log2 decay of the chunk
+            const int cx = c + 1 < c_end ? c + 1 : c;  // operand source of the refills for the next chunk
+            // this chunk's half of the double-buffered X, X~ and tables
+            const unsigned char* Xr = sm + Lay::X_OFF + (c & 1) * Lay::XBYTES;
+            const unsigned char* Xt = sm + Lay::XT_OFF + (c & 1) * Lay::XBYTES;
+            const float* T = reinterpret_cast<const float*>(sm + Lay::TB_OFF) + (c & 1) * Lay::TFLOATS;
+            const char* cbx = cb_base(cx);
+            const char* btx = bt_base(cx);
 
             // S4 state term y^T += H C^T from the chunk-start state (bf16 in LDS)
+            // and the chunk's C (staged in LDS by the loaders)
             f32x4 accA[NPTW], accB[NPTW];
             if constexpr (OUT) {
 #pragma unroll
@@ -397,28 +497,31 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
                     accB[q] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
                 if (has_out) {
+                    const unsigned char* cra = Cs + (16 * itA + l16) * (Lay::CP * 2) + 16 * kg;
+                    const unsigned char* crb = Cs + (16 * itB + l16) * (Lay::CP * 2) + 16 * kg;
 #pragma unroll
                     for (int ks = 0; ks < KS; ++ks) {
+                        const u32x4 ca = *reinterpret_cast<const u32x4*>(cra + 64 * ks);
+                        const u32x4 cb = *reinterpret_cast<const u32x4*>(crb + 64 * ks);
 #pragma unroll
                         for (int q = 0; q < NPTW; ++q) {
                             const u32x4 hf = *reinterpret_cast<const u32x4*>(
                                 Hs + (16 * (PTB + q) + l16) * Lay::HP + 32 * ks + 8 * kg);
-                            accA[q] = fu_mfma(hf, cA[ks], accA[q]);
-                            accB[q] = fu_mfma(hf, cB[ks], accB[q]);
+                            accA[q] = fu_mfma(hf, ca, accA[q]);
+                            accB[q] = fu_mfma(hf, cb, accB[q]);
                         }
                     }
-                    if (more) {
-                        fetch_c(cn, itA, cA);
-                        fetch_c(cn, itB, cB);
-                    }
                 }
-                lds_barrier();  // every wave has read the chunk-start state
+            }
+            lds_barrier();  // barrier 1: X, X~, tables of chunk c ready; H and C of chunk c read
+            if constexpr (!OUT) {
+#pragma unroll
+                for (int bb = 0; bb < NB; ++bb) sumG += T[Lay::T_GL + 32 * bb + 31];  // log2 decay of the chunk
             }
 
             // one pass over the 32-token blocks: S2c/S3 state jump, S2b intra product
-#pragma unroll
-            for (int jb = 0; jb < NB; ++jb) {
-                const int slot = jb % kRing;
+            fu_static_for<0, NB>([&](auto jbc) {
+                constexpr int jb = decltype(jbc)::value;
                 const int trx = 32 * jb + 8 * kg + (l16 >> 2);
                 u32x4 xf[4];
                 fu_load_xf<0, PT0, NPW, PTB, NPTW, OUT>(xf, Xt, trx, l16);
@@ -426,15 +529,8 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
                 fu_load_xf<2, PT0, NPW, PTB, NPTW, OUT>(xf, Xt, trx, l16);
                 fu_load_xf<3, PT0, NPW, PTB, NPTW, OUT>(xf, Xt, trx, l16);
                 const float qv = T[Lay::T_Q + jb];
-                {
-                    const u32x4 braw = btr[slot];
-                    if (jb + kRing < NB)
-                        btr[slot] = ldg_b128(btc + bt_lane + 64 * (jb + kRing));
-                    else if (more)
-                        btr[slot] = ldg_b128(btn + bt_lane + 64 * slot);
 #pragma unroll
-                    for (int j = 0; j < NPW; ++j) hacc[j] = fu_mfma(braw, xf[PT0 + j], hacc[j] * qv);
-                }
+                for (int j = 0; j < NPW; ++j) hacc[j] = fu_mfma(btr[jb], xf[PT0 + j], hacc[j] * qv);
                 if constexpr (OUT) {
                     if (has_out) {
                         auto tile_block = [&](f32x4 (&acc)[NPTW], const u32x4 cw, int it, int jd) {
@@ -499,25 +595,23 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
                                 }
                             }
                         };
-                        if (jb <= jdA) {
-                            const u32x4 cw = rA[slot];
-                            if (jb + kRing <= jdA)
-                                rA[slot] = ldg_b128(cbc + cbA_lane + 64 * (jb + kRing));
-                            else if (more)
-                                rA[slot] = ldg_b128(cbn + cbA_lane + 64 * slot);
-                            tile_block(accA, cw, itA, jdA);
+                        if constexpr (jb < RA) {
+                            if (jb <= jdA) tile_block(accA, rA[jb], itA, jdA);
                         }
-                        if (jb <= jdB) {
-                            const u32x4 cw = rB[slot];
-                            if (jb + kRing <= jdB)
-                                rB[slot] = ldg_b128(cbc + cbB_lane + 64 * (jb + kRing));
-                            else if (more)
-                                rB[slot] = ldg_b128(cbn + cbB_lane + 64 * slot);
-                            tile_block(accB, cw, itB, jdB);
-                        }
+                        if (jb <= jdB) tile_block(accB, rB[jb], itB, jdB);
                     }
                 }
-            }
+                // refill the block's ring slots for the next chunk, after their last
+                // use in this one (see the loader loop for why the order matters)
+                __builtin_amdgcn_sched_barrier(0);
+                btr[jb] = ldg_b128(btx + bt_lane + 64 * jb);
+                if constexpr (OUT) {
+                    if (has_out) {
+                        if constexpr (jb < RA) rA[jb] = ldg_b128(cbx + cbA_lane + 64 * jb);
+                        rB[jb] = ldg_b128(cbx + cbB_lane + 64 * jb);
+                    }
+                }
+            });
 
             if constexpr (OUT) {
                 if (has_out) {
@@ -549,17 +643,17 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
                     store_y(accA, itA);
                     store_y(accB, itB);
                 }
-                store_hs();  // every wave is past the state term (barrier above)
+                store_hs(l16, kg);  // every wave has read the chunk-start state (barrier 1)
             }
-            if (more && wave < NB) {
-                wait_vmcnt<NB>();  // this wave's X pieces of the next chunk: the B^T refills came after them
-                prep(dtn, nxt);
-            }
-            lds_barrier();  // next chunk's X~ and tables are complete; this chunk's buffers are free
+            lds_barrier();  // barrier 2: X of chunk c and the state copy are free / complete
         }
     };
     // the wave's head-dim offsets become compile-time constants (static register indices)
     auto run_phase = [&](auto out_tag) {
+        if (loader) {
+            run_loader(out_tag);
+            return;
+        }
         auto with_pt0 = [&](auto pt0_c) {
             if constexpr (decltype(out_tag)::value) {
                 auto with_ptb = [&](auto ptb_c) { run_chunks(out_tag, pt0_c, ptb_c); };
@@ -577,17 +671,19 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
         for (int j = 0; j < NPW; ++j) hacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         run_phase(FuPhase<false>{});
         const float alpha_seg = fexp2(sumG);
-        float* pay = p.payload + int64_t(tile) * 2 * (kFuThreads * Lay::NACC);
+        float* pay = p.payload + int64_t(tile) * 2 * (kFuCompute * Lay::NACC);
         float* pay_agg = pay + tid * Lay::NACC;
-        float* pay_inc = pay + kFuThreads * Lay::NACC + tid * Lay::NACC;
+        float* pay_inc = pay + kFuCompute * Lay::NACC + tid * Lay::NACC;
         f32x4 hin[NPW];
         if (seg == 0) {
-            load_h0(hin);
+            if (!loader) load_h0(hin);
         } else {
-            // publish the aggregate
+            // publish the aggregate (alpha_seg is wave 0's, which is a compute wave)
+            if (!loader) {
 #pragma unroll
-            for (int j = 0; j < NPW; ++j) store_payload(pay_agg + 4 * j, hacc[j]);
-            wait_vmem();
+                for (int j = 0; j < NPW; ++j) store_payload(pay_agg + 4 * j, hacc[j]);
+                wait_vmem();
+            }
             __syncthreads();
             if (tid == 0) store_coherent_b128(p.status + tile, u32x4{1u, as_uint(alpha_seg), 0u, 0u});
             // look back: wave 0 inspects up to 64 predecessors
@@ -622,12 +718,12 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
             const int kp = __builtin_amdgcn_readfirstlane(lb_int[1]);
 #pragma unroll
             for (int j = 0; j < NPW; ++j) hin[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (kp >= 0) {
+            if (kp >= 0 && !loader) {
                 const int base_seg = seg - 1 - kp;
-                const int64_t tile_floats = 2 * (kFuThreads * Lay::NACC);
+                const int64_t tile_floats = 2 * (kFuCompute * Lay::NACC);
                 if (base_seg >= 0) {
                     const float* src = p.payload + (int64_t(base_seg) * p.nchains + chain) * tile_floats +
-                                       kFuThreads * Lay::NACC + tid * Lay::NACC;
+                                       kFuCompute * Lay::NACC + tid * Lay::NACC;
 #pragma unroll
                     for (int j = 0; j < NPW; ++j) hin[j] = load_payload(src + 4 * j);
                 } else {
@@ -643,21 +739,23 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
             }
         }
         // publish the inclusive state at the segment end
+        if (!loader) {
 #pragma unroll
-        for (int j = 0; j < NPW; ++j) {
-            store_payload(pay_inc + 4 * j, hin[j] * alpha_seg + hacc[j]);
-            hacc[j] = hin[j];
+            for (int j = 0; j < NPW; ++j) {
+                store_payload(pay_inc + 4 * j, hin[j] * alpha_seg + hacc[j]);
+                hacc[j] = hin[j];
+            }
+            wait_vmem();
         }
-        wait_vmem();
         __syncthreads();
         if (tid == 0) store_coherent_b128(p.status + tile, u32x4{2u, as_uint(alpha_seg), 0u, 0u});
     } else {
-        load_h0(hacc);
+        if (!loader) load_h0(hacc);
     }
-    store_hs();
+    if (!loader) store_hs(l16, kg);
     lds_barrier();
     run_phase(FuPhase<true>{});
-    if (p.h_final && seg == p.nsegs - 1) {
+    if (p.h_final && seg == p.nsegs - 1 && !loader) {
 #pragma unroll
         for (int j = 0; j < NPW; ++j)
             *reinterpret_cast<f32x4*>(p.h_final + (bh * kFuP + 16 * (pt0 + j) + l16) * S + 16 * st + 4 * kg) = hacc[j];

@@ -67,9 +67,11 @@ struct SsdFusedParams {
 };
 
 // Plan of the fused head-dim-64 path for one shape (also sizes its workspace).
+constexpr int64_t kFusedMaxChunk = 128;  // longest quadratic block of the fused kernel
+
 struct SsdFusedPlan {
     bool use;
-    int TT, nsegs, seg_chunks, nchains, ntiles;
+    int TT, chunk, nsegs, seg_chunks, nchains, ntiles;  // chunk: the sub-chunk the kernel runs
     size_t status_off, payload_off, cb_off, bt_off, bytes;
 };
 
