@@ -180,15 +180,22 @@ struct FuLayout {
     static constexpr int HP = S + 8;                      // bf16 pitch of the state rows
     static constexpr int CP = S + 8;                      // bf16 pitch of the C rows
     // per-chunk tables (floats): block-local cumulative decay GL, dt, the split
-    // factors U = dt exp2(-GL) and VD = D exp2(-GL), and the block decays Q
-    static constexpr int T_GL = 0, T_DT = TT, T_U = 2 * TT, T_VD = 3 * TT, T_Q = 4 * TT;
+    // factor U = dt exp2(-GL), the row factor R = exp2(GL), and the block decays Q
+    static constexpr int T_GL = 0, T_DT = TT, T_U = 2 * TT, T_R = 3 * TT, T_Q = 4 * TT;
     static constexpr int TFLOATS = 4 * TT + 16;
+    // decay-weighted causal weights of the diagonal 32 x 32 blocks (bf16 rows)
+    static constexpr int WP = 40;                         // bf16 pitch of a weight row
+    static constexpr int WBLK = 32 * WP * 2;              // bytes of one block's weights
+    static constexpr int WBYTES = NB * WBLK;              // one chunk's weights
+    static constexpr int RA = (NPAIR - 1) >> 1;           // off-diagonal blocks tile A can reach
+    static constexpr int RB = NB - 1;                     // off-diagonal blocks tile B can reach
     static constexpr int X_OFF = 0;                       // 2 x raw X [TT][64] bf16, swizzled
     static constexpr int XT_OFF = X_OFF + 2 * XBYTES;     // 2 x X~, same layout
     static constexpr int H_OFF = XT_OFF + 2 * XBYTES;     // [64][HP] bf16 chunk-start state
     static constexpr int C_OFF = H_OFF + kFuP * HP * 2;   // [TT][CP] bf16 C of the chunk
     static constexpr int TB_OFF = C_OFF + TT * CP * 2;    // 2 x tables
-    static constexpr int MISC_OFF = TB_OFF + 2 * TFLOATS * 4;  // ints [4]
+    static constexpr int W_OFF = TB_OFF + 2 * TFLOATS * 4;     // 2 x diagonal weights
+    static constexpr int MISC_OFF = W_OFF + 2 * WBYTES;        // ints [4]
     static constexpr int ALPHA_OFF = MISC_OFF + 64;            // look-back decays [64]
     static constexpr int BYTES = ALPHA_OFF + 64 * 4;
 };
@@ -294,10 +301,17 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
     // the compute waves work on chunk c.
     // =======================================================================
     static_assert(Lay::NBL == 1, "one block per loader wave");
+    const int64_t bcg0 = b * p.nchunks * p.G + g;    // (b, chunk 0, g) of the operands shared by a group
+    auto cb_base = [&](int c) {
+        return reinterpret_cast<const char*>(p.cb + (bcg0 + int64_t(c) * p.G) * (int64_t(TT) * TT));
+    };
+
     const bool lblk = lw < NB;                       // this loader has a block
     const int lrow = 32 * lw + 8 * 0 + (lane >> 3);  // row of X piece m = 0 (+ 8 m)
     const uint32_t xrow_bytes = uint32_t(p.H * kFuP * 2);
     const uint32_t kNoRow = 0x7ffffff0u;             // offset past any range: reads zeros
+    // diagonal C B^T block of the loader's block: row lane / 2, 16 columns
+    const uint32_t cboff = lblk ? uint32_t(((32 * lw + (lane >> 1)) * TT + 32 * lw + 16 * (lane & 1)) * 2) : kNoRow;
     uint32_t xoff[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -310,6 +324,7 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
         coff[k] = uint32_t(r) * uint32_t(p.G * S * 2) + uint32_t((lane % (S / 8)) * 16);
     }
     u32x4 xreg[4];
+    u32x4 dreg[2];
     u32x4 creg[Lay::NCL];
     float dtv = 0.0f;
     // X and dt of chunk c into registers
@@ -323,8 +338,12 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
         const auto rd = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.dt + (b * L + tok0) * p.H + h), 0,
                                                           n * p.H * 4, 0x00020000);
         dtv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, int(dtoff), 0, 0));
+        const auto rcb = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(cb_base(c)), 0, TT * TT * 2, 0x00020000);
+        dreg[0] = __builtin_amdgcn_raw_buffer_load_b128(rcb, int(cboff), 0, 0);
+        dreg[1] = __builtin_amdgcn_raw_buffer_load_b128(rcb, int(cboff + 16), 0, 0);
     };
     // GL scan, tables, raw X and X~ of the loader's block into buffers `buf`
+    float lgl = 0.0f, lge = 0.0f;  // the scan's GL (lanes < 32) and block-end GL, for the weights
     auto prep = [&](int buf) {
         float* T = reinterpret_cast<float*>(sm + Lay::TB_OFF) + buf * Lay::TFLOATS;
         unsigned char* Xr = sm + Lay::X_OFF + buf * Lay::XBYTES;
@@ -340,13 +359,15 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
         v += fu_dpp_bcast15(v);
         const float gl = v;                                  // GL_t <= 0
         const float ge = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31));
+        lgl = gl;
+        lge = ge;
         const float cf = dtv * fexp2(ge - gl);               // X~ factor, <= dt
         if (lblk && lane < 32) {
             const float e = fexp2(fminf(-gl, 126.0f));  // used only when the block decay is <= 2^100
             T[Lay::T_GL + t] = gl;
             T[Lay::T_DT + t] = dtv;
             T[Lay::T_U + t] = dtv * e;
-            T[Lay::T_VD + t] = Dh * e;
+            T[Lay::T_R + t] = fexp2(gl);
             if (lane == 0) T[Lay::T_Q + lw] = fexp2(ge);
         }
         float f[4];
@@ -368,6 +389,54 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
                 *reinterpret_cast<u32x4*>(Xr + off) = xv;
                 *reinterpret_cast<u32x4*>(Xt + off) = w;
             }
+        }
+    };
+    auto prep_w = [&](int buf) {
+        const float* T = reinterpret_cast<const float*>(sm + Lay::TB_OFF) + buf * Lay::TFLOATS;
+        const float gl = lgl, ge = lge;
+        // Diagonal-block weights W[r][j] = CB[r][j] dt_j exp2(GL_r - GL_j) for j <= r,
+        // plus D on j = r (the skip term), rounded to bf16: lane holds row r = lane / 2,
+        // columns 16 (lane & 1) + e.  Split as CB U_j R_r (bounded factors) unless the
+        // block decays by more than 2^-100, where the exponent is formed per element.
+        if (lblk) {
+            unsigned char* Wb = sm + Lay::W_OFF + buf * Lay::WBYTES + lw * Lay::WBLK;
+            const int r = lane >> 1, c0 = 16 * (lane & 1);
+            const float gr = __shfl(gl, r, 64);
+            float cbv[16];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                cbv[e] = (e & 1) ? bf16_hi(dreg[0][e >> 1]) : bf16_lo(dreg[0][e >> 1]);
+                cbv[8 + e] = (e & 1) ? bf16_hi(dreg[1][e >> 1]) : bf16_lo(dreg[1][e >> 1]);
+            }
+            const float* Tb = T + 32 * lw + c0;
+            float w[16];
+            if (fexp2(ge) >= kFuSplitMin) {
+                const float rr = fexp2(gr);
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const f32x4 u = *reinterpret_cast<const f32x4*>(Tb + Lay::T_U + 4 * e4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[4 * e4 + e] = cbv[4 * e4 + e] * u[e] * rr;
+                }
+            } else {
+#pragma unroll
+                for (int e4 = 0; e4 < 4; ++e4) {
+                    const f32x4 gj = *reinterpret_cast<const f32x4*>(Tb + Lay::T_GL + 4 * e4);
+                    const f32x4 dj = *reinterpret_cast<const f32x4*>(Tb + Lay::T_DT + 4 * e4);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) w[4 * e4 + e] = cbv[4 * e4 + e] * dj[e] * fexp2(fminf(gr - gj[e], 0.0f));
+                }
+            }
+            u32x4 o[2];
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int j = c0 + e;
+                w[e] = (j < r) ? w[e] : (j == r ? w[e] + Dh : 0.0f);
+            }
+#pragma unroll
+            for (int e = 0; e < 8; ++e) o[e >> 2][e & 3] = pack_bf16x2(w[2 * e], w[2 * e + 1]);
+            *reinterpret_cast<u32x4*>(Wb + r * (Lay::WP * 2) + c0 * 2) = o[0];
+            *reinterpret_cast<u32x4*>(Wb + r * (Lay::WP * 2) + c0 * 2 + 16) = o[1];
         }
     };
     // C of chunk c into registers, and from there into the LDS copy
@@ -402,21 +471,23 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
         issue_x(c_begin);
         if constexpr (OUT) issue_c(c_begin);
         prep(c_begin & 1);
+        prep_w(c_begin & 1);
         if constexpr (OUT) store_c();
         __builtin_amdgcn_sched_barrier(0);
         issue_x(clampc(c_begin + 1));
         if constexpr (OUT) issue_c(clampc(c_begin + 1));
         lds_barrier();
         for (int c = c_begin; c < c_end; ++c) {
-            prep((c + 1) & 1);  // chunk c + 1 into the half chunk c - 1 used
+            // chunk c + 1 into the half chunk c - 1 used: scan, tables and X~ while
+            // the compute waves form the state term, the weights and the C copy
+            // while they run the block loop
+            prep((c + 1) & 1);
+            lds_barrier();  // barrier 1: the compute waves have read C and H of chunk c
+            prep_w((c + 1) & 1);
+            if constexpr (OUT) store_c();  // C of chunk c + 1
             __builtin_amdgcn_sched_barrier(0);
             issue_x(clampc(c + 2));
-            lds_barrier();  // barrier 1: the compute waves have read C and H of chunk c
-            if constexpr (OUT) {
-                store_c();  // C of chunk c + 1
-                __builtin_amdgcn_sched_barrier(0);
-                issue_c(clampc(c + 2));
-            }
+            if constexpr (OUT) issue_c(clampc(c + 2));
             lds_barrier();  // barrier 2
         }
     };
@@ -425,10 +496,6 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
     // Compute waves: operands shared by the heads of a group live per
     // (b, chunk, g); lane offsets are 32-bit.
     // =======================================================================
-    const int64_t bcg0 = b * p.nchunks * p.G + g;  // (b, chunk 0, g)
-    auto cb_base = [&](int c) {
-        return reinterpret_cast<const char*>(p.cb + (bcg0 + int64_t(c) * p.G) * (int64_t(TT) * TT));
-    };
     auto bt_base = [&](int c) {
         return reinterpret_cast<const char*>(p.bt + (bcg0 + int64_t(c) * p.G) * (int64_t(S) * TT));
     };
@@ -442,9 +509,9 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
     // chunk after the last one: a harmless reload), so every fragment is
     // fetched a whole chunk ahead.  A slot beyond the wave's causal extent is
     // reloaded every chunk and never read.
-    constexpr int RA = ((Lay::NPAIR - 1) >> 1) + 1;  // blocks tile A can reach
-    u32x4 btr[NB];                 // B^T fragments (state product)
-    u32x4 rA[RA], rB[NB];          // CB fragments of the two output tiles
+    constexpr int RA = Lay::RA, RB = Lay::RB;
+    u32x4 btr[NB];                                  // B^T fragments (state product)
+    u32x4 rA[RA > 0 ? RA : 1], rB[RB > 0 ? RB : 1];  // off-diagonal CB fragments of the output tiles
     float sumG = 0.0f;
 
     auto run_chunks = [&](auto out_tag, auto pt0_c, auto ptb_c) {
@@ -459,7 +526,7 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
 #pragma unroll
             for (int k = 0; k < RA; ++k) rA[k] = ldg_b128(cb_base(c_begin) + cbA_lane + 64 * k);
 #pragma unroll
-            for (int k = 0; k < NB; ++k) rB[k] = ldg_b128(cb_base(c_begin) + cbB_lane + 64 * k);
+            for (int k = 0; k < RB; ++k) rB[k] = ldg_b128(cb_base(c_begin) + cbB_lane + 64 * k);
         }
         lds_barrier();
 
@@ -484,6 +551,7 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
             const unsigned char* Xr = sm + Lay::X_OFF + (c & 1) * Lay::XBYTES;
             const unsigned char* Xt = sm + Lay::XT_OFF + (c & 1) * Lay::XBYTES;
             const float* T = reinterpret_cast<const float*>(sm + Lay::TB_OFF) + (c & 1) * Lay::TFLOATS;
+            const unsigned char* Wb = sm + Lay::W_OFF + (c & 1) * Lay::WBYTES;
             const char* cbx = cb_base(cx);
             const char* btx = bt_base(cx);
 
@@ -520,85 +588,52 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
             }
 
             // one pass over the 32-token blocks: S2c/S3 state jump, S2b intra product
+            // X~ fragments are read one block ahead, so their LDS latency overlaps
+            // the previous block's products
+            auto load_xf = [&](u32x4 (&dst)[4], int trx) {
+                fu_load_xf<0, PT0, NPW, PTB, NPTW, OUT>(dst, Xt, trx, l16);
+                fu_load_xf<1, PT0, NPW, PTB, NPTW, OUT>(dst, Xt, trx, l16);
+                fu_load_xf<2, PT0, NPW, PTB, NPTW, OUT>(dst, Xt, trx, l16);
+                fu_load_xf<3, PT0, NPW, PTB, NPTW, OUT>(dst, Xt, trx, l16);
+            };
+            u32x4 xf[4], xfn[4];
+            load_xf(xf, 8 * kg + (l16 >> 2));
             fu_static_for<0, NB>([&](auto jbc) {
                 constexpr int jb = decltype(jbc)::value;
                 const int trx = 32 * jb + 8 * kg + (l16 >> 2);
-                u32x4 xf[4];
-                fu_load_xf<0, PT0, NPW, PTB, NPTW, OUT>(xf, Xt, trx, l16);
-                fu_load_xf<1, PT0, NPW, PTB, NPTW, OUT>(xf, Xt, trx, l16);
-                fu_load_xf<2, PT0, NPW, PTB, NPTW, OUT>(xf, Xt, trx, l16);
-                fu_load_xf<3, PT0, NPW, PTB, NPTW, OUT>(xf, Xt, trx, l16);
+                if constexpr (jb + 1 < NB) load_xf(xfn, trx + 32);
                 const float qv = T[Lay::T_Q + jb];
 #pragma unroll
                 for (int j = 0; j < NPW; ++j) hacc[j] = fu_mfma(btr[jb], xf[PT0 + j], hacc[j] * qv);
                 if constexpr (OUT) {
                     if (has_out) {
-                        auto tile_block = [&](f32x4 (&acc)[NPTW], const u32x4 cw, int it, int jd) {
-                            if (jb < jd) {
+                        // off-diagonal block: the accumulator moves to this block's end
+                        auto tile_off = [&](f32x4 (&acc)[NPTW], const u32x4 cw) {
 #pragma unroll
-                                for (int q = 0; q < NPTW; ++q) acc[q] = fu_mfma(xf[PTB + q], cw, acc[q] * qv);
-                                return;
-                            }
-                            // jb == jd: diagonal block on raw X.  The accumulator holds the
-                            // contributions up to the previous block end; row i is exp2(GL_i)
-                            // further on.
+                            for (int q = 0; q < NPTW; ++q) acc[q] = fu_mfma(xf[PTB + q], cw, acc[q] * qv);
+                        };
+                        // diagonal block on raw X with the loaders' weights: the accumulator
+                        // holds the contributions up to the block start, row i is exp2(GL_i)
+                        // further on
+                        auto tile_diag = [&](f32x4 (&acc)[NPTW], int it) {
                             const int i = 16 * it + l16;
-                            const int il = i & 31;                 // row in the block
-                            const float gi = T[Lay::T_GL + i];
-                            const float ri = fexp2(gi);
-                            const int j0 = 32 * jd + 8 * kg;
-                            // causal position of the lane's first column: element e is kept
-                            // when e <= kd and is the diagonal when e == kd (kept opaque so
-                            // the per-element lane masks are not held across chunks)
-                            int kd = il - 8 * kg;
-                            asm volatile("" : "+v"(kd));
-                            u32x4 wf;
-                            if (qv >= kFuSplitMin) {
-                                // split form: CB dt_j exp2(-GL_j) (+ D exp2(-GL_i) on j = i), then ri
-                                const f32x4 u0 = *reinterpret_cast<const f32x4*>(T + Lay::T_U + j0);
-                                const f32x4 u1 = *reinterpret_cast<const f32x4*>(T + Lay::T_U + j0 + 4);
-                                const float vd = T[Lay::T_VD + i];
-                                float wv[8];
+                            const float ri = T[Lay::T_R + i];
+                            const u32x4 wf = *reinterpret_cast<const u32x4*>(
+                                Wb + jb * Lay::WBLK + (i & 31) * (Lay::WP * 2) + 16 * kg);
 #pragma unroll
-                                for (int e = 0; e < 8; ++e) {
-                                    const uint32_t word = cw[e >> 1];
-                                    const float cbv = (e & 1) ? bf16_hi(word) : bf16_lo(word);
-                                    const float u = e < 4 ? u0[e] : u1[e - 4];
-                                    float w = (e <= kd) ? cbv * u : 0.0f;
-                                    wv[e] = (e == kd) ? w + vd : w;
-                                }
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) wf[e] = pack_bf16x2(wv[2 * e], wv[2 * e + 1]);
-#pragma unroll
-                                for (int q = 0; q < NPTW; ++q) {
-                                    const uint32_t o1 = x_off(trx, PTB + q, 8 * (l16 & 3));
-                                    acc[q] = fu_mfma(lds_tr_pair(Xr, o1, o1 + 512), wf, acc[q]) * ri;
-                                }
-                            } else {
-                                // element-wise form
-                                float wv[8];
-#pragma unroll
-                                for (int e = 0; e < 8; ++e) {
-                                    const uint32_t word = cw[e >> 1];
-                                    const float cbv = (e & 1) ? bf16_hi(word) : bf16_lo(word);
-                                    const int j = j0 + e;
-                                    float w = cbv * fexp2(gi - T[Lay::T_GL + j]) * T[Lay::T_DT + j];
-                                    w = (e <= kd) ? w : 0.0f;
-                                    wv[e] = (e == kd) ? w + Dh : w;
-                                }
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) wf[e] = pack_bf16x2(wv[2 * e], wv[2 * e + 1]);
-#pragma unroll
-                                for (int q = 0; q < NPTW; ++q) {
-                                    const uint32_t o1 = x_off(trx, PTB + q, 8 * (l16 & 3));
-                                    acc[q] = fu_mfma(lds_tr_pair(Xr, o1, o1 + 512), wf, acc[q] * ri);
-                                }
+                            for (int q = 0; q < NPTW; ++q) {
+                                const uint32_t o1 = x_off(trx, PTB + q, 8 * (l16 & 3));
+                                acc[q] = fu_mfma(lds_tr_pair(Xr, o1, o1 + 512), wf, acc[q] * ri);
                             }
                         };
                         if constexpr (jb < RA) {
-                            if (jb <= jdA) tile_block(accA, rA[jb], itA, jdA);
+                            if (jb < jdA) tile_off(accA, rA[jb]);
                         }
-                        if (jb <= jdB) tile_block(accB, rB[jb], itB, jdB);
+                        if (jb == jdA) tile_diag(accA, itA);
+                        if constexpr (jb < RB) {
+                            if (jb < jdB) tile_off(accB, rB[jb]);
+                        }
+                        if (jb == jdB) tile_diag(accB, itB);
                     }
                 }
                 // refill the block's ring slots for the next chunk, after their last
@@ -608,8 +643,12 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
                 if constexpr (OUT) {
                     if (has_out) {
                         if constexpr (jb < RA) rA[jb] = ldg_b128(cbx + cbA_lane + 64 * jb);
-                        rB[jb] = ldg_b128(cbx + cbB_lane + 64 * jb);
+                        if constexpr (jb < RB) rB[jb] = ldg_b128(cbx + cbB_lane + 64 * jb);
                     }
+                }
+                if constexpr (jb + 1 < NB) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) xf[q] = xfn[q];
                 }
             });
 
@@ -651,7 +690,13 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
     // the wave's head-dim offsets become compile-time constants (static register indices)
     auto run_phase = [&](auto out_tag) {
         if (loader) {
+            // The loaders' work is short but on the path of every chunk: without a
+            // higher issue priority the older compute waves sharing their SIMD win
+            // every arbitration and the loaders' loads and arithmetic wait for
+            // the compute waves' block loop to drain.
+            __builtin_amdgcn_s_setprio(3);
             run_loader(out_tag);
+            __builtin_amdgcn_s_setprio(0);
             return;
         }
         auto with_pt0 = [&](auto pt0_c) {
