@@ -200,9 +200,12 @@ struct FuLayout {
     static constexpr int BYTES = ALPHA_OFF + 64 * 4;
 };
 
-// byte offset of (row t, 32-byte pair `pair`, byte `within` < 32) in X or X~
+// byte offset of (row t, 32-byte pair `pair`, byte `within` < 32) in X or X~.
+// The pair is swizzled by rows t & 3 and t >> 3 & 3, so the 16 rows a
+// transposed read touches (t = 8 kg + 0..3) fall on distinct 32-byte bank
+// groups of the two row halves.
 __device__ __forceinline__ uint32_t x_off(int t, int pair, int within) {
-    return uint32_t(t * 128 + ((pair ^ (t & 3)) << 5) + within);
+    return uint32_t(t * 128 + ((pair ^ (t & 3) ^ ((t >> 3) & 3)) << 5) + within);
 }
 
 // X~ fragment of head-dim tile PT for this wave, when the state (tiles PT0 ..)
