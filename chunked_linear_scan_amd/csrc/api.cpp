@@ -42,7 +42,7 @@ ScanPlan plan_scan(int64_t rows, int64_t L) {
         p.claim_off = kHeader;
         p.done_off = p.claim_off + round_up(size_t(rows) * 4, 256);
         p.status_off = p.done_off + round_up(size_t(rows) * 4, 256);
-        p.bytes = p.status_off + size_t(rows) * size_t(p.tiles_per_row) * 32;
+        p.bytes = p.status_off + size_t(rows) * size_t(p.tiles_per_row) * 16;
     }
     return p;
 }

@@ -84,14 +84,53 @@ __device__ __forceinline__ void store4(float* __restrict__ p, int64_t i, int64_t
     }
 }
 
-// Status word: {1, alpha, beta, 0}; all-zero means not yet published.
-__device__ __forceinline__ u32x4 pack_status(Pair v) {
-    return u32x4{1u, as_uint(v.a), as_uint(v.b), 0u};
+// Status word of a tile: {kind, alpha, beta, 0} with kind 1 for the tile's own
+// aggregate and 2 for its inclusive prefix, which later overwrites the
+// aggregate in place; all-zero means not yet published.  A reader sees one or
+// the other whole, as the word is written and read as one 16-byte access.
+__device__ __forceinline__ u32x4 pack_status(uint32_t kind, Pair v) {
+    return u32x4{kind, as_uint(v.a), as_uint(v.b), 0u};
+}
+
+// DPP move of a float / int: lanes whose source lies outside the pattern (or
+// whose row is not in ROWMASK) keep `old`.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old),
+                                                                 __builtin_bit_cast(int, v), CTRL, ROWMASK, 0xf,
+                                                                 false));
+}
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWMASK, 0xf, false);
+}
+
+// One step of the 64-lane inclusive scan: combine with the value a DPP pattern
+// brings from a lower lane (the identity where there is none).
+template <int CTRL, int ROWMASK, bool SEG>
+__device__ __forceinline__ Pair scan_step(Pair w) {
+    const Pair o{dpp_f<CTRL, ROWMASK>(1.0f, w.a), dpp_f<CTRL, ROWMASK>(0.0f, w.b),
+                 SEG ? dpp_i<CTRL, ROWMASK>(0, w.f) : 0};
+    return combine(o, w);
+}
+
+// Inclusive scan over the 64 lanes of a wave in lane order: row shifts by 1, 2,
+// 4, 8 inside each 16-lane row, then lane 15 of rows 0 and 2 into rows 1 and 3,
+// then lane 31 into rows 2 and 3 (the gfx9 DPP row broadcasts).
+template <bool SEG>
+__device__ __forceinline__ Pair wave_inclusive_scan(Pair w) {
+    w = scan_step<0x111, 0xf, SEG>(w);
+    w = scan_step<0x112, 0xf, SEG>(w);
+    w = scan_step<0x114, 0xf, SEG>(w);
+    w = scan_step<0x118, 0xf, SEG>(w);
+    w = scan_step<0x142, 0xa, SEG>(w);
+    w = scan_step<0x143, 0xc, SEG>(w);
+    return w;
 }
 
 // Exclusive prefix of tile j of a row: the ordered combination of tiles
 // 0..j-1.  Runs on one full wave; every lane returns the same value.
-// status_row holds [tile][2] 16-byte words: [0] aggregate, [1] inclusive.
+// status_row holds one 16-byte status word per tile.
 __device__ Pair lookback(const u32x4* status_row, int j, uint32_t* err) {
     const int lane = lane_id();
     Pair acc{1.0f, 0.0f, 0};  // combination of the predecessors already folded
@@ -104,17 +143,10 @@ __device__ Pair lookback(const u32x4* status_row, int j, uint32_t* err) {
         if (p < 0) {
             kind = 2;  // before the row start the state is 0: identity prefix
         } else {
-            const u32x4 inc = load_coherent_b128(status_row + 2 * p + 1);
-            if (inc[0]) {
-                kind = 2;
-                v.a = as_float(inc[1]);
-                v.b = as_float(inc[2]);
-            } else {
-                const u32x4 ag = load_coherent_b128(status_row + 2 * p);
-                kind = ag[0] ? 1 : 0;
-                v.a = as_float(ag[1]);
-                v.b = as_float(ag[2]);
-            }
+            const u32x4 w = load_coherent_b128(status_row + p);
+            kind = int(w[0]);
+            v.a = as_float(w[1]);
+            v.b = as_float(w[2]);
         }
         const uint64_t incm = __ballot(kind == 2);
         const uint64_t notready = __ballot(kind == 0);
@@ -229,15 +261,13 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
 #pragma unroll
     for (int q = 0; q < kLsSteps; ++q) {
         Pair w{av[q][3], bv[q][3], int((rmask >> (4 * q + 3)) & 1u)};
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            Pair o{shfl_up(w.a, d), shfl_up(w.b, d), SEGMENTED ? shfl_up_i(w.f, d) : 0};
-            if (lane >= d) w = combine(o, w);
-        }
+        w = wave_inclusive_scan<SEGMENTED>(w);
         Pair ex{shfl_up(w.a, 1), shfl_up(w.b, 1), SEGMENTED ? shfl_up_i(w.f, 1) : 0};
         if (lane == 0) ex = Pair{1.0f, 0.0f, 0};
         pre[q] = combine(carry, ex);
-        const Pair tot{__shfl(w.a, 63, 64), __shfl(w.b, 63, 64), SEGMENTED ? __shfl(w.f, 63, 64) : 0};
+        const Pair tot{__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w.a), 63)),
+                       __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w.b), 63)),
+                       SEGMENTED ? __builtin_amdgcn_readlane(w.f, 63) : 0};
         carry = combine(carry, tot);
     }
     if (lane == 0) {
@@ -256,16 +286,16 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
     }
 
     // LS3: publish the aggregate, look back, publish the inclusive prefix.
-    u32x4* srow = status + row * int64_t(tiles_per_row) * 2;
+    u32x4* srow = status + row * int64_t(tiles_per_row);
     if (!SEGMENTED) {
         if (wave == 0) {
             Pair prefix{1.0f, 0.0f, 0};
             if (!empty_tile) {
                 if (j > 0) {
-                    if (lane == 0) store_coherent_b128(srow + 2 * j, pack_status(tile_agg));
+                    if (lane == 0) store_coherent_b128(srow + j, pack_status(1u, tile_agg));
                     prefix = lookback(srow, j, err);
                 }
-                if (lane == 0) store_coherent_b128(srow + 2 * j + 1, pack_status(combine(prefix, tile_agg)));
+                if (lane == 0) store_coherent_b128(srow + j, pack_status(2u, combine(prefix, tile_agg)));
             }
             if (lane == 0) {
                 s_pa = prefix.a;
@@ -301,7 +331,7 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
         if (lane == 0) last = (atomic_add_u32(&done[row], 1u) == uint32_t(tiles_per_row - 1)) ? 1u : 0u;
         last = __builtin_amdgcn_readfirstlane(last);
         if (last) {
-            for (int q = lane; q < 2 * tiles_per_row; q += 64) store_coherent_b128(srow + q, u32x4{0u, 0u, 0u, 0u});
+            for (int q = lane; q < tiles_per_row; q += 64) store_coherent_b128(srow + q, u32x4{0u, 0u, 0u, 0u});
             if (lane == 0) {
                 store_coherent_u32(&claim[row], 0u);
                 store_coherent_u32(&done[row], 0u);
