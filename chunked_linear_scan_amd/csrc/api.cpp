@@ -11,7 +11,7 @@
 
 namespace {
 
-constexpr int64_t kLsTile = 4096;  // elements per linear-scan tile
+constexpr int64_t kLsTile = 8192;  // elements per linear-scan tile (linear_scan.hip)
 constexpr size_t kHeader = 256;    // bytes: error word and padding
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

@@ -7,12 +7,12 @@
 // in registers) follows its section "The five kernels" (levels 3b and 3c).
 //
 // MI355X choices:
-//   * a tile is 4 waves x 1024 elements; each wave owns a contiguous run and
+//   * a tile is 4 waves x 2048 elements; each wave owns a contiguous run and
 //     loads it as 16-byte vectors with lanes 16 bytes apart, so every
 //     wave-wide load covers 1 KB of consecutive memory; a 16-byte aligned
 //     window makes rows that start misaligned (ragged lengths) use the same
 //     vector loads; positions outside the row are the identity (a = 1, b = 0);
-//   * the in-tile scan is a 4-item serial scan per lane, a 64-lane wave scan
+//   * the in-tile scan is a 4-item serial scan per lane, a 64-lane DPP wave scan
 //     per 256-element step with the step carry kept wave-uniform, and a
 //     4-wave combine through LDS;
 //   * one 64-lane wave inspects 64 predecessors per look-back step and folds
@@ -37,9 +37,9 @@ namespace cls {
 
 constexpr int kLsThreads = 256;
 constexpr int kLsWaves = kLsThreads / 64;
-constexpr int kLsSteps = 4;                      // 256-element steps per wave
-constexpr int kLsWaveRun = kLsSteps * 256;       // 1024 elements per wave
-constexpr int kLsTile = kLsWaves * kLsWaveRun;   // 4096 elements per tile
+constexpr int kLsSteps = 8;                      // 256-element steps per wave
+constexpr int kLsWaveRun = kLsSteps * 256;       // 2048 elements per wave
+constexpr int kLsTile = kLsWaves * kLsWaveRun;   // 8192 elements per tile
 // Each look-back poll sleeps ~64 clocks; 2^24 polls is several seconds, far
 // beyond any legitimate wait, so a corrupted workspace ends the kernel instead
 // of hanging it (the error word is raised and the tile treats the missing

@@ -66,7 +66,7 @@ def test_linear_scan_workspace_size_is_monotone_and_row_scaled():
     long384 = lib.linear_scan_workspace_size(384, 65536)
     assert short > 0 and long1 > 0
     assert long384 > long1
-    assert long384 >= 384 * 16 * 16  # one 16-byte status word per tile
+    assert long384 >= 384 * 8 * 16  # one 16-byte status word per 8192-element tile
 
 
 def test_ssd_rejects_bad_arguments():
