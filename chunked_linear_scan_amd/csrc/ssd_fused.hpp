@@ -330,8 +330,10 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
     u32x4 dreg[2];
     u32x4 creg[Lay::NCL];
     float dtv = 0.0f;
-    // X and dt of chunk c into registers
-    auto issue_x = [&](int c) {
+    // X and dt of chunk c into registers (and, for the output phase, the
+    // diagonal C B^T block of the loader's block)
+    auto issue_x = [&](int c, auto out_tag) {
+        constexpr bool OUT = decltype(out_tag)::value;
         const int64_t tok0 = int64_t(c) * p.chunk;
         const int n = chunk_rows(c);
         const auto rx = __builtin_amdgcn_make_buffer_rsrc(
@@ -341,13 +343,18 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
         const auto rd = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.dt + (b * L + tok0) * p.H + h), 0,
                                                           n * p.H * 4, 0x00020000);
         dtv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, int(dtoff), 0, 0));
-        const auto rcb = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(cb_base(c)), 0, TT * TT * 2, 0x00020000);
-        dreg[0] = __builtin_amdgcn_raw_buffer_load_b128(rcb, int(cboff), 0, 0);
-        dreg[1] = __builtin_amdgcn_raw_buffer_load_b128(rcb, int(cboff + 16), 0, 0);
+        if constexpr (OUT) {
+            const auto rcb = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(cb_base(c)), 0, TT * TT * 2,
+                                                               0x00020000);
+            dreg[0] = __builtin_amdgcn_raw_buffer_load_b128(rcb, int(cboff), 0, 0);
+            dreg[1] = __builtin_amdgcn_raw_buffer_load_b128(rcb, int(cboff + 16), 0, 0);
+        }
     };
     // GL scan, tables, raw X and X~ of the loader's block into buffers `buf`
+    // (the aggregate phase needs only GL, the block decays and X~)
     float lgl = 0.0f, lge = 0.0f;  // the scan's GL (lanes < 32) and block-end GL, for the weights
-    auto prep = [&](int buf) {
+    auto prep = [&](int buf, auto out_tag) {
+        constexpr bool OUT = decltype(out_tag)::value;
         float* T = reinterpret_cast<float*>(sm + Lay::TB_OFF) + buf * Lay::TFLOATS;
         unsigned char* Xr = sm + Lay::X_OFF + buf * Lay::XBYTES;
         unsigned char* Xt = sm + Lay::XT_OFF + buf * Lay::XBYTES;
@@ -366,11 +373,13 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
         lge = ge;
         const float cf = dtv * fexp2(ge - gl);               // X~ factor, <= dt
         if (lblk && lane < 32) {
-            const float e = fexp2(fminf(-gl, 126.0f));  // used only when the block decay is <= 2^100
             T[Lay::T_GL + t] = gl;
-            T[Lay::T_DT + t] = dtv;
-            T[Lay::T_U + t] = dtv * e;
-            T[Lay::T_R + t] = fexp2(gl);
+            if constexpr (OUT) {
+                const float e = fexp2(fminf(-gl, 126.0f));  // used only when the block decay is <= 2^100
+                T[Lay::T_DT + t] = dtv;
+                T[Lay::T_U + t] = dtv * e;
+                T[Lay::T_R + t] = fexp2(gl);
+            }
             if (lane == 0) T[Lay::T_Q + lw] = fexp2(ge);
         }
         float f[4];
@@ -389,7 +398,7 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
                     const uint32_t word = xv[e];
                     w[e] = pack_bf16x2(bf16_lo(word) * f[m], bf16_hi(word) * f[m]);
                 }
-                *reinterpret_cast<u32x4*>(Xr + off) = xv;
+                if constexpr (OUT) *reinterpret_cast<u32x4*>(Xr + off) = xv;
                 *reinterpret_cast<u32x4*>(Xt + off) = w;
             }
         }
@@ -471,25 +480,29 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
         if (c_begin >= c_end) return;
         const int last = c_end - 1;
         auto clampc = [&](int c) { return c <= last ? c : last; };
-        issue_x(c_begin);
+        issue_x(c_begin, out_tag);
         if constexpr (OUT) issue_c(c_begin);
-        prep(c_begin & 1);
-        prep_w(c_begin & 1);
-        if constexpr (OUT) store_c();
+        prep(c_begin & 1, out_tag);
+        if constexpr (OUT) {
+            prep_w(c_begin & 1);
+            store_c();
+        }
         __builtin_amdgcn_sched_barrier(0);
-        issue_x(clampc(c_begin + 1));
+        issue_x(clampc(c_begin + 1), out_tag);
         if constexpr (OUT) issue_c(clampc(c_begin + 1));
         lds_barrier();
         for (int c = c_begin; c < c_end; ++c) {
             // chunk c + 1 into the half chunk c - 1 used: scan, tables and X~ while
             // the compute waves form the state term, the weights and the C copy
             // while they run the block loop
-            prep((c + 1) & 1);
+            prep((c + 1) & 1, out_tag);
             lds_barrier();  // barrier 1: the compute waves have read C and H of chunk c
-            prep_w((c + 1) & 1);
-            if constexpr (OUT) store_c();  // C of chunk c + 1
+            if constexpr (OUT) {
+                prep_w((c + 1) & 1);
+                store_c();  // C of chunk c + 1
+            }
             __builtin_amdgcn_sched_barrier(0);
-            issue_x(clampc(c + 2));
+            issue_x(clampc(c + 2), out_tag);
             if constexpr (OUT) issue_c(clampc(c + 2));
             lds_barrier();  // barrier 2
         }
