@@ -174,10 +174,11 @@ struct FuLayout {
     static constexpr int NB = TT / 32;                    // 32-token blocks
     static constexpr int NBL = (NB + kFuLoaders - 1) / kFuLoaders;  // blocks per loader wave (<= 2)
     static_assert(NBL <= 2, "a loader wave scans at most two blocks at once");
-    static constexpr int NCL = TT * S / 2048;             // 16-byte C loads per loader lane
-    static constexpr int CROWS = 512 / S;                 // C rows per 1 KB wave load
     static constexpr int XBYTES = TT * 128;               // X buffer [TT][64] bf16
     static constexpr int HP = S + 8;                      // bf16 pitch of the state rows
+    static constexpr int HBYTES = kFuP * HP * 2;          // one state copy
+    static constexpr int NCL = TT * S / 2048;             // 16-byte C loads per loader lane
+    static constexpr int CROWS = 512 / S;                 // C rows per 1 KB wave load
     static constexpr int CP = S + 8;                      // bf16 pitch of the C rows
     // per-chunk tables (floats): block-local cumulative decay GL, dt, the split
     // factor U = dt exp2(-GL), the row factor R = exp2(GL), and the block decays Q
@@ -191,13 +192,14 @@ struct FuLayout {
     static constexpr int RB = NB - 1;                     // off-diagonal blocks tile B can reach
     static constexpr int X_OFF = 0;                       // 2 x raw X [TT][64] bf16, swizzled
     static constexpr int XT_OFF = X_OFF + 2 * XBYTES;     // 2 x X~, same layout
-    static constexpr int H_OFF = XT_OFF + 2 * XBYTES;     // [64][HP] bf16 chunk-start state
-    static constexpr int C_OFF = H_OFF + kFuP * HP * 2;   // [TT][CP] bf16 C of the chunk
+    static constexpr int H_OFF = XT_OFF + 2 * XBYTES;     // 2 x [64][HP] bf16 chunk-start state
+    static constexpr int C_OFF = H_OFF + 2 * HBYTES;      // [TT][CP] bf16 C of the chunk
     static constexpr int TB_OFF = C_OFF + TT * CP * 2;    // 2 x tables
     static constexpr int W_OFF = TB_OFF + 2 * TFLOATS * 4;     // 2 x diagonal weights
     static constexpr int MISC_OFF = W_OFF + 2 * WBYTES;        // ints [4]
     static constexpr int ALPHA_OFF = MISC_OFF + 64;            // look-back decays [64]
     static constexpr int BYTES = ALPHA_OFF + 64 * 4;
+    static_assert(BYTES <= 160 * 1024, "LDS of one workgroup");
 };
 
 // byte offset of (row t, 32-byte pair `pair`, byte `within` < 32) in X or X~.
@@ -237,8 +239,11 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
     const bool loader = wave >= kFuWaves;
     const int lw = wave - kFuWaves;                               // loader index (loader waves)
     const int l16 = lane & 15, kg = lane >> 4;
-    uint16_t* Hs = reinterpret_cast<uint16_t*>(sm + Lay::H_OFF);
+    // bf16 copy of the chunk-start state, double-buffered by chunk parity
+    auto hs_buf = [&](int c) { return reinterpret_cast<uint16_t*>(sm + Lay::H_OFF + (c & 1) * Lay::HBYTES); };
     unsigned char* Cs = sm + Lay::C_OFF;
+    // lb_int[0]: claimed tile; [1]: look-back result; [2]: compute waves done
+    // with the C copy (running count over the output phase)
     int* lb_int = reinterpret_cast<int*>(sm + Lay::MISC_OFF);
     float* lb_alpha = reinterpret_cast<float*>(sm + Lay::ALPHA_OFF);
 
@@ -253,7 +258,10 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
     const int jdA_w = itA >> 1, jdB_w = itB >> 1;
 
     // ---- claim a segment (segment-major order) ----
-    if (tid == 0) lb_int[0] = int(atomic_add_u32(p.claim, 1u));
+    if (tid == 0) {
+        lb_int[0] = int(atomic_add_u32(p.claim, 1u));
+        lb_int[2] = 0;
+    }
     __syncthreads();
     const int tile = __builtin_amdgcn_readfirstlane(lb_int[0]);  // uniform: everything derived is scalar
     if (tile < 0 || tile >= p.nchains * p.nsegs) return;  // only a corrupted workspace gets here
@@ -280,7 +288,8 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
             dst[j] = v;
         }
     };
-    auto store_hs = [&](int l16, int kg) {
+    auto store_hs = [&](int c, int l16, int kg) {
+        uint16_t* Hs = hs_buf(c);
 #pragma unroll
         for (int j = 0; j < NPW; ++j) {
             u32x2 w;
@@ -467,8 +476,24 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
             *reinterpret_cast<u32x4*>(Cs + r * (Lay::CP * 2) + (lane % (S / 8)) * 16) = creg[k];
         }
     };
+    // The single C copy is overwritten once every compute wave has read it:
+    // the compute waves count their state terms in lb_int[2], and the loaders
+    // wait for the count instead of for a workgroup barrier, so the compute
+    // waves never wait for the loaders inside a chunk.  The wait is bounded;
+    // running out of it is reported in the error word.
+    auto wait_c_free = [&](int target) {
+        uint32_t spins = 0;
+        while (__hip_atomic_load(lb_int + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+            if (++spins > kFuSpinLimit) {
+                if (lane == 0) atomic_add_u32(p.err, 1u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");
+    };
     // The loader waves' share of a phase, with the same barriers as the compute
-    // waves.  Each register set is consumed before it is refilled, with the
+    // waves (one per chunk).  Each register set is consumed before it is refilled, with the
     // scheduler kept from hoisting the refill: a load issued while the old
     // value is live would land in other registers and be copied back at the
     // loop edge, which waits for the load to complete.  Loads are issued
@@ -492,19 +517,18 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
         if constexpr (OUT) issue_c(clampc(c_begin + 1));
         lds_barrier();
         for (int c = c_begin; c < c_end; ++c) {
-            // chunk c + 1 into the half chunk c - 1 used: scan, tables and X~ while
-            // the compute waves form the state term, the weights and the C copy
-            // while they run the block loop
+            // chunk c + 1 into the half chunk c - 1 used (free since the last
+            // barrier) while the compute waves work on chunk c
             prep((c + 1) & 1, out_tag);
-            lds_barrier();  // barrier 1: the compute waves have read C and H of chunk c
             if constexpr (OUT) {
                 prep_w((c + 1) & 1);
+                wait_c_free(kFuWaves * (c - c_begin + 1));
                 store_c();  // C of chunk c + 1
             }
             __builtin_amdgcn_sched_barrier(0);
             issue_x(clampc(c + 2), out_tag);
             if constexpr (OUT) issue_c(clampc(c + 2));
-            lds_barrier();  // barrier 2
+            lds_barrier();  // chunk c + 1 ready; chunk c's half free
         }
     };
 
@@ -544,7 +568,7 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
 #pragma unroll
             for (int k = 0; k < RB; ++k) rB[k] = ldg_b128(cb_base(c_begin) + cbB_lane + 64 * k);
         }
-        lds_barrier();
+        lds_barrier();  // the loaders have prepared the first chunk
 
         for (int c = c_begin; c < c_end; ++c) {
             // Lane-dependent offsets are rebuilt every chunk from an opaque copy of
@@ -571,8 +595,8 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
             const char* cbx = cb_base(cx);
             const char* btx = bt_base(cx);
 
-            // S4 state term y^T += H C^T from the chunk-start state (bf16 in LDS)
-            // and the chunk's C (staged in LDS by the loaders)
+            // S4 state term y^T += H C^T from the chunk-start state and the
+            // chunk's C (both bf16 in LDS)
             f32x4 accA[NPTW], accB[NPTW];
             if constexpr (OUT) {
 #pragma unroll
@@ -581,6 +605,7 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
                     accB[q] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
                 if (has_out) {
+                    const uint16_t* Hs = hs_buf(c);
                     const unsigned char* cra = Cs + (16 * itA + l16) * (Lay::CP * 2) + 16 * kg;
                     const unsigned char* crb = Cs + (16 * itB + l16) * (Lay::CP * 2) + 16 * kg;
 #pragma unroll
@@ -596,9 +621,10 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
                         }
                     }
                 }
-            }
-            lds_barrier();  // barrier 1: X, X~, tables of chunk c ready; H and C of chunk c read
-            if constexpr (!OUT) {
+                // the C copy has been read (its loads have returned): the loaders may refill it
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                if (lane == 0) __hip_atomic_fetch_add(lb_int + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            } else {
 #pragma unroll
                 for (int bb = 0; bb < NB; ++bb) sumG += T[Lay::T_GL + 32 * bb + 31];  // log2 decay of the chunk
             }
@@ -698,9 +724,9 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
                     store_y(accA, itA);
                     store_y(accB, itB);
                 }
-                store_hs(l16, kg);  // every wave has read the chunk-start state (barrier 1)
+                store_hs(c + 1, l16, kg);  // into the other copy: this chunk's is still being read
             }
-            lds_barrier();  // barrier 2: X of chunk c and the state copy are free / complete
+            lds_barrier();  // the next chunk's state copy, X, X~ and tables are complete
         }
     };
     // the wave's head-dim offsets become compile-time constants (static register indices)
@@ -813,7 +839,7 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
     } else {
         if (!loader) load_h0(hacc);
     }
-    if (!loader) store_hs(l16, kg);
+    if (!loader) store_hs(c_begin, l16, kg);
     lds_barrier();
     run_phase(FuPhase<true>{});
     if (p.h_final && seg == p.nsegs - 1 && !loader) {
