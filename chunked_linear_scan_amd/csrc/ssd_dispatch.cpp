@@ -28,11 +28,19 @@ int ssd_bf16_launch(int TT, int P, int S, const SsdBf16Params& prm, hipStream_t 
     }
 }
 
-// Segments per sequence for the fused kernel: one when there are at least 128
-// sequences (a segment after the first re-runs its chunks once for the state
-// aggregate, which costs more than idle compute units), else enough for about
-// 512 workgroups, at most 64 (the look-back window) and at most one per chunk.
+// Validation hooks (not part of the public header) that override the fused
+// kernel's segment plan: segments per split chain, and how many chains are split.
 static int g_segments_override = 0;
+static int g_split_override = 0;  // with the segment override: split only the last n chains (0: all)
+
+// concurrent workgroups of the fused kernel: one per CU
+int64_t fused_slots() {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+        return n;
+    return 256;
+}
 static int g_force_path = 0;  // 0 auto, 1 the per-(batch, head) chunk kernel, 2 the fused kernel
 
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
@@ -51,20 +59,32 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     if (!pl.use) return pl;
     const int64_t nc = (L + chunk - 1) / chunk;
     const int64_t nchains = batch * H;
-    int64_t nsegs;
+    // Each workgroup runs one chain (or segment) at a time, one per CU.  The
+    // chains that fill whole rounds of the CUs run whole; the remainder would
+    // leave most CUs idle in a last round, so it is split into segments that
+    // fill them, chained by the look-back.  A segment after the first costs
+    // about 5/3 of its length (its aggregate pass), which the split must beat.
+    int64_t nsegs = 1, nsplit = 0;
     if (g_segments_override > 0) {
         nsegs = g_segments_override;
-    } else if (nchains >= 128) {
-        nsegs = 1;
+        nsplit = (g_split_override > 0 && g_split_override < nchains) ? g_split_override : nchains;
     } else {
-        nsegs = (512 + nchains - 1) / nchains;
+        const int64_t slots = fused_slots();
+        const int64_t r = nchains % slots;
+        const int64_t sg = r > 0 ? slots / r : 0;
+        if (sg >= 2 && ((nc + sg - 1) / sg) * 5 < nc * 3) {
+            nsegs = sg;
+            nsplit = r;
+        }
     }
     if (nsegs > 64) nsegs = 64;
     if (nsegs > nc) nsegs = nc;
     if (nsegs < 1) nsegs = 1;
     const int64_t k = (nc + nsegs - 1) / nsegs;
     nsegs = (nc + k - 1) / k;
-    const int64_t ntiles = nsegs * nchains;
+    if (nsegs == 1) nsplit = 0;
+    const int64_t nsplit_tiles = nsegs * nsplit;
+    const int64_t ntiles = (nchains - nsplit) + nsplit_tiles;
     if (ntiles >= (int64_t(1) << 24)) {
         pl.use = false;
         return pl;
@@ -74,11 +94,12 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     pl.nsegs = int(nsegs);
     pl.seg_chunks = int(k);
     pl.nchains = int(nchains);
+    pl.nwhole = int(nchains - nsplit);
     pl.ntiles = int(ntiles);
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     pl.status_off = 256;
-    pl.payload_off = pl.status_off + up(size_t(ntiles) * 16);
-    const size_t pay = nsegs > 1 ? size_t(ntiles) * 2 * ssd_fused_state_floats(int(S)) * 4 : 0;
+    pl.payload_off = pl.status_off + up(size_t(nsplit_tiles) * 16);
+    const size_t pay = size_t(nsplit_tiles) * 2 * ssd_fused_state_floats(int(S)) * 4;
     pl.cb_off = pl.payload_off + up(pay);
     pl.bt_off = pl.cb_off + up(size_t(batch) * size_t(nc) * size_t(G) * size_t(TT) * TT * 2);
     pl.bytes = pl.bt_off + size_t(batch) * size_t(nc) * size_t(G) * size_t(S) * TT * 2;
@@ -149,6 +170,10 @@ extern "C" int cls_ssd_profile_read(double* cb_ms, double* fused_ms, int* calls)
 // Tuning hook (not part of the public header): force the number of segments
 // per sequence of the fused SSD kernel (0 restores the heuristic).
 extern "C" void cls_ssd_set_segments(int nsegs) { cls::g_segments_override = nsegs < 0 ? 0 : nsegs; }
+
+// With the segment override set: split only the last `nchains` (batch, head)
+// chains and run the others whole (0: split every chain).
+extern "C" void cls_ssd_set_split(int nchains) { cls::g_split_override = nchains < 0 ? 0 : nchains; }
 
 // Validation hook (not part of the public header): 1 forces the per-(batch,
 // head) chunk kernel for bf16 shapes the fused kernel also covers, 0 restores
@@ -226,7 +251,7 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
         p.bt = reinterpret_cast<uint16_t*>(ws + pl.bt_off);
         p.claim = reinterpret_cast<uint32_t*>(ws + 64);
         p.status = ws + pl.status_off;
-        p.zero_count = pl.ntiles;
+        p.zero_count = pl.ntiles - pl.nwhole;  // status words of the split tiles
         cls::SsdFusedParams f{};
         f.x = p.x;
         f.dt = p.dt;
@@ -252,6 +277,7 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
         f.seg_chunks = pl.seg_chunks;
         f.nsegs = pl.nsegs;
         f.nchains = pl.nchains;
+        f.nwhole = pl.nwhole;
         const int st = cls::ssd_fused_launch(pl.TT, int(s.dstate), p, f, pl.ntiles, stream, cls::ssd_profile_events());
         if (st == -8) return SSD_ERR_UNSUPPORTED;
         return st == 0 ? SSD_OK : SSD_ERR_HIP;

@@ -264,14 +264,19 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
     }
     __syncthreads();
     const int tile = __builtin_amdgcn_readfirstlane(lb_int[0]);  // uniform: everything derived is scalar
-    if (tile < 0 || tile >= p.nchains * p.nsegs) return;  // only a corrupted workspace gets here
-    const int seg = tile / p.nchains;
-    const int chain = tile % p.nchains;
+    const int nsplit = p.nchains - p.nwhole;                      // chains run as segments
+    if (tile < 0 || tile >= p.nwhole + p.nsegs * nsplit) return;  // only a corrupted workspace gets here
+    // whole chains first, then the segments of the split chains (segment-major,
+    // so every segment's predecessors were claimed before it)
+    const bool split = tile >= p.nwhole;
+    const int stile = tile - p.nwhole;  // index among the split tiles (status and payload)
+    const int seg = split ? stile / nsplit : 0;
+    const int chain = split ? p.nwhole + stile % nsplit : tile;
     const int64_t b = chain / p.H;
     const int h = chain % p.H;
     const int g = h / (p.H / p.G);
-    const int c_begin = seg * p.seg_chunks;
-    const int c_end = (c_begin + p.seg_chunks < p.nchunks) ? c_begin + p.seg_chunks : p.nchunks;
+    const int c_begin = split ? seg * p.seg_chunks : 0;
+    const int c_end = (split && c_begin + p.seg_chunks < p.nchunks) ? c_begin + p.seg_chunks : p.nchunks;
     const float A2 = p.A[h] * kLog2e;
     const float Dh = p.D ? p.D[h] : 0.0f;
     const int64_t L = p.L;
@@ -752,13 +757,13 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
         fu_static_switch<0, 4 / NPW>(pt0 / NPW, with_pt0);
     };
 
-    if (p.nsegs > 1) {
+    if (split) {
         // phase 1: this segment's own aggregate
 #pragma unroll
         for (int j = 0; j < NPW; ++j) hacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         run_phase(FuPhase<false>{});
         const float alpha_seg = fexp2(sumG);
-        float* pay = p.payload + int64_t(tile) * 2 * (kFuCompute * Lay::NACC);
+        float* pay = p.payload + int64_t(stile) * 2 * (kFuCompute * Lay::NACC);
         float* pay_agg = pay + tid * Lay::NACC;
         float* pay_inc = pay + kFuCompute * Lay::NACC + tid * Lay::NACC;
         f32x4 hin[NPW];
@@ -772,7 +777,7 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
                 wait_vmem();
             }
             __syncthreads();
-            if (tid == 0) store_coherent_b128(p.status + tile, u32x4{1u, as_uint(alpha_seg), 0u, 0u});
+            if (tid == 0) store_coherent_b128(p.status + stile, u32x4{1u, as_uint(alpha_seg), 0u, 0u});
             // look back: wave 0 inspects up to 64 predecessors
             if (wave == 0) {
                 const int pred = seg - 1 - lane;
@@ -782,7 +787,7 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
                 while (true) {
                     int kind = 2;
                     if (pred >= 0) {
-                        const u32x4 stw = load_coherent_b128(p.status + int64_t(pred) * p.nchains + chain);
+                        const u32x4 stw = load_coherent_b128(p.status + int64_t(pred) * nsplit + (chain - p.nwhole));
                         kind = int(stw[0]);
                         al = as_float(stw[1]);
                     }
@@ -809,7 +814,7 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
                 const int base_seg = seg - 1 - kp;
                 const int64_t tile_floats = 2 * (kFuCompute * Lay::NACC);
                 if (base_seg >= 0) {
-                    const float* src = p.payload + (int64_t(base_seg) * p.nchains + chain) * tile_floats +
+                    const float* src = p.payload + (int64_t(base_seg) * nsplit + (chain - p.nwhole)) * tile_floats +
                                        kFuCompute * Lay::NACC + tid * Lay::NACC;
 #pragma unroll
                     for (int j = 0; j < NPW; ++j) hin[j] = load_payload(src + 4 * j);
@@ -819,7 +824,8 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
                 for (int kk = kp - 1; kk >= 0; --kk) {
                     const float al = lb_alpha[kk];
                     const int sp = seg - 1 - kk;
-                    const float* src = p.payload + (int64_t(sp) * p.nchains + chain) * tile_floats + tid * Lay::NACC;
+                    const float* src =
+                        p.payload + (int64_t(sp) * nsplit + (chain - p.nwhole)) * tile_floats + tid * Lay::NACC;
 #pragma unroll
                     for (int j = 0; j < NPW; ++j) hin[j] = hin[j] * al + load_payload(src + 4 * j);
                 }
@@ -835,14 +841,14 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
             wait_vmem();
         }
         __syncthreads();
-        if (tid == 0) store_coherent_b128(p.status + tile, u32x4{2u, as_uint(alpha_seg), 0u, 0u});
+        if (tid == 0) store_coherent_b128(p.status + stile, u32x4{2u, as_uint(alpha_seg), 0u, 0u});
     } else {
         if (!loader) load_h0(hacc);
     }
     if (!loader) store_hs(c_begin, l16, kg);
     lds_barrier();
     run_phase(FuPhase<true>{});
-    if (p.h_final && seg == p.nsegs - 1 && !loader) {
+    if (p.h_final && (!split || seg == p.nsegs - 1) && !loader) {
 #pragma unroll
         for (int j = 0; j < NPW; ++j)
             *reinterpret_cast<f32x4*>(p.h_final + (bh * kFuP + 16 * (pt0 + j) + l16) * S + 16 * st + 4 * kg) = hacc[j];

@@ -59,11 +59,13 @@ struct SsdFusedParams {
     const uint16_t* cb;
     const uint16_t* bt;
     uint32_t* claim;
-    u32x4_t* status;     // [ntiles] {flag, alpha, 0, 0}
-    float* payload;      // [ntiles][2][threads][state floats per lane]
+    u32x4_t* status;     // [nsegs * (nchains - nwhole)] {flag, alpha, 0, 0}
+    float* payload;      // [nsegs * (nchains - nwhole)][2][threads][state floats per lane]
     uint32_t* err;
     int64_t batch, L;
-    int H, G, chunk, nchunks, seg_chunks, nsegs, nchains;
+    // chains [0, nwhole) run whole (tiles 0 .. nwhole - 1); chains [nwhole, nchains)
+    // are split into nsegs segments of seg_chunks chunks, claimed segment-major
+    int H, G, chunk, nchunks, seg_chunks, nsegs, nchains, nwhole;
 };
 
 // Plan of the fused head-dim-64 path for one shape (also sizes its workspace).
@@ -71,7 +73,7 @@ constexpr int64_t kFusedMaxChunk = 128;  // longest quadratic block of the fused
 
 struct SsdFusedPlan {
     bool use;
-    int TT, chunk, nsegs, seg_chunks, nchains, ntiles;  // chunk: the sub-chunk the kernel runs
+    int TT, chunk, nsegs, seg_chunks, nchains, nwhole, ntiles;  // chunk: the sub-chunk the kernel runs
     size_t status_off, payload_off, cb_off, bt_off, bytes;
 };
 

@@ -235,3 +235,26 @@ def test_segment_lookback_forced(nsegs):
     ry, rh, _, _ = oracle_run(inp)
     assert_close(y, ry, TOL_BF16, f"y nsegs={nsegs}")
     assert_close(hf, rh, TOL_BF16, f"h nsegs={nsegs}")
+
+
+@pytest.mark.parametrize("nsegs,nsplit,chunk", [(2, 1, 128), (5, 4, 128), (4, 5, 32), (3, 2, 64)])
+def test_segment_mixed_whole_and_split(nsegs, nsplit, chunk):
+    """Plans that run some (batch, head) chains whole and split the last
+    `nsplit` chains into segments (the shape of the plan that fills the CUs
+    left idle by a partial last round): both kinds of tile in one launch."""
+    ct = __import__("ctypes")
+    lib = cls.load_library()
+    lib.cls_ssd_set_segments.argtypes = [ct.c_int]
+    lib.cls_ssd_set_split.argtypes = [ct.c_int]
+    print(f"[ssd] mixed plan nsegs={nsegs} nsplit={nsplit} chunk={chunk}", flush=True)
+    inp = small_case(60 + nsegs, 2, 64 * 40 + 17, 3, 64, 128, 1, torch.bfloat16, dt_shift=-4.0)
+    lib.cls_ssd_set_segments(nsegs)
+    lib.cls_ssd_set_split(nsplit)
+    try:
+        y, hf = gpu_run(inp, chunk=chunk)
+    finally:
+        lib.cls_ssd_set_segments(0)
+        lib.cls_ssd_set_split(0)
+    ry, rh, _, _ = oracle_run(inp)
+    assert_close(y, ry, TOL_BF16, f"y nsegs={nsegs} nsplit={nsplit}")
+    assert_close(hf, rh, TOL_BF16, f"h nsegs={nsegs} nsplit={nsplit}")
