@@ -191,18 +191,20 @@ def bench_ssd(name, steps, warmup, want_cpu):
     lib = cls.load_library()
     import ctypes
     lib.cls_ssd_profile.argtypes = [ctypes.c_int]
-    lib.cls_ssd_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double)] * 2 + [ctypes.POINTER(ctypes.c_int)]
+    lib.cls_ssd_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double)] * 3 + [ctypes.POINTER(ctypes.c_int)]
     if lib.cls_ssd_profile(1) != 0:  # creates the events
         raise RuntimeError("could not create the profiling events")
     lib.cls_ssd_profile(0)
     t = time_loop(step, nsets, steps, warmup, stream, before_timed=lambda: lib.cls_ssd_profile(1))
-    cb_ms, fu_ms, ncalls = ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
-    if lib.cls_ssd_profile_read(ctypes.byref(cb_ms), ctypes.byref(fu_ms), ctypes.byref(ncalls)) != 0:
+    cb_ms, agg_ms, fu_ms, ncalls = ctypes.c_double(), ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
+    if lib.cls_ssd_profile_read(ctypes.byref(cb_ms), ctypes.byref(agg_ms), ctypes.byref(fu_ms),
+                                ctypes.byref(ncalls)) != 0:
         raise RuntimeError("reading the profiling events failed")
     lib.cls_ssd_profile(0)
     n = max(ncalls.value, 1)
     t_fused = fu_ms.value / 1e3 / n if ncalls.value else None
     t_cb = cb_ms.value / 1e3 / n if ncalls.value else None
+    t_agg = agg_ms.value / 1e3 / n if ncalls.value else None
     tokens = shape.batch * shape.seqlen
     flops = ssd_alg_flops(shape)
     t_kernel = t_fused if t_fused else t
@@ -216,9 +218,10 @@ def bench_ssd(name, steps, warmup, want_cpu):
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("ssd_fused_kernel:" + name, srcs),
-                     "kernel": "ssd_fused_kernel" if t_fused else "whole ssd_fwd call",
+                     "kernel": "ssd_fused_kernel (output launch)" if t_fused else "whole ssd_fwd call",
                      "kernel_us": round(t_kernel * 1e6, 2),
                      "cb_pass_us": None if t_cb is None else round(t_cb * 1e6, 2),
+                     "aggregate_pass_us": None if t_agg is None else round(t_agg * 1e6, 2),
                      "call_us": round(t * 1e6, 2),
                      "alg_bytes": alg_bytes, "alg_flops": flops,
                      "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),

@@ -62,14 +62,6 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cb_kernel(SsdBf16Params p) {
     constexpr int NIB = TT / 32;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kg = lane >> 4;
-    // reset the fused kernel's look-back bookkeeping (it runs after this pass)
-    if (p.status) {
-        u32x4* st = static_cast<u32x4*>(p.status);
-        for (int64_t q = int64_t(blockIdx.x) * kBfThreads + tid; q < p.zero_count;
-             q += int64_t(gridDim.x) * kBfThreads)
-            st[q] = u32x4{0u, 0u, 0u, 0u};
-        if (blockIdx.x == 0 && tid == 0) *p.claim = 0u;
-    }
     const int ib = int(blockIdx.x % NIB);
     const int64_t bcg = blockIdx.x / NIB;
     const int g = int(bcg % p.G);

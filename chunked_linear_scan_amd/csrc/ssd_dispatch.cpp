@@ -32,6 +32,8 @@ int ssd_bf16_launch(int TT, int P, int S, const SsdBf16Params& prm, hipStream_t 
 // kernel's segment plan: segments per split chain, and how many chains are split.
 static int g_segments_override = 0;
 static int g_split_override = 0;  // with the segment override: split only the last n chains (0: all)
+static int g_xcd_override = 0;    // XCDs of the tile mapping (0: kXcds)
+constexpr int kXcds = 8;          // MI355X: 8 XCDs of 32 CUs
 
 // concurrent workgroups of the fused kernel: one per CU
 int64_t fused_slots() {
@@ -62,8 +64,8 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     // Each workgroup runs one chain (or segment) at a time, one per CU.  The
     // chains that fill whole rounds of the CUs run whole; the remainder would
     // leave most CUs idle in a last round, so it is split into segments that
-    // fill them, chained by the look-back.  A segment after the first costs
-    // about 5/3 of its length (its aggregate pass), which the split must beat.
+    // fill them.  A segment costs its output pass plus its share of the
+    // aggregate launch (about half its length), which the split must beat.
     int64_t nsegs = 1, nsplit = 0;
     if (g_segments_override > 0) {
         nsegs = g_segments_override;
@@ -72,7 +74,7 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
         const int64_t slots = fused_slots();
         const int64_t r = nchains % slots;
         const int64_t sg = r > 0 ? slots / r : 0;
-        if (sg >= 2 && ((nc + sg - 1) / sg) * 5 < nc * 3) {
+        if (sg >= 2 && ((nc + sg - 1) / sg) * 3 < nc * 2) {
             nsegs = sg;
             nsplit = r;
         }
@@ -95,11 +97,11 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     pl.seg_chunks = int(k);
     pl.nchains = int(nchains);
     pl.nwhole = int(nchains - nsplit);
-    pl.ntiles = int(ntiles);
+    pl.nseg_tiles = int(nsplit_tiles);
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
-    pl.status_off = 256;
-    pl.payload_off = pl.status_off + up(size_t(nsplit_tiles) * 16);
-    const size_t pay = size_t(nsplit_tiles) * 2 * ssd_fused_state_floats(int(S)) * 4;
+    pl.payload_off = 256;
+    // per segment: its aggregate state (fp32) and its decay
+    const size_t pay = size_t(nsplit_tiles) * (size_t(ssd_fused_state_floats(int(S))) + 1) * 4;
     pl.cb_off = pl.payload_off + up(pay);
     pl.bt_off = pl.cb_off + up(size_t(batch) * size_t(nc) * size_t(G) * size_t(TT) * TT * 2);
     pl.bytes = pl.bt_off + size_t(batch) * size_t(nc) * size_t(G) * size_t(S) * TT * 2;
@@ -109,15 +111,17 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
 }  // namespace cls
 
 // Measurement hook (not part of the public header).  While enabled, every
-// fused-path ssd_fwd call records three events on its stream: before the CB
-// pass, between the CB pass and the fused kernel, and after the fused kernel.
+// fused-path ssd_fwd call records four events on its stream: before the CB
+// pass, after it, after the aggregate launch (recorded also when there is
+// none) and after the output launch.
 // Up to kProfCalls calls are kept (later calls reuse the slots round robin).
 namespace {
 constexpr int kProfCalls = 1024;
+constexpr int kProfEv = 4;
 struct ProfRecord {
     bool on = false;
     int calls = 0;
-    std::vector<hipEvent_t> ev;  // 3 per call
+    std::vector<hipEvent_t> ev;  // kProfEv per call
 };
 ProfRecord g_prof;
 }  // namespace
@@ -125,7 +129,7 @@ ProfRecord g_prof;
 namespace cls {
 hipEvent_t* ssd_profile_events() {
     if (!g_prof.on) return nullptr;
-    hipEvent_t* e = g_prof.ev.data() + 3 * (g_prof.calls % kProfCalls);
+    hipEvent_t* e = g_prof.ev.data() + kProfEv * (g_prof.calls % kProfCalls);
     ++g_prof.calls;
     return e;
 }
@@ -135,7 +139,7 @@ hipEvent_t* ssd_profile_events() {
 // Returns 0, or SSD_ERR_HIP when the events cannot be created.
 extern "C" int cls_ssd_profile(int enable) {
     if (enable && g_prof.ev.empty()) {
-        g_prof.ev.resize(3 * kProfCalls);
+        g_prof.ev.resize(kProfEv * kProfCalls);
         for (auto& e : g_prof.ev)
             if (hipEventCreate(&e) != hipSuccess) {
                 g_prof.ev.clear();
@@ -147,22 +151,25 @@ extern "C" int cls_ssd_profile(int enable) {
     return SSD_OK;
 }
 
-// Waits for the recorded calls and returns the summed CB-pass and fused-kernel
-// times in milliseconds and the number of calls summed.
-extern "C" int cls_ssd_profile_read(double* cb_ms, double* fused_ms, int* calls) {
-    double a = 0.0, b = 0.0;
+// Waits for the recorded calls and returns the summed times of the CB pass,
+// the aggregate launch and the output launch in milliseconds, and the number
+// of calls summed.
+extern "C" int cls_ssd_profile_read(double* cb_ms, double* agg_ms, double* out_ms, int* calls) {
+    double a = 0.0, b = 0.0, c = 0.0;
     const int n = g_prof.calls < kProfCalls ? g_prof.calls : kProfCalls;
     for (int i = 0; i < n; ++i) {
-        hipEvent_t* e = g_prof.ev.data() + 3 * i;
-        float t0 = 0.f, t1 = 0.f;
-        if (hipEventSynchronize(e[2]) != hipSuccess || hipEventElapsedTime(&t0, e[0], e[1]) != hipSuccess ||
-            hipEventElapsedTime(&t1, e[1], e[2]) != hipSuccess)
+        hipEvent_t* e = g_prof.ev.data() + kProfEv * i;
+        float t0 = 0.f, t1 = 0.f, t2 = 0.f;
+        if (hipEventSynchronize(e[3]) != hipSuccess || hipEventElapsedTime(&t0, e[0], e[1]) != hipSuccess ||
+            hipEventElapsedTime(&t1, e[1], e[2]) != hipSuccess || hipEventElapsedTime(&t2, e[2], e[3]) != hipSuccess)
             return SSD_ERR_HIP;
         a += t0;
         b += t1;
+        c += t2;
     }
     if (cb_ms) *cb_ms = a;
-    if (fused_ms) *fused_ms = b;
+    if (agg_ms) *agg_ms = b;
+    if (out_ms) *out_ms = c;
     if (calls) *calls = n;
     return SSD_OK;
 }
@@ -174,6 +181,10 @@ extern "C" void cls_ssd_set_segments(int nsegs) { cls::g_segments_override = nse
 // With the segment override set: split only the last `nchains` (batch, head)
 // chains and run the others whole (0: split every chain).
 extern "C" void cls_ssd_set_split(int nchains) { cls::g_split_override = nchains < 0 ? 0 : nchains; }
+
+// Tuning hook: the number of XCDs the fused kernel's tile mapping assumes
+// (1: plain index order; 0 restores the default).
+extern "C" void cls_ssd_set_xcds(int n) { cls::g_xcd_override = n < 0 ? 0 : n; }
 
 // Validation hook (not part of the public header): 1 forces the per-(batch,
 // head) chunk kernel for bf16 shapes the fused kernel also covers, 0 restores
@@ -249,9 +260,6 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
         char* ws = static_cast<char*>(a.workspace);
         p.cb = reinterpret_cast<uint16_t*>(ws + pl.cb_off);
         p.bt = reinterpret_cast<uint16_t*>(ws + pl.bt_off);
-        p.claim = reinterpret_cast<uint32_t*>(ws + 64);
-        p.status = ws + pl.status_off;
-        p.zero_count = pl.ntiles - pl.nwhole;  // status words of the split tiles
         cls::SsdFusedParams f{};
         f.x = p.x;
         f.dt = p.dt;
@@ -264,8 +272,6 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
         f.h_final = p.h_final;
         f.cb = p.cb;
         f.bt = p.bt;
-        f.claim = p.claim;
-        f.status = reinterpret_cast<cls::u32x4_t*>(ws + pl.status_off);
         f.payload = reinterpret_cast<float*>(ws + pl.payload_off);
         f.err = reinterpret_cast<uint32_t*>(ws);
         f.batch = s.batch;
@@ -278,7 +284,8 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
         f.nsegs = pl.nsegs;
         f.nchains = pl.nchains;
         f.nwhole = pl.nwhole;
-        const int st = cls::ssd_fused_launch(pl.TT, int(s.dstate), p, f, pl.ntiles, stream, cls::ssd_profile_events());
+        f.nxcd = cls::g_xcd_override > 0 ? cls::g_xcd_override : cls::kXcds;
+        const int st = cls::ssd_fused_launch(pl.TT, int(s.dstate), p, f, stream, cls::ssd_profile_events());
         if (st == -8) return SSD_ERR_UNSUPPORTED;
         return st == 0 ? SSD_OK : SSD_ERR_HIP;
     }

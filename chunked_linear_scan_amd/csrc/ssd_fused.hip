@@ -11,21 +11,13 @@ namespace cls {
 // token-contiguous copy B^T[s][t].  C and B rows are read through buffer loads
 // whose range ends at the chunk's last real token, so padded rows read as
 // zeros.  Wave w takes the 16-row tiles k and NIT-1-k (k = w, w + 4, ..), which
-// gives every wave the same number of tiles of the triangle.  The look-back
-// bookkeeping of the fused kernel is reset here as well.
+// gives every wave the same number of tiles of the triangle.
 template <int TT, int S>
 __global__ __launch_bounds__(kBfThreads) void ssd_cbt_kernel(SsdBf16Params p) {
     constexpr int KS = S / 32;
     constexpr int NIT = TT / 16;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kg = lane >> 4;
-    if (p.status) {
-        u32x4* st = static_cast<u32x4*>(p.status);
-        for (int64_t q = int64_t(blockIdx.x) * kBfThreads + tid; q < p.zero_count;
-             q += int64_t(gridDim.x) * kBfThreads)
-            st[q] = u32x4{0u, 0u, 0u, 0u};
-        if (blockIdx.x == 0 && tid == 0) *p.claim = 0u;
-    }
     const int64_t bcg = blockIdx.x;
     const int g = int(bcg % p.G);
     const int64_t c = (bcg / p.G) % p.nchunks;
@@ -83,25 +75,33 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cbt_kernel(SsdBf16Params p) {
 }
 
 template <int TT, int S>
-static int launch_fused_tpl(const SsdBf16Params& cbp, const SsdFusedParams& fp, int ntiles,
-                            hipStream_t stream, hipEvent_t* ev) {
+static int launch_fused_tpl(const SsdBf16Params& cbp, const SsdFusedParams& fp, hipStream_t stream,
+                            hipEvent_t* ev) {
     using Lay = FuLayout<TT, S>;
     static bool attr_set = false;
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_kernel<TT, S>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_kernel<TT, S, false>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, Lay::BYTES) != hipSuccess ||
+            hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_kernel<TT, S, true>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, Lay::BYTES) != hipSuccess)
             return -7;
         attr_set = true;
     }
+    const int nst = fp.nsegs * (fp.nchains - fp.nwhole);
     const dim3 gcb{uint32_t(cbp.batch * cbp.nchunks * cbp.G), 1u, 1u};
     const dim3 bcb{uint32_t(kBfThreads), 1u, 1u};
-    if (ev) hipEventRecord(ev[0], stream);
-    hipLaunchKernelGGL((ssd_cbt_kernel<TT, S>), gcb, bcb, 0, stream, cbp);
-    if (ev) hipEventRecord(ev[1], stream);
-    const dim3 gmain{uint32_t(ntiles), 1u, 1u};
     const dim3 bmain{uint32_t(kFuThreads), 1u, 1u};
-    hipLaunchKernelGGL((ssd_fused_kernel<TT, S>), gmain, bmain, Lay::BYTES, stream, fp);
-    if (ev) hipEventRecord(ev[2], stream);
+    if (ev) (void)hipEventRecord(ev[0], stream);
+    hipLaunchKernelGGL((ssd_cbt_kernel<TT, S>), gcb, bcb, 0, stream, cbp);
+    if (ev) (void)hipEventRecord(ev[1], stream);
+    if (nst > 0) {
+        const dim3 gagg{uint32_t(nst), 1u, 1u};
+        hipLaunchKernelGGL((ssd_fused_kernel<TT, S, true>), gagg, bmain, Lay::BYTES, stream, fp);
+    }
+    if (ev) (void)hipEventRecord(ev[2], stream);
+    const dim3 gout{uint32_t(fp.nwhole + nst), 1u, 1u};
+    hipLaunchKernelGGL((ssd_fused_kernel<TT, S, false>), gout, bmain, Lay::BYTES, stream, fp);
+    if (ev) (void)hipEventRecord(ev[3], stream);
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 
@@ -119,15 +119,15 @@ size_t ssd_fused_lds_bytes(int TT, int S) {
 
 int ssd_fused_state_floats(int S) { return kFuP * S; }
 
-int ssd_fused_launch(int TT, int S, const SsdBf16Params& cbp, const SsdFusedParams& fp, int ntiles,
-                     hipStream_t stream, hipEvent_t* ev) {
+int ssd_fused_launch(int TT, int S, const SsdBf16Params& cbp, const SsdFusedParams& fp, hipStream_t stream,
+                     hipEvent_t* ev) {
     switch (TT * 1000 + S) {
-        case 32064: return launch_fused_tpl<32, 64>(cbp, fp, ntiles, stream, ev);
-        case 32128: return launch_fused_tpl<32, 128>(cbp, fp, ntiles, stream, ev);
-        case 64064: return launch_fused_tpl<64, 64>(cbp, fp, ntiles, stream, ev);
-        case 64128: return launch_fused_tpl<64, 128>(cbp, fp, ntiles, stream, ev);
-        case 128064: return launch_fused_tpl<128, 64>(cbp, fp, ntiles, stream, ev);
-        case 128128: return launch_fused_tpl<128, 128>(cbp, fp, ntiles, stream, ev);
+        case 32064: return launch_fused_tpl<32, 64>(cbp, fp, stream, ev);
+        case 32128: return launch_fused_tpl<32, 128>(cbp, fp, stream, ev);
+        case 64064: return launch_fused_tpl<64, 64>(cbp, fp, stream, ev);
+        case 64128: return launch_fused_tpl<64, 128>(cbp, fp, stream, ev);
+        case 128064: return launch_fused_tpl<128, 64>(cbp, fp, stream, ev);
+        case 128128: return launch_fused_tpl<128, 128>(cbp, fp, stream, ev);
         default: return -8;
     }
 }

@@ -76,7 +76,7 @@ constexpr int kFuWaves = kFuCompute / 64;                    // compute waves
 constexpr int kFuLoaders = 4;                                // loader waves
 constexpr int kFuThreads = kFuCompute + 64 * kFuLoaders;     // workgroup size
 constexpr int kFuP = 64;  // head dim of this kernel
-constexpr uint32_t kFuSpinLimit = 1u << 24;
+constexpr uint32_t kFuSpinLimit = 1u << 24;  // bound of the loaders' wait for the C copy
 constexpr float kFuSplitMin = 7.8886091e-31f;  // 2^-100: weakest block decay of the split diagonal form
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -197,8 +197,7 @@ struct FuLayout {
     static constexpr int TB_OFF = C_OFF + TT * CP * 2;    // 2 x tables
     static constexpr int W_OFF = TB_OFF + 2 * TFLOATS * 4;     // 2 x diagonal weights
     static constexpr int MISC_OFF = W_OFF + 2 * WBYTES;        // ints [4]
-    static constexpr int ALPHA_OFF = MISC_OFF + 64;            // look-back decays [64]
-    static constexpr int BYTES = ALPHA_OFF + 64 * 4;
+    static constexpr int BYTES = MISC_OFF + 64;
     static_assert(BYTES <= 160 * 1024, "LDS of one workgroup");
 };
 
@@ -226,7 +225,26 @@ struct FuPhase {
 };
 
 // ---------------------------------------------------------------------------
-template <int TT, int S>
+// Tile of workgroup i among `n` work items that occupy workgroups
+// [base, base + n).  Workgroups are dispatched to the XCDs round robin (XCD
+// i % nx); the items are dealt so every XCD gets a contiguous range, i.e.
+// neighbouring (batch, head) chains that share B and C stay in one L2.
+__device__ __forceinline__ int fu_xcd_item(int i, int base, int n, int nx) {
+    // the range's workgroups on XCD k are base + r_k + m nx, r_k = (k - base) mod nx
+    const int x = i % nx;
+    int start = 0;
+    for (int k = 0; k < x; ++k) {
+        const int r = ((k - base) % nx + nx) % nx;
+        start += r < n ? (n - 1 - r) / nx + 1 : 0;
+    }
+    const int r = ((x - base) % nx + nx) % nx;
+    return start + (i - base - r) / nx;
+}
+
+// AGG: the aggregate launch (one workgroup per segment of a split chain: its
+// state from zero and its decay); otherwise the output launch (whole chains,
+// then the segments of split chains from the folded aggregates).
+template <int TT, int S, bool AGG>
 __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p) {
     using Lay = FuLayout<TT, S>;
     constexpr int NPW = Lay::NPW;
@@ -242,10 +260,9 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
     // bf16 copy of the chunk-start state, double-buffered by chunk parity
     auto hs_buf = [&](int c) { return reinterpret_cast<uint16_t*>(sm + Lay::H_OFF + (c & 1) * Lay::HBYTES); };
     unsigned char* Cs = sm + Lay::C_OFF;
-    // lb_int[0]: claimed tile; [1]: look-back result; [2]: compute waves done
-    // with the C copy (running count over the output phase)
+    // lb_int[2]: compute waves done with the C copy (running count over the
+    // output phase)
     int* lb_int = reinterpret_cast<int*>(sm + Lay::MISC_OFF);
-    float* lb_alpha = reinterpret_cast<float*>(sm + Lay::ALPHA_OFF);
 
     // state tile of this wave: s-tile st, head-dim tiles pt0 .. pt0 + NPW - 1
     const int st = wave % Lay::NST;
@@ -257,21 +274,28 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
     const int itA = pair, itB = Lay::NIT - 1 - pair;
     const int jdA_w = itA >> 1, jdB_w = itB >> 1;
 
-    // ---- claim a segment (segment-major order) ----
-    if (tid == 0) {
-        lb_int[0] = int(atomic_add_u32(p.claim, 1u));
-        lb_int[2] = 0;
+    // ---- the work item (workgroup-uniform: everything derived is scalar) ----
+    // Output launch: workgroups [0, nwhole) run whole chains, the rest the
+    // segments of the split chains; as workgroups start in index order, the
+    // long whole chains go first.  Items are chain-major within each list.
+    const int nsplit = p.nchains - p.nwhole;  // chains run as segments
+    const int nst = p.nsegs * nsplit;         // segments
+    const int wg = blockIdx.x;
+    bool split;
+    int item;
+    if constexpr (AGG) {
+        if (wg >= nst) return;
+        split = true;
+        item = fu_xcd_item(wg, 0, nst, p.nxcd);
+    } else {
+        if (wg >= p.nwhole + nst) return;
+        split = wg >= p.nwhole;
+        item = split ? fu_xcd_item(wg, p.nwhole, nst, p.nxcd) : fu_xcd_item(wg, 0, p.nwhole, p.nxcd);
     }
-    __syncthreads();
-    const int tile = __builtin_amdgcn_readfirstlane(lb_int[0]);  // uniform: everything derived is scalar
-    const int nsplit = p.nchains - p.nwhole;                      // chains run as segments
-    if (tile < 0 || tile >= p.nwhole + p.nsegs * nsplit) return;  // only a corrupted workspace gets here
-    // whole chains first, then the segments of the split chains (segment-major,
-    // so every segment's predecessors were claimed before it)
-    const bool split = tile >= p.nwhole;
-    const int stile = tile - p.nwhole;  // index among the split tiles (status and payload)
-    const int seg = split ? stile / nsplit : 0;
-    const int chain = split ? p.nwhole + stile % nsplit : tile;
+    const int seg = split ? item % p.nsegs : 0;
+    const int chain = split ? p.nwhole + item / p.nsegs : item;
+    const int stile = seg * nsplit + (chain - p.nwhole);  // payload slot of a segment
+    if (tid == 0) lb_int[2] = 0;
     const int64_t b = chain / p.H;
     const int h = chain % p.H;
     const int g = h / (p.H / p.G);
@@ -340,13 +364,11 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
         const int r = Lay::CROWS * (kFuLoaders * k + lw) + lane / (S / 8);
         coff[k] = uint32_t(r) * uint32_t(p.G * S * 2) + uint32_t((lane % (S / 8)) * 16);
     }
-    u32x4 xreg[4];
     u32x4 dreg[2];
     u32x4 creg[Lay::NCL];
-    float dtv = 0.0f;
-    // X and dt of chunk c into registers (and, for the output phase, the
-    // diagonal C B^T block of the loader's block)
-    auto issue_x = [&](int c, auto out_tag) {
+    // X and dt of chunk c into the register set (xreg, dtv) (and, for the
+    // output phase, the diagonal C B^T block of the loader's block)
+    auto issue_x = [&](int c, auto out_tag, u32x4 (&xreg)[4], float& dtv) {
         constexpr bool OUT = decltype(out_tag)::value;
         const int64_t tok0 = int64_t(c) * p.chunk;
         const int n = chunk_rows(c);
@@ -367,7 +389,7 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
     // GL scan, tables, raw X and X~ of the loader's block into buffers `buf`
     // (the aggregate phase needs only GL, the block decays and X~)
     float lgl = 0.0f, lge = 0.0f;  // the scan's GL (lanes < 32) and block-end GL, for the weights
-    auto prep = [&](int buf, auto out_tag) {
+    auto prep = [&](int buf, auto out_tag, const u32x4 (&xreg)[4], const float dtv) {
         constexpr bool OUT = decltype(out_tag)::value;
         float* T = reinterpret_cast<float*>(sm + Lay::TB_OFF) + buf * Lay::TFLOATS;
         unsigned char* Xr = sm + Lay::X_OFF + buf * Lay::XBYTES;
@@ -498,42 +520,69 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
         asm volatile("" ::: "memory");
     };
     // The loader waves' share of a phase, with the same barriers as the compute
-    // waves (one per chunk).  Each register set is consumed before it is refilled, with the
-    // scheduler kept from hoisting the refill: a load issued while the old
-    // value is live would land in other registers and be copied back at the
-    // loop edge, which waits for the load to complete.  Loads are issued
-    // unconditionally (past the last chunk the last one is reloaded and
-    // prepared into the free buffer half) so no register is merged across
-    // branches.
+    // waves (one per chunk).  X and dt are fetched D chunks ahead into a ring of
+    // D register sets: a load issued at the end of a chunk's preparation is
+    // consumed D barriers later.  In the output phase the loaders wait out
+    // most of every chunk at the barrier, which hides the latency with D = 1;
+    // the aggregate phase's chunks are short, and with one set its loads would
+    // be waited for soon after they are issued.  Each register set is consumed
+    // before it is refilled, with the scheduler kept from hoisting the refill:
+    // a load issued while the old value is live would land in other registers
+    // and be copied back at the loop edge, which waits for the load to
+    // complete.  Loads are issued unconditionally (past the last chunk the last
+    // one is reloaded and prepared into the free buffer half) so no register
+    // is merged across branches.
     auto run_loader = [&](auto out_tag) {
         constexpr bool OUT = decltype(out_tag)::value;
+        constexpr int D = OUT ? 1 : 2;
         if (c_begin >= c_end) return;
         const int last = c_end - 1;
         auto clampc = [&](int c) { return c <= last ? c : last; };
-        issue_x(c_begin, out_tag);
+        u32x4 xreg[D][4];  // chunk j in set (j - c_begin) % D
+        float dtv[D];
+        fu_static_for<0, D>([&](auto sc) {
+            constexpr int sl = decltype(sc)::value;
+            issue_x(clampc(c_begin + sl), out_tag, xreg[sl], dtv[sl]);
+        });
         if constexpr (OUT) issue_c(c_begin);
-        prep(c_begin & 1, out_tag);
+        prep(c_begin & 1, out_tag, xreg[0], dtv[0]);
         if constexpr (OUT) {
             prep_w(c_begin & 1);
             store_c();
         }
         __builtin_amdgcn_sched_barrier(0);
-        issue_x(clampc(c_begin + 1), out_tag);
+        issue_x(clampc(c_begin + D), out_tag, xreg[0], dtv[0]);
         if constexpr (OUT) issue_c(clampc(c_begin + 1));
         lds_barrier();
-        for (int c = c_begin; c < c_end; ++c) {
-            // chunk c + 1 into the half chunk c - 1 used (free since the last
-            // barrier) while the compute waves work on chunk c
-            prep((c + 1) & 1, out_tag);
+        // chunk c + 1 into the half chunk c - 1 used (free since the last
+        // barrier) while the compute waves work on chunk c
+        auto step = [&](auto kc, int c) {
+            constexpr int sl = (decltype(kc)::value + 1) % D;  // set of chunk c + 1
+            prep((c + 1) & 1, out_tag, xreg[sl], dtv[sl]);
             if constexpr (OUT) {
                 prep_w((c + 1) & 1);
                 wait_c_free(kFuWaves * (c - c_begin + 1));
                 store_c();  // C of chunk c + 1
             }
             __builtin_amdgcn_sched_barrier(0);
-            issue_x(clampc(c + 2), out_tag);
+            issue_x(clampc(c + 1 + D), out_tag, xreg[sl], dtv[sl]);
             if constexpr (OUT) issue_c(clampc(c + 2));
             lds_barrier();  // chunk c + 1 ready; chunk c's half free
+            __builtin_amdgcn_sched_barrier(0);  // the next step's waits stay after the barrier
+        };
+        // unrolled by D so the sets are static registers, with the loop's only
+        // exit at its end and the remainder after it: the loop head then sees
+        // the loads in one issue order on every path
+        static_assert(D == 1 || D == 2, "register sets");
+        const int nrounds = (c_end - c_begin) / D;
+        int c = c_begin;
+        for (int i = 0; i < nrounds; ++i) {
+            step(std::integral_constant<int, 0>{}, c);
+            if constexpr (D == 2) step(std::integral_constant<int, 1>{}, c + 1);
+            c += D;
+        }
+        if constexpr (D == 2) {
+            if (c < c_end) step(std::integral_constant<int, 0>{}, c);
         }
     };
 
@@ -757,101 +806,41 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
         fu_static_switch<0, 4 / NPW>(pt0 / NPW, with_pt0);
     };
 
-    if (split) {
-        // phase 1: this segment's own aggregate
+    float* pay_alpha = p.payload + int64_t(nst) * (kFuCompute * Lay::NACC);  // [nst] segment decays
+    if constexpr (AGG) {
+        // the segment's aggregate: its state from zero, and its decay
 #pragma unroll
         for (int j = 0; j < NPW; ++j) hacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         run_phase(FuPhase<false>{});
-        const float alpha_seg = fexp2(sumG);
-        float* pay = p.payload + int64_t(stile) * 2 * (kFuCompute * Lay::NACC);
-        float* pay_agg = pay + tid * Lay::NACC;
-        float* pay_inc = pay + kFuCompute * Lay::NACC + tid * Lay::NACC;
-        f32x4 hin[NPW];
-        if (seg == 0) {
-            if (!loader) load_h0(hin);
-        } else {
-            // publish the aggregate (alpha_seg is wave 0's, which is a compute wave)
-            if (!loader) {
-#pragma unroll
-                for (int j = 0; j < NPW; ++j) store_payload(pay_agg + 4 * j, hacc[j]);
-                wait_vmem();
-            }
-            __syncthreads();
-            if (tid == 0) store_coherent_b128(p.status + stile, u32x4{1u, as_uint(alpha_seg), 0u, 0u});
-            // look back: wave 0 inspects up to 64 predecessors
-            if (wave == 0) {
-                const int pred = seg - 1 - lane;
-                uint32_t spins = 0;
-                int kp = 64;
-                float al = 1.0f;
-                while (true) {
-                    int kind = 2;
-                    if (pred >= 0) {
-                        const u32x4 stw = load_coherent_b128(p.status + int64_t(pred) * nsplit + (chain - p.nwhole));
-                        kind = int(stw[0]);
-                        al = as_float(stw[1]);
-                    }
-                    const uint64_t incm = __ballot(kind == 2);
-                    const uint64_t notready = __ballot(kind == 0);
-                    kp = incm ? int(__builtin_ctzll(incm)) : 64;
-                    const uint64_t below = (kp >= 64) ? ~0ull : ((1ull << kp) - 1ull);
-                    if (!(notready & below) && kp < 64) break;
-                    if (++spins > kFuSpinLimit) {
-                        if (lane == 0) atomic_add_u32(p.err, 1u);
-                        kp = -1;
-                        break;
-                    }
-                    __builtin_amdgcn_s_sleep(1);
-                }
-                if (lane == 0) lb_int[1] = kp;
-                if (lane < kp) lb_alpha[lane] = al;
-            }
-            __syncthreads();
-            const int kp = __builtin_amdgcn_readfirstlane(lb_int[1]);
-#pragma unroll
-            for (int j = 0; j < NPW; ++j) hin[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (kp >= 0 && !loader) {
-                const int base_seg = seg - 1 - kp;
-                const int64_t tile_floats = 2 * (kFuCompute * Lay::NACC);
-                if (base_seg >= 0) {
-                    const float* src = p.payload + (int64_t(base_seg) * nsplit + (chain - p.nwhole)) * tile_floats +
-                                       kFuCompute * Lay::NACC + tid * Lay::NACC;
-#pragma unroll
-                    for (int j = 0; j < NPW; ++j) hin[j] = load_payload(src + 4 * j);
-                } else {
-                    load_h0(hin);  // every predecessor was an aggregate: start from h0
-                }
-                for (int kk = kp - 1; kk >= 0; --kk) {
-                    const float al = lb_alpha[kk];
-                    const int sp = seg - 1 - kk;
-                    const float* src =
-                        p.payload + (int64_t(sp) * nsplit + (chain - p.nwhole)) * tile_floats + tid * Lay::NACC;
-#pragma unroll
-                    for (int j = 0; j < NPW; ++j) hin[j] = hin[j] * al + load_payload(src + 4 * j);
-                }
-            }
-        }
-        // publish the inclusive state at the segment end
         if (!loader) {
+            float* pay = p.payload + int64_t(stile) * (kFuCompute * Lay::NACC) + tid * Lay::NACC;
 #pragma unroll
-            for (int j = 0; j < NPW; ++j) {
-                store_payload(pay_inc + 4 * j, hin[j] * alpha_seg + hacc[j]);
-                hacc[j] = hin[j];
-            }
-            wait_vmem();
+            for (int j = 0; j < NPW; ++j) *reinterpret_cast<f32x4*>(pay + 4 * j) = hacc[j];
         }
-        __syncthreads();
-        if (tid == 0) store_coherent_b128(p.status + stile, u32x4{2u, as_uint(alpha_seg), 0u, 0u});
+        if (tid == 0) pay_alpha[stile] = fexp2(sumG);  // wave 0's (a compute wave)
+        return;
     } else {
-        if (!loader) load_h0(hacc);
-    }
-    if (!loader) store_hs(c_begin, l16, kg);
-    lds_barrier();
-    run_phase(FuPhase<true>{});
-    if (p.h_final && (!split || seg == p.nsegs - 1) && !loader) {
+        if (!loader) {
+            load_h0(hacc);
+            // a segment starts from h0 folded through its predecessors'
+            // aggregates: h <- alpha_k h + S_k (the aggregate launch has finished)
+            for (int k = 0; k < seg; ++k) {
+                const int t = k * nsplit + (chain - p.nwhole);
+                const float al = pay_alpha[t];
+                const float* src = p.payload + int64_t(t) * (kFuCompute * Lay::NACC) + tid * Lay::NACC;
 #pragma unroll
-        for (int j = 0; j < NPW; ++j)
-            *reinterpret_cast<f32x4*>(p.h_final + (bh * kFuP + 16 * (pt0 + j) + l16) * S + 16 * st + 4 * kg) = hacc[j];
+                for (int j = 0; j < NPW; ++j) hacc[j] = hacc[j] * al + *reinterpret_cast<const f32x4*>(src + 4 * j);
+            }
+            store_hs(c_begin, l16, kg);
+        }
+        lds_barrier();
+        run_phase(FuPhase<true>{});
+        if (p.h_final && (!split || seg == p.nsegs - 1) && !loader) {
+#pragma unroll
+            for (int j = 0; j < NPW; ++j)
+                *reinterpret_cast<f32x4*>(p.h_final + (bh * kFuP + 16 * (pt0 + j) + l16) * S + 16 * st + 4 * kg) =
+                    hacc[j];
+        }
     }
 }
 

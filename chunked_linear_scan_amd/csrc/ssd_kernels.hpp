@@ -40,10 +40,6 @@ struct SsdBf16Params {
     uint16_t* bt;        // workspace: bf16 [Bt, Nc, G, S, TT] (B^T), or null when not needed
     int64_t batch, L;
     int H, G, chunk, nchunks;
-    // look-back bookkeeping the CB pass resets for the fused kernel
-    uint32_t* claim;     // tile claim counter
-    void* status;        // [zero_count] 16-byte status words
-    int zero_count;
 };
 
 struct SsdFusedParams {
@@ -58,14 +54,13 @@ struct SsdFusedParams {
     float* h_final;
     const uint16_t* cb;
     const uint16_t* bt;
-    uint32_t* claim;
-    u32x4_t* status;     // [nsegs * (nchains - nwhole)] {flag, alpha, 0, 0}
-    float* payload;      // [nsegs * (nchains - nwhole)][2][threads][state floats per lane]
+    float* payload;      // [nseg tiles][threads][state floats per lane] aggregates, then [nseg tiles] decays
     uint32_t* err;
     int64_t batch, L;
-    // chains [0, nwhole) run whole (tiles 0 .. nwhole - 1); chains [nwhole, nchains)
-    // are split into nsegs segments of seg_chunks chunks, claimed segment-major
+    // chains [0, nwhole) run whole; chains [nwhole, nchains) are split into
+    // nsegs segments of seg_chunks chunks (aggregate launch, then output launch)
     int H, G, chunk, nchunks, seg_chunks, nsegs, nchains, nwhole;
+    int nxcd;  // XCDs the workgroups are dealt across (tile mapping only)
 };
 
 // Plan of the fused head-dim-64 path for one shape (also sizes its workspace).
@@ -73,8 +68,9 @@ constexpr int64_t kFusedMaxChunk = 128;  // longest quadratic block of the fused
 
 struct SsdFusedPlan {
     bool use;
-    int TT, chunk, nsegs, seg_chunks, nchains, nwhole, ntiles;  // chunk: the sub-chunk the kernel runs
-    size_t status_off, payload_off, cb_off, bt_off, bytes;
+    int TT, chunk, nsegs, seg_chunks, nchains, nwhole;  // chunk: the sub-chunk the kernel runs
+    int nseg_tiles;                                     // segments of the split chains
+    size_t payload_off, cb_off, bt_off, bytes;
 };
 
 // Tile sizes of the bf16 path: the chunk is padded to a multiple of 32 tokens.
@@ -97,8 +93,10 @@ size_t ssd_fused_lds_bytes(int TT, int S);
 int ssd_fused_state_floats(int S);  // floats of one [64, S] state
 // ev: null, or three events recorded before the CB pass, between the passes
 // and after the fused kernel (measurement hook)
-int ssd_fused_launch(int TT, int S, const SsdBf16Params& cbp, const SsdFusedParams& fp, int ntiles,
-                     hipStream_t stream, hipEvent_t* ev);
+// CB pass, then (with split chains) the aggregate launch, then the output
+// launch; ev (optional): four events, before and between the launches.
+int ssd_fused_launch(int TT, int S, const SsdBf16Params& cbp, const SsdFusedParams& fp, hipStream_t stream,
+                     hipEvent_t* ev);
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
                             int64_t chunk, int dtype);
 int ssd_bf16_launch(int TT, int P, int S, const SsdBf16Params& prm, hipStream_t stream);
