@@ -195,7 +195,11 @@ def bench_ssd(name, steps, warmup, want_cpu):
     if lib.cls_ssd_profile(1) != 0:  # creates the events
         raise RuntimeError("could not create the profiling events")
     lib.cls_ssd_profile(0)
-    t = time_loop(step, nsets, steps, warmup, stream, before_timed=lambda: lib.cls_ssd_profile(1))
+    # the timed steps run without the library's events (recording them costs a
+    # few microseconds per call); a second, shorter loop records them for the
+    # per-launch breakdown
+    t = time_loop(step, nsets, steps, warmup, stream)
+    time_loop(step, nsets, max(10, steps // 4), 2, stream, before_timed=lambda: lib.cls_ssd_profile(1))
     cb_ms, agg_ms, fu_ms, ncalls = ctypes.c_double(), ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
     if lib.cls_ssd_profile_read(ctypes.byref(cb_ms), ctypes.byref(agg_ms), ctypes.byref(fu_ms),
                                 ctypes.byref(ncalls)) != 0:
@@ -222,6 +226,8 @@ def bench_ssd(name, steps, warmup, want_cpu):
                      "kernel_us": round(t_kernel * 1e6, 2),
                      "cb_pass_us": None if t_cb is None else round(t_cb * 1e6, 2),
                      "aggregate_pass_us": None if t_agg is None else round(t_agg * 1e6, 2),
+                     "fused_launches_frac": None if t_agg is None else
+                     round(alg_bytes / (t_agg + t_kernel) / 1e9 / HBM_PEAK_GBS, 4),
                      "call_us": round(t * 1e6, 2),
                      "alg_bytes": alg_bytes, "alg_flops": flops,
                      "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),

@@ -87,6 +87,17 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     if (nsegs == 1) nsplit = 0;
     const int64_t nsplit_tiles = nsegs * nsplit;
     const int64_t ntiles = (nchains - nsplit) + nsplit_tiles;
+    // Aggregate pieces: the segments but the last of each split chain, cut so
+    // the aggregate launch has about two workgroups per CU (it fits two).
+    int64_t agg_d = 1, agg_k = k;
+    if (nsplit > 0) {
+        agg_d = (2 * fused_slots()) / (nsplit * (nsegs - 1));
+        if (agg_d < 1) agg_d = 1;
+        if (agg_d > k) agg_d = k;
+        agg_k = (k + agg_d - 1) / agg_d;
+        agg_d = (k + agg_k - 1) / agg_k;
+    }
+    const int64_t npieces = nsplit * (nsegs - 1) * agg_d;
     if (ntiles >= (int64_t(1) << 24)) {
         pl.use = false;
         return pl;
@@ -97,11 +108,13 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     pl.seg_chunks = int(k);
     pl.nchains = int(nchains);
     pl.nwhole = int(nchains - nsplit);
-    pl.nseg_tiles = int(nsplit_tiles);
+    pl.agg_d = int(agg_d);
+    pl.agg_chunks = int(agg_k);
+    pl.npieces = int(npieces);
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
     pl.payload_off = 256;
-    // per segment: its aggregate state (fp32) and its decay
-    const size_t pay = size_t(nsplit_tiles) * (size_t(ssd_fused_state_floats(int(S))) + 1) * 4;
+    // per aggregate piece: its state (fp32) and its decay
+    const size_t pay = size_t(npieces) * (size_t(ssd_fused_state_floats(int(S))) + 1) * 4;
     pl.cb_off = pl.payload_off + up(pay);
     pl.bt_off = pl.cb_off + up(size_t(batch) * size_t(nc) * size_t(G) * size_t(TT) * TT * 2);
     pl.bytes = pl.bt_off + size_t(batch) * size_t(nc) * size_t(G) * size_t(S) * TT * 2;
@@ -284,6 +297,8 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
         f.nsegs = pl.nsegs;
         f.nchains = pl.nchains;
         f.nwhole = pl.nwhole;
+        f.agg_d = pl.agg_d;
+        f.agg_chunks = pl.agg_chunks;
         f.nxcd = cls::g_xcd_override > 0 ? cls::g_xcd_override : cls::kXcds;
         const int st = cls::ssd_fused_launch(pl.TT, int(s.dstate), p, f, stream, cls::ssd_profile_events());
         if (st == -8) return SSD_ERR_UNSUPPORTED;

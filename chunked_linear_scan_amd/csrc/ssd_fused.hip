@@ -78,29 +78,31 @@ template <int TT, int S>
 static int launch_fused_tpl(const SsdBf16Params& cbp, const SsdFusedParams& fp, hipStream_t stream,
                             hipEvent_t* ev) {
     using Lay = FuLayout<TT, S>;
+    using LayA = FuLayout<TT, S, true>;
     static bool attr_set = false;
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_kernel<TT, S, false>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_kernel<TT, S>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, Lay::BYTES) != hipSuccess ||
-            hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_kernel<TT, S, true>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, Lay::BYTES) != hipSuccess)
+            hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_agg_kernel<TT, S>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, LayA::BYTES) != hipSuccess)
             return -7;
         attr_set = true;
     }
-    const int nst = fp.nsegs * (fp.nchains - fp.nwhole);
+    const int nst = fp.nsegs * (fp.nchains - fp.nwhole);              // segments
+    const int npieces = (fp.nchains - fp.nwhole) * (fp.nsegs - 1) * fp.agg_d;  // aggregate pieces
     const dim3 gcb{uint32_t(cbp.batch * cbp.nchunks * cbp.G), 1u, 1u};
     const dim3 bcb{uint32_t(kBfThreads), 1u, 1u};
     const dim3 bmain{uint32_t(kFuThreads), 1u, 1u};
     if (ev) (void)hipEventRecord(ev[0], stream);
     hipLaunchKernelGGL((ssd_cbt_kernel<TT, S>), gcb, bcb, 0, stream, cbp);
     if (ev) (void)hipEventRecord(ev[1], stream);
-    if (nst > 0) {
-        const dim3 gagg{uint32_t(nst), 1u, 1u};
-        hipLaunchKernelGGL((ssd_fused_kernel<TT, S, true>), gagg, bmain, Lay::BYTES, stream, fp);
+    if (npieces > 0) {
+        const dim3 gagg{uint32_t(npieces), 1u, 1u};
+        hipLaunchKernelGGL((ssd_fused_agg_kernel<TT, S>), gagg, bmain, LayA::BYTES, stream, fp);
     }
     if (ev) (void)hipEventRecord(ev[2], stream);
     const dim3 gout{uint32_t(fp.nwhole + nst), 1u, 1u};
-    hipLaunchKernelGGL((ssd_fused_kernel<TT, S, false>), gout, bmain, Lay::BYTES, stream, fp);
+    hipLaunchKernelGGL((ssd_fused_kernel<TT, S>), gout, bmain, Lay::BYTES, stream, fp);
     if (ev) (void)hipEventRecord(ev[3], stream);
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }

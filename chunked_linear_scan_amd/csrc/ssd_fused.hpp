@@ -160,7 +160,9 @@ __device__ __forceinline__ float fu_dpp_bcast15(float v) {
                                                                  false));
 }
 
-template <int TT, int S>
+// LDS layout.  The aggregate launch (AGG) keeps only X~ and the tables, so two
+// of its workgroups fit a CU.
+template <int TT, int S, bool AGG = false>
 struct FuLayout {
     static_assert(S == 64 || S == 128, "state size of the fused kernel");
     static_assert(TT >= 32 && TT <= 128 && TT % 32 == 0, "tile tokens");
@@ -190,13 +192,13 @@ struct FuLayout {
     static constexpr int WBYTES = NB * WBLK;              // one chunk's weights
     static constexpr int RA = (NPAIR - 1) >> 1;           // off-diagonal blocks tile A can reach
     static constexpr int RB = NB - 1;                     // off-diagonal blocks tile B can reach
-    static constexpr int X_OFF = 0;                       // 2 x raw X [TT][64] bf16, swizzled
-    static constexpr int XT_OFF = X_OFF + 2 * XBYTES;     // 2 x X~, same layout
-    static constexpr int H_OFF = XT_OFF + 2 * XBYTES;     // 2 x [64][HP] bf16 chunk-start state
-    static constexpr int C_OFF = H_OFF + 2 * HBYTES;      // [TT][CP] bf16 C of the chunk
-    static constexpr int TB_OFF = C_OFF + TT * CP * 2;    // 2 x tables
-    static constexpr int W_OFF = TB_OFF + 2 * TFLOATS * 4;     // 2 x diagonal weights
-    static constexpr int MISC_OFF = W_OFF + 2 * WBYTES;        // ints [4]
+    static constexpr int X_OFF = 0;                                // 2 x raw X [TT][64] bf16, swizzled
+    static constexpr int XT_OFF = AGG ? 0 : X_OFF + 2 * XBYTES;    // 2 x X~, same layout
+    static constexpr int H_OFF = XT_OFF + 2 * XBYTES;              // 2 x [64][HP] bf16 chunk-start state
+    static constexpr int C_OFF = H_OFF + (AGG ? 0 : 2 * HBYTES);   // [TT][CP] bf16 C of the chunk
+    static constexpr int TB_OFF = C_OFF + (AGG ? 0 : TT * CP * 2); // 2 x tables
+    static constexpr int W_OFF = TB_OFF + 2 * TFLOATS * 4;         // 2 x diagonal weights
+    static constexpr int MISC_OFF = W_OFF + (AGG ? 0 : 2 * WBYTES);  // ints [4]
     static constexpr int BYTES = MISC_OFF + 64;
     static_assert(BYTES <= 160 * 1024, "LDS of one workgroup");
 };
@@ -245,8 +247,8 @@ __device__ __forceinline__ int fu_xcd_item(int i, int base, int n, int nx) {
 // state from zero and its decay); otherwise the output launch (whole chains,
 // then the segments of split chains from the folded aggregates).
 template <int TT, int S, bool AGG>
-__global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p) {
-    using Lay = FuLayout<TT, S>;
+__device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
+    using Lay = FuLayout<TT, S, AGG>;
     constexpr int NPW = Lay::NPW;
     constexpr int NPTW = Lay::NPTW;
     constexpr int NB = Lay::NB;
@@ -278,29 +280,36 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
     // Output launch: workgroups [0, nwhole) run whole chains, the rest the
     // segments of the split chains; as workgroups start in index order, the
     // long whole chains go first.  Items are chain-major within each list.
+    // Aggregate launch: piece m of segment seg (every segment but a chain's
+    // last), chain-major, so a chain's pieces are consecutive payload slots.
     const int nsplit = p.nchains - p.nwhole;  // chains run as segments
     const int nst = p.nsegs * nsplit;         // segments
+    const int npc = (p.nsegs - 1) * p.agg_d;  // aggregate pieces per split chain
     const int wg = blockIdx.x;
     bool split;
-    int item;
+    int item, seg, chain, c_begin, c_end;
     if constexpr (AGG) {
-        if (wg >= nst) return;
+        if (wg >= nsplit * npc) return;
         split = true;
-        item = fu_xcd_item(wg, 0, nst, p.nxcd);
+        item = fu_xcd_item(wg, 0, nsplit * npc, p.nxcd);  // payload slot
+        chain = p.nwhole + item / npc;
+        seg = (item % npc) / p.agg_d;
+        c_begin = seg * p.seg_chunks + (item % p.agg_d) * p.agg_chunks;
+        const int seg_end = (seg + 1) * p.seg_chunks;
+        c_end = c_begin + p.agg_chunks < seg_end ? c_begin + p.agg_chunks : seg_end;
     } else {
         if (wg >= p.nwhole + nst) return;
         split = wg >= p.nwhole;
         item = split ? fu_xcd_item(wg, p.nwhole, nst, p.nxcd) : fu_xcd_item(wg, 0, p.nwhole, p.nxcd);
+        seg = split ? item % p.nsegs : 0;
+        chain = split ? p.nwhole + item / p.nsegs : item;
+        c_begin = split ? seg * p.seg_chunks : 0;
+        c_end = (split && c_begin + p.seg_chunks < p.nchunks) ? c_begin + p.seg_chunks : p.nchunks;
     }
-    const int seg = split ? item % p.nsegs : 0;
-    const int chain = split ? p.nwhole + item / p.nsegs : item;
-    const int stile = seg * nsplit + (chain - p.nwhole);  // payload slot of a segment
     if (tid == 0) lb_int[2] = 0;
     const int64_t b = chain / p.H;
     const int h = chain % p.H;
     const int g = h / (p.H / p.G);
-    const int c_begin = split ? seg * p.seg_chunks : 0;
-    const int c_end = (split && c_begin + p.seg_chunks < p.nchunks) ? c_begin + p.seg_chunks : p.nchunks;
     const float A2 = p.A[h] * kLog2e;
     const float Dh = p.D ? p.D[h] : 0.0f;
     const int64_t L = p.L;
@@ -806,26 +815,27 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
         fu_static_switch<0, 4 / NPW>(pt0 / NPW, with_pt0);
     };
 
-    float* pay_alpha = p.payload + int64_t(nst) * (kFuCompute * Lay::NACC);  // [nst] segment decays
+    float* pay_alpha = p.payload + int64_t(nsplit) * npc * (kFuCompute * Lay::NACC);  // piece decays
     if constexpr (AGG) {
-        // the segment's aggregate: its state from zero, and its decay
+        // the piece's aggregate: its state from zero, and its decay
 #pragma unroll
         for (int j = 0; j < NPW; ++j) hacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         run_phase(FuPhase<false>{});
         if (!loader) {
-            float* pay = p.payload + int64_t(stile) * (kFuCompute * Lay::NACC) + tid * Lay::NACC;
+            float* pay = p.payload + int64_t(item) * (kFuCompute * Lay::NACC) + tid * Lay::NACC;
 #pragma unroll
             for (int j = 0; j < NPW; ++j) *reinterpret_cast<f32x4*>(pay + 4 * j) = hacc[j];
         }
-        if (tid == 0) pay_alpha[stile] = fexp2(sumG);  // wave 0's (a compute wave)
+        if (tid == 0) pay_alpha[item] = fexp2(sumG);  // wave 0's (a compute wave)
         return;
     } else {
         if (!loader) {
             load_h0(hacc);
-            // a segment starts from h0 folded through its predecessors'
-            // aggregates: h <- alpha_k h + S_k (the aggregate launch has finished)
-            for (int k = 0; k < seg; ++k) {
-                const int t = k * nsplit + (chain - p.nwhole);
+            // a segment starts from h0 folded through the aggregates of the
+            // pieces before it: h <- alpha_k h + S_k (the aggregate launch has
+            // finished)
+            for (int k = 0; k < seg * p.agg_d; ++k) {
+                const int t = (chain - p.nwhole) * npc + k;
                 const float al = pay_alpha[t];
                 const float* src = p.payload + int64_t(t) * (kFuCompute * Lay::NACC) + tid * Lay::NACC;
 #pragma unroll
@@ -842,6 +852,19 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
                     hacc[j];
         }
     }
+}
+
+// The two launches: outputs (one workgroup per CU), and the aggregate pass
+// of split chains (two workgroups per CU: it needs little LDS and few
+// registers).
+template <int TT, int S>
+__global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p) {
+    ssd_fused_body<TT, S, false>(p);
+}
+
+template <int TT, int S>
+__global__ __launch_bounds__(kFuThreads, 2) void ssd_fused_agg_kernel(SsdFusedParams p) {
+    ssd_fused_body<TT, S, true>(p);
 }
 
 }  // namespace cls

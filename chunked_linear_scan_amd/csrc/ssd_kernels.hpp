@@ -54,12 +54,15 @@ struct SsdFusedParams {
     float* h_final;
     const uint16_t* cb;
     const uint16_t* bt;
-    float* payload;      // [nseg tiles][threads][state floats per lane] aggregates, then [nseg tiles] decays
+    float* payload;      // [pieces][threads][state floats per lane] aggregates, then [pieces] decays
     uint32_t* err;
     int64_t batch, L;
     // chains [0, nwhole) run whole; chains [nwhole, nchains) are split into
-    // nsegs segments of seg_chunks chunks (aggregate launch, then output launch)
+    // nsegs segments of seg_chunks chunks.  The aggregate launch covers the
+    // segments but the last of every split chain, as agg_d pieces of at most
+    // agg_chunks chunks per segment.
     int H, G, chunk, nchunks, seg_chunks, nsegs, nchains, nwhole;
+    int agg_d, agg_chunks;
     int nxcd;  // XCDs the workgroups are dealt across (tile mapping only)
 };
 
@@ -69,7 +72,7 @@ constexpr int64_t kFusedMaxChunk = 128;  // longest quadratic block of the fused
 struct SsdFusedPlan {
     bool use;
     int TT, chunk, nsegs, seg_chunks, nchains, nwhole;  // chunk: the sub-chunk the kernel runs
-    int nseg_tiles;                                     // segments of the split chains
+    int agg_d, agg_chunks, npieces;                     // aggregate pieces (see SsdFusedParams)
     size_t payload_off, cb_off, bt_off, bytes;
 };
 
