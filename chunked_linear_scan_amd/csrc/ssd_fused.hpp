@@ -76,7 +76,7 @@ constexpr int kFuWaves = kFuCompute / 64;                    // compute waves
 constexpr int kFuLoaders = 4;                                // loader waves
 constexpr int kFuThreads = kFuCompute + 64 * kFuLoaders;     // workgroup size
 constexpr int kFuP = 64;  // head dim of this kernel
-constexpr uint32_t kFuSpinLimit = 1u << 24;  // bound of the loaders' wait for the C copy
+constexpr uint32_t kFuSpinLimit = 1u << 24;  // bound of the compute waves' wait for the state term
 constexpr float kFuSplitMin = 7.8886091e-31f;  // 2^-100: weakest block decay of the split diagonal form
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -179,9 +179,6 @@ struct FuLayout {
     static constexpr int XBYTES = TT * 128;               // X buffer [TT][64] bf16
     static constexpr int HP = S + 8;                      // bf16 pitch of the state rows
     static constexpr int HBYTES = kFuP * HP * 2;          // one state copy
-    static constexpr int NCL = TT * S / 2048;             // 16-byte C loads per loader lane
-    static constexpr int CROWS = 512 / S;                 // C rows per 1 KB wave load
-    static constexpr int CP = S + 8;                      // bf16 pitch of the C rows
     // per-chunk tables (floats): block-local cumulative decay GL, dt, the split
     // factor U = dt exp2(-GL), the row factor R = exp2(GL), and the block decays Q
     static constexpr int T_GL = 0, T_DT = TT, T_U = 2 * TT, T_R = 3 * TT, T_Q = 4 * TT;
@@ -195,8 +192,11 @@ struct FuLayout {
     static constexpr int X_OFF = 0;                                // 2 x raw X [TT][64] bf16, swizzled
     static constexpr int XT_OFF = AGG ? 0 : X_OFF + 2 * XBYTES;    // 2 x X~, same layout
     static constexpr int H_OFF = XT_OFF + 2 * XBYTES;              // 2 x [64][HP] bf16 chunk-start state
-    static constexpr int C_OFF = H_OFF + (AGG ? 0 : 2 * HBYTES);   // [TT][CP] bf16 C of the chunk
-    static constexpr int TB_OFF = C_OFF + (AGG ? 0 : TT * CP * 2); // 2 x tables
+    // the state term of the chunk, fp32, one 1 KB block per (16-token tile, head-dim
+    // tile) in the MFMA result layout
+    static constexpr int YBYTES = NIT * 4 * 1024;
+    static constexpr int Y_OFF = H_OFF + (AGG ? 0 : 2 * HBYTES);
+    static constexpr int TB_OFF = Y_OFF + (AGG ? 0 : YBYTES);      // 2 x tables
     static constexpr int W_OFF = TB_OFF + 2 * TFLOATS * 4;         // 2 x diagonal weights
     static constexpr int MISC_OFF = W_OFF + (AGG ? 0 : 2 * WBYTES);  // ints [4]
     static constexpr int BYTES = MISC_OFF + 64;
@@ -261,8 +261,8 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
     const int l16 = lane & 15, kg = lane >> 4;
     // bf16 copy of the chunk-start state, double-buffered by chunk parity
     auto hs_buf = [&](int c) { return reinterpret_cast<uint16_t*>(sm + Lay::H_OFF + (c & 1) * Lay::HBYTES); };
-    unsigned char* Cs = sm + Lay::C_OFF;
-    // lb_int[2]: compute waves done with the C copy (running count over the
+    float* Ys = reinterpret_cast<float*>(sm + Lay::Y_OFF);
+    // lb_int[2]: loader waves done with the state term (running count over the
     // output phase)
     int* lb_int = reinterpret_cast<int*>(sm + Lay::MISC_OFF);
 
@@ -367,14 +367,8 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
     for (int m = 0; m < 4; ++m)
         xoff[m] = lblk ? uint32_t(lrow + 8 * m) * xrow_bytes + uint32_t((lane & 7) * 16) : kNoRow;
     const uint32_t dtoff = (lblk && lane < 32) ? uint32_t(32 * lw + lane) * uint32_t(p.H * 4) : kNoRow;
-    uint32_t coff[Lay::NCL];
-#pragma unroll
-    for (int k = 0; k < Lay::NCL; ++k) {
-        const int r = Lay::CROWS * (kFuLoaders * k + lw) + lane / (S / 8);
-        coff[k] = uint32_t(r) * uint32_t(p.G * S * 2) + uint32_t((lane % (S / 8)) * 16);
-    }
     u32x4 dreg[2];
-    u32x4 creg[Lay::NCL];
+    u32x4 cfr[2][KS];  // C^T fragments (MFMA B operand) of the loader's two 16-token tiles
     // X and dt of chunk c into the register set (xreg, dtv) (and, for the
     // output phase, the diagonal C B^T block of the loader's block)
     auto issue_x = [&](int c, auto out_tag, u32x4 (&xreg)[4], float& dtv) {
@@ -496,37 +490,54 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
             *reinterpret_cast<u32x4*>(Wb + r * (Lay::WP * 2) + c0 * 2 + 16) = o[1];
         }
     };
-    // C of chunk c into registers, and from there into the LDS copy
-    auto issue_c = [&](int c) {
+    // S4 state term y^T = H C^T of the loader's block (16-token tiles 2 lw and
+    // 2 lw + 1, every head-dim tile) from the chunk-start state in LDS and C
+    // fragments loaded straight from global memory.  The loaders compute it
+    // while the compute waves run the chunk's block loop; the compute waves add
+    // it, decayed to each row, once their block loop is done.
+    auto issue_cf = [&](int c) {
         const int n = chunk_rows(c);
         const auto rc = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint16_t*>(p.C + ((b * L + int64_t(c) * p.chunk) * p.G + g) * S), 0, n * p.G * S * 2,
             0x00020000);
 #pragma unroll
-        for (int k = 0; k < Lay::NCL; ++k) creg[k] = __builtin_amdgcn_raw_buffer_load_b128(rc, int(coff[k]), 0, 0);
-    };
-    auto store_c = [&]() {
+        for (int it2 = 0; it2 < 2; ++it2) {
+            const uint32_t row = lblk ? uint32_t(32 * lw + 16 * it2 + (lane & 15)) * uint32_t(p.G * S * 2) +
+                                            uint32_t(16 * (lane >> 4))
+                                      : kNoRow;
 #pragma unroll
-        for (int k = 0; k < Lay::NCL; ++k) {
-            const int r = Lay::CROWS * (kFuLoaders * k + lw) + lane / (S / 8);
-            *reinterpret_cast<u32x4*>(Cs + r * (Lay::CP * 2) + (lane % (S / 8)) * 16) = creg[k];
+            for (int ks = 0; ks < KS; ++ks)
+                cfr[it2][ks] = __builtin_amdgcn_raw_buffer_load_b128(rc, int(row + (lblk ? 64 * ks : 0)), 0, 0);
         }
     };
-    // The single C copy is overwritten once every compute wave has read it:
-    // the compute waves count their state terms in lb_int[2], and the loaders
-    // wait for the count instead of for a workgroup barrier, so the compute
-    // waves never wait for the loaders inside a chunk.  The wait is bounded;
-    // running out of it is reported in the error word.
-    auto wait_c_free = [&](int target) {
-        uint32_t spins = 0;
-        while (__hip_atomic_load(lb_int + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
-            if (++spins > kFuSpinLimit) {
-                if (lane == 0) atomic_add_u32(p.err, 1u);
-                break;
+    auto ystate = [&](int c) {
+        if (lblk) {
+            const int l16 = lane & 15, kg = lane >> 4;
+            const uint16_t* Hs = hs_buf(c);
+            f32x4 y[2][4];
+#pragma unroll
+            for (int it2 = 0; it2 < 2; ++it2)
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) y[it2][pt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt) {
+                    const u32x4 hf =
+                        *reinterpret_cast<const u32x4*>(Hs + (16 * pt + l16) * Lay::HP + 32 * ks + 8 * kg);
+                    y[0][pt] = fu_mfma(hf, cfr[0][ks], y[0][pt]);
+                    y[1][pt] = fu_mfma(hf, cfr[1][ks], y[1][pt]);
+                }
             }
-            __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+            for (int it2 = 0; it2 < 2; ++it2)
+#pragma unroll
+                for (int pt = 0; pt < 4; ++pt)
+                    *reinterpret_cast<f32x4*>(Ys + (((2 * lw + it2) * 4 + pt) * 64 + lane) * 4) = y[it2][pt];
+            // written (LDS operations of a wave complete in order): publish
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (lane == 0) __hip_atomic_fetch_add(lb_int + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
-        asm volatile("" ::: "memory");
     };
     // The loader waves' share of a phase, with the same barriers as the compute
     // waves (one per chunk).  X and dt are fetched D chunks ahead into a ring of
@@ -553,29 +564,26 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
             constexpr int sl = decltype(sc)::value;
             issue_x(clampc(c_begin + sl), out_tag, xreg[sl], dtv[sl]);
         });
-        if constexpr (OUT) issue_c(c_begin);
+        if constexpr (OUT) issue_cf(c_begin);
         prep(c_begin & 1, out_tag, xreg[0], dtv[0]);
-        if constexpr (OUT) {
-            prep_w(c_begin & 1);
-            store_c();
-        }
+        if constexpr (OUT) prep_w(c_begin & 1);
         __builtin_amdgcn_sched_barrier(0);
         issue_x(clampc(c_begin + D), out_tag, xreg[0], dtv[0]);
-        if constexpr (OUT) issue_c(clampc(c_begin + 1));
         lds_barrier();
-        // chunk c + 1 into the half chunk c - 1 used (free since the last
-        // barrier) while the compute waves work on chunk c
+        // the state term of chunk c first (the compute waves wait for it at the
+        // end of their block loop), then chunk c + 1 into the half chunk c - 1
+        // used (free since the last barrier)
         auto step = [&](auto kc, int c) {
             constexpr int sl = (decltype(kc)::value + 1) % D;  // set of chunk c + 1
-            prep((c + 1) & 1, out_tag, xreg[sl], dtv[sl]);
             if constexpr (OUT) {
-                prep_w((c + 1) & 1);
-                wait_c_free(kFuWaves * (c - c_begin + 1));
-                store_c();  // C of chunk c + 1
+                ystate(c);
+                __builtin_amdgcn_sched_barrier(0);
+                issue_cf(clampc(c + 1));
             }
+            prep((c + 1) & 1, out_tag, xreg[sl], dtv[sl]);
+            if constexpr (OUT) prep_w((c + 1) & 1);
             __builtin_amdgcn_sched_barrier(0);
             issue_x(clampc(c + 1 + D), out_tag, xreg[sl], dtv[sl]);
-            if constexpr (OUT) issue_c(clampc(c + 2));
             lds_barrier();  // chunk c + 1 ready; chunk c's half free
             __builtin_amdgcn_sched_barrier(0);  // the next step's waits stay after the barrier
         };
@@ -617,6 +625,20 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
     u32x4 rA[RA > 0 ? RA : 1], rB[RB > 0 ? RB : 1];  // off-diagonal CB fragments of the output tiles
     float sumG = 0.0f;
 
+    // The compute waves wait for the loaders' state term of a chunk (a running
+    // count of the loader waves that have written theirs).  The wait is
+    // bounded; running out of it is reported in the error word.
+    auto wait_ystate = [&](int target) {
+        uint32_t spins = 0;
+        while (__hip_atomic_load(lb_int + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) < target) {
+            if (++spins > kFuSpinLimit) {
+                if (lane == 0) atomic_add_u32(p.err, 1u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");
+    };
     auto run_chunks = [&](auto out_tag, auto pt0_c, auto ptb_c) {
         constexpr bool OUT = decltype(out_tag)::value;
         constexpr int PT0 = decltype(pt0_c)::value * NPW;
@@ -658,8 +680,8 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
             const char* cbx = cb_base(cx);
             const char* btx = bt_base(cx);
 
-            // S4 state term y^T += H C^T from the chunk-start state and the
-            // chunk's C (both bf16 in LDS)
+            // intra-chunk outputs from zero; the state term is added after the
+            // block loop
             f32x4 accA[NPTW], accB[NPTW];
             if constexpr (OUT) {
 #pragma unroll
@@ -667,26 +689,6 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
                     accA[q] = f32x4{0.f, 0.f, 0.f, 0.f};
                     accB[q] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
-                if (has_out) {
-                    const uint16_t* Hs = hs_buf(c);
-                    const unsigned char* cra = Cs + (16 * itA + l16) * (Lay::CP * 2) + 16 * kg;
-                    const unsigned char* crb = Cs + (16 * itB + l16) * (Lay::CP * 2) + 16 * kg;
-#pragma unroll
-                    for (int ks = 0; ks < KS; ++ks) {
-                        const u32x4 ca = *reinterpret_cast<const u32x4*>(cra + 64 * ks);
-                        const u32x4 cb = *reinterpret_cast<const u32x4*>(crb + 64 * ks);
-#pragma unroll
-                        for (int q = 0; q < NPTW; ++q) {
-                            const u32x4 hf = *reinterpret_cast<const u32x4*>(
-                                Hs + (16 * (PTB + q) + l16) * Lay::HP + 32 * ks + 8 * kg);
-                            accA[q] = fu_mfma(hf, ca, accA[q]);
-                            accB[q] = fu_mfma(hf, cb, accB[q]);
-                        }
-                    }
-                }
-                // the C copy has been read (its loads have returned): the loaders may refill it
-                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                if (lane == 0) __hip_atomic_fetch_add(lb_int + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
             } else {
 #pragma unroll
                 for (int bb = 0; bb < NB; ++bb) sumG += T[Lay::T_GL + 32 * bb + 31];  // log2 decay of the chunk
@@ -759,6 +761,20 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
 
             if constexpr (OUT) {
                 if (has_out) {
+                    // S4: add the loaders' state term C_i h^T, decayed from the chunk
+                    // start to row i: exp2 of the row's cumulative log decay, as the
+                    // block decays before its block times exp2(GL_i)
+                    wait_ystate(NB * (c - c_begin + 1));
+                    auto add_state = [&](f32x4 (&acc)[NPTW], int it) {
+                        const int i = 16 * it + l16;
+                        float f = T[Lay::T_R + i];
+                        for (int bb = 0; bb < (it >> 1); ++bb) f *= T[Lay::T_Q + bb];
+#pragma unroll
+                        for (int q = 0; q < NPTW; ++q)
+                            acc[q] += *reinterpret_cast<const f32x4*>(Ys + ((it * 4 + PTB + q) * 64 + lane_c) * 4) * f;
+                    };
+                    add_state(accA, itA);
+                    add_state(accB, itB);
                     auto store_y = [&](const f32x4 (&acc)[NPTW], int it) {
                         const int i = 16 * it + l16;
                         uint16_t* row = p.y + ((b * L + tok0 + i) * p.H + h) * kFuP;
