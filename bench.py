@@ -87,6 +87,55 @@ def measured_traffic(kernel_key, sources, launches_per_step=1):
     return rec.get("hbm_bytes_per_launch")
 
 
+SSD_SOURCES = ["ssd_fused.hpp", "ssd_fused.hip", "common.hpp", "ssd_kernels.hpp"]
+SCAN_SOURCES = ["linear_scan.hip", "common.hpp"]
+
+
+def record_traffic(fetch_csv, write_csv, workload):
+    """Write profiles/traffic.json from two rocprofv3 --pmc runs of this script
+    with --copy-probe (one with FETCH_SIZE, one with WRITE_SIZE).  Each counter
+    is scaled by what it reads for the 1 GiB device copies of --copy-probe
+    (copyBuffer dispatches of 131072 workgroups), per dispatch of each kernel."""
+    import csv
+    import statistics
+
+    def read(path, name):
+        d = {}
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                if r["Counter_Name"] == name:
+                    d.setdefault((r["Kernel_Name"], r["Grid_Size"]), []).append(float(r["Counter_Value"]))
+        return d
+
+    fe, wr = read(fetch_csv, "FETCH_SIZE"), read(write_csv, "WRITE_SIZE")
+    copy_f = [v for (k, g), vs in fe.items() if "copyBuffer" in k and g == "131072" for v in vs]
+    copy_w = [v for (k, g), vs in wr.items() if "copyBuffer" in k and g == "131072" for v in vs]
+    if not copy_f or not copy_w:
+        raise SystemExit("no 1 GiB copy dispatches in the counter files (run bench.py with --copy-probe)")
+    sf = 1048576.0 / statistics.mean(copy_f)  # counters read KiB
+    sw = 1048576.0 / statistics.mean(copy_w)
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    db = {}
+    if os.path.exists(path):
+        with open(path) as f:
+            db = json.load(f)
+    for key, srcs, pat in [("ssd_fused_kernel:" + workload, SSD_SOURCES, "ssd_fused_kernel<"),
+                           ("ssd_fused_agg_kernel:" + workload, SSD_SOURCES, "ssd_fused_agg_kernel<"),
+                           ("linear_scan:scan", SCAN_SOURCES, "linear_scan_kernel")]:
+        f = [v for (k, g), vs in fe.items() if pat in k for v in vs]
+        w = [v for (k, g), vs in wr.items() if pat in k for v in vs]
+        if not f or not w:
+            continue
+        fb = statistics.mean(f) * sf * 1024
+        wb = statistics.mean(w) * sw * 1024
+        db[key] = {"source_digest": source_digest(srcs), "hbm_bytes_per_launch": round(fb + wb),
+                   "fetch_bytes": round(fb), "write_bytes": round(wb), "dispatches": len(f),
+                   "scale_fetch": round(sf, 4), "scale_write": round(sw, 4)}
+        print(key, db[key])
+    with open(path, "w") as f:
+        json.dump(db, f, indent=1, sort_keys=True)
+
+
 def time_loop(fn, nsets, steps, warmup, stream, before_timed=None):
     import torch
     for i in range(warmup):
@@ -215,13 +264,14 @@ def bench_ssd(name, steps, warmup, want_cpu):
     gbs = alg_bytes / t_kernel / 1e9
     tflops = flops / t_kernel / 1e12
     t_roof = max(alg_bytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12))
-    srcs = ["ssd_fused.hpp", "ssd_fused.hip", "common.hpp", "ssd_kernels.hpp"]
+    srcs = SSD_SOURCES
     res = {
         "t": t, "tokens_per_s": tokens / t, "alg_bytes": alg_bytes, "alg_flops": flops,
         "gbs": gbs, "tflops": tflops, "nsets": nsets,
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("ssd_fused_kernel:" + name, srcs),
+                     "aggregate_pass_traffic": measured_traffic("ssd_fused_agg_kernel:" + name, srcs),
                      "kernel": "ssd_fused_kernel (output launch)" if t_fused else "whole ssd_fwd call",
                      "kernel_us": round(t_kernel * 1e6, 2),
                      "cb_pass_us": None if t_cb is None else round(t_cb * 1e6, 2),
@@ -262,7 +312,7 @@ def bench_scan(name, steps, warmup, want_cpu):
            "us_per_call": round(t * 1e6, 2), "nsets": nsets,
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(gbs / HBM_PEAK_GBS, 4),
-                        "traffic": measured_traffic("linear_scan:" + name, ["linear_scan.hip", "common.hpp"])}}
+                        "traffic": measured_traffic("linear_scan:" + name, SCAN_SOURCES)}}
     if want_cpu:
         res["cpu_baseline"] = cpu_baseline_scan(inp)
     return res
@@ -281,7 +331,13 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run three plain 1 GiB device copies (the known-size reference that "
                          "scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write profiles/traffic.json from two rocprofv3 --pmc counter files of "
+                         "--copy-probe runs (FETCH_SIZE, WRITE_SIZE) for --workload, then exit")
     args = ap.parse_args()
+    if args.record_traffic:
+        record_traffic(args.record_traffic[0], args.record_traffic[1], args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (got --gpus {args.gpus}); run it with --gpus 1",
               file=sys.stderr)
