@@ -703,13 +703,22 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
                 fu_load_xf<2, PT0, NPW, PTB, NPTW, OUT>(dst, Xt, trx, l16);
                 fu_load_xf<3, PT0, NPW, PTB, NPTW, OUT>(dst, Xt, trx, l16);
             };
-            u32x4 xf[4], xfn[4];
-            load_xf(xf, 8 * kg + (l16 >> 2));
+            // X~ fragments XD blocks ahead (a ring of XD + 1 sets; the block loop is
+            // unrolled, so the set indices are static) and all block decays at once.
+            // Two blocks ahead measured no faster than one.
+            constexpr int XD = 1;
+            u32x4 xs[XD + 1][4];
+            fu_static_for<0, XD>([&](auto kc) {
+                constexpr int k = decltype(kc)::value;
+                if constexpr (k < NB) load_xf(xs[k], 32 * k + 8 * kg + (l16 >> 2));
+            });
+            const f32x4 qall = *reinterpret_cast<const f32x4*>(T + Lay::T_Q);
             fu_static_for<0, NB>([&](auto jbc) {
                 constexpr int jb = decltype(jbc)::value;
                 const int trx = 32 * jb + 8 * kg + (l16 >> 2);
-                if constexpr (jb + 1 < NB) load_xf(xfn, trx + 32);
-                const float qv = T[Lay::T_Q + jb];
+                if constexpr (jb + XD < NB) load_xf(xs[(jb + XD) % (XD + 1)], trx + 32 * XD);
+                u32x4 (&xf)[4] = xs[jb % (XD + 1)];
+                const float qv = qall[jb];
 #pragma unroll
                 for (int j = 0; j < NPW; ++j) hacc[j] = fu_mfma(btr[jb], xf[PT0 + j], hacc[j] * qv);
                 if constexpr (OUT) {
@@ -752,10 +761,6 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
                         if constexpr (jb < RA) rA[jb] = ldg_b128(cbx + cbA_lane + 64 * jb);
                         if constexpr (jb < RB) rB[jb] = ldg_b128(cbx + cbB_lane + 64 * jb);
                     }
-                }
-                if constexpr (jb + 1 < NB) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) xf[q] = xfn[q];
                 }
             });
 
@@ -811,13 +816,14 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
     // the wave's head-dim offsets become compile-time constants (static register indices)
     auto run_phase = [&](auto out_tag) {
         if (loader) {
-            // The loaders' work is short but on the path of every chunk: without a
-            // higher issue priority the older compute waves sharing their SIMD win
-            // every arbitration and the loaders' loads and arithmetic wait for
-            // the compute waves' block loop to drain.
-            __builtin_amdgcn_s_setprio(3);
+            // In the aggregate pass the loaders' work is on the path of every
+            // (short) chunk: without a higher issue priority the compute waves
+            // sharing their SIMD win every arbitration.  In the output pass the
+            // loaders finish well before the compute waves, and a raised priority
+            // only takes issue slots from them (measured 3 % slower).
+            if constexpr (!decltype(out_tag)::value) __builtin_amdgcn_s_setprio(3);
             run_loader(out_tag);
-            __builtin_amdgcn_s_setprio(0);
+            if constexpr (!decltype(out_tag)::value) __builtin_amdgcn_s_setprio(0);
             return;
         }
         auto with_pt0 = [&](auto pt0_c) {
@@ -879,7 +885,8 @@ __global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p)
 }
 
 template <int TT, int S>
-__global__ __launch_bounds__(kFuThreads, 2) void ssd_fused_agg_kernel(SsdFusedParams p) {
+__global__ __launch_bounds__(kFuThreads) __attribute__((amdgpu_waves_per_eu(6, 6))) void ssd_fused_agg_kernel(
+    SsdFusedParams p) {
     ssd_fused_body<TT, S, true>(p);
 }
 
