@@ -8,14 +8,26 @@ namespace cls {
 // S2a for the fused kernel: one workgroup (4 waves) per (batch, chunk, group).
 // Writes CB[i][j] = sum_s C[i][s] B[j][s] for the 32-token blocks with
 // block(j) <= block(i) (the only ones the fused kernel reads) and the
-// token-contiguous copy B^T[s][t].  C and B rows are read through buffer loads
-// whose range ends at the chunk's last real token, so padded rows read as
-// zeros.  Wave w takes the 16-row tiles k and NIT-1-k (k = w, w + 4, ..), which
-// gives every wave the same number of tiles of the triangle.
+// token-contiguous copy B^T[s][t].  The chunk's B rows are staged in LDS once
+// (every load issued at once, so the workgroup waits out one memory latency);
+// each wave loads the C rows of its two 16-row tiles k and NIT-1-k straight
+// into registers, which gives every wave the same share of the triangle.  C
+// and B rows are read through buffer loads whose range ends at the chunk's
+// last real token, so padded rows read as zeros.
+template <int TT, int S>
+struct CbtLayout {
+    static constexpr int BP = S + 8;                 // bf16 pitch of the staged B rows
+    static constexpr int BYTES = TT * BP * 2;
+};
+
 template <int TT, int S>
 __global__ __launch_bounds__(kBfThreads) void ssd_cbt_kernel(SsdBf16Params p) {
+    using Lay = CbtLayout<TT, S>;
     constexpr int KS = S / 32;
     constexpr int NIT = TT / 16;
+    constexpr int CPR = S / 8;  // 16-byte pieces per row
+    extern __shared__ __attribute__((aligned(16))) unsigned char cbt_sm[];
+    uint16_t* sB = reinterpret_cast<uint16_t*>(cbt_sm);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kg = lane >> 4;
     const int64_t bcg = blockIdx.x;
@@ -30,44 +42,70 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cbt_kernel(SsdBf16Params p) {
                                                       0x00020000);
     const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.B + base), 0, int(uint32_t(n) * rowb),
                                                       0x00020000);
-    uint16_t* out = p.cb + bcg * (TT * TT);
-    auto load_rows = [&](const __amdgpu_buffer_rsrc_t& r, int row, u32x4 (&dst)[KS]) {
+    // B rows into LDS: piece q of the tile is row q / CPR, 16 bytes (q % CPR)
+    constexpr int NBQ = TT * CPR / kBfThreads;
+    u32x4 bq[NBQ];
+#pragma unroll
+    for (int k = 0; k < NBQ; ++k) {
+        const int q = tid + kBfThreads * k;
+        bq[k] = __builtin_amdgcn_raw_buffer_load_b128(rb, int(uint32_t(q / CPR) * rowb + 16 * (q % CPR)), 0, 0);
+    }
+    // the C rows of this wave's tiles (MFMA B operand: row 16 it + l16, states 32 ks + 8 kg ..)
+    const bool has_tiles = wave < NIT / 2;
+    u32x4 cf[2][KS];
+#pragma unroll
+    for (int side = 0; side < 2; ++side) {
+        const int it = side ? NIT - 1 - wave : wave;
+        const uint32_t row = has_tiles ? uint32_t(16 * it + l16) * rowb + 16 * kg : 0x7ffffff0u;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            dst[ks] = __builtin_amdgcn_raw_buffer_load_b128(r, int(uint32_t(row) * rowb + 64 * ks + 16 * kg), 0, 0);
-    };
-    for (int k = wave; k < NIT / 2; k += 4) {
+            cf[side][ks] = __builtin_amdgcn_raw_buffer_load_b128(rc, int(row + (has_tiles ? 64 * ks : 0)), 0, 0);
+    }
+#pragma unroll
+    for (int k = 0; k < NBQ; ++k) {
+        const int q = tid + kBfThreads * k;
+        *reinterpret_cast<u32x4*>(sB + (q / CPR) * Lay::BP + 8 * (q % CPR)) = bq[k];
+    }
+    __syncthreads();
+
+    uint16_t* out = p.cb + bcg * (TT * TT);
+    if (has_tiles) {
 #pragma unroll
         for (int side = 0; side < 2; ++side) {
-            const int it = side ? NIT - 1 - k : k;
-            const int jmax = 2 * (it >> 1) + 1;  // last 16-column tile of the blocks <= block(it)
-            u32x4 cf[KS], bcur[KS], bnxt[KS];
-            load_rows(rc, 16 * it + l16, cf);
-            load_rows(rb, l16, bcur);
-            for (int jt = 0; jt <= jmax; ++jt) {
-                if (jt < jmax) load_rows(rb, 16 * (jt + 1) + l16, bnxt);
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const int it = side ? NIT - 1 - wave : wave;
+            const int ntj = 2 * (it >> 1) + 2;  // 16-column tiles of the blocks <= block(it), even
+            const int i = 16 * it + l16;
+            for (int jt = 0; jt < ntj; jt += 2) {
+                // lane holds CB[i][16 jt' + 4 kg + r], r = 0..3, for jt' = jt, jt + 1
+                f32x4 acc[2];
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(bcur[ks], cf[ks], acc);
-                // lane holds CB[i][16 jt + 4 kg + r], r = 0..3
-                u32x2 v;
-                v[0] = pack_bf16x2(acc[0], acc[1]);
-                v[1] = pack_bf16x2(acc[2], acc[3]);
-                *reinterpret_cast<u32x2*>(out + (16 * it + l16) * TT + 16 * jt + 4 * kg) = v;
+                for (int h2 = 0; h2 < 2; ++h2) {
+                    acc[h2] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    const uint16_t* brow = sB + (16 * (jt + h2) + l16) * Lay::BP + 8 * kg;
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks) bcur[ks] = bnxt[ks];
+                    for (int ks = 0; ks < KS; ++ks)
+                        acc[h2] = mfma16x16x32(*reinterpret_cast<const u32x4*>(brow + 32 * ks), cf[side][ks], acc[h2]);
+                }
+                // lanes kg, kg ^ 1 trade halves: each lane then holds 8 consecutive
+                // columns of row i, for one tile of the pair
+                const uint32_t e0 = pack_bf16x2(acc[0][0], acc[0][1]), e1 = pack_bf16x2(acc[0][2], acc[0][3]);
+                const uint32_t o0 = pack_bf16x2(acc[1][0], acc[1][1]), o1 = pack_bf16x2(acc[1][2], acc[1][3]);
+                const auto s0 = __builtin_amdgcn_permlane16_swap(e0, o0, false, false);
+                const auto s1 = __builtin_amdgcn_permlane16_swap(e1, o1, false, false);
+                const int jtile = jt + (kg & 1);
+                *reinterpret_cast<u32x4*>(out + i * TT + 16 * jtile + 8 * (kg >> 1)) = u32x4{s0[0], s1[0], s0[1], s1[1]};
             }
         }
     }
-    // B^T: item u covers tokens 8 tg .. 8 tg + 7 and states 8 sg .. 8 sg + 7,
-    // moved as eight 16-byte rows and transposed in registers
+    // B^T from the staged rows: thread u transposes the 8 x 8 block (tokens
+    // 8 tg .., states 8 sg ..); the 16 threads of an sg write one B^T row run
+    // of 256 contiguous bytes per store
     uint16_t* bt = p.bt + bcg * (int64_t(S) * TT);
     for (int u = tid; u < (TT / 8) * (S / 8); u += kBfThreads) {
-        const int tg = u / (S / 8), sg = u % (S / 8);
+        const int tg = u % (TT / 8), sg = u / (TT / 8);
         u32x4 rows[8], cols[8];
 #pragma unroll
-        for (int r = 0; r < 8; ++r)
-            rows[r] = __builtin_amdgcn_raw_buffer_load_b128(rb, int(uint32_t(8 * tg + r) * rowb + 16 * sg), 0, 0);
+        for (int r = 0; r < 8; ++r) rows[r] = *reinterpret_cast<const u32x4*>(sB + (8 * tg + r) * Lay::BP + 8 * sg);
         transpose8x8_b16(rows, cols);
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc) *reinterpret_cast<u32x4*>(bt + (8 * sg + cc) * TT + 8 * tg) = cols[cc];
@@ -81,7 +119,9 @@ static int launch_fused_tpl(const SsdBf16Params& cbp, const SsdFusedParams& fp, 
     using LayA = FuLayout<TT, S, true>;
     static bool attr_set = false;
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_kernel<TT, S>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_cbt_kernel<TT, S>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, CbtLayout<TT, S>::BYTES) != hipSuccess ||
+            hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_kernel<TT, S>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, Lay::BYTES) != hipSuccess ||
             hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_agg_kernel<TT, S>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, LayA::BYTES) != hipSuccess)
@@ -94,7 +134,8 @@ static int launch_fused_tpl(const SsdBf16Params& cbp, const SsdFusedParams& fp, 
     const dim3 bcb{uint32_t(kBfThreads), 1u, 1u};
     const dim3 bmain{uint32_t(kFuThreads), 1u, 1u};
     if (ev) (void)hipEventRecord(ev[0], stream);
-    hipLaunchKernelGGL((ssd_cbt_kernel<TT, S>), gcb, bcb, 0, stream, cbp);
+    constexpr unsigned cbt_lds = CbtLayout<TT, S>::BYTES;
+    hipLaunchKernelGGL((ssd_cbt_kernel<TT, S>), gcb, bcb, cbt_lds, stream, cbp);
     if (ev) (void)hipEventRecord(ev[1], stream);
     if (npieces > 0) {
         const dim3 gagg{uint32_t(npieces), 1u, 1u};

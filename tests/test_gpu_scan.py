@@ -46,7 +46,7 @@ def test_full_workload(name):
 @pytest.mark.parametrize("rows,L", [
     (1, 1), (3, 1), (5, 2), (7, 3), (2, 4), (4, 5), (3, 31), (3, 32), (3, 33), (1, 4089), (2, 4090),
     (2, 4091), (2, 4093), (2, 4096), (2, 4097), (3, 8185), (2, 8186), (2, 8187), (3, 8191), (3, 8192),
-    (3, 8193), (2, 16383), (2, 16385), (1, 65533),
+    (3, 8193), (2, 16383), (2, 16384), (2, 16385), (3, 24576), (3, 24580), (1, 65533),
     (5, 12345), (1000, 7), (257, 129)])
 def test_edge_sizes(rows, L):
     w = workloads.make_scan_inputs(rows, L, seed=rows * 7919 + L)
