@@ -191,12 +191,15 @@ struct FuLayout {
     static constexpr int RB = NB - 1;                     // off-diagonal blocks tile B can reach
     static constexpr int X_OFF = 0;                                // 2 x raw X [TT][64] bf16, swizzled
     static constexpr int XT_OFF = AGG ? 0 : X_OFF + 2 * XBYTES;    // 2 x X~, same layout
-    static constexpr int H_OFF = XT_OFF + 2 * XBYTES;              // 2 x [64][HP] bf16 chunk-start state
+    static constexpr int H_OFF = XT_OFF + 2 * XBYTES;              // [64][HP] bf16 chunk-start state
     // the state term of the chunk, fp32, one 1 KB block per (16-token tile, head-dim
     // tile) in the MFMA result layout
     static constexpr int YBYTES = NIT * 4 * 1024;
-    static constexpr int Y_OFF = H_OFF + (AGG ? 0 : 2 * HBYTES);
-    static constexpr int TB_OFF = Y_OFF + (AGG ? 0 : YBYTES);      // 2 x tables
+    static constexpr int Y_OFF = H_OFF + (AGG ? 0 : HBYTES);
+    // the chunk's bf16 outputs [TT][64], staged for the loaders' stores; 16-byte piece
+    // k of row r sits at k ^ (r & 7), so 8 rows written or read at once use every bank
+    static constexpr int YO_OFF = Y_OFF + (AGG ? 0 : YBYTES);
+    static constexpr int TB_OFF = YO_OFF + (AGG ? 0 : TT * 128);   // 2 x tables
     static constexpr int W_OFF = TB_OFF + 2 * TFLOATS * 4;         // 2 x diagonal weights
     static constexpr int MISC_OFF = W_OFF + (AGG ? 0 : 2 * WBYTES);  // ints [4]
     static constexpr int BYTES = MISC_OFF + 64;
@@ -259,8 +262,9 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
     const bool loader = wave >= kFuWaves;
     const int lw = wave - kFuWaves;                               // loader index (loader waves)
     const int l16 = lane & 15, kg = lane >> 4;
-    // bf16 copy of the chunk-start state, double-buffered by chunk parity
-    auto hs_buf = [&](int c) { return reinterpret_cast<uint16_t*>(sm + Lay::H_OFF + (c & 1) * Lay::HBYTES); };
+    // bf16 copy of the chunk-start state (one copy: the compute waves write the
+    // next chunk's only after every loader has read this chunk's, see below)
+    auto hs_buf = [&](int) { return reinterpret_cast<uint16_t*>(sm + Lay::H_OFF); };
     float* Ys = reinterpret_cast<float*>(sm + Lay::Y_OFF);
     // lb_int[2]: loader waves done with the state term (running count over the
     // output phase)
@@ -510,8 +514,32 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
                 cfr[it2][ks] = __builtin_amdgcn_raw_buffer_load_b128(rc, int(row + (lblk ? 64 * ks : 0)), 0, 0);
         }
     };
+    // The outputs of a chunk, staged in LDS by the compute waves, are stored by
+    // the loader waves during the next chunk, as whole 128-byte rows: 16-byte
+    // pieces m = 0..3 of the loader's block (rows lrow + 8 m, the X piece layout),
+    // through a buffer range that ends at the chunk's last real row.
+    auto read_yo = [&](u32x4 (&yo)[4]) {
+        const unsigned char* Yo = sm + Lay::YO_OFF;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const int r = lrow + 8 * m, cc = lane & 7;
+            yo[m] = *reinterpret_cast<const u32x4*>(Yo + r * 128 + ((cc ^ (r & 7)) << 4));
+        }
+    };
+    auto y_rsrc = [&](int cy, int rows) {
+        return __builtin_amdgcn_make_buffer_rsrc(p.y + ((b * L + int64_t(cy) * p.chunk) * p.H + h) * kFuP, 0,
+                                                 int(uint32_t(rows) * xrow_bytes), 0x00020000);
+    };
+    // the state term of chunk c; the previous chunk's staged outputs are read
+    // first (before the count that lets the compute waves overwrite them) and
+    // stored one piece per 32-state step of the product, so the stores leave
+    // under its LDS waits instead of in one burst that holds up the loads
+    // issued after them
     auto ystate = [&](int c) {
         if (lblk) {
+            u32x4 yo[4];
+            read_yo(yo);
+            const auto ry = y_rsrc(c > c_begin ? c - 1 : c, c > c_begin ? chunk_rows(c - 1) : 0);
             const int l16 = lane & 15, kg = lane >> 4;
             const uint16_t* Hs = hs_buf(c);
             f32x4 y[2][4];
@@ -528,6 +556,10 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
                     y[0][pt] = fu_mfma(hf, cfr[0][ks], y[0][pt]);
                     y[1][pt] = fu_mfma(hf, cfr[1][ks], y[1][pt]);
                 }
+#pragma unroll
+                for (int m = ks * 4 / KS; m < (ks + 1) * 4 / KS; ++m)
+                    __builtin_amdgcn_raw_buffer_store_b128(yo[m], ry, int(xoff[m]), 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
             for (int it2 = 0; it2 < 2; ++it2)
@@ -600,6 +632,15 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
         }
         if constexpr (D == 2) {
             if (c < c_end) step(std::integral_constant<int, 0>{}, c);
+        }
+        if constexpr (OUT) {
+            if (lblk) {  // the last chunk's outputs
+                u32x4 yo[4];
+                read_yo(yo);
+                const auto ry = y_rsrc(last, chunk_rows(last));
+#pragma unroll
+                for (int m = 0; m < 4; ++m) __builtin_amdgcn_raw_buffer_store_b128(yo[m], ry, int(xoff[m]), 0, 0);
+            }
         }
     };
 
@@ -765,11 +806,14 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
             });
 
             if constexpr (OUT) {
+                // every loader is done with this chunk's state copy and with the
+                // previous chunk's staged outputs once it has published its state
+                // term: the waves without outputs wait too, as they rewrite the copy
+                wait_ystate(NB * (c - c_begin + 1));
                 if (has_out) {
                     // S4: add the loaders' state term C_i h^T, decayed from the chunk
                     // start to row i: exp2 of the row's cumulative log decay, as the
                     // block decays before its block times exp2(GL_i)
-                    wait_ystate(NB * (c - c_begin + 1));
                     auto add_state = [&](f32x4 (&acc)[NPTW], int it) {
                         const int i = 16 * it + l16;
                         float f = T[Lay::T_R + i];
@@ -780,9 +824,10 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
                     };
                     add_state(accA, itA);
                     add_state(accB, itB);
+                    // the bf16 outputs into the LDS stage the loaders store from
                     auto store_y = [&](const f32x4 (&acc)[NPTW], int it) {
                         const int i = 16 * it + l16;
-                        uint16_t* row = p.y + ((b * L + tok0 + i) * p.H + h) * kFuP;
+                        unsigned char* yrow = sm + Lay::YO_OFF + i * 128;
                         u32x2 d[NPTW];
 #pragma unroll
                         for (int q = 0; q < NPTW; ++q) {
@@ -796,19 +841,19 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
                             for (int q = 0; q < NPTW; q += 2) {
                                 const auto s0 = __builtin_amdgcn_permlane16_swap(d[q][0], d[q + 1][0], false, false);
                                 const auto s1 = __builtin_amdgcn_permlane16_swap(d[q][1], d[q + 1][1], false, false);
-                                const int pt = PTB + ((kg & 1) ? q + 1 : q);
-                                if (i < n)
-                                    *reinterpret_cast<u32x4*>(row + 16 * pt + 8 * (kg >> 1)) =
-                                        u32x4{s0[0], s1[0], s0[1], s1[1]};
+                                const int e = 16 * (PTB + ((kg & 1) ? q + 1 : q)) + 8 * (kg >> 1);
+                                *reinterpret_cast<u32x4*>(yrow + (((e >> 3) ^ (i & 7)) << 4)) =
+                                    u32x4{s0[0], s1[0], s0[1], s1[1]};
                             }
                         } else {
-                            if (i < n) *reinterpret_cast<u32x2*>(row + 16 * PTB + 4 * kg) = d[0];
+                            const int e = 16 * PTB + 4 * kg;
+                            *reinterpret_cast<u32x2*>(yrow + (((e >> 3) ^ (i & 7)) << 4) + (e & 7) * 2) = d[0];
                         }
                     };
                     store_y(accA, itA);
                     store_y(accB, itB);
                 }
-                store_hs(c + 1, l16, kg);  // into the other copy: this chunk's is still being read
+                store_hs(c + 1, l16, kg);
             }
             lds_barrier();  // the next chunk's state copy, X, X~ and tables are complete
         }
