@@ -117,7 +117,8 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     const size_t pay = size_t(npieces) * (size_t(ssd_fused_state_floats(int(S))) + 1) * 4;
     pl.cb_off = pl.payload_off + up(pay);
     pl.bt_off = pl.cb_off + up(size_t(batch) * size_t(nc) * size_t(G) * size_t(TT) * TT * 2);
-    pl.bytes = pl.bt_off + size_t(batch) * size_t(nc) * size_t(G) * size_t(S) * TT * 2;
+    pl.cf_off = pl.bt_off + up(size_t(batch) * size_t(nc) * size_t(G) * size_t(S) * TT * 2);
+    pl.bytes = pl.cf_off + size_t(batch) * size_t(nc) * size_t(G) * size_t(S) * TT * 2;
     return pl;
 }
 
@@ -273,6 +274,7 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
         char* ws = static_cast<char*>(a.workspace);
         p.cb = reinterpret_cast<uint16_t*>(ws + pl.cb_off);
         p.bt = reinterpret_cast<uint16_t*>(ws + pl.bt_off);
+        p.cf = reinterpret_cast<uint16_t*>(ws + pl.cf_off);
         cls::SsdFusedParams f{};
         f.x = p.x;
         f.dt = p.dt;
@@ -285,6 +287,7 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
         f.h_final = p.h_final;
         f.cb = p.cb;
         f.bt = p.bt;
+        f.cf = p.cf;
         f.payload = reinterpret_cast<float*>(ws + pl.payload_off);
         f.err = reinterpret_cast<uint32_t*>(ws);
         f.batch = s.batch;

@@ -7,8 +7,13 @@ namespace cls {
 
 // S2a for the fused kernel: one workgroup (4 waves) per (batch, chunk, group).
 // Writes CB[i][j] = sum_s C[i][s] B[j][s] for the 32-token blocks with
-// block(j) <= block(i) (the only ones the fused kernel reads) and the
-// token-contiguous copy B^T[s][t].  The chunk's B rows are staged in LDS once
+// block(j) <= block(i) (the only ones the fused kernel reads), B^T[s][t], and
+// a copy of the chunk's C rows, all three fragment-major: the MFMA operand
+// fragment (16-row tile m, 32-column block k) holds row 16 m + l of the
+// operand, columns 32 k + 8 g .. + 7, in lane l + 16 g, and is stored as 64
+// lanes x 16 bytes at fragment index m * (columns / 32) + k.  A wave of the
+// fused kernel then loads a fragment as 1 KB in lane order (its cache
+// accesses are a quarter of what a row-major tile needs).  The chunk's B rows are staged in LDS once
 // (every load issued at once, so the workgroup waits out one memory latency);
 // each wave loads the C rows of its two 16-row tiles k and NIT-1-k straight
 // into registers, which gives every wave the same share of the triangle.  C
@@ -42,6 +47,7 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cbt_kernel(SsdBf16Params p) {
                                                       0x00020000);
     const auto rb = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(p.B + base), 0, int(uint32_t(n) * rowb),
                                                       0x00020000);
+    constexpr int NB = TT / 32;
     // B rows into LDS: piece q of the tile is row q / CPR, 16 bytes (q % CPR)
     constexpr int NBQ = TT * CPR / kBfThreads;
     u32x4 bq[NBQ];
@@ -65,6 +71,17 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cbt_kernel(SsdBf16Params p) {
     for (int k = 0; k < NBQ; ++k) {
         const int q = tid + kBfThreads * k;
         *reinterpret_cast<u32x4*>(sB + (q / CPR) * Lay::BP + 8 * (q % CPR)) = bq[k];
+    }
+    // the C fragments, as loaded (rows past the chunk's end are zeros)
+    if (has_tiles) {
+        uint16_t* cfo = p.cf + bcg * (int64_t(TT) * S);
+#pragma unroll
+        for (int side = 0; side < 2; ++side) {
+            const int it = side ? NIT - 1 - wave : wave;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                *reinterpret_cast<u32x4*>(cfo + ((it * KS + ks) * 64 + tid % 64) * 8) = cf[side][ks];
+        }
     }
     __syncthreads();
 
@@ -92,14 +109,15 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cbt_kernel(SsdBf16Params p) {
                 const uint32_t o0 = pack_bf16x2(acc[1][0], acc[1][1]), o1 = pack_bf16x2(acc[1][2], acc[1][3]);
                 const auto s0 = __builtin_amdgcn_permlane16_swap(e0, o0, false, false);
                 const auto s1 = __builtin_amdgcn_permlane16_swap(e1, o1, false, false);
-                const int jtile = jt + (kg & 1);
-                *reinterpret_cast<u32x4*>(out + i * TT + 16 * jtile + 8 * (kg >> 1)) = u32x4{s0[0], s1[0], s0[1], s1[1]};
+                const int j0 = 16 * (jt + (kg & 1)) + 8 * (kg >> 1);  // first of the lane's 8 columns
+                *reinterpret_cast<u32x4*>(out + ((it * NB + (j0 >> 5)) * 64 + l16 + 16 * ((j0 >> 3) & 3)) * 8) =
+                    u32x4{s0[0], s1[0], s0[1], s1[1]};
             }
         }
     }
     // B^T from the staged rows: thread u transposes the 8 x 8 block (tokens
-    // 8 tg .., states 8 sg ..); the 16 threads of an sg write one B^T row run
-    // of 256 contiguous bytes per store
+    // 8 tg .., states 8 sg ..); its 8 rows are 8 consecutive lanes of one
+    // fragment, 128 contiguous bytes
     uint16_t* bt = p.bt + bcg * (int64_t(S) * TT);
     for (int u = tid; u < (TT / 8) * (S / 8); u += kBfThreads) {
         const int tg = u % (TT / 8), sg = u / (TT / 8);
@@ -108,7 +126,9 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cbt_kernel(SsdBf16Params p) {
         for (int r = 0; r < 8; ++r) rows[r] = *reinterpret_cast<const u32x4*>(sB + (8 * tg + r) * Lay::BP + 8 * sg);
         transpose8x8_b16(rows, cols);
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) *reinterpret_cast<u32x4*>(bt + (8 * sg + cc) * TT + 8 * tg) = cols[cc];
+        for (int cc = 0; cc < 8; ++cc)
+            *reinterpret_cast<u32x4*>(bt + (((sg >> 1) * NB + (tg >> 2)) * 64 + 8 * (sg & 1) + cc + 16 * (tg & 3)) * 8) =
+                cols[cc];
     }
 }
 

@@ -183,10 +183,9 @@ struct FuLayout {
     // factor U = dt exp2(-GL), the row factor R = exp2(GL), and the block decays Q
     static constexpr int T_GL = 0, T_DT = TT, T_U = 2 * TT, T_R = 3 * TT, T_Q = 4 * TT;
     static constexpr int TFLOATS = 4 * TT + 16;
-    // decay-weighted causal weights of the diagonal 32 x 32 blocks (bf16 rows)
-    static constexpr int WP = 40;                         // bf16 pitch of a weight row
-    static constexpr int WBLK = 32 * WP * 2;              // bytes of one block's weights
-    static constexpr int WBYTES = NB * WBLK;              // one chunk's weights
+    // decay-weighted causal weights of the diagonal 32 x 32 blocks, as the MFMA
+    // B fragments of the output tiles (1 KB per 16-token tile, lane-major)
+    static constexpr int WBYTES = NIT * 1024;             // one chunk's weights
     static constexpr int RA = (NPAIR - 1) >> 1;           // off-diagonal blocks tile A can reach
     static constexpr int RB = NB - 1;                     // off-diagonal blocks tile B can reach
     static constexpr int X_OFF = 0;                                // 2 x raw X [TT][64] bf16, swizzled
@@ -364,8 +363,9 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
     const int lrow = 32 * lw + 8 * 0 + (lane >> 3);  // row of X piece m = 0 (+ 8 m)
     const uint32_t xrow_bytes = uint32_t(p.H * kFuP * 2);
     const uint32_t kNoRow = 0x7ffffff0u;             // offset past any range: reads zeros
-    // diagonal C B^T block of the loader's block: row lane / 2, 16 columns
-    const uint32_t cboff = lblk ? uint32_t(((32 * lw + (lane >> 1)) * TT + 32 * lw + 16 * (lane & 1)) * 2) : kNoRow;
+    // diagonal C B^T block of the loader's block: the fragments (tile 2 lw + h,
+    // block lw), h = 0, 1 (C B^T is stored fragment-major, see the CB pass)
+    const uint32_t cboff = lblk ? uint32_t(((2 * lw * NB + lw) * 64 + lane) * 16) : kNoRow;
     uint32_t xoff[4];
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -390,7 +390,7 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
             const auto rcb = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(cb_base(c)), 0, TT * TT * 2,
                                                                0x00020000);
             dreg[0] = __builtin_amdgcn_raw_buffer_load_b128(rcb, int(cboff), 0, 0);
-            dreg[1] = __builtin_amdgcn_raw_buffer_load_b128(rcb, int(cboff + 16), 0, 0);
+            dreg[1] = __builtin_amdgcn_raw_buffer_load_b128(rcb, int(cboff + (lblk ? NB * 1024 : 0)), 0, 0);
         }
     };
     // GL scan, tables, raw X and X~ of the loader's block into buffers `buf`
@@ -450,48 +450,43 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
         const float* T = reinterpret_cast<const float*>(sm + Lay::TB_OFF) + buf * Lay::TFLOATS;
         const float gl = lgl, ge = lge;
         // Diagonal-block weights W[r][j] = CB[r][j] dt_j exp2(GL_r - GL_j) for j <= r,
-        // plus D on j = r (the skip term), rounded to bf16: lane holds row r = lane / 2,
-        // columns 16 (lane & 1) + e.  Split as CB U_j R_r (bounded factors) unless the
-        // block decays by more than 2^-100, where the exponent is formed per element.
+        // plus D on j = r (the skip term), rounded to bf16, as the MFMA B fragments of
+        // the block's two 16-token tiles: for tile h the lane holds row r = 16 h + l16,
+        // columns 8 kg + e.  Split as CB U_j R_r (bounded factors) unless the block
+        // decays by more than 2^-100, where the exponent is formed per element.
         if (lblk) {
-            unsigned char* Wb = sm + Lay::W_OFF + buf * Lay::WBYTES + lw * Lay::WBLK;
-            const int r = lane >> 1, c0 = 16 * (lane & 1);
-            const float gr = __shfl(gl, r, 64);
-            float cbv[16];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                cbv[e] = (e & 1) ? bf16_hi(dreg[0][e >> 1]) : bf16_lo(dreg[0][e >> 1]);
-                cbv[8 + e] = (e & 1) ? bf16_hi(dreg[1][e >> 1]) : bf16_lo(dreg[1][e >> 1]);
-            }
+            unsigned char* Wb = sm + Lay::W_OFF + buf * Lay::WBYTES + 2 * lw * 1024;
+            const int l16 = lane & 15, kg = lane >> 4, c0 = 8 * kg;
             const float* Tb = T + 32 * lw + c0;
-            float w[16];
-            if (fexp2(ge) >= kFuSplitMin) {
+            const bool split = fexp2(ge) >= kFuSplitMin;
+            float a[8], gj[8];  // U_j (split) or dt_j, and GL_j
+#pragma unroll
+            for (int e4 = 0; e4 < 2; ++e4) {
+                const f32x4 av = *reinterpret_cast<const f32x4*>(Tb + (split ? Lay::T_U : Lay::T_DT) + 4 * e4);
+                const f32x4 gv = *reinterpret_cast<const f32x4*>(Tb + Lay::T_GL + 4 * e4);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    a[4 * e4 + e] = av[e];
+                    gj[4 * e4 + e] = gv[e];
+                }
+            }
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+                const int r = 16 * hh + l16;
+                const float gr = __shfl(gl, r, 64);
                 const float rr = fexp2(gr);
+                float w[8];
 #pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const f32x4 u = *reinterpret_cast<const f32x4*>(Tb + Lay::T_U + 4 * e4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) w[4 * e4 + e] = cbv[4 * e4 + e] * u[e] * rr;
+                for (int e = 0; e < 8; ++e) {
+                    const float cbv = (e & 1) ? bf16_hi(dreg[hh][e >> 1]) : bf16_lo(dreg[hh][e >> 1]);
+                    const float v = split ? cbv * a[e] * rr : cbv * a[e] * fexp2(fminf(gr - gj[e], 0.0f));
+                    const int jj = c0 + e;
+                    w[e] = (jj < r) ? v : (jj == r ? v + Dh : 0.0f);
                 }
-            } else {
-#pragma unroll
-                for (int e4 = 0; e4 < 4; ++e4) {
-                    const f32x4 gj = *reinterpret_cast<const f32x4*>(Tb + Lay::T_GL + 4 * e4);
-                    const f32x4 dj = *reinterpret_cast<const f32x4*>(Tb + Lay::T_DT + 4 * e4);
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) w[4 * e4 + e] = cbv[4 * e4 + e] * dj[e] * fexp2(fminf(gr - gj[e], 0.0f));
-                }
+                const u32x4 o = {pack_bf16x2(w[0], w[1]), pack_bf16x2(w[2], w[3]), pack_bf16x2(w[4], w[5]),
+                                 pack_bf16x2(w[6], w[7])};
+                *reinterpret_cast<u32x4*>(Wb + hh * 1024 + lane * 16) = o;
             }
-            u32x4 o[2];
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int j = c0 + e;
-                w[e] = (j < r) ? w[e] : (j == r ? w[e] + Dh : 0.0f);
-            }
-#pragma unroll
-            for (int e = 0; e < 8; ++e) o[e >> 2][e & 3] = pack_bf16x2(w[2 * e], w[2 * e + 1]);
-            *reinterpret_cast<u32x4*>(Wb + r * (Lay::WP * 2) + c0 * 2) = o[0];
-            *reinterpret_cast<u32x4*>(Wb + r * (Lay::WP * 2) + c0 * 2 + 16) = o[1];
         }
     };
     // S4 state term y^T = H C^T of the loader's block (16-token tiles 2 lw and
@@ -499,20 +494,18 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
     // fragments loaded straight from global memory.  The loaders compute it
     // while the compute waves run the chunk's block loop; the compute waves add
     // it, decayed to each row, once their block loop is done.
+    // C fragments from the CB pass's fragment-major copy of the chunk's C rows
+    // (fragment (tile, 32-state step) = 64 lanes x 16 bytes; rows past a ragged
+    // end are zeros there)
     auto issue_cf = [&](int c) {
-        const int n = chunk_rows(c);
         const auto rc = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(p.C + ((b * L + int64_t(c) * p.chunk) * p.G + g) * S), 0, n * p.G * S * 2,
-            0x00020000);
+            const_cast<uint16_t*>(p.cf + (bcg0 + int64_t(c) * p.G) * (int64_t(TT) * S)), 0, TT * S * 2, 0x00020000);
 #pragma unroll
-        for (int it2 = 0; it2 < 2; ++it2) {
-            const uint32_t row = lblk ? uint32_t(32 * lw + 16 * it2 + (lane & 15)) * uint32_t(p.G * S * 2) +
-                                            uint32_t(16 * (lane >> 4))
-                                      : kNoRow;
+        for (int it2 = 0; it2 < 2; ++it2)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                cfr[it2][ks] = __builtin_amdgcn_raw_buffer_load_b128(rc, int(row + (lblk ? 64 * ks : 0)), 0, 0);
-        }
+                cfr[it2][ks] = __builtin_amdgcn_raw_buffer_load_b128(
+                    rc, lblk ? int((((2 * lw + it2) * KS + ks) * 64 + lane) * 16) : int(kNoRow), 0, 0);
     };
     // The outputs of a chunk, staged in LDS by the compute waves, are stored by
     // the loader waves during the next chunk, as whole 128-byte rows: 16-byte
@@ -651,9 +644,11 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
     auto bt_base = [&](int c) {
         return reinterpret_cast<const char*>(p.bt + (bcg0 + int64_t(c) * p.G) * (int64_t(S) * TT));
     };
-    const uint32_t bt_lane = uint32_t(((16 * st + l16) * TT + 8 * kg) * 2);
-    const uint32_t cbA_lane = uint32_t(((16 * itA + l16) * TT + 8 * kg) * 2);
-    const uint32_t cbB_lane = uint32_t(((16 * itB + l16) * TT + 8 * kg) * 2);
+    // B^T and C B^T are stored fragment-major (the CB pass): fragment (tile, block)
+    // is 64 lanes x 16 bytes, so a wave's fragment load reads 1 KB in lane order
+    const uint32_t bt_lane = uint32_t((st * NB * 64 + lane) * 16);
+    const uint32_t cbA_lane = uint32_t((itA * NB * 64 + lane) * 16);
+    const uint32_t cbB_lane = uint32_t((itB * NB * 64 + lane) * 16);
 
     // Operand rings (the block loop is unrolled, so slots are static registers):
     // slot k holds block k of the current chunk.  When block k is consumed its
@@ -687,12 +682,12 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
         if (c_begin >= c_end) return;
         // prologue: the first chunk's operand rings (the loaders prepare its X and C)
 #pragma unroll
-        for (int k = 0; k < NB; ++k) btr[k] = ldg_b128(bt_base(c_begin) + bt_lane + 64 * k);
+        for (int k = 0; k < NB; ++k) btr[k] = ldg_b128(bt_base(c_begin) + bt_lane + 1024 * k);
         if (OUT && has_out) {
 #pragma unroll
-            for (int k = 0; k < RA; ++k) rA[k] = ldg_b128(cb_base(c_begin) + cbA_lane + 64 * k);
+            for (int k = 0; k < RA; ++k) rA[k] = ldg_b128(cb_base(c_begin) + cbA_lane + 1024 * k);
 #pragma unroll
-            for (int k = 0; k < RB; ++k) rB[k] = ldg_b128(cb_base(c_begin) + cbB_lane + 64 * k);
+            for (int k = 0; k < RB; ++k) rB[k] = ldg_b128(cb_base(c_begin) + cbB_lane + 1024 * k);
         }
         lds_barrier();  // the loaders have prepared the first chunk
 
@@ -707,9 +702,9 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
             // conditions are formed where they are used
             int jdA = jdA_w, jdB = jdB_w;
             asm volatile("" : "+s"(jdA), "+s"(jdB));
-            const uint32_t bt_lane = uint32_t(((16 * st + l16) * TT + 8 * kg) * 2);
-            const uint32_t cbA_lane = uint32_t(((16 * itA + l16) * TT + 8 * kg) * 2);
-            const uint32_t cbB_lane = uint32_t(((16 * itB + l16) * TT + 8 * kg) * 2);
+            const uint32_t bt_lane = uint32_t((st * NB * 64 + lane_c) * 16);
+            const uint32_t cbA_lane = uint32_t((itA * NB * 64 + lane_c) * 16);
+            const uint32_t cbB_lane = uint32_t((itB * NB * 64 + lane_c) * 16);
             const int64_t tok0 = int64_t(c) * p.chunk;
             const int n = chunk_rows(c);
             const int cx = c + 1 < c_end ? c + 1 : c;  // operand source of the refills for the next chunk
@@ -775,8 +770,7 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
                         auto tile_diag = [&](f32x4 (&acc)[NPTW], int it) {
                             const int i = 16 * it + l16;
                             const float ri = T[Lay::T_R + i];
-                            const u32x4 wf = *reinterpret_cast<const u32x4*>(
-                                Wb + jb * Lay::WBLK + (i & 31) * (Lay::WP * 2) + 16 * kg);
+                            const u32x4 wf = *reinterpret_cast<const u32x4*>(Wb + it * 1024 + lane_c * 16);
 #pragma unroll
                             for (int q = 0; q < NPTW; ++q) {
                                 const uint32_t o1 = x_off(trx, PTB + q, 8 * (l16 & 3));
@@ -796,11 +790,11 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
                 // refill the block's ring slots for the next chunk, after their last
                 // use in this one (see the loader loop for why the order matters)
                 __builtin_amdgcn_sched_barrier(0);
-                btr[jb] = ldg_b128(btx + bt_lane + 64 * jb);
+                btr[jb] = ldg_b128(btx + bt_lane + 1024 * jb);
                 if constexpr (OUT) {
                     if (has_out) {
-                        if constexpr (jb < RA) rA[jb] = ldg_b128(cbx + cbA_lane + 64 * jb);
-                        if constexpr (jb < RB) rB[jb] = ldg_b128(cbx + cbB_lane + 64 * jb);
+                        if constexpr (jb < RA) rA[jb] = ldg_b128(cbx + cbA_lane + 1024 * jb);
+                        if constexpr (jb < RB) rB[jb] = ldg_b128(cbx + cbB_lane + 1024 * jb);
                     }
                 }
             });
