@@ -163,7 +163,8 @@ static int launch_fused_tpl(const SsdBf16Params& cbp, const SsdFusedParams& fp, 
     }
     if (ev) (void)hipEventRecord(ev[2], stream);
     const dim3 gout{uint32_t(fp.nwhole + nst), 1u, 1u};
-    hipLaunchKernelGGL((ssd_fused_kernel<TT, S>), gout, bmain, Lay::BYTES, stream, fp);
+    const dim3 bout{uint32_t(kFuThreadsOut), 1u, 1u};
+    hipLaunchKernelGGL((ssd_fused_kernel<TT, S>), gout, bout, Lay::BYTES, stream, fp);
     if (ev) (void)hipEventRecord(ev[3], stream);
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }

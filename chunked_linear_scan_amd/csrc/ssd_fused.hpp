@@ -1,54 +1,47 @@
 // Fused bf16 SSD forward pass on gfx950 for head dim 64: one workgroup walks
-// a segment of chunks of one (batch, head) with the state on chip, and the
-// segments of a sequence are chained by a decoupled look-back over their
-// state aggregates.
+// a run of chunks of one (batch, head) with the state on chip.
 //
 // Follows "Accelerating Mamba-2 with high-performance forward pass kernels in
 // NVIDIA cuTile" (sections "Mamba-2 architecture", "Kernel 1/2/3"): per chunk
 // the cumulative sum G of a_t = A dt_t, the output from the chunk-start state,
 // the decayed intra-chunk product and the state jump
-// h <- exp(G_last) h + X^T (dt exp(G_last - G) . B).  The state recurrence
-// across chunks is the affine scan (a1, S1) then (a2, S2) = (a1 a2, a2 S1 + S2)
-// of "Selective-scan CUDA kernels" (section "The problem") lifted to a
-// matrix-valued state and run as a single-pass decoupled look-back (section
-// "The five kernels") over segments of chunks.
+// h <- exp(G_last) h + X^T (dt exp(G_last - G) . B).  Across chunks the state
+// follows the affine recurrence (a1, S1) then (a2, S2) = (a1 a2, a2 S1 + S2)
+// of "Selective-scan CUDA kernels" (section "The problem") with a
+// matrix-valued state, evaluated here as reduce-then-fold over segments.
 //
-// Work unit (one workgroup): segment `seg` of chain (b, h), i.e. chunks
-// [seg K, seg K + K).  A sequence split into several segments runs
-//   phase 1: the segment's own aggregate S_seg (zero initial state) and its
-//            decay alpha_seg = exp2(sum of the chunks' G_last);
-//   publish: the aggregate (flag 1), or for segment 0 the inclusive state
-//            alpha h0 + S_seg (flag 2);
-//   look-back: fold the predecessors' aggregates back to the nearest
-//            inclusive state -> the segment's initial state h_in;
-//   publish: the inclusive state alpha h_in + S_seg (flag 2);
-//   phase 2: outputs and states chunk by chunk from h_in.
-// A sequence with one segment runs phase 2 only.  Segments are claimed from a
-// counter in segment-major order, so a waiting segment's predecessors are
-// always claimed already.
+// Work units.  A (batch, head) chain runs whole in one workgroup or, so that
+// the last round of workgroups fills the CUs, as segments of chunks.  The
+// aggregate launch computes, for pieces of every segment but a chain's last,
+// the piece's state from zero S and its decay alpha = exp2(sum of the chunks'
+// G_last).  The output launch runs the whole chains and the segments; a
+// segment starts from h0 folded through the pieces before it, h <- alpha h + S.
 //
-// Wave roles.  Eight compute waves do every MFMA; four loader waves own the
-// HBM stream.  Vector memory operations of a wave complete in issue order, so
-// if the compute waves fetched X themselves, every wait for an L2-resident
-// operand issued after an X load would also wait out the HBM latency of that
-// load.  The loaders instead fetch the NEXT chunk's X while the current one
-// computes and prepare it; compute waves only issue L2-resident operand loads
-// and the y stores.  The two roles meet at two barriers per chunk (after the
-// state term, at the end).
+// Wave roles.  Eight compute waves run the chunk's MFMA work.  Loader waves do
+// the rest, one 32-token block each:
+//   * prep loaders fetch the next chunk's X and dt, scan GL, and write the
+//     per-token tables, the raw X tile, X~ and the diagonal-block weights;
+//   * state loaders (output launch only) compute the chunk's state term C h^T
+//     from the chunk-start state, and store the previous chunk's outputs.
+// The output launch has 16 waves (8 + 4 + 4), the aggregate launch 12.
+// Vector memory operations of a wave complete in issue order, so a wave that
+// fetched X from HBM would wait out that latency before any later L2 operand;
+// the compute waves only load L2-resident operands.  All waves meet at one
+// barrier per chunk; inside a chunk the compute waves wait only for the state
+// loaders' count.
 //
 // A chunk (TT tokens, padded to a multiple of 32) is handled as 32-token
 // blocks.  With GL the cumulative sum of a_t inside its block (log2 units,
 // <= 0) and every exponent formed <= 0 unless guarded:
-//   * prep (loader waves, block by block): X arrives straight from global
-//     memory into a double LDS buffer (global_load_lds_dwordx4); the wave scans
-//     GL, stores the per-token tables and the block decay Q = exp2(GL_end),
-//     and writes X~[t] = dt_t exp2(GL_end - GL_t) X[t] (a factor <= dt_t) to a
-//     second double buffer;
+//   * prep (loader waves, block by block): the wave scans GL, stores the
+//     per-token tables and the block decay Q = exp2(GL_end), and writes the
+//     raw X tile and X~[t] = dt_t exp2(GL_end - GL_t) X[t] (a factor <= dt_t)
+//     to double LDS buffers;
 //   * one pass over the blocks does the state jump (wave = state tile) and the
 //     intra product of two 16-token output tiles per wave, paired (i, NIT-1-i)
 //     so every wave has the same causal work.  Both use the X~ fragments of
 //     the block (ds_read_b64_tr_b16, which transposes 4x16 blocks of 16-bit
-//     values across a 16-lane group) and raw B^T or CB fragments; the decay
+//     values across a 16-lane group) and B^T or CB fragments; the decay
 //     between blocks is a running rescale of the fp32 accumulators by Q, which
 //     for the state also supplies exp2(G_last) h;
 //   * the diagonal block of a tile uses raw X with weights CB dt exp2(GL_i -
@@ -56,12 +49,14 @@
 //     at most 2^100 they are split as exp2(GL_i) [CB dt_j exp2(-GL_j)], so only
 //     per-token factors and one per-row scale are needed; stronger decay takes
 //     the element-wise form.
-//   * B^T comes ready-made from the CB pass; B^T, CB and C fragments are fetched
-//     ahead into register rings.  Every ring slot is refilled at every block
-//     (the address, not the load, depends on the wave's causal extent), so no
-//     ring register is merged across branches, which would force the load to
-//     complete on the spot; y leaves as 16-byte pieces assembled across lane
-//     rows with v_permlane16_swap.
+//   * B^T, CB and a copy of C come fragment-major from the CB pass (a wave's
+//     operand fragment is 1 KB in lane order); the compute waves fetch B^T and
+//     CB fragments a chunk ahead into register rings.  Every ring slot is
+//     refilled at every block (the address, not the load, depends on the
+//     wave's causal extent), so no ring register is merged across branches,
+//     which would force the load to complete on the spot.  y goes to LDS as
+//     16-byte pieces assembled across lane rows with v_permlane16_swap, and
+//     leaves for HBM as whole 128-byte rows from the state loaders.
 #pragma once
 
 #include <type_traits>
@@ -73,8 +68,9 @@ namespace cls {
 
 constexpr int kFuCompute = 512;                              // compute threads (8 waves)
 constexpr int kFuWaves = kFuCompute / 64;                    // compute waves
-constexpr int kFuLoaders = 4;                                // loader waves
-constexpr int kFuThreads = kFuCompute + 64 * kFuLoaders;     // workgroup size
+constexpr int kFuLoaders = 4;                                // loader waves of one role
+constexpr int kFuThreads = kFuCompute + 64 * kFuLoaders;     // workgroup size (aggregate launch)
+constexpr int kFuThreadsOut = kFuThreads + 64 * kFuLoaders;  // output launch: + state-term loaders
 constexpr int kFuP = 64;  // head dim of this kernel
 constexpr uint32_t kFuSpinLimit = 1u << 24;  // bound of the compute waves' wait for the state term
 constexpr float kFuSplitMin = 7.8886091e-31f;  // 2^-100: weakest block decay of the split diagonal form
@@ -259,7 +255,8 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches and bases
     const bool loader = wave >= kFuWaves;
-    const int lw = wave - kFuWaves;                               // loader index (loader waves)
+    const bool sloader = !AGG && wave >= kFuWaves + kFuLoaders;    // state-term loader (output launch)
+    const int lw = sloader ? wave - kFuWaves - kFuLoaders : wave - kFuWaves;  // loader's block
     const int l16 = lane & 15, kg = lane >> 4;
     // bf16 copy of the chunk-start state (one copy: the compute waves write the
     // next chunk's only after every loader has read this chunk's, see below)
@@ -371,11 +368,10 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
     for (int m = 0; m < 4; ++m)
         xoff[m] = lblk ? uint32_t(lrow + 8 * m) * xrow_bytes + uint32_t((lane & 7) * 16) : kNoRow;
     const uint32_t dtoff = (lblk && lane < 32) ? uint32_t(32 * lw + lane) * uint32_t(p.H * 4) : kNoRow;
-    u32x4 dreg[2];
     u32x4 cfr[2][KS];  // C^T fragments (MFMA B operand) of the loader's two 16-token tiles
     // X and dt of chunk c into the register set (xreg, dtv) (and, for the
     // output phase, the diagonal C B^T block of the loader's block)
-    auto issue_x = [&](int c, auto out_tag, u32x4 (&xreg)[4], float& dtv) {
+    auto issue_x = [&](int c, auto out_tag, u32x4 (&xreg)[4], float& dtv, u32x4 (&dreg)[2]) {
         constexpr bool OUT = decltype(out_tag)::value;
         const int64_t tok0 = int64_t(c) * p.chunk;
         const int n = chunk_rows(c);
@@ -446,7 +442,7 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
             }
         }
     };
-    auto prep_w = [&](int buf) {
+    auto prep_w = [&](int buf, const u32x4 (&dreg)[2]) {
         const float* T = reinterpret_cast<const float*>(sm + Lay::TB_OFF) + buf * Lay::TFLOATS;
         const float gl = lgl, ge = lge;
         // Diagonal-block weights W[r][j] = CB[r][j] dt_j exp2(GL_r - GL_j) for j <= r,
@@ -564,13 +560,12 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
             if (lane == 0) __hip_atomic_fetch_add(lb_int + 2, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
         }
     };
-    // The loader waves' share of a phase, with the same barriers as the compute
-    // waves (one per chunk).  X and dt are fetched D chunks ahead into a ring of
-    // D register sets: a load issued at the end of a chunk's preparation is
-    // consumed D barriers later.  In the output phase the loaders wait out
-    // most of every chunk at the barrier, which hides the latency with D = 1;
-    // the aggregate phase's chunks are short, and with one set its loads would
-    // be waited for soon after they are issued.  Each register set is consumed
+    // The prep loaders' share of a phase, with the same barriers as the compute
+    // waves (one per chunk).  X, dt and (output phase) the diagonal C B^T
+    // fragments are fetched D = 2 chunks ahead into a ring of two register
+    // sets: a load issued at the end of a chunk's preparation is consumed two
+    // barriers later.  With one set it would be consumed right after the next
+    // barrier, and its HBM latency would sit on the loaders' path.  Each register set is consumed
     // before it is refilled, with the scheduler kept from hoisting the refill:
     // a load issued while the old value is live would land in other registers
     // and be copied back at the loop edge, which waits for the load to
@@ -579,36 +574,29 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
     // is merged across branches.
     auto run_loader = [&](auto out_tag) {
         constexpr bool OUT = decltype(out_tag)::value;
-        constexpr int D = OUT ? 1 : 2;
+        constexpr int D = 2;
         if (c_begin >= c_end) return;
         const int last = c_end - 1;
         auto clampc = [&](int c) { return c <= last ? c : last; };
         u32x4 xreg[D][4];  // chunk j in set (j - c_begin) % D
         float dtv[D];
+        u32x4 dreg[D][2];  // (output phase) its diagonal C B^T fragments
         fu_static_for<0, D>([&](auto sc) {
             constexpr int sl = decltype(sc)::value;
-            issue_x(clampc(c_begin + sl), out_tag, xreg[sl], dtv[sl]);
+            issue_x(clampc(c_begin + sl), out_tag, xreg[sl], dtv[sl], dreg[sl]);
         });
-        if constexpr (OUT) issue_cf(c_begin);
         prep(c_begin & 1, out_tag, xreg[0], dtv[0]);
-        if constexpr (OUT) prep_w(c_begin & 1);
+        if constexpr (OUT) prep_w(c_begin & 1, dreg[0]);
         __builtin_amdgcn_sched_barrier(0);
-        issue_x(clampc(c_begin + D), out_tag, xreg[0], dtv[0]);
+        issue_x(clampc(c_begin + D), out_tag, xreg[0], dtv[0], dreg[0]);
         lds_barrier();
-        // the state term of chunk c first (the compute waves wait for it at the
-        // end of their block loop), then chunk c + 1 into the half chunk c - 1
-        // used (free since the last barrier)
+        // chunk c + 1 into the half chunk c - 1 used (free since the last barrier)
         auto step = [&](auto kc, int c) {
             constexpr int sl = (decltype(kc)::value + 1) % D;  // set of chunk c + 1
-            if constexpr (OUT) {
-                ystate(c);
-                __builtin_amdgcn_sched_barrier(0);
-                issue_cf(clampc(c + 1));
-            }
             prep((c + 1) & 1, out_tag, xreg[sl], dtv[sl]);
-            if constexpr (OUT) prep_w((c + 1) & 1);
+            if constexpr (OUT) prep_w((c + 1) & 1, dreg[sl]);
             __builtin_amdgcn_sched_barrier(0);
-            issue_x(clampc(c + 1 + D), out_tag, xreg[sl], dtv[sl]);
+            issue_x(clampc(c + 1 + D), out_tag, xreg[sl], dtv[sl], dreg[sl]);
             lds_barrier();  // chunk c + 1 ready; chunk c's half free
             __builtin_amdgcn_sched_barrier(0);  // the next step's waits stay after the barrier
         };
@@ -626,6 +614,24 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
         if constexpr (D == 2) {
             if (c < c_end) step(std::integral_constant<int, 0>{}, c);
         }
+    };
+
+    // The state loaders' share of the output phase: the state term of chunk c
+    // (which also stores chunk c - 1's outputs), then the C fragments of chunk
+    // c + 1, with the same barriers as every other wave (one per chunk).
+    auto run_state_loader = [&]() {
+        if (c_begin >= c_end) return;
+        const int last = c_end - 1;
+        issue_cf(c_begin);
+        lds_barrier();
+        for (int c = c_begin; c < c_end; ++c) {
+            ystate(c);
+            __builtin_amdgcn_sched_barrier(0);
+            issue_cf(c + 1 <= last ? c + 1 : last);
+            lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        constexpr bool OUT = true;
         if constexpr (OUT) {
             if (lblk) {  // the last chunk's outputs
                 u32x4 yo[4];
@@ -741,8 +747,10 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
             };
             // X~ fragments XD blocks ahead (a ring of XD + 1 sets; the block loop is
             // unrolled, so the set indices are static) and all block decays at once.
-            // Two blocks ahead measured no faster than one.
-            constexpr int XD = 1;
+            // Two blocks ahead measured no faster than one.  The output launch reads
+            // them in the block itself: at 16 waves a wave has 128 registers, and the
+            // prefetch set does not fit beside the operand rings.
+            constexpr int XD = OUT ? 0 : 1;
             u32x4 xs[XD + 1][4];
             fu_static_for<0, XD>([&](auto kc) {
                 constexpr int k = decltype(kc)::value;
@@ -857,10 +865,16 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
         if (loader) {
             // In the aggregate pass the loaders' work is on the path of every
             // (short) chunk: without a higher issue priority the compute waves
-            // sharing their SIMD win every arbitration.  In the output pass the
-            // loaders finish well before the compute waves, and a raised priority
-            // only takes issue slots from them (measured 3 % slower).
+            // sharing their SIMD win every arbitration.  In the output pass a
+            // raised priority only took issue slots from the compute waves
+            // (measured 3 % slower).
             if constexpr (!decltype(out_tag)::value) __builtin_amdgcn_s_setprio(3);
+            if constexpr (decltype(out_tag)::value) {
+                if (sloader) {
+                    run_state_loader();
+                    return;
+                }
+            }
             run_loader(out_tag);
             if constexpr (!decltype(out_tag)::value) __builtin_amdgcn_s_setprio(0);
             return;
@@ -919,7 +933,7 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
 // of split chains (two workgroups per CU: it needs little LDS and few
 // registers).
 template <int TT, int S>
-__global__ __launch_bounds__(kFuThreads) void ssd_fused_kernel(SsdFusedParams p) {
+__global__ __launch_bounds__(kFuThreadsOut) void ssd_fused_kernel(SsdFusedParams p) {
     ssd_fused_body<TT, S, false>(p);
 }
 

@@ -126,6 +126,27 @@ def test_bf16_edge_lengths():
         assert_close(hf, rh, TOL_BF16, f"h L={L}")
 
 
+@pytest.mark.parametrize("chunk", [32, 64, 128, 256])
+def test_whole_chains_many_chunks(chunk):
+    """Every (batch, head) chain in one workgroup (segments forced to 1), so a
+    workgroup walks tens of (sub-)chunks: the loaders' register sets, the
+    double-buffered LDS halves and the staged outputs all rotate many times,
+    with a ragged last chunk."""
+    ct = __import__("ctypes")
+    lib = cls.load_library()
+    lib.cls_ssd_set_segments.argtypes = [ct.c_int]
+    print(f"[ssd] whole chains, chunk={chunk}", flush=True)
+    inp = small_case(90 + chunk, 1, 64 * 40 + 17, 2, 64, 128, 1, torch.bfloat16, dt_shift=-3.0)
+    lib.cls_ssd_set_segments(1)
+    try:
+        y, hf = gpu_run(inp, chunk=chunk)
+    finally:
+        lib.cls_ssd_set_segments(0)
+    ry, rh, _, _ = oracle_run(inp)
+    assert_close(y, ry, TOL_BF16, f"y chunk={chunk}")
+    assert_close(hf, rh, TOL_BF16, f"h chunk={chunk}")
+
+
 def test_optional_arguments():
     inp = small_case(4, 1, 200, 2, 64, 128, 1, torch.bfloat16, h0=False, D=False)
     y, hf = gpu_run(inp, chunk=64, want_final=False)
@@ -220,10 +241,10 @@ def test_full_workloads_sampled(name, bsel, hsel):
 
 @pytest.mark.parametrize("nsegs", [1, 2, 3, 7, 64])
 def test_segment_lookback_forced(nsegs):
-    """The fused kernel splits each sequence into segments chained by a
-    decoupled look-back over state aggregates; force the segment count so the
-    protocol runs with one-chunk segments, uneven segments and the 64-segment
-    window."""
+    """The fused path splits each sequence into segments whose start states
+    come from the aggregate launch's pieces, folded in order; force the segment
+    count so the fold runs with one-chunk segments, uneven segments and many
+    segments."""
     lib = cls.load_library()
     lib.cls_ssd_set_segments.argtypes = [__import__("ctypes").c_int]
     inp = small_case(20 + nsegs, 2, 64 * 40 + 17, 3, 64, 128, 1, torch.bfloat16, dt_shift=-4.0)
