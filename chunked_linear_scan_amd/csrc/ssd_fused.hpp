@@ -663,6 +663,12 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
     // fetched a whole chunk ahead.  A slot beyond the wave's causal extent is
     // reloaded every chunk and never read.
     constexpr int RA = Lay::RA, RB = Lay::RB;
+    // CB fragment of chunk c at byte offset off (kNoRow: a slot past the wave's
+    // causal extent, read as zeros without touching memory)
+    auto cb_load = [&](int c, uint32_t off) {
+        const auto r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(cb_base(c)), 0, TT * TT * 2, 0x00020000);
+        return __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
+    };
     u32x4 btr[NB];                                  // B^T fragments (state product)
     u32x4 rA[RA > 0 ? RA : 1], rB[RB > 0 ? RB : 1];  // off-diagonal CB fragments of the output tiles
     float sumG = 0.0f;
@@ -691,9 +697,9 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
         for (int k = 0; k < NB; ++k) btr[k] = ldg_b128(bt_base(c_begin) + bt_lane + 1024 * k);
         if (OUT && has_out) {
 #pragma unroll
-            for (int k = 0; k < RA; ++k) rA[k] = ldg_b128(cb_base(c_begin) + cbA_lane + 1024 * k);
+            for (int k = 0; k < RA; ++k) rA[k] = cb_load(c_begin, k < jdA_w ? cbA_lane + 1024 * k : kNoRow);
 #pragma unroll
-            for (int k = 0; k < RB; ++k) rB[k] = ldg_b128(cb_base(c_begin) + cbB_lane + 1024 * k);
+            for (int k = 0; k < RB; ++k) rB[k] = cb_load(c_begin, k < jdB_w ? cbB_lane + 1024 * k : kNoRow);
         }
         lds_barrier();  // the loaders have prepared the first chunk
 
@@ -801,8 +807,8 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
                 btr[jb] = ldg_b128(btx + bt_lane + 1024 * jb);
                 if constexpr (OUT) {
                     if (has_out) {
-                        if constexpr (jb < RA) rA[jb] = ldg_b128(cbx + cbA_lane + 1024 * jb);
-                        if constexpr (jb < RB) rB[jb] = ldg_b128(cbx + cbB_lane + 1024 * jb);
+                        if constexpr (jb < RA) rA[jb] = cb_load(cx, jb < jdA ? cbA_lane + 1024 * jb : kNoRow);
+                        if constexpr (jb < RB) rB[jb] = cb_load(cx, jb < jdB ? cbB_lane + 1024 * jb : kNoRow);
                     }
                 }
             });
