@@ -118,7 +118,8 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     pl.cb_off = pl.payload_off + up(pay);
     pl.bt_off = pl.cb_off + up(size_t(batch) * size_t(nc) * size_t(G) * size_t(TT) * TT * 2);
     pl.cf_off = pl.bt_off + up(size_t(batch) * size_t(nc) * size_t(G) * size_t(S) * TT * 2);
-    pl.bytes = pl.cf_off + size_t(batch) * size_t(nc) * size_t(G) * size_t(S) * TT * 2;
+    pl.dtt_off = pl.cf_off + up(size_t(batch) * size_t(nc) * size_t(G) * size_t(S) * TT * 2);
+    pl.bytes = pl.dtt_off + size_t(batch) * size_t(nc) * size_t(H) * TT * 4;
     return pl;
 }
 
@@ -275,6 +276,7 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
         p.cb = reinterpret_cast<uint16_t*>(ws + pl.cb_off);
         p.bt = reinterpret_cast<uint16_t*>(ws + pl.bt_off);
         p.cf = reinterpret_cast<uint16_t*>(ws + pl.cf_off);
+        p.dtt = reinterpret_cast<float*>(ws + pl.dtt_off);
         cls::SsdFusedParams f{};
         f.x = p.x;
         f.dt = p.dt;
@@ -288,6 +290,7 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
         f.cb = p.cb;
         f.bt = p.bt;
         f.cf = p.cf;
+        f.dtt = p.dtt;
         f.payload = reinterpret_cast<float*>(ws + pl.payload_off);
         f.err = reinterpret_cast<uint32_t*>(ws);
         f.batch = s.batch;

@@ -5,7 +5,8 @@
 
 namespace cls {
 
-// S2a for the fused kernel: one workgroup (4 waves) per (batch, chunk, group).
+// S2a for the fused kernel: one workgroup (4 waves) per (batch, chunk, group),
+// then one per (batch, chunk) that rewrites dt head-major (cbt_dt_transpose).
 // Writes CB[i][j] = sum_s C[i][s] B[j][s] for the 32-token blocks with
 // block(j) <= block(i) (the only ones the fused kernel reads), B^T[s][t], and
 // a copy of the chunk's C rows, all three fragment-major: the MFMA operand
@@ -22,8 +23,49 @@ namespace cls {
 template <int TT, int S>
 struct CbtLayout {
     static constexpr int BP = S + 8;                 // bf16 pitch of the staged B rows
-    static constexpr int BYTES = TT * BP * 2;
+    static constexpr int DP = 65;                    // float pitch of a staged dt row (64 heads)
+    static constexpr int BYTES = TT * BP * 2 > TT * DP * 4 ? TT * BP * 2 : TT * DP * 4;
 };
+
+// The dt workgroups of the CB pass: dt of chunk c of batch row b, token-major
+// [t][h] in the input, rewritten head-major and token-contiguous [h][t] (zero
+// past the chunk's last real row), 64 heads at a time through LDS: the loads
+// read token rows and the stores whole per-head runs, both coalesced.
+template <int TT, int S>
+__device__ __forceinline__ void cbt_dt_transpose(const SsdBf16Params& p, int64_t bc, unsigned char* smem) {
+    using Lay = CbtLayout<TT, S>;
+    constexpr int DP = Lay::DP;
+    const int tid = threadIdx.x;
+    const int64_t c = bc % p.nchunks, b = bc / p.nchunks;
+    const int64_t tok0 = c * p.chunk;
+    const int n = int((p.L - tok0 < p.chunk) ? (p.L - tok0) : p.chunk);
+    float* st = reinterpret_cast<float*>(smem);
+    for (int h0 = 0; h0 < p.H; h0 += 64) {
+        constexpr int NL = TT * 64 / kBfThreads;
+        float v[NL];
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            const int idx = tid + kBfThreads * k, t = idx >> 6, hh = idx & 63;
+            v[k] = (t < n && h0 + hh < p.H) ? p.dt[(b * p.L + tok0 + t) * p.H + h0 + hh] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < NL; ++k) {
+            const int idx = tid + kBfThreads * k;
+            st[(idx >> 6) * DP + (idx & 63)] = v[k];
+        }
+        __syncthreads();
+        constexpr int NS = 64 * (TT / 4) / kBfThreads;
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            const int idx = tid + kBfThreads * k, hh = idx / (TT / 4), t4 = 4 * (idx % (TT / 4));
+            if (h0 + hh < p.H) {
+                const f32x4 o = {st[t4 * DP + hh], st[(t4 + 1) * DP + hh], st[(t4 + 2) * DP + hh], st[(t4 + 3) * DP + hh]};
+                *reinterpret_cast<f32x4*>(p.dtt + ((b * p.nchunks + c) * p.H + h0 + hh) * TT + t4) = o;
+            }
+        }
+        __syncthreads();
+    }
+}
 
 template <int TT, int S>
 __global__ __launch_bounds__(kBfThreads) void ssd_cbt_kernel(SsdBf16Params p) {
@@ -32,6 +74,12 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cbt_kernel(SsdBf16Params p) {
     constexpr int NIT = TT / 16;
     constexpr int CPR = S / 8;  // 16-byte pieces per row
     extern __shared__ __attribute__((aligned(16))) unsigned char cbt_sm[];
+    // workgroups past the (batch, chunk, group) tiles rewrite dt, one per (batch, chunk)
+    const int64_t ncbg = p.batch * p.nchunks * p.G;
+    if (int64_t(blockIdx.x) >= ncbg) {
+        cbt_dt_transpose<TT, S>(p, int64_t(blockIdx.x) - ncbg, cbt_sm);
+        return;
+    }
     uint16_t* sB = reinterpret_cast<uint16_t*>(cbt_sm);
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kg = lane >> 4;
@@ -150,7 +198,7 @@ static int launch_fused_tpl(const SsdBf16Params& cbp, const SsdFusedParams& fp, 
     }
     const int nst = fp.nsegs * (fp.nchains - fp.nwhole);              // segments
     const int npieces = (fp.nchains - fp.nwhole) * (fp.nsegs - 1) * fp.agg_d;  // aggregate pieces
-    const dim3 gcb{uint32_t(cbp.batch * cbp.nchunks * cbp.G), 1u, 1u};
+    const dim3 gcb{uint32_t(cbp.batch * cbp.nchunks * (cbp.G + 1)), 1u, 1u};  // + the dt workgroups
     const dim3 bcb{uint32_t(kBfThreads), 1u, 1u};
     const dim3 bmain{uint32_t(kFuThreads), 1u, 1u};
     if (ev) (void)hipEventRecord(ev[0], stream);

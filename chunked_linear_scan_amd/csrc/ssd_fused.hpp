@@ -367,7 +367,7 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
         xoff[m] = lblk ? uint32_t(lrow + 8 * m) * xrow_bytes + uint32_t((lane & 7) * 16) : kNoRow;
-    const uint32_t dtoff = (lblk && lane < 32) ? uint32_t(32 * lw + lane) * uint32_t(p.H * 4) : kNoRow;
+    const uint32_t dtoff = (lblk && lane < 32) ? uint32_t(32 * lw + lane) * 4u : kNoRow;  // token-contiguous dt
     u32x4 cfr[2][KS];  // C^T fragments (MFMA B operand) of the loader's two 16-token tiles
     // X and dt of chunk c into the register set (xreg, dtv) (and, for the
     // output phase, the diagonal C B^T block of the loader's block)
@@ -379,8 +379,9 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
             const_cast<uint16_t*>(p.x + ((b * L + tok0) * p.H + h) * kFuP), 0, int(uint32_t(n) * xrow_bytes), 0x00020000);
 #pragma unroll
         for (int m = 0; m < 4; ++m) xreg[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, int(xoff[m]), 0, 0);
-        const auto rd = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(p.dt + (b * L + tok0) * p.H + h), 0,
-                                                          n * p.H * 4, 0x00020000);
+        // dt from the CB pass's token-contiguous copy (zeros past the last real row)
+        const auto rd = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(p.dtt + ((b * p.nchunks + c) * p.H + h) * TT), 0, TT * 4, 0x00020000);
         dtv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, int(dtoff), 0, 0));
         if constexpr (OUT) {
             const auto rcb = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(cb_base(c)), 0, TT * TT * 2,

@@ -39,6 +39,8 @@ struct SsdBf16Params {
     uint16_t* cb;        // workspace: bf16 [Bt, Nc, G, TT, TT]
     uint16_t* bt;        // workspace: bf16 [Bt, Nc, G, S, TT] (B^T), or null when not needed
     uint16_t* cf;        // workspace of the fused path: bf16 C fragments [Bt, Nc, G, TT * S], or null
+    float* dtt;          // workspace of the fused path: dt per head, token-contiguous [Bt, Nc, H, TT], zero
+                         // past the sequence end, or null
     int64_t batch, L;
     int H, G, chunk, nchunks;
 };
@@ -56,6 +58,7 @@ struct SsdFusedParams {
     const uint16_t* cb;
     const uint16_t* bt;
     const uint16_t* cf;
+    const float* dtt;
     float* payload;      // [pieces][threads][state floats per lane] aggregates, then [pieces] decays
     uint32_t* err;
     int64_t batch, L;
@@ -75,7 +78,7 @@ struct SsdFusedPlan {
     bool use;
     int TT, chunk, nsegs, seg_chunks, nchains, nwhole;  // chunk: the sub-chunk the kernel runs
     int agg_d, agg_chunks, npieces;                     // aggregate pieces (see SsdFusedParams)
-    size_t payload_off, cb_off, bt_off, cf_off, bytes;
+    size_t payload_off, cb_off, bt_off, cf_off, dtt_off, bytes;
 };
 
 // Tile sizes of the bf16 path: the chunk is padded to a multiple of 32 tokens.
