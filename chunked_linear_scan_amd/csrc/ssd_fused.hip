@@ -59,7 +59,8 @@ __device__ __forceinline__ void cbt_dt_transpose(const SsdBf16Params& p, int64_t
         for (int k = 0; k < NS; ++k) {
             const int idx = tid + kBfThreads * k, hh = idx / (TT / 4), t4 = 4 * (idx % (TT / 4));
             if (h0 + hh < p.H) {
-                const f32x4 o = {st[t4 * DP + hh], st[(t4 + 1) * DP + hh], st[(t4 + 2) * DP + hh], st[(t4 + 3) * DP + hh]};
+                const f32x4 o = {st[t4 * DP + hh], st[(t4 + 1) * DP + hh], st[(t4 + 2) * DP + hh],
+                                 st[(t4 + 3) * DP + hh]};
                 *reinterpret_cast<f32x4*>(p.dtt + ((b * p.nchunks + c) * p.H + h0 + hh) * TT + t4) = o;
             }
         }
@@ -175,7 +176,8 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cbt_kernel(SsdBf16Params p) {
         transpose8x8_b16(rows, cols);
 #pragma unroll
         for (int cc = 0; cc < 8; ++cc)
-            *reinterpret_cast<u32x4*>(bt + (((sg >> 1) * NB + (tg >> 2)) * 64 + 8 * (sg & 1) + cc + 16 * (tg & 3)) * 8) =
+            *reinterpret_cast<u32x4*>(bt +
+                                      (((sg >> 1) * NB + (tg >> 2)) * 64 + 8 * (sg & 1) + cc + 16 * (tg & 3)) * 8) =
                 cols[cc];
     }
 }

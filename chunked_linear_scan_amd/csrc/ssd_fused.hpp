@@ -566,13 +566,13 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
     // fragments are fetched D = 2 chunks ahead into a ring of two register
     // sets: a load issued at the end of a chunk's preparation is consumed two
     // barriers later.  With one set it would be consumed right after the next
-    // barrier, and its HBM latency would sit on the loaders' path.  Each register set is consumed
-    // before it is refilled, with the scheduler kept from hoisting the refill:
-    // a load issued while the old value is live would land in other registers
-    // and be copied back at the loop edge, which waits for the load to
-    // complete.  Loads are issued unconditionally (past the last chunk the last
-    // one is reloaded and prepared into the free buffer half) so no register
-    // is merged across branches.
+    // barrier, and its HBM latency would sit on the loaders' path.  Each
+    // register set is consumed before it is refilled, with the scheduler kept
+    // from hoisting the refill: a load issued while the old value is live
+    // would land in other registers and be copied back at the loop edge, which
+    // waits for the load to complete.  Loads are issued unconditionally (past
+    // the last chunk the last one is reloaded and prepared into the free buffer
+    // half) so no register is merged across branches.
     auto run_loader = [&](auto out_tag) {
         constexpr bool OUT = decltype(out_tag)::value;
         constexpr int D = 2;
