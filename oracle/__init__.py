@@ -10,7 +10,8 @@ consume the same seeded host tensors.
 Modules
 -------
 ssd       the SSD recurrence as a token-by-token loop (the definition), plus a
-          brute-force unrolled sum and the decay-free linear-attention form
+          brute-force unrolled sum, the decay-free linear-attention form, and
+          one decode token (ssd_step)
 scan      the scalar recurrence h[t] = a[t] h[t-1] + b[t] as a loop, and its
           affine combine
 chunked   a float64 mirror of the chunked (state-space duality) algebra, used to

@@ -118,3 +118,36 @@ def ssd_linear_attention(x, dt, B, C, D=None, h0=None):
                 Y += D[hh] * X
             y[bb, :, hh, :] = Y
     return y
+
+
+def ssd_step(h, x, dt, A, B, C, D=None):
+    """One token of the recurrence, for sequential inference (decode).
+
+    The page ("Mamba-2 architecture") calls the recurrent form ideal for
+    sequential inference: with a = A dt and b = dt B_t, the state becomes
+    exp(a) h + b x^T and the output is c^T of the new state plus D x (the
+    same reading as ``ssd_loop``: the token's own update is seen by its
+    output).
+
+    h [Bt,H,P,S] (head-dim rows, state columns, as ``ssd_loop`` returns it),
+    x [Bt,H,P], dt [Bt,H], A [H], B and C [Bt,G,S], D [H] or None.  Returns
+    (y [Bt,H,P], the new state [Bt,H,P,S]); the inputs are not modified.
+    """
+    h, x, dt, A, B, C, D = map(_f64, (h, x, dt, A, B, C, D))
+    Bt, H, P = x.shape
+    if h.shape[:3] != (Bt, H, P) or dt.shape != (Bt, H) or A.shape != (H,):
+        raise ValueError("h must be [Bt,H,P,S], dt [Bt,H] and A [H]")
+    if B.ndim != 3 or B.shape[0] != Bt or C.shape != B.shape or B.shape[2] != h.shape[3]:
+        raise ValueError("B and C must be [Bt,G,S]")
+    G = B.shape[1]
+    if H % G:
+        raise ValueError("heads must be a multiple of groups")
+    grp = np.arange(H) // (H // G)
+    decay = np.exp(A[None, :] * dt)                        # exp(a)            [Bt,H]
+    b = dt[:, :, None] * B[:, grp, :]                      # b = dt B          [Bt,H,S]
+    c = C[:, grp, :]                                       #                   [Bt,H,S]
+    h_new = decay[:, :, None, None] * h + x[:, :, :, None] * b[:, :, None, :]
+    y = np.einsum("bhps,bhs->bhp", h_new, c)
+    if D is not None:
+        y = y + D[None, :, None] * x
+    return y, h_new

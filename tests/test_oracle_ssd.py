@@ -5,7 +5,9 @@ hand-worked fixture, the brute-force unrolled sum, the decay-free
 linear-attention closed form, the dt = 0 identity, chunk-size invariance of the
 independent chunked formulation, state carry across calls, the scalar-scan
 special case, and mutants (h_{t-1} output, strict mask, swapped groups) that
-must be caught.
+must be caught.  ``oracle.ssd.ssd_step`` (one decode token) is tied to numbers
+worked by hand, to the dt = 0 and full-decay identities, and, rolled over a
+sequence, to the independent chunked formulation.
 """
 import json
 import math
@@ -153,3 +155,66 @@ def test_identical_heads_in_a_group_agree():
     y, _ = ssd.ssd_loop(x, dt, A, B, C, D, None)
     for h in range(1, 4):
         assert np.array_equal(y[:, :, h], y[:, :, 0])
+
+
+# ---- the decode step ---------------------------------------------------------
+
+def test_step_hand_worked_token():
+    """One head, P = S = 2, worked by hand: A = -ln 2 and dt = 1 give a decay of
+    1/2 and b = dt B = (2, -1).  With h (rows p, columns s) = [[1, 2], [3, 4]]
+    and x = (1, -2):
+        h_new[0] = 0.5 (1, 2) + 1 (2, -1) = (2.5, 0.0)
+        h_new[1] = 0.5 (3, 4) - 2 (2, -1) = (-2.5, 4.0)
+    and with c = (1, 3), D = 0.5:  y[0] = 2.5 + 0 + 0.5 = 3.0,
+    y[1] = -2.5 + 12 - 1 = 8.5."""
+    h = np.array([[[[1.0, 2.0], [3.0, 4.0]]]])
+    x = np.array([[[1.0, -2.0]]])
+    dt = np.array([[1.0]])
+    A = np.array([-math.log(2.0)])
+    B = np.array([[[2.0, -1.0]]])
+    C = np.array([[[1.0, 3.0]]])
+    D = np.array([0.5])
+    y, hn = ssd.ssd_step(h, x, dt, A, B, C, D)
+    assert np.abs(hn[0, 0] - np.array([[2.5, 0.0], [-2.5, 4.0]])).max() < 1e-14
+    assert np.abs(y[0, 0] - np.array([3.0, 8.5])).max() < 1e-14
+
+
+def test_step_zero_timestep_keeps_state():
+    x, dt, A, B, C, D, h0 = rand_case(31, L=1)
+    y, hn = ssd.ssd_step(h0, x[:, 0], np.zeros_like(dt[:, 0]), A, B[:, 0], C[:, 0], D)
+    assert np.array_equal(hn, h0)
+    grp = np.arange(4) // 2
+    expect = np.einsum("bhps,bhs->bhp", h0, C[:, 0][:, grp]) + D[None, :, None] * x[:, 0]
+    assert np.abs(y - expect).max() < 1e-13
+
+
+def test_step_full_decay_forgets_the_state():
+    """A very negative A (decay exp(-inf-like) = 0): the new state is b x^T alone."""
+    x, dt, A, B, C, D, h0 = rand_case(32, L=1)
+    A = np.full_like(A, -1e6)
+    y, hn = ssd.ssd_step(h0, x[:, 0], dt[:, 0], A, B[:, 0], C[:, 0], None)
+    grp = np.arange(4) // 2
+    b = dt[:, 0, :, None] * B[:, 0][:, grp]
+    assert np.abs(hn - x[:, 0, :, :, None] * b[:, :, None, :]).max() < 1e-13
+
+
+@pytest.mark.parametrize("chunk", [4, 16])
+def test_step_rollout_matches_chunked(chunk):
+    """Decode after prefill: running the step token by token from h0 gives the
+    outputs and final state of the independent chunked formulation."""
+    x, dt, A, B, C, D, h0 = rand_case(33, L=37)
+    yc, hc = chunked.ssd_chunked(x, dt, A, B, C, D, h0, chunk=chunk)
+    h = h0.copy()
+    for t in range(x.shape[1]):
+        y, h = ssd.ssd_step(h, x[:, t], dt[:, t], A, B[:, t], C[:, t], D)
+        assert np.abs(y - yc[:, t]).max() < 1e-11
+    assert np.abs(h - hc).max() < 1e-11
+
+
+def test_step_previous_state_output_differs():
+    """The literal h_{t-1} reading of the page's renamed form gives other
+    outputs, so the reading the step takes is observable."""
+    x, dt, A, B, C, D, h0 = rand_case(34, L=1)
+    y, _ = ssd.ssd_step(h0, x[:, 0], dt[:, 0], A, B[:, 0], C[:, 0], D)
+    yp, _ = ssd.ssd_loop(x, dt, A, B, C, D, h0, y_uses_previous_state=True)
+    assert np.abs(y - yp[:, 0]).max() > 1e-3
