@@ -57,6 +57,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.ssd_fwd_workspace_size.restype = sz
         lib.ssd_fwd.argtypes = [vp, fp, fp, vp, vp, fp, fp] + [i64] * 7 + [ctypes.c_int, vp, fp, vp, sz, vp]
         lib.ssd_fwd.restype = ctypes.c_int
+        lib.ssd_step.argtypes = [fp, vp, fp, fp, vp, vp, fp] + [i64] * 5 + [ctypes.c_int, vp, vp]
+        lib.ssd_step.restype = ctypes.c_int
         _lib = lib
         return lib
 
@@ -175,5 +177,38 @@ def ssd_fwd(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, want_final_state:
     return y, hf
 
 
-__all__ = ["linear_scan", "ssd_fwd", "load_library", "strerror", "SSDError", "LIB_PATH",
+def ssd_step(h, x, dt, A, B, C, D=None, out: torch.Tensor | None = None):
+    """One decode token: updates the state h [Bt,H,P,S] (fp32) in place and
+    returns y [Bt,H,P].
+
+    x [Bt,H,P] and B, C [Bt,G,S] in fp32 or bf16 (same dtype); dt [Bt,H],
+    A [H] and D [H] (optional) in fp32.
+    """
+    lib = load_library()
+    if x.dtype not in _DTYPE_CODE:
+        raise TypeError("x must be float32 or bfloat16")
+    _check_cuda("x", x, x.dtype)
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, nheads, headdim]")
+    Bt, H, P = x.shape
+    _check_cuda("B", B, x.dtype)
+    if B.dim() != 3 or B.shape[0] != Bt:
+        raise ValueError("B must be [batch, ngroups, dstate]")
+    G, S = B.shape[1], B.shape[2]
+    _check_cuda("C", C, x.dtype, B.shape)
+    _check_cuda("h", h, torch.float32, (Bt, H, P, S))
+    _check_cuda("dt", dt, torch.float32, (Bt, H))
+    _check_cuda("A", A, torch.float32, (H,))
+    if D is not None:
+        _check_cuda("D", D, torch.float32, (H,))
+    y = torch.empty_like(x) if out is None else out
+    _check_cuda("out", y, x.dtype, x.shape)
+    st = lib.ssd_step(_ptr(h), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), Bt, H, P, S, G,
+                      _DTYPE_CODE[x.dtype], _ptr(y), _stream_handle(x.device))
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_step")
+    return y
+
+
+__all__ = ["linear_scan", "ssd_fwd", "ssd_step", "load_library", "strerror", "SSDError", "LIB_PATH",
            "SSD_F32", "SSD_BF16"]

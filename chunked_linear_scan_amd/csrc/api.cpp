@@ -119,4 +119,29 @@ int ssd_fwd(const void* x, const float* dt, const float* A, const void* B, const
     return cls_ssd_launch(s, args, static_cast<hipStream_t>(stream));
 }
 
+int ssd_step(float* h, const void* x, const float* dt, const float* A, const void* B, const void* C,
+             const float* D, int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
+             int dtype, void* y, void* stream) {
+    if (!h || !x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
+    if (dtype != SSD_F32 && dtype != SSD_BF16) return SSD_ERR_DTYPE;
+    if (batch <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0 || nheads % ngroups != 0)
+        return SSD_ERR_SHAPE;
+    if (nheads > (int64_t(1) << 20) || headdim > (int64_t(1) << 20) || batch * nheads >= (int64_t(1) << 31) ||
+        batch * nheads * headdim * dstate >= (int64_t(1) << 46))
+        return SSD_ERR_SHAPE;
+    if (dstate < 4 || dstate > 256 || (dstate & (dstate - 1)) != 0) return SSD_ERR_UNSUPPORTED;
+    // the state is read and written as 16-byte vectors; the others element by element
+    const uintptr_t esz = dtype == SSD_BF16 ? 2 : 4;
+    if (!aligned16(h)) return SSD_ERR_ALIGN;
+    const void* ep[] = {x, B, C, y};
+    for (const void* p : ep)
+        if (reinterpret_cast<uintptr_t>(p) % esz) return SSD_ERR_ALIGN;
+    const void* fp[] = {dt, A, D};
+    for (const void* p : fp)
+        if (p && reinterpret_cast<uintptr_t>(p) % 4) return SSD_ERR_ALIGN;
+    const int st = cls_ssd_step_launch(h, x, dt, A, B, C, D, y, batch, nheads, headdim, dstate, ngroups, dtype,
+                                       static_cast<hipStream_t>(stream));
+    return st == 0 ? SSD_OK : (st == -8 ? SSD_ERR_UNSUPPORTED : SSD_ERR_HIP);
+}
+
 }  // extern "C"

@@ -35,4 +35,9 @@ int cls_launch_linear_scan(const float* a, const float* b, float* h, int64_t row
 int cls_ssd_check(const SsdShape& s);
 size_t cls_ssd_workspace_bytes(const SsdShape& s);
 int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t stream);
+// One decode token (ssd_step.hip); shapes already validated.  0, or -7 when the
+// launch fails, -8 for a state size without a kernel.
+int cls_ssd_step_launch(float* h, const void* x, const float* dt, const float* A, const void* B,
+                        const void* C, const float* D, void* y, int64_t batch, int64_t nheads,
+                        int64_t headdim, int64_t dstate, int64_t ngroups, int dtype, hipStream_t stream);
 }

@@ -108,6 +108,33 @@ int linear_scan(const float* a, const float* b, float* h, int64_t rows,
                 int64_t length, void* workspace, size_t workspace_bytes,
                 void* stream);
 
+/*
+ * One decode token of the same recurrence, for sequential inference: the
+ * recurrent form of "Accelerating Mamba-2 with high-performance forward pass
+ * kernels in NVIDIA cuTile", section "Mamba-2 architecture", which that
+ * section names as the one for generation.  Per batch b and head h:
+ *     h <- exp(A[h] dt) h + dt B x^T,   y = c^T h + D[h] x
+ * (the output sees the token's own update, as ssd_fwd's does).  ssd_fwd's
+ * h_final is the state to continue a sequence from.
+ *
+ * Layouts (row-major, contiguous):
+ *   h         [batch, nheads, headdim, dstate]   fp32, device, read and
+ *                                                overwritten in place;
+ *                                                16-byte aligned
+ *   x, y      [batch, nheads, headdim]           dtype (y written)
+ *   dt        [batch, nheads]                    fp32
+ *   A, D      [nheads]                           fp32  (D may be NULL = 0)
+ *   B, C      [batch, ngroups, dstate]           dtype
+ * Head h reads group h / (nheads / ngroups).  dstate must be a power of two
+ * from 4 to 256 (SSD_ERR_UNSUPPORTED otherwise); any headdim.  No workspace.
+ * y must not alias an input.  Returns SSD_OK or a negative status (nothing
+ * is enqueued on a validation error).
+ */
+int ssd_step(float* h, const void* x, const float* dt, const float* A,
+             const void* B, const void* C, const float* D,
+             int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate,
+             int64_t ngroups, int dtype, void* y, void* stream);
+
 /* Human-readable text for a status code (static storage). */
 const char* ssd_strerror(int status);
 

@@ -27,7 +27,7 @@ def header_functions():
 def test_header_lists_expected_entry_points():
     assert set(header_functions()) == {
         "ssd_fwd_workspace_size", "ssd_fwd", "linear_scan_workspace_size", "linear_scan",
-        "ssd_strerror"}
+        "ssd_step", "ssd_strerror"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -96,3 +96,27 @@ def test_ssd_workspace_size_zero_for_invalid_shapes():
     lib = cls.load_library()
     assert lib.ssd_fwd_workspace_size(1, 64, 3, 16, 32, 2, 32, 1) == 0
     assert lib.ssd_fwd_workspace_size(1, 64, 2, 16, 32, 1, 33, 1) == 0
+
+
+def test_ssd_step_rejects_bad_arguments():
+    lib = cls.load_library()
+    args_ok = dict(Bt=2, H=4, P=64, S=128, G=2, dt=cls.SSD_BF16)
+
+    def call(h=FAKE, x=FAKE, dtp=FAKE, A=FAKE, B=FAKE, C=FAKE, y=FAKE, **kw):
+        a = dict(args_ok)
+        a.update(kw)
+        return lib.ssd_step(h, x, dtp, A, B, C, None, a["Bt"], a["H"], a["P"], a["S"], a["G"], a["dt"], y,
+                            None)
+
+    assert call(h=None) == -1
+    assert call(y=None) == -1
+    assert call(C=None) == -1
+    assert call(dt=5) == -3
+    assert call(Bt=0) == -2
+    assert call(P=-1) == -2
+    assert call(H=3, G=2) == -2
+    assert call(S=96) == -8
+    assert call(S=512) == -8
+    assert call(S=2) == -8
+    assert call(h=ctypes.c_void_p(0x10008)) == -5
+    assert call(x=ctypes.c_void_p(0x10001)) == -5
