@@ -12,7 +12,8 @@ each of its two kernels, which gives the fused kernel's own time for the
 roofline.  Input and output buffers rotate over enough copies that the
 footprint exceeds 1 GiB, so the 256 MB Infinity Cache cannot serve repeated
 steps.  The linear scan (one kernel) is timed the same way in its own loop and
-reported in the ``linear_scan`` object of the same JSON line.
+reported in the ``linear_scan`` object of the same JSON line, and so is one
+decode token (``ssd_step``, the ``ssd_step`` object).
 
 The CPU baseline is the float64 oracle, unmodified, run on a bounded sample
 of the same workload (a few whole (batch, head) sequences, one per worker
@@ -89,6 +90,7 @@ def measured_traffic(kernel_key, sources, launches_per_step=1):
 
 SSD_SOURCES = ["ssd_fused.hpp", "ssd_fused.hip", "common.hpp", "ssd_kernels.hpp"]
 SCAN_SOURCES = ["linear_scan.hip", "common.hpp"]
+STEP_SOURCES = ["ssd_step.hip", "common.hpp"]
 
 
 def record_traffic(fetch_csv, write_csv, workload):
@@ -121,7 +123,8 @@ def record_traffic(fetch_csv, write_csv, workload):
             db = json.load(f)
     for key, srcs, pat in [("ssd_fused_kernel:" + workload, SSD_SOURCES, "ssd_fused_kernel<"),
                            ("ssd_fused_agg_kernel:" + workload, SSD_SOURCES, "ssd_fused_agg_kernel<"),
-                           ("linear_scan:scan", SCAN_SOURCES, "linear_scan_kernel")]:
+                           ("linear_scan:scan", SCAN_SOURCES, "linear_scan_kernel"),
+                           ("ssd_step:decode_large", STEP_SOURCES, "ssd_step_kernel")]:
         f = [v for (k, g), vs in fe.items() if pat in k for v in vs]
         w = [v for (k, g), vs in wr.items() if pat in k for v in vs]
         if not f or not w:
@@ -211,6 +214,59 @@ def cpu_baseline_scan(inp):
     nbytes = 12 * inp["a"].numel()
     return {"value": nbytes / wall / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"whole workload ({tuple(inp['a'].shape)}), wall {wall:.2f}s"}
+
+
+def cpu_baseline_step(inp, nbytes):
+    from oracle import ssd as ossd
+    arrs = [inp[k].to(torch_f64()).numpy() for k in ("h", "x", "dt", "A", "B", "C", "D")]
+    t0 = time.perf_counter()
+    ossd.ssd_step(*arrs)
+    wall = time.perf_counter() - t0
+    return {"value": nbytes / wall / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"whole workload (one token, {tuple(inp['h'].shape)} state), wall {wall:.2f}s"}
+
+
+def torch_f64():
+    import torch
+    return torch.float64
+
+
+def bench_step(name, steps, warmup, want_cpu):
+    """One decode token per call (ssd_step) over the named workload; the state
+    is updated in place, so repeated calls keep decoding."""
+    import torch
+    import chunked_linear_scan_amd as cls
+    from chunked_linear_scan_amd import workloads
+    shape, _ = workloads.STEP_WORKLOADS[name]
+    inp = workloads.step_workload(name)
+    Bt, H, P, S, G = shape.batch, shape.nheads, shape.headdim, shape.dstate, shape.ngroups
+    esz = 2 if shape.dtype == "bf16" else 4
+    nbytes = (2 * Bt * H * P * S * 4 + 2 * Bt * H * P * esz + Bt * H * 4 + 2 * Bt * G * S * esz + 2 * H * 4)
+    nsets = max(1, math.ceil((1 << 30) / nbytes))
+    dev = torch.device("cuda:0")
+    sets = []
+    for _ in range(nsets):
+        d = {k: v.to(dev) for k, v in inp.items()}
+        d["y"] = torch.empty_like(d["x"])
+        sets.append(d)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        d = sets[i]
+        cls.ssd_step(d["h"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], out=d["y"])
+
+    t = time_loop(step, nsets, steps, warmup, stream)
+    gbs = nbytes / t / 1e9
+    res = {"workload": f"{name}: one decode token, batch {Bt}, {H} heads, P={P}, S={S}, {G} group(s), "
+                       f"{shape.dtype}",
+           "value": round(gbs, 1), "unit": "GB/s", "us_per_call": round(t * 1e6, 2), "nsets": nsets,
+           "tokens_per_s": round(Bt / t, 1),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(gbs / HBM_PEAK_GBS, 4), "alg_bytes": nbytes,
+                        "traffic": measured_traffic("ssd_step:" + name, STEP_SOURCES)}}
+    if want_cpu:
+        res["cpu_baseline"] = cpu_baseline_step(inp, nbytes)
+    return res
 
 
 # ---------------------------------------------------------------------------
@@ -380,6 +436,7 @@ def main():
         line["cpu_baseline"] = ssd["cpu_baseline"]
     if not args.no_scan:
         line["linear_scan"] = bench_scan(args.scan_workload, args.steps, args.warmup, want_cpu)
+        line["ssd_step"] = bench_step("decode_large", args.steps, args.warmup, want_cpu)
     print(json.dumps(line), flush=True)
 
 

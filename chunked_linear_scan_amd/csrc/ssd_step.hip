@@ -12,7 +12,10 @@
 // (batch, head).  A row of the state (one head-dim channel, S states) is held
 // by S/4 lanes as float4s, so one wave instruction reads or writes 1 KB of
 // consecutive state (64 / (S/4) rows).  Each thread loads kStU row steps
-// before it computes, so a workgroup keeps 16 KB of loads in flight.  The
+// before it computes, so a workgroup keeps 16 KB of loads in flight (eight
+// steps measured slower).  The state is read and written with non-temporal
+// accesses: each byte is touched once per token, and keeping it out of the
+// caches measured 14 % faster on a 64-sequence batch of 80 heads.  The
 // output's sum over the states is an xor-shuffle tree inside each row's lanes
 // (a fixed order: the result is the same from run to run).
 #include "common.hpp"
@@ -79,8 +82,8 @@ __global__ __launch_bounds__(kStThreads) void ssd_step_kernel(StepParams p) {
         for (int u = 0; u < kStU; ++u) {
             row[u] = p0 + (u * 4 + wave) * R + sub;
             const bool ok = row[u] < p.P;
-            hv[u] = ok ? *reinterpret_cast<const f32x4*>(hb + int64_t(row[u]) * p.S + 4 * l)
-                       : f32x4{0.f, 0.f, 0.f, 0.f};
+            const f32x4* src = reinterpret_cast<const f32x4*>(hb + int64_t(row[u]) * p.S + 4 * l);
+            hv[u] = ok ? __builtin_nontemporal_load(src) : f32x4{0.f, 0.f, 0.f, 0.f};
             xv[u] = ok ? load_e<BF16>(p.x, xb + row[u]) : 0.0f;
         }
 #pragma unroll
@@ -89,7 +92,7 @@ __global__ __launch_bounds__(kStThreads) void ssd_step_kernel(StepParams p) {
             f32x4 hn;
 #pragma unroll
             for (int e = 0; e < 4; ++e) hn[e] = fmaf(decay, hv[u][e], xv[u] * bv[e]);
-            if (ok) *reinterpret_cast<f32x4*>(hb + int64_t(row[u]) * p.S + 4 * l) = hn;
+            if (ok) __builtin_nontemporal_store(hn, reinterpret_cast<f32x4*>(hb + int64_t(row[u]) * p.S + 4 * l));
             float part = hn[0] * cv[0] + hn[1] * cv[1] + hn[2] * cv[2] + hn[3] * cv[3];
 #pragma unroll
             for (int o = LS / 2; o >= 1; o >>= 1) part += __shfl_xor(part, o, 64);

@@ -12,12 +12,16 @@ Workloads (synthetic; each is named by what it is and its sizes):
 * ``ssd_large``  batch 4, L=8192, 80 heads, P=64, S=128, 1 group, chunk 256, bf16
 * ``ssd_long``   batch 1, L=65536, 64 heads, P=64, S=128, 8 groups, chunk 128,
   bf16, slower decay (dt shift -4) and a nonzero initial state ~ N(0, 0.1^2)
+* ``decode_large`` one decode token (``ssd_step``) for 64 sequences of the
+  large-model layer's heads: batch 64, 80 heads, P=64, S=128, 1 group, bf16,
+  state ~ N(0, 0.5^2)
 
 SSD draw order (one ``torch.Generator`` seeded per workload): x, B, C, dt_raw,
 A_u, D, h0.  dt = softplus(dt_raw + shift); A = -exp(U(0, ln 16)).  x/B/C are
 drawn in fp32 and rounded to bf16 (round-to-nearest-even) where the workload is
 bf16.  Scan draw order: a_u, mask_u, b; a ~ U(0.9, 1.0) with an independent 1 %
-of entries replaced by 1 - 1e-6 (decay close to one).
+of entries replaced by 1 - 1e-6 (decay close to one).  Decode-step draw order:
+h, x, B, C, dt_raw, A_u, D (same distributions as the SSD workloads).
 """
 from __future__ import annotations
 
@@ -98,6 +102,45 @@ def make_scan_inputs(rows: int, length: int, seed: int) -> dict:
     a = 0.9 + 0.1 * a_u
     a = torch.where(mask_u < 0.01, torch.full_like(a, 1.0 - 1e-6), a)
     return {"a": a.to(torch.float32).contiguous(), "b": b.contiguous()}
+
+
+@dataclasses.dataclass(frozen=True)
+class StepShape:
+    batch: int
+    nheads: int
+    headdim: int
+    dstate: int
+    ngroups: int
+    dtype: str  # "f32" or "bf16" for x, B, C and y
+    dt_shift: float = -2.0
+    h_std: float = 0.5
+
+
+STEP_WORKLOADS = {
+    "decode_large": (StepShape(64, 80, 64, 128, 1, "bf16"), 5),
+}
+
+
+def make_step_inputs(shape: StepShape, seed: int) -> dict:
+    """Draw one decode-token input set on the host: h [Bt,H,P,S] fp32, x [Bt,H,P],
+    dt [Bt,H] fp32, A [H] fp32, B and C [Bt,G,S], D [H] fp32."""
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    Bt, H, P, S, G = shape.batch, shape.nheads, shape.headdim, shape.dstate, shape.ngroups
+    dt_ = _torch_dtype(shape.dtype)
+    h = torch.randn(Bt, H, P, S, generator=g) * shape.h_std
+    x = torch.randn(Bt, H, P, generator=g).to(dt_)
+    B = torch.randn(Bt, G, S, generator=g).to(dt_)
+    C = torch.randn(Bt, G, S, generator=g).to(dt_)
+    dt = torch.nn.functional.softplus(torch.randn(Bt, H, generator=g) + shape.dt_shift)
+    A = -torch.exp(torch.rand(H, generator=g) * math.log(16.0))
+    D = torch.randn(H, generator=g)
+    return {"h": h.contiguous(), "x": x.contiguous(), "dt": dt.contiguous(), "A": A.contiguous(),
+            "B": B.contiguous(), "C": C.contiguous(), "D": D.contiguous()}
+
+
+def step_workload(name: str) -> dict:
+    shape, seed = STEP_WORKLOADS[name]
+    return make_step_inputs(shape, seed)
 
 
 def ssd_workload(name: str) -> dict:
