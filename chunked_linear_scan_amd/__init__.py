@@ -57,6 +57,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.ssd_fwd_workspace_size.restype = sz
         lib.ssd_fwd.argtypes = [vp, fp, fp, vp, vp, fp, fp] + [i64] * 7 + [ctypes.c_int, vp, fp, vp, sz, vp]
         lib.ssd_fwd.restype = ctypes.c_int
+        lib.linear_scan_three_pass_workspace_size.argtypes = [i64, i64]
+        lib.linear_scan_three_pass_workspace_size.restype = sz
+        lib.linear_scan_three_pass.argtypes = [fp, fp, fp, i64, i64, vp, sz, vp]
+        lib.linear_scan_three_pass.restype = ctypes.c_int
         lib.ssd_step.argtypes = [fp, vp, fp, fp, vp, vp, fp] + [i64] * 5 + [ctypes.c_int, vp, vp]
         lib.ssd_step.restype = ctypes.c_int
         _lib = lib
@@ -177,6 +181,26 @@ def ssd_fwd(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, want_final_state:
     return y, hf
 
 
+def linear_scan_three_pass(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """h[r, t] = a[r, t] h[r, t-1] + b[r, t] by the three-pass (block scan, spine,
+    apply) kernels: the independent cross-check of ``linear_scan``."""
+    lib = load_library()
+    _check_cuda("a", a, torch.float32)
+    if a.dim() != 2:
+        raise ValueError("a must be [rows, length]")
+    _check_cuda("b", b, torch.float32, a.shape)
+    rows, L = a.shape
+    h = torch.empty_like(a) if out is None else out
+    _check_cuda("out", h, torch.float32, a.shape)
+    need = lib.linear_scan_three_pass_workspace_size(rows, L)
+    ws = torch.empty(max(need, 16), dtype=torch.uint8, device=a.device)
+    st = lib.linear_scan_three_pass(_ptr(a), _ptr(b), _ptr(h), rows, L, _ptr(ws), ws.numel(),
+                                    _stream_handle(a.device))
+    if st != SSD_OK:
+        raise SSDError(st, "linear_scan_three_pass")
+    return h
+
+
 def ssd_step(h, x, dt, A, B, C, D=None, out: torch.Tensor | None = None):
     """One decode token: updates the state h [Bt,H,P,S] (fp32) in place and
     returns y [Bt,H,P].
@@ -210,5 +234,5 @@ def ssd_step(h, x, dt, A, B, C, D=None, out: torch.Tensor | None = None):
     return y
 
 
-__all__ = ["linear_scan", "ssd_fwd", "ssd_step", "load_library", "strerror", "SSDError", "LIB_PATH",
+__all__ = ["linear_scan", "linear_scan_three_pass", "ssd_fwd", "ssd_step", "load_library", "strerror", "SSDError", "LIB_PATH",
            "SSD_F32", "SSD_BF16"]

@@ -119,6 +119,26 @@ int ssd_fwd(const void* x, const float* dt, const float* A, const void* B, const
     return cls_ssd_launch(s, args, static_cast<hipStream_t>(stream));
 }
 
+static bool ls3_sizes_ok(int64_t rows, int64_t L) {
+    if (rows <= 0 || L <= 0 || L > (int64_t(1) << 40) || rows > (int64_t(1) << 40)) return false;
+    const int64_t ntiles = (L + 8191) / 8192;
+    return rows * ntiles < (int64_t(1) << 31) && rows * L < (int64_t(1) << 46);
+}
+
+size_t linear_scan_three_pass_workspace_size(int64_t rows, int64_t length) {
+    return ls3_sizes_ok(rows, length) ? cls_ls3_workspace_bytes(rows, length) : 0;
+}
+
+int linear_scan_three_pass(const float* a, const float* b, float* h, int64_t rows, int64_t length,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    if (!a || !b || !h || !workspace) return SSD_ERR_NULL;
+    if (!ls3_sizes_ok(rows, length)) return SSD_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(h) || !aligned16(workspace)) return SSD_ERR_ALIGN;
+    if (workspace_bytes < cls_ls3_workspace_bytes(rows, length)) return SSD_ERR_WORKSPACE;
+    return cls_ls3_launch(a, b, h, rows, length, workspace, static_cast<hipStream_t>(stream)) == 0 ? SSD_OK
+                                                                                                 : SSD_ERR_HIP;
+}
+
 int ssd_step(float* h, const void* x, const float* dt, const float* A, const void* B, const void* C,
              const float* D, int64_t batch, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
              int dtype, void* y, void* stream) {

@@ -35,6 +35,9 @@ int cls_launch_linear_scan(const float* a, const float* b, float* h, int64_t row
 int cls_ssd_check(const SsdShape& s);
 size_t cls_ssd_workspace_bytes(const SsdShape& s);
 int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t stream);
+// Three-pass linear scan (linear_scan_3pass.hip); shapes already validated.
+size_t cls_ls3_workspace_bytes(int64_t rows, int64_t L);
+int cls_ls3_launch(const float* a, const float* b, float* h, int64_t rows, int64_t L, void* ws, hipStream_t stream);
 // One decode token (ssd_step.hip); shapes already validated.  0, or -7 when the
 // launch fails, -8 for a state size without a kernel.
 int cls_ssd_step_launch(float* h, const void* x, const float* dt, const float* A, const void* B,

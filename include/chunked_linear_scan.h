@@ -109,6 +109,24 @@ int linear_scan(const float* a, const float* b, float* h, int64_t rows,
                 void* stream);
 
 /*
+ * The same scalar recurrence as three launches: block scan, spine scan over
+ * the tile aggregates, prefix application ("Selective-scan CUDA kernels",
+ * section "The five kernels", level 2).  It moves seven arrays' worth of
+ * traffic where linear_scan moves three, and shares no code with it: an
+ * independent cross-check of the single-pass kernel.  Same layouts and
+ * alignment as linear_scan; h is also used as scratch between the passes.
+ * The workspace (size from linear_scan_three_pass_workspace_size, 16-byte
+ * aligned) needs no initial contents.  Results agree with linear_scan to
+ * fp32 rounding (the combine order inside a tile differs), and are the same
+ * from run to run.
+ */
+size_t linear_scan_three_pass_workspace_size(int64_t rows, int64_t length);
+
+int linear_scan_three_pass(const float* a, const float* b, float* h, int64_t rows,
+                           int64_t length, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
+/*
  * One decode token of the same recurrence, for sequential inference: the
  * recurrent form of "Accelerating Mamba-2 with high-performance forward pass
  * kernels in NVIDIA cuTile", section "Mamba-2 architecture", which that

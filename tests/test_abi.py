@@ -27,7 +27,7 @@ def header_functions():
 def test_header_lists_expected_entry_points():
     assert set(header_functions()) == {
         "ssd_fwd_workspace_size", "ssd_fwd", "linear_scan_workspace_size", "linear_scan",
-        "ssd_step", "ssd_strerror"}
+        "ssd_step", "linear_scan_three_pass_workspace_size", "linear_scan_three_pass", "ssd_strerror"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -120,3 +120,14 @@ def test_ssd_step_rejects_bad_arguments():
     assert call(S=2) == -8
     assert call(h=ctypes.c_void_p(0x10008)) == -5
     assert call(x=ctypes.c_void_p(0x10001)) == -5
+
+
+def test_linear_scan_three_pass_rejects_bad_arguments():
+    lib = cls.load_library()
+    ws = lib.linear_scan_three_pass_workspace_size(4, 100)
+    assert ws >= 4 * 100 * 4
+    assert lib.linear_scan_three_pass_workspace_size(0, 100) == 0
+    assert lib.linear_scan_three_pass(None, FAKE, FAKE, 4, 100, FAKE, ws, None) == -1
+    assert lib.linear_scan_three_pass(FAKE, FAKE, FAKE, 4, 0, FAKE, ws, None) == -2
+    assert lib.linear_scan_three_pass(FAKE, FAKE, ctypes.c_void_p(0x10004), 4, 100, FAKE, ws, None) == -5
+    assert lib.linear_scan_three_pass(FAKE, FAKE, FAKE, 4, 100, FAKE, ws - 1, None) == -6
