@@ -216,6 +216,38 @@ def cpu_baseline_scan(inp):
             "sample": f"whole workload ({tuple(inp['a'].shape)}), wall {wall:.2f}s"}
 
 
+def bench_scan3(name, steps, warmup, scan_us):
+    """The three-pass scan (block scan, spine, apply) on the same workload, and
+    the traffic model it tests: seven arrays of traffic against the single
+    pass's three, so at equal bus efficiency 7/3 of its time."""
+    import torch
+    import chunked_linear_scan_amd as cls
+    from chunked_linear_scan_amd import workloads
+    inp = workloads.scan_workload(name)
+    rows, L = inp["a"].shape
+    nbytes = 12 * rows * L
+    nsets = max(1, math.ceil((1 << 30) / nbytes))
+    dev = torch.device("cuda:0")
+    lib = cls.load_library()
+    sets = [(inp["a"].to(dev), inp["b"].to(dev), torch.empty(rows, L, device=dev)) for _ in range(nsets)]
+    ws = torch.empty(lib.linear_scan_three_pass_workspace_size(rows, L), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step(i):
+        a, b, h = sets[i]
+        st = lib.linear_scan_three_pass(cls._ptr(a), cls._ptr(b), cls._ptr(h), rows, L, cls._ptr(ws), ws.numel(),
+                                        cls._stream_handle(dev))
+        if st != 0:
+            raise RuntimeError(cls.strerror(st))
+
+    t = time_loop(step, nsets, steps, warmup, stream)
+    moved = 28 * rows * L
+    return {"workload": f"{name}: {rows} rows x {L} fp32", "value": round(nbytes / t / 1e9, 1), "unit": "GB/s",
+            "us_per_call": round(t * 1e6, 2), "moved_bytes": moved, "moved_gbs": round(moved / t / 1e9, 1),
+            "moved_frac_of_peak": round(moved / t / 1e9 / HBM_PEAK_GBS, 4),
+            "time_ratio_to_single_pass": round(t * 1e6 / scan_us, 3), "traffic_model_ratio": round(7 / 3, 3)}
+
+
 def cpu_baseline_step(inp, nbytes):
     from oracle import ssd as ossd
     arrs = [inp[k].to(torch_f64()).numpy() for k in ("h", "x", "dt", "A", "B", "C", "D")]
@@ -436,6 +468,8 @@ def main():
         line["cpu_baseline"] = ssd["cpu_baseline"]
     if not args.no_scan:
         line["linear_scan"] = bench_scan(args.scan_workload, args.steps, args.warmup, want_cpu)
+        line["linear_scan_three_pass"] = bench_scan3(args.scan_workload, args.steps, args.warmup,
+                                                     line["linear_scan"]["us_per_call"])
         line["ssd_step"] = bench_step("decode_large", args.steps, args.warmup, want_cpu)
     print(json.dumps(line), flush=True)
 
