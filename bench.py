@@ -401,9 +401,46 @@ def bench_scan(name, steps, warmup, want_cpu):
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(gbs / HBM_PEAK_GBS, 4),
                         "traffic": measured_traffic("linear_scan:" + name, SCAN_SOURCES)}}
+
+    # A plain elementwise kernel with the same traffic (read two arrays, write
+    # one) on the same buffers: the practical streaming ceiling for this
+    # access pattern, reported beside the scan (not part of the scan).
+    def mul_step(i):
+        a, b, h = sets[i]
+        torch.mul(a, b, out=h)
+
+    tm = time_loop(mul_step, nsets, steps, warmup, stream)
+    res["elementwise_ceiling"] = {"kernel": "torch.mul(a, b, out=h)", "us_per_call": round(tm * 1e6, 2),
+                                  "GB/s": round(nbytes / tm / 1e9, 1), "scan_over_ceiling": round(tm / t, 3)}
     if want_cpu:
         res["cpu_baseline"] = cpu_baseline_scan(inp)
     return res
+
+
+def scan_ceiling_sweep(steps, warmup):
+    """linear_scan against torch.mul(a, b, out=h), which moves the same bytes,
+    at 96 MiB per array and several row lengths, plus twice and half that size
+    at L = 65536."""
+    import torch
+    import chunked_linear_scan_amd as cls
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator(device=dev).manual_seed(1)
+    for rows, L in [(384, 65536), (768, 65536), (192, 65536), (3072, 8186), (1536, 16384), (96, 262144),
+                    (24, 1048576)]:
+        nsets = 3
+        sets = [(0.9 + 0.1 * torch.rand(rows, L, device=dev, generator=g),
+                 torch.randn(rows, L, device=dev, generator=g), torch.empty(rows, L, device=dev))
+                for _ in range(nsets)]
+        ws = torch.zeros(cls.load_library().linear_scan_workspace_size(rows, L), dtype=torch.uint8, device=dev)
+        ts = time_loop(lambda i: cls.linear_scan(sets[i][0], sets[i][1], out=sets[i][2], workspace=ws), nsets,
+                       steps, warmup, stream)
+        tm = time_loop(lambda i: torch.mul(sets[i][0], sets[i][1], out=sets[i][2]), nsets, steps, warmup, stream)
+        nb = 12 * rows * L
+        print(json.dumps({"rows": rows, "L": L, "scan_us": round(ts * 1e6, 2), "scan_GBs": round(nb / ts / 1e9, 1),
+                          "mul_us": round(tm * 1e6, 2), "mul_GBs": round(nb / tm / 1e9, 1),
+                          "mul_over_scan": round(tm / ts, 3)}), flush=True)
+        del sets, ws
 
 
 def main():
@@ -419,6 +456,9 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run three plain 1 GiB device copies (the known-size reference that "
                          "scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
+    ap.add_argument("--scan-ceiling-sweep", action="store_true",
+                    help="time linear_scan and torch.mul (same traffic) over a sweep of row lengths, "
+                         "print one JSON line per shape, then exit")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc counter files of "
                          "--copy-probe runs (FETCH_SIZE, WRITE_SIZE) for --workload, then exit")
@@ -434,6 +474,9 @@ def main():
     if not torch.cuda.is_available():
         print("no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.scan_ceiling_sweep:
+        scan_ceiling_sweep(args.steps, args.warmup)
+        return
     if args.copy_probe:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")
         dst = torch.empty_like(src)
