@@ -372,6 +372,24 @@ def bench_ssd(name, steps, warmup, want_cpu):
                      "call_frac_of_roofline": round(t_roof / t, 4)},
         "shape": shape,
     }
+    # The autotuner (ssd_fwd_autotune) on the same inputs: the plan it keeps
+    # and ssd_fwd's time on that plan, beside the built-in heuristic's, which
+    # is what the timed steps above ran.  The table is cleared afterwards.
+    heur = cls.ssd_fwd_plan(shape.batch, shape.seqlen, shape.nheads, shape.headdim, shape.dstate,
+                            shape.ngroups, shape.chunk, inp["x"].dtype)
+    d0 = sets[0]
+    _, _, info = cls.ssd_fwd_autotune(d0["x"], d0["dt"], d0["A"], d0["B"], d0["C"], d0["D"], d0["h0"],
+                                      chunk=shape.chunk, reps=5, out=d0["y"])
+    t_tuned = time_loop(step, nsets, steps, warmup, stream)
+    cls.ssd_fwd_autotune_reset()
+    # the heuristic again, right after, so that both loops run in the same
+    # state of the GPU (a later loop tends to run a little faster)
+    t_heur = time_loop(step, nsets, steps, warmup, stream)
+    res["autotune"] = {"plan": {"nsegs": info["nsegs"], "nsplit": info["nsplit"]},
+                       "heuristic_plan": {"nsegs": heur["nsegs"], "nsplit": heur["nsplit"]},
+                       "us_per_call_tuned": round(t_tuned * 1e6, 2),
+                       "us_per_call_heuristic": round(t_heur * 1e6, 2),
+                       "speedup": round(t_heur / t_tuned, 3)}
     if want_cpu:
         res["cpu_baseline"] = cpu_baseline_ssd(inp, shape)
     return res
@@ -506,6 +524,7 @@ def main():
                    "global_batch": shape.batch, "seq_len": shape.seqlen, "parallelism": "single GPU",
                    "buffer_sets": ssd["nsets"]},
         "roofline": ssd["roofline"],
+        "autotune": ssd["autotune"],
     }
     if "cpu_baseline" in ssd:
         line["cpu_baseline"] = ssd["cpu_baseline"]

@@ -63,6 +63,14 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.linear_scan_three_pass.restype = ctypes.c_int
         lib.ssd_step.argtypes = [fp, vp, fp, fp, vp, vp, fp] + [i64] * 5 + [ctypes.c_int, vp, vp]
         lib.ssd_step.restype = ctypes.c_int
+        pi64 = ctypes.POINTER(ctypes.c_int64)
+        lib.ssd_fwd_autotune.argtypes = lib.ssd_fwd.argtypes + [ctypes.c_int, pi64, pi64,
+                                                                ctypes.POINTER(ctypes.c_float)]
+        lib.ssd_fwd_autotune.restype = ctypes.c_int
+        lib.ssd_fwd_plan.argtypes = [i64] * 7 + [ctypes.c_int, pi64, pi64]
+        lib.ssd_fwd_plan.restype = ctypes.c_int
+        lib.ssd_fwd_autotune_reset.argtypes = []
+        lib.ssd_fwd_autotune_reset.restype = None
         _lib = lib
         return lib
 
@@ -140,14 +148,8 @@ def linear_scan(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = Non
     return h
 
 
-def ssd_fwd(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, want_final_state: bool = True,
-            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
-    """Mamba-2 SSD chunked forward pass.  Returns (y, h_final or None).
-
-    x [Bt,L,H,P] and B, C [Bt,L,G,S] in fp32 or bf16 (same dtype); dt
-    [Bt,L,H], A [H], D [H] (optional) and h0 [Bt,H,P,S] (optional) in fp32.
-    """
-    lib = load_library()
+def _ssd_fwd_args(lib, x, dt, A, B, C, D, h0, chunk, want_final_state, out, workspace):
+    """Checks ssd_fwd's tensors and returns the C call's argument list."""
     if x.dtype not in _DTYPE_CODE:
         raise TypeError("x must be float32 or bfloat16")
     _check_cuda("x", x, x.dtype)
@@ -173,12 +175,57 @@ def ssd_fwd(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, want_final_state:
     ws = workspace
     if ws is None:
         ws = _ssd_ws.get(x.device, max(need, 1))
-    st = lib.ssd_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0),
-                     Bt, L, H, P, S, G, int(chunk), code, _ptr(y), _ptr(hf), _ptr(ws), ws.numel(),
-                     _stream_handle(x.device))
+    args = [_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), Bt, L, H, P, S, G, int(chunk), code,
+            _ptr(y), _ptr(hf), _ptr(ws), ws.numel(), _stream_handle(x.device)]
+    return args, y, hf
+
+
+def ssd_fwd(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, want_final_state: bool = True,
+            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
+    """Mamba-2 SSD chunked forward pass.  Returns (y, h_final or None).
+
+    x [Bt,L,H,P] and B, C [Bt,L,G,S] in fp32 or bf16 (same dtype); dt
+    [Bt,L,H], A [H], D [H] (optional) and h0 [Bt,H,P,S] (optional) in fp32.
+    """
+    lib = load_library()
+    args, y, hf = _ssd_fwd_args(lib, x, dt, A, B, C, D, h0, chunk, want_final_state, out, workspace)
+    st = lib.ssd_fwd(*args)
     if st != SSD_OK:
         raise SSDError(st, "ssd_fwd")
     return y, hf
+
+
+def ssd_fwd_autotune(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, reps: int = 5,
+                     want_final_state: bool = True, out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None):
+    """Times ssd_fwd's candidate segment plans on these inputs and keeps the
+    fastest for this shape (later ssd_fwd calls use it).  Blocks until done.
+    Returns (y, h_final or None, {"nsegs", "nsplit", "ms_per_call"}); y and
+    h_final are the chosen plan's result.  nsegs == 0: nothing to tune."""
+    lib = load_library()
+    args, y, hf = _ssd_fwd_args(lib, x, dt, A, B, C, D, h0, chunk, want_final_state, out, workspace)
+    nsegs, nsplit, ms = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_float()
+    st = lib.ssd_fwd_autotune(*args, int(reps), ctypes.byref(nsegs), ctypes.byref(nsplit), ctypes.byref(ms))
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_fwd_autotune")
+    return y, hf, {"nsegs": nsegs.value, "nsplit": nsplit.value, "ms_per_call": ms.value}
+
+
+def ssd_fwd_plan(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype=torch.bfloat16):
+    """The segment plan ssd_fwd uses for a shape: {"nsegs", "nsplit",
+    "source": "tuned" | "heuristic" | "none"}.  Launches nothing."""
+    lib = load_library()
+    nsegs, nsplit = ctypes.c_int64(), ctypes.c_int64()
+    st = lib.ssd_fwd_plan(batch, seqlen, nheads, headdim, dstate, ngroups, int(chunk), _DTYPE_CODE[dtype],
+                          ctypes.byref(nsegs), ctypes.byref(nsplit))
+    if st < 0:
+        raise SSDError(st, "ssd_fwd_plan")
+    return {"nsegs": nsegs.value, "nsplit": nsplit.value, "source": {0: "heuristic", 1: "tuned", 2: "none"}[st]}
+
+
+def ssd_fwd_autotune_reset():
+    """Forget every tuned plan (ssd_fwd falls back to its built-in heuristic)."""
+    load_library().ssd_fwd_autotune_reset()
 
 
 def linear_scan_three_pass(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
@@ -234,5 +281,6 @@ def ssd_step(h, x, dt, A, B, C, D=None, out: torch.Tensor | None = None):
     return y
 
 
-__all__ = ["linear_scan", "linear_scan_three_pass", "ssd_fwd", "ssd_step", "load_library", "strerror", "SSDError", "LIB_PATH",
+__all__ = ["linear_scan", "linear_scan_three_pass", "ssd_fwd", "ssd_fwd_autotune", "ssd_fwd_plan",
+           "ssd_fwd_autotune_reset", "ssd_step", "load_library", "strerror", "SSDError", "LIB_PATH",
            "SSD_F32", "SSD_BF16"]

@@ -101,23 +101,55 @@ size_t ssd_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int
     return cls_ssd_workspace_bytes(s);
 }
 
+// The checks ssd_fwd and ssd_fwd_autotune make before any launch.
+static int ssd_fwd_validate(const SsdShape& s, const SsdArgs& a, size_t workspace_bytes) {
+    if (!a.x || !a.dt || !a.A || !a.B || !a.C || !a.y) return SSD_ERR_NULL;
+    const int st = cls_ssd_check(s);
+    if (st != SSD_OK) return st;
+    const size_t need = cls_ssd_workspace_bytes(s);
+    if (need > 0 && !a.workspace) return SSD_ERR_NULL;
+    if (workspace_bytes < need) return SSD_ERR_WORKSPACE;
+    const void* ptrs[] = {a.x, a.dt, a.A, a.B, a.C, a.D, a.h0, a.y, a.h_final, a.workspace};
+    for (const void* p : ptrs)
+        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
+    return SSD_OK;
+}
+
 int ssd_fwd(const void* x, const float* dt, const float* A, const void* B, const void* C,
             const float* D, const float* h0, int64_t batch, int64_t seqlen, int64_t nheads,
             int64_t headdim, int64_t dstate, int64_t ngroups, int64_t chunk, int dtype, void* y,
             float* h_final, void* workspace, size_t workspace_bytes, void* stream) {
-    if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_NULL;
-    SsdShape s{batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype};
-    const int st = cls_ssd_check(s);
+    const SsdShape s{batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype};
+    const SsdArgs args{x, dt, A, B, C, D, h0, y, h_final, workspace};
+    const int st = ssd_fwd_validate(s, args, workspace_bytes);
     if (st != SSD_OK) return st;
-    const size_t need = cls_ssd_workspace_bytes(s);
-    if (need > 0 && !workspace) return SSD_ERR_NULL;
-    if (workspace_bytes < need) return SSD_ERR_WORKSPACE;
-    const void* ptrs[] = {x, dt, A, B, C, D, h0, y, h_final, workspace};
-    for (const void* p : ptrs)
-        if (p && !aligned16(p)) return SSD_ERR_ALIGN;
-    SsdArgs args{x, dt, A, B, C, D, h0, y, h_final, workspace};
     return cls_ssd_launch(s, args, static_cast<hipStream_t>(stream));
 }
+
+int ssd_fwd_autotune(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                     const float* D, const float* h0, int64_t batch, int64_t seqlen, int64_t nheads,
+                     int64_t headdim, int64_t dstate, int64_t ngroups, int64_t chunk, int dtype, void* y,
+                     float* h_final, void* workspace, size_t workspace_bytes, void* stream, int reps,
+                     int64_t* nsegs, int64_t* nsplit, float* ms_per_call) {
+    if (!nsegs || !nsplit || !ms_per_call) return SSD_ERR_NULL;
+    if (reps < 1 || reps > 1000) return SSD_ERR_SHAPE;
+    const SsdShape s{batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype};
+    const SsdArgs args{x, dt, A, B, C, D, h0, y, h_final, workspace};
+    const int st = ssd_fwd_validate(s, args, workspace_bytes);
+    if (st != SSD_OK) return st;
+    return cls_ssd_autotune(s, args, static_cast<hipStream_t>(stream), reps, nsegs, nsplit, ms_per_call);
+}
+
+int ssd_fwd_plan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
+                 int64_t chunk, int dtype, int64_t* nsegs, int64_t* nsplit) {
+    if (!nsegs || !nsplit) return SSD_ERR_NULL;
+    const SsdShape s{batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype};
+    const int st = cls_ssd_check(s);
+    if (st != SSD_OK) return st;
+    return cls_ssd_plan_query(s, nsegs, nsplit);
+}
+
+void ssd_fwd_autotune_reset(void) { cls_ssd_autotune_reset(); }
 
 static bool ls3_sizes_ok(int64_t rows, int64_t L) {
     if (rows <= 0 || L <= 0 || L > (int64_t(1) << 40) || rows > (int64_t(1) << 40)) return false;

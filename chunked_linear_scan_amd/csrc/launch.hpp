@@ -35,6 +35,14 @@ int cls_launch_linear_scan(const float* a, const float* b, float* h, int64_t row
 int cls_ssd_check(const SsdShape& s);
 size_t cls_ssd_workspace_bytes(const SsdShape& s);
 int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t stream);
+// Times the fused path's candidate segment plans on these arguments, keeps the
+// fastest for the shape and leaves its result in y / h_final (blocking).
+int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t stream, int reps, int64_t* nsegs,
+                     int64_t* nsplit, float* ms);
+// The segment plan ssd_fwd uses for a shape: 1 tuned, 0 heuristic, 2 no plan
+// (not the fused path); negative status on error.
+int cls_ssd_plan_query(const SsdShape& s, int64_t* nsegs, int64_t* nsplit);
+void cls_ssd_autotune_reset();
 // Three-pass linear scan (linear_scan_3pass.hip); shapes already validated.
 size_t cls_ls3_workspace_bytes(int64_t rows, int64_t L);
 int cls_ls3_launch(const float* a, const float* b, float* h, int64_t rows, int64_t L, void* ws, hipStream_t stream);

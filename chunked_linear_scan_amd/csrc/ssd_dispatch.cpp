@@ -1,4 +1,7 @@
 // SSD validation, workspace sizing and dispatch to the fp32 or bf16 path.
+#include <array>
+#include <map>
+#include <mutex>
 #include <vector>
 
 #include "../../include/chunked_linear_scan.h"
@@ -45,8 +48,42 @@ int64_t fused_slots() {
 }
 static int g_force_path = 0;  // 0 auto, 1 the per-(batch, head) chunk kernel, 2 the fused kernel
 
+// Segment plans chosen by the autotuner, per (device, shape).
+using TuneKey = std::array<int64_t, 9>;
+std::mutex g_tune_mu;
+std::map<TuneKey, SegChoice> g_tuned;
+
+TuneKey tune_key(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G, int64_t chunk, int dtype) {
+    chunk = chunk > kFusedMaxChunk ? kFusedMaxChunk : chunk;  // the sub-chunk the kernel runs
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    return TuneKey{dev, batch, L, H, P, S, G, chunk, dtype};
+}
+
+bool tuned_choice(const TuneKey& k, SegChoice* out) {
+    std::lock_guard<std::mutex> lock(g_tune_mu);
+    const auto it = g_tuned.find(k);
+    if (it == g_tuned.end()) return false;
+    *out = it->second;
+    return true;
+}
+
+// The autotuner's search space: no split; the chains left over after whole
+// rounds of the CUs cut into 2..32 segments; every chain cut into 2..32
+// segments.  Plans of more than four rounds of workgroups are left out.
+std::vector<SegChoice> seg_candidates(int64_t nchains, int64_t nc, int64_t slots) {
+    std::vector<SegChoice> v{{1, 0}};
+    const int64_t r = nchains % slots;
+    for (int64_t g : {2, 3, 4, 6, 8, 12, 16, 24, 32}) {
+        if (g > nc) break;
+        if (r > 0 && (nchains - r) + r * g <= 4 * slots) v.push_back({g, r});
+        if (r != nchains && nchains * g <= 4 * slots) v.push_back({g, nchains});
+    }
+    return v;
+}
+
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
-                            int64_t chunk, int dtype) {
+                            int64_t chunk, int dtype, const SegChoice* force) {
     SsdFusedPlan pl{};
     // The kernel's quadratic block is at most 128 tokens: a longer chunk is run
     // as sub-chunks of 128 with the state passed between them, which changes the
@@ -67,9 +104,16 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     // fill them.  A segment costs its output pass plus its share of the
     // aggregate launch (about half its length), which the split must beat.
     int64_t nsegs = 1, nsplit = 0;
-    if (g_segments_override > 0) {
+    SegChoice tuned{};
+    if (force) {
+        nsegs = force->nsegs;
+        nsplit = (force->nsplit > 0 && force->nsplit < nchains) ? force->nsplit : nchains;
+    } else if (g_segments_override > 0) {
         nsegs = g_segments_override;
         nsplit = (g_split_override > 0 && g_split_override < nchains) ? g_split_override : nchains;
+    } else if (tuned_choice(tune_key(batch, L, H, P, S, G, chunk, dtype), &tuned)) {
+        nsegs = tuned.nsegs;
+        nsplit = tuned.nsplit;
     } else {
         const int64_t slots = fused_slots();
         const int64_t r = nchains % slots;
@@ -235,16 +279,40 @@ extern "C" int cls_ssd_check(const SsdShape& s) {
     return SSD_OK;
 }
 
+namespace {
+
+// The candidate plans of a fused-path shape (empty when the fused path is not used).
+std::vector<cls::SegChoice> fused_candidates(const SsdShape& s) {
+    const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
+                                                     s.ngroups, s.chunk, s.dtype);
+    if (!pl.use) return {};
+    const int64_t nc = (s.seqlen + pl.chunk - 1) / pl.chunk;
+    return cls::seg_candidates(s.batch * s.nheads, nc, cls::fused_slots());
+}
+
+}  // namespace
+
+// The workspace fits every plan the autotuner may choose, so a buffer sized
+// before tuning stays large enough after it.
 extern "C" size_t cls_ssd_workspace_bytes(const SsdShape& s) {
     if (s.dtype == SSD_F32) return 0;
     const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
                                                      s.ngroups, s.chunk, s.dtype);
-    if (pl.use) return pl.bytes;
+    if (pl.use) {
+        size_t bytes = pl.bytes;
+        for (const cls::SegChoice& c : fused_candidates(s)) {
+            const cls::SsdFusedPlan q = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
+                                                            s.ngroups, s.chunk, s.dtype, &c);
+            if (q.use && q.bytes > bytes) bytes = q.bytes;
+        }
+        return bytes;
+    }
     const int64_t TT = cls::bf16_tile_tokens(int(s.chunk));
     return size_t(s.batch) * size_t(nchunks(s)) * size_t(s.ngroups) * size_t(TT * TT) * 2 + 256;
 }
 
-extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t stream) {
+static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const cls::SegChoice* force,
+                           hipStream_t stream) {
     if (s.dtype == SSD_F32) {
         cls::SsdF32Params p{a.x, a.dt, a.A, a.B, a.C, a.D, a.h0, a.y, a.h_final, s.batch, s.seqlen,
                             int(s.nheads), int(s.headdim), int(s.dstate), int(s.ngroups), int(s.chunk)};
@@ -268,7 +336,7 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
     p.chunk = int(s.chunk);
     p.nchunks = int(nchunks(s));
     const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
-                                                     s.ngroups, s.chunk, s.dtype);
+                                                     s.ngroups, s.chunk, s.dtype, force);
     if (pl.use) {
         p.chunk = pl.chunk;
         p.nchunks = int((s.seqlen + pl.chunk - 1) / pl.chunk);
@@ -314,4 +382,95 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
     const int st = cls::ssd_bf16_launch(TT, int(s.headdim), int(s.dstate), p, stream);
     if (st == -8) return SSD_ERR_UNSUPPORTED;
     return st == 0 ? SSD_OK : SSD_ERR_HIP;
+}
+
+extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t stream) {
+    return ssd_launch_plan(s, a, nullptr, stream);
+}
+
+// Autotuner of the fused path's segment plan (the one run-time choice of its
+// launches): each candidate runs once untimed and `reps` times between two
+// events on the caller's stream; the fastest mean wins and is kept for the
+// shape on the current device.  Candidates that reduce to the same plan are
+// timed once.  The call ends with one more pass on the chosen plan, so y and
+// h_final hold exactly what a later ssd_fwd call returns.
+extern "C" int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t stream, int reps, int64_t* nsegs,
+                                int64_t* nsplit, float* ms) {
+    *nsegs = 0;
+    *nsplit = 0;
+    *ms = 0.0f;
+    const std::vector<cls::SegChoice> cands = fused_candidates(s);
+    if (cands.empty()) return ssd_launch_plan(s, a, nullptr, stream);
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess) return SSD_ERR_HIP;
+    if (hipEventCreate(&e1) != hipSuccess) {
+        (void)hipEventDestroy(e0);
+        return SSD_ERR_HIP;
+    }
+    int st = SSD_OK;
+    float best_ms = 0.0f;
+    cls::SegChoice best{0, 0};
+    std::vector<std::pair<int64_t, int64_t>> seen;
+    for (const cls::SegChoice& c : cands) {
+        const cls::SsdFusedPlan q = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
+                                                        s.ngroups, s.chunk, s.dtype, &c);
+        const std::pair<int64_t, int64_t> eff{q.nsegs, q.nsegs > 1 ? int64_t(q.nchains - q.nwhole) : 0};
+        bool dup = false;
+        for (const auto& e : seen) dup = dup || e == eff;
+        if (dup) continue;
+        seen.push_back(eff);
+        const cls::SegChoice ce{eff.first, eff.second};
+        st = ssd_launch_plan(s, a, &ce, stream);
+        if (st != SSD_OK) break;
+        if (hipEventRecord(e0, stream) != hipSuccess) {
+            st = SSD_ERR_HIP;
+            break;
+        }
+        for (int r = 0; r < reps && st == SSD_OK; ++r) st = ssd_launch_plan(s, a, &ce, stream);
+        if (st != SSD_OK) break;
+        float t = 0.0f;
+        if (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+            hipEventElapsedTime(&t, e0, e1) != hipSuccess) {
+            st = SSD_ERR_HIP;
+            break;
+        }
+        t /= float(reps);
+        if (best.nsegs == 0 || t < best_ms) {
+            best_ms = t;
+            best = ce;
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (st != SSD_OK) return st;
+    {
+        std::lock_guard<std::mutex> lock(cls::g_tune_mu);
+        cls::g_tuned[cls::tune_key(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk,
+                                   s.dtype)] = best;
+    }
+    *nsegs = best.nsegs;
+    *nsplit = best.nsplit;
+    *ms = best_ms;
+    return ssd_launch_plan(s, a, &best, stream);
+}
+
+extern "C" int cls_ssd_plan_query(const SsdShape& s, int64_t* nsegs, int64_t* nsplit) {
+    const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
+                                                     s.ngroups, s.chunk, s.dtype);
+    if (s.dtype == SSD_F32 || !pl.use) {
+        *nsegs = 0;
+        *nsplit = 0;
+        return 2;
+    }
+    *nsegs = pl.nsegs;
+    *nsplit = pl.nsegs > 1 ? int64_t(pl.nchains - pl.nwhole) : 0;
+    cls::SegChoice t{};
+    const bool tuned = cls::tuned_choice(cls::tune_key(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
+                                                       s.ngroups, s.chunk, s.dtype), &t);
+    return tuned && cls::g_segments_override == 0 ? 1 : 0;
+}
+
+extern "C" void cls_ssd_autotune_reset() {
+    std::lock_guard<std::mutex> lock(cls::g_tune_mu);
+    cls::g_tuned.clear();
 }

@@ -92,6 +92,51 @@ int ssd_fwd(const void* x, const float* dt, const float* A, const void* B,
             void* stream);
 
 /*
+ * Per-shape autotuning of ssd_fwd ("Accelerating Mamba-2 with high-performance
+ * forward pass kernels in NVIDIA cuTile", section "Mamba-2 performance
+ * optimization", its autotuner item: a search per input shape, since no one
+ * setting suits every shape).  The one run-time choice of the bf16 head-dim-64
+ * path is its segment plan: how many segments a long (batch, head) chain is
+ * cut into (each segment's start state comes from a separate aggregate
+ * launch), and which chains are cut.  Tile sizes and occupancy are fixed when
+ * the kernels are compiled.
+ *
+ * ssd_fwd_autotune takes exactly ssd_fwd's arguments (same layouts, same
+ * checks, same workspace) plus reps (1..1000).  It runs every candidate plan
+ * on these inputs once untimed and then reps times between two events on
+ * `stream`, and keeps the fastest for this shape on the current device.
+ * Later ssd_fwd calls with the same shape, dtype and chunk on that device use
+ * it.  It returns the chosen plan (*nsegs segments, the last *nsplit chains
+ * cut) and its mean time per call in ms.  y and h_final hold the result of
+ * the chosen plan, which is what ssd_fwd then returns.  Shapes outside the
+ * fused path have nothing to tune: one plain ssd_fwd pass, *nsegs = 0.
+ * The call blocks until its timed runs finish.  The table is process-wide and
+ * guarded by a lock; tuning while other calls of the same shape run changes
+ * their plan only between calls.  ssd_fwd_workspace_size already covers every
+ * candidate plan, so a workspace sized before tuning stays large enough.
+ * Every plan computes the same recurrence; results differ only by fp32
+ * rounding.
+ *
+ * ssd_fwd_plan reports the plan ssd_fwd would use for a shape without
+ * launching anything: returns 1 (a tuned plan), 0 (the built-in heuristic),
+ * 2 (the shape does not take the fused path; *nsegs = *nsplit = 0) or a
+ * negative status.  ssd_fwd_autotune_reset forgets every tuned plan.
+ */
+int ssd_fwd_autotune(const void* x, const float* dt, const float* A, const void* B,
+                     const void* C, const float* D, const float* h0,
+                     int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                     int64_t dstate, int64_t ngroups, int64_t chunk, int dtype,
+                     void* y, float* h_final, void* workspace, size_t workspace_bytes,
+                     void* stream, int reps, int64_t* nsegs, int64_t* nsplit,
+                     float* ms_per_call);
+
+int ssd_fwd_plan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                 int64_t dstate, int64_t ngroups, int64_t chunk, int dtype,
+                 int64_t* nsegs, int64_t* nsplit);
+
+void ssd_fwd_autotune_reset(void);
+
+/*
  * Scalar linear recurrence of "Selective-scan CUDA kernels", section "The
  * problem":  h[r, t] = a[r, t] h[r, t-1] + b[r, t],  h[r, -1] = 0,
  * independently for each of `rows` rows of `length` elements.

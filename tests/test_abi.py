@@ -26,8 +26,8 @@ def header_functions():
 
 def test_header_lists_expected_entry_points():
     assert set(header_functions()) == {
-        "ssd_fwd_workspace_size", "ssd_fwd", "linear_scan_workspace_size", "linear_scan",
-        "ssd_step", "linear_scan_three_pass_workspace_size", "linear_scan_three_pass", "ssd_strerror"}
+        "ssd_fwd_workspace_size", "ssd_fwd", "ssd_fwd_autotune", "ssd_fwd_plan", "ssd_fwd_autotune_reset",
+        "linear_scan_workspace_size", "linear_scan", "ssd_step", "linear_scan_three_pass_workspace_size", "linear_scan_three_pass", "ssd_strerror"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -131,3 +131,46 @@ def test_linear_scan_three_pass_rejects_bad_arguments():
     assert lib.linear_scan_three_pass(FAKE, FAKE, FAKE, 4, 0, FAKE, ws, None) == -2
     assert lib.linear_scan_three_pass(FAKE, FAKE, ctypes.c_void_p(0x10004), 4, 100, FAKE, ws, None) == -5
     assert lib.linear_scan_three_pass(FAKE, FAKE, FAKE, 4, 100, FAKE, ws - 1, None) == -6
+
+
+def test_ssd_autotune_rejects_bad_arguments():
+    """Validation happens on the host before any launch: missing outputs of
+    the tuner, a repetition count out of range, and ssd_fwd's own checks."""
+    lib = cls.load_library()
+    n1, n2, ms = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_float()
+
+    def call(x=FAKE, y=FAKE, reps=3, out=True, Bt=1, T=32, ws_bytes=1 << 30):
+        outs = (ctypes.byref(n1), ctypes.byref(n2), ctypes.byref(ms)) if out else (None, None, None)
+        return lib.ssd_fwd_autotune(x, FAKE, FAKE, FAKE, FAKE, None, None, Bt, 64, 2, 16, 32, 1, T, cls.SSD_BF16,
+                                    y, None, FAKE, ws_bytes, None, reps, *outs)
+
+    assert call(out=False) == -1
+    assert call(reps=0) == -2
+    assert call(reps=1001) == -2
+    assert call(x=None) == -1
+    assert call(y=None) == -1
+    assert call(Bt=0) == -2
+    assert call(T=48) == -4
+    assert call(ws_bytes=0) in (-6, -8)
+
+
+def test_ssd_plan_query_on_host():
+    """The plan ssd_fwd uses is host logic: the built-in heuristic splits the
+    chains left over after whole rounds of 256 CUs when that shortens the
+    last round; fp32 shapes and non-fused shapes report no plan; a forgotten
+    table leaves the heuristic."""
+    import torch
+    cls.ssd_fwd_autotune_reset()
+    # 4 x 80 chains: 64 left over after one round, cut into 4 segments
+    assert cls.ssd_fwd_plan(4, 8192, 80, 64, 128, 1, 256) == {"nsegs": 4, "nsplit": 64, "source": "heuristic"}
+    # 64 chains of 512 chunks: every chain cut into 4
+    assert cls.ssd_fwd_plan(1, 65536, 64, 64, 128, 8, 128) == {"nsegs": 4, "nsplit": 64, "source": "heuristic"}
+    # 192 chains of 16 chunks: a split would not pay, whole chains
+    assert cls.ssd_fwd_plan(8, 2048, 24, 64, 128, 1, 256) == {"nsegs": 1, "nsplit": 0, "source": "heuristic"}
+    assert cls.ssd_fwd_plan(1, 256, 2, 16, 16, 1, 32, torch.float32)["source"] == "none"
+    assert cls.ssd_fwd_plan(1, 256, 2, 32, 32, 1, 32)["source"] == "none"  # head dim 32: per-head kernel
+    with pytest.raises(cls.SSDError):
+        cls.ssd_fwd_plan(1, 256, 3, 64, 128, 2, 32)
+    lib = cls.load_library()
+    n1 = ctypes.c_int64()
+    assert lib.ssd_fwd_plan(1, 256, 2, 64, 128, 1, 32, 1, None, ctypes.byref(n1)) == -1

@@ -1,0 +1,110 @@
+"""GPU tests of the per-shape autotuner (ssd_fwd_autotune, ssd_fwd_plan,
+ssd_fwd_autotune_reset) through the C ABI.
+
+The tuner changes only how long chains are cut into segments, so its result,
+and every later ssd_fwd call on the tuned plan, must match the float64 oracle
+within the bf16 tolerance of the forward-pass tests (rel-L2 <= 2e-2 for y and
+the final state; fp32 shapes 1e-5).  The tuned plan is deterministic: a later
+ssd_fwd call returns the tuner's own output bit for bit.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import chunked_linear_scan_amd as cls
+from oracle import compare, ssd as ossd
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+TOL_F32 = 1e-5
+
+
+def case(seed, Bt, L, H, P, S, G, dtype):
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn(Bt, L, H, P, generator=g).to(dtype)
+    B = torch.randn(Bt, L, G, S, generator=g).to(dtype)
+    C = torch.randn(Bt, L, G, S, generator=g).to(dtype)
+    dt = torch.nn.functional.softplus(torch.randn(Bt, L, H, generator=g) - 2.0)
+    A = -torch.exp(torch.rand(H, generator=g) * math.log(16.0))
+    D = torch.randn(H, generator=g)
+    h0 = 0.3 * torch.randn(Bt, H, P, S, generator=g)
+    return dict(x=x, dt=dt, A=A, B=B, C=C, D=D, h0=h0)
+
+
+def oracle(c):
+    np64 = lambda t: t.to(torch.float64).numpy()
+    return ossd.ssd_loop(*(np64(c[k]) for k in ("x", "dt", "A", "B", "C", "D", "h0")))
+
+
+def check(label, got, ref, tol):
+    err = compare.rel_l2(got, ref)
+    print(f"  {label}: rel-L2 {err:.3e}", flush=True)
+    assert err <= tol, (label, err, compare.first_mismatch(got, ref, rtol=50 * tol, atol=50 * tol))
+
+
+@pytest.mark.parametrize("Bt,L,H,G,chunk", [(2, 2048, 24, 2, 128), (1, 1000, 12, 3, 64), (3, 4096, 8, 1, 256)])
+def test_autotune_result_plan_and_later_calls(Bt, L, H, G, chunk):
+    P, S = 64, 128
+    print(f"[autotune] Bt={Bt} L={L} H={H} G={G} chunk={chunk}", flush=True)
+    cls.ssd_fwd_autotune_reset()
+    c = case(31 + L, Bt, L, H, P, S, G, torch.bfloat16)
+    d = {k: v.cuda() for k, v in c.items()}
+    before = cls.ssd_fwd_plan(Bt, L, H, P, S, G, chunk)
+    assert before["source"] == "heuristic"
+    y, hf, info = cls.ssd_fwd_autotune(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=chunk,
+                                       reps=2)
+    torch.cuda.synchronize()
+    print(f"  chosen {info}, heuristic {before}", flush=True)
+    nchains = Bt * H
+    assert 1 <= info["nsegs"] <= 32 and info["ms_per_call"] > 0
+    assert (info["nsegs"] == 1) == (info["nsplit"] == 0) and 0 <= info["nsplit"] <= nchains
+    ry, rh = oracle(c)
+    check("tuned y", y.float().cpu().numpy(), ry, TOL_BF16)
+    check("tuned h_final", hf.cpu().numpy(), rh, TOL_BF16)
+    after = cls.ssd_fwd_plan(Bt, L, H, P, S, G, chunk)
+    assert after == {"nsegs": info["nsegs"], "nsplit": info["nsplit"], "source": "tuned"}
+    y2, hf2 = cls.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=chunk)
+    torch.cuda.synchronize()
+    assert torch.equal(y2.view(torch.int16), y.view(torch.int16))
+    assert torch.equal(hf2.view(torch.int32), hf.view(torch.int32))
+    # another shape keeps its own plan
+    assert cls.ssd_fwd_plan(Bt, L + 128, H, P, S, G, chunk)["source"] == "heuristic"
+    cls.ssd_fwd_autotune_reset()
+    assert cls.ssd_fwd_plan(Bt, L, H, P, S, G, chunk) == before
+
+
+def test_autotune_workspace_sized_before_tuning_suffices():
+    """A workspace from ssd_fwd_workspace_size before tuning serves the tuner
+    and every later call (it covers every candidate plan)."""
+    Bt, L, H, P, S, G, chunk = 1, 2048, 16, 64, 128, 1, 128
+    cls.ssd_fwd_autotune_reset()
+    c = case(5, Bt, L, H, P, S, G, torch.bfloat16)
+    d = {k: v.cuda() for k, v in c.items()}
+    need = cls.load_library().ssd_fwd_workspace_size(Bt, L, H, P, S, G, chunk, cls.SSD_BF16)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    y, hf, info = cls.ssd_fwd_autotune(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=chunk,
+                                       reps=1, workspace=ws)
+    y2, hf2 = cls.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=chunk, workspace=ws)
+    torch.cuda.synchronize()
+    ry, rh = oracle(c)
+    check("y", y2.float().cpu().numpy(), ry, TOL_BF16)
+    check("h_final", hf2.cpu().numpy(), rh, TOL_BF16)
+    cls.ssd_fwd_autotune_reset()
+
+
+def test_autotune_without_a_plan_runs_one_plain_pass():
+    """fp32 shapes (and bf16 shapes outside the fused path) have no segment
+    plan: the tuner runs ssd_fwd once and reports nsegs 0."""
+    for dtype, P, S, tol in [(torch.float32, 16, 32, TOL_F32), (torch.bfloat16, 32, 64, TOL_BF16)]:
+        c = case(9, 1, 300, 4, P, S, 2, dtype)
+        d = {k: v.cuda() for k, v in c.items()}
+        y, hf, info = cls.ssd_fwd_autotune(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=64)
+        torch.cuda.synchronize()
+        assert info["nsegs"] == 0 and info["nsplit"] == 0
+        assert cls.ssd_fwd_plan(1, 300, 4, P, S, 2, 64, dtype)["source"] == "none"
+        ry, rh = oracle(c)
+        check(f"{dtype} y", y.float().cpu().numpy(), ry, tol)
+        check(f"{dtype} h_final", hf.cpu().numpy(), rh, tol)
