@@ -48,6 +48,13 @@ int64_t fused_slots() {
 }
 static int g_force_path = 0;  // 0 auto, 1 the per-(batch, head) chunk kernel, 2 the fused kernel
 
+// Segment plan of the fused path: each split chain is cut into nsegs
+// segments, and the last nsplit (batch, head) chains are split (the others run
+// whole).
+struct SegChoice {
+    int64_t nsegs, nsplit;
+};
+
 // Segment plans chosen by the autotuner, per (device, shape).
 using TuneKey = std::array<int64_t, 9>;
 std::mutex g_tune_mu;
@@ -71,6 +78,9 @@ bool tuned_choice(const TuneKey& k, SegChoice* out) {
 // The autotuner's search space: no split; the chains left over after whole
 // rounds of the CUs cut into 2..32 segments; every chain cut into 2..32
 // segments.  Plans of more than four rounds of workgroups are left out.
+SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
+                            int64_t chunk, int dtype, const SegChoice* force);
+
 std::vector<SegChoice> seg_candidates(int64_t nchains, int64_t nc, int64_t slots) {
     std::vector<SegChoice> v{{1, 0}};
     const int64_t r = nchains % slots;
@@ -82,6 +92,8 @@ std::vector<SegChoice> seg_candidates(int64_t nchains, int64_t nc, int64_t slots
     return v;
 }
 
+// force: null (test override, else a tuned choice for this shape, else the
+// heuristic), or the segment plan to use.
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
                             int64_t chunk, int dtype, const SegChoice* force) {
     SsdFusedPlan pl{};
@@ -165,6 +177,11 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     pl.dtt_off = pl.cf_off + up(size_t(batch) * size_t(nc) * size_t(G) * size_t(S) * TT * 2);
     pl.bytes = pl.dtt_off + size_t(batch) * size_t(nc) * size_t(H) * TT * 4;
     return pl;
+}
+
+SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
+                            int64_t chunk, int dtype) {
+    return ssd_fused_plan(batch, L, H, P, S, G, chunk, dtype, nullptr);
 }
 
 }  // namespace cls

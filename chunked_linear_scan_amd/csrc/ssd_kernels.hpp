@@ -105,17 +105,8 @@ int ssd_fused_state_floats(int S);  // floats of one [64, S] state
 // launch; ev (optional): four events, before and between the launches.
 int ssd_fused_launch(int TT, int S, const SsdBf16Params& cbp, const SsdFusedParams& fp, hipStream_t stream,
                      hipEvent_t* ev);
-// Segment plan of the fused path: each split chain is cut into nsegs
-// segments, and the last nsplit (batch, head) chains are split (the others run
-// whole).
-struct SegChoice {
-    int64_t nsegs, nsplit;
-};
-
-// force: null (test override, else a tuned choice for this shape, else the
-// heuristic), or the segment plan to use.
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
-                            int64_t chunk, int dtype, const SegChoice* force = nullptr);
+                            int64_t chunk, int dtype);
 int ssd_bf16_launch(int TT, int P, int S, const SsdBf16Params& prm, hipStream_t stream);
 
 }  // namespace cls
