@@ -123,7 +123,7 @@ def record_traffic(fetch_csv, write_csv, workload):
             db = json.load(f)
     for key, srcs, pat in [("ssd_fused_kernel:" + workload, SSD_SOURCES, "ssd_fused_kernel<"),
                            ("ssd_fused_agg_kernel:" + workload, SSD_SOURCES, "ssd_fused_agg_kernel<"),
-                           ("linear_scan:scan", SCAN_SOURCES, "linear_scan_kernel"),
+                           ("linear_scan:scan", SCAN_SOURCES, "linear_scan_kernel<false, float, float>"),
                            ("ssd_step:decode_large", STEP_SOURCES, "ssd_step_kernel")]:
         f = [v for (k, g), vs in fe.items() if pat in k for v in vs]
         w = [v for (k, g), vs in wr.items() if pat in k for v in vs]
@@ -302,7 +302,7 @@ def bench_step(name, steps, warmup, want_cpu):
 
 
 # ---------------------------------------------------------------------------
-def bench_ssd(name, steps, warmup, want_cpu):
+def bench_ssd(name, steps, warmup, want_cpu, want_autotune=True):
     import torch
     import chunked_linear_scan_amd as cls
     from chunked_linear_scan_amd import workloads
@@ -375,21 +375,22 @@ def bench_ssd(name, steps, warmup, want_cpu):
     # The autotuner (ssd_fwd_autotune) on the same inputs: the plan it keeps
     # and ssd_fwd's time on that plan, beside the built-in heuristic's, which
     # is what the timed steps above ran.  The table is cleared afterwards.
-    heur = cls.ssd_fwd_plan(shape.batch, shape.seqlen, shape.nheads, shape.headdim, shape.dstate,
-                            shape.ngroups, shape.chunk, inp["x"].dtype)
-    d0 = sets[0]
-    _, _, info = cls.ssd_fwd_autotune(d0["x"], d0["dt"], d0["A"], d0["B"], d0["C"], d0["D"], d0["h0"],
-                                      chunk=shape.chunk, reps=5, out=d0["y"])
-    t_tuned = time_loop(step, nsets, steps, warmup, stream)
-    cls.ssd_fwd_autotune_reset()
-    # the heuristic again, right after, so that both loops run in the same
-    # state of the GPU (a later loop tends to run a little faster)
-    t_heur = time_loop(step, nsets, steps, warmup, stream)
-    res["autotune"] = {"plan": {"nsegs": info["nsegs"], "nsplit": info["nsplit"]},
-                       "heuristic_plan": {"nsegs": heur["nsegs"], "nsplit": heur["nsplit"]},
-                       "us_per_call_tuned": round(t_tuned * 1e6, 2),
-                       "us_per_call_heuristic": round(t_heur * 1e6, 2),
-                       "speedup": round(t_heur / t_tuned, 3)}
+    if want_autotune:
+        heur = cls.ssd_fwd_plan(shape.batch, shape.seqlen, shape.nheads, shape.headdim, shape.dstate,
+                                shape.ngroups, shape.chunk, inp["x"].dtype)
+        d0 = sets[0]
+        _, _, info = cls.ssd_fwd_autotune(d0["x"], d0["dt"], d0["A"], d0["B"], d0["C"], d0["D"], d0["h0"],
+                                          chunk=shape.chunk, reps=10, out=d0["y"])
+        t_tuned = time_loop(step, nsets, steps, warmup, stream)
+        cls.ssd_fwd_autotune_reset()
+        # the heuristic again, right after, so that both loops run in the same
+        # state of the GPU (a later loop tends to run a little faster)
+        t_heur = time_loop(step, nsets, steps, warmup, stream)
+        res["autotune"] = {"plan": {"nsegs": info["nsegs"], "nsplit": info["nsplit"]},
+                           "heuristic_plan": {"nsegs": heur["nsegs"], "nsplit": heur["nsplit"]},
+                           "us_per_call_tuned": round(t_tuned * 1e6, 2),
+                           "us_per_call_heuristic": round(t_heur * 1e6, 2),
+                           "speedup": round(t_heur / t_tuned, 3)}
     if want_cpu:
         res["cpu_baseline"] = cpu_baseline_ssd(inp, shape)
     return res
@@ -430,6 +431,22 @@ def bench_scan(name, steps, warmup, want_cpu):
     tm = time_loop(mul_step, nsets, steps, warmup, stream)
     res["elementwise_ceiling"] = {"kernel": "torch.mul(a, b, out=h)", "us_per_call": round(tm * 1e6, 2),
                                   "GB/s": round(nbytes / tm / 1e9, 1), "scan_over_ceiling": round(tm / t, 3)}
+    # bf16 elements (linear_scan_typed): the same rows, a and b rounded to bf16
+    res["bf16"] = {}
+    for dout, tag in [(torch.float32, "bf16_in_f32_out"), (torch.bfloat16, "bf16_in_bf16_out")]:
+        a16, b16 = inp["a"].to(torch.bfloat16), inp["b"].to(torch.bfloat16)
+        nb16 = (4 + (4 if dout == torch.float32 else 2)) * rows * L
+        ns16 = max(1, math.ceil((1 << 30) / nb16))
+        sets16 = [(a16.to(dev), b16.to(dev), torch.empty(rows, L, dtype=dout, device=dev)) for _ in range(ns16)]
+
+        def step16(i, sets16=sets16):
+            a, b, h = sets16[i]
+            cls.linear_scan(a, b, out=h, workspace=ws)
+
+        t16 = time_loop(step16, ns16, steps, warmup, stream)
+        res["bf16"][tag] = {"us_per_call": round(t16 * 1e6, 2), "bytes_per_elem": nb16 // (rows * L),
+                            "GB/s": round(nb16 / t16 / 1e9, 1), "frac": round(nb16 / t16 / 1e9 / HBM_PEAK_GBS, 4)}
+        del sets16
     if want_cpu:
         res["cpu_baseline"] = cpu_baseline_scan(inp)
     return res
@@ -471,6 +488,9 @@ def main():
     ap.add_argument("--scan-workload", default="scan", choices=["scan", "scan_ragged"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-scan", action="store_true")
+    ap.add_argument("--no-autotune", action="store_true",
+                    help="skip the autotuner comparison (counter runs: its candidate plans would mix into "
+                         "the per-launch figures)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run three plain 1 GiB device copies (the known-size reference that "
                          "scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
@@ -503,7 +523,7 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     want_cpu = not args.no_cpu_baseline
-    ssd = bench_ssd(args.workload, args.steps, args.warmup, want_cpu)
+    ssd = bench_ssd(args.workload, args.steps, args.warmup, want_cpu, not args.no_autotune)
     shape = ssd["shape"]
     line = {
         "metric": METRIC,
@@ -524,7 +544,7 @@ def main():
                    "global_batch": shape.batch, "seq_len": shape.seqlen, "parallelism": "single GPU",
                    "buffer_sets": ssd["nsets"]},
         "roofline": ssd["roofline"],
-        "autotune": ssd["autotune"],
+        "autotune": ssd.get("autotune"),
     }
     if "cpu_baseline" in ssd:
         line["cpu_baseline"] = ssd["cpu_baseline"]

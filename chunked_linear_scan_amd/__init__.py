@@ -53,6 +53,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.linear_scan_workspace_size.restype = sz
         lib.linear_scan.argtypes = [fp, fp, fp, i64, i64, vp, sz, vp]
         lib.linear_scan.restype = ctypes.c_int
+        lib.linear_scan_typed.argtypes = [vp, vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, vp, sz, vp]
+        lib.linear_scan_typed.restype = ctypes.c_int
         lib.ssd_fwd_workspace_size.argtypes = [i64] * 7 + [ctypes.c_int]
         lib.ssd_fwd_workspace_size.restype = sz
         lib.ssd_fwd.argtypes = [vp, fp, fp, vp, vp, fp, fp] + [i64] * 7 + [ctypes.c_int, vp, fp, vp, sz, vp]
@@ -127,22 +129,36 @@ def _check_cuda(name, t, dtype=None, shape=None):
 
 
 def linear_scan(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
-                workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """h[r, t] = a[r, t] h[r, t-1] + b[r, t] with h[r, -1] = 0, fp32 [rows, L]."""
+                workspace: torch.Tensor | None = None, out_dtype: torch.dtype | None = None) -> torch.Tensor:
+    """h[r, t] = a[r, t] h[r, t-1] + b[r, t] with h[r, -1] = 0, [rows, L].
+
+    a and b are both fp32 or both bf16; h is fp32 unless out (or out_dtype) is
+    bf16.  The scan runs in fp32 either way."""
     lib = load_library()
-    _check_cuda("a", a, torch.float32)
+    if a.dtype not in _DTYPE_CODE:
+        raise TypeError("a must be float32 or bfloat16")
+    _check_cuda("a", a, a.dtype)
     if a.dim() != 2:
         raise ValueError("a must be [rows, L]")
-    _check_cuda("b", b, torch.float32, a.shape)
+    _check_cuda("b", b, a.dtype, a.shape)
     rows, length = a.shape
-    h = torch.empty_like(a) if out is None else out
-    _check_cuda("out", h, torch.float32, a.shape)
+    if out is None:
+        h = torch.empty(a.shape, dtype=out_dtype or torch.float32, device=a.device)
+    else:
+        h = out
+    if h.dtype not in _DTYPE_CODE:
+        raise TypeError("out must be float32 or bfloat16")
+    _check_cuda("out", h, h.dtype, a.shape)
     need = lib.linear_scan_workspace_size(rows, length)
     if need == 0:
         raise SSDError(-2, "linear_scan_workspace_size")
     ws = _scan_ws.get(a.device, need) if workspace is None else workspace
-    st = lib.linear_scan(_ptr(a), _ptr(b), _ptr(h), rows, length, _ptr(ws), ws.numel(),
-                         _stream_handle(a.device))
+    if a.dtype == torch.float32 and h.dtype == torch.float32:
+        st = lib.linear_scan(_ptr(a), _ptr(b), _ptr(h), rows, length, _ptr(ws), ws.numel(),
+                             _stream_handle(a.device))
+    else:
+        st = lib.linear_scan_typed(_ptr(a), _ptr(b), _ptr(h), rows, length, _DTYPE_CODE[a.dtype],
+                                   _DTYPE_CODE[h.dtype], _ptr(ws), ws.numel(), _stream_handle(a.device))
     if st != SSD_OK:
         raise SSDError(st, "linear_scan")
     return h

@@ -79,19 +79,32 @@ size_t linear_scan_workspace_size(int64_t rows, int64_t length) {
     return plan_scan(rows, length).bytes;
 }
 
-int linear_scan(const float* a, const float* b, float* h, int64_t rows, int64_t length,
-                void* workspace, size_t workspace_bytes, void* stream) {
+static int linear_scan_launch(const void* a, const void* b, void* h, int64_t rows, int64_t length, int in16,
+                              int out16, void* workspace, size_t workspace_bytes, void* stream) {
     if (!a || !b || !h || !workspace) return SSD_ERR_NULL;
     if (!scan_sizes_ok(rows, length)) return SSD_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(b) || !aligned16(h) || !aligned16(workspace)) return SSD_ERR_ALIGN;
     const ScanPlan p = plan_scan(rows, length);
     if (workspace_bytes < p.bytes) return SSD_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
-    return cls_launch_linear_scan(a, b, h, rows, length, p.segmented ? 1 : 0, int(p.tiles_per_row),
+    return cls_launch_linear_scan(a, b, h, rows, length, in16, out16, p.segmented ? 1 : 0, int(p.tiles_per_row),
                                   int(p.rows_per_tile), p.ntiles,
                                   reinterpret_cast<uint32_t*>(ws + p.claim_off),
                                   reinterpret_cast<uint32_t*>(ws + p.done_off), ws + p.status_off,
                                   reinterpret_cast<uint32_t*>(ws), static_cast<hipStream_t>(stream));
+}
+
+int linear_scan(const float* a, const float* b, float* h, int64_t rows, int64_t length,
+                void* workspace, size_t workspace_bytes, void* stream) {
+    return linear_scan_launch(a, b, h, rows, length, 0, 0, workspace, workspace_bytes, stream);
+}
+
+int linear_scan_typed(const void* a, const void* b, void* h, int64_t rows, int64_t length, int in_dtype,
+                      int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if ((in_dtype != SSD_F32 && in_dtype != SSD_BF16) || (out_dtype != SSD_F32 && out_dtype != SSD_BF16))
+        return SSD_ERR_DTYPE;
+    return linear_scan_launch(a, b, h, rows, length, in_dtype == SSD_BF16 ? 1 : 0, out_dtype == SSD_BF16 ? 1 : 0,
+                              workspace, workspace_bytes, stream);
 }
 
 size_t ssd_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,

@@ -25,7 +25,8 @@ struct SsdArgs {
 };
 
 extern "C" {
-int cls_launch_linear_scan(const float* a, const float* b, float* h, int64_t rows, int64_t L,
+// a, b: fp32 (in16 = 0) or bf16 (1); h: fp32 (out16 = 0) or bf16 (1).
+int cls_launch_linear_scan(const void* a, const void* b, void* h, int64_t rows, int64_t L, int in16, int out16,
                            int segmented, int tiles_per_row, int rows_per_tile, int64_t ntiles,
                            uint32_t* claim, uint32_t* done, void* status, uint32_t* err,
                            hipStream_t stream);

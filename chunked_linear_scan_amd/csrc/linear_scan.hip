@@ -8,11 +8,12 @@
 //
 // MI355X choices:
 //   * a tile is 4 waves x 2048 elements; each wave owns a contiguous run and
-//     loads it as 16-byte vectors with lanes 16 bytes apart, so every
-//     wave-wide load covers 1 KB of consecutive memory; a 16-byte aligned
+//     loads it as 16-byte vectors (4 fp32 or 8 bf16 items per lane) with
+//     lanes 16 bytes apart, so every wave-wide load covers 1 KB of
+//     consecutive memory; a 16-byte aligned
 //     window makes rows that start misaligned (ragged lengths) use the same
 //     vector loads; positions outside the row are the identity (a = 1, b = 0);
-//   * the in-tile scan is a 4-item serial scan per lane, a 64-lane DPP wave scan
+//   * the in-tile scan is a serial scan over each lane's items of a step, a 64-lane DPP wave scan
 //     per 256-element step with the step carry kept wave-uniform, and a
 //     4-wave combine through LDS;
 //   * one 64-lane wave inspects 64 predecessors per look-back step and folds
@@ -30,15 +31,17 @@
 //     never an out-of-range address;
 //   * the output is written with non-temporal stores (it is never re-read);
 //   * rows no longer than a tile are packed whole into tiles and scanned with a
-//     row-start reset flag, with no look-back at all.
+//     row-start reset flag, with no look-back at all;
+//   * a, b and h may each be fp32 or bf16: bf16 items are widened to fp32 at
+//     the load and rounded to nearest even once at the store; the scan
+//     itself is fp32 either way.
 #include "common.hpp"
 
 namespace cls {
 
 constexpr int kLsThreads = 256;
 constexpr int kLsWaves = kLsThreads / 64;
-constexpr int kLsSteps = 8;                      // 256-element steps per wave
-constexpr int kLsWaveRun = kLsSteps * 256;       // 2048 elements per wave
+constexpr int kLsWaveRun = 2048;                 // elements per wave
 constexpr int kLsTile = kLsWaves * kLsWaveRun;   // 8192 elements per tile
 // Each look-back poll sleeps ~64 clocks; 2^24 polls is several seconds, far
 // beyond any legitimate wait, so a corrupted workspace ends the kernel instead
@@ -60,27 +63,117 @@ __device__ __forceinline__ Pair combine(Pair f, Pair s) {
     return Pair{f.a * s.a, fmaf(s.a, f.b, s.b), f.f};
 }
 
-__device__ __forceinline__ f32x4 load4(const float* __restrict__ p, int64_t i, int64_t lo, int64_t hi,
-                                       float ident) {
-    if (i >= lo && i + 4 <= hi) return __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + i));
-    f32x4 v;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-        const int64_t e = i + k;
-        v[k] = (e >= lo && e < hi) ? p[e] : ident;
-    }
-    return v;
-}
+// Items per lane and step: 4 fp32 (one 16-byte load) or 8 bf16 (one 16-byte
+// load), so every wave-wide load covers 1 KB of consecutive memory.
+template <typename T>
+struct ItemsPerLane {
+    static constexpr int value = 4;
+};
+template <>
+struct ItemsPerLane<uint16_t> {
+    static constexpr int value = 8;
+};
 
-__device__ __forceinline__ void store4(float* __restrict__ p, int64_t i, int64_t lo, int64_t hi, f32x4 v) {
+// 16-byte vectors at 8-byte aligned addresses (bf16 rows start on a 4-item
+// boundary).
+typedef uint32_t u32x4a8 __attribute__((ext_vector_type(4), aligned(8)));
+typedef uint32_t u32x2a8 __attribute__((ext_vector_type(2), aligned(8)));
+
+// Items i .. i+N-1 of p; positions outside [lo, hi) read as `ident`.
+__device__ __forceinline__ void load_items(const float* __restrict__ p, int64_t i, int64_t lo, int64_t hi,
+                                           float ident, float (&v)[4]) {
     if (i >= lo && i + 4 <= hi) {
-        __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(p + i));
+        const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + i));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[k] = w[k];
         return;
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
         const int64_t e = i + k;
+        v[k] = (e >= lo && e < hi) ? p[e] : ident;
+    }
+}
+
+__device__ __forceinline__ void load_items(const uint16_t* __restrict__ p, int64_t i, int64_t lo, int64_t hi,
+                                           float ident, float (&v)[8]) {
+    if (i >= lo && i + 8 <= hi) {
+        const u32x4a8 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4a8*>(p + i));
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = bf16_lo(w[k]);
+            v[2 * k + 1] = bf16_hi(w[k]);
+        }
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int64_t e = i + k;
+        v[k] = (e >= lo && e < hi) ? __builtin_bit_cast(float, uint32_t(p[e]) << 16) : ident;
+    }
+}
+
+// Items i .. i+7 of p as raw bf16 bits, two per word (item 2k in the low
+// half of word k); positions outside [lo, hi) hold `ident` (bf16 bits).
+__device__ __forceinline__ u32x4a8 load_raw8(const uint16_t* __restrict__ p, int64_t i, int64_t lo, int64_t hi,
+                                            uint32_t ident) {
+    if (i >= lo && i + 8 <= hi) return __builtin_nontemporal_load(reinterpret_cast<const u32x4a8*>(p + i));
+    u32x4a8 w{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int64_t e = i + k;
+        const uint32_t v = (e >= lo && e < hi) ? uint32_t(p[e]) : ident;
+        w[k / 2] |= v << (16 * (k & 1));
+    }
+    return w;
+}
+
+__device__ __forceinline__ float raw_item(const u32x4a8& w, int k) {
+    return (k & 1) ? bf16_hi(w[k / 2]) : bf16_lo(w[k / 2]);
+}
+
+// Unchecked forms for tiles that lie wholly inside [lo, hi).
+__device__ __forceinline__ void load_items_full(const float* __restrict__ p, int64_t i, float (&v)[4]) {
+    const f32x4 w = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + i));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = w[k];
+}
+
+// Stores items i .. i+N-1 that lie in [lo, hi).
+template <int N>
+__device__ __forceinline__ void store_items(float* __restrict__ p, int64_t i, int64_t lo, int64_t hi,
+                                            const float (&v)[N], bool full = false) {
+    if (full || (i >= lo && i + N <= hi)) {
+#pragma unroll
+        for (int c = 0; c < N; c += 4)
+            __builtin_nontemporal_store(f32x4{v[c], v[c + 1], v[c + 2], v[c + 3]},
+                                        reinterpret_cast<f32x4*>(p + i + c));
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const int64_t e = i + k;
         if (e >= lo && e < hi) p[e] = v[k];
+    }
+}
+
+template <int N>
+__device__ __forceinline__ void store_items(uint16_t* __restrict__ p, int64_t i, int64_t lo, int64_t hi,
+                                            const float (&v)[N], bool full = false) {
+    uint32_t w[N / 2];
+#pragma unroll
+    for (int k = 0; k < N / 2; ++k) w[k] = pack_bf16x2(v[2 * k], v[2 * k + 1]);
+    if (full || (i >= lo && i + N <= hi)) {
+        if constexpr (N == 8)
+            __builtin_nontemporal_store(u32x4a8{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4a8*>(p + i));
+        else
+            __builtin_nontemporal_store(u32x2a8{w[0], w[1]}, reinterpret_cast<u32x2a8*>(p + i));
+        return;
+    }
+#pragma unroll
+    for (int k = 0; k < N; ++k) {
+        const int64_t e = i + k;
+        if (e >= lo && e < hi) p[e] = uint16_t((w[k / 2] >> (16 * (k & 1))) & 0xffffu);
     }
 }
 
@@ -178,10 +271,11 @@ __device__ Pair lookback(const u32x4* status_row, int j, uint32_t* err) {
 
 // One tile per workgroup.  SEGMENTED: tiles hold whole rows and reset at each
 // row start (rows no longer than a tile); otherwise each tile belongs to one
-// row and the row's tiles chain through the look-back.
-template <bool SEGMENTED>
+// row and the row's tiles chain through the look-back.  TIn / TOut: float
+// (fp32) or uint16_t (bf16 bits).
+template <bool SEGMENTED, typename TIn, typename TOut>
 __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
-    const float* __restrict__ a, const float* __restrict__ b, float* __restrict__ h,
+    const TIn* __restrict__ a, const TIn* __restrict__ b, TOut* __restrict__ h,
     int64_t rows, int64_t L, int tiles_per_row, int rows_per_tile,
     uint32_t* __restrict__ claim, uint32_t* __restrict__ done, u32x4* __restrict__ status,
     uint32_t* __restrict__ err) {
@@ -213,54 +307,123 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
     const int j = in_range ? int(cnt) : 0;
     const int64_t abase = (lo & ~int64_t(3)) + int64_t(j) * kLsTile;
     const bool empty_tile = !SEGMENTED && (!in_range || abase >= hi);
-    const int64_t wbase = abase + int64_t(wave) * kLsWaveRun + 4 * lane;  // + 256 q
+    constexpr int IPL = ItemsPerLane<TIn>::value;  // items per lane and step
+    // An fp32 tile wholly inside its row (every tile but a row's first and
+    // last, unless the row is tile-aligned) loads and stores without bounds
+    // checks: 1-2 % faster for fp32, slower for bf16 items (measured), which
+    // keep the checked form.
+    const bool full = IPL == 4 && !empty_tile && abase >= lo && abase + kLsTile <= hi;
+    constexpr int NS = kLsWaveRun / (64 * IPL);      // steps per wave
+    constexpr int STEP = 64 * IPL;                   // elements per wave step
+    const int64_t wbase = abase + int64_t(wave) * kLsWaveRun + IPL * lane;  // + STEP q
 
-    // LS1: load 4 steps of 4 items; scan the 4 items of each step serially.
-    f32x4 av[kLsSteps], bv[kLsSteps];
-    uint32_t rmask = 0;  // bit 4q+k: the run up to item k of step q holds a row start
-    if (!empty_tile) {
+    // LS1: load every step's items; scan the items of each step serially.
+    // fp32 items keep their running prefix (a-product, state) per item.  bf16
+    // items stay packed as loaded (half the registers, so more workgroups fit
+    // a CU): only each step's lane aggregate is kept, and the output reruns
+    // the recurrence over the items from the state in front of them.
+    constexpr bool PACKED = IPL == 8;
+    float av[PACKED ? 1 : NS][IPL], bv[PACKED ? 1 : NS][IPL];
+    u32x4a8 ra[PACKED ? NS : 1], rb[PACKED ? NS : 1];
+    float la[NS], lb[NS];  // lane aggregate of each step's items
+    uint32_t rmask = 0;  // bit IPL q + k: the run up to item k of step q holds a row start
+    uint32_t smask = 0;  // bit IPL q + k: item k of step q starts a row (packed items)
+    if constexpr (PACKED) {
 #pragma unroll
-        for (int q = 0; q < kLsSteps; ++q) {
-            av[q] = load4(a, wbase + 256 * q, lo, hi, 1.0f);
-            bv[q] = load4(b, wbase + 256 * q, lo, hi, 0.0f);
+        for (int q = 0; q < NS; ++q) {
+            ra[q] = empty_tile ? u32x4a8{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}
+                               : load_raw8(a, wbase + STEP * q, lo, hi, 0x3f80u);
+            rb[q] = empty_tile ? u32x4a8{0u, 0u, 0u, 0u} : load_raw8(b, wbase + STEP * q, lo, hi, 0u);
         }
 #pragma unroll
-        for (int q = 0; q < kLsSteps; ++q) {
-            const int64_t t0 = wbase + 256 * q;
+        for (int q = 0; q < NS; ++q) {
+            const int64_t t0 = wbase + STEP * q;
             int64_t ns = 0;
             if (SEGMENTED) ns = ((t0 + L - 1) / L) * L;  // first row start >= t0
+            float A = 1.0f, Bs = 0.0f;
             int f = 0;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
+            for (int k = 0; k < IPL; ++k) {
+                const float x = raw_item(ra[q], k), y = raw_item(rb[q], k);
                 bool reset = false;
                 if (SEGMENTED && t0 + k == ns && ns < hi) {
                     reset = true;
                     ns += L;
                 }
-                if (k > 0 && !reset) {
-                    bv[q][k] = fmaf(av[q][k], bv[q][k - 1], bv[q][k]);
-                    av[q][k] = av[q][k - 1] * av[q][k];
+                if (reset) {
+                    A = x;
+                    Bs = y;
+                    f = 1;
+                    smask |= 1u << (IPL * q + k);
+                } else {
+                    Bs = fmaf(x, Bs, y);
+                    A = A * x;
                 }
-                f |= reset ? 1 : 0;
-                rmask |= uint32_t(f) << (4 * q + k);
             }
+            la[q] = A;
+            lb[q] = Bs;
+            rmask |= uint32_t(f) << (IPL * q + IPL - 1);
         }
     } else {
+        if (!empty_tile) {
+            if (full) {
 #pragma unroll
-        for (int q = 0; q < kLsSteps; ++q) {
-            av[q] = f32x4{1.0f, 1.0f, 1.0f, 1.0f};
-            bv[q] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+                for (int q = 0; q < NS; ++q) {
+                    load_items_full(a, wbase + STEP * q, av[q]);
+                    load_items_full(b, wbase + STEP * q, bv[q]);
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < NS; ++q) {
+                    load_items(a, wbase + STEP * q, lo, hi, 1.0f, av[q]);
+                    load_items(b, wbase + STEP * q, lo, hi, 0.0f, bv[q]);
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < NS; ++q) {
+                const int64_t t0 = wbase + STEP * q;
+                int64_t ns = 0;
+                if (SEGMENTED) ns = ((t0 + L - 1) / L) * L;  // first row start >= t0
+                int f = 0;
+#pragma unroll
+                for (int k = 0; k < IPL; ++k) {
+                    bool reset = false;
+                    if (SEGMENTED && t0 + k == ns && ns < hi) {
+                        reset = true;
+                        ns += L;
+                    }
+                    if (k > 0 && !reset) {
+                        bv[q][k] = fmaf(av[q][k], bv[q][k - 1], bv[q][k]);
+                        av[q][k] = av[q][k - 1] * av[q][k];
+                    }
+                    f |= reset ? 1 : 0;
+                    rmask |= uint32_t(f) << (IPL * q + k);
+                }
+            }
+        } else {
+#pragma unroll
+            for (int q = 0; q < NS; ++q)
+#pragma unroll
+                for (int k = 0; k < IPL; ++k) {
+                    av[q][k] = 1.0f;
+                    bv[q][k] = 0.0f;
+                }
+        }
+#pragma unroll
+        for (int q = 0; q < NS; ++q) {
+            la[q] = av[q][IPL - 1];
+            lb[q] = bv[q][IPL - 1];
         }
     }
 
     // LS2: per step, a 64-lane scan of the lane aggregates; the steps chain
     // through a wave-uniform carry.  pre[q] is the wave-local prefix in front
     // of this lane's items of step q.
-    Pair pre[kLsSteps];
+    Pair pre[NS];
     Pair carry{1.0f, 0.0f, 0};
 #pragma unroll
-    for (int q = 0; q < kLsSteps; ++q) {
-        Pair w{av[q][3], bv[q][3], int((rmask >> (4 * q + 3)) & 1u)};
+    for (int q = 0; q < NS; ++q) {
+        Pair w{la[q], lb[q], int((rmask >> (IPL * q + IPL - 1)) & 1u)};
         w = wave_inclusive_scan<SEGMENTED>(w);
         Pair ex{shfl_up(w.a, 1), shfl_up(w.b, 1), SEGMENTED ? shfl_up_i(w.f, 1) : 0};
         if (lane == 0) ex = Pair{1.0f, 0.0f, 0};
@@ -312,15 +475,31 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
         Pair tp = wave_excl;
         if (!SEGMENTED) tp = combine(Pair{s_pa, s_pb, 0}, tp);
 #pragma unroll
-        for (int q = 0; q < kLsSteps; ++q) {
+        for (int q = 0; q < NS; ++q) {
             const float hin = combine(tp, pre[q]).b;
-            f32x4 out;
+            float out[IPL];
+            if constexpr (PACKED) {
+                // An empty asm that claims to change the packed words keeps the
+                // compiler from holding the items unpacked since the scan above
+                // (which would cost the registers packing saves).
+                u32x4a8 wa = ra[q], wb = rb[q];
+                asm volatile("" : "+v"(wa), "+v"(wb));
+                float st = hin;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const bool own = SEGMENTED && ((rmask >> (4 * q + k)) & 1u);
-                out[k] = own ? bv[q][k] : fmaf(av[q][k], hin, bv[q][k]);
+                for (int k = 0; k < IPL; ++k) {
+                    const float x = raw_item(wa, k), y = raw_item(wb, k);
+                    const bool start = SEGMENTED && ((smask >> (IPL * q + k)) & 1u);
+                    st = start ? y : fmaf(x, st, y);
+                    out[k] = st;
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < IPL; ++k) {
+                    const bool own = SEGMENTED && ((rmask >> (IPL * q + k)) & 1u);
+                    out[k] = own ? bv[q][k] : fmaf(av[q][k], hin, bv[q][k]);
+                }
             }
-            store4(h, wbase + 256 * q, lo, hi, out);
+            store_items(h, wbase + STEP * q, lo, hi, out, full);
         }
     }
 
@@ -342,20 +521,48 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
 
 }  // namespace cls
 
-extern "C" int cls_launch_linear_scan(const float* a, const float* b, float* h, int64_t rows,
-                                      int64_t L, int segmented, int tiles_per_row,
-                                      int rows_per_tile, int64_t ntiles, uint32_t* claim,
-                                      uint32_t* done, void* status, uint32_t* err,
-                                      hipStream_t stream) {
+namespace {
+
+template <typename TIn, typename TOut>
+void launch_typed(const void* a, const void* b, void* h, int64_t rows, int64_t L, int segmented, int tiles_per_row,
+                  int rows_per_tile, int64_t ntiles, uint32_t* claim, uint32_t* done, void* status, uint32_t* err,
+                  hipStream_t stream) {
     using namespace cls;
     const dim3 grid{uint32_t(ntiles), 1u, 1u};
     const dim3 block{uint32_t(kLsThreads), 1u, 1u};
+    const TIn* ta = static_cast<const TIn*>(a);
+    const TIn* tb = static_cast<const TIn*>(b);
+    TOut* th = static_cast<TOut*>(h);
+    u32x4* st = reinterpret_cast<u32x4*>(status);
     if (segmented) {
-        hipLaunchKernelGGL(linear_scan_kernel<true>, grid, block, 0, stream, a, b, h, rows, L,
-                           tiles_per_row, rows_per_tile, claim, done, reinterpret_cast<u32x4*>(status), err);
+        hipLaunchKernelGGL((linear_scan_kernel<true, TIn, TOut>), grid, block, 0, stream, ta, tb, th, rows, L,
+                           tiles_per_row, rows_per_tile, claim, done, st, err);
     } else {
-        hipLaunchKernelGGL(linear_scan_kernel<false>, grid, block, 0, stream, a, b, h, rows, L,
-                           tiles_per_row, rows_per_tile, claim, done, reinterpret_cast<u32x4*>(status), err);
+        hipLaunchKernelGGL((linear_scan_kernel<false, TIn, TOut>), grid, block, 0, stream, ta, tb, th, rows, L,
+                           tiles_per_row, rows_per_tile, claim, done, st, err);
+    }
+}
+
+}  // namespace
+
+extern "C" int cls_launch_linear_scan(const void* a, const void* b, void* h, int64_t rows, int64_t L,
+                                      int in16, int out16, int segmented, int tiles_per_row, int rows_per_tile,
+                                      int64_t ntiles, uint32_t* claim, uint32_t* done, void* status,
+                                      uint32_t* err, hipStream_t stream) {
+    if (in16) {
+        if (out16)
+            launch_typed<uint16_t, uint16_t>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles,
+                                             claim, done, status, err, stream);
+        else
+            launch_typed<uint16_t, float>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles,
+                                          claim, done, status, err, stream);
+    } else {
+        if (out16)
+            launch_typed<float, uint16_t>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles,
+                                          claim, done, status, err, stream);
+        else
+            launch_typed<float, float>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles,
+                                       claim, done, status, err, stream);
     }
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }

@@ -406,10 +406,10 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
 }
 
 // Autotuner of the fused path's segment plan (the one run-time choice of its
-// launches): each candidate runs once untimed and `reps` times between two
-// events on the caller's stream; the fastest mean wins and is kept for the
-// shape on the current device.  Candidates that reduce to the same plan are
-// timed once.  The call ends with one more pass on the chosen plan, so y and
+// launches): after one untimed pass over every candidate, each runs `reps`
+// times between two events on the caller's stream, in two rounds; the lowest
+// mean of its better round wins and is kept for the shape on the current
+// device.  Candidates that reduce to the same plan are timed once.  The call ends with one more pass on the chosen plan, so y and
 // h_final hold exactly what a later ssd_fwd call returns.
 extern "C" int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t stream, int reps, int64_t* nsegs,
                                 int64_t* nsplit, float* ms) {
@@ -424,39 +424,49 @@ extern "C" int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t
         (void)hipEventDestroy(e0);
         return SSD_ERR_HIP;
     }
-    int st = SSD_OK;
-    float best_ms = 0.0f;
-    cls::SegChoice best{0, 0};
-    std::vector<std::pair<int64_t, int64_t>> seen;
+    // distinct plans only
+    std::vector<cls::SegChoice> plans;
     for (const cls::SegChoice& c : cands) {
         const cls::SsdFusedPlan q = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
                                                         s.ngroups, s.chunk, s.dtype, &c);
-        const std::pair<int64_t, int64_t> eff{q.nsegs, q.nsegs > 1 ? int64_t(q.nchains - q.nwhole) : 0};
+        const cls::SegChoice ce{q.nsegs, q.nsegs > 1 ? int64_t(q.nchains - q.nwhole) : 0};
         bool dup = false;
-        for (const auto& e : seen) dup = dup || e == eff;
-        if (dup) continue;
-        seen.push_back(eff);
-        const cls::SegChoice ce{eff.first, eff.second};
-        st = ssd_launch_plan(s, a, &ce, stream);
-        if (st != SSD_OK) break;
-        if (hipEventRecord(e0, stream) != hipSuccess) {
-            st = SSD_ERR_HIP;
-            break;
-        }
-        for (int r = 0; r < reps && st == SSD_OK; ++r) st = ssd_launch_plan(s, a, &ce, stream);
-        if (st != SSD_OK) break;
-        float t = 0.0f;
-        if (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
-            hipEventElapsedTime(&t, e0, e1) != hipSuccess) {
-            st = SSD_ERR_HIP;
-            break;
-        }
-        t /= float(reps);
-        if (best.nsegs == 0 || t < best_ms) {
-            best_ms = t;
-            best = ce;
+        for (const auto& e : plans) dup = dup || (e.nsegs == ce.nsegs && e.nsplit == ce.nsplit);
+        if (!dup) plans.push_back(ce);
+    }
+    // One untimed pass over every plan first (clocks and caches settle), then
+    // two timed rounds over all plans; each plan keeps its better round, so a
+    // plan is not favoured by where it falls in the sequence.
+    int st = SSD_OK;
+    std::vector<float> t_best(plans.size(), -1.0f);
+    for (size_t i = 0; i < plans.size() && st == SSD_OK; ++i) st = ssd_launch_plan(s, a, &plans[i], stream);
+    for (int round = 0; round < 2 && st == SSD_OK; ++round) {
+        for (size_t i = 0; i < plans.size() && st == SSD_OK; ++i) {
+            st = ssd_launch_plan(s, a, &plans[i], stream);
+            if (st != SSD_OK) break;
+            if (hipEventRecord(e0, stream) != hipSuccess) {
+                st = SSD_ERR_HIP;
+                break;
+            }
+            for (int r = 0; r < reps && st == SSD_OK; ++r) st = ssd_launch_plan(s, a, &plans[i], stream);
+            if (st != SSD_OK) break;
+            float t = 0.0f;
+            if (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                hipEventElapsedTime(&t, e0, e1) != hipSuccess) {
+                st = SSD_ERR_HIP;
+                break;
+            }
+            t /= float(reps);
+            if (t_best[i] < 0.0f || t < t_best[i]) t_best[i] = t;
         }
     }
+    float best_ms = 0.0f;
+    cls::SegChoice best{0, 0};
+    for (size_t i = 0; i < plans.size(); ++i)
+        if (t_best[i] >= 0.0f && (best.nsegs == 0 || t_best[i] < best_ms)) {
+            best_ms = t_best[i];
+            best = plans[i];
+        }
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
     if (st != SSD_OK) return st;

@@ -5,7 +5,8 @@
  * Every entry point takes plain pointers and sizes.  Device pointers are HIP
  * device memory on the current device; `stream` is a hipStream_t passed as
  * void* (NULL = the default stream).  All work is enqueued on that stream and
- * nothing synchronises the host.  The library never allocates or frees device
+ * nothing synchronises the host, except ssd_fwd_autotune, which waits for its
+ * own timed runs.  The library never allocates or frees device
  * memory: the caller owns every buffer, including the workspace.
  *
  * Errors: arguments are validated on the host before anything is launched.
@@ -103,8 +104,9 @@ int ssd_fwd(const void* x, const float* dt, const float* A, const void* B,
  *
  * ssd_fwd_autotune takes exactly ssd_fwd's arguments (same layouts, same
  * checks, same workspace) plus reps (1..1000).  It runs every candidate plan
- * on these inputs once untimed and then reps times between two events on
- * `stream`, and keeps the fastest for this shape on the current device.
+ * on these inputs once untimed, then in two rounds reps times each between two
+ * events on `stream`; each plan keeps its better round, and the fastest plan
+ * is kept for this shape on the current device.
  * Later ssd_fwd calls with the same shape, dtype and chunk on that device use
  * it.  It returns the chosen plan (*nsegs segments, the last *nsplit chains
  * cut) and its mean time per call in ms.  y and h_final hold the result of
@@ -152,6 +154,21 @@ size_t linear_scan_workspace_size(int64_t rows, int64_t length);
 int linear_scan(const float* a, const float* b, float* h, int64_t rows,
                 int64_t length, void* workspace, size_t workspace_bytes,
                 void* stream);
+
+/*
+ * linear_scan with bf16 or fp32 elements.  The page's scan is fp32 only
+ * ("Selective-scan CUDA kernels", section "Limitations"); this entry point
+ * takes a and b as in_dtype and writes h as out_dtype, each SSD_F32 or
+ * SSD_BF16 (SSD_ERR_DTYPE otherwise).  bf16 elements are raw bf16 bits
+ * (uint16_t).  The recurrence is evaluated in fp32 either way, exactly as
+ * linear_scan does: bf16 inputs are widened exactly, and a bf16 h is the fp32
+ * result rounded to nearest even once.  Same layouts, workspace (size from
+ * linear_scan_workspace_size), alignment, aliasing rule and status codes as
+ * linear_scan; with both dtypes SSD_F32 it is linear_scan.
+ */
+int linear_scan_typed(const void* a, const void* b, void* h, int64_t rows,
+                      int64_t length, int in_dtype, int out_dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The same scalar recurrence as three launches: block scan, spine scan over

@@ -27,7 +27,7 @@ def header_functions():
 def test_header_lists_expected_entry_points():
     assert set(header_functions()) == {
         "ssd_fwd_workspace_size", "ssd_fwd", "ssd_fwd_autotune", "ssd_fwd_plan", "ssd_fwd_autotune_reset",
-        "linear_scan_workspace_size", "linear_scan", "ssd_step", "linear_scan_three_pass_workspace_size", "linear_scan_three_pass", "ssd_strerror"}
+        "linear_scan_workspace_size", "linear_scan", "linear_scan_typed", "ssd_step", "linear_scan_three_pass_workspace_size", "linear_scan_three_pass", "ssd_strerror"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -174,3 +174,20 @@ def test_ssd_plan_query_on_host():
     lib = cls.load_library()
     n1 = ctypes.c_int64()
     assert lib.ssd_fwd_plan(1, 256, 2, 64, 128, 1, 32, 1, None, ctypes.byref(n1)) == -1
+
+
+def test_linear_scan_typed_rejects_bad_arguments():
+    lib = cls.load_library()
+
+    def call(a=FAKE, h=FAKE, rows=2, L=100, din=cls.SSD_BF16, dout=cls.SSD_F32, ws=FAKE, ws_bytes=1 << 20):
+        return lib.linear_scan_typed(a, FAKE, h, rows, L, din, dout, ws, ws_bytes, None)
+
+    assert call(din=2) == -3
+    assert call(dout=-1) == -3
+    assert call(a=None) == -1
+    assert call(h=None) == -1
+    assert call(ws=None) == -1
+    assert call(rows=0) == -2
+    assert call(L=-1) == -2
+    assert call(h=ctypes.c_void_p(0x10008)) == -5
+    assert call(ws_bytes=0) == -6

@@ -129,3 +129,44 @@ def test_workspace_reused_across_shapes():
         assert compare.rel_l2(got, ref) <= TOL, (r, L)
     torch.cuda.synchronize()
     assert int(ws[:4].view(torch.int32).item()) == 0
+
+
+TYPED = [(torch.bfloat16, torch.float32), (torch.bfloat16, torch.bfloat16), (torch.float32, torch.bfloat16)]
+
+
+@pytest.mark.parametrize("din,dout", TYPED)
+@pytest.mark.parametrize("rows,L", [(3, 1), (5, 7), (3, 33), (2, 4097), (3, 8186), (2, 8187), (3, 8193),
+                                    (2, 16385), (1000, 7), (257, 129), (4, 65536), (1, 65533)])
+def test_typed_scan_matches_oracle(din, dout, rows, L):
+    """bf16 / fp32 elements through linear_scan_typed.  The oracle runs on the
+    exact float64 values of the (possibly bf16) inputs.  With an fp32 h the
+    scan is the fp32 scan (rel-L2 <= 1e-5); a bf16 h is that fp32 result
+    rounded to nearest even once, so it equals the fp32-output run rounded on
+    the host bit for bit, and stays within bf16 rounding of the oracle."""
+    print(f"[scan typed] {din} -> {dout} rows={rows} L={L}", flush=True)
+    w = workloads.make_scan_inputs(rows, L, seed=rows * 31 + L)
+    a, b = w["a"].to(din), w["b"].to(din)
+    h = cls.linear_scan(a.cuda(), b.cuda(), out_dtype=dout)
+    torch.cuda.synchronize()
+    assert h.dtype == dout
+    ref = oscan.scan_loop(a.double().numpy(), b.double().numpy())
+    got = h.float().cpu().numpy()
+    err = compare.rel_l2(got, ref)
+    print(f"  rel-L2 {err:.3e}", flush=True)
+    assert err <= (TOL if dout == torch.float32 else 1e-2), (err, compare.first_mismatch(got, ref, 1e-2, 1e-3))
+    if dout == torch.bfloat16:
+        h32 = cls.linear_scan(a.cuda(), b.cuda(), out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(h.cpu().view(torch.int16), h32.cpu().to(torch.bfloat16).view(torch.int16))
+
+
+def test_typed_scan_full_workload_bf16_inputs():
+    w = workloads.scan_workload("scan")
+    a, b = w["a"].to(torch.bfloat16), w["b"].to(torch.bfloat16)
+    print(f"[scan typed] full workload bf16 -> fp32 {tuple(a.shape)}", flush=True)
+    h = cls.linear_scan(a.cuda(), b.cuda())
+    torch.cuda.synchronize()
+    ref = oscan.scan_loop(a.double().numpy(), b.double().numpy())
+    err = compare.rel_l2(h.cpu().numpy(), ref)
+    print(f"  rel-L2 {err:.3e}", flush=True)
+    assert err <= TOL
