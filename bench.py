@@ -63,13 +63,26 @@ def ssd_alg_flops(shape):
     return cb + shape.batch * nc * shape.nheads * per_head
 
 
-def source_digest(names):
+def code_text(src):
+    """Source text without comments and with whitespace runs collapsed: what
+    the compiler sees, so an edit to a comment keeps a kernel's digest."""
+    import re
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
+def source_digest(names, read=None):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "chunked_linear_scan_amd", "csrc")
     for n in sorted(names):
-        with open(os.path.join(csrc, n), "rb") as f:
-            h.update(n.encode())
-            h.update(f.read())
+        if read is None:
+            with open(os.path.join(csrc, n), encoding="utf-8") as f:
+                text = f.read()
+        else:
+            text = read(n)
+        h.update(n.encode())
+        h.update(code_text(text).encode())
     return h.hexdigest()[:16]
 
 

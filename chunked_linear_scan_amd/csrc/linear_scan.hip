@@ -13,9 +13,9 @@
 //     consecutive memory; a 16-byte aligned
 //     window makes rows that start misaligned (ragged lengths) use the same
 //     vector loads; positions outside the row are the identity (a = 1, b = 0);
-//   * the in-tile scan is a serial scan over each lane's items of a step, a 64-lane DPP wave scan
-//     per 256-element step with the step carry kept wave-uniform, and a
-//     4-wave combine through LDS;
+//   * the in-tile scan is a serial scan over each lane's items of a step, a
+//     64-lane DPP wave scan per step (256 fp32 or 512 bf16 items) with the
+//     step carry kept wave-uniform, and a 4-wave combine through LDS;
 //   * one 64-lane wave inspects 64 predecessors per look-back step and folds
 //     every aggregate between the tile and the nearest inclusive prefix with a
 //     6-step order-preserving tree reduction;
