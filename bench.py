@@ -399,8 +399,10 @@ def bench_ssd(name, steps, warmup, want_cpu, want_autotune=True):
         # the heuristic again, right after, so that both loops run in the same
         # state of the GPU (a later loop tends to run a little faster)
         t_heur = time_loop(step, nsets, steps, warmup, stream)
-        res["autotune"] = {"plan": {"nsegs": info["nsegs"], "nsplit": info["nsplit"]},
-                           "heuristic_plan": {"nsegs": heur["nsegs"], "nsplit": heur["nsplit"]},
+        res["autotune"] = {"plan": {"nsegs": info["nsegs"], "nsplit": info["nsplit"],
+                                    "agg_pieces": info["agg_pieces"]},
+                           "heuristic_plan": {"nsegs": heur["nsegs"], "nsplit": heur["nsplit"],
+                                              "agg_pieces": heur["agg_pieces"]},
                            "us_per_call_tuned": round(t_tuned * 1e6, 2),
                            "us_per_call_heuristic": round(t_heur * 1e6, 2),
                            "speedup": round(t_heur / t_tuned, 3)}

@@ -66,10 +66,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.ssd_step.argtypes = [fp, vp, fp, fp, vp, vp, fp] + [i64] * 5 + [ctypes.c_int, vp, vp]
         lib.ssd_step.restype = ctypes.c_int
         pi64 = ctypes.POINTER(ctypes.c_int64)
-        lib.ssd_fwd_autotune.argtypes = lib.ssd_fwd.argtypes + [ctypes.c_int, pi64, pi64,
+        lib.ssd_fwd_autotune.argtypes = lib.ssd_fwd.argtypes + [ctypes.c_int, pi64, pi64, pi64,
                                                                 ctypes.POINTER(ctypes.c_float)]
         lib.ssd_fwd_autotune.restype = ctypes.c_int
-        lib.ssd_fwd_plan.argtypes = [i64] * 7 + [ctypes.c_int, pi64, pi64]
+        lib.ssd_fwd_plan.argtypes = [i64] * 7 + [ctypes.c_int, pi64, pi64, pi64]
         lib.ssd_fwd_plan.restype = ctypes.c_int
         lib.ssd_fwd_autotune_reset.argtypes = []
         lib.ssd_fwd_autotune_reset.restype = None
@@ -216,27 +216,30 @@ def ssd_fwd_autotune(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, reps: in
                      workspace: torch.Tensor | None = None):
     """Times ssd_fwd's candidate segment plans on these inputs and keeps the
     fastest for this shape (later ssd_fwd calls use it).  Blocks until done.
-    Returns (y, h_final or None, {"nsegs", "nsplit", "ms_per_call"}); y and
+    Returns (y, h_final or None, {"nsegs", "nsplit", "agg_pieces", "ms_per_call"}); y and
     h_final are the chosen plan's result.  nsegs == 0: nothing to tune."""
     lib = load_library()
     args, y, hf = _ssd_fwd_args(lib, x, dt, A, B, C, D, h0, chunk, want_final_state, out, workspace)
-    nsegs, nsplit, ms = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_float()
-    st = lib.ssd_fwd_autotune(*args, int(reps), ctypes.byref(nsegs), ctypes.byref(nsplit), ctypes.byref(ms))
+    nsegs, nsplit, pieces, ms = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_float()
+    st = lib.ssd_fwd_autotune(*args, int(reps), ctypes.byref(nsegs), ctypes.byref(nsplit), ctypes.byref(pieces),
+                              ctypes.byref(ms))
     if st != SSD_OK:
         raise SSDError(st, "ssd_fwd_autotune")
-    return y, hf, {"nsegs": nsegs.value, "nsplit": nsplit.value, "ms_per_call": ms.value}
+    return y, hf, {"nsegs": nsegs.value, "nsplit": nsplit.value, "agg_pieces": pieces.value,
+                   "ms_per_call": ms.value}
 
 
 def ssd_fwd_plan(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype=torch.bfloat16):
     """The segment plan ssd_fwd uses for a shape: {"nsegs", "nsplit",
-    "source": "tuned" | "heuristic" | "none"}.  Launches nothing."""
+    "agg_pieces", "source": "tuned" | "heuristic" | "none"}.  Launches nothing."""
     lib = load_library()
-    nsegs, nsplit = ctypes.c_int64(), ctypes.c_int64()
+    nsegs, nsplit, pieces = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
     st = lib.ssd_fwd_plan(batch, seqlen, nheads, headdim, dstate, ngroups, int(chunk), _DTYPE_CODE[dtype],
-                          ctypes.byref(nsegs), ctypes.byref(nsplit))
+                          ctypes.byref(nsegs), ctypes.byref(nsplit), ctypes.byref(pieces))
     if st < 0:
         raise SSDError(st, "ssd_fwd_plan")
-    return {"nsegs": nsegs.value, "nsplit": nsplit.value, "source": {0: "heuristic", 1: "tuned", 2: "none"}[st]}
+    return {"nsegs": nsegs.value, "nsplit": nsplit.value, "agg_pieces": pieces.value,
+            "source": {0: "heuristic", 1: "tuned", 2: "none"}[st]}
 
 
 def ssd_fwd_autotune_reset():

@@ -143,23 +143,24 @@ int ssd_fwd_autotune(const void* x, const float* dt, const float* A, const void*
                      const float* D, const float* h0, int64_t batch, int64_t seqlen, int64_t nheads,
                      int64_t headdim, int64_t dstate, int64_t ngroups, int64_t chunk, int dtype, void* y,
                      float* h_final, void* workspace, size_t workspace_bytes, void* stream, int reps,
-                     int64_t* nsegs, int64_t* nsplit, float* ms_per_call) {
-    if (!nsegs || !nsplit || !ms_per_call) return SSD_ERR_NULL;
+                     int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces, float* ms_per_call) {
+    if (!nsegs || !nsplit || !agg_pieces || !ms_per_call) return SSD_ERR_NULL;
     if (reps < 1 || reps > 1000) return SSD_ERR_SHAPE;
     const SsdShape s{batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype};
     const SsdArgs args{x, dt, A, B, C, D, h0, y, h_final, workspace};
     const int st = ssd_fwd_validate(s, args, workspace_bytes);
     if (st != SSD_OK) return st;
-    return cls_ssd_autotune(s, args, static_cast<hipStream_t>(stream), reps, nsegs, nsplit, ms_per_call);
+    return cls_ssd_autotune(s, args, static_cast<hipStream_t>(stream), reps, nsegs, nsplit, agg_pieces,
+                            ms_per_call);
 }
 
 int ssd_fwd_plan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
-                 int64_t chunk, int dtype, int64_t* nsegs, int64_t* nsplit) {
-    if (!nsegs || !nsplit) return SSD_ERR_NULL;
+                 int64_t chunk, int dtype, int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces) {
+    if (!nsegs || !nsplit || !agg_pieces) return SSD_ERR_NULL;
     const SsdShape s{batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype};
     const int st = cls_ssd_check(s);
     if (st != SSD_OK) return st;
-    return cls_ssd_plan_query(s, nsegs, nsplit);
+    return cls_ssd_plan_query(s, nsegs, nsplit, agg_pieces);
 }
 
 void ssd_fwd_autotune_reset(void) { cls_ssd_autotune_reset(); }

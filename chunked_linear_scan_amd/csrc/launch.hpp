@@ -39,10 +39,10 @@ int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t stream);
 // Times the fused path's candidate segment plans on these arguments, keeps the
 // fastest for the shape and leaves its result in y / h_final (blocking).
 int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t stream, int reps, int64_t* nsegs,
-                     int64_t* nsplit, float* ms);
+                     int64_t* nsplit, int64_t* agg_pieces, float* ms);
 // The segment plan ssd_fwd uses for a shape: 1 tuned, 0 heuristic, 2 no plan
 // (not the fused path); negative status on error.
-int cls_ssd_plan_query(const SsdShape& s, int64_t* nsegs, int64_t* nsplit);
+int cls_ssd_plan_query(const SsdShape& s, int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces);
 void cls_ssd_autotune_reset();
 // Three-pass linear scan (linear_scan_3pass.hip); shapes already validated.
 size_t cls_ls3_workspace_bytes(int64_t rows, int64_t L);

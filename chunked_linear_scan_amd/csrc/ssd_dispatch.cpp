@@ -1,4 +1,5 @@
 // SSD validation, workspace sizing and dispatch to the fp32 or bf16 path.
+#include <algorithm>
 #include <array>
 #include <map>
 #include <mutex>
@@ -36,6 +37,7 @@ int ssd_bf16_launch(int TT, int P, int S, const SsdBf16Params& prm, hipStream_t 
 static int g_segments_override = 0;
 static int g_split_override = 0;  // with the segment override: split only the last n chains (0: all)
 static int g_xcd_override = 0;    // XCDs of the tile mapping (0: kXcds)
+static int g_agg_override = 0;    // with the segment override: aggregate pieces per segment (0: heuristic)
 constexpr int kXcds = 8;          // MI355X: 8 XCDs of 32 CUs
 
 // concurrent workgroups of the fused kernel: one per CU
@@ -53,6 +55,7 @@ static int g_force_path = 0;  // 0 auto, 1 the per-(batch, head) chunk kernel, 2
 // whole).
 struct SegChoice {
     int64_t nsegs, nsplit;
+    int64_t agg_d = 0;  // aggregate pieces per segment (0: the heuristic's)
 };
 
 // Segment plans chosen by the autotuner, per (device, shape).
@@ -84,10 +87,16 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
 std::vector<SegChoice> seg_candidates(int64_t nchains, int64_t nc, int64_t slots) {
     std::vector<SegChoice> v{{1, 0}};
     const int64_t r = nchains % slots;
+    auto add = [&](int64_t g, int64_t ns) {
+        // the aggregate launch's pieces per segment: the heuristic's count
+        // (about two workgroups per CU, rounded down), and 2x and 4x finer
+        const int64_t h = std::max<int64_t>(1, (2 * slots) / (ns * (g - 1)));
+        for (int64_t m : {1, 2, 4}) v.push_back({g, ns, m == 1 ? 0 : h * m});
+    };
     for (int64_t g : {2, 3, 4, 6, 8, 12, 16, 24, 32}) {
         if (g > nc) break;
-        if (r > 0 && (nchains - r) + r * g <= 4 * slots) v.push_back({g, r});
-        if (r != nchains && nchains * g <= 4 * slots) v.push_back({g, nchains});
+        if (r > 0 && (nchains - r) + r * g <= 4 * slots) add(g, r);
+        if (r != nchains && nchains * g <= 4 * slots) add(g, nchains);
     }
     return v;
 }
@@ -115,17 +124,20 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     // leave most CUs idle in a last round, so it is split into segments that
     // fill them.  A segment costs its output pass plus its share of the
     // aggregate launch (about half its length), which the split must beat.
-    int64_t nsegs = 1, nsplit = 0;
+    int64_t nsegs = 1, nsplit = 0, want_agg_d = 0;
     SegChoice tuned{};
     if (force) {
         nsegs = force->nsegs;
         nsplit = (force->nsplit > 0 && force->nsplit < nchains) ? force->nsplit : nchains;
+        want_agg_d = force->agg_d;
     } else if (g_segments_override > 0) {
         nsegs = g_segments_override;
         nsplit = (g_split_override > 0 && g_split_override < nchains) ? g_split_override : nchains;
+        want_agg_d = g_agg_override;
     } else if (tuned_choice(tune_key(batch, L, H, P, S, G, chunk, dtype), &tuned)) {
         nsegs = tuned.nsegs;
         nsplit = tuned.nsplit;
+        want_agg_d = tuned.agg_d;
     } else {
         const int64_t slots = fused_slots();
         const int64_t r = nchains % slots;
@@ -147,7 +159,7 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     // the aggregate launch has about two workgroups per CU (it fits two).
     int64_t agg_d = 1, agg_k = k;
     if (nsplit > 0) {
-        agg_d = (2 * fused_slots()) / (nsplit * (nsegs - 1));
+        agg_d = want_agg_d > 0 ? want_agg_d : (2 * fused_slots()) / (nsplit * (nsegs - 1));
         if (agg_d < 1) agg_d = 1;
         if (agg_d > k) agg_d = k;
         agg_k = (k + agg_d - 1) / agg_d;
@@ -257,6 +269,10 @@ extern "C" void cls_ssd_set_segments(int nsegs) { cls::g_segments_override = nse
 // With the segment override set: split only the last `nchains` (batch, head)
 // chains and run the others whole (0: split every chain).
 extern "C" void cls_ssd_set_split(int nchains) { cls::g_split_override = nchains < 0 ? 0 : nchains; }
+
+// With the segment override set: cut each segment into n aggregate pieces
+// (0: the heuristic's count).
+extern "C" void cls_ssd_set_agg_pieces(int n) { cls::g_agg_override = n < 0 ? 0 : n; }
 
 // Tuning hook: the number of XCDs the fused kernel's tile mapping assumes
 // (1: plain index order; 0 restores the default).
@@ -412,9 +428,10 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t s
 // device.  Candidates that reduce to the same plan are timed once.  The call ends with one more pass on the chosen plan, so y and
 // h_final hold exactly what a later ssd_fwd call returns.
 extern "C" int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t stream, int reps, int64_t* nsegs,
-                                int64_t* nsplit, float* ms) {
+                                int64_t* nsplit, int64_t* agg_pieces, float* ms) {
     *nsegs = 0;
     *nsplit = 0;
+    *agg_pieces = 0;
     *ms = 0.0f;
     const std::vector<cls::SegChoice> cands = fused_candidates(s);
     if (cands.empty()) return ssd_launch_plan(s, a, nullptr, stream);
@@ -429,9 +446,11 @@ extern "C" int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t
     for (const cls::SegChoice& c : cands) {
         const cls::SsdFusedPlan q = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
                                                         s.ngroups, s.chunk, s.dtype, &c);
-        const cls::SegChoice ce{q.nsegs, q.nsegs > 1 ? int64_t(q.nchains - q.nwhole) : 0};
+        const cls::SegChoice ce{q.nsegs, q.nsegs > 1 ? int64_t(q.nchains - q.nwhole) : 0,
+                                q.nsegs > 1 ? int64_t(q.agg_d) : 0};
         bool dup = false;
-        for (const auto& e : plans) dup = dup || (e.nsegs == ce.nsegs && e.nsplit == ce.nsplit);
+        for (const auto& e : plans)
+            dup = dup || (e.nsegs == ce.nsegs && e.nsplit == ce.nsplit && e.agg_d == ce.agg_d);
         if (!dup) plans.push_back(ce);
     }
     // One untimed pass over every plan first (clocks and caches settle), then
@@ -461,7 +480,7 @@ extern "C" int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t
         }
     }
     float best_ms = 0.0f;
-    cls::SegChoice best{0, 0};
+    cls::SegChoice best{0, 0, 0};
     for (size_t i = 0; i < plans.size(); ++i)
         if (t_best[i] >= 0.0f && (best.nsegs == 0 || t_best[i] < best_ms)) {
             best_ms = t_best[i];
@@ -477,20 +496,23 @@ extern "C" int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t
     }
     *nsegs = best.nsegs;
     *nsplit = best.nsplit;
+    *agg_pieces = best.agg_d;
     *ms = best_ms;
     return ssd_launch_plan(s, a, &best, stream);
 }
 
-extern "C" int cls_ssd_plan_query(const SsdShape& s, int64_t* nsegs, int64_t* nsplit) {
+extern "C" int cls_ssd_plan_query(const SsdShape& s, int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces) {
     const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
                                                      s.ngroups, s.chunk, s.dtype);
     if (s.dtype == SSD_F32 || !pl.use) {
         *nsegs = 0;
         *nsplit = 0;
+        *agg_pieces = 0;
         return 2;
     }
     *nsegs = pl.nsegs;
     *nsplit = pl.nsegs > 1 ? int64_t(pl.nchains - pl.nwhole) : 0;
+    *agg_pieces = pl.nsegs > 1 ? int64_t(pl.agg_d) : 0;
     cls::SegChoice t{};
     const bool tuned = cls::tuned_choice(cls::tune_key(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
                                                        s.ngroups, s.chunk, s.dtype), &t);

@@ -99,8 +99,10 @@ int ssd_fwd(const void* x, const float* dt, const float* A, const void* B,
  * setting suits every shape).  The one run-time choice of the bf16 head-dim-64
  * path is its segment plan: how many segments a long (batch, head) chain is
  * cut into (each segment's start state comes from a separate aggregate
- * launch), and which chains are cut.  Tile sizes and occupancy are fixed when
- * the kernels are compiled.
+ * launch), which chains are cut, and how many pieces the aggregate launch cuts
+ * each segment into (more pieces fill more of the GPU, and the output launch
+ * folds more of them).  Tile sizes and occupancy are fixed when the kernels
+ * are compiled.
  *
  * ssd_fwd_autotune takes exactly ssd_fwd's arguments (same layouts, same
  * checks, same workspace) plus reps (1..1000).  It runs every candidate plan
@@ -109,7 +111,8 @@ int ssd_fwd(const void* x, const float* dt, const float* A, const void* B,
  * is kept for this shape on the current device.
  * Later ssd_fwd calls with the same shape, dtype and chunk on that device use
  * it.  It returns the chosen plan (*nsegs segments, the last *nsplit chains
- * cut) and its mean time per call in ms.  y and h_final hold the result of
+ * cut, *agg_pieces aggregate pieces per segment; 0 when nothing is cut) and
+ * its mean time per call in ms.  y and h_final hold the result of
  * the chosen plan, which is what ssd_fwd then returns.  Shapes outside the
  * fused path have nothing to tune: one plain ssd_fwd pass, *nsegs = 0.
  * The call blocks until its timed runs finish.  The table is process-wide and
@@ -121,7 +124,7 @@ int ssd_fwd(const void* x, const float* dt, const float* A, const void* B,
  *
  * ssd_fwd_plan reports the plan ssd_fwd would use for a shape without
  * launching anything: returns 1 (a tuned plan), 0 (the built-in heuristic),
- * 2 (the shape does not take the fused path; *nsegs = *nsplit = 0) or a
+ * 2 (the shape does not take the fused path; all three outputs 0) or a
  * negative status.  ssd_fwd_autotune_reset forgets every tuned plan.
  */
 int ssd_fwd_autotune(const void* x, const float* dt, const float* A, const void* B,
@@ -130,11 +133,11 @@ int ssd_fwd_autotune(const void* x, const float* dt, const float* A, const void*
                      int64_t dstate, int64_t ngroups, int64_t chunk, int dtype,
                      void* y, float* h_final, void* workspace, size_t workspace_bytes,
                      void* stream, int reps, int64_t* nsegs, int64_t* nsplit,
-                     float* ms_per_call);
+                     int64_t* agg_pieces, float* ms_per_call);
 
 int ssd_fwd_plan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                  int64_t dstate, int64_t ngroups, int64_t chunk, int dtype,
-                 int64_t* nsegs, int64_t* nsplit);
+                 int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces);
 
 void ssd_fwd_autotune_reset(void);
 

@@ -61,11 +61,13 @@ def test_autotune_result_plan_and_later_calls(Bt, L, H, G, chunk):
     nchains = Bt * H
     assert 1 <= info["nsegs"] <= 32 and info["ms_per_call"] > 0
     assert (info["nsegs"] == 1) == (info["nsplit"] == 0) and 0 <= info["nsplit"] <= nchains
+    assert (info["nsegs"] == 1) == (info["agg_pieces"] == 0) and info["agg_pieces"] >= 0
     ry, rh = oracle(c)
     check("tuned y", y.float().cpu().numpy(), ry, TOL_BF16)
     check("tuned h_final", hf.cpu().numpy(), rh, TOL_BF16)
     after = cls.ssd_fwd_plan(Bt, L, H, P, S, G, chunk)
-    assert after == {"nsegs": info["nsegs"], "nsplit": info["nsplit"], "source": "tuned"}
+    assert after == {"nsegs": info["nsegs"], "nsplit": info["nsplit"], "agg_pieces": info["agg_pieces"],
+                     "source": "tuned"}
     y2, hf2 = cls.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=chunk)
     torch.cuda.synchronize()
     assert torch.equal(y2.view(torch.int16), y.view(torch.int16))
@@ -103,7 +105,7 @@ def test_autotune_without_a_plan_runs_one_plain_pass():
         d = {k: v.cuda() for k, v in c.items()}
         y, hf, info = cls.ssd_fwd_autotune(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=64)
         torch.cuda.synchronize()
-        assert info["nsegs"] == 0 and info["nsplit"] == 0
+        assert info["nsegs"] == 0 and info["nsplit"] == 0 and info["agg_pieces"] == 0
         assert cls.ssd_fwd_plan(1, 300, 4, P, S, 2, 64, dtype)["source"] == "none"
         ry, rh = oracle(c)
         check(f"{dtype} y", y.float().cpu().numpy(), ry, tol)

@@ -279,3 +279,27 @@ def test_segment_mixed_whole_and_split(nsegs, nsplit, chunk):
     ry, rh, _, _ = oracle_run(inp)
     assert_close(y, ry, TOL_BF16, f"y nsegs={nsegs} nsplit={nsplit}")
     assert_close(hf, rh, TOL_BF16, f"h nsegs={nsegs} nsplit={nsplit}")
+
+
+@pytest.mark.parametrize("nsegs,pieces,chunk", [(3, 1, 64), (3, 5, 64), (4, 16, 32), (2, 40, 64), (5, 3, 128)])
+def test_aggregate_pieces_forced(nsegs, pieces, chunk):
+    """The aggregate launch cuts each segment but the last into `pieces`
+    pieces (the autotuner searches this count); the output launch folds them
+    in order.  Counts from one piece per segment to one chunk per piece (the
+    count is capped at the segment's chunks), uneven last pieces included."""
+    ct = __import__("ctypes")
+    lib = cls.load_library()
+    lib.cls_ssd_set_segments.argtypes = [ct.c_int]
+    lib.cls_ssd_set_agg_pieces.argtypes = [ct.c_int]
+    print(f"[ssd] aggregate pieces nsegs={nsegs} pieces={pieces} chunk={chunk}", flush=True)
+    inp = small_case(80 + pieces, 2, 64 * 40 + 17, 3, 64, 128, 1, torch.bfloat16, dt_shift=-4.0)
+    lib.cls_ssd_set_segments(nsegs)
+    lib.cls_ssd_set_agg_pieces(pieces)
+    try:
+        y, hf = gpu_run(inp, chunk=chunk)
+    finally:
+        lib.cls_ssd_set_segments(0)
+        lib.cls_ssd_set_agg_pieces(0)
+    ry, rh, _, _ = oracle_run(inp)
+    assert_close(y, ry, TOL_BF16, f"y nsegs={nsegs} pieces={pieces}")
+    assert_close(hf, rh, TOL_BF16, f"h nsegs={nsegs} pieces={pieces}")
