@@ -8,12 +8,14 @@
 // chunked pass).
 //
 // The step reads and rewrites the state, P x S fp32 per (batch, head), and
-// touches little else, so it is bound by HBM.  One 256-thread workgroup per
+// touches little else, so it is bound by HBM.  One 512-thread workgroup per
 // (batch, head).  A row of the state (one head-dim channel, S states) is held
 // by S/4 lanes as float4s, so one wave instruction reads or writes 1 KB of
 // consecutive state (64 / (S/4) rows).  Each thread loads kStU row steps
-// before it computes, so a workgroup keeps 16 KB of loads in flight (eight
-// steps measured slower).  The state is read and written with non-temporal
+// before it computes, so a workgroup keeps 16 KB of loads in flight: the
+// whole 64 x 128 state in one pass.  Measured on a 64-sequence, 80-head
+// token: 512 threads x 2 steps 55.6-56.0 us; 256 x 4 57.1; 512 x 1 56.7-56.9;
+// 1024 x 1 or 2 58.5-59.2; 256 x 2 58.9; 128 x 4 61.5.  The state is read and written with non-temporal
 // accesses: each byte is touched once per token, and keeping it out of the
 // caches measured 14 % faster on a 64-sequence batch of 80 heads.  The
 // output's sum over the states is an xor-shuffle tree inside each row's lanes
@@ -24,8 +26,9 @@
 namespace cls {
 namespace {
 
-constexpr int kStThreads = 256;
-constexpr int kStU = 4;  // row steps a thread loads at once
+constexpr int kStThreads = 512;
+constexpr int kStWaves = kStThreads / 64;
+constexpr int kStU = 2;  // row steps a thread loads at once
 
 struct StepParams {
     float* h;
@@ -74,13 +77,13 @@ __global__ __launch_bounds__(kStThreads) void ssd_step_kernel(StepParams p) {
     }
     float* hb = p.h + bh * int64_t(p.P) * p.S;
     const int64_t xb = bh * p.P;
-    for (int p0 = 0; p0 < p.P; p0 += 4 * R * kStU) {
+    for (int p0 = 0; p0 < p.P; p0 += kStWaves * R * kStU) {
         f32x4 hv[kStU];
         float xv[kStU];
         int row[kStU];
 #pragma unroll
         for (int u = 0; u < kStU; ++u) {
-            row[u] = p0 + (u * 4 + wave) * R + sub;
+            row[u] = p0 + (u * kStWaves + wave) * R + sub;
             const bool ok = row[u] < p.P;
             const f32x4* src = reinterpret_cast<const f32x4*>(hb + int64_t(row[u]) * p.S + 4 * l);
             hv[u] = ok ? __builtin_nontemporal_load(src) : f32x4{0.f, 0.f, 0.f, 0.f};
