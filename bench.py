@@ -12,8 +12,15 @@ each of its two kernels, which gives the fused kernel's own time for the
 roofline.  Input and output buffers rotate over enough copies that the
 footprint exceeds 1 GiB, so the 256 MB Infinity Cache cannot serve repeated
 steps.  The linear scan (one kernel) is timed the same way in its own loop and
-reported in the ``linear_scan`` object of the same JSON line, and so is one
-decode token (``ssd_step``, the ``ssd_step`` object).
+reported in the ``linear_scan`` object of the same JSON line (with its bf16
+forms and a plain elementwise kernel of the same traffic beside it), and so are
+the three-pass scan (``linear_scan_three_pass``) and one decode token
+(``ssd_step``).  The ``autotune`` object compares the plan ssd_fwd_autotune
+keeps for the workload with the built-in heuristic's, timed back to back.
+
+Other modes: ``--scan-ceiling-sweep`` (linear_scan against torch.mul over row
+lengths), ``--copy-probe`` / ``--record-traffic`` (the HBM traffic counters),
+``--no-autotune`` (counter and trace runs), ``--no-scan``, ``--workload``.
 
 The CPU baseline is the float64 oracle, unmodified, run on a bounded sample
 of the same workload (a few whole (batch, head) sequences, one per worker
