@@ -475,16 +475,18 @@ def bench_scan(name, steps, warmup, want_cpu):
 
 
 def scan_ceiling_sweep(steps, warmup):
-    """linear_scan against torch.mul(a, b, out=h), which moves the same bytes,
-    at 96 MiB per array and several row lengths, plus twice and half that size
-    at L = 65536."""
+    """linear_scan against torch.mul(a, b, out=h), which moves the same bytes:
+    the row lengths of the page's table ("Selective-scan CUDA kernels",
+    section "Results": 96 MiB per array, L = 2048 ... 65536), then twice and
+    half that size at L = 65536, packed rows of 8186 and longer rows."""
     import torch
     import chunked_linear_scan_amd as cls
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev)
     g = torch.Generator(device=dev).manual_seed(1)
-    for rows, L in [(384, 65536), (768, 65536), (192, 65536), (3072, 8186), (1536, 16384), (96, 262144),
-                    (24, 1048576)]:
+    # the page's table: 96 MiB per array at L = 2048 ... 65536; then other sizes
+    for rows, L in [(12288, 2048), (6144, 4096), (3072, 8192), (1536, 16384), (768, 32768), (384, 65536),
+                    (768, 65536), (192, 65536), (3072, 8186), (96, 262144), (24, 1048576)]:
         nsets = 3
         sets = [(0.9 + 0.1 * torch.rand(rows, L, device=dev, generator=g),
                  torch.randn(rows, L, device=dev, generator=g), torch.empty(rows, L, device=dev))

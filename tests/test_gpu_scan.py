@@ -47,7 +47,8 @@ def test_full_workload(name):
     (1, 1), (3, 1), (5, 2), (7, 3), (2, 4), (4, 5), (3, 31), (3, 32), (3, 33), (1, 4089), (2, 4090),
     (2, 4091), (2, 4093), (2, 4096), (2, 4097), (3, 8185), (2, 8186), (2, 8187), (3, 8191), (3, 8192),
     (3, 8193), (2, 16383), (2, 16384), (2, 16385), (3, 24576), (3, 24580), (1, 65533),
-    (5, 12345), (1000, 7), (257, 129)])
+    (5, 12345), (1000, 7), (257, 129), (5, 4096), (9, 2048), (3, 8184), (7, 1024), (33, 256), (5, 4), (17, 8),
+    (4097, 4)])
 def test_edge_sizes(rows, L):
     w = workloads.make_scan_inputs(rows, L, seed=rows * 7919 + L)
     check(w["a"], w["b"], label="edge")
@@ -171,3 +172,12 @@ def test_typed_scan_full_workload_bf16_inputs():
     err = compare.rel_l2(h.cpu().numpy(), ref)
     print(f"  rel-L2 {err:.3e}", flush=True)
     assert err <= TOL
+
+
+@pytest.mark.parametrize("rows,L", [(12288, 2048), (6144, 4096)])
+def test_page_table_row_lengths(rows, L):
+    """Two of the row lengths of the page's table ("Selective-scan CUDA
+    kernels", section "Results": 96 MiB per array), which run as whole rows
+    packed several to a tile."""
+    w = workloads.make_scan_inputs(rows, L, seed=rows + L)
+    check(w["a"], w["b"], label=f"page table L={L}")
