@@ -138,7 +138,8 @@ TYPED = [(torch.bfloat16, torch.float32), (torch.bfloat16, torch.bfloat16), (tor
 @pytest.mark.parametrize("din,dout", TYPED)
 @pytest.mark.parametrize("rows,L", [(3, 1), (5, 7), (3, 33), (2, 4097), (3, 8186), (2, 8187), (3, 8193),
                                     (2, 16378), (2, 16379), (2, 16384), (2, 16385), (3, 32771), (1000, 7),
-                                    (257, 129), (3, 5461), (4, 65536), (1, 65533)])
+                                    (257, 129), (3, 5461), (5, 4096), (9, 2048), (33, 256), (4097, 4),
+                                    (4, 65536), (1, 65533)])
 def test_typed_scan_matches_oracle(din, dout, rows, L):
     """bf16 / fp32 elements through linear_scan_typed.  The oracle runs on the
     exact float64 values of the (possibly bf16) inputs.  With an fp32 h the
