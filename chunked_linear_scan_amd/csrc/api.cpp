@@ -31,10 +31,11 @@ ScanPlan plan_scan(int64_t rows, int64_t L) {
     p.segmented = L <= kLsTile - 6;
     if (p.segmented) {
         // A packed tile covers its rows from the 16-byte boundary at or before
-        // the first row's start (up to 3 elements early).  When L is a
-        // multiple of 4 every row starts on such a boundary (the base is
-        // 16-byte aligned), so whole rows fill the tile exactly.
-        p.rows_per_tile = (L % 4 == 0) ? kLsTile / L : (kLsTile - 6) / L;
+        // the first row's start, up to 3 elements early, so its rows may hold
+        // kLsTile - 3 elements.  When L is a multiple of 4 every row starts on
+        // such a boundary (the base is 16-byte aligned), so whole rows fill
+        // the tile exactly.
+        p.rows_per_tile = (L % 4 == 0) ? kLsTile / L : (kLsTile - 3) / L;
         p.tiles_per_row = 1;
         p.ntiles = (rows + p.rows_per_tile - 1) / p.rows_per_tile;
         p.claim_off = p.done_off = p.status_off = kHeader;

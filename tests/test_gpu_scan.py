@@ -48,7 +48,7 @@ def test_full_workload(name):
     (2, 4091), (2, 4093), (2, 4096), (2, 4097), (3, 8185), (2, 8186), (2, 8187), (3, 8191), (3, 8192),
     (3, 8193), (2, 16383), (2, 16384), (2, 16385), (3, 24576), (3, 24580), (1, 65533),
     (5, 12345), (1000, 7), (257, 129), (5, 4096), (9, 2048), (3, 8184), (7, 1024), (33, 256), (5, 4), (17, 8),
-    (4097, 4)])
+    (4097, 4), (5, 4094), (7, 2730), (4, 4093), (3, 8186), (11, 2047)])
 def test_edge_sizes(rows, L):
     w = workloads.make_scan_inputs(rows, L, seed=rows * 7919 + L)
     check(w["a"], w["b"], label="edge")
