@@ -27,6 +27,17 @@ _lib = None
 _lib_lock = threading.Lock()
 
 
+class PlanRequest(ctypes.Structure):
+    """``ssd_plan_request`` of include/chunked_linear_scan_testing.h."""
+    _fields_ = [("path", ctypes.c_int32), ("s3", ctypes.c_int32), ("nsegs", ctypes.c_int64),
+                ("nsplit", ctypes.c_int64), ("agg_pieces", ctypes.c_int64), ("xcds", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+PATH = {"auto": 0, "chunk": 1, "fused": 2}
+S3 = {"auto": 0, "reduce": 1, "lookback": 2}
+
+
 class SSDError(RuntimeError):
     """A negative status returned by the library."""
 
@@ -73,6 +84,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.ssd_fwd_plan.restype = ctypes.c_int
         lib.ssd_fwd_autotune_reset.argtypes = []
         lib.ssd_fwd_autotune_reset.restype = None
+        lib.ssd_fwd_planned.argtypes = lib.ssd_fwd.argtypes + [ctypes.POINTER(PlanRequest), vp]
+        lib.ssd_fwd_planned.restype = ctypes.c_int
+        lib.ssd_fwd_planned_workspace_size.argtypes = [i64] * 7 + [ctypes.c_int, ctypes.POINTER(PlanRequest)]
+        lib.ssd_fwd_planned_workspace_size.restype = sz
         _lib = lib
         return lib
 
@@ -92,23 +107,58 @@ def _stream_handle(device: torch.device):
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-class _Workspace:
-    """Per-device cached workspace.  It is zero-filled when (re)allocated; the
-    kernels leave their flags and counters at zero, so it is reused as is."""
+def _stream_key(device: torch.device) -> int:
+    return int(torch.cuda.current_stream(device).cuda_stream)
 
-    def __init__(self):
+
+def workspace_errors(workspaces=None, reset: bool = True) -> int:
+    """Sum of the error words of the given workspaces (default: every
+    workspace the binding has cached), after waiting for their devices.
+
+    The kernels' bounded waits (the scans' look-back, the SSD kernels'
+    hand-offs between wave roles) never hang: when one gives up it adds 1 to
+    the 32-bit word at the start of its workspace and carries on, so its
+    outputs are then wrong.  Nonzero means such a call happened since the
+    word was last cleared; ``reset`` clears it."""
+    if workspaces is None:
+        workspaces = [b for _, b in _scan_ws.buffers()] + [b for _, b in _ssd_ws.buffers()]
+    total = 0
+    for ws in workspaces:
+        if ws.device.type == "cuda":
+            torch.cuda.synchronize(ws.device)
+        word = ws[:4].view(torch.int32)
+        v = int(word.item())
+        if v and reset:
+            word.zero_()
+        total += v
+    return total
+
+
+class _Workspace:
+    """Workspaces cached per (device, stream).  Calls that share a workspace
+    must be ordered on one stream (the library's contract), so each stream of
+    each device gets its own; it is allocated while that stream is current,
+    so torch's allocator orders its reuse after the work queued on it.  It is
+    zero-filled when (re)allocated; the kernels leave their flags and
+    counters at zero, so it is reused as is."""
+
+    def __init__(self, alloc=None):
         self._buf = {}
         self._lock = threading.Lock()
+        self._alloc = alloc or (lambda device, size: torch.zeros(size, dtype=torch.uint8, device=device))
 
-    def get(self, device: torch.device, nbytes: int) -> torch.Tensor:
-        key = (device.type, device.index)
+    def get(self, device, stream_key, nbytes: int) -> torch.Tensor:
+        key = (str(device), stream_key)
         with self._lock:
             buf = self._buf.get(key)
             if buf is None or buf.numel() < nbytes:
-                size = max(nbytes, 4096)
-                buf = torch.zeros(size, dtype=torch.uint8, device=device)
+                buf = self._alloc(device, max(nbytes, 4096))
                 self._buf[key] = buf
             return buf
+
+    def buffers(self):
+        with self._lock:
+            return list(self._buf.items())
 
 
 _scan_ws = _Workspace()
@@ -152,7 +202,7 @@ def linear_scan(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = Non
     need = lib.linear_scan_workspace_size(rows, length)
     if need == 0:
         raise SSDError(-2, "linear_scan_workspace_size")
-    ws = _scan_ws.get(a.device, need) if workspace is None else workspace
+    ws = _scan_ws.get(a.device, _stream_key(a.device), need) if workspace is None else workspace
     if a.dtype == torch.float32 and h.dtype == torch.float32:
         st = lib.linear_scan(_ptr(a), _ptr(b), _ptr(h), rows, length, _ptr(ws), ws.numel(),
                              _stream_handle(a.device))
@@ -164,7 +214,7 @@ def linear_scan(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = Non
     return h
 
 
-def _ssd_fwd_args(lib, x, dt, A, B, C, D, h0, chunk, want_final_state, out, workspace):
+def _ssd_fwd_args(lib, x, dt, A, B, C, D, h0, chunk, want_final_state, out, workspace, plan=None):
     """Checks ssd_fwd's tensors and returns the C call's argument list."""
     if x.dtype not in _DTYPE_CODE:
         raise TypeError("x must be float32 or bfloat16")
@@ -187,10 +237,13 @@ def _ssd_fwd_args(lib, x, dt, A, B, C, D, h0, chunk, want_final_state, out, work
     _check_cuda("out", y, x.dtype, x.shape)
     hf = torch.empty((Bt, H, P, S), dtype=torch.float32, device=x.device) if want_final_state else None
     code = _DTYPE_CODE[x.dtype]
-    need = lib.ssd_fwd_workspace_size(Bt, L, H, P, S, G, chunk, code)
+    if plan is None:
+        need = lib.ssd_fwd_workspace_size(Bt, L, H, P, S, G, chunk, code)
+    else:
+        need = lib.ssd_fwd_planned_workspace_size(Bt, L, H, P, S, G, chunk, code, ctypes.byref(plan))
     ws = workspace
     if ws is None:
-        ws = _ssd_ws.get(x.device, max(need, 1))
+        ws = _ssd_ws.get(x.device, _stream_key(x.device), max(need, 1))
     args = [_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(h0), Bt, L, H, P, S, G, int(chunk), code,
             _ptr(y), _ptr(hf), _ptr(ws), ws.numel(), _stream_handle(x.device)]
     return args, y, hf
@@ -208,6 +261,36 @@ def ssd_fwd(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, want_final_state:
     st = lib.ssd_fwd(*args)
     if st != SSD_OK:
         raise SSDError(st, "ssd_fwd")
+    return y, hf
+
+
+def plan_request(path="auto", s3="auto", nsegs=0, nsplit=0, agg_pieces=0, xcds=0) -> PlanRequest:
+    """An explicit plan for ``ssd_fwd_planned`` (see the testing header)."""
+    return PlanRequest(PATH[path], S3[s3], int(nsegs), int(nsplit), int(agg_pieces), int(xcds), 0)
+
+
+def ssd_fwd_planned(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, plan: PlanRequest | None = None,
+                    events=None, want_final_state: bool = True, out: torch.Tensor | None = None,
+                    workspace: torch.Tensor | None = None):
+    """``ssd_fwd`` with an explicit plan (tests and measurement).  ``events``:
+    None, or four torch.cuda.Event(enable_timing=True) recorded on the current
+    stream before the first launch, after the CB pass, after the aggregate
+    launch and after the output launch."""
+    lib = load_library()
+    plan = plan if plan is not None else plan_request()
+    args, y, hf = _ssd_fwd_args(lib, x, dt, A, B, C, D, h0, chunk, want_final_state, out, workspace, plan)
+    evp = None
+    if events is not None:
+        if len(events) != 4:
+            raise ValueError("events must be four torch.cuda.Event")
+        stream = torch.cuda.current_stream(x.device)
+        for e in events:
+            if e.cuda_event == 0:  # torch creates the event at its first record
+                e.record(stream)
+        evp = (ctypes.c_void_p * 4)(*[e.cuda_event for e in events])
+    st = lib.ssd_fwd_planned(*args, ctypes.byref(plan), evp)
+    if st != SSD_OK:
+        raise SSDError(st, "ssd_fwd_planned")
     return y, hf
 
 
@@ -301,5 +384,5 @@ def ssd_step(h, x, dt, A, B, C, D=None, out: torch.Tensor | None = None):
 
 
 __all__ = ["linear_scan", "linear_scan_three_pass", "ssd_fwd", "ssd_fwd_autotune", "ssd_fwd_plan",
-           "ssd_fwd_autotune_reset", "ssd_step", "load_library", "strerror", "SSDError", "LIB_PATH",
-           "SSD_F32", "SSD_BF16"]
+           "ssd_fwd_autotune_reset", "ssd_fwd_planned", "plan_request", "ssd_step", "load_library", "strerror",
+           "workspace_errors", "SSDError", "LIB_PATH", "SSD_F32", "SSD_BF16"]

@@ -7,7 +7,9 @@
 #include <string.h>
 
 #include "../../include/chunked_linear_scan.h"
+#include "../../include/chunked_linear_scan_testing.h"
 #include "launch.hpp"
+
 
 namespace {
 
@@ -141,7 +143,62 @@ int ssd_fwd(const void* x, const float* dt, const float* A, const void* B, const
     const SsdArgs args{x, dt, A, B, C, D, h0, y, h_final, workspace};
     const int st = ssd_fwd_validate(s, args, workspace_bytes);
     if (st != SSD_OK) return st;
-    return cls_ssd_launch(s, args, static_cast<hipStream_t>(stream));
+    return cls_ssd_launch(s, args, SsdLaunchOpts{}, static_cast<hipStream_t>(stream));
+}
+
+// The launch options an ssd_plan_request asks for (false: a field is out of range).
+static bool plan_options(const ssd_plan_request* plan, cls::SegChoice* seg, SsdLaunchOpts* o) {
+    *o = SsdLaunchOpts{};
+    if (!plan) return true;
+    if (plan->path < SSD_PATH_AUTO || plan->path > SSD_PATH_FUSED) return false;
+    if (plan->s3 < SSD_S3_AUTO || plan->s3 > SSD_S3_LOOKBACK) return false;
+    if (plan->nsegs < 0 || plan->nsegs > 64 || plan->nsplit < 0 || plan->agg_pieces < 0) return false;
+    if (plan->agg_pieces > (int64_t(1) << 20) || plan->nsplit > (int64_t(1) << 31)) return false;
+    if (plan->xcds < 0 || plan->xcds > 64 || plan->reserved != 0) return false;
+    o->path = plan->path;
+    o->s3 = plan->s3;
+    o->xcds = plan->xcds;
+    if (plan->nsegs > 0) {
+        *seg = cls::SegChoice{plan->nsegs, plan->nsplit, plan->agg_pieces};
+        o->force = seg;
+    }
+    return true;
+}
+
+size_t ssd_fwd_planned_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                                      int64_t dstate, int64_t ngroups, int64_t chunk, int dtype,
+                                      const ssd_plan_request* plan) {
+    const SsdShape s{batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype};
+    cls::SegChoice seg{};
+    SsdLaunchOpts o{};
+    if (cls_ssd_check(s) != SSD_OK || !plan_options(plan, &seg, &o)) return 0;
+    const size_t need = cls_ssd_plan_bytes(s, o);
+    const size_t base = cls_ssd_workspace_bytes(s);
+    return need > base ? need : base;
+}
+
+int ssd_fwd_planned(const void* x, const float* dt, const float* A, const void* B, const void* C,
+                    const float* D, const float* h0, int64_t batch, int64_t seqlen, int64_t nheads,
+                    int64_t headdim, int64_t dstate, int64_t ngroups, int64_t chunk, int dtype, void* y,
+                    float* h_final, void* workspace, size_t workspace_bytes, void* stream,
+                    const ssd_plan_request* plan, void* const* events) {
+    const SsdShape s{batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype};
+    const SsdArgs args{x, dt, A, B, C, D, h0, y, h_final, workspace};
+    cls::SegChoice seg{};
+    SsdLaunchOpts o{};
+    if (!plan_options(plan, &seg, &o)) return SSD_ERR_SHAPE;
+    const int st = ssd_fwd_validate(s, args, workspace_bytes);
+    if (st != SSD_OK) return st;
+    if (workspace_bytes < cls_ssd_plan_bytes(s, o)) return SSD_ERR_WORKSPACE;
+    hipEvent_t ev[4];
+    if (events) {
+        for (int k = 0; k < 4; ++k) {
+            if (!events[k]) return SSD_ERR_NULL;
+            ev[k] = static_cast<hipEvent_t>(events[k]);
+        }
+        o.ev = ev;
+    }
+    return cls_ssd_launch(s, args, o, static_cast<hipStream_t>(stream));
 }
 
 int ssd_fwd_autotune(const void* x, const float* dt, const float* A, const void* B, const void* C,

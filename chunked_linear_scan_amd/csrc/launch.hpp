@@ -11,6 +11,25 @@ struct SsdShape {
     int dtype;
 };
 
+namespace cls {
+// Segment plan of the fused SSD path: each split chain is cut into nsegs
+// segments, and the last nsplit (batch, head) chains are split (the others run
+// whole).
+struct SegChoice {
+    int64_t nsegs, nsplit;
+    int64_t agg_d = 0;  // aggregate pieces per segment (0: the heuristic's)
+};
+}  // namespace cls
+
+// Per-call choices of ssd_fwd_planned (ssd_fwd passes the defaults).
+struct SsdLaunchOpts {
+    int path = 0;                          // SSD_PATH_*
+    int s3 = 0;                            // SSD_S3_*
+    const cls::SegChoice* force = nullptr;  // segment plan, or null: tuned or heuristic
+    int xcds = 0;                          // XCDs of the chain mapping (0: the device's)
+    hipEvent_t* ev = nullptr;              // four events to record, or null
+};
+
 struct SsdArgs {
     const void* x;
     const float* dt;
@@ -35,7 +54,10 @@ int cls_launch_linear_scan(const void* a, const void* b, void* h, int64_t rows, 
 // negative status).
 int cls_ssd_check(const SsdShape& s);
 size_t cls_ssd_workspace_bytes(const SsdShape& s);
-int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t stream);
+int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, const SsdLaunchOpts& o, hipStream_t stream);
+// Workspace bytes of the plan a call with these options runs (0 for paths
+// without a workspace).
+size_t cls_ssd_plan_bytes(const SsdShape& s, const SsdLaunchOpts& o);
 // Times the fused path's candidate segment plans on these arguments, keeps the
 // fastest for the shape and leaves its result in y / h_final (blocking).
 int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t stream, int reps, int64_t* nsegs,

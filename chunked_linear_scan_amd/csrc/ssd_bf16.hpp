@@ -28,6 +28,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "device_once.hpp"
 #include "ssd_kernels.hpp"
 
 namespace cls {
@@ -337,13 +338,14 @@ __global__ __launch_bounds__(kBfThreads) void ssd_chunk_kernel(SsdBf16Params p) 
 template <int TT, int P, int S>
 int launch_ssd_bf16_tpl(const SsdBf16Params& prm, hipStream_t stream) {
     const size_t lds = ssd_bf16_lds_bytes(TT, P, S);
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_chunk_kernel<TT, P, S>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) != hipSuccess)
-            return -7;
-        attr_set = true;
-    }
+    static DeviceOnce attrs;
+    if (run_once_per_device(attrs, [lds] {
+            return hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_chunk_kernel<TT, P, S>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) == hipSuccess
+                       ? 0
+                       : -7;
+        }) != 0)
+        return -7;
     const dim3 block{uint32_t(kBfThreads), 1u, 1u};
     const dim3 gcb{cb_grid<TT>(prm), 1u, 1u};
     hipLaunchKernelGGL((ssd_cb_kernel<TT, S>), gcb, block, 0, stream, prm);

@@ -32,13 +32,7 @@ int ssd_bf16_launch(int TT, int P, int S, const SsdBf16Params& prm, hipStream_t 
     }
 }
 
-// Validation hooks (not part of the public header) that override the fused
-// kernel's segment plan: segments per split chain, and how many chains are split.
-static int g_segments_override = 0;
-static int g_split_override = 0;  // with the segment override: split only the last n chains (0: all)
-static int g_xcd_override = 0;    // XCDs of the tile mapping (0: kXcds)
-static int g_agg_override = 0;    // with the segment override: aggregate pieces per segment (0: heuristic)
-constexpr int kXcds = 8;          // MI355X: 8 XCDs of 32 CUs
+constexpr int kXcds = 8;  // MI355X: 8 XCDs of 32 CUs
 
 // concurrent workgroups of the fused kernel: one per CU
 int64_t fused_slots() {
@@ -48,15 +42,6 @@ int64_t fused_slots() {
         return n;
     return 256;
 }
-static int g_force_path = 0;  // 0 auto, 1 the per-(batch, head) chunk kernel, 2 the fused kernel
-
-// Segment plan of the fused path: each split chain is cut into nsegs
-// segments, and the last nsplit (batch, head) chains are split (the others run
-// whole).
-struct SegChoice {
-    int64_t nsegs, nsplit;
-    int64_t agg_d = 0;  // aggregate pieces per segment (0: the heuristic's)
-};
 
 // Segment plans chosen by the autotuner, per (device, shape).
 using TuneKey = std::array<int64_t, 9>;
@@ -82,7 +67,7 @@ bool tuned_choice(const TuneKey& k, SegChoice* out) {
 // rounds of the CUs cut into 2..32 segments; every chain cut into 2..32
 // segments.  Plans of more than four rounds of workgroups are left out.
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
-                            int64_t chunk, int dtype, const SegChoice* force);
+                            int64_t chunk, int dtype, const SegChoice* force, int path);
 
 std::vector<SegChoice> seg_candidates(int64_t nchains, int64_t nc, int64_t slots) {
     std::vector<SegChoice> v{{1, 0}};
@@ -101,10 +86,11 @@ std::vector<SegChoice> seg_candidates(int64_t nchains, int64_t nc, int64_t slots
     return v;
 }
 
-// force: null (test override, else a tuned choice for this shape, else the
-// heuristic), or the segment plan to use.
+// force: null (a tuned choice for this shape, else the heuristic), or the
+// segment plan to use.  path: SSD_PATH_* of the call (SSD_PATH_CHUNK keeps
+// the fused path out).
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
-                            int64_t chunk, int dtype, const SegChoice* force) {
+                            int64_t chunk, int dtype, const SegChoice* force, int path) {
     SsdFusedPlan pl{};
     // The kernel's quadratic block is at most 128 tokens: a longer chunk is run
     // as sub-chunks of 128 with the state passed between them, which changes the
@@ -113,7 +99,7 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     chunk = chunk > kFusedMaxChunk ? kFusedMaxChunk : chunk;
     const int TT = bf16_tile_tokens(int(chunk));
     pl.use = dtype == 1 && P == 64 && (S == 64 || S == 128) && ssd_fused_lds_bytes(TT, int(S)) > 0 &&
-             ssd_fused_lds_bytes(TT, int(S)) <= 160 * 1024 && g_force_path != 1;
+             ssd_fused_lds_bytes(TT, int(S)) <= 160 * 1024 && path != 1;
     // the kernel's per-chunk buffer ranges and lane offsets are 32-bit
     if (H * 64 * 2 * TT >= (int64_t(1) << 31) || G * S * 2 * TT >= (int64_t(1) << 31)) pl.use = false;
     if (!pl.use) return pl;
@@ -130,10 +116,6 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
         nsegs = force->nsegs;
         nsplit = (force->nsplit > 0 && force->nsplit < nchains) ? force->nsplit : nchains;
         want_agg_d = force->agg_d;
-    } else if (g_segments_override > 0) {
-        nsegs = g_segments_override;
-        nsplit = (g_split_override > 0 && g_split_override < nchains) ? g_split_override : nchains;
-        want_agg_d = g_agg_override;
     } else if (tuned_choice(tune_key(batch, L, H, P, S, G, chunk, dtype), &tuned)) {
         nsegs = tuned.nsegs;
         nsplit = tuned.nsplit;
@@ -193,95 +175,10 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
 
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
                             int64_t chunk, int dtype) {
-    return ssd_fused_plan(batch, L, H, P, S, G, chunk, dtype, nullptr);
+    return ssd_fused_plan(batch, L, H, P, S, G, chunk, dtype, nullptr, 0);
 }
 
 }  // namespace cls
-
-// Measurement hook (not part of the public header).  While enabled, every
-// fused-path ssd_fwd call records four events on its stream: before the CB
-// pass, after it, after the aggregate launch (recorded also when there is
-// none) and after the output launch.
-// Up to kProfCalls calls are kept (later calls reuse the slots round robin).
-namespace {
-constexpr int kProfCalls = 1024;
-constexpr int kProfEv = 4;
-struct ProfRecord {
-    bool on = false;
-    int calls = 0;
-    std::vector<hipEvent_t> ev;  // kProfEv per call
-};
-ProfRecord g_prof;
-}  // namespace
-
-namespace cls {
-hipEvent_t* ssd_profile_events() {
-    if (!g_prof.on) return nullptr;
-    hipEvent_t* e = g_prof.ev.data() + kProfEv * (g_prof.calls % kProfCalls);
-    ++g_prof.calls;
-    return e;
-}
-}  // namespace cls
-
-// enable != 0: start a new record (creating the events once); 0: stop.
-// Returns 0, or SSD_ERR_HIP when the events cannot be created.
-extern "C" int cls_ssd_profile(int enable) {
-    if (enable && g_prof.ev.empty()) {
-        g_prof.ev.resize(kProfEv * kProfCalls);
-        for (auto& e : g_prof.ev)
-            if (hipEventCreate(&e) != hipSuccess) {
-                g_prof.ev.clear();
-                return SSD_ERR_HIP;
-            }
-    }
-    g_prof.on = enable != 0;
-    if (enable) g_prof.calls = 0;
-    return SSD_OK;
-}
-
-// Waits for the recorded calls and returns the summed times of the CB pass,
-// the aggregate launch and the output launch in milliseconds, and the number
-// of calls summed.
-extern "C" int cls_ssd_profile_read(double* cb_ms, double* agg_ms, double* out_ms, int* calls) {
-    double a = 0.0, b = 0.0, c = 0.0;
-    const int n = g_prof.calls < kProfCalls ? g_prof.calls : kProfCalls;
-    for (int i = 0; i < n; ++i) {
-        hipEvent_t* e = g_prof.ev.data() + kProfEv * i;
-        float t0 = 0.f, t1 = 0.f, t2 = 0.f;
-        if (hipEventSynchronize(e[3]) != hipSuccess || hipEventElapsedTime(&t0, e[0], e[1]) != hipSuccess ||
-            hipEventElapsedTime(&t1, e[1], e[2]) != hipSuccess || hipEventElapsedTime(&t2, e[2], e[3]) != hipSuccess)
-            return SSD_ERR_HIP;
-        a += t0;
-        b += t1;
-        c += t2;
-    }
-    if (cb_ms) *cb_ms = a;
-    if (agg_ms) *agg_ms = b;
-    if (out_ms) *out_ms = c;
-    if (calls) *calls = n;
-    return SSD_OK;
-}
-
-// Tuning hook (not part of the public header): force the number of segments
-// per sequence of the fused SSD kernel (0 restores the heuristic).
-extern "C" void cls_ssd_set_segments(int nsegs) { cls::g_segments_override = nsegs < 0 ? 0 : nsegs; }
-
-// With the segment override set: split only the last `nchains` (batch, head)
-// chains and run the others whole (0: split every chain).
-extern "C" void cls_ssd_set_split(int nchains) { cls::g_split_override = nchains < 0 ? 0 : nchains; }
-
-// With the segment override set: cut each segment into n aggregate pieces
-// (0: the heuristic's count).
-extern "C" void cls_ssd_set_agg_pieces(int n) { cls::g_agg_override = n < 0 ? 0 : n; }
-
-// Tuning hook: the number of XCDs the fused kernel's tile mapping assumes
-// (1: plain index order; 0 restores the default).
-extern "C" void cls_ssd_set_xcds(int n) { cls::g_xcd_override = n < 0 ? 0 : n; }
-
-// Validation hook (not part of the public header): 1 forces the per-(batch,
-// head) chunk kernel for bf16 shapes the fused kernel also covers, 0 restores
-// the automatic choice.
-extern "C" void cls_ssd_force_path(int path) { cls::g_force_path = path; }
 
 namespace {
 
@@ -335,7 +232,7 @@ extern "C" size_t cls_ssd_workspace_bytes(const SsdShape& s) {
         size_t bytes = pl.bytes;
         for (const cls::SegChoice& c : fused_candidates(s)) {
             const cls::SsdFusedPlan q = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
-                                                            s.ngroups, s.chunk, s.dtype, &c);
+                                                            s.ngroups, s.chunk, s.dtype, &c, 0);
             if (q.use && q.bytes > bytes) bytes = q.bytes;
         }
         return bytes;
@@ -344,12 +241,34 @@ extern "C" size_t cls_ssd_workspace_bytes(const SsdShape& s) {
     return size_t(s.batch) * size_t(nchunks(s)) * size_t(s.ngroups) * size_t(TT * TT) * 2 + 256;
 }
 
-static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const cls::SegChoice* force,
-                           hipStream_t stream) {
+extern "C" size_t cls_ssd_plan_bytes(const SsdShape& s, const SsdLaunchOpts& o) {
+    if (s.dtype == SSD_F32) return 0;
+    const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
+                                                     s.ngroups, s.chunk, s.dtype, o.force, o.path);
+    if (pl.use) return pl.bytes;
+    const int64_t TT = cls::bf16_tile_tokens(int(s.chunk));
+    return size_t(s.batch) * size_t(nchunks(s)) * size_t(s.ngroups) * size_t(TT * TT) * 2 + 256;
+}
+
+static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const SsdLaunchOpts& o, hipStream_t stream) {
+    if (o.s3 == 2) return SSD_ERR_UNSUPPORTED;  // the single-pass look-back is not built yet
+    const cls::SegChoice* force = o.force;
+    hipEvent_t* ev = o.ev;
+    // single-launch paths record the call's four events around their launch
+    auto ev_pre = [&]() {
+        if (ev)
+            for (int k = 0; k < 3; ++k) (void)hipEventRecord(ev[k], stream);
+    };
+    auto ev_post = [&]() {
+        if (ev) (void)hipEventRecord(ev[3], stream);
+    };
     if (s.dtype == SSD_F32) {
         cls::SsdF32Params p{a.x, a.dt, a.A, a.B, a.C, a.D, a.h0, a.y, a.h_final, s.batch, s.seqlen,
                             int(s.nheads), int(s.headdim), int(s.dstate), int(s.ngroups), int(s.chunk)};
-        return cls::ssd_f32_launch(p, stream) == 0 ? SSD_OK : SSD_ERR_HIP;
+        ev_pre();
+        const int st = cls::ssd_f32_launch(p, stream);
+        ev_post();
+        return st == 0 ? SSD_OK : SSD_ERR_HIP;
     }
     cls::SsdBf16Params p{};
     p.x = static_cast<const uint16_t*>(a.x);
@@ -369,7 +288,7 @@ static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const cls::SegCh
     p.chunk = int(s.chunk);
     p.nchunks = int(nchunks(s));
     const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
-                                                     s.ngroups, s.chunk, s.dtype, force);
+                                                     s.ngroups, s.chunk, s.dtype, force, o.path);
     if (pl.use) {
         p.chunk = pl.chunk;
         p.nchunks = int((s.seqlen + pl.chunk - 1) / pl.chunk);
@@ -406,19 +325,21 @@ static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const cls::SegCh
         f.nwhole = pl.nwhole;
         f.agg_d = pl.agg_d;
         f.agg_chunks = pl.agg_chunks;
-        f.nxcd = cls::g_xcd_override > 0 ? cls::g_xcd_override : cls::kXcds;
-        const int st = cls::ssd_fused_launch(pl.TT, int(s.dstate), p, f, stream, cls::ssd_profile_events());
+        f.nxcd = o.xcds > 0 ? o.xcds : cls::kXcds;
+        const int st = cls::ssd_fused_launch(pl.TT, int(s.dstate), p, f, stream, ev);
         if (st == -8) return SSD_ERR_UNSUPPORTED;
         return st == 0 ? SSD_OK : SSD_ERR_HIP;
     }
     const int TT = cls::bf16_tile_tokens(int(s.chunk));
+    ev_pre();
     const int st = cls::ssd_bf16_launch(TT, int(s.headdim), int(s.dstate), p, stream);
+    ev_post();
     if (st == -8) return SSD_ERR_UNSUPPORTED;
     return st == 0 ? SSD_OK : SSD_ERR_HIP;
 }
 
-extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, hipStream_t stream) {
-    return ssd_launch_plan(s, a, nullptr, stream);
+extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, const SsdLaunchOpts& o, hipStream_t stream) {
+    return ssd_launch_plan(s, a, o, stream);
 }
 
 // Autotuner of the fused path's segment plan (the one run-time choice of its
@@ -434,7 +355,12 @@ extern "C" int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t
     *agg_pieces = 0;
     *ms = 0.0f;
     const std::vector<cls::SegChoice> cands = fused_candidates(s);
-    if (cands.empty()) return ssd_launch_plan(s, a, nullptr, stream);
+    if (cands.empty()) return ssd_launch_plan(s, a, SsdLaunchOpts{}, stream);
+    auto with = [](const cls::SegChoice* c) {
+        SsdLaunchOpts o{};
+        o.force = c;
+        return o;
+    };
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (hipEventCreate(&e0) != hipSuccess) return SSD_ERR_HIP;
     if (hipEventCreate(&e1) != hipSuccess) {
@@ -445,7 +371,7 @@ extern "C" int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t
     std::vector<cls::SegChoice> plans;
     for (const cls::SegChoice& c : cands) {
         const cls::SsdFusedPlan q = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
-                                                        s.ngroups, s.chunk, s.dtype, &c);
+                                                        s.ngroups, s.chunk, s.dtype, &c, 0);
         const cls::SegChoice ce{q.nsegs, q.nsegs > 1 ? int64_t(q.nchains - q.nwhole) : 0,
                                 q.nsegs > 1 ? int64_t(q.agg_d) : 0};
         bool dup = false;
@@ -458,16 +384,16 @@ extern "C" int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t
     // plan is not favoured by where it falls in the sequence.
     int st = SSD_OK;
     std::vector<float> t_best(plans.size(), -1.0f);
-    for (size_t i = 0; i < plans.size() && st == SSD_OK; ++i) st = ssd_launch_plan(s, a, &plans[i], stream);
+    for (size_t i = 0; i < plans.size() && st == SSD_OK; ++i) st = ssd_launch_plan(s, a, with(&plans[i]), stream);
     for (int round = 0; round < 2 && st == SSD_OK; ++round) {
         for (size_t i = 0; i < plans.size() && st == SSD_OK; ++i) {
-            st = ssd_launch_plan(s, a, &plans[i], stream);
+            st = ssd_launch_plan(s, a, with(&plans[i]), stream);
             if (st != SSD_OK) break;
             if (hipEventRecord(e0, stream) != hipSuccess) {
                 st = SSD_ERR_HIP;
                 break;
             }
-            for (int r = 0; r < reps && st == SSD_OK; ++r) st = ssd_launch_plan(s, a, &plans[i], stream);
+            for (int r = 0; r < reps && st == SSD_OK; ++r) st = ssd_launch_plan(s, a, with(&plans[i]), stream);
             if (st != SSD_OK) break;
             float t = 0.0f;
             if (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
@@ -498,7 +424,7 @@ extern "C" int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t
     *nsplit = best.nsplit;
     *agg_pieces = best.agg_d;
     *ms = best_ms;
-    return ssd_launch_plan(s, a, &best, stream);
+    return ssd_launch_plan(s, a, with(&best), stream);
 }
 
 extern "C" int cls_ssd_plan_query(const SsdShape& s, int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces) {
@@ -516,7 +442,7 @@ extern "C" int cls_ssd_plan_query(const SsdShape& s, int64_t* nsegs, int64_t* ns
     cls::SegChoice t{};
     const bool tuned = cls::tuned_choice(cls::tune_key(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
                                                        s.ngroups, s.chunk, s.dtype), &t);
-    return tuned && cls::g_segments_override == 0 ? 1 : 0;
+    return tuned ? 1 : 0;
 }
 
 extern "C" void cls_ssd_autotune_reset() {

@@ -13,6 +13,7 @@
 // order with the state in LDS; it is correct for any head dim / state size
 // whose state fits in LDS, and is not the throughput path.
 #include "common.hpp"
+#include "device_once.hpp"
 #include "ssd_kernels.hpp"
 
 namespace cls {
@@ -147,13 +148,14 @@ size_t ssd_f32_lds_bytes(int P, int S) {
 
 int ssd_f32_launch(const SsdF32Params& prm, hipStream_t stream) {
     const size_t lds = ssd_f32_lds_bytes(prm.P, prm.S);
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_f32_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-            return -7;
-        attr_set = true;
-    }
+    static DeviceOnce attrs;
+    if (run_once_per_device(attrs, [] {
+            return hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_f32_kernel),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess
+                       ? 0
+                       : -7;
+        }) != 0)
+        return -7;
     const dim3 grid{uint32_t(prm.batch * prm.H), 1u, 1u};
     const dim3 block{uint32_t(kF32Threads), 1u, 1u};
     hipLaunchKernelGGL(ssd_f32_kernel, grid, block, lds, stream, prm);

@@ -1,5 +1,6 @@
 // Launchers of the fused head-dim-64 SSD kernel (see ssd_fused.hpp) and of
 // the CB pass that precedes it.
+#include "device_once.hpp"
 #include "ssd_bf16.hpp"
 #include "ssd_fused.hpp"
 
@@ -187,17 +188,18 @@ static int launch_fused_tpl(const SsdBf16Params& cbp, const SsdFusedParams& fp, 
                             hipEvent_t* ev) {
     using Lay = FuLayout<TT, S>;
     using LayA = FuLayout<TT, S, true>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_cbt_kernel<TT, S>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, CbtLayout<TT, S>::BYTES) != hipSuccess ||
-            hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_kernel<TT, S>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, Lay::BYTES) != hipSuccess ||
-            hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_agg_kernel<TT, S>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, LayA::BYTES) != hipSuccess)
-            return -7;
-        attr_set = true;
-    }
+    static DeviceOnce attrs;
+    const int ast = run_once_per_device(attrs, [] {
+        return (hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_cbt_kernel<TT, S>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, CbtLayout<TT, S>::BYTES) != hipSuccess ||
+                hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_kernel<TT, S>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, Lay::BYTES) != hipSuccess ||
+                hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_agg_kernel<TT, S>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, LayA::BYTES) != hipSuccess)
+                   ? -7
+                   : 0;
+    });
+    if (ast != 0) return ast;
     const int nst = fp.nsegs * (fp.nchains - fp.nwhole);              // segments
     const int npieces = (fp.nchains - fp.nwhole) * (fp.nsegs - 1) * fp.agg_d;  // aggregate pieces
     const dim3 gcb{uint32_t(cbp.batch * cbp.nchunks * (cbp.G + 1)), 1u, 1u};  // + the dt workgroups

@@ -1,0 +1,87 @@
+/*
+ * chunked_linear_scan — entry point for tests and measurement.
+ *
+ * ssd_fwd chooses its kernels and, on the fused head-dim-64 bf16 path, its
+ * segment plan by itself (a tuned plan from ssd_fwd_autotune, else a built-in
+ * heuristic).  ssd_fwd_planned is ssd_fwd with that choice made explicitly by
+ * the caller, per call: parity tests use it to force every plan shape (whole
+ * chains, split chains, one-chunk segments, the per-(batch, head) kernel, each
+ * inter-chunk state scheme), and the benchmark uses it to time the launches of
+ * one call separately.  Nothing it sets outlives the call: the library keeps
+ * no override state between calls.
+ */
+#ifndef CHUNKED_LINEAR_SCAN_TESTING_H
+#define CHUNKED_LINEAR_SCAN_TESTING_H
+
+#include <stdint.h>
+
+#include "chunked_linear_scan.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Kernel choice of one call. */
+enum {
+    SSD_PATH_AUTO = 0,   /* what ssd_fwd would run                                 */
+    SSD_PATH_CHUNK = 1,  /* the per-(batch, head) chunk kernel (any bf16 shape)    */
+    SSD_PATH_FUSED = 2   /* the fused head-dim-64 kernels (falls back to AUTO where
+                            they do not apply)                                     */
+};
+
+/* How a split chain's segments get the state at their start (fused path;
+ * "Selective-scan CUDA kernels", section "The five kernels", levels 2 and 3). */
+enum {
+    SSD_S3_AUTO = 0,      /* the library's choice                                  */
+    SSD_S3_REDUCE = 1,    /* reduce-then-fold: an aggregate launch computes every
+                             piece's (decay, state), the output launch folds them  */
+    SSD_S3_LOOKBACK = 2   /* single pass: segments claimed from a counter publish
+                             their aggregate and look back over their predecessors */
+};
+
+typedef struct {
+    int32_t path;        /* SSD_PATH_*                                               */
+    int32_t s3;          /* SSD_S3_*                                                 */
+    int64_t nsegs;       /* segments per split chain, 1..64; 0: tuned or heuristic   */
+    int64_t nsplit;      /* with nsegs: split only the last nsplit (batch, head)
+                            chains, the others run whole; 0: split every chain      */
+    int64_t agg_pieces;  /* with nsegs and SSD_S3_REDUCE: aggregate pieces per
+                            segment; 0: the heuristic's count                      */
+    int32_t xcds;        /* XCDs the workgroups are dealt across (chain mapping
+                            only); 0: the device's 8; 1: plain index order          */
+    int32_t reserved;    /* must be 0                                                */
+} ssd_plan_request;
+
+/*
+ * ssd_fwd with an explicit plan.  All of ssd_fwd's arguments, layouts,
+ * checks, workspace rules and status codes apply.  `plan` may be NULL (then
+ * this is ssd_fwd).  Fields outside their ranges return SSD_ERR_SHAPE before
+ * anything is launched.  A forced segment plan may need more workspace than
+ * ssd_fwd_workspace_size reports (which covers the plans ssd_fwd itself may
+ * run): size it with ssd_fwd_planned_workspace_size; a smaller workspace
+ * returns SSD_ERR_WORKSPACE.
+ *
+ * events: NULL, or four hipEvent_t handles (created by the caller, owned by
+ * the caller) that are recorded on `stream`: before the call's first launch,
+ * after the CB pass, after the aggregate launch (recorded also when there is
+ * none) and after the output launch.  On paths with a single launch events
+ * 1 and 2 are recorded right after event 0.
+ */
+int ssd_fwd_planned(const void* x, const float* dt, const float* A, const void* B,
+                    const void* C, const float* D, const float* h0,
+                    int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
+                    int64_t dstate, int64_t ngroups, int64_t chunk, int dtype,
+                    void* y, float* h_final, void* workspace, size_t workspace_bytes,
+                    void* stream, const ssd_plan_request* plan, void* const* events);
+
+/* Workspace bytes ssd_fwd_planned needs for this shape and plan (at least
+ * ssd_fwd_workspace_size); 0 for an invalid shape or plan. */
+size_t ssd_fwd_planned_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads,
+                                      int64_t headdim, int64_t dstate, int64_t ngroups,
+                                      int64_t chunk, int dtype, const ssd_plan_request* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CHUNKED_LINEAR_SCAN_TESTING_H */

@@ -37,3 +37,18 @@ def combine(first, second):
     a1, b1 = first
     a2, b2 = second
     return (a1 * a2, a2 * b1 + b2)
+
+
+def scan_error_scale(a, b):
+    """Scale of the rounding error of an evaluation of the scan, per element.
+
+    With h_abs = scan(|a|, |b|) (the sum of the absolute values of the terms
+    of h[t]), one rounding of relative size u per combine adds at most about
+    u * h_abs[t] at step t, and that error is carried forward by the later a's
+    like any other term.  The accumulated error at t is therefore bounded by a
+    small multiple of u * scan(|a|, h_abs)[t], which this returns (divided by
+    u).  Parity bounds are stated against it.
+    """
+    aa = np.abs(np.asarray(a, dtype=np.float64))
+    h_abs = scan_loop(aa, np.abs(np.asarray(b, dtype=np.float64)))
+    return scan_loop(aa, h_abs)

@@ -151,3 +151,23 @@ def ssd_step(h, x, dt, A, B, C, D=None):
     if D is not None:
         y = y + D[None, :, None] * x
     return y, h_new
+
+
+def ssd_abs_terms(x, dt, A, B, C, D=None, h0=None):
+    """Sum of the absolute values of the terms that form each output.
+
+    Every y_t and h_t of ``ssd_loop`` is a sum of products of inputs with
+    positive decay weights exp(sum a_k) (dt >= 0): h_t = sum_j w_tj dt_j B_j
+    x_j^T + w_t0 h0 and y_t = c_t^T h_t + D x_t.  Replacing x, B, C, D and h0
+    by their absolute values turns every term into its absolute value, so the
+    same loop returns (y_abs, h_abs) with y_abs = sum |term| >= |y|.  A
+    rounding error of relative size u in each term's factors is therefore
+    bounded, element by element, by a small multiple of u * y_abs: this is
+    the scale the element-wise parity bounds are stated against.  Requires
+    dt >= 0.
+    """
+    dt = _f64(dt)
+    if np.any(dt < 0):
+        raise ValueError("ssd_abs_terms needs dt >= 0 (positive decay weights)")
+    ab = lambda v: None if v is None else np.abs(_f64(v))
+    return ssd_loop(ab(x), dt, A, ab(B), ab(C), ab(D), ab(h0))

@@ -196,3 +196,75 @@ def test_linear_scan_typed_rejects_bad_arguments():
     assert call(L=-1) == -2
     assert call(h=ctypes.c_void_p(0x10008)) == -5
     assert call(ws_bytes=0) == -6
+
+
+TESTING_HEADER = os.path.join(ROOT, "include", "chunked_linear_scan_testing.h")
+
+
+def test_testing_header_entry_points_are_exported():
+    text = re.sub(r"/\*.*?\*/", "", open(TESTING_HEADER).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "sizeof", "defined"})
+    assert names == ["ssd_fwd_planned", "ssd_fwd_planned_workspace_size"]
+    lib = ctypes.CDLL(cls.LIB_PATH)
+    for name in names:
+        assert hasattr(lib, name), name
+
+
+def test_no_process_wide_override_hooks():
+    """Plans are passed per call (ssd_fwd_planned): the library exports no
+    setter that would change what every later call does."""
+    lib = ctypes.CDLL(cls.LIB_PATH)
+    for name in ("cls_ssd_set_segments", "cls_ssd_set_split", "cls_ssd_set_agg_pieces", "cls_ssd_set_xcds",
+                 "cls_ssd_force_path", "cls_ssd_profile", "cls_ssd_profile_read"):
+        assert not hasattr(lib, name), name
+
+
+def test_planned_call_validates_the_plan_on_host():
+    lib = cls.load_library()
+    shape = (1, 65536, 8, 64, 128, 1, 128, cls.SSD_BF16)
+
+    def call(plan, events=None, ws_bytes=1 << 34):
+        return lib.ssd_fwd_planned(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, *shape, FAKE, None, FAKE, ws_bytes,
+                                   None, ctypes.byref(plan) if plan is not None else None, events)
+
+    for bad in (cls.plan_request(nsegs=65), cls.PlanRequest(3, 0, 0, 0, 0, 0, 0), cls.PlanRequest(0, 3, 0, 0, 0, 0, 0),
+                cls.PlanRequest(0, 0, -1, 0, 0, 0, 0), cls.PlanRequest(0, 0, 2, -1, 0, 0, 0),
+                cls.PlanRequest(0, 0, 0, 0, 0, 65, 0), cls.PlanRequest(0, 0, 0, 0, 0, 0, 7)):
+        assert call(bad) == -2
+        assert lib.ssd_fwd_planned_workspace_size(*shape, ctypes.byref(bad)) == 0
+    # a forced plan's workspace: at least ssd_fwd's, more when it splits finer than the tuner would
+    base = lib.ssd_fwd_workspace_size(*shape)
+    fine = lib.ssd_fwd_planned_workspace_size(*shape, ctypes.byref(cls.plan_request(nsegs=64, agg_pieces=1000)))
+    assert base > 0 and fine > base
+    assert call(cls.plan_request(nsegs=64, agg_pieces=1000), ws_bytes=base) == -6
+    # four events or none
+    ev = (ctypes.c_void_p * 4)(0x10, 0x20, None, 0x40)
+    assert call(cls.plan_request(), events=ev) == -1
+
+
+def test_workspace_cache_is_keyed_by_device_and_stream():
+    """Two streams of one device get two workspaces (calls sharing one must be
+    stream-ordered); growing one stream's buffer leaves the other's alone."""
+    import torch
+    made = []
+
+    def alloc(device, size):
+        made.append((device, size))
+        return torch.zeros(size, dtype=torch.uint8)
+
+    c = cls._Workspace(alloc)
+    a1 = c.get("cuda:0", 111, 5000)
+    assert c.get("cuda:0", 111, 100) is a1          # same stream, fits: reused
+    b1 = c.get("cuda:0", 222, 5000)
+    assert b1 is not a1                              # another stream: its own buffer
+    d1 = c.get("cuda:1", 111, 5000)
+    assert d1 is not a1                              # another device: its own buffer
+    a2 = c.get("cuda:0", 111, 9000)
+    assert a2 is not a1 and a2.numel() == 9000       # grows
+    assert c.get("cuda:0", 222, 10) is b1            # the other stream's buffer is untouched
+    assert len(made) == 4
+    # the error-word reader sums and clears the words of the given buffers
+    a2[:4].view(torch.int32).fill_(3)
+    b1[:4].view(torch.int32).fill_(2)
+    assert cls.workspace_errors([a2, b1]) == 5
+    assert cls.workspace_errors([a2, b1]) == 0

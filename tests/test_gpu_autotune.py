@@ -15,6 +15,7 @@ import torch
 
 import chunked_linear_scan_amd as cls
 from oracle import compare, ssd as ossd
+import parity
 
 pytestmark = pytest.mark.gpu
 
@@ -34,17 +35,6 @@ def case(seed, Bt, L, H, P, S, G, dtype):
     return dict(x=x, dt=dt, A=A, B=B, C=C, D=D, h0=h0)
 
 
-def oracle(c):
-    np64 = lambda t: t.to(torch.float64).numpy()
-    return ossd.ssd_loop(*(np64(c[k]) for k in ("x", "dt", "A", "B", "C", "D", "h0")))
-
-
-def check(label, got, ref, tol):
-    err = compare.rel_l2(got, ref)
-    print(f"  {label}: rel-L2 {err:.3e}", flush=True)
-    assert err <= tol, (label, err, compare.first_mismatch(got, ref, rtol=50 * tol, atol=50 * tol))
-
-
 @pytest.mark.parametrize("Bt,L,H,G,chunk", [(2, 2048, 24, 2, 128), (1, 1000, 12, 3, 64), (3, 4096, 8, 1, 256)])
 def test_autotune_result_plan_and_later_calls(Bt, L, H, G, chunk):
     P, S = 64, 128
@@ -62,9 +52,7 @@ def test_autotune_result_plan_and_later_calls(Bt, L, H, G, chunk):
     assert 1 <= info["nsegs"] <= 32 and info["ms_per_call"] > 0
     assert (info["nsegs"] == 1) == (info["nsplit"] == 0) and 0 <= info["nsplit"] <= nchains
     assert (info["nsegs"] == 1) == (info["agg_pieces"] == 0) and info["agg_pieces"] >= 0
-    ry, rh = oracle(c)
-    check("tuned y", y.float().cpu().numpy(), ry, TOL_BF16)
-    check("tuned h_final", hf.cpu().numpy(), rh, TOL_BF16)
+    parity.check_ssd(c, y.float().cpu().numpy(), hf.cpu().numpy(), chunk, "tuned")
     after = cls.ssd_fwd_plan(Bt, L, H, P, S, G, chunk)
     assert after == {"nsegs": info["nsegs"], "nsplit": info["nsplit"], "agg_pieces": info["agg_pieces"],
                      "source": "tuned"}
@@ -91,9 +79,8 @@ def test_autotune_workspace_sized_before_tuning_suffices():
                                        reps=1, workspace=ws)
     y2, hf2 = cls.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=chunk, workspace=ws)
     torch.cuda.synchronize()
-    ry, rh = oracle(c)
-    check("y", y2.float().cpu().numpy(), ry, TOL_BF16)
-    check("h_final", hf2.cpu().numpy(), rh, TOL_BF16)
+    parity.check_ssd(c, y2.float().cpu().numpy(), hf2.cpu().numpy(), chunk, "after tuning")
+    assert cls.workspace_errors([ws]) == 0
     cls.ssd_fwd_autotune_reset()
 
 
@@ -107,6 +94,4 @@ def test_autotune_without_a_plan_runs_one_plain_pass():
         torch.cuda.synchronize()
         assert info["nsegs"] == 0 and info["nsplit"] == 0 and info["agg_pieces"] == 0
         assert cls.ssd_fwd_plan(1, 300, 4, P, S, 2, 64, dtype)["source"] == "none"
-        ry, rh = oracle(c)
-        check(f"{dtype} y", y.float().cpu().numpy(), ry, tol)
-        check(f"{dtype} h_final", hf.cpu().numpy(), rh, tol)
+        parity.check_ssd(c, y.float().cpu().numpy(), hf.cpu().numpy(), 64, f"{dtype}")

@@ -9,6 +9,7 @@ import torch
 import chunked_linear_scan_amd as cls
 from chunked_linear_scan_amd import workloads
 from oracle import compare, scan as oscan
+import parity
 
 pytestmark = pytest.mark.gpu
 
@@ -22,17 +23,13 @@ def inputs(seed, rows, L):
     return a, b
 
 
-def check(a, b, label):
+def check(a, b, label, elementwise=True):
     print(f"[scan3] {label} rows={a.shape[0]} L={a.shape[1]}", flush=True)
     got = cls.linear_scan_three_pass(a.cuda(), b.cuda())
     one = cls.linear_scan(a.cuda(), b.cuda())
     torch.cuda.synchronize()
     got, one = got.cpu().numpy(), one.cpu().numpy()
-    ref = oscan.scan_loop(a.numpy(), b.numpy())
-    err = compare.rel_l2(got, ref)
-    row_err = max(compare.rel_l2(got[r], ref[r]) for r in range(a.shape[0]))
-    assert err <= TOL, (label, err, compare.first_mismatch(got, ref, rtol=1e-4, atol=1e-5))
-    assert row_err <= 10 * TOL, (label, row_err)
+    parity.check_scan(a, b, got, label=label, elementwise=elementwise)
     assert compare.rel_l2(got, one) <= 2 * TOL, label  # the two GPU paths agree
 
 
@@ -40,7 +37,7 @@ def check(a, b, label):
                                     (3, 24581), (7, 40000), (1, 1 << 20)])
 def test_edge_lengths(rows, L):
     a, b = inputs(rows * 1000 + L % 997, rows, L)
-    check(a, b, f"edge {rows}x{L}")
+    check(a, b, f"edge {rows}x{L}", elementwise=L < (1 << 20))
 
 
 @pytest.mark.parametrize("name", ["scan", "scan_ragged"])
@@ -59,9 +56,9 @@ def test_decay_one_is_cumsum_and_zero_is_identity():
     assert np.array_equal(got0, b.numpy())
 
 
-def test_deterministic():
+def test_deterministic_100_runs():
     a, b = inputs(9, 16, 70000)
     da, db = a.cuda(), b.cuda()
-    h0 = cls.linear_scan_three_pass(da, db).cpu().numpy()
-    for _ in range(3):
-        assert np.array_equal(cls.linear_scan_three_pass(da, db).cpu().numpy(), h0)
+    h0 = cls.linear_scan_three_pass(da, db)
+    for i in range(100):
+        assert torch.equal(cls.linear_scan_three_pass(da, db), h0), i

@@ -1,14 +1,16 @@
 """GPU parity tests for ssd_fwd (HIP path through the C ABI) against the
 float64 oracle.
 
-Tolerances: rel-L2 <= 1e-5 for fp32 inputs and <= 2e-2 for bf16 inputs (fp32
-state), for y and for the final state.  Small shapes are compared element by
-element in full; the full-size workloads are compared on sampled
-(batch, head) sequences, which the oracle runs exactly (a head's outputs
-depend only on its own inputs and its group's B/C).
+Every test compares whole outputs (tests/parity.py): the global rel-L2
+against the method's tolerance (1e-5 for fp32 inputs, 2e-2 for bf16 inputs
+with fp32 state) for y and for the final state, the rel-L2 of every
+chunk-long band of the sequence, and an element-wise bound derived from the
+roundings of each path.  The full-size workloads are compared whole too, with
+the oracle spread over a process pool.  Forced plans go through
+ssd_fwd_planned (include/chunked_linear_scan_testing.h), which takes the plan
+per call.
 """
 import math
-import sys
 
 import numpy as np
 import pytest
@@ -16,57 +18,26 @@ import torch
 
 import chunked_linear_scan_amd as cls
 from chunked_linear_scan_amd import workloads
-from oracle import compare, ssd as ossd
+from oracle import compare
+import parity
 
 pytestmark = pytest.mark.gpu
 
-TOL_F32 = 1e-5
-TOL_BF16 = 2e-2
-
 
 def to_dev(inp):
-    out = {}
-    for k, v in inp.items():
-        out[k] = v.cuda() if isinstance(v, torch.Tensor) else v
-    return out
+    return {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
 
 
-def gpu_run(inp, chunk=None, want_final=True):
+def gpu_run(inp, chunk=None, want_final=True, plan=None, workspace=None):
     d = to_dev(inp)
-    y, hf = cls.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d.get("D"), d.get("h0"),
-                        chunk=chunk or inp["chunk"], want_final_state=want_final)
+    args = (d["x"], d["dt"], d["A"], d["B"], d["C"], d.get("D"), d.get("h0"))
+    if plan is None:
+        y, hf = cls.ssd_fwd(*args, chunk=chunk or inp["chunk"], want_final_state=want_final, workspace=workspace)
+    else:
+        y, hf = cls.ssd_fwd_planned(*args, chunk=chunk or inp["chunk"], plan=plan, want_final_state=want_final,
+                                    workspace=workspace)
     torch.cuda.synchronize()
     return y.float().cpu().numpy(), (None if hf is None else hf.cpu().numpy())
-
-
-def np64(t):
-    return None if t is None else t.to(torch.float64).numpy()
-
-
-def oracle_run(inp, batches=None, heads=None):
-    """Oracle on a subset of (batch, head); each chosen head gets its own group."""
-    x, dt, A, B, C, D, h0 = (inp[k] for k in ("x", "dt", "A", "B", "C", "D", "h0"))
-    H, G = x.shape[2], B.shape[2]
-    bsel = list(range(x.shape[0])) if batches is None else list(batches)
-    hsel = list(range(H)) if heads is None else list(heads)
-    if heads is None:
-        sub = dict(x=x[bsel], dt=dt[bsel], A=A, B=B[bsel], C=C[bsel], D=D,
-                   h0=None if h0 is None else h0[bsel])
-    else:
-        grp = [h // (H // G) for h in hsel]
-        sub = dict(x=x[bsel][:, :, hsel], dt=dt[bsel][:, :, hsel], A=A[hsel],
-                   B=B[bsel][:, :, grp], C=C[bsel][:, :, grp], D=None if D is None else D[hsel],
-                   h0=None if h0 is None else h0[bsel][:, hsel])
-    y, hf = ossd.ssd_loop(*(np64(sub[k]) for k in ("x", "dt", "A", "B", "C", "D", "h0")))
-    return y, hf, bsel, hsel
-
-
-def assert_close(got, ref, tol, label):
-    err = compare.rel_l2(got, ref)
-    mm = compare.first_mismatch(got, ref, rtol=50 * tol, atol=50 * tol)
-    print(f"  {label}: rel-L2 {err:.3e}", flush=True)
-    assert err <= tol, (label, err, mm)
-    return err
 
 
 def small_case(seed, Bt, L, H, P, S, G, dtype, h0=True, D=True, dt_shift=-2.0):
@@ -81,92 +52,110 @@ def small_case(seed, Bt, L, H, P, S, G, dtype, h0=True, D=True, dt_shift=-2.0):
     return {"x": x, "dt": dt, "A": A, "B": B, "C": C, "D": Dv, "h0": hv, "chunk": 32}
 
 
+def run_and_check(inp, chunk, label, plan=None, want_final=True):
+    print(f"[ssd] {label}", flush=True)
+    y, hf = gpu_run(inp, chunk=chunk, plan=plan, want_final=want_final)
+    parity.check_ssd(inp, y, hf, chunk, label)
+    return y, hf
+
+
 def test_tiny_fp32_workload():
     inp = workloads.ssd_workload("ssd_tiny")
-    print("[ssd] ssd_tiny fp32", flush=True)
-    y, hf = gpu_run(inp)
-    ry, rh, _, _ = oracle_run(inp)
-    assert_close(y, ry, TOL_F32, "y")
-    assert_close(hf, rh, TOL_F32, "h_final")
+    run_and_check(inp, inp["chunk"], "ssd_tiny fp32")
 
 
 @pytest.mark.parametrize("chunk", [16, 32, 64, 128, 256])
 def test_fp32_chunk_sizes_and_ragged(chunk):
     inp = small_case(1, 2, 300, 4, 16, 16, 2, torch.float32)
-    print(f"[ssd] fp32 chunk={chunk}", flush=True)
-    y, hf = gpu_run(inp, chunk=chunk)
-    ry, rh, _, _ = oracle_run(inp)
-    assert_close(y, ry, TOL_F32, "y")
-    assert_close(hf, rh, TOL_F32, "h_final")
+    run_and_check(inp, chunk, f"fp32 chunk={chunk}")
 
 
 @pytest.mark.parametrize("chunk", [16, 32, 64, 128, 256])
-@pytest.mark.parametrize("P,S", [(16, 32), (64, 128), (32, 64), (128, 64)])
+@pytest.mark.parametrize("P,S", [(16, 32), (64, 128), (32, 64), (128, 64), (64, 64)])
 def test_bf16_shapes_chunks_ragged(P, S, chunk):
     if not cls.load_library().ssd_fwd_workspace_size(2, 301, 4, P, S, 2, chunk, cls.SSD_BF16):
         pytest.skip("shape not supported by the bf16 kernels at this chunk")
     inp = small_case(2, 2, 301, 4, P, S, 2, torch.bfloat16)
-    print(f"[ssd] bf16 P={P} S={S} chunk={chunk}", flush=True)
-    y, hf = gpu_run(inp, chunk=chunk)
-    ry, rh, _, _ = oracle_run(inp)
-    e = assert_close(y, ry, TOL_BF16, "y")
-    assert_close(hf, rh, TOL_BF16, "h_final")
-    assert e < 1e-2  # bf16 operand rounding alone stays well under the bound
-    head, tail = compare.band_report(y, ry, chunk, axis=1)
-    assert head <= TOL_BF16 and tail <= TOL_BF16
+    y, _ = run_and_check(inp, chunk, f"bf16 P={P} S={S} chunk={chunk}")
+
+
+@pytest.mark.parametrize("chunk", [32, 128, 256])
+def test_bf16_chunk_kernel_on_fused_shapes(chunk):
+    """The per-(batch, head) chunk kernel forced on a head-dim-64 shape that
+    the fused kernels would otherwise take."""
+    inp = small_case(12 + chunk, 2, 700, 4, 64, 128, 2, torch.bfloat16)
+    run_and_check(inp, chunk, f"chunk kernel forced, chunk={chunk}", plan=cls.plan_request(path="chunk"))
 
 
 def test_bf16_edge_lengths():
-    for L in (1, 2, 31, 32, 33, 255, 257):
+    for L in (1, 2, 31, 32, 33, 127, 128, 129, 255, 257):
         inp = small_case(3 + L, 1, L, 2, 64, 128, 1, torch.bfloat16)
-        print(f"[ssd] bf16 L={L}", flush=True)
-        y, hf = gpu_run(inp, chunk=256)
-        ry, rh, _, _ = oracle_run(inp)
-        assert_close(y, ry, TOL_BF16, f"y L={L}")
-        assert_close(hf, rh, TOL_BF16, f"h L={L}")
+        run_and_check(inp, 256, f"bf16 L={L}")
 
 
 @pytest.mark.parametrize("chunk", [32, 64, 128, 256])
 def test_whole_chains_many_chunks(chunk):
-    """Every (batch, head) chain in one workgroup (segments forced to 1), so a
+    """Every (batch, head) chain in one workgroup (one segment), so a
     workgroup walks tens of (sub-)chunks: the loaders' register sets, the
     double-buffered LDS halves and the staged outputs all rotate many times,
     with a ragged last chunk."""
-    ct = __import__("ctypes")
-    lib = cls.load_library()
-    lib.cls_ssd_set_segments.argtypes = [ct.c_int]
-    print(f"[ssd] whole chains, chunk={chunk}", flush=True)
     inp = small_case(90 + chunk, 1, 64 * 40 + 17, 2, 64, 128, 1, torch.bfloat16, dt_shift=-3.0)
-    lib.cls_ssd_set_segments(1)
-    try:
-        y, hf = gpu_run(inp, chunk=chunk)
-    finally:
-        lib.cls_ssd_set_segments(0)
-    ry, rh, _, _ = oracle_run(inp)
-    assert_close(y, ry, TOL_BF16, f"y chunk={chunk}")
-    assert_close(hf, rh, TOL_BF16, f"h chunk={chunk}")
+    run_and_check(inp, chunk, f"whole chains, chunk={chunk}", plan=cls.plan_request(nsegs=1))
 
 
 def test_optional_arguments():
     inp = small_case(4, 1, 200, 2, 64, 128, 1, torch.bfloat16, h0=False, D=False)
     y, hf = gpu_run(inp, chunk=64, want_final=False)
     assert hf is None
-    ry, _, _, _ = oracle_run(inp)
-    assert_close(y, ry, TOL_BF16, "y (no D, no h0)")
+    parity.check_ssd(inp, y, None, 64, "no D, no h0, no final state")
 
 
 def test_decay_free_and_zero_timestep():
     inp = small_case(5, 1, 160, 2, 64, 128, 1, torch.bfloat16)
     inp["A"] = torch.zeros_like(inp["A"])  # linear attention
-    y, hf = gpu_run(inp, chunk=64)
-    ry, rh, _, _ = oracle_run(inp)
-    assert_close(y, ry, TOL_BF16, "y a=0")
+    run_and_check(inp, 64, "a = 0")
     inp = small_case(6, 1, 160, 2, 64, 128, 1, torch.bfloat16)
-    inp["dt"] = torch.zeros_like(inp["dt"])  # state stays h0
-    y, hf = gpu_run(inp, chunk=64)
+    inp["dt"] = torch.zeros_like(inp["dt"])  # the state stays h0
+    y, hf = run_and_check(inp, 64, "dt = 0")
     assert np.abs(hf - inp["h0"].numpy()).max() == 0.0
-    ry, _, _, _ = oracle_run(inp)
-    assert_close(y, ry, TOL_BF16, "y dt=0")
+
+
+def block_decay_case(seed, levels, chunk, L=1000, S=128):
+    """Heads whose 32-token blocks decay by a chosen total: with A = -8 and dt
+    constant inside a block, the block's log2 decay is 32 * A * log2(e) * dt.
+    ``levels[h]`` lists the log2 decays of head h's blocks, cycled along the
+    sequence."""
+    H = len(levels)
+    inp = small_case(seed, 2, L, H, 64, S, 1, torch.bfloat16)
+    A = -8.0
+    inp["A"] = torch.full((H,), A)
+    dt = torch.empty(2, L, H)
+    for h, lv in enumerate(levels):
+        for t0 in range(0, L, 32):
+            ge = lv[(t0 // 32) % len(lv)]
+            dt[:, t0:t0 + 32, h] = ge / (32.0 * A * math.log2(math.e))
+    inp["dt"] = dt
+    inp["chunk"] = chunk
+    return inp
+
+
+@pytest.mark.parametrize("chunk", [32, 64, 128])
+def test_diagonal_weights_both_sides_of_the_strong_decay_threshold(chunk):
+    """The diagonal-block weights CB dt exp2(GL_i - GL_j) are formed from
+    bounded per-token factors when a 32-token block decays by at most 2^100,
+    and element by element when it decays more (the factors would overflow).
+    Heads sit just above the threshold, just below it, far on each side, and
+    alternate between the two forms from block to block."""
+    levels = [[-99.99], [-100.01], [-60.0], [-150.0], [-99.99, -100.01], [-150.0, -5.0, -100.01, -0.5]]
+    inp = block_decay_case(40 + chunk, levels, chunk)
+    run_and_check(inp, chunk, f"block decays around 2^-100, chunk={chunk}")
+
+
+def test_decay_underflow_to_zero():
+    """Blocks whose decay underflows fp32 entirely (2^-400): the state resets
+    and only the tokens' own block contributes."""
+    inp = block_decay_case(47, [[-400.0], [-400.0, -1.0], [-1.0]], 128)
+    run_and_check(inp, 128, "block decays of 2^-400")
 
 
 def test_chained_calls_carry_state():
@@ -183,6 +172,7 @@ def test_chained_calls_carry_state():
     # the chunk boundaries coincide, so the split run performs the same arithmetic
     assert torch.equal(torch.cat([y1, y2], dim=1), y_full)
     assert torch.equal(h2, h_full)
+    parity.check_ssd(inp, y_full.float().cpu().numpy(), h_full.cpu().numpy(), 128, "chained")
 
 
 def test_one_state_one_channel_matches_linear_scan():
@@ -207,78 +197,53 @@ def test_one_state_one_channel_matches_linear_scan():
     assert compare.rel_l2(ys, h) < 1e-5
 
 
-def test_deterministic():
+@pytest.mark.parametrize("plan", [None, {"nsegs": 4, "nsplit": 5}], ids=["default", "split"])
+def test_deterministic_100_runs(plan):
+    """100 reruns are bit-identical, with whole chains and with split chains
+    (the aggregate launch and the fold at each segment start)."""
     inp = small_case(9, 2, 1024, 8, 64, 128, 2, torch.bfloat16)
     d = to_dev(inp)
-    y0, h0 = cls.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=256)
-    for _ in range(20):
-        y1, h1 = cls.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=256)
-        assert torch.equal(y0, y1) and torch.equal(h0, h1)
+    args = (d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"])
+    pr = cls.plan_request(**plan) if plan else None
+    run = (lambda: cls.ssd_fwd(*args, chunk=256)) if pr is None else \
+        (lambda: cls.ssd_fwd_planned(*args, chunk=256, plan=pr))
+    y0, h0 = run()
+    for i in range(100):
+        y1, h1 = run()
+        assert torch.equal(y0.view(torch.int16), y1.view(torch.int16)), i
+        assert torch.equal(h0.view(torch.int32), h1.view(torch.int32)), i
+    torch.cuda.synchronize()
+    parity.check_ssd(inp, y0.float().cpu().numpy(), h0.cpu().numpy(), 256, "determinism")
 
 
-FULL = [("ssd_small", [0, 7], [0, 13, 23]), ("ssd_large", [0, 3], [0, 41, 79]),
-        ("ssd_long", [0], [0, 9, 18, 63])]
-
-
-@pytest.mark.parametrize("name,bsel,hsel", FULL)
-def test_full_workloads_sampled(name, bsel, hsel):
-    print(f"[ssd] {name} full size, sampled b={bsel} h={hsel}", flush=True)
+@pytest.mark.parametrize("name", ["ssd_small", "ssd_large", "ssd_long"])
+def test_full_workloads_whole(name):
+    """The full-size workloads as ssd_fwd runs them by default, every output
+    compared (the oracle runs over all (batch, head) sequences in a pool)."""
+    print(f"[ssd] {name} full size, whole outputs", flush=True)
     inp = workloads.ssd_workload(name)
     y, hf = gpu_run(inp)
-    ry, rh, _, _ = oracle_run(inp, batches=bsel, heads=hsel)
-    gy = y[bsel][:, :, hsel]
-    gh = hf[bsel][:, hsel]
-    assert_close(gy, ry, TOL_BF16, f"{name} y")
-    assert_close(gh, rh, TOL_BF16, f"{name} h_final")
-    # every sampled sequence on its own, and its last chunk
-    for bi in range(len(bsel)):
-        for hi in range(len(hsel)):
-            assert compare.rel_l2(gy[bi, :, hi], ry[bi, :, hi]) <= TOL_BF16
-            T = inp["chunk"]
-            assert compare.rel_l2(gy[bi, -T:, hi], ry[bi, -T:, hi]) <= TOL_BF16
     assert np.isfinite(y).all()
+    parity.check_ssd_workload(name, y, hf)
 
 
 @pytest.mark.parametrize("nsegs", [1, 2, 3, 7, 64])
-def test_segment_lookback_forced(nsegs):
-    """The fused path splits each sequence into segments whose start states
-    come from the aggregate launch's pieces, folded in order; force the segment
-    count so the fold runs with one-chunk segments, uneven segments and many
-    segments."""
-    lib = cls.load_library()
-    lib.cls_ssd_set_segments.argtypes = [__import__("ctypes").c_int]
+def test_segments_forced(nsegs):
+    """Every sequence split into segments whose start states come from the
+    aggregate launch's pieces, folded in order: one-chunk segments, uneven
+    segments and many segments."""
     inp = small_case(20 + nsegs, 2, 64 * 40 + 17, 3, 64, 128, 1, torch.bfloat16, dt_shift=-4.0)
-    lib.cls_ssd_set_segments(nsegs)
-    try:
-        y, hf = gpu_run(inp, chunk=32)
-    finally:
-        lib.cls_ssd_set_segments(0)
-    ry, rh, _, _ = oracle_run(inp)
-    assert_close(y, ry, TOL_BF16, f"y nsegs={nsegs}")
-    assert_close(hf, rh, TOL_BF16, f"h nsegs={nsegs}")
+    run_and_check(inp, 32, f"nsegs={nsegs}", plan=cls.plan_request(nsegs=nsegs))
 
 
 @pytest.mark.parametrize("nsegs,nsplit,chunk", [(2, 1, 128), (5, 4, 128), (4, 5, 32), (3, 2, 64)])
 def test_segment_mixed_whole_and_split(nsegs, nsplit, chunk):
     """Plans that run some (batch, head) chains whole and split the last
     `nsplit` chains into segments (the shape of the plan that fills the CUs
-    left idle by a partial last round): both kinds of tile in one launch."""
-    ct = __import__("ctypes")
-    lib = cls.load_library()
-    lib.cls_ssd_set_segments.argtypes = [ct.c_int]
-    lib.cls_ssd_set_split.argtypes = [ct.c_int]
-    print(f"[ssd] mixed plan nsegs={nsegs} nsplit={nsplit} chunk={chunk}", flush=True)
+    left idle by a partial last round): both kinds of work item in one launch."""
     inp = small_case(60 + nsegs, 2, 64 * 40 + 17, 3, 64, 128, 1, torch.bfloat16, dt_shift=-4.0)
-    lib.cls_ssd_set_segments(nsegs)
-    lib.cls_ssd_set_split(nsplit)
-    try:
-        y, hf = gpu_run(inp, chunk=chunk)
-    finally:
-        lib.cls_ssd_set_segments(0)
-        lib.cls_ssd_set_split(0)
-    ry, rh, _, _ = oracle_run(inp)
-    assert_close(y, ry, TOL_BF16, f"y nsegs={nsegs} nsplit={nsplit}")
-    assert_close(hf, rh, TOL_BF16, f"h nsegs={nsegs} nsplit={nsplit}")
+    run_and_check(inp, chunk, f"mixed nsegs={nsegs} nsplit={nsplit} chunk={chunk}",
+                  plan=cls.plan_request(nsegs=nsegs, nsplit=nsplit))
 
 
 @pytest.mark.parametrize("nsegs,pieces,chunk", [(3, 1, 64), (3, 5, 64), (4, 16, 32), (2, 40, 64), (5, 3, 128)])
@@ -287,19 +252,40 @@ def test_aggregate_pieces_forced(nsegs, pieces, chunk):
     pieces (the autotuner searches this count); the output launch folds them
     in order.  Counts from one piece per segment to one chunk per piece (the
     count is capped at the segment's chunks), uneven last pieces included."""
-    ct = __import__("ctypes")
-    lib = cls.load_library()
-    lib.cls_ssd_set_segments.argtypes = [ct.c_int]
-    lib.cls_ssd_set_agg_pieces.argtypes = [ct.c_int]
-    print(f"[ssd] aggregate pieces nsegs={nsegs} pieces={pieces} chunk={chunk}", flush=True)
     inp = small_case(80 + pieces, 2, 64 * 40 + 17, 3, 64, 128, 1, torch.bfloat16, dt_shift=-4.0)
-    lib.cls_ssd_set_segments(nsegs)
-    lib.cls_ssd_set_agg_pieces(pieces)
-    try:
-        y, hf = gpu_run(inp, chunk=chunk)
-    finally:
-        lib.cls_ssd_set_segments(0)
-        lib.cls_ssd_set_agg_pieces(0)
-    ry, rh, _, _ = oracle_run(inp)
-    assert_close(y, ry, TOL_BF16, f"y nsegs={nsegs} pieces={pieces}")
-    assert_close(hf, rh, TOL_BF16, f"h nsegs={nsegs} pieces={pieces}")
+    run_and_check(inp, chunk, f"nsegs={nsegs} pieces={pieces} chunk={chunk}",
+                  plan=cls.plan_request(nsegs=nsegs, agg_pieces=pieces))
+
+
+@pytest.mark.parametrize("xcds", [1, 3])
+def test_chain_mapping_over_xcds(xcds):
+    """The workgroup-to-chain mapping dealt over other XCD counts (1: plain
+    index order) runs the same chains."""
+    inp = small_case(70 + xcds, 3, 700, 6, 64, 128, 2, torch.bfloat16)
+    run_and_check(inp, 128, f"xcds={xcds}", plan=cls.plan_request(nsegs=3, nsplit=7, xcds=xcds))
+
+
+def test_explicit_workspace_error_word_stays_zero():
+    """A caller-owned workspace, reused over shapes and plans: the error word
+    at its start stays 0 (no bounded wait gave up)."""
+    lib = cls.load_library()
+    shapes = [(2, 1000, 4, 2, 128), (1, 3000, 6, 3, 64), (2, 2000, 8, 1, 256)]
+    need = max(lib.ssd_fwd_planned_workspace_size(b, L, H, 64, 128, G, T, cls.SSD_BF16,
+                                                  cls.plan_request(nsegs=5)) for b, L, H, G, T in shapes)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for i, (b, L, H, G, T) in enumerate(shapes):
+        inp = small_case(200 + i, b, L, H, 64, 128, G, torch.bfloat16)
+        for plan in (None, cls.plan_request(nsegs=5)):
+            y, hf = gpu_run(inp, chunk=T, plan=plan, workspace=ws)
+            parity.check_ssd(inp, y, hf, T, f"shared workspace {i}")
+    assert cls.workspace_errors([ws]) == 0
+
+
+def test_planned_call_rejects_bad_plans():
+    inp = small_case(3, 1, 64, 2, 64, 128, 1, torch.bfloat16)
+    d = to_dev(inp)
+    args = (d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"])
+    for bad in (cls.plan_request(nsegs=65), cls.PlanRequest(3, 0, 0, 0, 0, 0, 0),
+                cls.PlanRequest(0, 3, 0, 0, 0, 0, 0), cls.PlanRequest(0, 0, 0, 0, 0, 0, 1)):
+        with pytest.raises(cls.SSDError):
+            cls.ssd_fwd_planned(*args, chunk=32, plan=bad)

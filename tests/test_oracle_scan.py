@@ -113,3 +113,20 @@ def test_lookback_matrix_payload_carries_chunk_states():
         ref.append(h)
     out = lookback.lookback_scan(elems, scan.combine, None, tile=3, window=4, seed=3, resident=6)
     assert max(np.abs(o[1] - r).max() for o, r in zip(out, ref)) < 1e-12
+
+
+def test_error_scale_hand_values():
+    """a = (0.5, -2, 1), b = (1, -1, 2): h_abs = scan(|a|, |b|) is 1, then
+    2*1 + 1 = 3, then 1*3 + 2 = 5; the scale scan(|a|, h_abs) is 1, then
+    2*1 + 3 = 5, then 1*5 + 5 = 10."""
+    a = np.array([[0.5, -2.0, 1.0]])
+    b = np.array([[1.0, -1.0, 2.0]])
+    np.testing.assert_allclose(scan.scan_error_scale(a, b), [[1.0, 5.0, 10.0]], rtol=1e-15)
+
+
+def test_error_scale_of_cumsum():
+    """a = 1: h_abs is the running sum of |b| and the scale its running sum."""
+    rng = np.random.default_rng(4)
+    b = rng.standard_normal((3, 50))
+    want = np.cumsum(np.cumsum(np.abs(b), axis=1), axis=1)
+    np.testing.assert_allclose(scan.scan_error_scale(np.ones_like(b), b), want, rtol=1e-13)

@@ -218,3 +218,41 @@ def test_step_previous_state_output_differs():
     y, _ = ssd.ssd_step(h0, x[:, 0], dt[:, 0], A, B[:, 0], C[:, 0], D)
     yp, _ = ssd.ssd_loop(x, dt, A, B, C, D, h0, y_uses_previous_state=True)
     assert np.abs(y - yp[:, 0]).max() > 1e-3
+
+
+def test_abs_terms_hand_value():
+    """One token, P = S = 1: y = c (exp(a) h0 + dt b x) + D x.  With a = A dt =
+    -ln 2 * 1 the decay is 1/2; x = -3, B = 2, C = -1, D = 0.5, h0 = -4, dt = 1:
+    the terms of h are (1/2)(-4) = -2 and 1*2*(-3) = -6, so h = -8 and
+    h_abs = 2 + 6 = 8; y = (-1)(-8) + 0.5(-3) = 6.5 and y_abs = 1*8 + 0.5*3 = 9.5."""
+    x = np.array([[[[-3.0]]]])
+    dt = np.array([[[1.0]]])
+    A = np.array([-math.log(2.0)])
+    B = np.array([[[[2.0]]]])
+    C = np.array([[[[-1.0]]]])
+    D = np.array([0.5])
+    h0 = np.array([[[[-4.0]]]])
+    y, h = ssd.ssd_loop(x, dt, A, B, C, D, h0)
+    ya, ha = ssd.ssd_abs_terms(x, dt, A, B, C, D, h0)
+    assert y[0, 0, 0, 0] == pytest.approx(6.5, abs=1e-14) and h[0, 0, 0, 0] == pytest.approx(-8.0, abs=1e-14)
+    assert ya[0, 0, 0, 0] == pytest.approx(9.5, abs=1e-14) and ha[0, 0, 0, 0] == pytest.approx(8.0, abs=1e-14)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_abs_terms_bound_the_outputs(seed):
+    """Triangle inequality: |y| <= y_abs and |h| <= h_abs element by element,
+    with equality when every input is nonnegative."""
+    case = rand_case(100 + seed)
+    y, h = ssd.ssd_loop(*case)
+    ya, ha = ssd.ssd_abs_terms(*case)
+    assert np.all(np.abs(y) <= ya * (1 + 1e-12)) and np.all(np.abs(h) <= ha * (1 + 1e-12))
+    assert np.mean(ya) > 1.5 * np.mean(np.abs(y))  # random signs cancel: the scale is not |y|
+    pos = [None if v is None else np.abs(v) for v in case]
+    pos[1] = case[1]
+    pos[2] = case[2]
+    yp, hp = ssd.ssd_loop(*pos)
+    yq, hq = ssd.ssd_abs_terms(*pos)
+    np.testing.assert_allclose(yq, yp, rtol=1e-13)
+    np.testing.assert_allclose(hq, hp, rtol=1e-13)
+    with pytest.raises(ValueError):
+        ssd.ssd_abs_terms(case[0], -case[1], *case[2:])
