@@ -1,30 +1,44 @@
 """Throughput benchmark of the SSD forward pass and the linear scan on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ssd_large]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload ssd_long]
 
-One step is one ``ssd_fwd`` call over one batch of the named workload, with
-inputs already resident in HBM: the CB pass (C B^T per (batch, chunk, group)
-and the token-contiguous copy of B) and the fused kernel (segment sums,
-intra-chunk products, chunk states, the inter-chunk recurrence and outputs).
-K steps are timed with HIP events on the launch stream, bracketed by device
-synchronisation; during the same steps the library records events around
-each of its two kernels, which gives the fused kernel's own time for the
-roofline.  Input and output buffers rotate over enough copies that the
-footprint exceeds 1 GiB, so the 256 MB Infinity Cache cannot serve repeated
-steps.  The linear scan (one kernel) is timed the same way in its own loop and
-reported in the ``linear_scan`` object of the same JSON line (with its bf16
-forms and a plain elementwise kernel of the same traffic beside it), and so are
-the three-pass scan (``linear_scan_three_pass``) and one decode token
-(``ssd_step``).  The ``autotune`` object compares the plan ssd_fwd_autotune
-keeps for the workload with the built-in heuristic's, timed back to back.
+One step is one ``ssd_fwd`` call (every launch of the call: the CB pass, the
+aggregate launch when chains are split, the output launch) over one batch of
+the named workload, with inputs already resident in HBM.  The headline
+workload is the long-context prefill (batch 1, L = 65536, 64 heads, P = 64,
+S = 128, 8 groups, chunk 128, nonzero initial state), the largest of the
+workloads.
 
-Other modes: ``--scan-ceiling-sweep`` (linear_scan against torch.mul over row
-lengths), ``--copy-probe`` / ``--record-traffic`` (the HBM traffic counters),
-``--no-autotune`` (counter and trace runs), ``--no-scan``, ``--workload``.
+Timing protocol ("Selective-scan CUDA kernels", section "Results": median of
+15 interleaved samples, repetitions inside the timed window; section "Two real
+bugs the tests caught": kernels too short for the GPU to boost):
 
-The CPU baseline is the float64 oracle, unmodified, run on a bounded sample
-of the same workload (a few whole (batch, head) sequences, one per worker
-process) and scaled to the metric's unit.
+* every workload is warmed up with W steps and then until at least 50 ms of
+  its own GPU time has run;
+* the K timed steps of the headline run as 15 windows, each bracketed by HIP
+  events on the launch stream; the other workloads (the small- and
+  large-model layer shapes, the scans, the decode step) run their own
+  windows of at least 5 ms, interleaved with the headline's: window w of
+  every workload runs before window w + 1 of any;
+* inputs and outputs rotate over enough buffer copies that each workload's
+  footprint exceeds 1 GiB, so the 256 MB Infinity Cache cannot serve repeats;
+* ``value`` is tokens / (mean time per step over the K timed steps); the
+  median and IQR of the 15 windows are reported beside it;
+* GPU clocks and power (amd-smi, else rocm-smi) are recorded before and after.
+
+``roofline`` is for the whole ssd_fwd call: algorithmic bytes (every input
+read once, every output written once) over the mean call time, against
+8 TB/s; the MFMA side (causal-triangle flops over 2.5 PFLOP/s) is reported
+beside it, and ``per_launch`` splits the call into its launches (a separate
+loop that records events between them through ssd_fwd_planned).
+
+The CPU baseline is the float64 oracle, unmodified, over a process pool on the
+host's cores (one whole (batch, head) sequence or row block per job), scaled
+to the metric's unit.
+
+Other modes: ``--scan-ceiling-sweep``, ``--copy-probe`` / ``--record-traffic``
+(HBM traffic counters), ``--no-autotune``, ``--no-cpu-baseline``,
+``--only-headline`` (the headline workload alone, for counter runs).
 
 Prints exactly one JSON line.
 """
@@ -35,6 +49,8 @@ import hashlib
 import json
 import math
 import os
+import statistics
+import subprocess
 import sys
 import time
 
@@ -43,8 +59,10 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
-FP32_PEAK_TFLOPS = 157.3
 METRIC = "SSD fwd tokens/sec (B·L) + % of HBM/MFMA roofline; linear-scan GB/s"
+NWIN = 15                      # timed windows per workload
+MIN_WINDOW_S = 5e-3            # each window of a side workload lasts at least this long
+WARM_S = 50e-3                 # GPU time each workload runs before its first window
 
 
 def _nbytes(t):
@@ -70,6 +88,9 @@ def ssd_alg_flops(shape):
     return cb + shape.batch * nc * shape.nheads * per_head
 
 
+# ---------------------------------------------------------------------------
+# traffic counters (rocprofv3 --pmc) committed under profiles/
+# ---------------------------------------------------------------------------
 def code_text(src):
     """Source text without comments and with whitespace runs collapsed: what
     the compiler sees, so an edit to a comment keeps a kernel's digest."""
@@ -93,33 +114,32 @@ def source_digest(names, read=None):
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel_key, sources, launches_per_step=1):
-    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
-    summary, only if it was taken on the current kernel sources."""
-    path = os.path.join(ROOT, "profiles", "traffic.json")
+SSD_SOURCES = ["ssd_fused.hpp", "ssd_fused.hip", "common.hpp", "ssd_kernels.hpp", "ssd_dispatch.cpp"]
+SCAN_SOURCES = ["linear_scan.hip", "common.hpp"]
+STEP_SOURCES = ["ssd_step.hip", "common.hpp"]
+
+
+def measured_traffic(key, sources):
+    """HBM bytes per call from profiles/traffic.json, only if they were taken
+    on the current kernel sources."""
     try:
-        with open(path) as f:
+        with open(os.path.join(ROOT, "profiles", "traffic.json")) as f:
             db = json.load(f)
     except (OSError, ValueError):
         return None
-    rec = db.get(kernel_key)
+    rec = db.get(key)
     if not rec or rec.get("source_digest") != source_digest(sources):
         return None
-    return rec.get("hbm_bytes_per_launch")
-
-
-SSD_SOURCES = ["ssd_fused.hpp", "ssd_fused.hip", "common.hpp", "ssd_kernels.hpp"]
-SCAN_SOURCES = ["linear_scan.hip", "common.hpp"]
-STEP_SOURCES = ["ssd_step.hip", "common.hpp"]
+    return rec.get("hbm_bytes_per_call")
 
 
 def record_traffic(fetch_csv, write_csv, workload):
     """Write profiles/traffic.json from two rocprofv3 --pmc runs of this script
     with --copy-probe (one with FETCH_SIZE, one with WRITE_SIZE).  Each counter
     is scaled by what it reads for the 1 GiB device copies of --copy-probe
-    (copyBuffer dispatches of 131072 workgroups), per dispatch of each kernel."""
+    (copyBuffer dispatches of 131072 workgroups).  An SSD call's bytes are the
+    sum over its kernels (per-dispatch means)."""
     import csv
-    import statistics
 
     def read(path, name):
         d = {}
@@ -141,60 +161,315 @@ def record_traffic(fetch_csv, write_csv, workload):
     if os.path.exists(path):
         with open(path) as f:
             db = json.load(f)
-    for key, srcs, pat in [("ssd_fused_kernel:" + workload, SSD_SOURCES, "ssd_fused_kernel<"),
-                           ("ssd_fused_agg_kernel:" + workload, SSD_SOURCES, "ssd_fused_agg_kernel<"),
-                           ("linear_scan:scan", SCAN_SOURCES, "linear_scan_kernel<false, float, float>"),
-                           ("ssd_step:decode_large", STEP_SOURCES, "ssd_step_kernel")]:
+
+    def per_kernel(pat):
         f = [v for (k, g), vs in fe.items() if pat in k for v in vs]
         w = [v for (k, g), vs in wr.items() if pat in k for v in vs]
         if not f or not w:
+            return None
+        return statistics.mean(f) * sf * 1024, statistics.mean(w) * sw * 1024, len(f)
+
+    groups = [("ssd_fwd:" + workload, SSD_SOURCES, ["ssd_cbt_kernel<", "ssd_fused_agg_kernel<", "ssd_fused_kernel<"]),
+              ("linear_scan:scan", SCAN_SOURCES, ["linear_scan_kernel<false, float, float>"]),
+              ("ssd_step:decode_large", STEP_SOURCES, ["ssd_step_kernel"])]
+    for key, srcs, pats in groups:
+        parts = {p.rstrip("<"): per_kernel(p) for p in pats}
+        parts = {k: v for k, v in parts.items() if v is not None}
+        if not parts:
             continue
-        fb = statistics.mean(f) * sf * 1024
-        wb = statistics.mean(w) * sw * 1024
-        db[key] = {"source_digest": source_digest(srcs), "hbm_bytes_per_launch": round(fb + wb),
-                   "fetch_bytes": round(fb), "write_bytes": round(wb), "dispatches": len(f),
+        fb = sum(v[0] for v in parts.values())
+        wb = sum(v[1] for v in parts.values())
+        db[key] = {"source_digest": source_digest(srcs), "hbm_bytes_per_call": round(fb + wb),
+                   "fetch_bytes": round(fb), "write_bytes": round(wb),
+                   "per_kernel": {k: {"fetch_bytes": round(v[0]), "write_bytes": round(v[1]), "dispatches": v[2]}
+                                  for k, v in parts.items()},
                    "scale_fetch": round(sf, 4), "scale_write": round(sw, 4)}
         print(key, db[key])
     with open(path, "w") as f:
         json.dump(db, f, indent=1, sort_keys=True)
 
 
-def time_loop(fn, nsets, steps, warmup, stream, before_timed=None):
+# ---------------------------------------------------------------------------
+# clocks and power
+# ---------------------------------------------------------------------------
+def gpu_state():
+    """GPU clocks and power as amd-smi (else rocm-smi) reports them, as text
+    trimmed to the lines that carry them; None when neither tool answers."""
+    for cmd in (["amd-smi", "metric", "-g", "0", "-c", "-p"], ["rocm-smi", "--showclocks", "--showpower"]):
+        try:
+            r = subprocess.run(cmd, capture_output=True, text=True, timeout=20)
+        except (OSError, subprocess.SubprocessError):
+            continue
+        if r.returncode != 0 or not r.stdout.strip():
+            continue
+        keep = [ln.strip() for ln in r.stdout.splitlines()
+                if any(k in ln.upper() for k in ("CLK", "CLOCK", "POWER", "MHZ", " W"))]
+        return {"tool": cmd[0], "lines": keep[:40]}
+    return None
+
+
+# ---------------------------------------------------------------------------
+# workloads as runners: step(i) enqueues one call on buffer set i
+# ---------------------------------------------------------------------------
+class Runner:
+    name = ""
+    nsets = 1
+
+    def step(self, i):
+        raise NotImplementedError
+
+
+def _dev():
     import torch
-    for i in range(warmup):
-        fn(i % nsets)
-    torch.cuda.synchronize()
-    if before_timed is not None:
-        before_timed()
-    start = torch.cuda.Event(enable_timing=True)
-    end = torch.cuda.Event(enable_timing=True)
-    start.record(stream)
-    for i in range(steps):
-        fn(i % nsets)
-    end.record(stream)
-    torch.cuda.synchronize()
-    return start.elapsed_time(end) / 1e3 / steps  # seconds per step
+    return torch.device("cuda:0")
+
+
+class SsdRunner(Runner):
+    def __init__(self, name):
+        import torch
+        import chunked_linear_scan_amd as cls
+        from chunked_linear_scan_amd import workloads
+        self.cls = cls
+        self.name = name
+        self.shape, _ = workloads.SSD_WORKLOADS[name]
+        self.inp = workloads.ssd_workload(name)
+        self.alg_bytes = ssd_alg_bytes(self.inp, self.shape)
+        self.flops = ssd_alg_flops(self.shape)
+        self.tokens = self.shape.batch * self.shape.seqlen
+        self.nsets = max(1, math.ceil((1 << 30) / self.alg_bytes))
+        dev = _dev()
+        s = self.shape
+        self.sets = []
+        for _ in range(self.nsets):
+            d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in self.inp.items()}
+            d["y"] = torch.empty_like(d["x"])
+            self.sets.append(d)
+        self.hf = torch.empty(s.batch, s.nheads, s.headdim, s.dstate, dtype=torch.float32, device=dev)
+
+    def step(self, i):
+        d = self.sets[i % self.nsets]
+        self.cls.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=self.shape.chunk,
+                         out=d["y"])
+
+    def describe(self):
+        s = self.shape
+        return (f"{self.name}: batch {s.batch}, L={s.seqlen}, {s.nheads} heads, P={s.headdim}, S={s.dstate}, "
+                f"{s.ngroups} group(s), chunk {s.chunk}, {s.dtype}"
+                + (f", h0 ~ N(0, {s.h0_std}^2)" if s.h0_std > 0 else ""))
+
+    def per_launch(self, calls=20):
+        """Mean time of each launch of a call: events between the launches
+        (ssd_fwd_planned with the default plan), on their own loop."""
+        import torch
+        cls = self.cls
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(calls)]
+        for k in range(calls):
+            d = self.sets[k % self.nsets]
+            cls.ssd_fwd_planned(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=self.shape.chunk,
+                                out=d["y"], events=evs[k])
+        torch.cuda.synchronize()
+        t = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / calls * 1e3 for j in range(3)]
+        plan = cls.ssd_fwd_plan(self.shape.batch, self.shape.seqlen, self.shape.nheads, self.shape.headdim,
+                                self.shape.dstate, self.shape.ngroups, self.shape.chunk, self.inp["x"].dtype)
+        return {"cb_pass_us": round(t[0], 2), "aggregate_launch_us": round(t[1], 2),
+                "output_launch_us": round(t[2], 2), "sum_us": round(sum(t), 2), "plan": plan}
+
+
+class ScanRunner(Runner):
+    def __init__(self, name, dtype_in="f32", dtype_out="f32"):
+        import torch
+        import chunked_linear_scan_amd as cls
+        from chunked_linear_scan_amd import workloads
+        self.cls = cls
+        self.name = name + ("" if (dtype_in, dtype_out) == ("f32", "f32") else f":{dtype_in}->{dtype_out}")
+        self.inp = workloads.scan_workload(name)
+        rows, L = self.inp["a"].shape
+        self.rows, self.L = rows, L
+        tin = torch.float32 if dtype_in == "f32" else torch.bfloat16
+        tout = torch.float32 if dtype_out == "f32" else torch.bfloat16
+        self.bytes_per_elem = 2 * (4 if dtype_in == "f32" else 2) + (4 if dtype_out == "f32" else 2)
+        self.alg_bytes = self.bytes_per_elem * rows * L
+        self.nsets = max(1, math.ceil((1 << 30) / self.alg_bytes))
+        dev = _dev()
+        self.sets = [(self.inp["a"].to(tin).to(dev), self.inp["b"].to(tin).to(dev),
+                      torch.empty(rows, L, dtype=tout, device=dev)) for _ in range(self.nsets)]
+        self.ws = torch.zeros(cls.load_library().linear_scan_workspace_size(rows, L), dtype=torch.uint8, device=dev)
+
+    def step(self, i):
+        a, b, h = self.sets[i % self.nsets]
+        self.cls.linear_scan(a, b, out=h, workspace=self.ws)
+
+
+class Scan3Runner(ScanRunner):
+    def __init__(self, name):
+        super().__init__(name)
+        self.name = name + ":three_pass"
+
+    def step(self, i):
+        a, b, h = self.sets[i % self.nsets]
+        self.cls.linear_scan_three_pass(a, b, out=h)
+
+
+class MulRunner(ScanRunner):
+    """torch.mul(a, b, out=h): a plain elementwise kernel with the scan's
+    traffic (read two arrays, write one), as context for the scan."""
+
+    def __init__(self, name):
+        super().__init__(name)
+        self.name = name + ":torch.mul"
+
+    def step(self, i):
+        import torch
+        a, b, h = self.sets[i % self.nsets]
+        torch.mul(a, b, out=h)
+
+
+class StepRunner(Runner):
+    def __init__(self, name):
+        import torch
+        import chunked_linear_scan_amd as cls
+        from chunked_linear_scan_amd import workloads
+        self.cls = cls
+        self.name = name
+        self.shape, _ = workloads.STEP_WORKLOADS[name]
+        self.inp = workloads.step_workload(name)
+        s = self.shape
+        esz = 2 if s.dtype == "bf16" else 4
+        Bt, H, P, S, G = s.batch, s.nheads, s.headdim, s.dstate, s.ngroups
+        self.alg_bytes = (2 * Bt * H * P * S * 4 + 2 * Bt * H * P * esz + Bt * H * 4 + 2 * Bt * G * S * esz
+                          + 2 * H * 4)
+        self.nsets = max(1, math.ceil((1 << 30) / self.alg_bytes))
+        dev = _dev()
+        self.sets = []
+        for _ in range(self.nsets):
+            d = {k: v.to(dev) for k, v in self.inp.items()}
+            d["y"] = torch.empty_like(d["x"])
+            self.sets.append(d)
+
+    def step(self, i):
+        d = self.sets[i % self.nsets]
+        self.cls.ssd_step(d["h"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], out=d["y"])
 
 
 # ---------------------------------------------------------------------------
-# CPU baseline: the oracle on a bounded sample, one (batch, head) per process
+# timing
 # ---------------------------------------------------------------------------
-def _oracle_ssd_job(args):
-    import numpy as np
-    from oracle import ssd as ossd
-    x, dt, A, B, C, D, h0 = args
+def warm(runner, warmup_steps):
+    """W steps, then more until >= 50 ms of this workload's GPU time has run.
+    Returns (warm-up GPU seconds, seconds per step estimate)."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for i in range(warmup_steps):
+        runner.step(i)
+    torch.cuda.synchronize()
+    total, n, est = 0.0, 4, None
+    while total < WARM_S:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(n):
+            runner.step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        dt = e0.elapsed_time(e1) / 1e3
+        total += dt
+        est = dt / n
+        n = min(4 * n, 1024)
+    return total, est
+
+
+def split_steps(k, nwin):
+    base, extra = divmod(k, nwin)
+    return [base + (1 if w < extra else 0) for w in range(nwin)]
+
+
+def timed_windows(runners, plan):
+    """Interleaved windows: window w of every runner before window w + 1 of
+    any.  plan[name] = steps per window (list of NWIN).  Returns per runner the
+    seconds of each window."""
+    import torch
+    stream = torch.cuda.current_stream()
+    out = {r.name: [] for r in runners}
+    offs = {r.name: 0 for r in runners}
+    torch.cuda.synchronize()
+    for w in range(NWIN):
+        for r in runners:
+            n = plan[r.name][w]
+            if n == 0:
+                out[r.name].append(0.0)
+                continue
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(n):
+                r.step(offs[r.name] + i)
+            e1.record(stream)
+            offs[r.name] += n
+            out[r.name].append((e0, e1))
+    torch.cuda.synchronize()
+    res = {}
+    for r in runners:
+        res[r.name] = [(x[0].elapsed_time(x[1]) / 1e3 if isinstance(x, tuple) else 0.0) for x in out[r.name]]
+    return res
+
+
+def summarize(window_s, steps):
+    """Mean over all steps, and median / quartiles of the per-step time of
+    the windows (seconds)."""
+    per = sorted(t / n for t, n in zip(window_s, steps) if n > 0)
+    q = statistics.quantiles(per, n=4) if len(per) >= 2 else [per[0]] * 3
+    return {"mean": sum(window_s) / sum(steps), "median": statistics.median(per), "q1": q[0], "q3": q[2],
+            "min": per[0], "max": per[-1]}
+
+
+def _us(s):
+    return round(s * 1e6, 2)
+
+
+def timing_block(st, steps):
+    return {"windows": NWIN, "steps_per_window": steps, "mean_us": _us(st["mean"]), "median_us": _us(st["median"]),
+            "q1_us": _us(st["q1"]), "q3_us": _us(st["q3"]), "iqr_us": _us(st["q3"] - st["q1"]),
+            "min_us": _us(st["min"]), "max_us": _us(st["max"])}
+
+
+# ---------------------------------------------------------------------------
+# CPU baselines: the oracle over a process pool on the host's cores
+# ---------------------------------------------------------------------------
+def _cores():
+    n = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else (os.cpu_count() or 1)
+    return max(1, min(n, 64))
+
+
+def _pool_run(fn, jobs, cores):
+    import multiprocessing as mp
+    for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
+        os.environ[k] = "1"
     t0 = time.perf_counter()
-    ossd.ssd_loop(x, dt, A, B, C, D, h0)
+    with mp.get_context("spawn").Pool(cores) as pool:
+        pool.map(fn, jobs, chunksize=1)
     return time.perf_counter() - t0
 
 
-def cpu_baseline_ssd(inp, shape, budget_s=15.0):
+def _oracle_ssd_job(args):
+    from oracle import ssd as ossd
+    ossd.ssd_loop(*args)
+
+
+def _oracle_scan_job(args):
+    from oracle import scan as oscan
+    oscan.scan_loop(*args)
+
+
+def _oracle_step_job(args):
+    from oracle import ssd as ossd
+    ossd.ssd_step(*args)
+
+
+def cpu_baseline_ssd(runner, budget_s=15.0):
     """Oracle wall time on as many whole (batch, head) sequences as fit the
-    budget (all of them when they do), one sequence per job, one job per core."""
-    import multiprocessing as mp
+    budget (all of them when they do), one sequence per job."""
     import torch
-    cores = len(os.sched_getaffinity(0))
-    H, G = shape.nheads, shape.ngroups
+    inp, shape = runner.inp, runner.shape
+    cores = _cores()
+    H, G, L = shape.nheads, shape.ngroups, shape.seqlen
     np64 = lambda t: None if t is None else t.to(dtype=torch.float64).numpy()
 
     def job(bb, h, n=None):
@@ -205,316 +480,135 @@ def cpu_baseline_ssd(inp, shape, budget_s=15.0):
                 np64(inp["C"][bb:bb + 1, sl, g:g + 1]), np64(inp["D"][h:h + 1]),
                 None if inp["h0"] is None else np64(inp["h0"][bb:bb + 1, h:h + 1]))
 
-    L = shape.seqlen
     probe = min(L, 1024)
-    t_job = _oracle_ssd_job(job(0, 0, probe)) * L / probe
+    t0 = time.perf_counter()
+    _oracle_ssd_job(job(0, 0, probe))
+    t_job = (time.perf_counter() - t0) * L / probe
     total = shape.batch * H
     njobs = max(1, min(total, int(budget_s * cores / max(t_job, 1e-6))))
-    # spread the sampled sequences over batches and heads
-    pairs = [(k % shape.batch, (k * 7919) % H) for k in range(total)][:njobs] if njobs < total \
-        else [(bb, h) for bb in range(shape.batch) for h in range(H)]
-    for k in ("OMP_NUM_THREADS", "OPENBLAS_NUM_THREADS", "MKL_NUM_THREADS"):
-        os.environ[k] = "1"
-    jobs = [job(bb, h) for bb, h in pairs]
-    t0 = time.perf_counter()
-    with mp.get_context("spawn").Pool(cores) as pool:
-        pool.map(_oracle_ssd_job, jobs, chunksize=1)
-    wall = time.perf_counter() - t0
-    tok_equiv = L * len(jobs) / H  # a token counts once all H heads of its row are done
+    pairs = [(bb, h) for bb in range(shape.batch) for h in range(H)]
+    if njobs < total:
+        pairs = [(k % shape.batch, (k * 7919) % H) for k in range(njobs)]
+    wall = _pool_run(_oracle_ssd_job, [job(bb, h) for bb, h in pairs], cores)
+    tok_equiv = L * len(pairs) / H  # a token counts once all H heads of its row are done
     return {"value": tok_equiv / wall, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{len(jobs)} of {total} whole (batch, head) sequences of {L} tokens, "
-                      f"one per job on {cores} processes, wall {wall:.1f}s"}
+            "sample": f"{len(pairs)} of {total} whole (batch, head) sequences of {L} tokens, one per job on "
+                      f"{cores} processes, wall {wall:.1f}s"}
 
 
-def cpu_baseline_scan(inp):
-    from oracle import scan as oscan
-    t0 = time.perf_counter()
-    oscan.scan_loop(inp["a"].numpy(), inp["b"].numpy())
-    wall = time.perf_counter() - t0
-    nbytes = 12 * inp["a"].numel()
-    return {"value": nbytes / wall / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"whole workload ({tuple(inp['a'].shape)}), wall {wall:.2f}s"}
+def cpu_baseline_scan(runner):
+    """The whole workload, its rows split into one block per core."""
+    a, b = runner.inp["a"].numpy(), runner.inp["b"].numpy()
+    cores = _cores()
+    blk = max(1, math.ceil(a.shape[0] / cores))
+    jobs = [(a[r:r + blk], b[r:r + blk]) for r in range(0, a.shape[0], blk)]
+    wall = _pool_run(_oracle_scan_job, jobs, min(cores, len(jobs)))
+    return {"value": runner.alg_bytes / wall / 1e9, "unit": "GB/s", "cores": min(cores, len(jobs)),
+            "kind": "oracle", "sample": f"whole workload {tuple(a.shape)}, rows in {len(jobs)} blocks, "
+                                        f"one per process, wall {wall:.2f}s"}
 
 
-def bench_scan3(name, steps, warmup, scan_us):
-    """The three-pass scan (block scan, spine, apply) on the same workload, and
-    the traffic model it tests: seven arrays of traffic against the single
-    pass's three, so at equal bus efficiency 7/3 of its time."""
+def cpu_baseline_step(runner):
+    """One decode token of the whole batch, batch rows split over the cores."""
     import torch
-    import chunked_linear_scan_amd as cls
-    from chunked_linear_scan_amd import workloads
-    inp = workloads.scan_workload(name)
-    rows, L = inp["a"].shape
-    nbytes = 12 * rows * L
-    nsets = max(1, math.ceil((1 << 30) / nbytes))
-    dev = torch.device("cuda:0")
-    lib = cls.load_library()
-    sets = [(inp["a"].to(dev), inp["b"].to(dev), torch.empty(rows, L, device=dev)) for _ in range(nsets)]
-    ws = torch.empty(lib.linear_scan_three_pass_workspace_size(rows, L), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream(dev)
-
-    def step(i):
-        a, b, h = sets[i]
-        st = lib.linear_scan_three_pass(cls._ptr(a), cls._ptr(b), cls._ptr(h), rows, L, cls._ptr(ws), ws.numel(),
-                                        cls._stream_handle(dev))
-        if st != 0:
-            raise RuntimeError(cls.strerror(st))
-
-    t = time_loop(step, nsets, steps, warmup, stream)
-    moved = 28 * rows * L
-    return {"workload": f"{name}: {rows} rows x {L} fp32", "value": round(nbytes / t / 1e9, 1), "unit": "GB/s",
-            "us_per_call": round(t * 1e6, 2), "moved_bytes": moved, "moved_gbs": round(moved / t / 1e9, 1),
-            "moved_frac_of_peak": round(moved / t / 1e9 / HBM_PEAK_GBS, 4),
-            "time_ratio_to_single_pass": round(t * 1e6 / scan_us, 3), "traffic_model_ratio": round(7 / 3, 3)}
-
-
-def cpu_baseline_step(inp, nbytes):
-    from oracle import ssd as ossd
-    arrs = [inp[k].to(torch_f64()).numpy() for k in ("h", "x", "dt", "A", "B", "C", "D")]
-    t0 = time.perf_counter()
-    ossd.ssd_step(*arrs)
-    wall = time.perf_counter() - t0
-    return {"value": nbytes / wall / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"whole workload (one token, {tuple(inp['h'].shape)} state), wall {wall:.2f}s"}
-
-
-def torch_f64():
-    import torch
-    return torch.float64
-
-
-def bench_step(name, steps, warmup, want_cpu):
-    """One decode token per call (ssd_step) over the named workload; the state
-    is updated in place, so repeated calls keep decoding."""
-    import torch
-    import chunked_linear_scan_amd as cls
-    from chunked_linear_scan_amd import workloads
-    shape, _ = workloads.STEP_WORKLOADS[name]
-    inp = workloads.step_workload(name)
-    Bt, H, P, S, G = shape.batch, shape.nheads, shape.headdim, shape.dstate, shape.ngroups
-    esz = 2 if shape.dtype == "bf16" else 4
-    nbytes = (2 * Bt * H * P * S * 4 + 2 * Bt * H * P * esz + Bt * H * 4 + 2 * Bt * G * S * esz + 2 * H * 4)
-    nsets = max(1, math.ceil((1 << 30) / nbytes))
-    dev = torch.device("cuda:0")
-    sets = []
-    for _ in range(nsets):
-        d = {k: v.to(dev) for k, v in inp.items()}
-        d["y"] = torch.empty_like(d["x"])
-        sets.append(d)
-    stream = torch.cuda.current_stream(dev)
-
-    def step(i):
-        d = sets[i]
-        cls.ssd_step(d["h"], d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], out=d["y"])
-
-    t = time_loop(step, nsets, steps, warmup, stream)
-    gbs = nbytes / t / 1e9
-    res = {"workload": f"{name}: one decode token, batch {Bt}, {H} heads, P={P}, S={S}, {G} group(s), "
-                       f"{shape.dtype}",
-           "value": round(gbs, 1), "unit": "GB/s", "us_per_call": round(t * 1e6, 2), "nsets": nsets,
-           "tokens_per_s": round(Bt / t, 1),
-           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(gbs / HBM_PEAK_GBS, 4), "alg_bytes": nbytes,
-                        "traffic": measured_traffic("ssd_step:" + name, STEP_SOURCES)}}
-    if want_cpu:
-        res["cpu_baseline"] = cpu_baseline_step(inp, nbytes)
-    return res
+    arrs = [runner.inp[k].to(torch.float64).numpy() for k in ("h", "x", "dt", "A", "B", "C", "D")]
+    Bt = arrs[0].shape[0]
+    cores = _cores()
+    blk = max(1, math.ceil(Bt / cores))
+    jobs = []
+    for r in range(0, Bt, blk):
+        jobs.append(tuple(v[r:r + blk] if k not in (3, 6) else v for k, v in enumerate(arrs)))
+    wall = _pool_run(_oracle_step_job, jobs, min(cores, len(jobs)))
+    return {"value": runner.alg_bytes / wall / 1e9, "unit": "GB/s", "cores": min(cores, len(jobs)),
+            "kind": "oracle", "sample": f"whole workload (one token, state {tuple(arrs[0].shape)}), batch rows in "
+                                        f"{len(jobs)} blocks, one per process, wall {wall:.2f}s"}
 
 
 # ---------------------------------------------------------------------------
-def bench_ssd(name, steps, warmup, want_cpu, want_autotune=True):
-    import torch
-    import chunked_linear_scan_amd as cls
-    from chunked_linear_scan_amd import workloads
-    shape, seed = workloads.SSD_WORKLOADS[name]
-    inp = workloads.make_ssd_inputs(shape, seed)
-    alg_bytes = ssd_alg_bytes(inp, shape)
-    nsets = max(1, math.ceil((1 << 30) / alg_bytes))
-    dev = torch.device("cuda:0")
-    sets = []
-    for _ in range(nsets):
-        d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
-        d["y"] = torch.empty_like(d["x"])
-        d["hf"] = torch.empty(shape.batch, shape.nheads, shape.headdim, shape.dstate,
-                              dtype=torch.float32, device=dev)
-        sets.append(d)
-    stream = torch.cuda.current_stream(dev)
-
-    def step(i):
-        d = sets[i]
-        cls.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=shape.chunk,
-                    out=d["y"])
-
-    lib = cls.load_library()
-    import ctypes
-    lib.cls_ssd_profile.argtypes = [ctypes.c_int]
-    lib.cls_ssd_profile_read.argtypes = [ctypes.POINTER(ctypes.c_double)] * 3 + [ctypes.POINTER(ctypes.c_int)]
-    if lib.cls_ssd_profile(1) != 0:  # creates the events
-        raise RuntimeError("could not create the profiling events")
-    lib.cls_ssd_profile(0)
-    # the timed steps run without the library's events (recording them costs a
-    # few microseconds per call); a second, shorter loop records them for the
-    # per-launch breakdown
-    t = time_loop(step, nsets, steps, warmup, stream)
-    time_loop(step, nsets, max(10, steps // 4), 2, stream, before_timed=lambda: lib.cls_ssd_profile(1))
-    cb_ms, agg_ms, fu_ms, ncalls = ctypes.c_double(), ctypes.c_double(), ctypes.c_double(), ctypes.c_int()
-    if lib.cls_ssd_profile_read(ctypes.byref(cb_ms), ctypes.byref(agg_ms), ctypes.byref(fu_ms),
-                                ctypes.byref(ncalls)) != 0:
-        raise RuntimeError("reading the profiling events failed")
-    lib.cls_ssd_profile(0)
-    n = max(ncalls.value, 1)
-    t_fused = fu_ms.value / 1e3 / n if ncalls.value else None
-    t_cb = cb_ms.value / 1e3 / n if ncalls.value else None
-    t_agg = agg_ms.value / 1e3 / n if ncalls.value else None
-    tokens = shape.batch * shape.seqlen
-    flops = ssd_alg_flops(shape)
-    t_kernel = t_fused if t_fused else t
-    gbs = alg_bytes / t_kernel / 1e9
-    tflops = flops / t_kernel / 1e12
-    t_roof = max(alg_bytes / (HBM_PEAK_GBS * 1e9), flops / (BF16_PEAK_TFLOPS * 1e12))
-    srcs = SSD_SOURCES
-    res = {
-        "t": t, "tokens_per_s": tokens / t, "alg_bytes": alg_bytes, "alg_flops": flops,
-        "gbs": gbs, "tflops": tflops, "nsets": nsets,
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gbs / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("ssd_fused_kernel:" + name, srcs),
-                     "aggregate_pass_traffic": measured_traffic("ssd_fused_agg_kernel:" + name, srcs),
-                     "kernel": "ssd_fused_kernel (output launch)" if t_fused else "whole ssd_fwd call",
-                     "kernel_us": round(t_kernel * 1e6, 2),
-                     "cb_pass_us": None if t_cb is None else round(t_cb * 1e6, 2),
-                     "aggregate_pass_us": None if t_agg is None else round(t_agg * 1e6, 2),
-                     "fused_launches_frac": None if t_agg is None else
-                     round(alg_bytes / (t_agg + t_kernel) / 1e9 / HBM_PEAK_GBS, 4),
-                     "call_us": round(t * 1e6, 2),
-                     "alg_bytes": alg_bytes, "alg_flops": flops,
-                     "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                     "call_frac_of_roofline": round(t_roof / t, 4)},
-        "shape": shape,
-    }
-    # The autotuner (ssd_fwd_autotune) on the same inputs: the plan it keeps
-    # and ssd_fwd's time on that plan, beside the built-in heuristic's, which
-    # is what the timed steps above ran.  The table is cleared afterwards.
-    if want_autotune:
-        heur = cls.ssd_fwd_plan(shape.batch, shape.seqlen, shape.nheads, shape.headdim, shape.dstate,
-                                shape.ngroups, shape.chunk, inp["x"].dtype)
-        d0 = sets[0]
-        _, _, info = cls.ssd_fwd_autotune(d0["x"], d0["dt"], d0["A"], d0["B"], d0["C"], d0["D"], d0["h0"],
-                                          chunk=shape.chunk, reps=10, out=d0["y"])
-        t_tuned = time_loop(step, nsets, steps, warmup, stream)
-        cls.ssd_fwd_autotune_reset()
-        # the heuristic again, right after, so that both loops run in the same
-        # state of the GPU (a later loop tends to run a little faster)
-        t_heur = time_loop(step, nsets, steps, warmup, stream)
-        res["autotune"] = {"plan": {"nsegs": info["nsegs"], "nsplit": info["nsplit"],
-                                    "agg_pieces": info["agg_pieces"]},
-                           "heuristic_plan": {"nsegs": heur["nsegs"], "nsplit": heur["nsplit"],
-                                              "agg_pieces": heur["agg_pieces"]},
-                           "us_per_call_tuned": round(t_tuned * 1e6, 2),
-                           "us_per_call_heuristic": round(t_heur * 1e6, 2),
-                           "speedup": round(t_heur / t_tuned, 3)}
-    if want_cpu:
-        res["cpu_baseline"] = cpu_baseline_ssd(inp, shape)
-    return res
-
-
-def bench_scan(name, steps, warmup, want_cpu):
-    import torch
-    import chunked_linear_scan_amd as cls
-    from chunked_linear_scan_amd import workloads
-    inp = workloads.scan_workload(name)
-    rows, L = inp["a"].shape
-    nbytes = 12 * rows * L
-    nsets = max(1, math.ceil((1 << 30) / nbytes))
-    dev = torch.device("cuda:0")
-    sets = [(inp["a"].to(dev), inp["b"].to(dev), torch.empty(rows, L, device=dev)) for _ in range(nsets)]
-    stream = torch.cuda.current_stream(dev)
-    ws = torch.zeros(cls.load_library().linear_scan_workspace_size(rows, L), dtype=torch.uint8, device=dev)
-
-    def step(i):
-        a, b, h = sets[i]
-        cls.linear_scan(a, b, out=h, workspace=ws)
-
-    t = time_loop(step, nsets, steps, warmup, stream)
-    gbs = nbytes / t / 1e9
-    res = {"workload": f"{name}: {rows} rows x {L} fp32", "value": round(gbs, 1), "unit": "GB/s",
-           "us_per_call": round(t * 1e6, 2), "nsets": nsets,
+def ssd_result(r, st, steps):
+    t = st["mean"]
+    gbs = r.alg_bytes / t / 1e9
+    tflops = r.flops / t / 1e12
+    res = {"workload": r.describe(), "value": round(r.tokens / t, 1), "unit": "tokens/s",
+           "us_per_call": _us(t), "timing": timing_block(st, steps), "buffer_sets": r.nsets,
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(gbs / HBM_PEAK_GBS, 4),
-                        "traffic": measured_traffic("linear_scan:" + name, SCAN_SOURCES)}}
-
-    # A plain elementwise kernel with the same traffic (read two arrays, write
-    # one) on the same buffers: the practical streaming ceiling for this
-    # access pattern, reported beside the scan (not part of the scan).
-    def mul_step(i):
-        a, b, h = sets[i]
-        torch.mul(a, b, out=h)
-
-    tm = time_loop(mul_step, nsets, steps, warmup, stream)
-    res["elementwise_ceiling"] = {"kernel": "torch.mul(a, b, out=h)", "us_per_call": round(tm * 1e6, 2),
-                                  "GB/s": round(nbytes / tm / 1e9, 1), "scan_over_ceiling": round(tm / t, 3)}
-    # bf16 elements (linear_scan_typed): the same rows, a and b rounded to bf16
-    res["bf16"] = {}
-    for dout, tag in [(torch.float32, "bf16_in_f32_out"), (torch.bfloat16, "bf16_in_bf16_out")]:
-        a16, b16 = inp["a"].to(torch.bfloat16), inp["b"].to(torch.bfloat16)
-        nb16 = (4 + (4 if dout == torch.float32 else 2)) * rows * L
-        ns16 = max(1, math.ceil((1 << 30) / nb16))
-        sets16 = [(a16.to(dev), b16.to(dev), torch.empty(rows, L, dtype=dout, device=dev)) for _ in range(ns16)]
-
-        def step16(i, sets16=sets16):
-            a, b, h = sets16[i]
-            cls.linear_scan(a, b, out=h, workspace=ws)
-
-        t16 = time_loop(step16, ns16, steps, warmup, stream)
-        res["bf16"][tag] = {"us_per_call": round(t16 * 1e6, 2), "bytes_per_elem": nb16 // (rows * L),
-                            "GB/s": round(nb16 / t16 / 1e9, 1), "frac": round(nb16 / t16 / 1e9 / HBM_PEAK_GBS, 4)}
-        del sets16
-    if want_cpu:
-        res["cpu_baseline"] = cpu_baseline_scan(inp)
+                        "traffic": measured_traffic("ssd_fwd:" + r.name, SSD_SOURCES),
+                        "kernel": "whole ssd_fwd call", "alg_bytes": r.alg_bytes,
+                        "frac_at_median": round(r.alg_bytes / st["median"] / 1e9 / HBM_PEAK_GBS, 4),
+                        "mfma": {"alg_flops": r.flops, "achieved_tflops": round(tflops, 1),
+                                 "peak_tflops": BF16_PEAK_TFLOPS, "frac": round(tflops / BF16_PEAK_TFLOPS, 4)}}}
     return res
 
 
-def scan_ceiling_sweep(steps, warmup):
-    """linear_scan against torch.mul(a, b, out=h), which moves the same bytes:
-    the row lengths of the page's table ("Selective-scan CUDA kernels",
-    section "Results": 96 MiB per array, L = 2048 ... 65536), then twice and
-    half that size at L = 65536, packed rows of 8186 and longer rows."""
-    import torch
-    import chunked_linear_scan_amd as cls
-    dev = torch.device("cuda:0")
-    stream = torch.cuda.current_stream(dev)
-    g = torch.Generator(device=dev).manual_seed(1)
-    # the page's table: 96 MiB per array at L = 2048 ... 65536; then other sizes
-    for rows, L in [(12288, 2048), (6144, 4096), (3072, 8192), (1536, 16384), (768, 32768), (384, 65536),
-                    (768, 65536), (192, 65536), (3072, 8186), (96, 262144), (24, 1048576)]:
-        nsets = 3
-        sets = [(0.9 + 0.1 * torch.rand(rows, L, device=dev, generator=g),
-                 torch.randn(rows, L, device=dev, generator=g), torch.empty(rows, L, device=dev))
-                for _ in range(nsets)]
-        ws = torch.zeros(cls.load_library().linear_scan_workspace_size(rows, L), dtype=torch.uint8, device=dev)
-        ts = time_loop(lambda i: cls.linear_scan(sets[i][0], sets[i][1], out=sets[i][2], workspace=ws), nsets,
-                       steps, warmup, stream)
-        tm = time_loop(lambda i: torch.mul(sets[i][0], sets[i][1], out=sets[i][2]), nsets, steps, warmup, stream)
-        nb = 12 * rows * L
-        print(json.dumps({"rows": rows, "L": L, "scan_us": round(ts * 1e6, 2), "scan_GBs": round(nb / ts / 1e9, 1),
-                          "mul_us": round(tm * 1e6, 2), "mul_GBs": round(nb / tm / 1e9, 1),
-                          "mul_over_scan": round(tm / ts, 3)}), flush=True)
-        del sets, ws
+def scan_result(r, st, steps):
+    t = st["mean"]
+    gbs = r.alg_bytes / t / 1e9
+    return {"workload": f"{r.name}: {r.rows} rows x {r.L}", "value": round(gbs, 1), "unit": "GB/s",
+            "us_per_call": _us(t), "timing": timing_block(st, steps), "buffer_sets": r.nsets,
+            "bytes_per_elem": r.bytes_per_elem,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4)}}
+
+
+def step_result(r, st, steps):
+    t = st["mean"]
+    gbs = r.alg_bytes / t / 1e9
+    return {"value": round(gbs, 1), "unit": "GB/s", "us_per_call": _us(t), "timing": timing_block(st, steps),
+            "buffer_sets": r.nsets,
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "alg_bytes": r.alg_bytes}}
+
+
+def autotune_compare(r, steps, warmup):
+    """The plan ssd_fwd_autotune keeps for the workload against the built-in
+    heuristic, each timed in interleaved windows right after tuning."""
+    cls = r.cls
+    s = r.shape
+    heur = cls.ssd_fwd_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk, r.inp["x"].dtype)
+    d0 = r.sets[0]
+    _, _, info = cls.ssd_fwd_autotune(d0["x"], d0["dt"], d0["A"], d0["B"], d0["C"], d0["D"], d0["h0"],
+                                      chunk=s.chunk, reps=10, out=d0["y"])
+    tuned = cls.plan_request(nsegs=info["nsegs"], nsplit=info["nsplit"], agg_pieces=info["agg_pieces"]) \
+        if info["nsegs"] > 0 else None
+    cls.ssd_fwd_autotune_reset()
+
+    class Planned(Runner):
+        def __init__(self, name, plan):
+            self.name, self.plan, self.nsets = name, plan, r.nsets
+
+        def step(self, i):
+            d = r.sets[i % r.nsets]
+            if self.plan is None:
+                cls.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=s.chunk, out=d["y"])
+            else:
+                cls.ssd_fwd_planned(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=s.chunk,
+                                    out=d["y"], plan=self.plan)
+
+    a, b = Planned("tuned", tuned), Planned("heuristic", None)
+    for x in (a, b):
+        warm(x, warmup)
+    n = split_steps(steps, NWIN)
+    ws = timed_windows([a, b], {"tuned": n, "heuristic": n})
+    ta, tb = summarize(ws["tuned"], n), summarize(ws["heuristic"], n)
+    return {"plan": {k: info[k] for k in ("nsegs", "nsplit", "agg_pieces")},
+            "heuristic_plan": {k: heur[k] for k in ("nsegs", "nsplit", "agg_pieces")},
+            "us_per_call_tuned": _us(ta["median"]), "us_per_call_heuristic": _us(tb["median"]),
+            "speedup": round(tb["median"] / ta["median"], 3)}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=30)
-    ap.add_argument("--workload", default="ssd_large",
-                    choices=["ssd_small", "ssd_large", "ssd_long", "ssd_tiny"])
-    ap.add_argument("--scan-workload", default="scan", choices=["scan", "scan_ragged"])
+    ap.add_argument("--steps", type=int, default=300)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="ssd_long", choices=["ssd_small", "ssd_large", "ssd_long", "ssd_tiny"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-scan", action="store_true")
     ap.add_argument("--no-autotune", action="store_true",
                     help="skip the autotuner comparison (counter runs: its candidate plans would mix into "
-                         "the per-launch figures)")
+                         "the per-kernel figures)")
+    ap.add_argument("--only-headline", action="store_true",
+                    help="time the headline workload alone (counter and trace runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run three plain 1 GiB device copies (the known-size reference that "
                          "scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
@@ -529,8 +623,11 @@ def main():
         record_traffic(args.record_traffic[0], args.record_traffic[1], args.workload)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); run it with --gpus 1",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build runs on a single GPU; "
+              f"run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    if args.steps < NWIN:
+        print(f"--steps must be at least {NWIN} (one per timed window)", file=sys.stderr)
         sys.exit(2)
     import torch
     if not torch.cuda.is_available():
@@ -547,37 +644,146 @@ def main():
         torch.cuda.synchronize()
         del src, dst
     want_cpu = not args.no_cpu_baseline
-    ssd = bench_ssd(args.workload, args.steps, args.warmup, want_cpu, not args.no_autotune)
-    shape = ssd["shape"]
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    clocks_before = gpu_state()
+    head = SsdRunner(args.workload)
+    log(f"headline {head.describe()}, {head.nsets} buffer set(s)")
+    side = []
+    if not args.only_headline:
+        for name in ("ssd_large", "ssd_small", "ssd_tiny"):
+            if name != args.workload:
+                side.append(SsdRunner(name))
+        side += [ScanRunner("scan"), ScanRunner("scan_ragged"), ScanRunner("scan", "bf16", "f32"),
+                 ScanRunner("scan", "bf16", "bf16"), Scan3Runner("scan"), MulRunner("scan"),
+                 StepRunner("decode_large")]
+    runners = [head] + side
+    plan = {head.name: split_steps(args.steps, NWIN)}
+    warm_s = {}
+    for r in runners:
+        warm_s[r.name], est = warm(r, args.warmup)
+        if r is not head:
+            n = max(1, min(2000, math.ceil(MIN_WINDOW_S / max(est, 1e-7))))
+            plan[r.name] = [n] * NWIN
+        log(f"warmed {r.name}: {warm_s[r.name] * 1e3:.1f} ms, ~{est * 1e6:.1f} us/step")
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    win = timed_windows(runners, plan)
+    t_wall = time.perf_counter() - t_wall
+    stats = {r.name: summarize(win[r.name], plan[r.name]) for r in runners}
+    clocks_after = gpu_state()
+    log(f"timed {sum(sum(v) for v in win.values()) * 1e3:.1f} ms of GPU time in {t_wall:.2f} s")
+
+    hs = stats[head.name]
+    res = ssd_result(head, hs, plan[head.name])
+    res["roofline"]["per_launch"] = head.per_launch()
     line = {
         "metric": METRIC,
-        "value": round(ssd["tokens_per_s"], 1),
+        "value": res["value"],
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ssd["t"] * 1e3, 5),
+        "ms_per_step": round(hs["mean"] * 1e3, 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if shape.dtype == "bf16" else "f32",
-        "data": "synthetic (seeded; shapes and distributions of the named workload)",
-        "config": {"workload": f"{args.workload}: batch {shape.batch}, L={shape.seqlen}, "
-                               f"{shape.nheads} heads, P={shape.headdim}, S={shape.dstate}, "
-                               f"{shape.ngroups} group(s), chunk {shape.chunk}, {shape.dtype}",
-                   "global_batch": shape.batch, "seq_len": shape.seqlen, "parallelism": "single GPU",
-                   "buffer_sets": ssd["nsets"]},
-        "roofline": ssd["roofline"],
-        "autotune": ssd.get("autotune"),
+        "dtype": head.shape.dtype,
+        "data": "synthetic (seeded; shapes and value distributions of the named workload)",
+        "config": {"workload": head.describe(), "global_batch": head.shape.batch, "seq_len": head.shape.seqlen,
+                   "parallelism": "single GPU", "buffer_sets": head.nsets},
+        "timing": dict(res["timing"], warmup_gpu_ms=round(warm_s[head.name] * 1e3, 1)),
+        "roofline": res["roofline"],
+        "clocks": {"before": clocks_before, "after": clocks_after},
     }
-    if "cpu_baseline" in ssd:
-        line["cpu_baseline"] = ssd["cpu_baseline"]
-    if not args.no_scan:
-        line["linear_scan"] = bench_scan(args.scan_workload, args.steps, args.warmup, want_cpu)
-        line["linear_scan_three_pass"] = bench_scan3(args.scan_workload, args.steps, args.warmup,
-                                                     line["linear_scan"]["us_per_call"])
-        line["ssd_step"] = bench_step("decode_large", args.steps, args.warmup, want_cpu)
+    others = {}
+    for r in side:
+        st = stats[r.name]
+        if isinstance(r, SsdRunner):
+            o = ssd_result(r, st, plan[r.name])
+            o["roofline"]["per_launch"] = r.per_launch()
+        elif isinstance(r, StepRunner):
+            o = step_result(r, st, plan[r.name])
+        else:
+            o = scan_result(r, st, plan[r.name])
+        others[r.name] = o
+    if others:
+        line["workloads"] = {k: v for k, v in others.items() if k.startswith("ssd_") and k != "decode_large"}
+        sc = others["scan"]
+        sc["three_pass"] = others["scan:three_pass"]
+        sc["three_pass"]["time_ratio_to_single_pass"] = round(
+            stats["scan:three_pass"]["mean"] / stats["scan"]["mean"], 3)
+        sc["three_pass"]["traffic_model_ratio"] = round(7 / 3, 3)
+        sc["elementwise_ceiling"] = dict(others["scan:torch.mul"], kernel="torch.mul(a, b, out=h)",
+                                         scan_over_ceiling=round(stats["scan:torch.mul"]["mean"]
+                                                                 / stats["scan"]["mean"], 3))
+        sc["bf16"] = {"bf16_in_f32_out": others["scan:bf16->f32"], "bf16_in_bf16_out": others["scan:bf16->bf16"]}
+        sc["ragged"] = others["scan_ragged"]
+        sc["roofline"]["traffic"] = measured_traffic("linear_scan:scan", SCAN_SOURCES)
+        line["linear_scan"] = sc
+        step = next(r for r in side if isinstance(r, StepRunner))
+        so = others[step.name]
+        so["workload"] = (f"{step.name}: one decode token, batch {step.shape.batch}, {step.shape.nheads} heads, "
+                          f"P={step.shape.headdim}, S={step.shape.dstate}, {step.shape.ngroups} group(s), "
+                          f"{step.shape.dtype}")
+        so["tokens_per_s"] = round(step.shape.batch / stats[step.name]["mean"], 1)
+        so["roofline"]["traffic"] = measured_traffic("ssd_step:" + step.name, STEP_SOURCES)
+        line["ssd_step"] = so
+    if not args.no_autotune:
+        log("autotune comparison")
+        line["autotune"] = autotune_compare(head, max(args.steps // 2, NWIN), args.warmup)
+    if want_cpu:
+        log("cpu baselines")
+        line["cpu_baseline"] = cpu_baseline_ssd(head)
+        if others:
+            line["linear_scan"]["cpu_baseline"] = cpu_baseline_scan(next(r for r in side if r.name == "scan"))
+            line["ssd_step"]["cpu_baseline"] = cpu_baseline_step(next(r for r in side if isinstance(r, StepRunner)))
     print(json.dumps(line), flush=True)
+
+
+def scan_ceiling_sweep(steps, warmup):
+    """linear_scan against torch.mul(a, b, out=h), which moves the same bytes:
+    the row lengths of the page's table ("Selective-scan CUDA kernels",
+    section "Results": 96 MiB per array, L = 2048 ... 65536), then twice and
+    half that size at L = 65536, packed rows of 8186 and longer rows."""
+    import torch
+    import chunked_linear_scan_amd as cls
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev).manual_seed(1)
+    for rows, L in [(12288, 2048), (6144, 4096), (3072, 8192), (1536, 16384), (768, 32768), (384, 65536),
+                    (768, 65536), (192, 65536), (3072, 8186), (96, 262144), (24, 1048576)]:
+        sets = [(0.9 + 0.1 * torch.rand(rows, L, device=dev, generator=g),
+                 torch.randn(rows, L, device=dev, generator=g), torch.empty(rows, L, device=dev))
+                for _ in range(3)]
+        ws = torch.zeros(cls.load_library().linear_scan_workspace_size(rows, L), dtype=torch.uint8, device=dev)
+
+        class S(Runner):
+            name, nsets = "scan", 3
+
+            def step(self, i):
+                a, b, h = sets[i % 3]
+                cls.linear_scan(a, b, out=h, workspace=ws)
+
+        class M(Runner):
+            name, nsets = "mul", 3
+
+            def step(self, i):
+                a, b, h = sets[i % 3]
+                torch.mul(a, b, out=h)
+
+        rs = [S(), M()]
+        for r in rs:
+            warm(r, warmup)
+        n = split_steps(max(steps, NWIN), NWIN)
+        win = timed_windows(rs, {"scan": n, "mul": n})
+        ts, tm = summarize(win["scan"], n)["median"], summarize(win["mul"], n)["median"]
+        nb = 12 * rows * L
+        print(json.dumps({"rows": rows, "L": L, "scan_us": _us(ts), "scan_GBs": round(nb / ts / 1e9, 1),
+                          "mul_us": _us(tm), "mul_GBs": round(nb / tm / 1e9, 1),
+                          "mul_over_scan": round(tm / ts, 3)}), flush=True)
+        del sets, ws
 
 
 if __name__ == "__main__":

@@ -2,11 +2,13 @@
 //
 // Cross-workgroup communication (the decoupled look-back) follows the gfx942 /
 // gfx950 memory model: the L2 is per XCD and an agent-scope fence writes back
-// and invalidates it, which is slow.  Status words are therefore written and
-// read as single 16-byte accesses with the sc1 (device-coherent) cache policy,
-// so a flag and its payload always travel together and no agent fence is
-// needed for them.  Larger payloads are written with sc1 stores, completed
-// with a vmcnt wait, and only then announced by a flag store.
+// and invalidates it, which is slow.  Status words and payloads are
+// therefore written and read with relaxed agent-scope atomics of at most 64
+// bits (sc1, device coherent: single-copy atomic, and seen by every XCD
+// without a fence).  A status word of more than 64 bits is made of halves
+// that each carry its tag, and a reader accepts it only when the tags agree.
+// Larger payloads are written with such stores, completed with a vmcnt wait
+// and a workgroup barrier, and only then announced by a flag store.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -20,21 +22,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
-
-// ---------------------------------------------------------------------------
-// Device-coherent 16-byte status words.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ u32x4 load_coherent_b128(const void* p) {
-    u32x4 v;
-    asm volatile("global_load_dwordx4 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)"
-                 : "=v"(v) : "v"(p) : "memory");
-    return v;
-}
-
-__device__ __forceinline__ void store_coherent_b128(void* p, u32x4 v) {
-    asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)"
-                 : : "v"(p), "v"(v) : "memory");
-}
 
 // Payloads larger than a status word are written and read with compiler-
 // generated relaxed agent-scope 64-bit atomics (sc1, device coherent).  They

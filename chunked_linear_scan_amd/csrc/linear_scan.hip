@@ -177,12 +177,31 @@ __device__ __forceinline__ void store_items(uint16_t* __restrict__ p, int64_t i,
     }
 }
 
-// Status word of a tile: {kind, alpha, beta, 0} with kind 1 for the tile's own
-// aggregate and 2 for its inclusive prefix, which later overwrites the
-// aggregate in place; all-zero means not yet published.  A reader sees one or
-// the other whole, as the word is written and read as one 16-byte access.
-__device__ __forceinline__ u32x4 pack_status(uint32_t kind, Pair v) {
-    return u32x4{kind, as_uint(v.a), as_uint(v.b), 0u};
+// Status word of a tile: two 64-bit halves {kind, alpha} and {kind, beta},
+// kind 1 for the tile's own aggregate and 2 for its inclusive prefix, which
+// later overwrites the aggregate in place; 0 means not yet published.  Each
+// half is stored and loaded as one aligned 64-bit access (single-copy atomic
+// on this device), but the two halves are separate accesses: a reader may see
+// one half of the aggregate and the other of the prefix, or one published
+// half beside an unpublished one.  It takes the word only when both halves
+// carry the same nonzero kind, and polls again otherwise.
+struct Status {
+    uint32_t kind;
+    Pair v;
+};
+
+__device__ __forceinline__ void store_status(uint64_t* w, uint32_t kind, Pair v) {
+    __hip_atomic_store(w, uint64_t(kind) | (uint64_t(as_uint(v.a)) << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(w + 1, uint64_t(kind) | (uint64_t(as_uint(v.b)) << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ Status load_status(const uint64_t* w) {
+    const uint64_t lo = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t hi = __hip_atomic_load(w + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t k0 = uint32_t(lo), k1 = uint32_t(hi);
+    return Status{k0 == k1 ? k0 : 0u, Pair{as_float(uint32_t(lo >> 32)), as_float(uint32_t(hi >> 32)), 0}};
 }
 
 // DPP move of a float / int: lanes whose source lies outside the pattern (or
@@ -223,8 +242,8 @@ __device__ __forceinline__ Pair wave_inclusive_scan(Pair w) {
 
 // Exclusive prefix of tile j of a row: the ordered combination of tiles
 // 0..j-1.  Runs on one full wave; every lane returns the same value.
-// status_row holds one 16-byte status word per tile.
-__device__ Pair lookback(const u32x4* status_row, int j, uint32_t* err) {
+// status_row holds one status word (two 64-bit halves) per tile.
+__device__ Pair lookback(const uint64_t* status_row, int j, uint32_t* err) {
     const int lane = lane_id();
     Pair acc{1.0f, 0.0f, 0};  // combination of the predecessors already folded
     int base = j - 1;         // tile inspected by lane 0
@@ -236,10 +255,10 @@ __device__ Pair lookback(const u32x4* status_row, int j, uint32_t* err) {
         if (p < 0) {
             kind = 2;  // before the row start the state is 0: identity prefix
         } else {
-            const u32x4 w = load_coherent_b128(status_row + p);
-            kind = int(w[0]);
-            v.a = as_float(w[1]);
-            v.b = as_float(w[2]);
+            const Status w = load_status(status_row + 2 * int64_t(p));
+            kind = int(w.kind);
+            v.a = w.v.a;
+            v.b = w.v.b;
         }
         const uint64_t incm = __ballot(kind == 2);
         const uint64_t notready = __ballot(kind == 0);
@@ -277,7 +296,7 @@ template <bool SEGMENTED, typename TIn, typename TOut>
 __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
     const TIn* __restrict__ a, const TIn* __restrict__ b, TOut* __restrict__ h,
     int64_t rows, int64_t L, int tiles_per_row, int rows_per_tile,
-    uint32_t* __restrict__ claim, uint32_t* __restrict__ done, u32x4* __restrict__ status,
+    uint32_t* __restrict__ claim, uint32_t* __restrict__ done, uint64_t* __restrict__ status,
     uint32_t* __restrict__ err) {
     __shared__ uint32_t s_claim;
     __shared__ float s_wa[kLsWaves], s_wb[kLsWaves];
@@ -449,16 +468,16 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
     }
 
     // LS3: publish the aggregate, look back, publish the inclusive prefix.
-    u32x4* srow = status + row * int64_t(tiles_per_row);
+    uint64_t* srow = status + 2 * row * int64_t(tiles_per_row);
     if (!SEGMENTED) {
         if (wave == 0) {
             Pair prefix{1.0f, 0.0f, 0};
             if (!empty_tile) {
                 if (j > 0) {
-                    if (lane == 0) store_coherent_b128(srow + j, pack_status(1u, tile_agg));
+                    if (lane == 0) store_status(srow + 2 * j, 1u, tile_agg);
                     prefix = lookback(srow, j, err);
                 }
-                if (lane == 0) store_coherent_b128(srow + j, pack_status(2u, combine(prefix, tile_agg)));
+                if (lane == 0) store_status(srow + 2 * j, 2u, combine(prefix, tile_agg));
             }
             if (lane == 0) {
                 s_pa = prefix.a;
@@ -510,7 +529,8 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
         if (lane == 0) last = (atomic_add_u32(&done[row], 1u) == uint32_t(tiles_per_row - 1)) ? 1u : 0u;
         last = __builtin_amdgcn_readfirstlane(last);
         if (last) {
-            for (int q = lane; q < tiles_per_row; q += 64) store_coherent_b128(srow + q, u32x4{0u, 0u, 0u, 0u});
+            for (int q = lane; q < 2 * tiles_per_row; q += 64)
+                __hip_atomic_store(srow + q, uint64_t(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if (lane == 0) {
                 store_coherent_u32(&claim[row], 0u);
                 store_coherent_u32(&done[row], 0u);
@@ -533,7 +553,7 @@ void launch_typed(const void* a, const void* b, void* h, int64_t rows, int64_t L
     const TIn* ta = static_cast<const TIn*>(a);
     const TIn* tb = static_cast<const TIn*>(b);
     TOut* th = static_cast<TOut*>(h);
-    u32x4* st = reinterpret_cast<u32x4*>(status);
+    uint64_t* st = reinterpret_cast<uint64_t*>(status);
     if (segmented) {
         hipLaunchKernelGGL((linear_scan_kernel<true, TIn, TOut>), grid, block, 0, stream, ta, tb, th, rows, L,
                            tiles_per_row, rows_per_tile, claim, done, st, err);

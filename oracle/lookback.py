@@ -119,3 +119,105 @@ def lookback_scan(elements, combine, identity, tile, window=64, seed=0,
         else:  # stalled tile
             continue
     return out
+
+
+def lookback_scan_halves(pairs, combine, tile, window=64, seed=0, resident=8, check_tags=True,
+                         max_steps=10_000_000):
+    """The look-back protocol of ``lookback_scan`` with each status word
+    written and read as two halves, (tag, a) and (tag, b), where a and b are
+    the two parts of the scalar recurrence's affine pair and the tag is the
+    word's kind (0 unpublished, AGG, INC).
+
+    A writer stores the two halves in two separate steps, and a tile's
+    inclusive prefix later overwrites its aggregate in place; a reader loads
+    the halves of its window in two separate steps.  Any interleaving can
+    therefore show a reader one half of one publication and the other half of
+    another (a torn read).  With ``check_tags`` a word counts only when both
+    halves carry the same nonzero tag (otherwise it is read as not yet
+    published and polled again); ``check_tags=False`` is the broken variant
+    that trusts the first half's tag, which a torn read corrupts.
+    """
+    rng = random.Random(seed)
+    n = len(pairs)
+    ntiles = -(-n // tile)
+    halves = [[(EMPTY, None), (EMPTY, None)] for _ in range(ntiles)]
+    out = [None] * n
+    next_claim = 0
+    active = {}
+    steps = 0
+    done = 0
+
+    def local_scan(t):
+        acc = None
+        pref = []
+        for i in range(t * tile, min((t + 1) * tile, n)):
+            acc = pairs[i] if acc is None else combine(acc, pairs[i])
+            pref.append(acc)
+        return pref
+
+    while done < ntiles:
+        steps += 1
+        if steps > max_steps:
+            raise Deadlock(f"no progress after {max_steps} steps; waiting tiles {sorted(active)}")
+        while len(active) < resident and next_claim < ntiles:
+            active[next_claim] = {"phase": "scan"}
+            next_claim += 1
+        t = rng.choice(sorted(active))
+        st = active[t]
+        ph = st["phase"]
+        if ph == "scan":
+            st["local"] = local_scan(t)
+            st["pub"] = (INC if t == 0 else AGG, st["local"][-1], "half0")
+            st["prefix"] = None
+            st["phase"] = "publish"
+        elif ph == "publish":  # one half per step
+            kind, val, which = st["pub"]
+            if which == "half0":
+                halves[t][0] = (kind, val[0])
+                st["pub"] = (kind, val, "half1")
+            else:
+                halves[t][1] = (kind, val[1])
+                if kind == INC:
+                    st["phase"] = "apply"
+                else:
+                    st["phase"] = "read0"
+                    st["look"] = t - 1
+                    st["acc"] = None
+        elif ph == "read0":  # first halves of the window, nearest first
+            lo = max(st["look"] - window + 1, 0)
+            st["view"] = list(range(st["look"], lo - 1, -1))
+            st["w0"] = [halves[p][0] for p in st["view"]]
+            st["phase"] = "read1"
+        elif ph == "read1":  # second halves, at a later step
+            w1 = [halves[p][1] for p in st["view"]]
+            acc = st["acc"]
+            resolved = False
+            retry = False
+            for p, (t0, a), (t1, b) in zip(st["view"], st["w0"], w1):
+                kind = (t0 if t0 == t1 else EMPTY) if check_tags else t0
+                if kind == EMPTY:
+                    retry = True
+                    break
+                val = (a, b)
+                if kind == INC:
+                    prefix = val if acc is None else combine(val, acc)
+                    resolved = True
+                    break
+                acc = val if acc is None else combine(val, acc)
+            if resolved:
+                st["prefix"] = prefix
+                st["pub"] = (INC, combine(prefix, st["local"][-1]), "half0")
+                st["phase"] = "publish"
+            elif retry:
+                st["phase"] = "read0"  # poll again from the same place
+            else:
+                st["acc"] = acc
+                st["look"] = st["view"][-1] - 1
+                st["phase"] = "read0"
+        elif ph == "apply":
+            lo = t * tile
+            for k, v in enumerate(st["local"]):
+                out[lo + k] = v if st["prefix"] is None else combine(st["prefix"], v)
+            del active[t]
+            done += 1
+    return out

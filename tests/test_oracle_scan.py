@@ -130,3 +130,37 @@ def test_error_scale_of_cumsum():
     b = rng.standard_normal((3, 50))
     want = np.cumsum(np.cumsum(np.abs(b), axis=1), axis=1)
     np.testing.assert_allclose(scan.scan_error_scale(np.ones_like(b), b), want, rtol=1e-13)
+
+
+@pytest.mark.parametrize("tile,window,resident", [(8, 4, 6), (3, 64, 16), (16, 2, 3)])
+@pytest.mark.parametrize("seed", range(6))
+def test_lookback_with_torn_halves_matches_loop(tile, window, resident, seed):
+    """Status words written and read as two tagged halves at separate steps,
+    with inclusive prefixes overwriting aggregates in place: a reader that
+    accepts a word only when both halves carry the same tag gets the scan of
+    the loop under every interleaving."""
+    rng = np.random.default_rng(50 + seed)
+    a = rng.uniform(0.5, 1.0, 150)
+    b = rng.standard_normal(150)
+    out = lookback.lookback_scan_halves(_pairs(a, b), scan.combine, tile=tile, window=window, seed=seed,
+                                        resident=resident)
+    ref = scan.scan_loop(a[None], b[None])[0]
+    np.testing.assert_allclose([o[1] for o in out], ref, rtol=1e-12, atol=1e-12)
+
+
+def test_lookback_trusting_one_half_is_caught():
+    """The broken reader that trusts the first half's tag mixes two
+    publications (or a published half with an unpublished one)."""
+    rng = np.random.default_rng(7)
+    a = rng.uniform(0.5, 1.0, 200)
+    b = rng.standard_normal(200)
+    ref = scan.scan_loop(a[None], b[None])[0]
+    caught = 0
+    for seed in range(10):
+        try:
+            out = lookback.lookback_scan_halves(_pairs(a, b), scan.combine, tile=8, window=4, seed=seed,
+                                                resident=6, check_tags=False)
+            caught += not np.allclose([o[1] for o in out], ref, rtol=1e-9, atol=1e-9)
+        except TypeError:  # an unpublished half (None) reached the combine
+            caught += 1
+    assert caught >= 8
