@@ -106,6 +106,21 @@ int linear_scan(const float* a, const float* b, float* h, int64_t rows, int64_t 
     return linear_scan_launch(a, b, h, rows, length, 0, 0, workspace, workspace_bytes, stream);
 }
 
+int linear_scan_noalloc(const float* a, const float* b, float* h, int64_t rows, int64_t length, void* stream) {
+    if (!a || !b || !h) return SSD_ERR_NULL;
+    if (!scan_sizes_ok(rows, length)) return SSD_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(h)) return SSD_ERR_ALIGN;
+    const ScanPlan p = plan_scan(rows, length);
+    if (p.bytes > CLS_NOALLOC_SCAN_SCRATCH_BYTES) return SSD_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (cls_noalloc_scratch(&ws) != 0) return SSD_ERR_HIP;
+    // the array keeps whatever the last call left: clear the counters, the
+    // status words and the error word this call uses
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    if (cls_zero_fill(ws, round_up(p.bytes, 16), s) != 0) return SSD_ERR_HIP;
+    return linear_scan_launch(a, b, h, rows, length, 0, 0, ws, CLS_NOALLOC_SCAN_SCRATCH_BYTES, stream);
+}
+
 int linear_scan_typed(const void* a, const void* b, void* h, int64_t rows, int64_t length, int in_dtype,
                       int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
     if ((in_dtype != SSD_F32 && in_dtype != SSD_BF16) || (out_dtype != SSD_F32 && out_dtype != SSD_BF16))

@@ -43,7 +43,15 @@ struct SsdArgs {
     void* workspace;
 };
 
+// Size of the fixed device array behind linear_scan_noalloc.
+#define CLS_NOALLOC_SCAN_SCRATCH_BYTES (1u << 20)
+
 extern "C" {
+// Device address of the current device's fixed scratch array (looked up
+// once per device); 0 or -7.
+int cls_noalloc_scratch(void** ptr);
+// Zero `bytes` (a multiple of 16) at p with a store kernel on `stream`.
+int cls_zero_fill(void* p, size_t bytes, hipStream_t stream);
 // a, b: fp32 (in16 = 0) or bf16 (1); h: fp32 (out16 = 0) or bf16 (1).
 int cls_launch_linear_scan(const void* a, const void* b, void* h, int64_t rows, int64_t L, int in16, int out16,
                            int segmented, int tiles_per_row, int rows_per_tile, int64_t ntiles,

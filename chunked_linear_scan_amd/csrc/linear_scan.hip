@@ -36,6 +36,8 @@
 //     the load and rounded to nearest even once at the store; the scan
 //     itself is fp32 either way.
 #include "common.hpp"
+#include "device_once.hpp"
+#include "launch.hpp"
 
 namespace cls {
 
@@ -539,7 +541,47 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
     }
 }
 
+// Zero n16 16-byte words at p (a plain store kernel, so that a caller may
+// capture it in a graph; memset nodes are avoided there).
+__global__ __launch_bounds__(256) void zero_fill_kernel(u32x4* __restrict__ p, uint64_t n16) {
+    for (uint64_t i = uint64_t(blockIdx.x) * 256 + threadIdx.x; i < n16; i += uint64_t(gridDim.x) * 256)
+        p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
 }  // namespace cls
+
+// The workspace of linear_scan_noalloc: a fixed array in device memory that
+// each GPU holds for the life of the process (its address comes from
+// hipGetSymbolAddress; in host code this name is not a device address).
+static __device__ __align__(256) unsigned char scratch[CLS_NOALLOC_SCAN_SCRATCH_BYTES];
+
+// Device address of this device's scratch array, looked up once per device.
+extern "C" int cls_noalloc_scratch(void** ptr) {
+    static cls::DeviceOnce once;
+    static void* addr[cls::kMaxDevices];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= cls::kMaxDevices) return -7;
+    const int st = cls::run_once_per_device(once, [&] {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return -7;
+        addr[dev] = p;
+        return 0;
+    });
+    if (st != 0) return st;
+    *ptr = addr[dev];
+    return 0;
+}
+
+// Zero `bytes` (a multiple of 16) at p on `stream`.
+extern "C" int cls_zero_fill(void* p, size_t bytes, hipStream_t stream) {
+    const uint64_t n16 = bytes / 16;
+    if (n16 == 0) return 0;
+    const uint64_t blocks = (n16 + 255) / 256;
+    const dim3 grid{uint32_t(blocks < 1024 ? blocks : 1024), 1u, 1u};
+    const dim3 block{256u, 1u, 1u};
+    hipLaunchKernelGGL(cls::zero_fill_kernel, grid, block, 0, stream, static_cast<cls::u32x4*>(p), n16);
+    return hipGetLastError() == hipSuccess ? 0 : -7;
+}
 
 namespace {
 

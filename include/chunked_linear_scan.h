@@ -159,6 +159,25 @@ int linear_scan(const float* a, const float* b, float* h, int64_t rows,
                 void* stream);
 
 /*
+ * linear_scan for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same scan, kernels and results as linear_scan (bit for bit), with the
+ * workspace taken from a fixed 1 MiB array in device memory that the library
+ * holds on each GPU it runs on until the process ends, instead of a caller's
+ * buffer.  Nothing is allocated or freed.  Each call first clears the part of
+ * the array it uses with a store kernel on `stream`, then runs the scan.
+ * Shapes whose workspace (linear_scan_workspace_size) exceeds 1 MiB return
+ * SSD_ERR_WORKSPACE with nothing enqueued: rows of up to 8186 elements need
+ * none beyond a 256-byte header, longer rows need 16 bytes per 8192-element
+ * tile plus 8 bytes per row.  All calls on one GPU share its array: calls
+ * that may overlap on one GPU (other streams, other host threads) race and
+ * must be serialised by the caller.  Same layouts, alignment and status codes
+ * as linear_scan.
+ */
+int linear_scan_noalloc(const float* a, const float* b, float* h, int64_t rows,
+                        int64_t length, void* stream);
+
+/*
  * linear_scan with bf16 or fp32 elements.  The page's scan is fp32 only
  * ("Selective-scan CUDA kernels", section "Limitations"); this entry point
  * takes a and b as in_dtype and writes h as out_dtype, each SSD_F32 or

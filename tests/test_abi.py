@@ -27,7 +27,7 @@ def header_functions():
 def test_header_lists_expected_entry_points():
     assert set(header_functions()) == {
         "ssd_fwd_workspace_size", "ssd_fwd", "ssd_fwd_autotune", "ssd_fwd_plan", "ssd_fwd_autotune_reset",
-        "linear_scan_workspace_size", "linear_scan", "linear_scan_typed", "ssd_step", "linear_scan_three_pass_workspace_size", "linear_scan_three_pass", "ssd_strerror"}
+        "linear_scan_workspace_size", "linear_scan", "linear_scan_typed", "linear_scan_noalloc", "ssd_step", "linear_scan_three_pass_workspace_size", "linear_scan_three_pass", "ssd_strerror"}
 
 
 def test_library_exports_every_declared_symbol():
