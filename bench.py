@@ -597,6 +597,40 @@ def autotune_compare(r, steps, warmup):
             "speedup": round(tb["median"] / ta["median"], 3)}
 
 
+def s3_ab(steps, warmup, names=("ssd_large", "ssd_long")):
+    """The two inter-segment schemes of split chains timed against each other
+    on the workloads whose plans split chains: reduce-then-fold (aggregate
+    launch, then a fold at each segment start) and the single-pass look-back
+    (segments publish aggregates and look back), each at the built-in segment
+    count and at other counts, in interleaved windows.  One JSON line per
+    workload."""
+    import chunked_linear_scan_amd as cls
+
+    class Planned(Runner):
+        def __init__(self, base, name, plan):
+            self.base, self.name, self.plan, self.nsets = base, name, plan, base.nsets
+
+        def step(self, i):
+            d = self.base.sets[i % self.base.nsets]
+            cls.ssd_fwd_planned(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
+                                chunk=self.base.shape.chunk, out=d["y"], plan=self.plan)
+
+    for name in names:
+        base = SsdRunner(name)
+        runners = []
+        for nsegs in (0, 2, 4, 8, 16):
+            for s3 in ("reduce", "lookback"):
+                runners.append(Planned(base, f"{s3}:nsegs={nsegs or 'heuristic'}",
+                                       cls.plan_request(nsegs=nsegs, s3=s3)))
+        for r in runners:
+            warm(r, warmup)
+        n = split_steps(max(steps, NWIN), NWIN)
+        win = timed_windows(runners, {r.name: n for r in runners})
+        out = {r.name: _us(summarize(win[r.name], n)["median"]) for r in runners}
+        print(json.dumps({"workload": base.describe(), "median_us_per_call": out}), flush=True)
+        del base, runners
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -615,6 +649,9 @@ def main():
     ap.add_argument("--scan-ceiling-sweep", action="store_true",
                     help="time linear_scan and torch.mul (same traffic) over a sweep of row lengths, "
                          "print one JSON line per shape, then exit")
+    ap.add_argument("--s3-ab", action="store_true",
+                    help="time reduce-then-fold against the single-pass look-back for split chains "
+                         "(ssd_large, ssd_long), print one JSON line per workload, then exit")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write profiles/traffic.json from two rocprofv3 --pmc counter files of "
                          "--copy-probe runs (FETCH_SIZE, WRITE_SIZE) for --workload, then exit")
@@ -635,6 +672,9 @@ def main():
         sys.exit(1)
     if args.scan_ceiling_sweep:
         scan_ceiling_sweep(args.steps, args.warmup)
+        return
+    if args.s3_ab:
+        s3_ab(args.steps, args.warmup)
         return
     if args.copy_probe:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda:0")

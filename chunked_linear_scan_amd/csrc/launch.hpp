@@ -18,6 +18,7 @@ namespace cls {
 struct SegChoice {
     int64_t nsegs, nsplit;
     int64_t agg_d = 0;  // aggregate pieces per segment (0: the heuristic's)
+    int s3 = 0;         // inter-segment scheme (SSD_S3_*; 0: the built-in choice)
 };
 }  // namespace cls
 

@@ -32,8 +32,6 @@ int ssd_bf16_launch(int TT, int P, int S, const SsdBf16Params& prm, hipStream_t 
     }
 }
 
-constexpr int kXcds = 8;  // MI355X: 8 XCDs of 32 CUs
-
 // concurrent workgroups of the fused kernel: one per CU
 int64_t fused_slots() {
     int dev = 0, n = 0;
@@ -67,7 +65,7 @@ bool tuned_choice(const TuneKey& k, SegChoice* out) {
 // rounds of the CUs cut into 2..32 segments; every chain cut into 2..32
 // segments.  Plans of more than four rounds of workgroups are left out.
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
-                            int64_t chunk, int dtype, const SegChoice* force, int path);
+                            int64_t chunk, int dtype, const SegChoice* force, int path, int s3, int xcds);
 
 std::vector<SegChoice> seg_candidates(int64_t nchains, int64_t nc, int64_t slots) {
     std::vector<SegChoice> v{{1, 0}};
@@ -90,7 +88,7 @@ std::vector<SegChoice> seg_candidates(int64_t nchains, int64_t nc, int64_t slots
 // segment plan to use.  path: SSD_PATH_* of the call (SSD_PATH_CHUNK keeps
 // the fused path out).
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
-                            int64_t chunk, int dtype, const SegChoice* force, int path) {
+                            int64_t chunk, int dtype, const SegChoice* force, int path, int s3, int xcds) {
     SsdFusedPlan pl{};
     // The kernel's quadratic block is at most 128 tokens: a longer chunk is run
     // as sub-chunks of 128 with the state passed between them, which changes the
@@ -111,15 +109,18 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     // fill them.  A segment costs its output pass plus its share of the
     // aggregate launch (about half its length), which the split must beat.
     int64_t nsegs = 1, nsplit = 0, want_agg_d = 0;
+    int want_s3 = 0;
     SegChoice tuned{};
     if (force) {
         nsegs = force->nsegs;
         nsplit = (force->nsplit > 0 && force->nsplit < nchains) ? force->nsplit : nchains;
         want_agg_d = force->agg_d;
+        want_s3 = force->s3;
     } else if (tuned_choice(tune_key(batch, L, H, P, S, G, chunk, dtype), &tuned)) {
         nsegs = tuned.nsegs;
         nsplit = tuned.nsplit;
         want_agg_d = tuned.agg_d;
+        want_s3 = tuned.s3;
     } else {
         const int64_t slots = fused_slots();
         const int64_t r = nchains % slots;
@@ -147,7 +148,11 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
         agg_k = (k + agg_d - 1) / agg_d;
         agg_d = (k + agg_k - 1) / agg_k;
     }
-    const int64_t npieces = nsplit * (nsegs - 1) * agg_d;
+    // the inter-segment scheme: the call's request, else the plan's, else
+    // reduce-then-fold
+    const int scheme = s3 > 0 ? s3 : (want_s3 > 0 ? want_s3 : 1);
+    pl.lookback = nsplit > 0 && scheme == 2;
+    const int64_t npieces = pl.lookback ? 0 : nsplit * (nsegs - 1) * agg_d;
     if (ntiles >= (int64_t(1) << 24)) {
         pl.use = false;
         return pl;
@@ -161,11 +166,18 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     pl.agg_d = int(agg_d);
     pl.agg_chunks = int(agg_k);
     pl.npieces = int(npieces);
+    const int nx = xcds > 0 ? xcds : kXcds;
+    pl.nranges = int(nsplit < nx ? nsplit : nx);
     auto up = [](size_t v) { return (v + 255) / 256 * 256; };
-    pl.payload_off = 256;
-    // per aggregate piece: its state (fp32) and its decay
+    pl.payload_off = kSsdWsHeader;
+    // reduce-then-fold, per aggregate piece: its state (fp32) and its decay
     const size_t pay = size_t(npieces) * (size_t(ssd_fused_state_floats(int(S))) + 1) * 4;
-    pl.cb_off = pl.payload_off + up(pay);
+    // look-back, per segment: a status word, an aggregate and a prefix state, a decay
+    const size_t nseg = pl.lookback ? size_t(nsegs * nsplit) : 0;
+    pl.status_off = pl.payload_off + up(pay);
+    pl.segpay_off = pl.status_off + up(nseg * 8);
+    pl.alpha_off = pl.segpay_off + up(nseg * 2 * size_t(ssd_fused_state_floats(int(S))) * 4);
+    pl.cb_off = pl.alpha_off + up(nseg * 4);
     pl.bt_off = pl.cb_off + up(size_t(batch) * size_t(nc) * size_t(G) * size_t(TT) * TT * 2);
     pl.cf_off = pl.bt_off + up(size_t(batch) * size_t(nc) * size_t(G) * size_t(S) * TT * 2);
     pl.dtt_off = pl.cf_off + up(size_t(batch) * size_t(nc) * size_t(G) * size_t(S) * TT * 2);
@@ -175,7 +187,7 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
 
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
                             int64_t chunk, int dtype) {
-    return ssd_fused_plan(batch, L, H, P, S, G, chunk, dtype, nullptr, 0);
+    return ssd_fused_plan(batch, L, H, P, S, G, chunk, dtype, nullptr, 0, 0, 0);
 }
 
 }  // namespace cls
@@ -232,26 +244,25 @@ extern "C" size_t cls_ssd_workspace_bytes(const SsdShape& s) {
         size_t bytes = pl.bytes;
         for (const cls::SegChoice& c : fused_candidates(s)) {
             const cls::SsdFusedPlan q = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
-                                                            s.ngroups, s.chunk, s.dtype, &c, 0);
+                                                            s.ngroups, s.chunk, s.dtype, &c, 0, 0, 0);
             if (q.use && q.bytes > bytes) bytes = q.bytes;
         }
         return bytes;
     }
     const int64_t TT = cls::bf16_tile_tokens(int(s.chunk));
-    return size_t(s.batch) * size_t(nchunks(s)) * size_t(s.ngroups) * size_t(TT * TT) * 2 + 256;
+    return size_t(s.batch) * size_t(nchunks(s)) * size_t(s.ngroups) * size_t(TT * TT) * 2 + cls::kSsdWsHeader;
 }
 
 extern "C" size_t cls_ssd_plan_bytes(const SsdShape& s, const SsdLaunchOpts& o) {
     if (s.dtype == SSD_F32) return 0;
     const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
-                                                     s.ngroups, s.chunk, s.dtype, o.force, o.path);
+                                                     s.ngroups, s.chunk, s.dtype, o.force, o.path, o.s3, o.xcds);
     if (pl.use) return pl.bytes;
     const int64_t TT = cls::bf16_tile_tokens(int(s.chunk));
-    return size_t(s.batch) * size_t(nchunks(s)) * size_t(s.ngroups) * size_t(TT * TT) * 2 + 256;
+    return size_t(s.batch) * size_t(nchunks(s)) * size_t(s.ngroups) * size_t(TT * TT) * 2 + cls::kSsdWsHeader;
 }
 
 static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const SsdLaunchOpts& o, hipStream_t stream) {
-    if (o.s3 == 2) return SSD_ERR_UNSUPPORTED;  // the single-pass look-back is not built yet
     const cls::SegChoice* force = o.force;
     hipEvent_t* ev = o.ev;
     // single-launch paths record the call's four events around their launch
@@ -280,7 +291,7 @@ static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const SsdLaunchO
     p.h0 = a.h0;
     p.y = static_cast<uint16_t*>(a.y);
     p.h_final = a.h_final;
-    p.cb = reinterpret_cast<uint16_t*>(static_cast<char*>(a.workspace) + 256);
+    p.cb = reinterpret_cast<uint16_t*>(static_cast<char*>(a.workspace) + cls::kSsdWsHeader);
     p.batch = s.batch;
     p.L = s.seqlen;
     p.H = int(s.nheads);
@@ -288,7 +299,7 @@ static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const SsdLaunchO
     p.chunk = int(s.chunk);
     p.nchunks = int(nchunks(s));
     const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
-                                                     s.ngroups, s.chunk, s.dtype, force, o.path);
+                                                     s.ngroups, s.chunk, s.dtype, force, o.path, o.s3, o.xcds);
     if (pl.use) {
         p.chunk = pl.chunk;
         p.nchunks = int((s.seqlen + pl.chunk - 1) / pl.chunk);
@@ -326,6 +337,12 @@ static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const SsdLaunchO
         f.agg_d = pl.agg_d;
         f.agg_chunks = pl.agg_chunks;
         f.nxcd = o.xcds > 0 ? o.xcds : cls::kXcds;
+        f.lookback = pl.lookback ? 1 : 0;
+        f.nranges = pl.nranges > 0 ? pl.nranges : 1;
+        f.seg_ctl = reinterpret_cast<uint32_t*>(ws + cls::kSsdCtlOff);
+        f.seg_status = reinterpret_cast<uint64_t*>(ws + pl.status_off);
+        f.seg_pay = reinterpret_cast<float*>(ws + pl.segpay_off);
+        f.seg_alpha = reinterpret_cast<float*>(ws + pl.alpha_off);
         const int st = cls::ssd_fused_launch(pl.TT, int(s.dstate), p, f, stream, ev);
         if (st == -8) return SSD_ERR_UNSUPPORTED;
         return st == 0 ? SSD_OK : SSD_ERR_HIP;
@@ -371,7 +388,7 @@ extern "C" int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t
     std::vector<cls::SegChoice> plans;
     for (const cls::SegChoice& c : cands) {
         const cls::SsdFusedPlan q = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
-                                                        s.ngroups, s.chunk, s.dtype, &c, 0);
+                                                        s.ngroups, s.chunk, s.dtype, &c, 0, 0, 0);
         const cls::SegChoice ce{q.nsegs, q.nsegs > 1 ? int64_t(q.nchains - q.nwhole) : 0,
                                 q.nsegs > 1 ? int64_t(q.agg_d) : 0};
         bool dup = false;

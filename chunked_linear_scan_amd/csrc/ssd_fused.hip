@@ -194,6 +194,8 @@ static int launch_fused_tpl(const SsdBf16Params& cbp, const SsdFusedParams& fp, 
                                     hipFuncAttributeMaxDynamicSharedMemorySize, CbtLayout<TT, S>::BYTES) != hipSuccess ||
                 hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_kernel<TT, S>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, Lay::BYTES) != hipSuccess ||
+                hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_lb_kernel<TT, S>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, Lay::BYTES) != hipSuccess ||
                 hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_agg_kernel<TT, S>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, LayA::BYTES) != hipSuccess)
                    ? -7
@@ -201,7 +203,8 @@ static int launch_fused_tpl(const SsdBf16Params& cbp, const SsdFusedParams& fp, 
     });
     if (ast != 0) return ast;
     const int nst = fp.nsegs * (fp.nchains - fp.nwhole);              // segments
-    const int npieces = (fp.nchains - fp.nwhole) * (fp.nsegs - 1) * fp.agg_d;  // aggregate pieces
+    // aggregate pieces (none when split chains pass state by look-back)
+    const int npieces = fp.lookback ? 0 : (fp.nchains - fp.nwhole) * (fp.nsegs - 1) * fp.agg_d;
     const dim3 gcb{uint32_t(cbp.batch * cbp.nchunks * (cbp.G + 1)), 1u, 1u};  // + the dt workgroups
     const dim3 bcb{uint32_t(kBfThreads), 1u, 1u};
     const dim3 bmain{uint32_t(kFuThreads), 1u, 1u};
@@ -216,7 +219,10 @@ static int launch_fused_tpl(const SsdBf16Params& cbp, const SsdFusedParams& fp, 
     if (ev) (void)hipEventRecord(ev[2], stream);
     const dim3 gout{uint32_t(fp.nwhole + nst), 1u, 1u};
     const dim3 bout{uint32_t(kFuThreadsOut), 1u, 1u};
-    hipLaunchKernelGGL((ssd_fused_kernel<TT, S>), gout, bout, Lay::BYTES, stream, fp);
+    if (fp.lookback)
+        hipLaunchKernelGGL((ssd_fused_lb_kernel<TT, S>), gout, bout, Lay::BYTES, stream, fp);
+    else
+        hipLaunchKernelGGL((ssd_fused_kernel<TT, S>), gout, bout, Lay::BYTES, stream, fp);
     if (ev) (void)hipEventRecord(ev[3], stream);
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }

@@ -196,7 +196,7 @@ struct FuLayout {
     static constexpr int YO_OFF = Y_OFF + (AGG ? 0 : YBYTES);
     static constexpr int TB_OFF = YO_OFF + (AGG ? 0 : TT * 128);   // 2 x tables
     static constexpr int W_OFF = TB_OFF + 2 * TFLOATS * 4;         // 2 x diagonal weights
-    static constexpr int MISC_OFF = W_OFF + (AGG ? 0 : 2 * WBYTES);  // ints [4]
+    static constexpr int MISC_OFF = W_OFF + (AGG ? 0 : 2 * WBYTES);  // ints [16]
     static constexpr int BYTES = MISC_OFF + 64;
     static_assert(BYTES <= 160 * 1024, "LDS of one workgroup");
 };
@@ -241,10 +241,143 @@ __device__ __forceinline__ int fu_xcd_item(int i, int base, int n, int nx) {
     return start + (i - base - r) / nx;
 }
 
+// Tagged status word of segment `item` of a look-back call: the call's epoch,
+// the segment's index and its kind (1: its aggregate is published, 2: its
+// inclusive prefix is).  A word left by another call, another shape or other
+// data in the workspace never matches both the epoch and the index.
+__device__ __forceinline__ uint64_t fu_seg_tag(uint32_t epoch, int item, uint32_t kind) {
+    return (uint64_t(epoch) << 32) | (uint64_t(uint32_t(item)) << 2) | kind;
+}
+
+// Look-back over the earlier segments of a chain, on one 64-lane wave: lane l
+// inspects segment seg - 1 - l (item - 1 - l); the nearest inclusive prefix
+// is found with a ballot, and every segment between it and this one must
+// have published its aggregate.  A chain has at most 64 segments, so one
+// window always reaches its first segment, which publishes an inclusive
+// prefix.  Returns the segment index of that nearest prefix.  The wait is
+// bounded; giving up raises the error word and returns 0.
+__device__ __forceinline__ int fu_segment_lookback(const SsdFusedParams& p, int item, int seg, uint32_t epoch,
+                                                   int lane) {
+    const int pred = seg - 1 - lane;
+    const int it = item - 1 - lane;
+    uint32_t spins = 0;
+    while (true) {
+        uint32_t kind = 0;
+        if (pred >= 0) {
+            const uint64_t w = __hip_atomic_load(p.seg_status + it, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((w & ~uint64_t(3)) == fu_seg_tag(epoch, it, 0)) kind = uint32_t(w & 3u);
+        }
+        const uint64_t incm = __ballot(kind == 2u);
+        const uint64_t waiting = __ballot(pred >= 0 && kind == 0u);
+        const int kp = incm ? int(__builtin_ctzll(incm)) : 64;
+        const uint64_t nearer = kp >= 64 ? ~0ull : ((1ull << kp) - 1ull);
+        if (incm && !(waiting & nearer)) return seg - 1 - kp;
+        if (++spins > kFuSpinLimit) {
+            if (lane == 0) atomic_add_u32(p.err, 1u);
+            return 0;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+}
+
+// The inter-chunk state pass of a split chain's segment as a single-pass
+// decoupled look-back ("Selective-scan CUDA kernels", section "The five
+// kernels", levels 3 and 3b; the combine of section "The problem" with the
+// matrix state of "Accelerating Mamba-2 ...", section "Kernel 2:
+// fwd_pass_state"):
+//   * every segment but a chain's last runs its chunks once without outputs
+//     (the aggregate phase) and publishes its aggregate (alpha_k, S_k); the
+//     first segment starts that phase from h0, so it publishes its inclusive
+//     prefix P_0 directly;
+//   * wave 0 looks back for the nearest inclusive prefix P_j; all compute
+//     waves fold h <- alpha_i h + S_i over the aggregates after it, which
+//     gives the state at the segment's start;
+//   * a segment that has successors publishes P_k = alpha_k h + S_k.
+// Payloads are written with agent-scope 64-bit stores, completed (vmcnt
+// wait) and joined at a workgroup barrier before one thread writes the
+// status word; readers take payloads only after they have seen the word.
+// Aggregates and prefixes have separate payload slots, so a reader folding an
+// aggregate never races its replacement.  On return the compute waves hold
+// the state at the segment's start in hacc.
+template <int TT, int S, typename HArr, typename LoadH0, typename RunPhase>
+__device__ __forceinline__ void ssd_lookback_segment(const SsdFusedParams& p, int item, int seg, int nst, int wave,
+                                                     int lane, int tid, bool loader, HArr& hacc, float& sumG,
+                                                     int* lb_int, LoadH0& load_h0, RunPhase& run_phase) {
+    using Lay = FuLayout<TT, S>;
+    constexpr int NPW = Lay::NPW;
+    constexpr int NACC = Lay::NACC;
+    const uint32_t epoch = uint32_t(__builtin_amdgcn_readfirstlane(lb_int[5]));
+    const bool last = seg == p.nsegs - 1;
+    const int64_t slot = int64_t(kFuCompute) * NACC;
+    float* payA = p.seg_pay;
+    float* payP = p.seg_pay + int64_t(nst) * slot;
+    uint32_t* alpha = reinterpret_cast<uint32_t*>(p.seg_alpha);
+    if (!last) {
+        if (!loader) {
+            if (seg == 0) {
+                load_h0(hacc);
+            } else {
+#pragma unroll
+                for (int j = 0; j < NPW; ++j) hacc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+        run_phase(FuPhase<false>{});
+        if (!loader) {
+            float* dst = (seg == 0 ? payP : payA) + int64_t(item) * slot + tid * NACC;
+#pragma unroll
+            for (int j = 0; j < NPW; ++j) store_payload(dst + 4 * j, hacc[j]);
+            if (tid == 0 && seg > 0) store_coherent_u32(alpha + item, as_uint(fexp2(sumG)));
+            wait_vmem();
+        }
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(p.seg_status + item, fu_seg_tag(epoch, item, seg == 0 ? 2u : 1u), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (seg == 0) {
+        if (!loader) load_h0(hacc);  // the output pass starts from h0
+        return;
+    }
+    if (wave == 0) {
+        const int kp = fu_segment_lookback(p, item, seg, epoch, lane);
+        if (lane == 0) lb_int[6] = kp;
+    }
+    __syncthreads();
+    const int kp = __builtin_amdgcn_readfirstlane(lb_int[6]);
+    if (!loader) {
+        const int base = item - seg;  // this chain's first segment
+        const float* src = payP + int64_t(base + kp) * slot + tid * NACC;
+#pragma unroll
+        for (int j = 0; j < NPW; ++j) hacc[j] = load_payload(src + 4 * j);
+        for (int k = kp + 1; k < seg; ++k) {
+            const float al = as_float(load_coherent_u32(alpha + base + k));
+            const float* a = payA + int64_t(base + k) * slot + tid * NACC;
+#pragma unroll
+            for (int j = 0; j < NPW; ++j) hacc[j] = hacc[j] * al + load_payload(a + 4 * j);
+        }
+        if (!last) {
+            // this segment's inclusive prefix, from its own aggregate as published
+            // (this thread's own stores, read back)
+            const float ak = fexp2(sumG);
+            const float* own = payA + int64_t(item) * slot + tid * NACC;
+            float* dst = payP + int64_t(item) * slot + tid * NACC;
+#pragma unroll
+            for (int j = 0; j < NPW; ++j) store_payload(dst + 4 * j, hacc[j] * ak + load_payload(own + 4 * j));
+            wait_vmem();
+        }
+    }
+    if (!last) {
+        __syncthreads();
+        if (tid == 0)
+            __hip_atomic_store(p.seg_status + item, fu_seg_tag(epoch, item, 2u), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+}
+
 // AGG: the aggregate launch (one workgroup per segment of a split chain: its
 // state from zero and its decay); otherwise the output launch (whole chains,
 // then the segments of split chains from the folded aggregates).
-template <int TT, int S, bool AGG>
+template <int TT, int S, bool AGG, bool LB = false>
 __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
     using Lay = FuLayout<TT, S, AGG>;
     constexpr int NPW = Lay::NPW;
@@ -301,6 +434,29 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
         if (wg >= p.nwhole + nst) return;
         split = wg >= p.nwhole;
         item = split ? fu_xcd_item(wg, p.nwhole, nst, p.nxcd) : fu_xcd_item(wg, 0, p.nwhole, p.nxcd);
+        if (LB && split) {
+            // The segment is claimed, not assigned: range r holds whole split
+            // chains, its segments in chain order, so a segment's predecessors
+            // hold smaller claims of the same counter and are already running
+            // (or done) when it waits for them.  A workgroup starts at the range
+            // of its XCD and moves on when that range is used up.
+            if (tid == 0) {
+                const int r0 = (wg % p.nxcd) % p.nranges;
+                int got = -1;
+                for (int k = 0; k < p.nranges && got < 0; ++k) {
+                    const int r = (r0 + k) % p.nranges;
+                    const int cb = int(int64_t(nsplit) * r / p.nranges);
+                    const int ce = int(int64_t(nsplit) * (r + 1) / p.nranges);
+                    const uint32_t t = atomic_add_u32(p.seg_ctl + 16 + r, 1u);
+                    if (t < uint32_t((ce - cb) * p.nsegs)) got = cb * p.nsegs + int(t);
+                }
+                lb_int[4] = got;
+                lb_int[5] = int(load_coherent_u32(p.seg_ctl));  // this call's epoch
+            }
+            __syncthreads();
+            item = __builtin_amdgcn_readfirstlane(lb_int[4]);
+            if (item < 0) item = 0;  // unreachable: the grid has one workgroup per segment
+        }
         seg = split ? item % p.nsegs : 0;
         chain = split ? p.nwhole + item / p.nsegs : item;
         c_begin = split ? seg * p.seg_chunks : 0;
@@ -757,7 +913,7 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
             // Two blocks ahead measured no faster than one.  The output launch reads
             // them in the block itself: at 16 waves a wave has 128 registers, and the
             // prefetch set does not fit beside the operand rings.
-            constexpr int XD = OUT ? 0 : 1;
+            constexpr int XD = (OUT || LB) ? 0 : 1;
             u32x4 xs[XD + 1][4];
             fu_static_for<0, XD>([&](auto kc) {
                 constexpr int k = decltype(kc)::value;
@@ -881,6 +1037,15 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
                     run_state_loader();
                     return;
                 }
+            } else if constexpr (!AGG && LB) {
+                // a segment's own aggregate inside the output launch: the state
+                // loaders have nothing to do but meet the other waves' barriers
+                // (one before the first chunk and one per chunk)
+                if (sloader) {
+                    for (int c = c_begin; c <= c_end && c_begin < c_end; ++c) lds_barrier();
+                    __builtin_amdgcn_s_setprio(0);
+                    return;
+                }
             }
             run_loader(out_tag);
             if constexpr (!decltype(out_tag)::value) __builtin_amdgcn_s_setprio(0);
@@ -911,7 +1076,12 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
         if (tid == 0) pay_alpha[item] = fexp2(sumG);  // wave 0's (a compute wave)
         return;
     } else {
-        if (!loader) {
+        if (LB && split) {
+            // the state at the segment's start by look-back over the chain's
+            // earlier segments (this segment's own aggregate published first)
+            ssd_lookback_segment<TT, S>(p, item, seg, nst, wave, lane, tid, loader, hacc, sumG, lb_int,
+                                        load_h0, run_phase);
+        } else if (!loader) {
             load_h0(hacc);
             // a segment starts from h0 folded through the aggregates of the
             // pieces before it: h <- alpha_k h + S_k (the aggregate launch has
@@ -923,8 +1093,8 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
 #pragma unroll
                 for (int j = 0; j < NPW; ++j) hacc[j] = hacc[j] * al + *reinterpret_cast<const f32x4*>(src + 4 * j);
             }
-            store_hs(c_begin, l16, kg);
         }
+        if (!loader) store_hs(c_begin, l16, kg);
         lds_barrier();
         run_phase(FuPhase<true>{});
         if (p.h_final && (!split || seg == p.nsegs - 1) && !loader) {
@@ -932,6 +1102,18 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
             for (int j = 0; j < NPW; ++j)
                 *reinterpret_cast<f32x4*>(p.h_final + (bh * kFuP + 16 * (pt0 + j) + l16) * S + 16 * st + 4 * kg) =
                     hacc[j];
+        }
+        if (LB && split) {
+            // The last segment to finish resets the claim counters and the
+            // finish count and moves the epoch on, so the next call starts
+            // clean without any clearing launch (every segment has done its
+            // look-back reads before it counts itself finished).
+            __syncthreads();
+            if (tid == 0 && atomic_add_u32(p.seg_ctl + 1, 1u) == uint32_t(nst - 1)) {
+                for (int r = 0; r < p.nranges; ++r) store_coherent_u32(p.seg_ctl + 16 + r, 0u);
+                store_coherent_u32(p.seg_ctl + 1, 0u);
+                store_coherent_u32(p.seg_ctl, uint32_t(lb_int[5]) + 1u);
+            }
         }
     }
 }
@@ -942,6 +1124,14 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
 template <int TT, int S>
 __global__ __launch_bounds__(kFuThreadsOut) void ssd_fused_kernel(SsdFusedParams p) {
     ssd_fused_body<TT, S, false>(p);
+}
+
+// The output launch of plans whose split chains pass state by look-back: the
+// segments claim their work, run their own aggregate and look back (see
+// ssd_lookback_segment); whole chains run as in ssd_fused_kernel.
+template <int TT, int S>
+__global__ __launch_bounds__(kFuThreadsOut) void ssd_fused_lb_kernel(SsdFusedParams p) {
+    ssd_fused_body<TT, S, false, true>(p);
 }
 
 template <int TT, int S>

@@ -69,16 +69,37 @@ struct SsdFusedParams {
     int H, G, chunk, nchunks, seg_chunks, nsegs, nchains, nwhole;
     int agg_d, agg_chunks;
     int nxcd;  // XCDs the workgroups are dealt across (tile mapping only)
+    // Single-pass look-back over the segments of split chains (no aggregate
+    // launch).  The output launch's segment workgroups claim their segment
+    // from one counter per range of split chains, run the segment's own
+    // aggregate (all segments but a chain's last), publish it, look back over
+    // the chain's earlier segments and then run the output pass.
+    int lookback;        // 1: this scheme; 0: reduce-then-fold over the aggregate launch's pieces
+    int nranges;         // claim ranges: contiguous runs of whole split chains
+    uint32_t* seg_ctl;   // [0] epoch of the call, [1] finished segments, [16 + r] claims of range r
+    uint64_t* seg_status;  // [segments] tagged status words
+    float* seg_pay;      // [2][segments][compute threads][state floats per lane]: aggregates, prefixes
+    float* seg_alpha;    // [segments] decays of the aggregates
 };
 
 // Plan of the fused head-dim-64 path for one shape (also sizes its workspace).
 constexpr int64_t kFusedMaxChunk = 128;  // longest quadratic block of the fused kernel
 
+// The first bytes of every bf16 SSD workspace: the error word at 0 and the
+// look-back control words (epoch, finish count, claim counters) at
+// [kSsdCtlOff, kSsdWsHeader).  No plan puts data there, so the control words
+// stay valid whichever plans and shapes share a workspace.
+constexpr size_t kSsdCtlOff = 256;
+constexpr size_t kSsdWsHeader = 1024;
+
 struct SsdFusedPlan {
     bool use;
     int TT, chunk, nsegs, seg_chunks, nchains, nwhole;  // chunk: the sub-chunk the kernel runs
     int agg_d, agg_chunks, npieces;                     // aggregate pieces (see SsdFusedParams)
+    bool lookback;                                      // split chains: single-pass look-back
+    int nranges;                                        // look-back claim ranges
     size_t payload_off, cb_off, bt_off, cf_off, dtt_off, bytes;
+    size_t status_off, segpay_off, alpha_off;           // look-back status words and payloads
 };
 
 // Tile sizes of the bf16 path: the chunk is padded to a multiple of 32 tokens.
@@ -107,6 +128,7 @@ int ssd_fused_launch(int TT, int S, const SsdBf16Params& cbp, const SsdFusedPara
                      hipEvent_t* ev);
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
                             int64_t chunk, int dtype);
+constexpr int kXcds = 8;  // MI355X: 8 XCDs of 32 CUs
 int ssd_bf16_launch(int TT, int P, int S, const SsdBf16Params& prm, hipStream_t stream);
 
 }  // namespace cls

@@ -197,10 +197,15 @@ def test_one_state_one_channel_matches_linear_scan():
     assert compare.rel_l2(ys, h) < 1e-5
 
 
-@pytest.mark.parametrize("plan", [None, {"nsegs": 4, "nsplit": 5}], ids=["default", "split"])
+@pytest.mark.parametrize("plan", [None, {"nsegs": 4, "nsplit": 5}, {"nsegs": 4, "nsplit": 5, "s3": "lookback"},
+                                  {"nsegs": 16, "s3": "lookback"}],
+                         ids=["default", "split", "lookback", "lookback16"])
 def test_deterministic_100_runs(plan):
     """100 reruns are bit-identical, with whole chains and with split chains
-    (the aggregate launch and the fold at each segment start)."""
+    (reduce-then-fold: the aggregate launch and the fold at each segment
+    start; look-back: segments claimed in whatever order the workgroups run,
+    folding whatever their predecessors have published, which must not change
+    a bit of the result)."""
     inp = small_case(9, 2, 1024, 8, 64, 128, 2, torch.bfloat16)
     d = to_dev(inp)
     args = (d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"])
@@ -227,23 +232,27 @@ def test_full_workloads_whole(name):
     parity.check_ssd_workload(name, y, hf)
 
 
+@pytest.mark.parametrize("s3", ["reduce", "lookback"])
 @pytest.mark.parametrize("nsegs", [1, 2, 3, 7, 64])
-def test_segments_forced(nsegs):
-    """Every sequence split into segments whose start states come from the
-    aggregate launch's pieces, folded in order: one-chunk segments, uneven
-    segments and many segments."""
+def test_segments_forced(nsegs, s3):
+    """Every sequence split into segments: reduce-then-fold (start states from
+    the aggregate launch's pieces, folded in order) and the single-pass
+    look-back (each segment publishes its aggregate, then looks back over the
+    chain's earlier segments); one-chunk segments, uneven segments and many
+    segments (64: one look-back window reaches back to the first)."""
     inp = small_case(20 + nsegs, 2, 64 * 40 + 17, 3, 64, 128, 1, torch.bfloat16, dt_shift=-4.0)
-    run_and_check(inp, 32, f"nsegs={nsegs}", plan=cls.plan_request(nsegs=nsegs))
+    run_and_check(inp, 32, f"nsegs={nsegs} {s3}", plan=cls.plan_request(nsegs=nsegs, s3=s3))
 
 
+@pytest.mark.parametrize("s3", ["reduce", "lookback"])
 @pytest.mark.parametrize("nsegs,nsplit,chunk", [(2, 1, 128), (5, 4, 128), (4, 5, 32), (3, 2, 64)])
-def test_segment_mixed_whole_and_split(nsegs, nsplit, chunk):
+def test_segment_mixed_whole_and_split(nsegs, nsplit, chunk, s3):
     """Plans that run some (batch, head) chains whole and split the last
     `nsplit` chains into segments (the shape of the plan that fills the CUs
     left idle by a partial last round): both kinds of work item in one launch."""
     inp = small_case(60 + nsegs, 2, 64 * 40 + 17, 3, 64, 128, 1, torch.bfloat16, dt_shift=-4.0)
-    run_and_check(inp, chunk, f"mixed nsegs={nsegs} nsplit={nsplit} chunk={chunk}",
-                  plan=cls.plan_request(nsegs=nsegs, nsplit=nsplit))
+    run_and_check(inp, chunk, f"mixed nsegs={nsegs} nsplit={nsplit} chunk={chunk} {s3}",
+                  plan=cls.plan_request(nsegs=nsegs, nsplit=nsplit, s3=s3))
 
 
 @pytest.mark.parametrize("nsegs,pieces,chunk", [(3, 1, 64), (3, 5, 64), (4, 16, 32), (2, 40, 64), (5, 3, 128)])
@@ -257,25 +266,42 @@ def test_aggregate_pieces_forced(nsegs, pieces, chunk):
                   plan=cls.plan_request(nsegs=nsegs, agg_pieces=pieces))
 
 
-@pytest.mark.parametrize("xcds", [1, 3])
-def test_chain_mapping_over_xcds(xcds):
+@pytest.mark.parametrize("s3", ["reduce", "lookback"])
+@pytest.mark.parametrize("xcds", [1, 3, 64])
+def test_chain_mapping_over_xcds(xcds, s3):
     """The workgroup-to-chain mapping dealt over other XCD counts (1: plain
-    index order) runs the same chains."""
+    index order; for the look-back, that many claim ranges, or one per split
+    chain when there are fewer) runs the same chains."""
     inp = small_case(70 + xcds, 3, 700, 6, 64, 128, 2, torch.bfloat16)
-    run_and_check(inp, 128, f"xcds={xcds}", plan=cls.plan_request(nsegs=3, nsplit=7, xcds=xcds))
+    run_and_check(inp, 128, f"xcds={xcds} {s3}", plan=cls.plan_request(nsegs=3, nsplit=7, xcds=xcds, s3=s3))
+
+
+@pytest.mark.parametrize("name", ["ssd_large", "ssd_long"])
+def test_full_workloads_lookback(name):
+    """The two workloads whose plans split chains, with the split chains'
+    state passed by the single-pass look-back instead of reduce-then-fold;
+    every output compared."""
+    print(f"[ssd] {name} full size, look-back plan", flush=True)
+    inp = workloads.ssd_workload(name)
+    y, hf = gpu_run(inp, plan=cls.plan_request(s3="lookback"))
+    parity.check_ssd_workload(name, y, hf, label=f"{name} look-back")
 
 
 def test_explicit_workspace_error_word_stays_zero():
-    """A caller-owned workspace, reused over shapes and plans: the error word
-    at its start stays 0 (no bounded wait gave up)."""
+    """A caller-owned workspace, reused over shapes and plans (reduce-then-fold
+    and look-back, whose claim counters, finish count and epoch must be left
+    ready for the next call whatever ran in between): results match the
+    oracle and the error word at its start stays 0 (no bounded wait gave up)."""
     lib = cls.load_library()
-    shapes = [(2, 1000, 4, 2, 128), (1, 3000, 6, 3, 64), (2, 2000, 8, 1, 256)]
-    need = max(lib.ssd_fwd_planned_workspace_size(b, L, H, 64, 128, G, T, cls.SSD_BF16,
-                                                  cls.plan_request(nsegs=5)) for b, L, H, G, T in shapes)
+    shapes = [(2, 1000, 4, 2, 128), (1, 3000, 6, 3, 64), (2, 2000, 8, 1, 256), (1, 700, 4, 2, 32)]
+    plans = (None, cls.plan_request(nsegs=5), cls.plan_request(nsegs=5, s3="lookback"),
+             cls.plan_request(nsegs=3, nsplit=2, s3="lookback"))
+    need = max(lib.ssd_fwd_planned_workspace_size(b, L, H, 64, 128, G, T, cls.SSD_BF16, pl or cls.plan_request())
+               for b, L, H, G, T in shapes for pl in plans)
     ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
     for i, (b, L, H, G, T) in enumerate(shapes):
         inp = small_case(200 + i, b, L, H, 64, 128, G, torch.bfloat16)
-        for plan in (None, cls.plan_request(nsegs=5)):
+        for plan in plans:
             y, hf = gpu_run(inp, chunk=T, plan=plan, workspace=ws)
             parity.check_ssd(inp, y, hf, T, f"shared workspace {i}")
     assert cls.workspace_errors([ws]) == 0
