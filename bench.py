@@ -285,8 +285,8 @@ class ScanRunner(Runner):
         self.inp = workloads.scan_workload(name)
         rows, L = self.inp["a"].shape
         self.rows, self.L = rows, L
-        tin = torch.float32 if dtype_in == "f32" else torch.bfloat16
-        tout = torch.float32 if dtype_out == "f32" else torch.bfloat16
+        tdt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+        tin, tout = tdt[dtype_in], tdt[dtype_out]
         self.bytes_per_elem = 2 * (4 if dtype_in == "f32" else 2) + (4 if dtype_out == "f32" else 2)
         self.alg_bytes = self.bytes_per_elem * rows * L
         self.nsets = max(1, math.ceil((1 << 30) / self.alg_bytes))
@@ -298,6 +298,19 @@ class ScanRunner(Runner):
     def step(self, i):
         a, b, h = self.sets[i % self.nsets]
         self.cls.linear_scan(a, b, out=h, workspace=self.ws)
+
+
+class HillisSteeleRunner(ScanRunner):
+    """linear_scan_hillis_steele: the register-resident Hillis-Steele in-tile
+    scan, the page's fair comparison for the work-efficient kernel."""
+
+    def __init__(self, name):
+        super().__init__(name)
+        self.name = name + ":hillis_steele"
+
+    def step(self, i):
+        a, b, h = self.sets[i % self.nsets]
+        self.cls.linear_scan_hillis_steele(a, b, out=h, workspace=self.ws)
 
 
 class Scan3Runner(ScanRunner):
@@ -569,7 +582,9 @@ def autotune_compare(r, steps, warmup):
     d0 = r.sets[0]
     _, _, info = cls.ssd_fwd_autotune(d0["x"], d0["dt"], d0["A"], d0["B"], d0["C"], d0["D"], d0["h0"],
                                       chunk=s.chunk, reps=10, out=d0["y"])
-    tuned = cls.plan_request(nsegs=info["nsegs"], nsplit=info["nsplit"], agg_pieces=info["agg_pieces"]) \
+    base = min(s.chunk, 128)
+    tuned = cls.plan_request(nsegs=info["nsegs"], nsplit=info["nsplit"], agg_pieces=info["agg_pieces"],
+                             s3=info["s3"], sub_chunk=0 if info["sub_chunk"] == base else info["sub_chunk"]) \
         if info["nsegs"] > 0 else None
     cls.ssd_fwd_autotune_reset()
 
@@ -591,8 +606,9 @@ def autotune_compare(r, steps, warmup):
     n = split_steps(steps, NWIN)
     ws = timed_windows([a, b], {"tuned": n, "heuristic": n})
     ta, tb = summarize(ws["tuned"], n), summarize(ws["heuristic"], n)
-    return {"plan": {k: info[k] for k in ("nsegs", "nsplit", "agg_pieces")},
-            "heuristic_plan": {k: heur[k] for k in ("nsegs", "nsplit", "agg_pieces")},
+    keys = ("nsegs", "nsplit", "agg_pieces", "sub_chunk", "s3")
+    return {"plan": {k: info[k] for k in keys}, "heuristic_plan": {k: heur[k] for k in keys},
+            "tuner_ms_per_call": round(info["ms_per_call"], 4),
             "us_per_call_tuned": _us(ta["median"]), "us_per_call_heuristic": _us(tb["median"]),
             "speedup": round(tb["median"] / ta["median"], 3)}
 
@@ -697,8 +713,8 @@ def main():
             if name != args.workload:
                 side.append(SsdRunner(name))
         side += [ScanRunner("scan"), ScanRunner("scan_ragged"), ScanRunner("scan", "bf16", "f32"),
-                 ScanRunner("scan", "bf16", "bf16"), Scan3Runner("scan"), MulRunner("scan"),
-                 StepRunner("decode_large")]
+                 ScanRunner("scan", "bf16", "bf16"), ScanRunner("scan", "f16", "f32"), ScanRunner("scan", "f16", "f16"),
+                 HillisSteeleRunner("scan"), Scan3Runner("scan"), MulRunner("scan"), StepRunner("decode_large")]
     runners = [head] + side
     plan = {head.name: split_steps(args.steps, NWIN)}
     warm_s = {}
@@ -760,6 +776,9 @@ def main():
                                          scan_over_ceiling=round(stats["scan:torch.mul"]["mean"]
                                                                  / stats["scan"]["mean"], 3))
         sc["bf16"] = {"bf16_in_f32_out": others["scan:bf16->f32"], "bf16_in_bf16_out": others["scan:bf16->bf16"]}
+        sc["f16"] = {"f16_in_f32_out": others["scan:f16->f32"], "f16_in_f16_out": others["scan:f16->f16"]}
+        sc["hillis_steele"] = dict(others["scan:hillis_steele"], time_ratio_to_single_pass=round(
+            stats["scan:hillis_steele"]["mean"] / stats["scan"]["mean"], 3))
         sc["ragged"] = others["scan_ragged"]
         sc["roofline"]["traffic"] = measured_traffic("linear_scan:scan", SCAN_SOURCES)
         line["linear_scan"] = sc

@@ -21,7 +21,9 @@ LIB_PATH = os.path.join(_HERE, "libchunked_linear_scan.so")
 SSD_OK = 0
 SSD_F32 = 0
 SSD_BF16 = 1
-_DTYPE_CODE = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}
+SSD_F16 = 2
+_DTYPE_CODE = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16}           # SSD operands
+_SCAN_CODE = {torch.float32: SSD_F32, torch.bfloat16: SSD_BF16, torch.float16: SSD_F16}  # scan elements
 
 _lib = None
 _lib_lock = threading.Lock()
@@ -31,11 +33,12 @@ class PlanRequest(ctypes.Structure):
     """``ssd_plan_request`` of include/chunked_linear_scan_testing.h."""
     _fields_ = [("path", ctypes.c_int32), ("s3", ctypes.c_int32), ("nsegs", ctypes.c_int64),
                 ("nsplit", ctypes.c_int64), ("agg_pieces", ctypes.c_int64), ("xcds", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("sub_chunk", ctypes.c_int32)]
 
 
 PATH = {"auto": 0, "chunk": 1, "fused": 2}
 S3 = {"auto": 0, "reduce": 1, "lookback": 2}
+_S3_NAME = {0: None, 1: "reduce", 2: "lookback"}
 
 
 class SSDError(RuntimeError):
@@ -66,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.linear_scan.restype = ctypes.c_int
         lib.linear_scan_typed.argtypes = [vp, vp, vp, i64, i64, ctypes.c_int, ctypes.c_int, vp, sz, vp]
         lib.linear_scan_typed.restype = ctypes.c_int
+        lib.linear_scan_hillis_steele.argtypes = [fp, fp, fp, i64, i64, vp, sz, vp]
+        lib.linear_scan_hillis_steele.restype = ctypes.c_int
         lib.ssd_fwd_workspace_size.argtypes = [i64] * 7 + [ctypes.c_int]
         lib.ssd_fwd_workspace_size.restype = sz
         lib.ssd_fwd.argtypes = [vp, fp, fp, vp, vp, fp, fp] + [i64] * 7 + [ctypes.c_int, vp, fp, vp, sz, vp]
@@ -77,10 +82,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.ssd_step.argtypes = [fp, vp, fp, fp, vp, vp, fp] + [i64] * 5 + [ctypes.c_int, vp, vp]
         lib.ssd_step.restype = ctypes.c_int
         pi64 = ctypes.POINTER(ctypes.c_int64)
-        lib.ssd_fwd_autotune.argtypes = lib.ssd_fwd.argtypes + [ctypes.c_int, pi64, pi64, pi64,
+        pint = ctypes.POINTER(ctypes.c_int)
+        lib.ssd_fwd_autotune.argtypes = lib.ssd_fwd.argtypes + [ctypes.c_int, pi64, pi64, pi64, pi64, pint,
                                                                 ctypes.POINTER(ctypes.c_float)]
         lib.ssd_fwd_autotune.restype = ctypes.c_int
-        lib.ssd_fwd_plan.argtypes = [i64] * 7 + [ctypes.c_int, pi64, pi64, pi64]
+        lib.ssd_fwd_plan.argtypes = [i64] * 7 + [ctypes.c_int, pi64, pi64, pi64, pi64, pint]
         lib.ssd_fwd_plan.restype = ctypes.c_int
         lib.ssd_fwd_autotune_reset.argtypes = []
         lib.ssd_fwd_autotune_reset.restype = None
@@ -182,11 +188,11 @@ def linear_scan(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = Non
                 workspace: torch.Tensor | None = None, out_dtype: torch.dtype | None = None) -> torch.Tensor:
     """h[r, t] = a[r, t] h[r, t-1] + b[r, t] with h[r, -1] = 0, [rows, L].
 
-    a and b are both fp32 or both bf16; h is fp32 unless out (or out_dtype) is
-    bf16.  The scan runs in fp32 either way."""
+    a and b are both fp32, both bf16 or both fp16; h is fp32 unless out (or
+    out_dtype) is bf16 or fp16.  The scan runs in fp32 either way."""
     lib = load_library()
-    if a.dtype not in _DTYPE_CODE:
-        raise TypeError("a must be float32 or bfloat16")
+    if a.dtype not in _SCAN_CODE:
+        raise TypeError("a must be float32, bfloat16 or float16")
     _check_cuda("a", a, a.dtype)
     if a.dim() != 2:
         raise ValueError("a must be [rows, L]")
@@ -196,8 +202,8 @@ def linear_scan(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = Non
         h = torch.empty(a.shape, dtype=out_dtype or torch.float32, device=a.device)
     else:
         h = out
-    if h.dtype not in _DTYPE_CODE:
-        raise TypeError("out must be float32 or bfloat16")
+    if h.dtype not in _SCAN_CODE:
+        raise TypeError("out must be float32, bfloat16 or float16")
     _check_cuda("out", h, h.dtype, a.shape)
     need = lib.linear_scan_workspace_size(rows, length)
     if need == 0:
@@ -207,8 +213,8 @@ def linear_scan(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = Non
         st = lib.linear_scan(_ptr(a), _ptr(b), _ptr(h), rows, length, _ptr(ws), ws.numel(),
                              _stream_handle(a.device))
     else:
-        st = lib.linear_scan_typed(_ptr(a), _ptr(b), _ptr(h), rows, length, _DTYPE_CODE[a.dtype],
-                                   _DTYPE_CODE[h.dtype], _ptr(ws), ws.numel(), _stream_handle(a.device))
+        st = lib.linear_scan_typed(_ptr(a), _ptr(b), _ptr(h), rows, length, _SCAN_CODE[a.dtype],
+                                   _SCAN_CODE[h.dtype], _ptr(ws), ws.numel(), _stream_handle(a.device))
     if st != SSD_OK:
         raise SSDError(st, "linear_scan")
     return h
@@ -264,9 +270,10 @@ def ssd_fwd(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, want_final_state:
     return y, hf
 
 
-def plan_request(path="auto", s3="auto", nsegs=0, nsplit=0, agg_pieces=0, xcds=0) -> PlanRequest:
+def plan_request(path="auto", s3="auto", nsegs=0, nsplit=0, agg_pieces=0, xcds=0, sub_chunk=0) -> PlanRequest:
     """An explicit plan for ``ssd_fwd_planned`` (see the testing header)."""
-    return PlanRequest(PATH[path], S3[s3], int(nsegs), int(nsplit), int(agg_pieces), int(xcds), 0)
+    return PlanRequest(PATH[path], S3[s3 or "auto"], int(nsegs), int(nsplit), int(agg_pieces), int(xcds),
+                       int(sub_chunk))
 
 
 def ssd_fwd_planned(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, plan: PlanRequest | None = None,
@@ -297,37 +304,66 @@ def ssd_fwd_planned(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, plan: Pla
 def ssd_fwd_autotune(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, reps: int = 5,
                      want_final_state: bool = True, out: torch.Tensor | None = None,
                      workspace: torch.Tensor | None = None):
-    """Times ssd_fwd's candidate segment plans on these inputs and keeps the
-    fastest for this shape (later ssd_fwd calls use it).  Blocks until done.
-    Returns (y, h_final or None, {"nsegs", "nsplit", "agg_pieces", "ms_per_call"}); y and
-    h_final are the chosen plan's result.  nsegs == 0: nothing to tune."""
+    """Times ssd_fwd's candidate plans on these inputs against the built-in
+    heuristic's and keeps the fastest for this shape (later ssd_fwd calls use
+    it).  Blocks until done.  Returns (y, h_final or None, {"nsegs", "nsplit",
+    "agg_pieces", "sub_chunk", "s3", "ms_per_call"}); y and h_final are the
+    chosen plan's result.  nsegs == 0: nothing to tune."""
     lib = load_library()
     args, y, hf = _ssd_fwd_args(lib, x, dt, A, B, C, D, h0, chunk, want_final_state, out, workspace)
-    nsegs, nsplit, pieces, ms = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_float()
+    nsegs, nsplit, pieces, sub, ms = (ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(),
+                                      ctypes.c_float())
+    s3 = ctypes.c_int()
     st = lib.ssd_fwd_autotune(*args, int(reps), ctypes.byref(nsegs), ctypes.byref(nsplit), ctypes.byref(pieces),
-                              ctypes.byref(ms))
+                              ctypes.byref(sub), ctypes.byref(s3), ctypes.byref(ms))
     if st != SSD_OK:
         raise SSDError(st, "ssd_fwd_autotune")
     return y, hf, {"nsegs": nsegs.value, "nsplit": nsplit.value, "agg_pieces": pieces.value,
-                   "ms_per_call": ms.value}
+                   "sub_chunk": sub.value, "s3": _S3_NAME[s3.value], "ms_per_call": ms.value}
 
 
 def ssd_fwd_plan(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype=torch.bfloat16):
-    """The segment plan ssd_fwd uses for a shape: {"nsegs", "nsplit",
-    "agg_pieces", "source": "tuned" | "heuristic" | "none"}.  Launches nothing."""
+    """The plan ssd_fwd uses for a shape: {"nsegs", "nsplit", "agg_pieces",
+    "sub_chunk", "s3", "source": "tuned" | "heuristic" | "none"}.  Launches
+    nothing."""
     lib = load_library()
-    nsegs, nsplit, pieces = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    nsegs, nsplit, pieces, sub = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    s3 = ctypes.c_int()
     st = lib.ssd_fwd_plan(batch, seqlen, nheads, headdim, dstate, ngroups, int(chunk), _DTYPE_CODE[dtype],
-                          ctypes.byref(nsegs), ctypes.byref(nsplit), ctypes.byref(pieces))
+                          ctypes.byref(nsegs), ctypes.byref(nsplit), ctypes.byref(pieces), ctypes.byref(sub),
+                          ctypes.byref(s3))
     if st < 0:
         raise SSDError(st, "ssd_fwd_plan")
-    return {"nsegs": nsegs.value, "nsplit": nsplit.value, "agg_pieces": pieces.value,
-            "source": {0: "heuristic", 1: "tuned", 2: "none"}[st]}
+    return {"nsegs": nsegs.value, "nsplit": nsplit.value, "agg_pieces": pieces.value, "sub_chunk": sub.value,
+            "s3": _S3_NAME[s3.value], "source": {0: "heuristic", 1: "tuned", 2: "none"}[st]}
 
 
 def ssd_fwd_autotune_reset():
     """Forget every tuned plan (ssd_fwd falls back to its built-in heuristic)."""
     load_library().ssd_fwd_autotune_reset()
+
+
+def linear_scan_hillis_steele(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None,
+                              workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """The same scan (fp32) with a register-resident Hillis-Steele scan inside
+    each tile (the work-inefficient comparison kernel)."""
+    lib = load_library()
+    _check_cuda("a", a, torch.float32)
+    if a.dim() != 2:
+        raise ValueError("a must be [rows, L]")
+    _check_cuda("b", b, torch.float32, a.shape)
+    rows, length = a.shape
+    h = torch.empty_like(a) if out is None else out
+    _check_cuda("out", h, torch.float32, a.shape)
+    need = lib.linear_scan_workspace_size(rows, length)
+    if need == 0:
+        raise SSDError(-2, "linear_scan_workspace_size")
+    ws = _scan_ws.get(a.device, _stream_key(a.device), need) if workspace is None else workspace
+    st = lib.linear_scan_hillis_steele(_ptr(a), _ptr(b), _ptr(h), rows, length, _ptr(ws), ws.numel(),
+                                       _stream_handle(a.device))
+    if st != SSD_OK:
+        raise SSDError(st, "linear_scan_hillis_steele")
+    return h
 
 
 def linear_scan_three_pass(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
@@ -383,6 +419,6 @@ def ssd_step(h, x, dt, A, B, C, D=None, out: torch.Tensor | None = None):
     return y
 
 
-__all__ = ["linear_scan", "linear_scan_three_pass", "ssd_fwd", "ssd_fwd_autotune", "ssd_fwd_plan",
+__all__ = ["linear_scan", "linear_scan_hillis_steele", "linear_scan_three_pass", "ssd_fwd", "ssd_fwd_autotune", "ssd_fwd_plan",
            "ssd_fwd_autotune_reset", "ssd_fwd_planned", "plan_request", "ssd_step", "load_library", "strerror",
-           "workspace_errors", "SSDError", "LIB_PATH", "SSD_F32", "SSD_BF16"]
+           "workspace_errors", "SSDError", "LIB_PATH", "SSD_F32", "SSD_BF16", "SSD_F16"]

@@ -86,19 +86,20 @@ size_t linear_scan_workspace_size(int64_t rows, int64_t length) {
     return plan_scan(rows, length).bytes;
 }
 
-static int linear_scan_launch(const void* a, const void* b, void* h, int64_t rows, int64_t length, int in16,
-                              int out16, void* workspace, size_t workspace_bytes, void* stream) {
+// in_fmt / out_fmt: 0 fp32, 1 bf16, 2 fp16; hs: the Hillis-Steele in-tile scan
+static int linear_scan_launch(const void* a, const void* b, void* h, int64_t rows, int64_t length, int in_fmt,
+                              int out_fmt, void* workspace, size_t workspace_bytes, void* stream, int hs = 0) {
     if (!a || !b || !h || !workspace) return SSD_ERR_NULL;
     if (!scan_sizes_ok(rows, length)) return SSD_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(b) || !aligned16(h) || !aligned16(workspace)) return SSD_ERR_ALIGN;
     const ScanPlan p = plan_scan(rows, length);
     if (workspace_bytes < p.bytes) return SSD_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
-    return cls_launch_linear_scan(a, b, h, rows, length, in16, out16, p.segmented ? 1 : 0, int(p.tiles_per_row),
+    return cls_launch_linear_scan(a, b, h, rows, length, in_fmt, out_fmt, p.segmented ? 1 : 0, int(p.tiles_per_row),
                                   int(p.rows_per_tile), p.ntiles,
                                   reinterpret_cast<uint32_t*>(ws + p.claim_off),
                                   reinterpret_cast<uint32_t*>(ws + p.done_off), ws + p.status_off,
-                                  reinterpret_cast<uint32_t*>(ws), static_cast<hipStream_t>(stream));
+                                  reinterpret_cast<uint32_t*>(ws), static_cast<hipStream_t>(stream), hs);
 }
 
 int linear_scan(const float* a, const float* b, float* h, int64_t rows, int64_t length,
@@ -123,10 +124,15 @@ int linear_scan_noalloc(const float* a, const float* b, float* h, int64_t rows, 
 
 int linear_scan_typed(const void* a, const void* b, void* h, int64_t rows, int64_t length, int in_dtype,
                       int out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-    if ((in_dtype != SSD_F32 && in_dtype != SSD_BF16) || (out_dtype != SSD_F32 && out_dtype != SSD_BF16))
-        return SSD_ERR_DTYPE;
-    return linear_scan_launch(a, b, h, rows, length, in_dtype == SSD_BF16 ? 1 : 0, out_dtype == SSD_BF16 ? 1 : 0,
-                              workspace, workspace_bytes, stream);
+    auto fmt = [](int d) { return d == SSD_F32 ? 0 : d == SSD_BF16 ? 1 : d == SSD_F16 ? 2 : -1; };
+    if (fmt(in_dtype) < 0 || fmt(out_dtype) < 0) return SSD_ERR_DTYPE;
+    return linear_scan_launch(a, b, h, rows, length, fmt(in_dtype), fmt(out_dtype), workspace, workspace_bytes,
+                              stream);
+}
+
+int linear_scan_hillis_steele(const float* a, const float* b, float* h, int64_t rows, int64_t length,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+    return linear_scan_launch(a, b, h, rows, length, 0, 0, workspace, workspace_bytes, stream, 1);
 }
 
 size_t ssd_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
@@ -169,12 +175,15 @@ static bool plan_options(const ssd_plan_request* plan, cls::SegChoice* seg, SsdL
     if (plan->s3 < SSD_S3_AUTO || plan->s3 > SSD_S3_LOOKBACK) return false;
     if (plan->nsegs < 0 || plan->nsegs > 64 || plan->nsplit < 0 || plan->agg_pieces < 0) return false;
     if (plan->agg_pieces > (int64_t(1) << 20) || plan->nsplit > (int64_t(1) << 31)) return false;
-    if (plan->xcds < 0 || plan->xcds > 64 || plan->reserved != 0) return false;
+    if (plan->xcds < 0 || plan->xcds > 64) return false;
+    if (plan->sub_chunk != 0 && plan->sub_chunk != 32 && plan->sub_chunk != 64) return false;
     o->path = plan->path;
     o->s3 = plan->s3;
     o->xcds = plan->xcds;
     if (plan->nsegs > 0) {
         *seg = cls::SegChoice{plan->nsegs, plan->nsplit, plan->agg_pieces};
+        seg->s3 = plan->s3;
+        seg->sub = plan->sub_chunk;
         o->force = seg;
     }
     return true;
@@ -220,24 +229,26 @@ int ssd_fwd_autotune(const void* x, const float* dt, const float* A, const void*
                      const float* D, const float* h0, int64_t batch, int64_t seqlen, int64_t nheads,
                      int64_t headdim, int64_t dstate, int64_t ngroups, int64_t chunk, int dtype, void* y,
                      float* h_final, void* workspace, size_t workspace_bytes, void* stream, int reps,
-                     int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces, float* ms_per_call) {
-    if (!nsegs || !nsplit || !agg_pieces || !ms_per_call) return SSD_ERR_NULL;
+                     int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces, int64_t* sub_chunk, int* s3,
+                     float* ms_per_call) {
+    if (!nsegs || !nsplit || !agg_pieces || !sub_chunk || !s3 || !ms_per_call) return SSD_ERR_NULL;
     if (reps < 1 || reps > 1000) return SSD_ERR_SHAPE;
     const SsdShape s{batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype};
     const SsdArgs args{x, dt, A, B, C, D, h0, y, h_final, workspace};
     const int st = ssd_fwd_validate(s, args, workspace_bytes);
     if (st != SSD_OK) return st;
-    return cls_ssd_autotune(s, args, static_cast<hipStream_t>(stream), reps, nsegs, nsplit, agg_pieces,
-                            ms_per_call);
+    return cls_ssd_autotune(s, args, static_cast<hipStream_t>(stream), reps, nsegs, nsplit, agg_pieces, sub_chunk,
+                            s3, ms_per_call);
 }
 
 int ssd_fwd_plan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
-                 int64_t chunk, int dtype, int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces) {
-    if (!nsegs || !nsplit || !agg_pieces) return SSD_ERR_NULL;
+                 int64_t chunk, int dtype, int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces, int64_t* sub_chunk,
+                 int* s3) {
+    if (!nsegs || !nsplit || !agg_pieces || !sub_chunk || !s3) return SSD_ERR_NULL;
     const SsdShape s{batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype};
     const int st = cls_ssd_check(s);
     if (st != SSD_OK) return st;
-    return cls_ssd_plan_query(s, nsegs, nsplit, agg_pieces);
+    return cls_ssd_plan_query(s, nsegs, nsplit, agg_pieces, sub_chunk, s3);
 }
 
 void ssd_fwd_autotune_reset(void) { cls_ssd_autotune_reset(); }

@@ -19,6 +19,7 @@ struct SegChoice {
     int64_t nsegs, nsplit;
     int64_t agg_d = 0;  // aggregate pieces per segment (0: the heuristic's)
     int s3 = 0;         // inter-segment scheme (SSD_S3_*; 0: the built-in choice)
+    int64_t sub = 0;    // sub-chunk the kernel runs (0: the chunk, at most 128)
 };
 }  // namespace cls
 
@@ -53,11 +54,12 @@ extern "C" {
 int cls_noalloc_scratch(void** ptr);
 // Zero `bytes` (a multiple of 16) at p with a store kernel on `stream`.
 int cls_zero_fill(void* p, size_t bytes, hipStream_t stream);
-// a, b: fp32 (in16 = 0) or bf16 (1); h: fp32 (out16 = 0) or bf16 (1).
-int cls_launch_linear_scan(const void* a, const void* b, void* h, int64_t rows, int64_t L, int in16, int out16,
+// a, b and h: fp32 (format 0), bf16 (1) or fp16 (2); hs = 1: the
+// Hillis-Steele in-tile scan (fp32 only).
+int cls_launch_linear_scan(const void* a, const void* b, void* h, int64_t rows, int64_t L, int in_fmt, int out_fmt,
                            int segmented, int tiles_per_row, int rows_per_tile, int64_t ntiles,
                            uint32_t* claim, uint32_t* done, void* status, uint32_t* err,
-                           hipStream_t stream);
+                           hipStream_t stream, int hs);
 
 // Shape/dtype/chunk validation shared by sizing and launching (SSD_OK or a
 // negative status).
@@ -70,10 +72,11 @@ size_t cls_ssd_plan_bytes(const SsdShape& s, const SsdLaunchOpts& o);
 // Times the fused path's candidate segment plans on these arguments, keeps the
 // fastest for the shape and leaves its result in y / h_final (blocking).
 int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t stream, int reps, int64_t* nsegs,
-                     int64_t* nsplit, int64_t* agg_pieces, float* ms);
+                     int64_t* nsplit, int64_t* agg_pieces, int64_t* sub_chunk, int* s3, float* ms);
 // The segment plan ssd_fwd uses for a shape: 1 tuned, 0 heuristic, 2 no plan
 // (not the fused path); negative status on error.
-int cls_ssd_plan_query(const SsdShape& s, int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces);
+int cls_ssd_plan_query(const SsdShape& s, int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces, int64_t* sub_chunk,
+                       int* s3);
 void cls_ssd_autotune_reset();
 // Three-pass linear scan (linear_scan_3pass.hip); shapes already validated.
 size_t cls_ls3_workspace_bytes(int64_t rows, int64_t L);

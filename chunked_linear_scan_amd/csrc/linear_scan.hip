@@ -65,15 +65,45 @@ __device__ __forceinline__ Pair combine(Pair f, Pair s) {
     return Pair{f.a * s.a, fmaf(s.a, f.b, s.b), f.f};
 }
 
-// Items per lane and step: 4 fp32 (one 16-byte load) or 8 bf16 (one 16-byte
-// load), so every wave-wide load covers 1 KB of consecutive memory.
+// 16-bit element formats: raw bits, two to a 32-bit word (the earlier item in
+// the low half).  Items are widened to fp32 exactly and results rounded to
+// nearest even once.
+struct bf16_t {
+    uint16_t v;
+};
+struct f16_t {
+    uint16_t v;
+};
 template <typename T>
-struct ItemsPerLane {
-    static constexpr int value = 4;
+struct Fmt16;
+template <>
+struct Fmt16<bf16_t> {
+    static constexpr uint32_t one = 0x3f80u;  // 1.0
+    __device__ static float lo(uint32_t w) { return bf16_lo(w); }
+    __device__ static float hi(uint32_t w) { return bf16_hi(w); }
+    __device__ static uint32_t pack(float a, float b) { return pack_bf16x2(a, b); }
 };
 template <>
-struct ItemsPerLane<uint16_t> {
-    static constexpr int value = 8;
+struct Fmt16<f16_t> {
+    static constexpr uint32_t one = 0x3c00u;  // 1.0
+    __device__ static float lo(uint32_t w) { return float(__builtin_bit_cast(_Float16, uint16_t(w & 0xffffu))); }
+    __device__ static float hi(uint32_t w) { return float(__builtin_bit_cast(_Float16, uint16_t(w >> 16))); }
+    // The fp32 values are pinned in registers first: otherwise the compiler
+    // fuses the producing fma with the conversion (v_fma_mixlo_f16), which
+    // rounds the exact product-sum to fp16 once instead of rounding the fp32
+    // result, and differs from it at fp32 values that are exact fp16 ties.
+    __device__ static uint32_t pack(float a, float b) {
+        asm volatile("" : "+v"(a), "+v"(b));
+        return uint32_t(__builtin_bit_cast(uint16_t, _Float16(a))) |
+               (uint32_t(__builtin_bit_cast(uint16_t, _Float16(b))) << 16);
+    }
+};
+
+// Items per lane and step: 4 fp32 (one 16-byte load) or 8 16-bit items (one
+// 16-byte load), so every wave-wide load covers 1 KB of consecutive memory.
+template <typename T>
+struct ItemsPerLane {
+    static constexpr int value = sizeof(T) == 2 ? 8 : 4;
 };
 
 // 16-byte vectors at 8-byte aligned addresses (bf16 rows start on a 4-item
@@ -97,28 +127,12 @@ __device__ __forceinline__ void load_items(const float* __restrict__ p, int64_t 
     }
 }
 
-__device__ __forceinline__ void load_items(const uint16_t* __restrict__ p, int64_t i, int64_t lo, int64_t hi,
-                                           float ident, float (&v)[8]) {
-    if (i >= lo && i + 8 <= hi) {
-        const u32x4a8 w = __builtin_nontemporal_load(reinterpret_cast<const u32x4a8*>(p + i));
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            v[2 * k] = bf16_lo(w[k]);
-            v[2 * k + 1] = bf16_hi(w[k]);
-        }
-        return;
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        const int64_t e = i + k;
-        v[k] = (e >= lo && e < hi) ? __builtin_bit_cast(float, uint32_t(p[e]) << 16) : ident;
-    }
-}
-
-// Items i .. i+7 of p as raw bf16 bits, two per word (item 2k in the low
-// half of word k); positions outside [lo, hi) hold `ident` (bf16 bits).
-__device__ __forceinline__ u32x4a8 load_raw8(const uint16_t* __restrict__ p, int64_t i, int64_t lo, int64_t hi,
+// Items i .. i+7 of p as raw 16-bit words, two per word (item 2k in the low
+// half of word k); positions outside [lo, hi) hold `ident` (raw bits).
+template <typename T>
+__device__ __forceinline__ u32x4a8 load_raw8(const T* __restrict__ pt, int64_t i, int64_t lo, int64_t hi,
                                             uint32_t ident) {
+    const uint16_t* p = reinterpret_cast<const uint16_t*>(pt);
     if (i >= lo && i + 8 <= hi) return __builtin_nontemporal_load(reinterpret_cast<const u32x4a8*>(p + i));
     u32x4a8 w{0u, 0u, 0u, 0u};
 #pragma unroll
@@ -130,8 +144,9 @@ __device__ __forceinline__ u32x4a8 load_raw8(const uint16_t* __restrict__ p, int
     return w;
 }
 
+template <typename T>
 __device__ __forceinline__ float raw_item(const u32x4a8& w, int k) {
-    return (k & 1) ? bf16_hi(w[k / 2]) : bf16_lo(w[k / 2]);
+    return (k & 1) ? Fmt16<T>::hi(w[k / 2]) : Fmt16<T>::lo(w[k / 2]);
 }
 
 // Unchecked forms for tiles that lie wholly inside [lo, hi).
@@ -159,12 +174,13 @@ __device__ __forceinline__ void store_items(float* __restrict__ p, int64_t i, in
     }
 }
 
-template <int N>
-__device__ __forceinline__ void store_items(uint16_t* __restrict__ p, int64_t i, int64_t lo, int64_t hi,
+template <int N, typename T>
+__device__ __forceinline__ void store_items(T* __restrict__ pt, int64_t i, int64_t lo, int64_t hi,
                                             const float (&v)[N], bool full = false) {
+    uint16_t* p = reinterpret_cast<uint16_t*>(pt);
     uint32_t w[N / 2];
 #pragma unroll
-    for (int k = 0; k < N / 2; ++k) w[k] = pack_bf16x2(v[2 * k], v[2 * k + 1]);
+    for (int k = 0; k < N / 2; ++k) w[k] = Fmt16<T>::pack(v[2 * k], v[2 * k + 1]);
     if (full || (i >= lo && i + N <= hi)) {
         if constexpr (N == 8)
             __builtin_nontemporal_store(u32x4a8{w[0], w[1], w[2], w[3]}, reinterpret_cast<u32x4a8*>(p + i));
@@ -294,7 +310,49 @@ __device__ Pair lookback(const uint64_t* status_row, int j, uint32_t* err) {
 // row start (rows no longer than a tile); otherwise each tile belongs to one
 // row and the row's tiles chain through the look-back.  TIn / TOut: float
 // (fp32) or uint16_t (bf16 bits).
-template <bool SEGMENTED, typename TIn, typename TOut>
+// Register-resident Hillis-Steele scan of one step's 64 x 4 items (item k of
+// lane l is element 4 l + k): at distance d = 1, 2, 4, ..., 128 every element
+// combines with the one d places before it, all at once (double-buffered),
+// so after log2(256) = 8 rounds element i holds the inclusive prefix of
+// elements 0..i.  O(n log n) combines, against the O(n) of the serial-items
+// plus wave-scan form; items come from other lanes by shuffles.  x_f marks a
+// row start (packed rows), carried by the combine.
+template <bool SEGMENTED>
+__device__ __forceinline__ void hillis_steele_step(float (&x_a)[4], float (&x_b)[4], int (&x_f)[4], int lane) {
+#pragma unroll
+    for (int d = 1; d < 256; d <<= 1) {
+        float na[4], nb[4];
+        int nf[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int off = d < 4 ? (k >= d ? 0 : 1) : d / 4;  // lanes back
+            const int sk = d < 4 ? (k - d + 4) % 4 : k;        // item there
+            Pair prev{x_a[sk], x_b[sk], SEGMENTED ? x_f[sk] : 0};
+            bool valid = true;
+            if (off > 0) {
+                prev.a = shfl_up(prev.a, off);
+                prev.b = shfl_up(prev.b, off);
+                if (SEGMENTED) prev.f = shfl_up_i(prev.f, off);
+                valid = lane >= off;
+            }
+            const Pair cur{x_a[k], x_b[k], SEGMENTED ? x_f[k] : 0};
+            const Pair r = valid ? combine(prev, cur) : cur;
+            na[k] = r.a;
+            nb[k] = r.b;
+            nf[k] = r.f;
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            x_a[k] = na[k];
+            x_b[k] = nb[k];
+            x_f[k] = nf[k];
+        }
+    }
+}
+
+// HS: the in-tile scan by Hillis-Steele rounds (fp32 items only) instead of
+// serial items plus the wave scan; tiles, look-back and stores are shared.
+template <bool SEGMENTED, typename TIn, typename TOut, bool HS = false>
 __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
     const TIn* __restrict__ a, const TIn* __restrict__ b, TOut* __restrict__ h,
     int64_t rows, int64_t L, int tiles_per_row, int rows_per_tile,
@@ -352,8 +410,8 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
     if constexpr (PACKED) {
 #pragma unroll
         for (int q = 0; q < NS; ++q) {
-            ra[q] = empty_tile ? u32x4a8{0x3f803f80u, 0x3f803f80u, 0x3f803f80u, 0x3f803f80u}
-                               : load_raw8(a, wbase + STEP * q, lo, hi, 0x3f80u);
+            constexpr uint32_t one = Fmt16<TIn>::one, one2 = one | (one << 16);
+            ra[q] = empty_tile ? u32x4a8{one2, one2, one2, one2} : load_raw8(a, wbase + STEP * q, lo, hi, one);
             rb[q] = empty_tile ? u32x4a8{0u, 0u, 0u, 0u} : load_raw8(b, wbase + STEP * q, lo, hi, 0u);
         }
 #pragma unroll
@@ -365,7 +423,7 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
             int f = 0;
 #pragma unroll
             for (int k = 0; k < IPL; ++k) {
-                const float x = raw_item(ra[q], k), y = raw_item(rb[q], k);
+                const float x = raw_item<TIn>(ra[q], k), y = raw_item<TIn>(rb[q], k);
                 bool reset = false;
                 if (SEGMENTED && t0 + k == ns && ns < hi) {
                     reset = true;
@@ -406,6 +464,7 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
                 int64_t ns = 0;
                 if (SEGMENTED) ns = ((t0 + L - 1) / L) * L;  // first row start >= t0
                 int f = 0;
+                int hf[IPL];  // row start at this item (Hillis-Steele form)
 #pragma unroll
                 for (int k = 0; k < IPL; ++k) {
                     bool reset = false;
@@ -413,12 +472,22 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
                         reset = true;
                         ns += L;
                     }
-                    if (k > 0 && !reset) {
-                        bv[q][k] = fmaf(av[q][k], bv[q][k - 1], bv[q][k]);
-                        av[q][k] = av[q][k - 1] * av[q][k];
+                    hf[k] = reset ? 1 : 0;
+                    if constexpr (!HS) {
+                        if (k > 0 && !reset) {
+                            bv[q][k] = fmaf(av[q][k], bv[q][k - 1], bv[q][k]);
+                            av[q][k] = av[q][k - 1] * av[q][k];
+                        }
+                        f |= reset ? 1 : 0;
+                        rmask |= uint32_t(f) << (IPL * q + k);
                     }
-                    f |= reset ? 1 : 0;
-                    rmask |= uint32_t(f) << (IPL * q + k);
+                }
+                if constexpr (HS) {
+                    // the step's inclusive prefixes; a prefix whose run holds a
+                    // row start does not see what precedes the step
+                    hillis_steele_step<SEGMENTED>(av[q], bv[q], hf, lane);
+#pragma unroll
+                    for (int k = 0; k < IPL; ++k) rmask |= uint32_t(hf[k] & 1) << (IPL * q + k);
                 }
             }
         } else {
@@ -444,6 +513,17 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
     Pair carry{1.0f, 0.0f, 0};
 #pragma unroll
     for (int q = 0; q < NS; ++q) {
+        if constexpr (HS) {
+            // items already hold the step's inclusive prefixes: only the carry
+            // from earlier steps is in front of them; the step's total is the
+            // last item of lane 63
+            pre[q] = carry;
+            const Pair tot{__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, la[q]), 63)),
+                           __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lb[q]), 63)),
+                           SEGMENTED ? int(__builtin_amdgcn_readlane(int((rmask >> (IPL * q + IPL - 1)) & 1u), 63)) : 0};
+            carry = combine(carry, tot);
+            continue;
+        }
         Pair w{la[q], lb[q], int((rmask >> (IPL * q + IPL - 1)) & 1u)};
         w = wave_inclusive_scan<SEGMENTED>(w);
         Pair ex{shfl_up(w.a, 1), shfl_up(w.b, 1), SEGMENTED ? shfl_up_i(w.f, 1) : 0};
@@ -508,7 +588,7 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
                 float st = hin;
 #pragma unroll
                 for (int k = 0; k < IPL; ++k) {
-                    const float x = raw_item(wa, k), y = raw_item(wb, k);
+                    const float x = raw_item<TIn>(wa, k), y = raw_item<TIn>(wb, k);
                     const bool start = SEGMENTED && ((smask >> (IPL * q + k)) & 1u);
                     st = start ? y : fmaf(x, st, y);
                     out[k] = st;
@@ -605,26 +685,62 @@ void launch_typed(const void* a, const void* b, void* h, int64_t rows, int64_t L
     }
 }
 
+template <typename TIn>
+void launch_in(const void* a, const void* b, void* h, int64_t rows, int64_t L, int out_fmt, int segmented,
+               int tiles_per_row, int rows_per_tile, int64_t ntiles, uint32_t* claim, uint32_t* done, void* status,
+               uint32_t* err, hipStream_t stream) {
+    using namespace cls;
+    switch (out_fmt) {
+        case 1:
+            launch_typed<TIn, bf16_t>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles, claim, done,
+                                      status, err, stream);
+            break;
+        case 2:
+            launch_typed<TIn, f16_t>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles, claim, done,
+                                     status, err, stream);
+            break;
+        default:
+            launch_typed<TIn, float>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles, claim, done,
+                                     status, err, stream);
+    }
+}
+
 }  // namespace
 
+// in_fmt / out_fmt: 0 fp32, 1 bf16, 2 fp16; hs: the Hillis-Steele in-tile
+// scan (fp32 in and out only).
 extern "C" int cls_launch_linear_scan(const void* a, const void* b, void* h, int64_t rows, int64_t L,
-                                      int in16, int out16, int segmented, int tiles_per_row, int rows_per_tile,
+                                      int in_fmt, int out_fmt, int segmented, int tiles_per_row, int rows_per_tile,
                                       int64_t ntiles, uint32_t* claim, uint32_t* done, void* status,
-                                      uint32_t* err, hipStream_t stream) {
-    if (in16) {
-        if (out16)
-            launch_typed<uint16_t, uint16_t>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles,
-                                             claim, done, status, err, stream);
+                                      uint32_t* err, hipStream_t stream, int hs) {
+    using namespace cls;
+    if (hs) {
+        const dim3 grid{uint32_t(ntiles), 1u, 1u};
+        const dim3 block{uint32_t(kLsThreads), 1u, 1u};
+        const float* ta = static_cast<const float*>(a);
+        const float* tb = static_cast<const float*>(b);
+        float* th = static_cast<float*>(h);
+        uint64_t* st = reinterpret_cast<uint64_t*>(status);
+        if (segmented)
+            hipLaunchKernelGGL((linear_scan_kernel<true, float, float, true>), grid, block, 0, stream, ta, tb, th,
+                               rows, L, tiles_per_row, rows_per_tile, claim, done, st, err);
         else
-            launch_typed<uint16_t, float>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles,
-                                          claim, done, status, err, stream);
-    } else {
-        if (out16)
-            launch_typed<float, uint16_t>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles,
-                                          claim, done, status, err, stream);
-        else
-            launch_typed<float, float>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles,
-                                       claim, done, status, err, stream);
+            hipLaunchKernelGGL((linear_scan_kernel<false, float, float, true>), grid, block, 0, stream, ta, tb, th,
+                               rows, L, tiles_per_row, rows_per_tile, claim, done, st, err);
+        return hipGetLastError() == hipSuccess ? 0 : -7;
+    }
+    switch (in_fmt) {
+        case 1:
+            launch_in<bf16_t>(a, b, h, rows, L, out_fmt, segmented, tiles_per_row, rows_per_tile, ntiles, claim, done,
+                              status, err, stream);
+            break;
+        case 2:
+            launch_in<f16_t>(a, b, h, rows, L, out_fmt, segmented, tiles_per_row, rows_per_tile, ntiles, claim, done,
+                             status, err, stream);
+            break;
+        default:
+            launch_in<float>(a, b, h, rows, L, out_fmt, segmented, tiles_per_row, rows_per_tile, ntiles, claim, done,
+                             status, err, stream);
     }
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }

@@ -1,5 +1,6 @@
 // SSD validation, workspace sizing and dispatch to the fp32 or bf16 path.
 #include <algorithm>
+#include <cmath>
 #include <array>
 #include <map>
 #include <mutex>
@@ -67,6 +68,10 @@ bool tuned_choice(const TuneKey& k, SegChoice* out) {
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
                             int64_t chunk, int dtype, const SegChoice* force, int path, int s3, int xcds);
 
+// Passed as `force`: the built-in heuristic, ignoring any tuned plan (the
+// autotuner's incumbent).
+const SegChoice kUseHeuristic{-1, 0};
+
 std::vector<SegChoice> seg_candidates(int64_t nchains, int64_t nc, int64_t slots) {
     std::vector<SegChoice> v{{1, 0}};
     const int64_t r = nchains % slots;
@@ -93,8 +98,19 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     // The kernel's quadratic block is at most 128 tokens: a longer chunk is run
     // as sub-chunks of 128 with the state passed between them, which changes the
     // result only by rounding (the chunked form equals the recurrence for every
-    // chunk length).
+    // chunk length).  A plan may ask for shorter sub-chunks (64 or 32 tokens).
     chunk = chunk > kFusedMaxChunk ? kFusedMaxChunk : chunk;
+    const int64_t nchains = batch * H;
+    // the segment plan: forced, else tuned for this shape, else the heuristic
+    SegChoice ch{1, 0};
+    bool heuristic = true;
+    if (force && force != &kUseHeuristic) {
+        ch = *force;
+        heuristic = false;
+    } else if (!force && dtype == 1 && tuned_choice(tune_key(batch, L, H, P, S, G, chunk, dtype), &ch)) {
+        heuristic = false;
+    }
+    if (!heuristic && ch.sub >= 32 && ch.sub < chunk && chunk % ch.sub == 0) chunk = ch.sub;
     const int TT = bf16_tile_tokens(int(chunk));
     pl.use = dtype == 1 && P == 64 && (S == 64 || S == 128) && ssd_fused_lds_bytes(TT, int(S)) > 0 &&
              ssd_fused_lds_bytes(TT, int(S)) <= 160 * 1024 && path != 1;
@@ -102,7 +118,6 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     if (H * 64 * 2 * TT >= (int64_t(1) << 31) || G * S * 2 * TT >= (int64_t(1) << 31)) pl.use = false;
     if (!pl.use) return pl;
     const int64_t nc = (L + chunk - 1) / chunk;
-    const int64_t nchains = batch * H;
     // Each workgroup runs one chain (or segment) at a time, one per CU.  The
     // chains that fill whole rounds of the CUs run whole; the remainder would
     // leave most CUs idle in a last round, so it is split into segments that
@@ -110,17 +125,11 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     // aggregate launch (about half its length), which the split must beat.
     int64_t nsegs = 1, nsplit = 0, want_agg_d = 0;
     int want_s3 = 0;
-    SegChoice tuned{};
-    if (force) {
-        nsegs = force->nsegs;
-        nsplit = (force->nsplit > 0 && force->nsplit < nchains) ? force->nsplit : nchains;
-        want_agg_d = force->agg_d;
-        want_s3 = force->s3;
-    } else if (tuned_choice(tune_key(batch, L, H, P, S, G, chunk, dtype), &tuned)) {
-        nsegs = tuned.nsegs;
-        nsplit = tuned.nsplit;
-        want_agg_d = tuned.agg_d;
-        want_s3 = tuned.s3;
+    if (!heuristic) {
+        nsegs = ch.nsegs;
+        nsplit = (ch.nsplit > 0 && ch.nsplit < nchains) ? ch.nsplit : nchains;
+        want_agg_d = ch.agg_d;
+        want_s3 = ch.s3;
     } else {
         const int64_t slots = fused_slots();
         const int64_t r = nchains % slots;
@@ -223,13 +232,30 @@ extern "C" int cls_ssd_check(const SsdShape& s) {
 
 namespace {
 
-// The candidate plans of a fused-path shape (empty when the fused path is not used).
+// The candidate plans of a fused-path shape (empty when the fused path is not
+// used): the segment plans of seg_candidates, each with reduce-then-fold and,
+// when it splits chains, with the look-back; for every sub-chunk the kernel
+// may run (the chunk up to 128 tokens, and 64 when the chunk is longer).
 std::vector<cls::SegChoice> fused_candidates(const SsdShape& s) {
     const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
                                                      s.ngroups, s.chunk, s.dtype);
     if (!pl.use) return {};
-    const int64_t nc = (s.seqlen + pl.chunk - 1) / pl.chunk;
-    return cls::seg_candidates(s.batch * s.nheads, nc, cls::fused_slots());
+    const int64_t base = s.chunk > cls::kFusedMaxChunk ? cls::kFusedMaxChunk : s.chunk;
+    std::vector<cls::SegChoice> out;
+    for (int64_t sub : {base, int64_t(64)}) {
+        if (sub != base && !(sub < base && base % sub == 0)) continue;
+        const int64_t nc = (s.seqlen + sub - 1) / sub;
+        for (cls::SegChoice c : cls::seg_candidates(s.batch * s.nheads, nc, cls::fused_slots())) {
+            c.sub = sub == base ? 0 : sub;
+            c.s3 = 1;
+            out.push_back(c);
+            if (c.nsegs > 1 && c.agg_d == 0) {
+                c.s3 = 2;
+                out.push_back(c);
+            }
+        }
+    }
+    return out;
 }
 
 }  // namespace
@@ -359,17 +385,51 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, const SsdLaun
     return ssd_launch_plan(s, a, o, stream);
 }
 
-// Autotuner of the fused path's segment plan (the one run-time choice of its
-// launches): after one untimed pass over every candidate, each runs `reps`
-// times between two events on the caller's stream, in two rounds; the lowest
-// mean of its better round wins and is kept for the shape on the current
-// device.  Candidates that reduce to the same plan are timed once.  The call ends with one more pass on the chosen plan, so y and
-// h_final hold exactly what a later ssd_fwd call returns.
+// Autotuner of the fused path's plan (segment plan, inter-segment scheme,
+// sub-chunk): the built-in heuristic's plan is the incumbent.  After one
+// untimed pass over every distinct candidate, each runs `reps` times between
+// two events on the caller's stream, in two rounds, and keeps its better
+// round.  The fastest challenger replaces the incumbent only when it is faster
+// by more than the incumbent's own round-to-round spread (at least 1 %), and
+// again by that margin in a head-to-head of three alternating rounds; so the
+// tuned plan never loses to the heuristic by more than the noise.  The winner
+// is kept for the shape on the current device.  The call ends with one more
+// pass on the chosen plan, so y and h_final hold exactly what a later ssd_fwd
+// call returns.
+namespace {
+
+struct PlanId {
+    int64_t nsegs, nsplit, agg_d, sub;
+    int s3;
+    bool operator==(const PlanId& o) const {
+        return nsegs == o.nsegs && nsplit == o.nsplit && agg_d == o.agg_d && sub == o.sub && s3 == o.s3;
+    }
+};
+
+// The plan a choice realises (segment counts are capped and rounded, pieces
+// apply to reduce-then-fold only), as the choice to store.
+cls::SegChoice realised(const SsdShape& s, const cls::SegChoice* c, PlanId* id) {
+    const cls::SsdFusedPlan q = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups,
+                                                    s.chunk, s.dtype, c, 0, 0, 0);
+    const int64_t base = s.chunk > cls::kFusedMaxChunk ? cls::kFusedMaxChunk : s.chunk;
+    const bool split = q.nsegs > 1;
+    *id = PlanId{q.nsegs, split ? int64_t(q.nchains - q.nwhole) : 0, split && !q.lookback ? int64_t(q.agg_d) : 0,
+                 q.chunk == base ? 0 : int64_t(q.chunk), split ? (q.lookback ? 2 : 1) : 0};
+    cls::SegChoice out{id->nsegs, id->nsplit, id->agg_d};
+    out.s3 = id->s3;
+    out.sub = id->sub;
+    return out;
+}
+
+}  // namespace
+
 extern "C" int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t stream, int reps, int64_t* nsegs,
-                                int64_t* nsplit, int64_t* agg_pieces, float* ms) {
+                                int64_t* nsplit, int64_t* agg_pieces, int64_t* sub_chunk, int* s3, float* ms) {
     *nsegs = 0;
     *nsplit = 0;
     *agg_pieces = 0;
+    *sub_chunk = 0;
+    *s3 = 0;
     *ms = 0.0f;
     const std::vector<cls::SegChoice> cands = fused_candidates(s);
     if (cands.empty()) return ssd_launch_plan(s, a, SsdLaunchOpts{}, stream);
@@ -378,84 +438,120 @@ extern "C" int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t
         o.force = c;
         return o;
     };
+    // distinct plans, the incumbent (the heuristic's) first
+    std::vector<cls::SegChoice> plans;
+    std::vector<PlanId> ids;
+    auto add = [&](const cls::SegChoice* c) {
+        PlanId id{};
+        const cls::SegChoice r = realised(s, c, &id);
+        for (const PlanId& e : ids)
+            if (e == id) return;
+        ids.push_back(id);
+        plans.push_back(r);
+    };
+    add(&cls::kUseHeuristic);
+    for (const cls::SegChoice& c : cands) add(&c);
+
     hipEvent_t e0 = nullptr, e1 = nullptr;
     if (hipEventCreate(&e0) != hipSuccess) return SSD_ERR_HIP;
     if (hipEventCreate(&e1) != hipSuccess) {
         (void)hipEventDestroy(e0);
         return SSD_ERR_HIP;
     }
-    // distinct plans only
-    std::vector<cls::SegChoice> plans;
-    for (const cls::SegChoice& c : cands) {
-        const cls::SsdFusedPlan q = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
-                                                        s.ngroups, s.chunk, s.dtype, &c, 0, 0, 0);
-        const cls::SegChoice ce{q.nsegs, q.nsegs > 1 ? int64_t(q.nchains - q.nwhole) : 0,
-                                q.nsegs > 1 ? int64_t(q.agg_d) : 0};
-        bool dup = false;
-        for (const auto& e : plans)
-            dup = dup || (e.nsegs == ce.nsegs && e.nsplit == ce.nsplit && e.agg_d == ce.agg_d);
-        if (!dup) plans.push_back(ce);
-    }
-    // One untimed pass over every plan first (clocks and caches settle), then
-    // two timed rounds over all plans; each plan keeps its better round, so a
-    // plan is not favoured by where it falls in the sequence.
     int st = SSD_OK;
-    std::vector<float> t_best(plans.size(), -1.0f);
+    // mean ms per call of plan i over `reps` calls (after one untimed call)
+    auto time_plan = [&](size_t i, float* out) {
+        st = ssd_launch_plan(s, a, with(&plans[i]), stream);
+        if (st != SSD_OK) return;
+        if (hipEventRecord(e0, stream) != hipSuccess) {
+            st = SSD_ERR_HIP;
+            return;
+        }
+        for (int r = 0; r < reps && st == SSD_OK; ++r) st = ssd_launch_plan(s, a, with(&plans[i]), stream);
+        if (st != SSD_OK) return;
+        float t = 0.0f;
+        if (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+            hipEventElapsedTime(&t, e0, e1) != hipSuccess) {
+            st = SSD_ERR_HIP;
+            return;
+        }
+        *out = t / float(reps);
+    };
     for (size_t i = 0; i < plans.size() && st == SSD_OK; ++i) st = ssd_launch_plan(s, a, with(&plans[i]), stream);
-    for (int round = 0; round < 2 && st == SSD_OK; ++round) {
+    std::vector<float> t_best(plans.size(), -1.0f);
+    float inc_round[2] = {0.0f, 0.0f};  // the incumbent's two rounds
+    for (int round = 0; round < 2 && st == SSD_OK; ++round)
         for (size_t i = 0; i < plans.size() && st == SSD_OK; ++i) {
-            st = ssd_launch_plan(s, a, with(&plans[i]), stream);
-            if (st != SSD_OK) break;
-            if (hipEventRecord(e0, stream) != hipSuccess) {
-                st = SSD_ERR_HIP;
-                break;
-            }
-            for (int r = 0; r < reps && st == SSD_OK; ++r) st = ssd_launch_plan(s, a, with(&plans[i]), stream);
-            if (st != SSD_OK) break;
             float t = 0.0f;
-            if (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
-                hipEventElapsedTime(&t, e0, e1) != hipSuccess) {
-                st = SSD_ERR_HIP;
-                break;
-            }
-            t /= float(reps);
+            time_plan(i, &t);
+            if (st != SSD_OK) break;
+            if (i == 0) inc_round[round] = t;
             if (t_best[i] < 0.0f || t < t_best[i]) t_best[i] = t;
         }
-    }
-    float best_ms = 0.0f;
-    cls::SegChoice best{0, 0, 0};
-    for (size_t i = 0; i < plans.size(); ++i)
-        if (t_best[i] >= 0.0f && (best.nsegs == 0 || t_best[i] < best_ms)) {
-            best_ms = t_best[i];
-            best = plans[i];
+    size_t chosen = 0;  // the incumbent
+    float chosen_ms = t_best.empty() ? 0.0f : t_best[0];
+    if (st == SSD_OK && plans.size() > 1) {
+        size_t ch = 1;
+        for (size_t i = 2; i < plans.size(); ++i)
+            if (t_best[i] < t_best[ch]) ch = i;
+        const float spread = std::fabs(inc_round[0] - inc_round[1]) / std::min(inc_round[0], inc_round[1]);
+        const float margin = std::max(spread, 0.01f);
+        if (t_best[ch] < t_best[0] * (1.0f - margin)) {
+            // head-to-head: three alternating rounds, medians compared
+            float ti[3], tc[3];
+            for (int k = 0; k < 3 && st == SSD_OK; ++k) {
+                time_plan(0, &ti[k]);
+                if (st == SSD_OK) time_plan(ch, &tc[k]);
+            }
+            if (st == SSD_OK) {
+                std::sort(ti, ti + 3);
+                std::sort(tc, tc + 3);
+                if (tc[1] < ti[1] * (1.0f - margin)) {
+                    chosen = ch;
+                    chosen_ms = tc[1];
+                } else {
+                    chosen_ms = ti[1];
+                }
+            }
         }
+    }
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
     if (st != SSD_OK) return st;
+    const cls::SegChoice best = plans[chosen];
     {
         std::lock_guard<std::mutex> lock(cls::g_tune_mu);
         cls::g_tuned[cls::tune_key(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk,
                                    s.dtype)] = best;
     }
+    const cls::SsdFusedPlan qb = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups,
+                                                     s.chunk, s.dtype, &best, 0, 0, 0);
     *nsegs = best.nsegs;
     *nsplit = best.nsplit;
     *agg_pieces = best.agg_d;
-    *ms = best_ms;
+    *sub_chunk = qb.chunk;
+    *s3 = best.s3;
+    *ms = chosen_ms;
     return ssd_launch_plan(s, a, with(&best), stream);
 }
 
-extern "C" int cls_ssd_plan_query(const SsdShape& s, int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces) {
+extern "C" int cls_ssd_plan_query(const SsdShape& s, int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces,
+                                  int64_t* sub_chunk, int* s3) {
     const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
                                                      s.ngroups, s.chunk, s.dtype);
-    if (s.dtype == SSD_F32 || !pl.use) {
-        *nsegs = 0;
-        *nsplit = 0;
-        *agg_pieces = 0;
-        return 2;
-    }
-    *nsegs = pl.nsegs;
-    *nsplit = pl.nsegs > 1 ? int64_t(pl.nchains - pl.nwhole) : 0;
-    *agg_pieces = pl.nsegs > 1 ? int64_t(pl.agg_d) : 0;
+    *nsegs = 0;
+    *nsplit = 0;
+    *agg_pieces = 0;
+    *sub_chunk = 0;
+    *s3 = 0;
+    if (s.dtype == SSD_F32 || !pl.use) return 2;
+    PlanId id{};
+    (void)realised(s, nullptr, &id);
+    *nsegs = id.nsegs;
+    *nsplit = id.nsplit;
+    *agg_pieces = id.agg_d;
+    *sub_chunk = pl.chunk;
+    *s3 = id.s3;
     cls::SegChoice t{};
     const bool tuned = cls::tuned_choice(cls::tune_key(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
                                                        s.ngroups, s.chunk, s.dtype), &t);

@@ -44,8 +44,9 @@ enum {
     SSD_ERR_UNSUPPORTED = -8  /* head dim / state size outside the kernel's set  */
 };
 
-/* Element types of x, B, C and y.  dt, A, D and both states are always fp32. */
-enum { SSD_F32 = 0, SSD_BF16 = 1 };
+/* Element types of x, B, C and y (SSD_F32, SSD_BF16); dt, A, D and both
+ * states are always fp32.  The scan's elements may also be SSD_F16. */
+enum { SSD_F32 = 0, SSD_BF16 = 1, SSD_F16 = 2 };
 
 /*
  * Mamba-2 SSD (state-space duality) chunked forward pass.
@@ -96,48 +97,69 @@ int ssd_fwd(const void* x, const float* dt, const float* A, const void* B,
  * Per-shape autotuning of ssd_fwd ("Accelerating Mamba-2 with high-performance
  * forward pass kernels in NVIDIA cuTile", section "Mamba-2 performance
  * optimization", its autotuner item: a search per input shape, since no one
- * setting suits every shape).  The one run-time choice of the bf16 head-dim-64
- * path is its segment plan: how many segments a long (batch, head) chain is
- * cut into (each segment's start state comes from a separate aggregate
- * launch), which chains are cut, and how many pieces the aggregate launch cuts
- * each segment into (more pieces fill more of the GPU, and the output launch
- * folds more of them).  Tile sizes and occupancy are fixed when the kernels
- * are compiled.
+ * setting suits every shape).  The run-time choices of the bf16 head-dim-64
+ * path form its plan:
+ *   - the segment plan: how many segments a long (batch, head) chain is cut
+ *     into, which chains are cut, and, for reduce-then-fold, how many pieces
+ *     the aggregate launch cuts each segment into;
+ *   - how a cut chain's segments get their start state: reduce-then-fold (an
+ *     aggregate launch, then a fold) or the single-pass look-back
+ *     ("Selective-scan CUDA kernels", section "The five kernels");
+ *   - the sub-chunk the kernels run: the chunk up to 128 tokens, or 64 (a
+ *     different instantiation of the kernels: its tiles, register and LDS
+ *     budget; results differ only by rounding).
+ * Tile shapes and occupancy within each instantiation are fixed at compile
+ * time.
  *
  * ssd_fwd_autotune takes exactly ssd_fwd's arguments (same layouts, same
- * checks, same workspace) plus reps (1..1000).  It runs every candidate plan
- * on these inputs once untimed, then in two rounds reps times each between two
- * events on `stream`; each plan keeps its better round, and the fastest plan
- * is kept for this shape on the current device.
- * Later ssd_fwd calls with the same shape, dtype and chunk on that device use
- * it.  It returns the chosen plan (*nsegs segments, the last *nsplit chains
- * cut, *agg_pieces aggregate pieces per segment; 0 when nothing is cut) and
- * its mean time per call in ms.  y and h_final hold the result of
- * the chosen plan, which is what ssd_fwd then returns.  Shapes outside the
- * fused path have nothing to tune: one plain ssd_fwd pass, *nsegs = 0.
- * The call blocks until its timed runs finish.  The table is process-wide and
- * guarded by a lock; tuning while other calls of the same shape run changes
- * their plan only between calls.  ssd_fwd_workspace_size already covers every
- * candidate plan, so a workspace sized before tuning stays large enough.
- * Every plan computes the same recurrence; results differ only by fp32
- * rounding.
+ * checks, same workspace) plus reps (1..1000).  The built-in heuristic's plan
+ * is the incumbent.  Every distinct candidate runs once untimed, then in two
+ * rounds reps times between two events on `stream`, keeping its better round.
+ * The fastest challenger replaces the incumbent only if it is faster by more
+ * than the incumbent's round-to-round spread (at least 1 %), and again by that
+ * margin in a head-to-head of three alternating rounds.  The chosen plan is
+ * kept for this shape on the current device; later ssd_fwd calls with the
+ * same shape, dtype and chunk on that device use it.  It returns the chosen
+ * plan (*nsegs segments, the last *nsplit chains cut, *agg_pieces aggregate
+ * pieces per segment, each 0 when nothing is cut or not applicable;
+ * *sub_chunk tokens per sub-chunk; *s3 = SSD_S3_REDUCE or SSD_S3_LOOKBACK
+ * when chains are cut, else 0) and its time per call in ms.  y and h_final
+ * hold the result of the chosen plan, which is what ssd_fwd then returns.
+ * Shapes outside the fused path have nothing to tune: one plain ssd_fwd pass,
+ * all outputs 0.  The call blocks until its timed runs finish.  The table is
+ * process-wide and guarded by a lock; tuning while other calls of the same
+ * shape run changes their plan only between calls.  ssd_fwd_workspace_size
+ * already covers every candidate plan, so a workspace sized before tuning
+ * stays large enough.  Every plan computes the same recurrence; results
+ * differ only by fp32 rounding.
  *
  * ssd_fwd_plan reports the plan ssd_fwd would use for a shape without
- * launching anything: returns 1 (a tuned plan), 0 (the built-in heuristic),
- * 2 (the shape does not take the fused path; all three outputs 0) or a
+ * launching anything (same outputs as ssd_fwd_autotune; *sub_chunk 0 and all
+ * others 0 for shapes outside the fused path): returns 1 (a tuned plan), 0
+ * (the built-in heuristic), 2 (the shape does not take the fused path) or a
  * negative status.  ssd_fwd_autotune_reset forgets every tuned plan.
  */
+/* How a cut chain's segments get their start state. */
+enum {
+    SSD_S3_AUTO = 0,      /* the library's choice (in a plan request)                */
+    SSD_S3_REDUCE = 1,    /* reduce-then-fold: an aggregate launch computes every
+                             piece's (decay, state), the output launch folds them   */
+    SSD_S3_LOOKBACK = 2   /* single pass: segments claimed from a counter publish
+                             their aggregate and look back over their predecessors  */
+};
+
 int ssd_fwd_autotune(const void* x, const float* dt, const float* A, const void* B,
                      const void* C, const float* D, const float* h0,
                      int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                      int64_t dstate, int64_t ngroups, int64_t chunk, int dtype,
                      void* y, float* h_final, void* workspace, size_t workspace_bytes,
                      void* stream, int reps, int64_t* nsegs, int64_t* nsplit,
-                     int64_t* agg_pieces, float* ms_per_call);
+                     int64_t* agg_pieces, int64_t* sub_chunk, int* s3, float* ms_per_call);
 
 int ssd_fwd_plan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                  int64_t dstate, int64_t ngroups, int64_t chunk, int dtype,
-                 int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces);
+                 int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces,
+                 int64_t* sub_chunk, int* s3);
 
 void ssd_fwd_autotune_reset(void);
 
@@ -178,19 +200,38 @@ int linear_scan_noalloc(const float* a, const float* b, float* h, int64_t rows,
                         int64_t length, void* stream);
 
 /*
- * linear_scan with bf16 or fp32 elements.  The page's scan is fp32 only
+ * linear_scan with fp32, bf16 or fp16 elements.  The page's scan is fp32 only
  * ("Selective-scan CUDA kernels", section "Limitations"); this entry point
- * takes a and b as in_dtype and writes h as out_dtype, each SSD_F32 or
- * SSD_BF16 (SSD_ERR_DTYPE otherwise).  bf16 elements are raw bf16 bits
+ * takes a and b as in_dtype and writes h as out_dtype, each SSD_F32, SSD_BF16
+ * or SSD_F16 (SSD_ERR_DTYPE otherwise).  16-bit elements are raw bits
  * (uint16_t).  The recurrence is evaluated in fp32 either way, exactly as
- * linear_scan does: bf16 inputs are widened exactly, and a bf16 h is the fp32
- * result rounded to nearest even once.  Same layouts, workspace (size from
+ * linear_scan does: 16-bit inputs are widened exactly, and a 16-bit h is the
+ * fp32 result rounded to nearest even once (fp16: values past its range
+ * become infinities).  Same layouts, workspace (size from
  * linear_scan_workspace_size), alignment, aliasing rule and status codes as
  * linear_scan; with both dtypes SSD_F32 it is linear_scan.
  */
 int linear_scan_typed(const void* a, const void* b, void* h, int64_t rows,
                       int64_t length, int in_dtype, int out_dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * The same scan with a register-resident Hillis-Steele scan inside each tile:
+ * the work-inefficient, step-efficient scan that "Selective-scan CUDA
+ * kernels" (sections "Findings" and "Limitations") measures only as a
+ * PyTorch baseline of full-array passes and names as the fair comparison
+ * still to build.  Within each 256-item step of a wave, log2(256) = 8 rounds
+ * combine every item with the one 1, 2, 4, ..., 128 places before it, all at
+ * once, with items exchanged between lanes by shuffles: O(n log n) combines
+ * instead of linear_scan's serial items plus wave scan.  Tiles, claims, the
+ * look-back, the workspace and every argument rule are linear_scan's (fp32
+ * elements; size the workspace with linear_scan_workspace_size).  Results
+ * agree with linear_scan to fp32 rounding (the combine order differs) and are
+ * the same from run to run.
+ */
+int linear_scan_hillis_steele(const float* a, const float* b, float* h, int64_t rows,
+                              int64_t length, void* workspace, size_t workspace_bytes,
+                              void* stream);
 
 /*
  * The same scalar recurrence as three launches: block scan, spine scan over

@@ -29,15 +29,9 @@ enum {
                             they do not apply)                                     */
 };
 
-/* How a split chain's segments get the state at their start (fused path;
- * "Selective-scan CUDA kernels", section "The five kernels", levels 2 and 3). */
-enum {
-    SSD_S3_AUTO = 0,      /* the library's choice                                  */
-    SSD_S3_REDUCE = 1,    /* reduce-then-fold: an aggregate launch computes every
-                             piece's (decay, state), the output launch folds them  */
-    SSD_S3_LOOKBACK = 2   /* single pass: segments claimed from a counter publish
-                             their aggregate and look back over their predecessors */
-};
+/* The inter-segment schemes (SSD_S3_AUTO, SSD_S3_REDUCE, SSD_S3_LOOKBACK) are
+ * declared in chunked_linear_scan.h ("Selective-scan CUDA kernels", section
+ * "The five kernels", levels 2 and 3). */
 
 typedef struct {
     int32_t path;        /* SSD_PATH_*                                               */
@@ -49,7 +43,8 @@ typedef struct {
                             segment; 0: the heuristic's count                      */
     int32_t xcds;        /* XCDs the workgroups are dealt across (chain mapping
                             only); 0: the device's 8; 1: plain index order          */
-    int32_t reserved;    /* must be 0                                                */
+    int32_t sub_chunk;   /* with nsegs: the sub-chunk the kernels run (32 or 64, a
+                            divisor of the chunk capped at 128); 0: that cap      */
 } ssd_plan_request;
 
 /*

@@ -213,8 +213,13 @@ def check_ssd_workload(name, y_got, h_got, label=""):
 # ---------------------------------------------------------------------------
 # scalar scan
 # ---------------------------------------------------------------------------
-def check_scan(a, b, h_got, out_bf16=False, label="", row_tol_factor=10.0, elementwise=True, band=8192):
-    """Whole-output parity of a scan result: rel-L2 <= 1e-5 (bf16 h: 1e-2),
+U_F16 = 2.0 ** -11
+
+
+def check_scan(a, b, h_got, out_bf16=False, label="", row_tol_factor=10.0, elementwise=True, band=8192,
+               out_f16=False):
+    """Whole-output parity of a scan result: rel-L2 <= 1e-5 (bf16 h: 1e-2,
+    fp16 h: 1e-3),
     every row's rel-L2 within ``row_tol_factor`` of that, the rel-L2 of every
     ``band``-long stretch of the rows (a tile of the kernels) within the same
     factor, and the element-wise bound against ``scan_error_scale``.
@@ -224,8 +229,9 @@ def check_scan(a, b, h_got, out_bf16=False, label="", row_tol_factor=10.0, eleme
     ref = oscan.scan_loop(a64, b64)
     scale = oscan.scan_error_scale(a64, b64) if elementwise else np.full(ref.shape, np.inf)
     got = np.asarray(h_got, np.float64)
-    tol = 1e-2 if out_bf16 else TOL_F32
-    bound = (16.0, U_F32, 2.0 if out_bf16 else 4.0, U_BF16 if out_bf16 else U_F32)
+    tol = 1e-2 if out_bf16 else (1e-3 if out_f16 else TOL_F32)
+    bound = (16.0, U_F32, 2.0 if (out_bf16 or out_f16) else 4.0,
+             U_BF16 if out_bf16 else (U_F16 if out_f16 else U_F32))
     st = _merge([_stats(got, ref, scale, bound, 0)])
     _assert(st, tol, f"{label} h", 0)
     if band and got.shape[1] > band:

@@ -27,7 +27,7 @@ def header_functions():
 def test_header_lists_expected_entry_points():
     assert set(header_functions()) == {
         "ssd_fwd_workspace_size", "ssd_fwd", "ssd_fwd_autotune", "ssd_fwd_plan", "ssd_fwd_autotune_reset",
-        "linear_scan_workspace_size", "linear_scan", "linear_scan_typed", "linear_scan_noalloc", "ssd_step", "linear_scan_three_pass_workspace_size", "linear_scan_three_pass", "ssd_strerror"}
+        "linear_scan_workspace_size", "linear_scan", "linear_scan_typed", "linear_scan_noalloc", "linear_scan_hillis_steele", "ssd_step", "linear_scan_three_pass_workspace_size", "linear_scan_three_pass", "ssd_strerror"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -137,10 +137,12 @@ def test_ssd_autotune_rejects_bad_arguments():
     """Validation happens on the host before any launch: missing outputs of
     the tuner, a repetition count out of range, and ssd_fwd's own checks."""
     lib = cls.load_library()
-    n1, n2, n3, ms = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_float()
+    n1, n2, n3, n4, ms = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_float()
+    s3 = ctypes.c_int()
 
     def call(x=FAKE, y=FAKE, reps=3, out=True, Bt=1, T=32, ws_bytes=1 << 30):
-        outs = (ctypes.byref(n1), ctypes.byref(n2), ctypes.byref(n3), ctypes.byref(ms)) if out else (None,) * 4
+        outs = (ctypes.byref(n1), ctypes.byref(n2), ctypes.byref(n3), ctypes.byref(n4), ctypes.byref(s3),
+                ctypes.byref(ms)) if out else (None,) * 6
         return lib.ssd_fwd_autotune(x, FAKE, FAKE, FAKE, FAKE, None, None, Bt, 64, 2, 16, 32, 1, T, cls.SSD_BF16,
                                     y, None, FAKE, ws_bytes, None, reps, *outs)
 
@@ -162,23 +164,30 @@ def test_ssd_plan_query_on_host():
     import torch
     cls.ssd_fwd_autotune_reset()
     # 4 x 80 chains: 64 left over after one round, cut into 4 segments
-    # (192 pieces of 3 segments fit 512 aggregate slots twice: 2 pieces per segment)
+    # (192 pieces of 3 segments fit 512 aggregate slots twice: 2 pieces per segment);
+    # a 256-token chunk runs as 128-token sub-chunks
     assert cls.ssd_fwd_plan(4, 8192, 80, 64, 128, 1, 256) == {"nsegs": 4, "nsplit": 64, "agg_pieces": 2,
+                                                              "sub_chunk": 128, "s3": "reduce",
                                                               "source": "heuristic"}
     # 64 chains of 512 chunks: every chain cut into 4
     assert cls.ssd_fwd_plan(1, 65536, 64, 64, 128, 8, 128) == {"nsegs": 4, "nsplit": 64, "agg_pieces": 2,
+                                                               "sub_chunk": 128, "s3": "reduce",
                                                                "source": "heuristic"}
     # 192 chains of 16 chunks: a split would not pay, whole chains
     assert cls.ssd_fwd_plan(8, 2048, 24, 64, 128, 1, 256) == {"nsegs": 1, "nsplit": 0, "agg_pieces": 0,
+                                                              "sub_chunk": 128, "s3": None,
                                                               "source": "heuristic"}
+    assert cls.ssd_fwd_plan(1, 1000, 4, 64, 128, 1, 32)["sub_chunk"] == 32
     assert cls.ssd_fwd_plan(1, 256, 2, 16, 16, 1, 32, torch.float32)["source"] == "none"
     assert cls.ssd_fwd_plan(1, 256, 2, 32, 32, 1, 32)["source"] == "none"  # head dim 32: per-head kernel
     with pytest.raises(cls.SSDError):
         cls.ssd_fwd_plan(1, 256, 3, 64, 128, 2, 32)
     lib = cls.load_library()
-    n1, n2 = ctypes.c_int64(), ctypes.c_int64()
-    assert lib.ssd_fwd_plan(1, 256, 2, 64, 128, 1, 32, 1, None, ctypes.byref(n1), ctypes.byref(n2)) == -1
-    assert lib.ssd_fwd_plan(1, 256, 2, 64, 128, 1, 32, 1, ctypes.byref(n1), ctypes.byref(n2), None) == -1
+    n1, n2, n3, n4, s3 = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int()
+    assert lib.ssd_fwd_plan(1, 256, 2, 64, 128, 1, 32, 1, None, ctypes.byref(n1), ctypes.byref(n2),
+                            ctypes.byref(n3), ctypes.byref(s3)) == -1
+    assert lib.ssd_fwd_plan(1, 256, 2, 64, 128, 1, 32, 1, ctypes.byref(n1), ctypes.byref(n2), ctypes.byref(n3),
+                            ctypes.byref(n4), None) == -1
 
 
 def test_linear_scan_typed_rejects_bad_arguments():
@@ -187,7 +196,7 @@ def test_linear_scan_typed_rejects_bad_arguments():
     def call(a=FAKE, h=FAKE, rows=2, L=100, din=cls.SSD_BF16, dout=cls.SSD_F32, ws=FAKE, ws_bytes=1 << 20):
         return lib.linear_scan_typed(a, FAKE, h, rows, L, din, dout, ws, ws_bytes, None)
 
-    assert call(din=2) == -3
+    assert call(din=3) == -3
     assert call(dout=-1) == -3
     assert call(a=None) == -1
     assert call(h=None) == -1

@@ -51,11 +51,13 @@ def test_autotune_result_plan_and_later_calls(Bt, L, H, G, chunk):
     nchains = Bt * H
     assert 1 <= info["nsegs"] <= 32 and info["ms_per_call"] > 0
     assert (info["nsegs"] == 1) == (info["nsplit"] == 0) and 0 <= info["nsplit"] <= nchains
-    assert (info["nsegs"] == 1) == (info["agg_pieces"] == 0) and info["agg_pieces"] >= 0
+    assert (info["nsegs"] > 1) == (info["s3"] is not None)
+    assert (info["agg_pieces"] > 0) == (info["s3"] == "reduce") and info["agg_pieces"] >= 0
+    assert info["sub_chunk"] in (min(chunk, 128), 64) and info["sub_chunk"] <= min(chunk, 128)
     parity.check_ssd(c, y.float().cpu().numpy(), hf.cpu().numpy(), chunk, "tuned")
     after = cls.ssd_fwd_plan(Bt, L, H, P, S, G, chunk)
     assert after == {"nsegs": info["nsegs"], "nsplit": info["nsplit"], "agg_pieces": info["agg_pieces"],
-                     "source": "tuned"}
+                     "sub_chunk": info["sub_chunk"], "s3": info["s3"], "source": "tuned"}
     y2, hf2 = cls.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=chunk)
     torch.cuda.synchronize()
     assert torch.equal(y2.view(torch.int16), y.view(torch.int16))
@@ -92,6 +94,6 @@ def test_autotune_without_a_plan_runs_one_plain_pass():
         d = {k: v.cuda() for k, v in c.items()}
         y, hf, info = cls.ssd_fwd_autotune(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=64)
         torch.cuda.synchronize()
-        assert info["nsegs"] == 0 and info["nsplit"] == 0 and info["agg_pieces"] == 0
+        assert info["nsegs"] == 0 and info["nsplit"] == 0 and info["agg_pieces"] == 0 and info["sub_chunk"] == 0
         assert cls.ssd_fwd_plan(1, 300, 4, P, S, 2, 64, dtype)["source"] == "none"
         parity.check_ssd(c, y.float().cpu().numpy(), hf.cpu().numpy(), 64, f"{dtype}")

@@ -129,7 +129,9 @@ def test_workspace_reused_across_shapes():
     assert int(ws[:4].view(torch.int32).item()) == 0
 
 
-TYPED = [(torch.bfloat16, torch.float32), (torch.bfloat16, torch.bfloat16), (torch.float32, torch.bfloat16)]
+TYPED = [(torch.bfloat16, torch.float32), (torch.bfloat16, torch.bfloat16), (torch.float32, torch.bfloat16),
+         (torch.float16, torch.float32), (torch.float16, torch.float16), (torch.float32, torch.float16),
+         (torch.bfloat16, torch.float16)]
 
 
 @pytest.mark.parametrize("din,dout", TYPED)
@@ -138,11 +140,12 @@ TYPED = [(torch.bfloat16, torch.float32), (torch.bfloat16, torch.bfloat16), (tor
                                     (257, 129), (3, 5461), (5, 4096), (9, 2048), (33, 256), (4097, 4),
                                     (4, 65536), (1, 65533)])
 def test_typed_scan_matches_oracle(din, dout, rows, L):
-    """bf16 / fp32 elements through linear_scan_typed.  The oracle runs on the
-    exact float64 values of the (possibly bf16) inputs.  With an fp32 h the
-    scan is the fp32 scan (rel-L2 <= 1e-5); a bf16 h is that fp32 result
-    rounded to nearest even once, so it equals the fp32-output run rounded on
-    the host bit for bit, and stays within bf16 rounding of the oracle."""
+    """bf16 / fp16 / fp32 elements through linear_scan_typed.  The oracle runs
+    on the exact float64 values of the (possibly 16-bit) inputs.  With an fp32
+    h the scan is the fp32 scan (rel-L2 <= 1e-5); a 16-bit h is that fp32
+    result rounded to nearest even once, so it equals the fp32-output run
+    rounded on the host bit for bit, and stays within that rounding of the
+    oracle."""
     print(f"[scan typed] {din} -> {dout} rows={rows} L={L}", flush=True)
     w = workloads.make_scan_inputs(rows, L, seed=rows * 31 + L)
     a, b = w["a"].to(din), w["b"].to(din)
@@ -150,11 +153,12 @@ def test_typed_scan_matches_oracle(din, dout, rows, L):
     torch.cuda.synchronize()
     assert h.dtype == dout
     got = h.float().cpu().numpy()
-    parity.check_scan(a, b, got, out_bf16=dout == torch.bfloat16, label=f"{din}->{dout}")
-    if dout == torch.bfloat16:
+    parity.check_scan(a, b, got, out_bf16=dout == torch.bfloat16, out_f16=dout == torch.float16,
+                      label=f"{din}->{dout}")
+    if dout != torch.float32:
         h32 = cls.linear_scan(a.cuda(), b.cuda(), out_dtype=torch.float32)
         torch.cuda.synchronize()
-        assert torch.equal(h.cpu().view(torch.int16), h32.cpu().to(torch.bfloat16).view(torch.int16))
+        assert torch.equal(h.cpu().view(torch.int16), h32.cpu().to(dout).view(torch.int16))
 
 
 def test_typed_scan_full_workload_bf16_inputs():
@@ -173,3 +177,43 @@ def test_page_table_row_lengths(rows, L):
     packed several to a tile."""
     w = workloads.make_scan_inputs(rows, L, seed=rows + L)
     check(w["a"], w["b"], label=f"page table L={L}")
+
+
+@pytest.mark.parametrize("rows,L", [(1, 1), (3, 5), (2, 255), (2, 256), (3, 257), (5, 4096), (3, 8186), (2, 8187),
+                                    (3, 8193), (2, 20000), (1000, 7), (257, 129), (4097, 4), (11, 2047)])
+def test_hillis_steele_matches_oracle_and_single_pass(rows, L):
+    """The register-resident Hillis-Steele kernel: whole-output parity with
+    the oracle, on long rows (look-back across tiles) and packed short rows
+    (row starts carried through the Hillis-Steele rounds), and agreement with
+    the work-efficient kernel to fp32 rounding."""
+    w = workloads.make_scan_inputs(rows, L, seed=rows * 13 + L)
+    a, b = w["a"].cuda(), w["b"].cuda()
+    print(f"[scan hs] rows={rows} L={L}", flush=True)
+    hs = cls.linear_scan_hillis_steele(a, b)
+    one = cls.linear_scan(a, b)
+    torch.cuda.synchronize()
+    got = hs.cpu().numpy()
+    parity.check_scan(w["a"], w["b"], got, label=f"hillis-steele {rows}x{L}")
+    assert compare.rel_l2(got, one.cpu().numpy()) <= 2 * TOL
+
+
+@pytest.mark.parametrize("name", ["scan", "scan_ragged"])
+def test_hillis_steele_full_workload(name):
+    w = workloads.scan_workload(name)
+    print(f"[scan hs] {name}", flush=True)
+    got = cls.linear_scan_hillis_steele(w["a"].cuda(), w["b"].cuda()).cpu().numpy()
+    parity.check_scan(w["a"], w["b"], got, label=f"hillis-steele {name}")
+
+
+def test_hillis_steele_special_cases_and_determinism():
+    g = torch.Generator().manual_seed(6)
+    b = torch.randn(3, 30000, generator=g).cuda()
+    assert torch.equal(cls.linear_scan_hillis_steele(torch.zeros_like(b), b), b)  # a = 0: h = b exactly
+    got = cls.linear_scan_hillis_steele(torch.ones_like(b), b).cpu().numpy()
+    ref = np.cumsum(b.cpu().numpy().astype(np.float64), axis=1)
+    assert compare.rel_l2(got, ref) < TOL
+    w = workloads.make_scan_inputs(16, 70000, seed=9)
+    a, bb = w["a"].cuda(), w["b"].cuda()
+    first = cls.linear_scan_hillis_steele(a, bb)
+    for i in range(100):
+        assert torch.equal(cls.linear_scan_hillis_steele(a, bb), first), i

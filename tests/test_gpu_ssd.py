@@ -315,3 +315,14 @@ def test_planned_call_rejects_bad_plans():
                 cls.PlanRequest(0, 3, 0, 0, 0, 0, 0), cls.PlanRequest(0, 0, 0, 0, 0, 0, 1)):
         with pytest.raises(cls.SSDError):
             cls.ssd_fwd_planned(*args, chunk=32, plan=bad)
+
+
+@pytest.mark.parametrize("chunk,sub,s3", [(128, 64, "reduce"), (256, 64, "lookback"), (256, 32, "reduce"),
+                                          (64, 32, "lookback"), (128, 64, "lookback")])
+def test_sub_chunk_forced(chunk, sub, s3):
+    """The fused kernels run shorter sub-chunks than the chunk (an
+    instantiation the autotuner may pick); the chunked form equals the
+    recurrence at every chunk length, so only rounding changes."""
+    inp = small_case(150 + sub + chunk, 2, 64 * 30 + 5, 3, 64, 128, 1, torch.bfloat16, dt_shift=-3.0)
+    run_and_check(inp, chunk, f"chunk={chunk} sub={sub} {s3}",
+                  plan=cls.plan_request(nsegs=3, nsplit=4, s3=s3, sub_chunk=sub))
