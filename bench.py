@@ -337,6 +337,32 @@ class MulRunner(ScanRunner):
         torch.mul(a, b, out=h)
 
 
+class StreamRunner(ScanRunner):
+    """stream_mul_f32: a hand-written kernel that moves the scan's exact bytes
+    (h = a * b), one configuration of its vector width and cache policy."""
+
+    def __init__(self, name, vec, nt):
+        super().__init__(name)
+        self.vec, self.nt = vec, nt
+        self.name = f"{name}:stream_v{vec}_{'nt' if nt else 'default'}"
+
+    def step(self, i):
+        a, b, h = self.sets[i % self.nsets]
+        self.cls.stream_mul(a, b, out=h, vec=self.vec, nt=self.nt)
+
+
+class TiledScanRunner(ScanRunner):
+    """fp32 linear_scan with an explicit tile size (linear_scan_planned)."""
+
+    def __init__(self, base, name, tile):
+        self.__dict__.update(base.__dict__)
+        self.name, self.tile = name, tile
+
+    def step(self, i):
+        a, b, h = self.sets[i % self.nsets]
+        self.cls.linear_scan_planned(a, b, tile=self.tile, out=h, workspace=self.ws)
+
+
 class StepRunner(Runner):
     def __init__(self, name):
         import torch
@@ -613,6 +639,28 @@ def autotune_compare(r, steps, warmup):
             "speedup": round(tb["median"] / ta["median"], 3)}
 
 
+def scan_autotune_compare(runners, steps, warmup):
+    """The tile linear_scan_autotune keeps for each scan workload against the
+    built-in 8192-element tile, timed in interleaved windows after tuning."""
+    out = {}
+    for r in runners:
+        cls = r.cls
+        cls.linear_scan_autotune_reset()
+        a, b, h = r.sets[0]
+        _, info = cls.linear_scan_autotune(a, b, out=h, reps=20, workspace=r.ws)
+        cls.linear_scan_autotune_reset()
+        tuned, builtin = TiledScanRunner(r, "tuned", info["tile"]), TiledScanRunner(r, "built-in", 8192)
+        for x in (tuned, builtin):
+            warm(x, warmup)
+        n = [max(1, min(2000, math.ceil(MIN_WINDOW_S / 50e-6)))] * NWIN
+        ws = timed_windows([tuned, builtin], {"tuned": n, "built-in": n})
+        ta, tb = summarize(ws["tuned"], n), summarize(ws["built-in"], n)
+        out[r.name] = {"tile": info["tile"], "built_in_tile": 8192, "tuner_ms_per_call": round(info["ms_per_call"], 4),
+                       "us_per_call_tuned": _us(ta["median"]), "us_per_call_built_in": _us(tb["median"]),
+                       "speedup": round(tb["median"] / ta["median"], 3)}
+    return out
+
+
 def s3_ab(steps, warmup, names=("ssd_large", "ssd_long")):
     """The two inter-segment schemes of split chains timed against each other
     on the workloads whose plans split chains: reduce-then-fold (aggregate
@@ -714,7 +762,8 @@ def main():
                 side.append(SsdRunner(name))
         side += [ScanRunner("scan"), ScanRunner("scan_ragged"), ScanRunner("scan", "bf16", "f32"),
                  ScanRunner("scan", "bf16", "bf16"), ScanRunner("scan", "f16", "f32"), ScanRunner("scan", "f16", "f16"),
-                 HillisSteeleRunner("scan"), Scan3Runner("scan"), MulRunner("scan"), StepRunner("decode_large")]
+                 HillisSteeleRunner("scan"), Scan3Runner("scan"), MulRunner("scan"), StreamRunner("scan", 2, True),
+                 StreamRunner("scan", 4, True), StreamRunner("scan", 2, False), StepRunner("decode_large")]
     runners = [head] + side
     plan = {head.name: split_steps(args.steps, NWIN)}
     warm_s = {}
@@ -775,6 +824,13 @@ def main():
         sc["elementwise_ceiling"] = dict(others["scan:torch.mul"], kernel="torch.mul(a, b, out=h)",
                                          scan_over_ceiling=round(stats["scan:torch.mul"]["mean"]
                                                                  / stats["scan"]["mean"], 3))
+        streams = [r for r in side if isinstance(r, StreamRunner)]
+        best = min(streams, key=lambda r: stats[r.name]["median"])
+        sc["stream_ceiling"] = dict(
+            others[best.name], kernel=f"stream_mul_f32 (h = a * b), vec={best.vec}, nt={int(best.nt)}: the fastest of "
+                                      + ", ".join(f"{r.name.split(':')[1]} {_us(stats[r.name]['median'])} us"
+                                                  for r in streams),
+            scan_over_ceiling=round(stats[best.name]["median"] / stats["scan"]["median"], 3))
         sc["bf16"] = {"bf16_in_f32_out": others["scan:bf16->f32"], "bf16_in_bf16_out": others["scan:bf16->bf16"]}
         sc["f16"] = {"f16_in_f32_out": others["scan:f16->f32"], "f16_in_f16_out": others["scan:f16->f16"]}
         sc["hillis_steele"] = dict(others["scan:hillis_steele"], time_ratio_to_single_pass=round(
@@ -793,6 +849,11 @@ def main():
     if not args.no_autotune:
         log("autotune comparison")
         line["autotune"] = autotune_compare(head, max(args.steps // 2, NWIN), args.warmup)
+        if others:
+            log("scan autotune comparison")
+            line["linear_scan"]["autotune"] = scan_autotune_compare(
+                [r for r in side if type(r) is ScanRunner and r.name in ("scan", "scan_ragged")], args.steps,
+                args.warmup)
     if want_cpu:
         log("cpu baselines")
         line["cpu_baseline"] = cpu_baseline_ssd(head)
@@ -832,16 +893,25 @@ def scan_ceiling_sweep(steps, warmup):
                 a, b, h = sets[i % 3]
                 torch.mul(a, b, out=h)
 
-        rs = [S(), M()]
+        class K(Runner):
+            name, nsets = "stream", 3
+
+            def step(self, i):
+                a, b, h = sets[i % 3]
+                cls.stream_mul(a, b, out=h, vec=2, nt=True)
+
+        rs = [S(), M(), K()]
         for r in rs:
             warm(r, warmup)
         n = split_steps(max(steps, NWIN), NWIN)
-        win = timed_windows(rs, {"scan": n, "mul": n})
+        win = timed_windows(rs, {"scan": n, "mul": n, "stream": n})
         ts, tm = summarize(win["scan"], n)["median"], summarize(win["mul"], n)["median"]
+        tk = summarize(win["stream"], n)["median"]
         nb = 12 * rows * L
         print(json.dumps({"rows": rows, "L": L, "scan_us": _us(ts), "scan_GBs": round(nb / ts / 1e9, 1),
                           "mul_us": _us(tm), "mul_GBs": round(nb / tm / 1e9, 1),
-                          "mul_over_scan": round(tm / ts, 3)}), flush=True)
+                          "mul_over_scan": round(tm / ts, 3), "stream_us": _us(tk),
+                          "stream_GBs": round(nb / tk / 1e9, 1), "stream_over_scan": round(tk / ts, 3)}), flush=True)
         del sets, ws
 
 

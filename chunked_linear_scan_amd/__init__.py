@@ -94,6 +94,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.ssd_fwd_planned.restype = ctypes.c_int
         lib.ssd_fwd_planned_workspace_size.argtypes = [i64] * 7 + [ctypes.c_int, ctypes.POINTER(PlanRequest)]
         lib.ssd_fwd_planned_workspace_size.restype = sz
+        lib.stream_mul_f32.argtypes = [fp, fp, fp, i64, ctypes.c_int, ctypes.c_int, i64, vp]
+        lib.stream_mul_f32.restype = ctypes.c_int
+        lib.linear_scan_planned.argtypes = [fp, fp, fp, i64, i64, i64, vp, sz, vp]
+        lib.linear_scan_planned.restype = ctypes.c_int
+        lib.linear_scan_autotune.argtypes = [fp, fp, fp, i64, i64, vp, sz, vp, ctypes.c_int, pi64,
+                                             ctypes.POINTER(ctypes.c_float)]
+        lib.linear_scan_autotune.restype = ctypes.c_int
+        lib.linear_scan_plan.argtypes = [i64, i64, pi64]
+        lib.linear_scan_plan.restype = ctypes.c_int
+        lib.linear_scan_autotune_reset.argtypes = []
+        lib.linear_scan_autotune_reset.restype = None
         _lib = lib
         return lib
 
@@ -218,6 +229,67 @@ def linear_scan(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = Non
     if st != SSD_OK:
         raise SSDError(st, "linear_scan")
     return h
+
+
+def _scan_f32_args(lib, a, b, out, workspace):
+    _check_cuda("a", a, torch.float32)
+    if a.dim() != 2:
+        raise ValueError("a must be [rows, L]")
+    _check_cuda("b", b, torch.float32, a.shape)
+    rows, length = a.shape
+    h = torch.empty_like(a) if out is None else out
+    _check_cuda("out", h, torch.float32, a.shape)
+    need = lib.linear_scan_workspace_size(rows, length)
+    if need == 0:
+        raise SSDError(-2, "linear_scan_workspace_size")
+    ws = _scan_ws.get(a.device, _stream_key(a.device), need) if workspace is None else workspace
+    return rows, length, h, ws
+
+
+def linear_scan_planned(a: torch.Tensor, b: torch.Tensor, tile: int = 0, out: torch.Tensor | None = None,
+                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """fp32 linear_scan with an explicit tile size (4096, 8192 or 16384
+    elements; 0: what linear_scan runs), ``linear_scan_planned`` of the
+    testing header."""
+    lib = load_library()
+    rows, length, h, ws = _scan_f32_args(lib, a, b, out, workspace)
+    st = lib.linear_scan_planned(_ptr(a), _ptr(b), _ptr(h), rows, length, int(tile), _ptr(ws), ws.numel(),
+                                 _stream_handle(a.device))
+    if st != SSD_OK:
+        raise SSDError(st, "linear_scan_planned")
+    return h
+
+
+def linear_scan_autotune(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None, reps: int = 10,
+                         workspace: torch.Tensor | None = None):
+    """Times the fp32 scan's tile sizes on these arguments and keeps the
+    fastest for the shape (the built-in 8192 unless another is faster by more
+    than the noise).  Returns (h, {"tile", "ms_per_call"}); h is what a later
+    linear_scan of the shape returns."""
+    lib = load_library()
+    rows, length, h, ws = _scan_f32_args(lib, a, b, out, workspace)
+    tile, ms = ctypes.c_int64(), ctypes.c_float()
+    st = lib.linear_scan_autotune(_ptr(a), _ptr(b), _ptr(h), rows, length, _ptr(ws), ws.numel(),
+                                  _stream_handle(a.device), int(reps), ctypes.byref(tile), ctypes.byref(ms))
+    if st != SSD_OK:
+        raise SSDError(st, "linear_scan_autotune")
+    return h, {"tile": tile.value, "ms_per_call": ms.value}
+
+
+def linear_scan_plan(rows: int, length: int) -> dict:
+    """The tile an fp32 linear_scan of this shape runs on the current device:
+    {"tile", "source": "tuned" | "built-in"}.  Launches nothing."""
+    lib = load_library()
+    tile = ctypes.c_int64()
+    st = lib.linear_scan_plan(int(rows), int(length), ctypes.byref(tile))
+    if st < 0:
+        raise SSDError(st, "linear_scan_plan")
+    return {"tile": tile.value, "source": "tuned" if st == 1 else "built-in"}
+
+
+def linear_scan_autotune_reset():
+    """Forgets every tuned scan tile."""
+    load_library().linear_scan_autotune_reset()
 
 
 def _ssd_fwd_args(lib, x, dt, A, B, C, D, h0, chunk, want_final_state, out, workspace, plan=None):
@@ -363,6 +435,23 @@ def linear_scan_hillis_steele(a: torch.Tensor, b: torch.Tensor, out: torch.Tenso
                                        _stream_handle(a.device))
     if st != SSD_OK:
         raise SSDError(st, "linear_scan_hillis_steele")
+    return h
+
+
+def stream_mul(a: torch.Tensor, b: torch.Tensor, out: torch.Tensor | None = None, vec: int = 4, nt: bool = True,
+               grid_blocks: int = 0) -> torch.Tensor:
+    """h = a * b elementwise over contiguous fp32 tensors (``stream_mul_f32``
+    of the testing header): the linear scan's traffic without the scan, the
+    measured ceiling of a three-stream kernel."""
+    lib = load_library()
+    _check_cuda("a", a, torch.float32)
+    _check_cuda("b", b, torch.float32, a.shape)
+    h = torch.empty_like(a) if out is None else out
+    _check_cuda("out", h, torch.float32, a.shape)
+    st = lib.stream_mul_f32(_ptr(a), _ptr(b), _ptr(h), a.numel(), int(vec), 1 if nt else 0, int(grid_blocks),
+                            _stream_handle(a.device))
+    if st != SSD_OK:
+        raise SSDError(st, "stream_mul_f32")
     return h
 
 

@@ -6,14 +6,22 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <array>
+#include <map>
+#include <mutex>
+#include <vector>
+
 #include "../../include/chunked_linear_scan.h"
 #include "../../include/chunked_linear_scan_testing.h"
 #include "launch.hpp"
+#include "tune.hpp"
 
 
 namespace {
 
-constexpr int64_t kLsTile = 8192;  // elements per linear-scan tile (linear_scan.hip)
+constexpr int64_t kLsTile = 8192;  // elements per linear-scan tile: the built-in choice
+// fp32 tiles the scan autotuner may choose (the built-in one first)
+constexpr int64_t kLsTileCandidates[] = {8192, 4096, 16384};
 constexpr size_t kHeader = 256;    // bytes: error word and padding
 
 inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -22,29 +30,31 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 
 struct ScanPlan {
     bool segmented;
+    int64_t tile;
     int64_t tiles_per_row;
     int64_t rows_per_tile;
     int64_t ntiles;
     size_t claim_off, done_off, status_off, bytes;
 };
 
-ScanPlan plan_scan(int64_t rows, int64_t L) {
+ScanPlan plan_scan(int64_t rows, int64_t L, int64_t tile = kLsTile) {
     ScanPlan p{};
-    p.segmented = L <= kLsTile - 6;
+    p.tile = tile;
+    p.segmented = L <= tile - 6;
     if (p.segmented) {
         // A packed tile covers its rows from the 16-byte boundary at or before
         // the first row's start, up to 3 elements early, so its rows may hold
-        // kLsTile - 3 elements.  When L is a multiple of 4 every row starts on
+        // tile - 3 elements.  When L is a multiple of 4 every row starts on
         // such a boundary (the base is 16-byte aligned), so whole rows fill
         // the tile exactly.
-        p.rows_per_tile = (L % 4 == 0) ? kLsTile / L : (kLsTile - 3) / L;
+        p.rows_per_tile = (L % 4 == 0) ? tile / L : (tile - 3) / L;
         p.tiles_per_row = 1;
         p.ntiles = (rows + p.rows_per_tile - 1) / p.rows_per_tile;
         p.claim_off = p.done_off = p.status_off = kHeader;
         p.bytes = kHeader;
     } else {
         p.rows_per_tile = 1;
-        p.tiles_per_row = (L + 3 + kLsTile - 1) / kLsTile;
+        p.tiles_per_row = (L + 3 + tile - 1) / tile;
         p.ntiles = rows * p.tiles_per_row;
         p.claim_off = kHeader;
         p.done_off = p.claim_off + round_up(size_t(rows) * 4, 256);
@@ -54,12 +64,41 @@ ScanPlan plan_scan(int64_t rows, int64_t L) {
     return p;
 }
 
+// grid x times 256 work-items must stay below 2^32
+bool plan_fits(const ScanPlan& p) { return p.ntiles <= (int64_t(1) << 23) && p.tiles_per_row < (int64_t(1) << 30); }
+
 bool scan_sizes_ok(int64_t rows, int64_t L) {
     if (rows <= 0 || L <= 0) return false;
     if (L > (int64_t(1) << 40) || rows > (int64_t(1) << 40)) return false;
-    const ScanPlan p = plan_scan(rows, L);
-    // grid x times 256 work-items must stay below 2^32
-    return p.ntiles <= (int64_t(1) << 23) && p.tiles_per_row < (int64_t(1) << 30);
+    return plan_fits(plan_scan(rows, L));
+}
+
+// Workspace that every candidate tile of a valid shape fits.
+size_t scan_ws_bytes(int64_t rows, int64_t L) {
+    size_t b = 0;
+    for (int64_t t : kLsTileCandidates) {
+        const ScanPlan p = plan_scan(rows, L, t);
+        if (plan_fits(p)) b = p.bytes > b ? p.bytes : b;
+    }
+    return b;
+}
+
+// fp32 tiles chosen by linear_scan_autotune, per (device, rows, length).
+std::mutex g_scan_mu;
+std::map<std::array<int64_t, 3>, int64_t> g_scan_tuned;
+
+std::array<int64_t, 3> scan_key(int64_t rows, int64_t L) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = -1;
+    return {dev, rows, L};
+}
+
+// The tile an fp32 linear_scan of this shape runs, and whether it is tuned.
+int64_t scan_tile(int64_t rows, int64_t L, bool* tuned = nullptr) {
+    std::lock_guard<std::mutex> lock(g_scan_mu);
+    const auto it = g_scan_tuned.find(scan_key(rows, L));
+    if (tuned) *tuned = it != g_scan_tuned.end();
+    return it != g_scan_tuned.end() ? it->second : kLsTile;
 }
 
 }  // namespace
@@ -83,23 +122,30 @@ const char* ssd_strerror(int status) {
 
 size_t linear_scan_workspace_size(int64_t rows, int64_t length) {
     if (!scan_sizes_ok(rows, length)) return 0;
-    return plan_scan(rows, length).bytes;
+    return scan_ws_bytes(rows, length);
 }
 
-// in_fmt / out_fmt: 0 fp32, 1 bf16, 2 fp16; hs: the Hillis-Steele in-tile scan
+// in_fmt / out_fmt: 0 fp32, 1 bf16, 2 fp16; hs: the Hillis-Steele in-tile
+// scan; tile: elements per tile (0: the tuned fp32 tile of the shape, else the
+// built-in one).
 static int linear_scan_launch(const void* a, const void* b, void* h, int64_t rows, int64_t length, int in_fmt,
-                              int out_fmt, void* workspace, size_t workspace_bytes, void* stream, int hs = 0) {
+                              int out_fmt, void* workspace, size_t workspace_bytes, void* stream, int hs = 0,
+                              int64_t tile = 0) {
     if (!a || !b || !h || !workspace) return SSD_ERR_NULL;
     if (!scan_sizes_ok(rows, length)) return SSD_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(b) || !aligned16(h) || !aligned16(workspace)) return SSD_ERR_ALIGN;
-    const ScanPlan p = plan_scan(rows, length);
+    if (tile == 0) tile = (in_fmt == 0 && out_fmt == 0 && !hs) ? scan_tile(rows, length) : kLsTile;
+    const ScanPlan p = plan_scan(rows, length, tile);
+    if (!plan_fits(p)) return SSD_ERR_SHAPE;
     if (workspace_bytes < p.bytes) return SSD_ERR_WORKSPACE;
     char* ws = static_cast<char*>(workspace);
-    return cls_launch_linear_scan(a, b, h, rows, length, in_fmt, out_fmt, p.segmented ? 1 : 0, int(p.tiles_per_row),
-                                  int(p.rows_per_tile), p.ntiles,
-                                  reinterpret_cast<uint32_t*>(ws + p.claim_off),
-                                  reinterpret_cast<uint32_t*>(ws + p.done_off), ws + p.status_off,
-                                  reinterpret_cast<uint32_t*>(ws), static_cast<hipStream_t>(stream), hs);
+    const int st = cls_launch_linear_scan(a, b, h, rows, length, in_fmt, out_fmt, p.segmented ? 1 : 0,
+                                          int(p.tiles_per_row), int(p.rows_per_tile), p.ntiles,
+                                          reinterpret_cast<uint32_t*>(ws + p.claim_off),
+                                          reinterpret_cast<uint32_t*>(ws + p.done_off), ws + p.status_off,
+                                          reinterpret_cast<uint32_t*>(ws), static_cast<hipStream_t>(stream), hs,
+                                          int(tile));
+    return st == 0 ? SSD_OK : st == -2 ? SSD_ERR_SHAPE : SSD_ERR_HIP;
 }
 
 int linear_scan(const float* a, const float* b, float* h, int64_t rows, int64_t length,
@@ -111,15 +157,18 @@ int linear_scan_noalloc(const float* a, const float* b, float* h, int64_t rows, 
     if (!a || !b || !h) return SSD_ERR_NULL;
     if (!scan_sizes_ok(rows, length)) return SSD_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(b) || !aligned16(h)) return SSD_ERR_ALIGN;
-    const ScanPlan p = plan_scan(rows, length);
-    if (p.bytes > CLS_NOALLOC_SCAN_SCRATCH_BYTES) return SSD_ERR_WORKSPACE;
+    if (scan_ws_bytes(rows, length) > CLS_NOALLOC_SCAN_SCRATCH_BYTES) return SSD_ERR_WORKSPACE;
+    // the tile linear_scan runs for this shape (tuned or built-in), fixed here
+    // so the cleared range and the launch agree
+    const int64_t tile = scan_tile(rows, length);
+    const ScanPlan p = plan_scan(rows, length, tile);
     void* ws = nullptr;
     if (cls_noalloc_scratch(&ws) != 0) return SSD_ERR_HIP;
     // the array keeps whatever the last call left: clear the counters, the
     // status words and the error word this call uses
     const hipStream_t s = static_cast<hipStream_t>(stream);
     if (cls_zero_fill(ws, round_up(p.bytes, 16), s) != 0) return SSD_ERR_HIP;
-    return linear_scan_launch(a, b, h, rows, length, 0, 0, ws, CLS_NOALLOC_SCAN_SCRATCH_BYTES, stream);
+    return linear_scan_launch(a, b, h, rows, length, 0, 0, ws, CLS_NOALLOC_SCAN_SCRATCH_BYTES, stream, 0, tile);
 }
 
 int linear_scan_typed(const void* a, const void* b, void* h, int64_t rows, int64_t length, int in_dtype,
@@ -130,9 +179,75 @@ int linear_scan_typed(const void* a, const void* b, void* h, int64_t rows, int64
                               stream);
 }
 
+int linear_scan_planned(const float* a, const float* b, float* h, int64_t rows, int64_t length, int64_t tile,
+                        void* workspace, size_t workspace_bytes, void* stream) {
+    if (tile != 0 && tile != 4096 && tile != 8192 && tile != 16384) return SSD_ERR_SHAPE;
+    return linear_scan_launch(a, b, h, rows, length, 0, 0, workspace, workspace_bytes, stream, 0, tile);
+}
+
+int linear_scan_autotune(const float* a, const float* b, float* h, int64_t rows, int64_t length, void* workspace,
+                         size_t workspace_bytes, void* stream, int reps, int64_t* tile, float* ms_per_call) {
+    if (!tile || !ms_per_call) return SSD_ERR_NULL;
+    *tile = 0;
+    *ms_per_call = 0.0f;
+    if (!a || !b || !h || !workspace) return SSD_ERR_NULL;
+    if (!scan_sizes_ok(rows, length)) return SSD_ERR_SHAPE;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(h) || !aligned16(workspace)) return SSD_ERR_ALIGN;
+    if (workspace_bytes < scan_ws_bytes(rows, length)) return SSD_ERR_WORKSPACE;
+    if (reps < 1 || reps > 10000) return SSD_ERR_SHAPE;
+    std::vector<int64_t> cands;  // valid tiles, the built-in one first
+    for (int64_t t : kLsTileCandidates)
+        if (plan_fits(plan_scan(rows, length, t))) cands.push_back(t);
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    size_t chosen = 0;
+    float ms = 0.0f;
+    const int st = cls::tune_candidates(
+        cands.size(),
+        [&](size_t i) {
+            return linear_scan_launch(a, b, h, rows, length, 0, 0, workspace, workspace_bytes, stream, 0, cands[i]);
+        },
+        s, reps, SSD_ERR_HIP, &chosen, &ms);
+    if (st != SSD_OK) return st;
+    {
+        std::lock_guard<std::mutex> lock(g_scan_mu);
+        g_scan_tuned[scan_key(rows, length)] = cands[chosen];
+    }
+    *tile = cands[chosen];
+    *ms_per_call = ms;
+    // h ends as a later linear_scan of this shape returns it
+    return linear_scan_launch(a, b, h, rows, length, 0, 0, workspace, workspace_bytes, stream, 0, cands[chosen]);
+}
+
+int linear_scan_plan(int64_t rows, int64_t length, int64_t* tile) {
+    if (!tile) return SSD_ERR_NULL;
+    *tile = 0;
+    if (!scan_sizes_ok(rows, length)) return SSD_ERR_SHAPE;
+    bool tuned = false;
+    *tile = scan_tile(rows, length, &tuned);
+    return tuned ? 1 : 0;
+}
+
+void linear_scan_autotune_reset(void) {
+    std::lock_guard<std::mutex> lock(g_scan_mu);
+    g_scan_tuned.clear();
+}
+
 int linear_scan_hillis_steele(const float* a, const float* b, float* h, int64_t rows, int64_t length,
                               void* workspace, size_t workspace_bytes, void* stream) {
     return linear_scan_launch(a, b, h, rows, length, 0, 0, workspace, workspace_bytes, stream, 1);
+}
+
+int stream_mul_f32(const float* a, const float* b, float* h, int64_t n, int vec, int nt, int64_t grid_blocks,
+                   void* stream) {
+    if (!a || !b || !h) return SSD_ERR_NULL;
+    if (!aligned16(a) || !aligned16(b) || !aligned16(h)) return SSD_ERR_ALIGN;
+    if (n <= 0 || n % 4 != 0 || n > (int64_t(1) << 40)) return SSD_ERR_SHAPE;
+    if (!(vec == 1 || vec == 2 || vec == 4 || vec == 8) || (nt != 0 && nt != 1)) return SSD_ERR_SHAPE;
+    if (grid_blocks < 0 || grid_blocks > (int64_t(1) << 23)) return SSD_ERR_SHAPE;
+    if (grid_blocks == 0 && (n / 4 + 256 * vec - 1) / (256 * vec) > (int64_t(1) << 23)) return SSD_ERR_SHAPE;
+    return cls_launch_stream_mul(a, b, h, n, vec, nt, grid_blocks, static_cast<hipStream_t>(stream)) == 0
+               ? SSD_OK
+               : SSD_ERR_HIP;
 }
 
 size_t ssd_fwd_workspace_size(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,

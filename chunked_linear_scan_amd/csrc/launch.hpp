@@ -55,11 +55,12 @@ int cls_noalloc_scratch(void** ptr);
 // Zero `bytes` (a multiple of 16) at p with a store kernel on `stream`.
 int cls_zero_fill(void* p, size_t bytes, hipStream_t stream);
 // a, b and h: fp32 (format 0), bf16 (1) or fp16 (2); hs = 1: the
-// Hillis-Steele in-tile scan (fp32 only).
+// Hillis-Steele in-tile scan (fp32 only); tile: elements per tile, 8192, or
+// 4096 or 16384 for fp32 without hs (else -2).
 int cls_launch_linear_scan(const void* a, const void* b, void* h, int64_t rows, int64_t L, int in_fmt, int out_fmt,
                            int segmented, int tiles_per_row, int rows_per_tile, int64_t ntiles,
                            uint32_t* claim, uint32_t* done, void* status, uint32_t* err,
-                           hipStream_t stream, int hs);
+                           hipStream_t stream, int hs, int tile);
 
 // Shape/dtype/chunk validation shared by sizing and launching (SSD_OK or a
 // negative status).
@@ -78,6 +79,11 @@ int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t stream, in
 int cls_ssd_plan_query(const SsdShape& s, int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces, int64_t* sub_chunk,
                        int* s3);
 void cls_ssd_autotune_reset();
+// h[i] = a[i] b[i] for i < n (stream_ceiling.hip): n a multiple of 4, vec 1,
+// 2, 4 or 8 (else -2), nt 0 or 1, grid_blocks 0 (one pass) or the grid of a
+// grid-stride loop; arguments already validated.
+int cls_launch_stream_mul(const float* a, const float* b, float* h, int64_t n, int vec, int nt,
+                          int64_t grid_blocks, hipStream_t s);
 // Three-pass linear scan (linear_scan_3pass.hip); shapes already validated.
 size_t cls_ls3_workspace_bytes(int64_t rows, int64_t L);
 int cls_ls3_launch(const float* a, const float* b, float* h, int64_t rows, int64_t L, void* ws, hipStream_t stream);

@@ -7,7 +7,8 @@
 // in registers) follows its section "The five kernels" (levels 3b and 3c).
 //
 // MI355X choices:
-//   * a tile is 4 waves x 2048 elements; each wave owns a contiguous run and
+//   * a tile is 4 waves x 2048 elements (the built-in choice; fp32 scans may
+//     also run 1024 or 4096 per wave); each wave owns a contiguous run and
 //     loads it as 16-byte vectors (4 fp32 or 8 bf16 items per lane) with
 //     lanes 16 bytes apart, so every wave-wide load covers 1 KB of
 //     consecutive memory; a 16-byte aligned
@@ -29,12 +30,16 @@
 //   * a claimed index outside the row is treated as an empty tile, so even a
 //     corrupted workspace can only produce wrong values and bounded waits,
 //     never an out-of-range address;
-//   * the output is written with non-temporal stores (it is never re-read);
+//   * inputs are read with non-temporal loads (each is read once); fp32
+//     outputs are stored with the default policy, 1-3 % faster than
+//     non-temporal stores (measured), 16-bit outputs non-temporally;
 //   * rows no longer than a tile are packed whole into tiles and scanned with a
 //     row-start reset flag, with no look-back at all;
 //   * a, b and h may each be fp32 or bf16: bf16 items are widened to fp32 at
 //     the load and rounded to nearest even once at the store; the scan
 //     itself is fp32 either way.
+#include <type_traits>
+
 #include "common.hpp"
 #include "device_once.hpp"
 #include "launch.hpp"
@@ -43,8 +48,9 @@ namespace cls {
 
 constexpr int kLsThreads = 256;
 constexpr int kLsWaves = kLsThreads / 64;
-constexpr int kLsWaveRun = 2048;                 // elements per wave
-constexpr int kLsTile = kLsWaves * kLsWaveRun;   // 8192 elements per tile
+// Elements per wave (RUN) and per tile (4 RUN): 2048 / 8192 is the built-in
+// choice for every element type; fp32 scans also have 1024 / 4096 and
+// 4096 / 16384 instances, which the autotuner may pick per shape.
 // Each look-back poll sleeps ~64 clocks; 2^24 polls is several seconds, far
 // beyond any legitimate wait, so a corrupted workspace ends the kernel instead
 // of hanging it (the error word is raised and the tile treats the missing
@@ -163,8 +169,7 @@ __device__ __forceinline__ void store_items(float* __restrict__ p, int64_t i, in
     if (full || (i >= lo && i + N <= hi)) {
 #pragma unroll
         for (int c = 0; c < N; c += 4)
-            __builtin_nontemporal_store(f32x4{v[c], v[c + 1], v[c + 2], v[c + 3]},
-                                        reinterpret_cast<f32x4*>(p + i + c));
+            *reinterpret_cast<f32x4*>(p + i + c) = f32x4{v[c], v[c + 1], v[c + 2], v[c + 3]};
         return;
     }
 #pragma unroll
@@ -352,7 +357,7 @@ __device__ __forceinline__ void hillis_steele_step(float (&x_a)[4], float (&x_b)
 
 // HS: the in-tile scan by Hillis-Steele rounds (fp32 items only) instead of
 // serial items plus the wave scan; tiles, look-back and stores are shared.
-template <bool SEGMENTED, typename TIn, typename TOut, bool HS = false>
+template <bool SEGMENTED, typename TIn, typename TOut, bool HS = false, int RUN = 2048>
 __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
     const TIn* __restrict__ a, const TIn* __restrict__ b, TOut* __restrict__ h,
     int64_t rows, int64_t L, int tiles_per_row, int rows_per_tile,
@@ -384,17 +389,18 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
     }
     const bool in_range = SEGMENTED || cnt < uint32_t(tiles_per_row);
     const int j = in_range ? int(cnt) : 0;
-    const int64_t abase = (lo & ~int64_t(3)) + int64_t(j) * kLsTile;
+    constexpr int TILE = kLsWaves * RUN;
+    const int64_t abase = (lo & ~int64_t(3)) + int64_t(j) * TILE;
     const bool empty_tile = !SEGMENTED && (!in_range || abase >= hi);
     constexpr int IPL = ItemsPerLane<TIn>::value;  // items per lane and step
     // An fp32 tile wholly inside its row (every tile but a row's first and
     // last, unless the row is tile-aligned) loads and stores without bounds
     // checks: 1-2 % faster for fp32, slower for bf16 items (measured), which
     // keep the checked form.
-    const bool full = IPL == 4 && !empty_tile && abase >= lo && abase + kLsTile <= hi;
-    constexpr int NS = kLsWaveRun / (64 * IPL);      // steps per wave
+    const bool full = IPL == 4 && !empty_tile && abase >= lo && abase + TILE <= hi;
+    constexpr int NS = RUN / (64 * IPL);             // steps per wave
     constexpr int STEP = 64 * IPL;                   // elements per wave step
-    const int64_t wbase = abase + int64_t(wave) * kLsWaveRun + IPL * lane;  // + STEP q
+    const int64_t wbase = abase + int64_t(wave) * RUN + IPL * lane;  // + STEP q
 
     // LS1: load every step's items; scan the items of each step serially.
     // fp32 items keep their running prefix (a-product, state) per item.  bf16
@@ -405,8 +411,10 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
     float av[PACKED ? 1 : NS][IPL], bv[PACKED ? 1 : NS][IPL];
     u32x4a8 ra[PACKED ? NS : 1], rb[PACKED ? NS : 1];
     float la[NS], lb[NS];  // lane aggregate of each step's items
-    uint32_t rmask = 0;  // bit IPL q + k: the run up to item k of step q holds a row start
-    uint32_t smask = 0;  // bit IPL q + k: item k of step q starts a row (packed items)
+    // one bit per item of the lane (NS IPL of them)
+    using Mask = std::conditional_t<(NS * IPL > 32), uint64_t, uint32_t>;
+    Mask rmask = 0;  // bit IPL q + k: the run up to item k of step q holds a row start
+    Mask smask = 0;  // bit IPL q + k: item k of step q starts a row (packed items)
     if constexpr (PACKED) {
 #pragma unroll
         for (int q = 0; q < NS; ++q) {
@@ -433,7 +441,7 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
                     A = x;
                     Bs = y;
                     f = 1;
-                    smask |= 1u << (IPL * q + k);
+                    smask |= Mask(1) << (IPL * q + k);
                 } else {
                     Bs = fmaf(x, Bs, y);
                     A = A * x;
@@ -441,7 +449,7 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
             }
             la[q] = A;
             lb[q] = Bs;
-            rmask |= uint32_t(f) << (IPL * q + IPL - 1);
+            rmask |= Mask(f) << (IPL * q + IPL - 1);
         }
     } else {
         if (!empty_tile) {
@@ -479,7 +487,7 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
                             av[q][k] = av[q][k - 1] * av[q][k];
                         }
                         f |= reset ? 1 : 0;
-                        rmask |= uint32_t(f) << (IPL * q + k);
+                        rmask |= Mask(f) << (IPL * q + k);
                     }
                 }
                 if constexpr (HS) {
@@ -487,7 +495,7 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
                     // row start does not see what precedes the step
                     hillis_steele_step<SEGMENTED>(av[q], bv[q], hf, lane);
 #pragma unroll
-                    for (int k = 0; k < IPL; ++k) rmask |= uint32_t(hf[k] & 1) << (IPL * q + k);
+                    for (int k = 0; k < IPL; ++k) rmask |= Mask(hf[k] & 1) << (IPL * q + k);
                 }
             }
         } else {
@@ -665,7 +673,7 @@ extern "C" int cls_zero_fill(void* p, size_t bytes, hipStream_t stream) {
 
 namespace {
 
-template <typename TIn, typename TOut>
+template <typename TIn, typename TOut, bool HS = false, int RUN = 2048>
 void launch_typed(const void* a, const void* b, void* h, int64_t rows, int64_t L, int segmented, int tiles_per_row,
                   int rows_per_tile, int64_t ntiles, uint32_t* claim, uint32_t* done, void* status, uint32_t* err,
                   hipStream_t stream) {
@@ -677,11 +685,11 @@ void launch_typed(const void* a, const void* b, void* h, int64_t rows, int64_t L
     TOut* th = static_cast<TOut*>(h);
     uint64_t* st = reinterpret_cast<uint64_t*>(status);
     if (segmented) {
-        hipLaunchKernelGGL((linear_scan_kernel<true, TIn, TOut>), grid, block, 0, stream, ta, tb, th, rows, L,
-                           tiles_per_row, rows_per_tile, claim, done, st, err);
+        hipLaunchKernelGGL((linear_scan_kernel<true, TIn, TOut, HS, RUN>), grid, block, 0, stream, ta, tb, th, rows,
+                           L, tiles_per_row, rows_per_tile, claim, done, st, err);
     } else {
-        hipLaunchKernelGGL((linear_scan_kernel<false, TIn, TOut>), grid, block, 0, stream, ta, tb, th, rows, L,
-                           tiles_per_row, rows_per_tile, claim, done, st, err);
+        hipLaunchKernelGGL((linear_scan_kernel<false, TIn, TOut, HS, RUN>), grid, block, 0, stream, ta, tb, th, rows,
+                           L, tiles_per_row, rows_per_tile, claim, done, st, err);
     }
 }
 
@@ -708,25 +716,28 @@ void launch_in(const void* a, const void* b, void* h, int64_t rows, int64_t L, i
 }  // namespace
 
 // in_fmt / out_fmt: 0 fp32, 1 bf16, 2 fp16; hs: the Hillis-Steele in-tile
-// scan (fp32 in and out only).
+// scan (fp32 in and out only); tile: elements per tile, 8192, or 4096 or
+// 16384 for fp32 in and out without hs (else -2).
 extern "C" int cls_launch_linear_scan(const void* a, const void* b, void* h, int64_t rows, int64_t L,
                                       int in_fmt, int out_fmt, int segmented, int tiles_per_row, int rows_per_tile,
                                       int64_t ntiles, uint32_t* claim, uint32_t* done, void* status,
-                                      uint32_t* err, hipStream_t stream, int hs) {
+                                      uint32_t* err, hipStream_t stream, int hs, int tile) {
     using namespace cls;
+    const bool f32 = in_fmt == 0 && out_fmt == 0;
+    if (tile != 8192 && (!f32 || hs || (tile != 4096 && tile != 16384))) return -2;
     if (hs) {
-        const dim3 grid{uint32_t(ntiles), 1u, 1u};
-        const dim3 block{uint32_t(kLsThreads), 1u, 1u};
-        const float* ta = static_cast<const float*>(a);
-        const float* tb = static_cast<const float*>(b);
-        float* th = static_cast<float*>(h);
-        uint64_t* st = reinterpret_cast<uint64_t*>(status);
-        if (segmented)
-            hipLaunchKernelGGL((linear_scan_kernel<true, float, float, true>), grid, block, 0, stream, ta, tb, th,
-                               rows, L, tiles_per_row, rows_per_tile, claim, done, st, err);
-        else
-            hipLaunchKernelGGL((linear_scan_kernel<false, float, float, true>), grid, block, 0, stream, ta, tb, th,
-                               rows, L, tiles_per_row, rows_per_tile, claim, done, st, err);
+        launch_typed<float, float, true>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles, claim,
+                                         done, status, err, stream);
+        return hipGetLastError() == hipSuccess ? 0 : -7;
+    }
+    if (tile == 4096) {
+        launch_typed<float, float, false, 1024>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles,
+                                                claim, done, status, err, stream);
+        return hipGetLastError() == hipSuccess ? 0 : -7;
+    }
+    if (tile == 16384) {
+        launch_typed<float, float, false, 4096>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles,
+                                                claim, done, status, err, stream);
         return hipGetLastError() == hipSuccess ? 0 : -7;
     }
     switch (in_fmt) {

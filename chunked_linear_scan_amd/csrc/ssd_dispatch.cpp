@@ -9,6 +9,7 @@
 #include "../../include/chunked_linear_scan.h"
 #include "launch.hpp"
 #include "ssd_kernels.hpp"
+#include "tune.hpp"
 
 namespace cls {
 
@@ -386,16 +387,11 @@ extern "C" int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, const SsdLaun
 }
 
 // Autotuner of the fused path's plan (segment plan, inter-segment scheme,
-// sub-chunk): the built-in heuristic's plan is the incumbent.  After one
-// untimed pass over every distinct candidate, each runs `reps` times between
-// two events on the caller's stream, in two rounds, and keeps its better
-// round.  The fastest challenger replaces the incumbent only when it is faster
-// by more than the incumbent's own round-to-round spread (at least 1 %), and
-// again by that margin in a head-to-head of three alternating rounds; so the
-// tuned plan never loses to the heuristic by more than the noise.  The winner
-// is kept for the shape on the current device.  The call ends with one more
-// pass on the chosen plan, so y and h_final hold exactly what a later ssd_fwd
-// call returns.
+// sub-chunk): the built-in heuristic's plan is the incumbent, the timing loop
+// is tune_candidates (tune.hpp), so the tuned plan never loses to the
+// heuristic by more than the noise.  The winner is kept for the shape on the
+// current device.  The call ends with one more pass on the chosen plan, so y
+// and h_final hold exactly what a later ssd_fwd call returns.
 namespace {
 
 struct PlanId {
@@ -452,71 +448,11 @@ extern "C" int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t
     add(&cls::kUseHeuristic);
     for (const cls::SegChoice& c : cands) add(&c);
 
-    hipEvent_t e0 = nullptr, e1 = nullptr;
-    if (hipEventCreate(&e0) != hipSuccess) return SSD_ERR_HIP;
-    if (hipEventCreate(&e1) != hipSuccess) {
-        (void)hipEventDestroy(e0);
-        return SSD_ERR_HIP;
-    }
-    int st = SSD_OK;
-    // mean ms per call of plan i over `reps` calls (after one untimed call)
-    auto time_plan = [&](size_t i, float* out) {
-        st = ssd_launch_plan(s, a, with(&plans[i]), stream);
-        if (st != SSD_OK) return;
-        if (hipEventRecord(e0, stream) != hipSuccess) {
-            st = SSD_ERR_HIP;
-            return;
-        }
-        for (int r = 0; r < reps && st == SSD_OK; ++r) st = ssd_launch_plan(s, a, with(&plans[i]), stream);
-        if (st != SSD_OK) return;
-        float t = 0.0f;
-        if (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
-            hipEventElapsedTime(&t, e0, e1) != hipSuccess) {
-            st = SSD_ERR_HIP;
-            return;
-        }
-        *out = t / float(reps);
-    };
-    for (size_t i = 0; i < plans.size() && st == SSD_OK; ++i) st = ssd_launch_plan(s, a, with(&plans[i]), stream);
-    std::vector<float> t_best(plans.size(), -1.0f);
-    float inc_round[2] = {0.0f, 0.0f};  // the incumbent's two rounds
-    for (int round = 0; round < 2 && st == SSD_OK; ++round)
-        for (size_t i = 0; i < plans.size() && st == SSD_OK; ++i) {
-            float t = 0.0f;
-            time_plan(i, &t);
-            if (st != SSD_OK) break;
-            if (i == 0) inc_round[round] = t;
-            if (t_best[i] < 0.0f || t < t_best[i]) t_best[i] = t;
-        }
     size_t chosen = 0;  // the incumbent
-    float chosen_ms = t_best.empty() ? 0.0f : t_best[0];
-    if (st == SSD_OK && plans.size() > 1) {
-        size_t ch = 1;
-        for (size_t i = 2; i < plans.size(); ++i)
-            if (t_best[i] < t_best[ch]) ch = i;
-        const float spread = std::fabs(inc_round[0] - inc_round[1]) / std::min(inc_round[0], inc_round[1]);
-        const float margin = std::max(spread, 0.01f);
-        if (t_best[ch] < t_best[0] * (1.0f - margin)) {
-            // head-to-head: three alternating rounds, medians compared
-            float ti[3], tc[3];
-            for (int k = 0; k < 3 && st == SSD_OK; ++k) {
-                time_plan(0, &ti[k]);
-                if (st == SSD_OK) time_plan(ch, &tc[k]);
-            }
-            if (st == SSD_OK) {
-                std::sort(ti, ti + 3);
-                std::sort(tc, tc + 3);
-                if (tc[1] < ti[1] * (1.0f - margin)) {
-                    chosen = ch;
-                    chosen_ms = tc[1];
-                } else {
-                    chosen_ms = ti[1];
-                }
-            }
-        }
-    }
-    (void)hipEventDestroy(e0);
-    (void)hipEventDestroy(e1);
+    float chosen_ms = 0.0f;
+    const int st = cls::tune_candidates(
+        plans.size(), [&](size_t i) { return ssd_launch_plan(s, a, with(&plans[i]), stream); }, stream, reps,
+        SSD_ERR_HIP, &chosen, &chosen_ms);
     if (st != SSD_OK) return st;
     const cls::SegChoice best = plans[chosen];
     {

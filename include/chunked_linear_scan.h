@@ -173,6 +173,13 @@ void ssd_fwd_autotune_reset(void);
  * each row is split into tiles that publish their aggregate and look back
  * over up to 64 predecessors at a time (decoupled look-back).  The result is
  * bit-identical from run to run.  h must not alias a or b.
+ *
+ * A tile is 8192 elements unless linear_scan_autotune has chosen another
+ * size (4096 or 16384) for this shape on this device; the tile changes only
+ * the fp32 rounding order.  linear_scan_workspace_size covers every tile
+ * size: 256 bytes for rows of up to 4090 elements, else 256 + 8 bytes per row
+ * (rounded up to 256 bytes twice) + 16 bytes per 4096-element tile of every
+ * row.
  */
 size_t linear_scan_workspace_size(int64_t rows, int64_t length);
 
@@ -189,15 +196,45 @@ int linear_scan(const float* a, const float* b, float* h, int64_t rows,
  * buffer.  Nothing is allocated or freed.  Each call first clears the part of
  * the array it uses with a store kernel on `stream`, then runs the scan.
  * Shapes whose workspace (linear_scan_workspace_size) exceeds 1 MiB return
- * SSD_ERR_WORKSPACE with nothing enqueued: rows of up to 8186 elements need
- * none beyond a 256-byte header, longer rows need 16 bytes per 8192-element
- * tile plus 8 bytes per row.  All calls on one GPU share its array: calls
+ * SSD_ERR_WORKSPACE with nothing enqueued: rows of up to 4090 elements need
+ * none beyond a 256-byte header, longer rows need 16 bytes per 4096 elements
+ * plus 8 bytes per row.  It runs the tile linear_scan runs for the shape
+ * (tuned or built-in).  All calls on one GPU share its array: calls
  * that may overlap on one GPU (other streams, other host threads) race and
  * must be serialised by the caller.  Same layouts, alignment and status codes
  * as linear_scan.
  */
 int linear_scan_noalloc(const float* a, const float* b, float* h, int64_t rows,
                         int64_t length, void* stream);
+
+/*
+ * Autotuner of linear_scan's tile size ("Accelerating Mamba-2 ...", section
+ * "Optimizations", which closes with an autotuner that picks kernel settings
+ * per input shape).  The tile size is a compile-time setting of the kernel;
+ * fp32 instances exist for 4096, 8192 (the built-in choice, the incumbent)
+ * and 16384 elements per tile.  Each runs `reps` times (1..10000) in two
+ * timed rounds on the caller's arguments; a challenger replaces the built-in
+ * tile only when faster by more than the built-in tile's own round-to-round
+ * spread (at least 1 %), and again by that margin in a head-to-head of three
+ * alternating rounds.  The winner is kept per (device, rows, length) for the
+ * life of the process: later fp32 linear_scan, linear_scan_typed (fp32 in
+ * and out) and linear_scan_noalloc calls of that shape use it.  On return h
+ * holds what such a later call returns, *tile the chosen size and
+ * *ms_per_call its mean time.  Blocking (waits for the timed rounds).  Same
+ * arguments, workspace (linear_scan_workspace_size) and status codes as
+ * linear_scan, plus SSD_ERR_NULL for tile or ms_per_call and SSD_ERR_SHAPE
+ * for reps out of range.
+ */
+int linear_scan_autotune(const float* a, const float* b, float* h, int64_t rows,
+                         int64_t length, void* workspace, size_t workspace_bytes,
+                         void* stream, int reps, int64_t* tile, float* ms_per_call);
+
+/* The tile an fp32 linear_scan of this shape runs on the current device:
+ * returns 1 (tuned), 0 (built-in), or SSD_ERR_SHAPE / SSD_ERR_NULL. */
+int linear_scan_plan(int64_t rows, int64_t length, int64_t* tile);
+
+/* Forgets every tuned scan tile (all devices). */
+void linear_scan_autotune_reset(void);
 
 /*
  * linear_scan with fp32, bf16 or fp16 elements.  The page's scan is fp32 only

@@ -75,6 +75,36 @@ size_t ssd_fwd_planned_workspace_size(int64_t batch, int64_t seqlen, int64_t nhe
                                       int64_t headdim, int64_t dstate, int64_t ngroups,
                                       int64_t chunk, int dtype, const ssd_plan_request* plan);
 
+/*
+ * linear_scan with the tile size chosen by the caller: tile 4096, 8192 or
+ * 16384 elements (0: what linear_scan would run for the shape), else
+ * SSD_ERR_SHAPE.  Parity tests use it to run every tile instance; nothing it
+ * sets outlives the call.  All of linear_scan's arguments, checks, workspace
+ * rule (linear_scan_workspace_size covers every tile) and status codes
+ * apply.
+ */
+int linear_scan_planned(const float* a, const float* b, float* h, int64_t rows, int64_t length,
+                        int64_t tile, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * A plain streaming kernel with linear_scan's HBM traffic: h[i] = a[i] * b[i]
+ * for 0 <= i < n (read two fp32 arrays, write one).  It is no part of the
+ * scan: it measures what a kernel that only streams those bytes reaches on
+ * the device, the ceiling the scan's bandwidth is read against.
+ *
+ * a, b, h: n fp32 each, 16-byte aligned; h must not alias a or b.  n: a
+ * positive multiple of 4, at most 2^40.  vec: 16-byte vectors of each array a
+ * thread moves per iteration, 1, 2, 4 or 8.  nt: 1 for non-temporal loads and
+ * stores (the scan's policy), 0 for the default policy.  grid_blocks: 0 for
+ * one pass (one 256-thread workgroup per 256 * vec vectors), else 1 .. 2^23
+ * workgroups in a grid-stride loop.  Returns SSD_OK, SSD_ERR_NULL,
+ * SSD_ERR_ALIGN, SSD_ERR_SHAPE (n, vec, nt or grid_blocks out of range, or a
+ * one-pass grid above 2^23 workgroups) or SSD_ERR_HIP.  Asynchronous on
+ * `stream`.
+ */
+int stream_mul_f32(const float* a, const float* b, float* h, int64_t n, int vec, int nt,
+                   int64_t grid_blocks, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,8 @@ def header_functions():
 def test_header_lists_expected_entry_points():
     assert set(header_functions()) == {
         "ssd_fwd_workspace_size", "ssd_fwd", "ssd_fwd_autotune", "ssd_fwd_plan", "ssd_fwd_autotune_reset",
-        "linear_scan_workspace_size", "linear_scan", "linear_scan_typed", "linear_scan_noalloc", "linear_scan_hillis_steele", "ssd_step", "linear_scan_three_pass_workspace_size", "linear_scan_three_pass", "ssd_strerror"}
+        "linear_scan_workspace_size", "linear_scan", "linear_scan_typed", "linear_scan_noalloc", "linear_scan_hillis_steele", "ssd_step", "linear_scan_three_pass_workspace_size", "linear_scan_three_pass", "ssd_strerror",
+        "linear_scan_autotune", "linear_scan_plan", "linear_scan_autotune_reset"}
 
 
 def test_library_exports_every_declared_symbol():
@@ -67,6 +68,38 @@ def test_linear_scan_workspace_size_is_monotone_and_row_scaled():
     assert short > 0 and long1 > 0
     assert long384 > long1
     assert long384 >= 384 * 8 * 16  # one 16-byte status word per 8192-element tile
+
+
+def test_scan_workspace_covers_every_tile_size():
+    """The size covers the smallest candidate tile (4096 elements): rows past
+    4090 elements need status words even where 8192-element tiles pack them."""
+    lib = cls.load_library()
+    assert lib.linear_scan_workspace_size(5, 4090) == 256      # every tile size packs these rows
+    assert lib.linear_scan_workspace_size(2, 8000) == 256 + 256 + 256 + 2 * 2 * 16
+    # a row's tiles cover it from the 16-byte boundary at or before its start
+    tiles = (65536 + 3 + 4095) // 4096
+    assert lib.linear_scan_workspace_size(384, 65536) == 256 + 2 * 1536 + 384 * tiles * 16
+
+
+def test_scan_plan_and_tuner_validate_on_host():
+    lib = cls.load_library()
+    lib.linear_scan_autotune_reset()
+    tile = ctypes.c_int64()
+    assert lib.linear_scan_plan(4, 100, ctypes.byref(tile)) == 0 and tile.value == 8192
+    assert lib.linear_scan_plan(0, 100, ctypes.byref(tile)) == -2
+    assert lib.linear_scan_plan(4, 100, None) == -1
+    ws = lib.linear_scan_workspace_size(4, 100)
+    for bad in (1000, 8193, -1, 32768):
+        assert lib.linear_scan_planned(FAKE, FAKE, FAKE, 4, 100, bad, FAKE, ws, None) == -2, bad
+    assert lib.linear_scan_planned(None, FAKE, FAKE, 4, 100, 4096, FAKE, ws, None) == -1
+    ms = ctypes.c_float()
+    assert lib.linear_scan_autotune(FAKE, FAKE, FAKE, 4, 100, FAKE, ws, None, 5, None, ctypes.byref(ms)) == -1
+    assert lib.linear_scan_autotune(FAKE, FAKE, FAKE, 4, 100, FAKE, ws, None, 0, ctypes.byref(tile),
+                                    ctypes.byref(ms)) == -2
+    assert lib.linear_scan_autotune(FAKE, FAKE, FAKE, 4, 100, FAKE, ws - 16, None, 5, ctypes.byref(tile),
+                                    ctypes.byref(ms)) in (-6, -2)
+    assert lib.linear_scan_autotune(FAKE, FAKE, FAKE, 0, 100, FAKE, ws, None, 5, ctypes.byref(tile),
+                                    ctypes.byref(ms)) == -2
 
 
 def test_ssd_rejects_bad_arguments():
@@ -213,10 +246,23 @@ TESTING_HEADER = os.path.join(ROOT, "include", "chunked_linear_scan_testing.h")
 def test_testing_header_entry_points_are_exported():
     text = re.sub(r"/\*.*?\*/", "", open(TESTING_HEADER).read(), flags=re.S)
     names = sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", text)) - {"if", "sizeof", "defined"})
-    assert names == ["ssd_fwd_planned", "ssd_fwd_planned_workspace_size"]
+    assert names == ["linear_scan_planned", "ssd_fwd_planned", "ssd_fwd_planned_workspace_size", "stream_mul_f32"]
     lib = ctypes.CDLL(cls.LIB_PATH)
     for name in names:
         assert hasattr(lib, name), name
+
+
+def test_stream_kernel_rejects_bad_arguments():
+    lib = cls.load_library()
+
+    def call(a=FAKE, b=FAKE, h=FAKE, n=1024, vec=4, nt=1, grid=0):
+        return lib.stream_mul_f32(a, b, h, n, vec, nt, grid, None)
+
+    assert call(a=None) == -1
+    assert call(h=ctypes.c_void_p(0x10004)) == -5
+    for bad in (dict(n=0), dict(n=1022), dict(n=-4), dict(vec=3), dict(vec=16), dict(nt=2), dict(grid=-1),
+                dict(grid=(1 << 23) + 1), dict(n=1 << 41)):
+        assert call(**bad) == -2, bad
 
 
 def test_no_process_wide_override_hooks():

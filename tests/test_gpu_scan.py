@@ -217,3 +217,19 @@ def test_hillis_steele_special_cases_and_determinism():
     first = cls.linear_scan_hillis_steele(a, bb)
     for i in range(100):
         assert torch.equal(cls.linear_scan_hillis_steele(a, bb), first), i
+
+
+@pytest.mark.parametrize("vec,nt,grid", [(1, 1, 0), (2, 0, 0), (4, 1, 0), (8, 1, 0), (8, 0, 0), (4, 1, 7),
+                                         (8, 0, 300)])
+def test_stream_kernel_is_an_exact_product(vec, nt, grid):
+    """The streaming ceiling kernel computes h = a * b (one fp32 rounding, the
+    same as torch's product) over every element, ragged tails included."""
+    print(f"[stream] vec={vec} nt={nt} grid={grid}", flush=True)
+    g = torch.Generator().manual_seed(vec * 10 + nt + grid)
+    for n in (4, 1020, 256 * 4 * vec + 12, 1 << 20):
+        a = torch.randn(n, generator=g).cuda()
+        b = torch.randn(n, generator=g).cuda()
+        h = torch.full_like(a, float("nan"))
+        cls.stream_mul(a, b, out=h, vec=vec, nt=bool(nt), grid_blocks=grid)
+        torch.cuda.synchronize()
+        assert torch.equal(h, a * b), n
