@@ -71,6 +71,7 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
         // outputs, 16 rows at a time
         for (int i0 = 0; i0 < n; i0 += 16) {
             const int nr = (n - i0 < 16) ? (n - i0) : 16;
+#pragma unroll 4
             for (int q = tid; q < 16 * S; q += kF32Threads) {
                 const int r = q / S, ss = q % S;
                 Cb[q] = (r < nr) ? Cm[((b * L + tok0 + i0 + r) * p.G + g) * S + ss] : 0.0f;
@@ -82,7 +83,19 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
                 const float* brow = Bm + ((b * L + tok0 + j) * p.G + g) * S;
-                for (int ss = 0; ss < S; ++ss) {
+                // eight loads in flight at a time: one at a time, each waited for
+                // before the next, the chunk cost a global-memory latency per item
+                int ss = 0;
+                for (; ss + 8 <= S; ss += 8) {
+                    float bv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) bv[e] = brow[ss + e];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) acc[r] = fmaf(Cb[r * S + ss + e], bv[e], acc[r]);
+                }
+                for (; ss < S; ++ss) {
                     const float bv = brow[ss];
 #pragma unroll
                     for (int r = 0; r < 16; ++r) acc[r] = fmaf(Cb[r * S + ss], bv, acc[r]);
@@ -103,8 +116,17 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
                 float s1 = 0.0f;
                 for (int ss = 0; ss < S; ++ss) s1 = fmaf(Cb[r * S + ss], Hs[pp * HP + ss], s1);
                 float out = expf(Gs[i]) * s1;
-                for (int j = 0; j <= i; ++j)
-                    out = fmaf(Wb[r * 256 + j], x[((b * L + tok0 + j) * p.H + h) * P + pp], out);
+                const float* xc = x + ((b * L + tok0) * p.H + h) * P + pp;  // token j at j * H * P
+                const int64_t xs = int64_t(p.H) * P;
+                int j = 0;
+                for (; j + 8 <= i + 1; j += 8) {  // eight loads in flight, as above
+                    float xv[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) xv[e] = xc[(j + e) * xs];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) out = fmaf(Wb[r * 256 + j + e], xv[e], out);
+                }
+                for (; j <= i; ++j) out = fmaf(Wb[r * 256 + j], xc[j * xs], out);
                 y[((b * L + tok0 + i) * p.H + h) * P + pp] = out;
             }
             __syncthreads();
@@ -114,10 +136,12 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
         const float alpha = expf(Glast);
         for (int j0 = 0; j0 < n; j0 += 32) {
             const int nj = (n - j0 < 32) ? (n - j0) : 32;
+#pragma unroll 4
             for (int q = tid; q < 32 * P; q += kF32Threads) {
                 const int jj = q / P, pp = q % P;
                 Xs[q] = (jj < nj) ? ws[j0 + jj] * x[((b * L + tok0 + j0 + jj) * p.H + h) * P + pp] : 0.0f;
             }
+#pragma unroll 4
             for (int q = tid; q < 32 * S; q += kF32Threads) {
                 const int jj = q / S, ss = q % S;
                 Bs[q] = (jj < nj) ? Bm[((b * L + tok0 + j0 + jj) * p.G + g) * S + ss] : 0.0f;
