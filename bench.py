@@ -38,7 +38,9 @@ to the metric's unit.
 
 Other modes: ``--scan-ceiling-sweep``, ``--copy-probe`` / ``--record-traffic``
 (HBM traffic counters), ``--no-autotune``, ``--no-cpu-baseline``,
-``--only-headline`` (the headline workload alone, for counter runs).
+``--only-headline`` (the headline workload alone, for counter runs),
+``--no-side-ssd`` (the headline, the scans and the decode step: a counter run
+that holds one SSD shape), ``--s3-ab`` (the two inter-segment schemes).
 
 Prints exactly one JSON line.
 """
@@ -170,7 +172,7 @@ def record_traffic(fetch_csv, write_csv, workload):
         return statistics.mean(f) * sf * 1024, statistics.mean(w) * sw * 1024, len(f)
 
     groups = [("ssd_fwd:" + workload, SSD_SOURCES, ["ssd_cbt_kernel<", "ssd_fused_agg_kernel<", "ssd_fused_kernel<"]),
-              ("linear_scan:scan", SCAN_SOURCES, ["linear_scan_kernel<false, float, float>"]),
+              ("linear_scan:scan", SCAN_SOURCES, ["linear_scan_kernel<false, float, float, false, 2048>"]),
               ("ssd_step:decode_large", STEP_SOURCES, ["ssd_step_kernel"])]
     for key, srcs, pats in groups:
         parts = {p.rstrip("<"): per_kernel(p) for p in pats}
@@ -707,6 +709,12 @@ def main():
                          "the per-kernel figures)")
     ap.add_argument("--only-headline", action="store_true",
                     help="time the headline workload alone (counter and trace runs)")
+    ap.add_argument("--no-clocks", action="store_true",
+                    help="do not run amd-smi for the clock lines (for runs under a profiler, whose preloaded "
+                         "library would start the GPU in that child too)")
+    ap.add_argument("--no-side-ssd", action="store_true",
+                    help="run no SSD workload but the headline (scans and the decode step still run): "
+                         "counter runs then hold one SSD shape's kernels")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run three plain 1 GiB device copies (the known-size reference that "
                          "scales rocprofv3 FETCH_SIZE/WRITE_SIZE readings)")
@@ -752,13 +760,13 @@ def main():
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
-    clocks_before = gpu_state()
+    clocks_before = None if args.no_clocks else gpu_state()
     head = SsdRunner(args.workload)
     log(f"headline {head.describe()}, {head.nsets} buffer set(s)")
     side = []
     if not args.only_headline:
         for name in ("ssd_large", "ssd_small", "ssd_tiny"):
-            if name != args.workload:
+            if name != args.workload and not args.no_side_ssd:
                 side.append(SsdRunner(name))
         side += [ScanRunner("scan"), ScanRunner("scan_ragged"), ScanRunner("scan", "bf16", "f32"),
                  ScanRunner("scan", "bf16", "bf16"), ScanRunner("scan", "f16", "f32"), ScanRunner("scan", "f16", "f16"),
@@ -778,7 +786,7 @@ def main():
     win = timed_windows(runners, plan)
     t_wall = time.perf_counter() - t_wall
     stats = {r.name: summarize(win[r.name], plan[r.name]) for r in runners}
-    clocks_after = gpu_state()
+    clocks_after = None if args.no_clocks else gpu_state()
     log(f"timed {sum(sum(v) for v in win.values()) * 1e3:.1f} ms of GPU time in {t_wall:.2f} s")
 
     hs = stats[head.name]
