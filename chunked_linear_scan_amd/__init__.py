@@ -33,7 +33,7 @@ class PlanRequest(ctypes.Structure):
     """``ssd_plan_request`` of include/chunked_linear_scan_testing.h."""
     _fields_ = [("path", ctypes.c_int32), ("s3", ctypes.c_int32), ("nsegs", ctypes.c_int64),
                 ("nsplit", ctypes.c_int64), ("agg_pieces", ctypes.c_int64), ("xcds", ctypes.c_int32),
-                ("sub_chunk", ctypes.c_int32)]
+                ("sub_chunk", ctypes.c_int32), ("stress_seed", ctypes.c_uint32)]
 
 
 PATH = {"auto": 0, "chunk": 1, "fused": 2}
@@ -96,7 +96,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.ssd_fwd_planned_workspace_size.restype = sz
         lib.stream_mul_f32.argtypes = [fp, fp, fp, i64, ctypes.c_int, ctypes.c_int, i64, vp]
         lib.stream_mul_f32.restype = ctypes.c_int
-        lib.linear_scan_planned.argtypes = [fp, fp, fp, i64, i64, i64, vp, sz, vp]
+        lib.linear_scan_planned.argtypes = [fp, fp, fp, i64, i64, i64, ctypes.c_uint32, vp, sz, vp]
         lib.linear_scan_planned.restype = ctypes.c_int
         lib.linear_scan_autotune.argtypes = [fp, fp, fp, i64, i64, vp, sz, vp, ctypes.c_int, pi64,
                                              ctypes.POINTER(ctypes.c_float)]
@@ -247,14 +247,14 @@ def _scan_f32_args(lib, a, b, out, workspace):
 
 
 def linear_scan_planned(a: torch.Tensor, b: torch.Tensor, tile: int = 0, out: torch.Tensor | None = None,
-                        workspace: torch.Tensor | None = None) -> torch.Tensor:
+                        workspace: torch.Tensor | None = None, stress_seed: int = 0) -> torch.Tensor:
     """fp32 linear_scan with an explicit tile size (4096, 8192 or 16384
-    elements; 0: what linear_scan runs), ``linear_scan_planned`` of the
-    testing header."""
+    elements; 0: what linear_scan runs) and an optional look-back stress
+    seed, ``linear_scan_planned`` of the testing header."""
     lib = load_library()
     rows, length, h, ws = _scan_f32_args(lib, a, b, out, workspace)
-    st = lib.linear_scan_planned(_ptr(a), _ptr(b), _ptr(h), rows, length, int(tile), _ptr(ws), ws.numel(),
-                                 _stream_handle(a.device))
+    st = lib.linear_scan_planned(_ptr(a), _ptr(b), _ptr(h), rows, length, int(tile), int(stress_seed), _ptr(ws),
+                                 ws.numel(), _stream_handle(a.device))
     if st != SSD_OK:
         raise SSDError(st, "linear_scan_planned")
     return h
@@ -342,10 +342,11 @@ def ssd_fwd(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, want_final_state:
     return y, hf
 
 
-def plan_request(path="auto", s3="auto", nsegs=0, nsplit=0, agg_pieces=0, xcds=0, sub_chunk=0) -> PlanRequest:
+def plan_request(path="auto", s3="auto", nsegs=0, nsplit=0, agg_pieces=0, xcds=0, sub_chunk=0,
+                 stress_seed=0) -> PlanRequest:
     """An explicit plan for ``ssd_fwd_planned`` (see the testing header)."""
     return PlanRequest(PATH[path], S3[s3 or "auto"], int(nsegs), int(nsplit), int(agg_pieces), int(xcds),
-                       int(sub_chunk))
+                       int(sub_chunk), int(stress_seed))
 
 
 def ssd_fwd_planned(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, plan: PlanRequest | None = None,

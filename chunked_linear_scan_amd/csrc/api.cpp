@@ -130,7 +130,7 @@ size_t linear_scan_workspace_size(int64_t rows, int64_t length) {
 // built-in one).
 static int linear_scan_launch(const void* a, const void* b, void* h, int64_t rows, int64_t length, int in_fmt,
                               int out_fmt, void* workspace, size_t workspace_bytes, void* stream, int hs = 0,
-                              int64_t tile = 0) {
+                              int64_t tile = 0, uint32_t stress = 0) {
     if (!a || !b || !h || !workspace) return SSD_ERR_NULL;
     if (!scan_sizes_ok(rows, length)) return SSD_ERR_SHAPE;
     if (!aligned16(a) || !aligned16(b) || !aligned16(h) || !aligned16(workspace)) return SSD_ERR_ALIGN;
@@ -144,7 +144,7 @@ static int linear_scan_launch(const void* a, const void* b, void* h, int64_t row
                                           reinterpret_cast<uint32_t*>(ws + p.claim_off),
                                           reinterpret_cast<uint32_t*>(ws + p.done_off), ws + p.status_off,
                                           reinterpret_cast<uint32_t*>(ws), static_cast<hipStream_t>(stream), hs,
-                                          int(tile));
+                                          int(tile), stress);
     return st == 0 ? SSD_OK : st == -2 ? SSD_ERR_SHAPE : SSD_ERR_HIP;
 }
 
@@ -180,9 +180,10 @@ int linear_scan_typed(const void* a, const void* b, void* h, int64_t rows, int64
 }
 
 int linear_scan_planned(const float* a, const float* b, float* h, int64_t rows, int64_t length, int64_t tile,
-                        void* workspace, size_t workspace_bytes, void* stream) {
+                        uint32_t stress_seed, void* workspace, size_t workspace_bytes, void* stream) {
     if (tile != 0 && tile != 4096 && tile != 8192 && tile != 16384) return SSD_ERR_SHAPE;
-    return linear_scan_launch(a, b, h, rows, length, 0, 0, workspace, workspace_bytes, stream, 0, tile);
+    return linear_scan_launch(a, b, h, rows, length, 0, 0, workspace, workspace_bytes, stream, 0, tile,
+                              stress_seed);
 }
 
 int linear_scan_autotune(const float* a, const float* b, float* h, int64_t rows, int64_t length, void* workspace,
@@ -295,6 +296,7 @@ static bool plan_options(const ssd_plan_request* plan, cls::SegChoice* seg, SsdL
     o->path = plan->path;
     o->s3 = plan->s3;
     o->xcds = plan->xcds;
+    o->stress = plan->stress_seed;
     if (plan->nsegs > 0) {
         *seg = cls::SegChoice{plan->nsegs, plan->nsplit, plan->agg_pieces};
         seg->s3 = plan->s3;

@@ -30,6 +30,7 @@ struct SsdLaunchOpts {
     const cls::SegChoice* force = nullptr;  // segment plan, or null: tuned or heuristic
     int xcds = 0;                          // XCDs of the chain mapping (0: the device's)
     hipEvent_t* ev = nullptr;              // four events to record, or null
+    uint32_t stress = 0;                   // look-back stress seed of the segment look-back (0: none)
 };
 
 struct SsdArgs {
@@ -56,11 +57,12 @@ int cls_noalloc_scratch(void** ptr);
 int cls_zero_fill(void* p, size_t bytes, hipStream_t stream);
 // a, b and h: fp32 (format 0), bf16 (1) or fp16 (2); hs = 1: the
 // Hillis-Steele in-tile scan (fp32 only); tile: elements per tile, 8192, or
-// 4096 or 16384 for fp32 without hs (else -2).
+// 4096 or 16384 for fp32 without hs (else -2); stress: look-back stress seed
+// (fp32 without hs; 0: none).
 int cls_launch_linear_scan(const void* a, const void* b, void* h, int64_t rows, int64_t L, int in_fmt, int out_fmt,
                            int segmented, int tiles_per_row, int rows_per_tile, int64_t ntiles,
                            uint32_t* claim, uint32_t* done, void* status, uint32_t* err,
-                           hipStream_t stream, int hs, int tile);
+                           hipStream_t stream, int hs, int tile, uint32_t stress);
 
 // Shape/dtype/chunk validation shared by sizing and launching (SSD_OK or a
 // negative status).

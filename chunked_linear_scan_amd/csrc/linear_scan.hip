@@ -3,8 +3,11 @@
 // The recurrence and its affine combine follow "Selective-scan CUDA kernels",
 // section "The problem"; the single-pass scheme (tiles claimed in order from a
 // counter, local aggregate published under flag A, look-back over a window of
-// predecessors until an inclusive prefix P is found, items scanned serially
-// in registers) follows its section "The five kernels" (levels 3b and 3c).
+// predecessors to an inclusive prefix P, items scanned serially in registers)
+// follows its section "The five kernels" (levels 3b and 3c).  The look-back
+// is anchored: only every 64th tile publishes an inclusive prefix, and a tile
+// always folds from its anchor, so the combine order (and every bit of the
+// result) does not depend on which predecessors happened to have published.
 //
 // MI355X choices:
 //   * a tile is 4 waves x 2048 elements (the built-in choice; fp32 scans may
@@ -17,9 +20,9 @@
 //   * the in-tile scan is a serial scan over each lane's items of a step, a
 //     64-lane DPP wave scan per step (256 fp32 or 512 bf16 items) with the
 //     step carry kept wave-uniform, and a 4-wave combine through LDS;
-//   * one 64-lane wave inspects 64 predecessors per look-back step and folds
-//     every aggregate between the tile and the nearest inclusive prefix with a
-//     6-step order-preserving tree reduction;
+//   * one 64-lane wave inspects the tile's predecessors back to its anchor
+//     (at most 63) in one step and folds the anchor's inclusive prefix and
+//     the aggregates after it with a 6-step order-preserving tree reduction;
 //   * rows are independent chains: tiles are claimed from one counter per row,
 //     so claims never contend across rows and a row's chain never waits on
 //     another row;
@@ -263,52 +266,64 @@ __device__ __forceinline__ Pair wave_inclusive_scan(Pair w) {
     return w;
 }
 
-// Exclusive prefix of tile j of a row: the ordered combination of tiles
-// 0..j-1.  Runs on one full wave; every lane returns the same value.
-// status_row holds one status word (two 64-bit halves) per tile.
+// Tiles whose index in the row is a multiple of kLsAnchor are anchors: they
+// publish only their inclusive prefix, every other tile only its aggregate.
+constexpr int kLsAnchor = 64;
+
+// Exclusive prefix of tile j > 0 of a row: the inclusive prefix of its anchor
+// a = 64 floor((j - 1) / 64) followed by the aggregates of tiles a + 1 .. j - 1
+// ("anchored" look-back).  The page's tiles take the nearest inclusive prefix
+// they find, so the grouping of the combines, and the fp32 rounding, follows
+// the timing; here the grouping depends on j alone, so every run gives the
+// same bits.  The anchor is at most 63 tiles back: one 64-lane window (lane l
+// reads tile j - 1 - l) always reaches it.  Runs on one full wave; every lane
+// returns the same value.  status_row holds one status word (two 64-bit
+// halves) per tile.
 __device__ Pair lookback(const uint64_t* status_row, int j, uint32_t* err) {
     const int lane = lane_id();
-    Pair acc{1.0f, 0.0f, 0};  // combination of the predecessors already folded
-    int base = j - 1;         // tile inspected by lane 0
+    const int kp = (j - 1) % kLsAnchor;  // the anchor's lane
+    const int p = j - 1 - lane;
+    Pair v{1.0f, 0.0f, 0};
     uint32_t spins = 0;
     while (true) {
-        const int p = base - lane;
-        int kind;  // 2 inclusive, 1 aggregate, 0 not yet published in this call
-        Pair v{1.0f, 0.0f, 0};
-        if (p < 0) {
-            kind = 2;  // before the row start the state is 0: identity prefix
-        } else {
+        bool ready = true;
+        if (lane <= kp) {
             const Status w = load_status(status_row + 2 * int64_t(p));
-            kind = int(w.kind);
-            v.a = w.v.a;
-            v.b = w.v.b;
+            ready = w.kind == (lane == kp ? 2u : 1u);
+            v = Pair{w.v.a, w.v.b, 0};
         }
-        const uint64_t incm = __ballot(kind == 2);
-        const uint64_t notready = __ballot(kind == 0);
-        const int kp = incm ? int(__builtin_ctzll(incm)) : 64;
-        const uint64_t below = (kp >= 64) ? ~0ull : ((1ull << kp) - 1ull);
-        if (notready & below) {
-            if (++spins > kLsSpinLimit) {
-                if (lane == 0) atomic_add_u32(err, 1u);
-                return acc;
-            }
-            __builtin_amdgcn_s_sleep(1);
-            continue;
+        if (__ballot(!ready) == 0) break;
+        if (++spins > kLsSpinLimit) {
+            if (lane == 0) atomic_add_u32(err, 1u);
+            return Pair{1.0f, 0.0f, 0};
         }
-        if (lane > kp) v = Pair{1.0f, 0.0f, 0};
-        // Ordered tree reduction: lane k ends up holding lanes [k, k+2d) with
-        // the higher lane (the earlier tile) applied first.
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-            Pair o{shfl_down(v.a, d), shfl_down(v.b, d), 0};
-            if (lane + d >= 64) o = Pair{1.0f, 0.0f, 0};
-            v = combine(o, v);
-        }
-        const Pair win{bcast_lane0(v.a), bcast_lane0(v.b), 0};
-        acc = combine(win, acc);
-        if (kp < 64) return acc;
-        base -= 64;
+        __builtin_amdgcn_s_sleep(1);
     }
+    if (lane > kp) v = Pair{1.0f, 0.0f, 0};
+    // Ordered tree reduction: lane k ends up holding lanes [k, k+2d) with the
+    // higher lane (the earlier tile) applied first.
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        Pair o{shfl_down(v.a, d), shfl_down(v.b, d), 0};
+        if (lane + d >= 64) o = Pair{1.0f, 0.0f, 0};
+        v = combine(o, v);
+    }
+    return Pair{bcast_lane0(v.a), bcast_lane0(v.b), 0};
+}
+
+// Look-back stress (tests only): with a nonzero seed, wave 0 of about one tile
+// in four sleeps a pseudo-random 0 .. 31 x 8K clocks before it publishes and
+// looks back, so tiles publish out of order.  Seed 0: no delay.
+__device__ __forceinline__ void stress_delay(uint32_t seed, int64_t row, int j) {
+    if (seed == 0) return;
+    uint32_t x = seed ^ (uint32_t(row) * 0x9E3779B1u) ^ (uint32_t(j) * 0x85EBCA77u);
+    x ^= x >> 15;
+    x *= 0x2C1B3C6Du;
+    x ^= x >> 12;
+    x *= 0x297A2D39u;
+    x ^= x >> 15;
+    if ((x & 3u) != 0u) return;
+    for (uint32_t k = (x >> 2) & 31u; k > 0; --k) __builtin_amdgcn_s_sleep(127);
 }
 
 // One tile per workgroup.  SEGMENTED: tiles hold whole rows and reset at each
@@ -362,7 +377,7 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
     const TIn* __restrict__ a, const TIn* __restrict__ b, TOut* __restrict__ h,
     int64_t rows, int64_t L, int tiles_per_row, int rows_per_tile,
     uint32_t* __restrict__ claim, uint32_t* __restrict__ done, uint64_t* __restrict__ status,
-    uint32_t* __restrict__ err) {
+    uint32_t* __restrict__ err, uint32_t stress) {
     __shared__ uint32_t s_claim;
     __shared__ float s_wa[kLsWaves], s_wb[kLsWaves];
     __shared__ int s_wf[kLsWaves];
@@ -557,17 +572,20 @@ __global__ __launch_bounds__(kLsThreads) void linear_scan_kernel(
         tile_agg = combine(tile_agg, s);
     }
 
-    // LS3: publish the aggregate, look back, publish the inclusive prefix.
+    // LS3: publish the aggregate (anchors: nothing yet), look back, and
+    // (anchors only) publish the inclusive prefix.
     uint64_t* srow = status + 2 * row * int64_t(tiles_per_row);
     if (!SEGMENTED) {
         if (wave == 0) {
             Pair prefix{1.0f, 0.0f, 0};
             if (!empty_tile) {
+                stress_delay(stress, row, j);
+                const bool anchor = j % kLsAnchor == 0;
                 if (j > 0) {
-                    if (lane == 0) store_status(srow + 2 * j, 1u, tile_agg);
+                    if (!anchor && lane == 0) store_status(srow + 2 * j, 1u, tile_agg);
                     prefix = lookback(srow, j, err);
                 }
-                if (lane == 0) store_status(srow + 2 * j, 2u, combine(prefix, tile_agg));
+                if (anchor && lane == 0) store_status(srow + 2 * j, 2u, combine(prefix, tile_agg));
             }
             if (lane == 0) {
                 s_pa = prefix.a;
@@ -676,7 +694,7 @@ namespace {
 template <typename TIn, typename TOut, bool HS = false, int RUN = 2048>
 void launch_typed(const void* a, const void* b, void* h, int64_t rows, int64_t L, int segmented, int tiles_per_row,
                   int rows_per_tile, int64_t ntiles, uint32_t* claim, uint32_t* done, void* status, uint32_t* err,
-                  hipStream_t stream) {
+                  hipStream_t stream, uint32_t stress = 0) {
     using namespace cls;
     const dim3 grid{uint32_t(ntiles), 1u, 1u};
     const dim3 block{uint32_t(kLsThreads), 1u, 1u};
@@ -686,10 +704,10 @@ void launch_typed(const void* a, const void* b, void* h, int64_t rows, int64_t L
     uint64_t* st = reinterpret_cast<uint64_t*>(status);
     if (segmented) {
         hipLaunchKernelGGL((linear_scan_kernel<true, TIn, TOut, HS, RUN>), grid, block, 0, stream, ta, tb, th, rows,
-                           L, tiles_per_row, rows_per_tile, claim, done, st, err);
+                           L, tiles_per_row, rows_per_tile, claim, done, st, err, stress);
     } else {
         hipLaunchKernelGGL((linear_scan_kernel<false, TIn, TOut, HS, RUN>), grid, block, 0, stream, ta, tb, th, rows,
-                           L, tiles_per_row, rows_per_tile, claim, done, st, err);
+                           L, tiles_per_row, rows_per_tile, claim, done, st, err, stress);
     }
 }
 
@@ -717,14 +735,16 @@ void launch_in(const void* a, const void* b, void* h, int64_t rows, int64_t L, i
 
 // in_fmt / out_fmt: 0 fp32, 1 bf16, 2 fp16; hs: the Hillis-Steele in-tile
 // scan (fp32 in and out only); tile: elements per tile, 8192, or 4096 or
-// 16384 for fp32 in and out without hs (else -2).
+// 16384 for fp32 in and out without hs (else -2); stress: look-back stress
+// seed (fp32 in and out without hs only, else -2; 0: none).
 extern "C" int cls_launch_linear_scan(const void* a, const void* b, void* h, int64_t rows, int64_t L,
                                       int in_fmt, int out_fmt, int segmented, int tiles_per_row, int rows_per_tile,
                                       int64_t ntiles, uint32_t* claim, uint32_t* done, void* status,
-                                      uint32_t* err, hipStream_t stream, int hs, int tile) {
+                                      uint32_t* err, hipStream_t stream, int hs, int tile, uint32_t stress) {
     using namespace cls;
     const bool f32 = in_fmt == 0 && out_fmt == 0;
     if (tile != 8192 && (!f32 || hs || (tile != 4096 && tile != 16384))) return -2;
+    if (stress != 0 && (!f32 || hs)) return -2;
     if (hs) {
         launch_typed<float, float, true>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles, claim,
                                          done, status, err, stream);
@@ -732,12 +752,17 @@ extern "C" int cls_launch_linear_scan(const void* a, const void* b, void* h, int
     }
     if (tile == 4096) {
         launch_typed<float, float, false, 1024>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles,
-                                                claim, done, status, err, stream);
+                                                claim, done, status, err, stream, stress);
         return hipGetLastError() == hipSuccess ? 0 : -7;
     }
     if (tile == 16384) {
         launch_typed<float, float, false, 4096>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles,
-                                                claim, done, status, err, stream);
+                                                claim, done, status, err, stream, stress);
+        return hipGetLastError() == hipSuccess ? 0 : -7;
+    }
+    if (f32) {
+        launch_typed<float, float>(a, b, h, rows, L, segmented, tiles_per_row, rows_per_tile, ntiles, claim, done,
+                                   status, err, stream, stress);
         return hipGetLastError() == hipSuccess ? 0 : -7;
     }
     switch (in_fmt) {

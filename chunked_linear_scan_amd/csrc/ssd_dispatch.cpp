@@ -364,6 +364,7 @@ static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const SsdLaunchO
         f.agg_d = pl.agg_d;
         f.agg_chunks = pl.agg_chunks;
         f.nxcd = o.xcds > 0 ? o.xcds : cls::kXcds;
+        f.stress = o.stress;
         f.lookback = pl.lookback ? 1 : 0;
         f.nranges = pl.nranges > 0 ? pl.nranges : 1;
         f.seg_ctl = reinterpret_cast<uint32_t*>(ws + cls::kSsdCtlOff);

@@ -250,34 +250,48 @@ __device__ __forceinline__ uint64_t fu_seg_tag(uint32_t epoch, int item, uint32_
 }
 
 // Look-back over the earlier segments of a chain, on one 64-lane wave: lane l
-// inspects segment seg - 1 - l (item - 1 - l); the nearest inclusive prefix
-// is found with a ballot, and every segment between it and this one must
-// have published its aggregate.  A chain has at most 64 segments, so one
-// window always reaches its first segment, which publishes an inclusive
-// prefix.  Returns the segment index of that nearest prefix.  The wait is
-// bounded; giving up raises the error word and returns 0.
-__device__ __forceinline__ int fu_segment_lookback(const SsdFusedParams& p, int item, int seg, uint32_t epoch,
-                                                   int lane) {
+// inspects segment seg - 1 - l (item - 1 - l).  It is anchored at the chain's
+// first segment: it waits until segment 0 holds its inclusive prefix (which
+// that segment publishes directly, from h0) and every segment in between holds
+// its aggregate.  The fold over them then has one order whatever the timing
+// (the page's tiles fold up to the nearest inclusive prefix they find, and the
+// fp32 grouping follows the timing).  A chain has at most 64 segments, so one
+// window reaches segment 0.  The wait is bounded; giving up raises the error
+// word.
+__device__ __forceinline__ void fu_segment_lookback(const SsdFusedParams& p, int item, int seg, uint32_t epoch,
+                                                    int lane) {
     const int pred = seg - 1 - lane;
     const int it = item - 1 - lane;
     uint32_t spins = 0;
     while (true) {
-        uint32_t kind = 0;
+        bool ready = true;
         if (pred >= 0) {
             const uint64_t w = __hip_atomic_load(p.seg_status + it, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if ((w & ~uint64_t(3)) == fu_seg_tag(epoch, it, 0)) kind = uint32_t(w & 3u);
+            const uint32_t kind = (w & ~uint64_t(3)) == fu_seg_tag(epoch, it, 0) ? uint32_t(w & 3u) : 0u;
+            ready = kind == (pred == 0 ? 2u : 1u);
         }
-        const uint64_t incm = __ballot(kind == 2u);
-        const uint64_t waiting = __ballot(pred >= 0 && kind == 0u);
-        const int kp = incm ? int(__builtin_ctzll(incm)) : 64;
-        const uint64_t nearer = kp >= 64 ? ~0ull : ((1ull << kp) - 1ull);
-        if (incm && !(waiting & nearer)) return seg - 1 - kp;
+        if (__ballot(!ready) == 0) return;
         if (++spins > kFuSpinLimit) {
             if (lane == 0) atomic_add_u32(p.err, 1u);
-            return 0;
+            return;
         }
         __builtin_amdgcn_s_sleep(1);
     }
+}
+
+// Look-back stress (tests only): with a nonzero seed, about one segment in
+// four sleeps a pseudo-random 0 .. 31 x 8K clocks before it publishes, so
+// segments publish out of order.  Seed 0: no delay.
+__device__ __forceinline__ void fu_stress_delay(uint32_t seed, int item) {
+    if (seed == 0) return;
+    uint32_t x = seed ^ (uint32_t(item) * 0x9E3779B1u);
+    x ^= x >> 15;
+    x *= 0x2C1B3C6Du;
+    x ^= x >> 12;
+    x *= 0x297A2D39u;
+    x ^= x >> 15;
+    if ((x & 3u) != 0u) return;
+    for (uint32_t k = (x >> 2) & 31u; k > 0; --k) __builtin_amdgcn_s_sleep(127);
 }
 
 // The inter-chunk state pass of a split chain's segment as a single-pass
@@ -289,16 +303,17 @@ __device__ __forceinline__ int fu_segment_lookback(const SsdFusedParams& p, int 
 //     (the aggregate phase) and publishes its aggregate (alpha_k, S_k); the
 //     first segment starts that phase from h0, so it publishes its inclusive
 //     prefix P_0 directly;
-//   * wave 0 looks back for the nearest inclusive prefix P_j; all compute
-//     waves fold h <- alpha_i h + S_i over the aggregates after it, which
-//     gives the state at the segment's start;
-//   * a segment that has successors publishes P_k = alpha_k h + S_k.
+//   * wave 0 looks back, anchored at the first segment (fu_segment_lookback);
+//     all compute waves fold h <- alpha_i h + S_i over the aggregates after
+//     P_0, which gives the state at the segment's start, in the same order on
+//     every run.
 // Payloads are written with agent-scope 64-bit stores, completed (vmcnt
 // wait) and joined at a workgroup barrier before one thread writes the
 // status word; readers take payloads only after they have seen the word.
-// Aggregates and prefixes have separate payload slots, so a reader folding an
-// aggregate never races its replacement.  On return the compute waves hold
-// the state at the segment's start in hacc.
+// Each payload is written once per call (the first segment's inclusive prefix
+// and the other segments' aggregates have separate slots), so a reader never
+// races a rewrite.  On return the compute waves hold the state at the
+// segment's start in hacc.
 template <int TT, int S, typename HArr, typename LoadH0, typename RunPhase>
 __device__ __forceinline__ void ssd_lookback_segment(const SsdFusedParams& p, int item, int seg, int nst, int wave,
                                                      int lane, int tid, bool loader, HArr& hacc, float& sumG,
@@ -329,6 +344,7 @@ __device__ __forceinline__ void ssd_lookback_segment(const SsdFusedParams& p, in
             if (tid == 0 && seg > 0) store_coherent_u32(alpha + item, as_uint(fexp2(sumG)));
             wait_vmem();
         }
+        fu_stress_delay(p.stress, item);
         __syncthreads();
         if (tid == 0)
             __hip_atomic_store(p.seg_status + item, fu_seg_tag(epoch, item, seg == 0 ? 2u : 1u), __ATOMIC_RELAXED,
@@ -338,39 +354,19 @@ __device__ __forceinline__ void ssd_lookback_segment(const SsdFusedParams& p, in
         if (!loader) load_h0(hacc);  // the output pass starts from h0
         return;
     }
-    if (wave == 0) {
-        const int kp = fu_segment_lookback(p, item, seg, epoch, lane);
-        if (lane == 0) lb_int[6] = kp;
-    }
+    if (wave == 0) fu_segment_lookback(p, item, seg, epoch, lane);
     __syncthreads();
-    const int kp = __builtin_amdgcn_readfirstlane(lb_int[6]);
     if (!loader) {
         const int base = item - seg;  // this chain's first segment
-        const float* src = payP + int64_t(base + kp) * slot + tid * NACC;
+        const float* src = payP + int64_t(base) * slot + tid * NACC;
 #pragma unroll
         for (int j = 0; j < NPW; ++j) hacc[j] = load_payload(src + 4 * j);
-        for (int k = kp + 1; k < seg; ++k) {
+        for (int k = 1; k < seg; ++k) {
             const float al = as_float(load_coherent_u32(alpha + base + k));
             const float* a = payA + int64_t(base + k) * slot + tid * NACC;
 #pragma unroll
             for (int j = 0; j < NPW; ++j) hacc[j] = hacc[j] * al + load_payload(a + 4 * j);
         }
-        if (!last) {
-            // this segment's inclusive prefix, from its own aggregate as published
-            // (this thread's own stores, read back)
-            const float ak = fexp2(sumG);
-            const float* own = payA + int64_t(item) * slot + tid * NACC;
-            float* dst = payP + int64_t(item) * slot + tid * NACC;
-#pragma unroll
-            for (int j = 0; j < NPW; ++j) store_payload(dst + 4 * j, hacc[j] * ak + load_payload(own + 4 * j));
-            wait_vmem();
-        }
-    }
-    if (!last) {
-        __syncthreads();
-        if (tid == 0)
-            __hip_atomic_store(p.seg_status + item, fu_seg_tag(epoch, item, 2u), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 

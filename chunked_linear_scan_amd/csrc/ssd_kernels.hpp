@@ -80,6 +80,7 @@ struct SsdFusedParams {
     uint64_t* seg_status;  // [segments] tagged status words
     float* seg_pay;      // [2][segments][compute threads][state floats per lane]: aggregates, prefixes
     float* seg_alpha;    // [segments] decays of the aggregates
+    uint32_t stress;     // look-back stress seed (tests only; 0: none)
 };
 
 // Plan of the fused head-dim-64 path for one shape (also sizes its workspace).

@@ -170,9 +170,12 @@ void ssd_fwd_autotune_reset(void);
  *
  * Layout: a, b, h are [rows, length] fp32, row-major, contiguous, 16-byte
  * aligned at the base (rows need not be aligned).  One single-pass kernel:
- * each row is split into tiles that publish their aggregate and look back
- * over up to 64 predecessors at a time (decoupled look-back).  The result is
- * bit-identical from run to run.  h must not alias a or b.
+ * each row is split into tiles that look back over their predecessors in
+ * one 64-wide window (decoupled look-back).  The look-back is anchored: every
+ * 64th tile of a row publishes its inclusive prefix, the others only their
+ * aggregate, and each tile folds from its anchor.  The combine order depends
+ * on the tile index alone, so the result is bit-identical from run to run
+ * whatever order tiles finish in.  h must not alias a or b.
  *
  * A tile is 8192 elements unless linear_scan_autotune has chosen another
  * size (4096 or 16384) for this shape on this device; the tile changes only

@@ -45,6 +45,12 @@ typedef struct {
                             only); 0: the device's 8; 1: plain index order          */
     int32_t sub_chunk;   /* with nsegs: the sub-chunk the kernels run (32 or 64, a
                             divisor of the chunk capped at 128); 0: that cap      */
+    uint32_t stress_seed; /* look-back stress (SSD_S3_LOOKBACK plans): 0, or a seed
+                            by which about one segment in four waits a pseudo-
+                            random 0 to 31 sleeps of ~8K clocks before it
+                            publishes, so segments publish out of order; the
+                            results must not change ("Selective-scan CUDA
+                            kernels", section "Correctness")                      */
 } ssd_plan_request;
 
 /*
@@ -82,9 +88,18 @@ size_t ssd_fwd_planned_workspace_size(int64_t batch, int64_t seqlen, int64_t nhe
  * sets outlives the call.  All of linear_scan's arguments, checks, workspace
  * rule (linear_scan_workspace_size covers every tile) and status codes
  * apply.
+ *
+ * stress_seed: 0, or a look-back stress run ("Selective-scan CUDA kernels",
+ * section "Correctness": look-back races show up only under other
+ * schedules).  About one tile in four, chosen by a hash of the seed, the row
+ * and the tile, then waits a pseudo-random 0 to 31 sleeps of about 8K clocks
+ * each before it publishes and looks back, so tiles publish out of order.
+ * The results must equal those of the unperturbed call bit for bit (the
+ * look-back's combine order does not depend on timing).
  */
 int linear_scan_planned(const float* a, const float* b, float* h, int64_t rows, int64_t length,
-                        int64_t tile, void* workspace, size_t workspace_bytes, void* stream);
+                        int64_t tile, uint32_t stress_seed, void* workspace, size_t workspace_bytes,
+                        void* stream);
 
 /*
  * A plain streaming kernel with linear_scan's HBM traffic: h[i] = a[i] * b[i]

@@ -122,7 +122,7 @@ def lookback_scan(elements, combine, identity, tile, window=64, seed=0,
 
 
 def lookback_scan_halves(pairs, combine, tile, window=64, seed=0, resident=8, check_tags=True,
-                         max_steps=10_000_000):
+                         max_steps=10_000_000, anchor=None):
     """The look-back protocol of ``lookback_scan`` with each status word
     written and read as two halves, (tag, a) and (tag, b), where a and b are
     the two parts of the scalar recurrence's affine pair and the tag is the
@@ -136,7 +136,19 @@ def lookback_scan_halves(pairs, combine, tile, window=64, seed=0, resident=8, ch
     halves carry the same nonzero tag (otherwise it is read as not yet
     published and polled again); ``check_tags=False`` is the broken variant
     that trusts the first half's tag, which a torn read corrupts.
+
+    ``anchor``: the anchored form of the protocol.  Tiles whose index is a
+    multiple of ``anchor`` (anchors) publish only their inclusive prefix; the
+    others publish only their aggregate.  Tile t looks back exactly to the
+    anchor a = anchor * ((t - 1) // anchor), takes its inclusive prefix and
+    folds the aggregates of tiles a + 1 .. t - 1, nearest first.  Which
+    predecessors had published when a tile looked back then changes nothing in
+    the combine order, so every interleaving gives the same values to the
+    last bit (with the nearest-prefix form, the grouping follows the timing).
+    ``anchor`` must not exceed ``window``, so one window reaches the anchor.
     """
+    if anchor is not None and not 1 <= anchor <= window:
+        raise ValueError("anchor must be in [1, window]")
     rng = random.Random(seed)
     n = len(pairs)
     ntiles = -(-n // tile)
@@ -167,8 +179,14 @@ def lookback_scan_halves(pairs, combine, tile, window=64, seed=0, resident=8, ch
         ph = st["phase"]
         if ph == "scan":
             st["local"] = local_scan(t)
-            st["pub"] = (INC if t == 0 else AGG, st["local"][-1], "half0")
             st["prefix"] = None
+            if anchor is not None and t > 0 and t % anchor == 0:
+                # an anchor publishes nothing before its look-back
+                st["phase"] = "read0"
+                st["look"] = t - 1
+                st["acc"] = None
+                continue
+            st["pub"] = (INC if t == 0 else AGG, st["local"][-1], "half0")
             st["phase"] = "publish"
         elif ph == "publish":  # one half per step
             kind, val, which = st["pub"]
@@ -177,7 +195,7 @@ def lookback_scan_halves(pairs, combine, tile, window=64, seed=0, resident=8, ch
                 st["pub"] = (kind, val, "half1")
             else:
                 halves[t][1] = (kind, val[1])
-                if kind == INC:
+                if kind == INC or (anchor is not None and st["prefix"] is not None):
                     st["phase"] = "apply"
                 else:
                     st["phase"] = "read0"
@@ -185,6 +203,8 @@ def lookback_scan_halves(pairs, combine, tile, window=64, seed=0, resident=8, ch
                     st["acc"] = None
         elif ph == "read0":  # first halves of the window, nearest first
             lo = max(st["look"] - window + 1, 0)
+            if anchor is not None:
+                lo = anchor * (st["look"] // anchor)  # exactly back to the anchor
             st["view"] = list(range(st["look"], lo - 1, -1))
             st["w0"] = [halves[p][0] for p in st["view"]]
             st["phase"] = "read1"
@@ -195,6 +215,8 @@ def lookback_scan_halves(pairs, combine, tile, window=64, seed=0, resident=8, ch
             retry = False
             for p, (t0, a), (t1, b) in zip(st["view"], st["w0"], w1):
                 kind = (t0 if t0 == t1 else EMPTY) if check_tags else t0
+                if anchor is not None and p % anchor == 0 and kind != INC:
+                    kind = EMPTY  # an anchor counts only once it holds its inclusive prefix
                 if kind == EMPTY:
                     retry = True
                     break
@@ -206,8 +228,11 @@ def lookback_scan_halves(pairs, combine, tile, window=64, seed=0, resident=8, ch
                 acc = val if acc is None else combine(val, acc)
             if resolved:
                 st["prefix"] = prefix
-                st["pub"] = (INC, combine(prefix, st["local"][-1]), "half0")
-                st["phase"] = "publish"
+                if anchor is not None and t % anchor != 0:
+                    st["phase"] = "apply"  # only anchors publish an inclusive prefix
+                else:
+                    st["pub"] = (INC, combine(prefix, st["local"][-1]), "half0")
+                    st["phase"] = "publish"
             elif retry:
                 st["phase"] = "read0"  # poll again from the same place
             else:

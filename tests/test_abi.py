@@ -90,8 +90,8 @@ def test_scan_plan_and_tuner_validate_on_host():
     assert lib.linear_scan_plan(4, 100, None) == -1
     ws = lib.linear_scan_workspace_size(4, 100)
     for bad in (1000, 8193, -1, 32768):
-        assert lib.linear_scan_planned(FAKE, FAKE, FAKE, 4, 100, bad, FAKE, ws, None) == -2, bad
-    assert lib.linear_scan_planned(None, FAKE, FAKE, 4, 100, 4096, FAKE, ws, None) == -1
+        assert lib.linear_scan_planned(FAKE, FAKE, FAKE, 4, 100, bad, 0, FAKE, ws, None) == -2, bad
+    assert lib.linear_scan_planned(None, FAKE, FAKE, 4, 100, 4096, 0, FAKE, ws, None) == -1
     ms = ctypes.c_float()
     assert lib.linear_scan_autotune(FAKE, FAKE, FAKE, 4, 100, FAKE, ws, None, 5, None, ctypes.byref(ms)) == -1
     assert lib.linear_scan_autotune(FAKE, FAKE, FAKE, 4, 100, FAKE, ws, None, 0, ctypes.byref(tile),

@@ -79,3 +79,24 @@ def test_autotune_result_plan_and_later_calls(rows, L):
     finally:
         cls.linear_scan_autotune_reset()
     assert cls.linear_scan_plan(rows, L)["source"] == "built-in"
+
+
+@pytest.mark.parametrize("seed", [1, 77, 4099])
+@pytest.mark.parametrize("tile,rows,L", [(8192, 384, 65536), (8192, 7, 100003), (4096, 3, 300000),
+                                         (16384, 2, 200000), (8192, 1, 8192 * 200), (8192, 1000, 7)])
+def test_lookback_stress_gives_the_same_bits(seed, tile, rows, L):
+    """Look-back stress ("Selective-scan CUDA kernels", section "Correctness"):
+    a quarter of the tiles, picked by a hash of the seed, wait up to ~100 us
+    before they publish, so tiles publish and look back out of order.  The
+    anchored look-back folds in an order fixed by the tile index, so the
+    output equals the unperturbed call bit for bit, and the oracle within the
+    scan's bounds.  1 x 8192·200 runs three anchors deep."""
+    print(f"[scan stress] seed={seed} tile={tile} rows={rows} L={L}", flush=True)
+    w = workloads.make_scan_inputs(rows, L, seed=seed + rows + L)
+    a, b = w["a"].cuda(), w["b"].cuda()
+    ref = cls.linear_scan_planned(a, b, tile=tile)
+    got = cls.linear_scan_planned(a, b, tile=tile, stress_seed=seed)
+    torch.cuda.synchronize()
+    assert torch.equal(got.view(torch.int32), ref.view(torch.int32))
+    if rows * L <= 4_000_000:
+        parity.check_scan(w["a"], w["b"], got.cpu().numpy(), label=f"stress {seed}", elementwise=rows * L < 1_000_000)

@@ -287,6 +287,26 @@ def test_full_workloads_lookback(name):
     parity.check_ssd_workload(name, y, hf, label=f"{name} look-back")
 
 
+@pytest.mark.parametrize("seed", [3, 1001])
+@pytest.mark.parametrize("nsegs,nsplit,L", [(4, 0, 4096), (16, 0, 4096), (64, 3, 8192)])
+def test_segment_lookback_stress_gives_the_same_bits(seed, nsegs, nsplit, L):
+    """Look-back stress on the SSD segments ("Selective-scan CUDA kernels",
+    section "Correctness"): a quarter of the segments, picked by a hash of the
+    seed, wait up to ~100 us before they publish their aggregate.  The look-back
+    folds from the chain's first segment in segment order whatever the timing,
+    so y and h_final equal the unperturbed look-back call bit for bit, and the
+    oracle within the bf16 bounds."""
+    print(f"[ssd stress] seed={seed} nsegs={nsegs} nsplit={nsplit} L={L}", flush=True)
+    inp = small_case(seed, 2, L, 4, 64, 128, 1, torch.bfloat16)
+    base = cls.plan_request(nsegs=nsegs, nsplit=nsplit, s3="lookback")
+    stress = cls.plan_request(nsegs=nsegs, nsplit=nsplit, s3="lookback", stress_seed=seed)
+    y0, h0 = gpu_run(inp, chunk=128, plan=base)
+    y1, h1 = gpu_run(inp, chunk=128, plan=stress)
+    assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
+    assert np.array_equal(h0.view(np.uint32), h1.view(np.uint32))
+    parity.check_ssd(inp, y1, h1, 128, f"stress {seed}")
+
+
 def test_explicit_workspace_error_word_stays_zero():
     """A caller-owned workspace, reused over shapes and plans (reduce-then-fold
     and look-back, whose claim counters, finish count and epoch must be left

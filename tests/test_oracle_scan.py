@@ -164,3 +164,48 @@ def test_lookback_trusting_one_half_is_caught():
         except TypeError:  # an unpublished half (None) reached the combine
             caught += 1
     assert caught >= 8
+
+
+@pytest.mark.parametrize("tile,anchor,resident", [(4, 4, 6), (3, 8, 16), (2, 64, 64), (5, 1, 3)])
+@pytest.mark.parametrize("seed", range(5))
+def test_anchored_lookback_matches_loop(tile, anchor, resident, seed):
+    """The anchored form (inclusive prefixes only at every anchor-th tile,
+    aggregates elsewhere) is the scan under any interleaving, torn reads
+    included."""
+    rng = np.random.default_rng(100 + seed)
+    n = 257
+    a = rng.uniform(0.5, 1.0, n)
+    b = rng.standard_normal(n)
+    ref = scan.scan_loop(a[None], b[None])[0]
+    out = lookback.lookback_scan_halves(_pairs(a, b), scan.combine, tile=tile, window=64, seed=seed,
+                                        resident=resident, anchor=anchor)
+    assert np.abs(np.array([v[1] for v in out]) - ref).max() < 1e-12
+
+
+def _f32_combine(first, second):
+    a1, b1 = first
+    a2, b2 = second
+    return (np.float32(a1 * a2), np.float32(np.float32(a2 * b1) + b2))
+
+
+def test_anchored_lookback_is_bit_identical_across_interleavings():
+    """fp32 arithmetic: with the nearest-prefix protocol the combine grouping
+    follows which predecessors had published, so seeded interleavings give
+    different last bits; the anchored form gives one answer for every
+    interleaving."""
+    rng = np.random.default_rng(9)
+    n = 600
+    pairs = [(np.float32(x), np.float32(y)) for x, y in zip(rng.uniform(0.9, 1.0, n), rng.standard_normal(n))]
+    nearest = {tuple(float(v[1]) for v in lookback.lookback_scan_halves(pairs, _f32_combine, tile=5, window=64,
+                                                                         seed=s, resident=16))
+               for s in range(20)}
+    anchored = {tuple(float(v[1]) for v in lookback.lookback_scan_halves(pairs, _f32_combine, tile=5, window=64,
+                                                                          seed=s, resident=16, anchor=8))
+                for s in range(20)}
+    assert len(nearest) > 1
+    assert len(anchored) == 1
+
+
+def test_anchor_wider_than_window_is_rejected():
+    with pytest.raises(ValueError):
+        lookback.lookback_scan_halves([(1.0, 0.0)] * 8, scan.combine, tile=1, window=4, anchor=8)
