@@ -45,7 +45,7 @@ def test_full_workload(name):
     (2, 4091), (2, 4093), (2, 4096), (2, 4097), (3, 8185), (2, 8186), (2, 8187), (3, 8191), (3, 8192),
     (3, 8193), (2, 16383), (2, 16384), (2, 16385), (3, 24576), (3, 24580), (1, 65533),
     (5, 12345), (1000, 7), (257, 129), (5, 4096), (9, 2048), (3, 8184), (7, 1024), (33, 256), (5, 4), (17, 8),
-    (4097, 4), (5, 4094), (7, 2730), (4, 4093), (3, 8186), (11, 2047)])
+    (4097, 4), (5, 4094), (7, 2730), (4, 4093), (3, 8186), (11, 2047), (50, 431), (39, 431)])
 def test_edge_sizes(rows, L):
     w = workloads.make_scan_inputs(rows, L, seed=rows * 7919 + L)
     check(w["a"], w["b"], label="edge")
@@ -138,7 +138,7 @@ TYPED = [(torch.bfloat16, torch.float32), (torch.bfloat16, torch.bfloat16), (tor
 @pytest.mark.parametrize("rows,L", [(3, 1), (5, 7), (3, 33), (2, 4097), (3, 8186), (2, 8187), (3, 8193),
                                     (2, 16378), (2, 16379), (2, 16384), (2, 16385), (3, 32771), (1000, 7),
                                     (257, 129), (3, 5461), (5, 4096), (9, 2048), (33, 256), (4097, 4),
-                                    (4, 65536), (1, 65533)])
+                                    (4, 65536), (1, 65533), (50, 431), (9, 2047), (5, 4094)])
 def test_typed_scan_matches_oracle(din, dout, rows, L):
     """bf16 / fp16 / fp32 elements through linear_scan_typed.  The oracle runs
     on the exact float64 values of the (possibly 16-bit) inputs.  With an fp32
