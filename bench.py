@@ -612,7 +612,8 @@ def autotune_compare(r, steps, warmup):
                                       chunk=s.chunk, reps=10, out=d0["y"])
     base = min(s.chunk, 128)
     tuned = cls.plan_request(nsegs=info["nsegs"], nsplit=info["nsplit"], agg_pieces=info["agg_pieces"],
-                             s3=info["s3"], sub_chunk=0 if info["sub_chunk"] == base else info["sub_chunk"]) \
+                             s3=info["s3"], sub_chunk=0 if info["sub_chunk"] == base else info["sub_chunk"],
+                             cache_policy=info["cache_policy"]) \
         if info["nsegs"] > 0 else None
     cls.ssd_fwd_autotune_reset()
 
@@ -634,7 +635,7 @@ def autotune_compare(r, steps, warmup):
     n = split_steps(steps, NWIN)
     ws = timed_windows([a, b], {"tuned": n, "heuristic": n})
     ta, tb = summarize(ws["tuned"], n), summarize(ws["heuristic"], n)
-    keys = ("nsegs", "nsplit", "agg_pieces", "sub_chunk", "s3")
+    keys = ("nsegs", "nsplit", "agg_pieces", "sub_chunk", "s3", "cache_policy")
     return {"plan": {k: info[k] for k in keys}, "heuristic_plan": {k: heur[k] for k in keys},
             "tuner_ms_per_call": round(info["ms_per_call"], 4),
             "us_per_call_tuned": _us(ta["median"]), "us_per_call_heuristic": _us(tb["median"]),

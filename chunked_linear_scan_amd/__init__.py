@@ -33,12 +33,14 @@ class PlanRequest(ctypes.Structure):
     """``ssd_plan_request`` of include/chunked_linear_scan_testing.h."""
     _fields_ = [("path", ctypes.c_int32), ("s3", ctypes.c_int32), ("nsegs", ctypes.c_int64),
                 ("nsplit", ctypes.c_int64), ("agg_pieces", ctypes.c_int64), ("xcds", ctypes.c_int32),
-                ("sub_chunk", ctypes.c_int32), ("stress_seed", ctypes.c_uint32)]
+                ("sub_chunk", ctypes.c_int32), ("stress_seed", ctypes.c_uint32), ("cache_policy", ctypes.c_int32)]
 
 
 PATH = {"auto": 0, "chunk": 1, "fused": 2}
 S3 = {"auto": 0, "reduce": 1, "lookback": 2}
 _S3_NAME = {0: None, 1: "reduce", 2: "lookback"}
+CACHE = {"auto": 0, "default": 1, "nontemporal": 2}
+_CACHE_NAME = {0: None, 1: "default", 2: "nontemporal"}
 
 
 class SSDError(RuntimeError):
@@ -83,10 +85,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         lib.ssd_step.restype = ctypes.c_int
         pi64 = ctypes.POINTER(ctypes.c_int64)
         pint = ctypes.POINTER(ctypes.c_int)
-        lib.ssd_fwd_autotune.argtypes = lib.ssd_fwd.argtypes + [ctypes.c_int, pi64, pi64, pi64, pi64, pint,
+        lib.ssd_fwd_autotune.argtypes = lib.ssd_fwd.argtypes + [ctypes.c_int, pi64, pi64, pi64, pi64, pint, pint,
                                                                 ctypes.POINTER(ctypes.c_float)]
         lib.ssd_fwd_autotune.restype = ctypes.c_int
-        lib.ssd_fwd_plan.argtypes = [i64] * 7 + [ctypes.c_int, pi64, pi64, pi64, pi64, pint]
+        lib.ssd_fwd_plan.argtypes = [i64] * 7 + [ctypes.c_int, pi64, pi64, pi64, pi64, pint, pint]
         lib.ssd_fwd_plan.restype = ctypes.c_int
         lib.ssd_fwd_autotune_reset.argtypes = []
         lib.ssd_fwd_autotune_reset.restype = None
@@ -343,10 +345,10 @@ def ssd_fwd(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, want_final_state:
 
 
 def plan_request(path="auto", s3="auto", nsegs=0, nsplit=0, agg_pieces=0, xcds=0, sub_chunk=0,
-                 stress_seed=0) -> PlanRequest:
+                 stress_seed=0, cache_policy="auto") -> PlanRequest:
     """An explicit plan for ``ssd_fwd_planned`` (see the testing header)."""
     return PlanRequest(PATH[path], S3[s3 or "auto"], int(nsegs), int(nsplit), int(agg_pieces), int(xcds),
-                       int(sub_chunk), int(stress_seed))
+                       int(sub_chunk), int(stress_seed), CACHE[cache_policy or "auto"])
 
 
 def ssd_fwd_planned(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, plan: PlanRequest | None = None,
@@ -380,35 +382,37 @@ def ssd_fwd_autotune(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, reps: in
     """Times ssd_fwd's candidate plans on these inputs against the built-in
     heuristic's and keeps the fastest for this shape (later ssd_fwd calls use
     it).  Blocks until done.  Returns (y, h_final or None, {"nsegs", "nsplit",
-    "agg_pieces", "sub_chunk", "s3", "ms_per_call"}); y and h_final are the
-    chosen plan's result.  nsegs == 0: nothing to tune."""
+    "agg_pieces", "sub_chunk", "s3", "cache_policy", "ms_per_call"}); y and
+    h_final are the chosen plan's result.  nsegs == 0: nothing to tune."""
     lib = load_library()
     args, y, hf = _ssd_fwd_args(lib, x, dt, A, B, C, D, h0, chunk, want_final_state, out, workspace)
     nsegs, nsplit, pieces, sub, ms = (ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(),
                                       ctypes.c_float())
-    s3 = ctypes.c_int()
+    s3, pol = ctypes.c_int(), ctypes.c_int()
     st = lib.ssd_fwd_autotune(*args, int(reps), ctypes.byref(nsegs), ctypes.byref(nsplit), ctypes.byref(pieces),
-                              ctypes.byref(sub), ctypes.byref(s3), ctypes.byref(ms))
+                              ctypes.byref(sub), ctypes.byref(s3), ctypes.byref(pol), ctypes.byref(ms))
     if st != SSD_OK:
         raise SSDError(st, "ssd_fwd_autotune")
     return y, hf, {"nsegs": nsegs.value, "nsplit": nsplit.value, "agg_pieces": pieces.value,
-                   "sub_chunk": sub.value, "s3": _S3_NAME[s3.value], "ms_per_call": ms.value}
+                   "sub_chunk": sub.value, "s3": _S3_NAME[s3.value], "cache_policy": _CACHE_NAME[pol.value],
+                   "ms_per_call": ms.value}
 
 
 def ssd_fwd_plan(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype=torch.bfloat16):
     """The plan ssd_fwd uses for a shape: {"nsegs", "nsplit", "agg_pieces",
-    "sub_chunk", "s3", "source": "tuned" | "heuristic" | "none"}.  Launches
-    nothing."""
+    "sub_chunk", "s3", "cache_policy", "source": "tuned" | "heuristic" |
+    "none"}.  Launches nothing."""
     lib = load_library()
     nsegs, nsplit, pieces, sub = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
-    s3 = ctypes.c_int()
+    s3, pol = ctypes.c_int(), ctypes.c_int()
     st = lib.ssd_fwd_plan(batch, seqlen, nheads, headdim, dstate, ngroups, int(chunk), _DTYPE_CODE[dtype],
                           ctypes.byref(nsegs), ctypes.byref(nsplit), ctypes.byref(pieces), ctypes.byref(sub),
-                          ctypes.byref(s3))
+                          ctypes.byref(s3), ctypes.byref(pol))
     if st < 0:
         raise SSDError(st, "ssd_fwd_plan")
     return {"nsegs": nsegs.value, "nsplit": nsplit.value, "agg_pieces": pieces.value, "sub_chunk": sub.value,
-            "s3": _S3_NAME[s3.value], "source": {0: "heuristic", 1: "tuned", 2: "none"}[st]}
+            "s3": _S3_NAME[s3.value], "cache_policy": _CACHE_NAME[pol.value],
+            "source": {0: "heuristic", 1: "tuned", 2: "none"}[st]}
 
 
 def ssd_fwd_autotune_reset():

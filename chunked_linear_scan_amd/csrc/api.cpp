@@ -293,14 +293,17 @@ static bool plan_options(const ssd_plan_request* plan, cls::SegChoice* seg, SsdL
     if (plan->agg_pieces > (int64_t(1) << 20) || plan->nsplit > (int64_t(1) << 31)) return false;
     if (plan->xcds < 0 || plan->xcds > 64) return false;
     if (plan->sub_chunk != 0 && plan->sub_chunk != 32 && plan->sub_chunk != 64) return false;
+    if (plan->cache_policy < 0 || plan->cache_policy > 2) return false;
     o->path = plan->path;
     o->s3 = plan->s3;
     o->xcds = plan->xcds;
     o->stress = plan->stress_seed;
+    o->policy = plan->cache_policy;
     if (plan->nsegs > 0) {
         *seg = cls::SegChoice{plan->nsegs, plan->nsplit, plan->agg_pieces};
         seg->s3 = plan->s3;
         seg->sub = plan->sub_chunk;
+        seg->nt = plan->cache_policy;
         o->force = seg;
     }
     return true;
@@ -347,25 +350,25 @@ int ssd_fwd_autotune(const void* x, const float* dt, const float* A, const void*
                      int64_t headdim, int64_t dstate, int64_t ngroups, int64_t chunk, int dtype, void* y,
                      float* h_final, void* workspace, size_t workspace_bytes, void* stream, int reps,
                      int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces, int64_t* sub_chunk, int* s3,
-                     float* ms_per_call) {
-    if (!nsegs || !nsplit || !agg_pieces || !sub_chunk || !s3 || !ms_per_call) return SSD_ERR_NULL;
+                     int* cache_policy, float* ms_per_call) {
+    if (!nsegs || !nsplit || !agg_pieces || !sub_chunk || !s3 || !cache_policy || !ms_per_call) return SSD_ERR_NULL;
     if (reps < 1 || reps > 1000) return SSD_ERR_SHAPE;
     const SsdShape s{batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype};
     const SsdArgs args{x, dt, A, B, C, D, h0, y, h_final, workspace};
     const int st = ssd_fwd_validate(s, args, workspace_bytes);
     if (st != SSD_OK) return st;
     return cls_ssd_autotune(s, args, static_cast<hipStream_t>(stream), reps, nsegs, nsplit, agg_pieces, sub_chunk,
-                            s3, ms_per_call);
+                            s3, cache_policy, ms_per_call);
 }
 
 int ssd_fwd_plan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim, int64_t dstate, int64_t ngroups,
                  int64_t chunk, int dtype, int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces, int64_t* sub_chunk,
-                 int* s3) {
-    if (!nsegs || !nsplit || !agg_pieces || !sub_chunk || !s3) return SSD_ERR_NULL;
+                 int* s3, int* cache_policy) {
+    if (!nsegs || !nsplit || !agg_pieces || !sub_chunk || !s3 || !cache_policy) return SSD_ERR_NULL;
     const SsdShape s{batch, seqlen, nheads, headdim, dstate, ngroups, chunk, dtype};
     const int st = cls_ssd_check(s);
     if (st != SSD_OK) return st;
-    return cls_ssd_plan_query(s, nsegs, nsplit, agg_pieces, sub_chunk, s3);
+    return cls_ssd_plan_query(s, nsegs, nsplit, agg_pieces, sub_chunk, s3, cache_policy);
 }
 
 void ssd_fwd_autotune_reset(void) { cls_ssd_autotune_reset(); }

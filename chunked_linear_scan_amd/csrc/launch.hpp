@@ -20,6 +20,7 @@ struct SegChoice {
     int64_t agg_d = 0;  // aggregate pieces per segment (0: the heuristic's)
     int s3 = 0;         // inter-segment scheme (SSD_S3_*; 0: the built-in choice)
     int64_t sub = 0;    // sub-chunk the kernel runs (0: the chunk, at most 128)
+    int nt = 0;         // cache policy of x loads and y stores: 0 the heuristic's, 1 default, 2 non-temporal
 };
 }  // namespace cls
 
@@ -31,6 +32,7 @@ struct SsdLaunchOpts {
     int xcds = 0;                          // XCDs of the chain mapping (0: the device's)
     hipEvent_t* ev = nullptr;              // four events to record, or null
     uint32_t stress = 0;                   // look-back stress seed of the segment look-back (0: none)
+    int policy = 0;                        // x/y cache policy: 0 the plan's, 1 default, 2 non-temporal
 };
 
 struct SsdArgs {
@@ -75,11 +77,11 @@ size_t cls_ssd_plan_bytes(const SsdShape& s, const SsdLaunchOpts& o);
 // Times the fused path's candidate segment plans on these arguments, keeps the
 // fastest for the shape and leaves its result in y / h_final (blocking).
 int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t stream, int reps, int64_t* nsegs,
-                     int64_t* nsplit, int64_t* agg_pieces, int64_t* sub_chunk, int* s3, float* ms);
+                     int64_t* nsplit, int64_t* agg_pieces, int64_t* sub_chunk, int* s3, int* policy, float* ms);
 // The segment plan ssd_fwd uses for a shape: 1 tuned, 0 heuristic, 2 no plan
 // (not the fused path); negative status on error.
 int cls_ssd_plan_query(const SsdShape& s, int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces, int64_t* sub_chunk,
-                       int* s3);
+                       int* s3, int* policy);
 void cls_ssd_autotune_reset();
 // h[i] = a[i] b[i] for i < n (stream_ceiling.hip): n a multiple of 4, vec 1,
 // 2, 4 or 8 (else -2), nt 0 or 1, grid_blocks 0 (one pass) or the grid of a

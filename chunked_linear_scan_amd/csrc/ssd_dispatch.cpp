@@ -67,7 +67,8 @@ bool tuned_choice(const TuneKey& k, SegChoice* out) {
 // rounds of the CUs cut into 2..32 segments; every chain cut into 2..32
 // segments.  Plans of more than four rounds of workgroups are left out.
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
-                            int64_t chunk, int dtype, const SegChoice* force, int path, int s3, int xcds);
+                            int64_t chunk, int dtype, const SegChoice* force, int path, int s3, int xcds,
+                            int policy = 0);
 
 // Passed as `force`: the built-in heuristic, ignoring any tuned plan (the
 // autotuner's incumbent).
@@ -92,9 +93,10 @@ std::vector<SegChoice> seg_candidates(int64_t nchains, int64_t nc, int64_t slots
 
 // force: null (a tuned choice for this shape, else the heuristic), or the
 // segment plan to use.  path: SSD_PATH_* of the call (SSD_PATH_CHUNK keeps
-// the fused path out).
+// the fused path out).  policy: the call's x/y cache policy (0: the plan's).
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
-                            int64_t chunk, int dtype, const SegChoice* force, int path, int s3, int xcds) {
+                            int64_t chunk, int dtype, const SegChoice* force, int path, int s3, int xcds,
+                            int policy) {
     SsdFusedPlan pl{};
     // The kernel's quadratic block is at most 128 tokens: a longer chunk is run
     // as sub-chunks of 128 with the state passed between them, which changes the
@@ -162,6 +164,13 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     // reduce-then-fold
     const int scheme = s3 > 0 ? s3 : (want_s3 > 0 ? want_s3 : 1);
     pl.lookback = nsplit > 0 && scheme == 2;
+    // x/y cache policy: the call's request, else the plan's, else non-temporal
+    // when a workgroup walks at least 32 sub-chunks (long chains: measured
+    // 1-4 % faster; on chains of 16 sub-chunks the default policy is 4 %
+    // faster).  Non-temporal instances exist for 128-token sub-chunks only.
+    const int64_t run = (nchains - nsplit) > 0 ? nc : k;  // longest walk of a workgroup
+    const int want_nt = policy > 0 ? policy : (!heuristic && ch.nt > 0 ? ch.nt : (run >= 32 ? 2 : 1));
+    pl.nt = want_nt == 2 && TT == 128;
     const int64_t npieces = pl.lookback ? 0 : nsplit * (nsegs - 1) * agg_d;
     if (ntiles >= (int64_t(1) << 24)) {
         pl.use = false;
@@ -236,7 +245,8 @@ namespace {
 // The candidate plans of a fused-path shape (empty when the fused path is not
 // used): the segment plans of seg_candidates, each with reduce-then-fold and,
 // when it splits chains, with the look-back; for every sub-chunk the kernel
-// may run (the chunk up to 128 tokens, and 64 when the chunk is longer).
+// may run (the chunk up to 128 tokens, and 64 when the chunk is longer); each
+// with the default and the non-temporal x/y cache policy.
 std::vector<cls::SegChoice> fused_candidates(const SsdShape& s) {
     const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
                                                      s.ngroups, s.chunk, s.dtype);
@@ -248,11 +258,14 @@ std::vector<cls::SegChoice> fused_candidates(const SsdShape& s) {
         const int64_t nc = (s.seqlen + sub - 1) / sub;
         for (cls::SegChoice c : cls::seg_candidates(s.batch * s.nheads, nc, cls::fused_slots())) {
             c.sub = sub == base ? 0 : sub;
-            c.s3 = 1;
-            out.push_back(c);
-            if (c.nsegs > 1 && c.agg_d == 0) {
-                c.s3 = 2;
+            for (int nt : {1, 2}) {
+                c.nt = nt;
+                c.s3 = 1;
                 out.push_back(c);
+                if (c.nsegs > 1 && c.agg_d == 0) {
+                    c.s3 = 2;
+                    out.push_back(c);
+                }
             }
         }
     }
@@ -326,7 +339,8 @@ static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const SsdLaunchO
     p.chunk = int(s.chunk);
     p.nchunks = int(nchunks(s));
     const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
-                                                     s.ngroups, s.chunk, s.dtype, force, o.path, o.s3, o.xcds);
+                                                     s.ngroups, s.chunk, s.dtype, force, o.path, o.s3, o.xcds,
+                                                     o.policy);
     if (pl.use) {
         p.chunk = pl.chunk;
         p.nchunks = int((s.seqlen + pl.chunk - 1) / pl.chunk);
@@ -371,7 +385,7 @@ static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const SsdLaunchO
         f.seg_status = reinterpret_cast<uint64_t*>(ws + pl.status_off);
         f.seg_pay = reinterpret_cast<float*>(ws + pl.segpay_off);
         f.seg_alpha = reinterpret_cast<float*>(ws + pl.alpha_off);
-        const int st = cls::ssd_fused_launch(pl.TT, int(s.dstate), p, f, stream, ev);
+        const int st = cls::ssd_fused_launch(pl.TT, int(s.dstate), p, f, stream, ev, pl.nt);
         if (st == -8) return SSD_ERR_UNSUPPORTED;
         return st == 0 ? SSD_OK : SSD_ERR_HIP;
     }
@@ -397,9 +411,10 @@ namespace {
 
 struct PlanId {
     int64_t nsegs, nsplit, agg_d, sub;
-    int s3;
+    int s3, nt;
     bool operator==(const PlanId& o) const {
-        return nsegs == o.nsegs && nsplit == o.nsplit && agg_d == o.agg_d && sub == o.sub && s3 == o.s3;
+        return nsegs == o.nsegs && nsplit == o.nsplit && agg_d == o.agg_d && sub == o.sub && s3 == o.s3 &&
+               nt == o.nt;
     }
 };
 
@@ -411,22 +426,25 @@ cls::SegChoice realised(const SsdShape& s, const cls::SegChoice* c, PlanId* id) 
     const int64_t base = s.chunk > cls::kFusedMaxChunk ? cls::kFusedMaxChunk : s.chunk;
     const bool split = q.nsegs > 1;
     *id = PlanId{q.nsegs, split ? int64_t(q.nchains - q.nwhole) : 0, split && !q.lookback ? int64_t(q.agg_d) : 0,
-                 q.chunk == base ? 0 : int64_t(q.chunk), split ? (q.lookback ? 2 : 1) : 0};
+                 q.chunk == base ? 0 : int64_t(q.chunk), split ? (q.lookback ? 2 : 1) : 0, q.nt ? 2 : 1};
     cls::SegChoice out{id->nsegs, id->nsplit, id->agg_d};
     out.s3 = id->s3;
     out.sub = id->sub;
+    out.nt = id->nt;
     return out;
 }
 
 }  // namespace
 
 extern "C" int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t stream, int reps, int64_t* nsegs,
-                                int64_t* nsplit, int64_t* agg_pieces, int64_t* sub_chunk, int* s3, float* ms) {
+                                int64_t* nsplit, int64_t* agg_pieces, int64_t* sub_chunk, int* s3, int* policy,
+                                float* ms) {
     *nsegs = 0;
     *nsplit = 0;
     *agg_pieces = 0;
     *sub_chunk = 0;
     *s3 = 0;
+    *policy = 0;
     *ms = 0.0f;
     const std::vector<cls::SegChoice> cands = fused_candidates(s);
     if (cands.empty()) return ssd_launch_plan(s, a, SsdLaunchOpts{}, stream);
@@ -468,12 +486,13 @@ extern "C" int cls_ssd_autotune(const SsdShape& s, const SsdArgs& a, hipStream_t
     *agg_pieces = best.agg_d;
     *sub_chunk = qb.chunk;
     *s3 = best.s3;
+    *policy = qb.nt ? 2 : 1;
     *ms = chosen_ms;
     return ssd_launch_plan(s, a, with(&best), stream);
 }
 
 extern "C" int cls_ssd_plan_query(const SsdShape& s, int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces,
-                                  int64_t* sub_chunk, int* s3) {
+                                  int64_t* sub_chunk, int* s3, int* policy) {
     const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
                                                      s.ngroups, s.chunk, s.dtype);
     *nsegs = 0;
@@ -481,6 +500,7 @@ extern "C" int cls_ssd_plan_query(const SsdShape& s, int64_t* nsegs, int64_t* ns
     *agg_pieces = 0;
     *sub_chunk = 0;
     *s3 = 0;
+    *policy = 0;
     if (s.dtype == SSD_F32 || !pl.use) return 2;
     PlanId id{};
     (void)realised(s, nullptr, &id);
@@ -489,6 +509,7 @@ extern "C" int cls_ssd_plan_query(const SsdShape& s, int64_t* nsegs, int64_t* ns
     *agg_pieces = id.agg_d;
     *sub_chunk = pl.chunk;
     *s3 = id.s3;
+    *policy = id.nt;
     cls::SegChoice t{};
     const bool tuned = cls::tuned_choice(cls::tune_key(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
                                                        s.ngroups, s.chunk, s.dtype), &t);

@@ -183,7 +183,8 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cbt_kernel(SsdBf16Params p) {
     }
 }
 
-template <int TT, int S>
+// NT: the kernel instances with non-temporal x loads and y stores
+template <int TT, int S, bool NT>
 static int launch_fused_tpl(const SsdBf16Params& cbp, const SsdFusedParams& fp, hipStream_t stream,
                             hipEvent_t* ev) {
     using Lay = FuLayout<TT, S>;
@@ -192,11 +193,11 @@ static int launch_fused_tpl(const SsdBf16Params& cbp, const SsdFusedParams& fp, 
     const int ast = run_once_per_device(attrs, [] {
         return (hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_cbt_kernel<TT, S>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, CbtLayout<TT, S>::BYTES) != hipSuccess ||
-                hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_kernel<TT, S>),
+                hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_kernel<TT, S, NT>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, Lay::BYTES) != hipSuccess ||
-                hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_lb_kernel<TT, S>),
+                hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_lb_kernel<TT, S, NT>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, Lay::BYTES) != hipSuccess ||
-                hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_agg_kernel<TT, S>),
+                hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_fused_agg_kernel<TT, S, NT>),
                                     hipFuncAttributeMaxDynamicSharedMemorySize, LayA::BYTES) != hipSuccess)
                    ? -7
                    : 0;
@@ -214,15 +215,15 @@ static int launch_fused_tpl(const SsdBf16Params& cbp, const SsdFusedParams& fp, 
     if (ev) (void)hipEventRecord(ev[1], stream);
     if (npieces > 0) {
         const dim3 gagg{uint32_t(npieces), 1u, 1u};
-        hipLaunchKernelGGL((ssd_fused_agg_kernel<TT, S>), gagg, bmain, LayA::BYTES, stream, fp);
+        hipLaunchKernelGGL((ssd_fused_agg_kernel<TT, S, NT>), gagg, bmain, LayA::BYTES, stream, fp);
     }
     if (ev) (void)hipEventRecord(ev[2], stream);
     const dim3 gout{uint32_t(fp.nwhole + nst), 1u, 1u};
     const dim3 bout{uint32_t(kFuThreadsOut), 1u, 1u};
     if (fp.lookback)
-        hipLaunchKernelGGL((ssd_fused_lb_kernel<TT, S>), gout, bout, Lay::BYTES, stream, fp);
+        hipLaunchKernelGGL((ssd_fused_lb_kernel<TT, S, NT>), gout, bout, Lay::BYTES, stream, fp);
     else
-        hipLaunchKernelGGL((ssd_fused_kernel<TT, S>), gout, bout, Lay::BYTES, stream, fp);
+        hipLaunchKernelGGL((ssd_fused_kernel<TT, S, NT>), gout, bout, Lay::BYTES, stream, fp);
     if (ev) (void)hipEventRecord(ev[3], stream);
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }
@@ -242,14 +243,20 @@ size_t ssd_fused_lds_bytes(int TT, int S) {
 int ssd_fused_state_floats(int S) { return kFuP * S; }
 
 int ssd_fused_launch(int TT, int S, const SsdBf16Params& cbp, const SsdFusedParams& fp, hipStream_t stream,
-                     hipEvent_t* ev) {
+                     hipEvent_t* ev, bool nt) {
+    // non-temporal instances exist for 128-token sub-chunks only (the plan
+    // asks for them nowhere else)
     switch (TT * 1000 + S) {
-        case 32064: return launch_fused_tpl<32, 64>(cbp, fp, stream, ev);
-        case 32128: return launch_fused_tpl<32, 128>(cbp, fp, stream, ev);
-        case 64064: return launch_fused_tpl<64, 64>(cbp, fp, stream, ev);
-        case 64128: return launch_fused_tpl<64, 128>(cbp, fp, stream, ev);
-        case 128064: return launch_fused_tpl<128, 64>(cbp, fp, stream, ev);
-        case 128128: return launch_fused_tpl<128, 128>(cbp, fp, stream, ev);
+        case 32064: return launch_fused_tpl<32, 64, false>(cbp, fp, stream, ev);
+        case 32128: return launch_fused_tpl<32, 128, false>(cbp, fp, stream, ev);
+        case 64064: return launch_fused_tpl<64, 64, false>(cbp, fp, stream, ev);
+        case 64128: return launch_fused_tpl<64, 128, false>(cbp, fp, stream, ev);
+        case 128064:
+            return nt ? launch_fused_tpl<128, 64, true>(cbp, fp, stream, ev)
+                      : launch_fused_tpl<128, 64, false>(cbp, fp, stream, ev);
+        case 128128:
+            return nt ? launch_fused_tpl<128, 128, true>(cbp, fp, stream, ev)
+                      : launch_fused_tpl<128, 128, false>(cbp, fp, stream, ev);
         default: return -8;
     }
 }

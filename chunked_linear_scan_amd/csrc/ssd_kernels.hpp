@@ -98,6 +98,7 @@ struct SsdFusedPlan {
     int TT, chunk, nsegs, seg_chunks, nchains, nwhole;  // chunk: the sub-chunk the kernel runs
     int agg_d, agg_chunks, npieces;                     // aggregate pieces (see SsdFusedParams)
     bool lookback;                                      // split chains: single-pass look-back
+    bool nt;                                            // non-temporal x loads and y stores
     int nranges;                                        // look-back claim ranges
     size_t payload_off, cb_off, bt_off, cf_off, dtt_off, bytes;
     size_t status_off, segpay_off, alpha_off;           // look-back status words and payloads
@@ -126,7 +127,7 @@ int ssd_fused_state_floats(int S);  // floats of one [64, S] state
 // CB pass, then (with split chains) the aggregate launch, then the output
 // launch; ev (optional): four events, before and between the launches.
 int ssd_fused_launch(int TT, int S, const SsdBf16Params& cbp, const SsdFusedParams& fp, hipStream_t stream,
-                     hipEvent_t* ev);
+                     hipEvent_t* ev, bool nt);
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
                             int64_t chunk, int dtype);
 constexpr int kXcds = 8;  // MI355X: 8 XCDs of 32 CUs

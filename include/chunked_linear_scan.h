@@ -107,7 +107,11 @@ int ssd_fwd(const void* x, const float* dt, const float* A, const void* B,
  *     ("Selective-scan CUDA kernels", section "The five kernels");
  *   - the sub-chunk the kernels run: the chunk up to 128 tokens, or 64 (a
  *     different instantiation of the kernels: its tiles, register and LDS
- *     budget; results differ only by rounding).
+ *     budget; results differ only by rounding);
+ *   - the cache policy of the x loads and y stores (128-token sub-chunks):
+ *     default, or non-temporal (a separate instantiation; results are
+ *     identical bit for bit).  The heuristic takes non-temporal when a
+ *     workgroup walks at least 32 sub-chunks.
  * Tile shapes and occupancy within each instantiation are fixed at compile
  * time.
  *
@@ -123,7 +127,8 @@ int ssd_fwd(const void* x, const float* dt, const float* A, const void* B,
  * plan (*nsegs segments, the last *nsplit chains cut, *agg_pieces aggregate
  * pieces per segment, each 0 when nothing is cut or not applicable;
  * *sub_chunk tokens per sub-chunk; *s3 = SSD_S3_REDUCE or SSD_S3_LOOKBACK
- * when chains are cut, else 0) and its time per call in ms.  y and h_final
+ * when chains are cut, else 0; *cache_policy = SSD_CACHE_DEFAULT or
+ * SSD_CACHE_NONTEMPORAL) and its time per call in ms.  y and h_final
  * hold the result of the chosen plan, which is what ssd_fwd then returns.
  * Shapes outside the fused path have nothing to tune: one plain ssd_fwd pass,
  * all outputs 0.  The call blocks until its timed runs finish.  The table is
@@ -139,6 +144,13 @@ int ssd_fwd(const void* x, const float* dt, const float* A, const void* B,
  * (the built-in heuristic), 2 (the shape does not take the fused path) or a
  * negative status.  ssd_fwd_autotune_reset forgets every tuned plan.
  */
+/* Cache policy of the x loads and y stores of the fused path. */
+enum {
+    SSD_CACHE_AUTO = 0,        /* the plan's choice (in a plan request)                 */
+    SSD_CACHE_DEFAULT = 1,     /* the default policy                                    */
+    SSD_CACHE_NONTEMPORAL = 2  /* non-temporal: x and y are touched once per launch     */
+};
+
 /* How a cut chain's segments get their start state. */
 enum {
     SSD_S3_AUTO = 0,      /* the library's choice (in a plan request)                */
@@ -154,12 +166,13 @@ int ssd_fwd_autotune(const void* x, const float* dt, const float* A, const void*
                      int64_t dstate, int64_t ngroups, int64_t chunk, int dtype,
                      void* y, float* h_final, void* workspace, size_t workspace_bytes,
                      void* stream, int reps, int64_t* nsegs, int64_t* nsplit,
-                     int64_t* agg_pieces, int64_t* sub_chunk, int* s3, float* ms_per_call);
+                     int64_t* agg_pieces, int64_t* sub_chunk, int* s3, int* cache_policy,
+                     float* ms_per_call);
 
 int ssd_fwd_plan(int64_t batch, int64_t seqlen, int64_t nheads, int64_t headdim,
                  int64_t dstate, int64_t ngroups, int64_t chunk, int dtype,
                  int64_t* nsegs, int64_t* nsplit, int64_t* agg_pieces,
-                 int64_t* sub_chunk, int* s3);
+                 int64_t* sub_chunk, int* s3, int* cache_policy);
 
 void ssd_fwd_autotune_reset(void);
 

@@ -51,6 +51,8 @@ typedef struct {
                             publishes, so segments publish out of order; the
                             results must not change ("Selective-scan CUDA
                             kernels", section "Correctness")                      */
+    int32_t cache_policy; /* SSD_CACHE_*: the x/y cache policy (128-token sub-chunks
+                            only); 0: the plan's choice                            */
 } ssd_plan_request;
 
 /*

@@ -171,11 +171,11 @@ def test_ssd_autotune_rejects_bad_arguments():
     the tuner, a repetition count out of range, and ssd_fwd's own checks."""
     lib = cls.load_library()
     n1, n2, n3, n4, ms = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_float()
-    s3 = ctypes.c_int()
+    s3, pol = ctypes.c_int(), ctypes.c_int()
 
     def call(x=FAKE, y=FAKE, reps=3, out=True, Bt=1, T=32, ws_bytes=1 << 30):
         outs = (ctypes.byref(n1), ctypes.byref(n2), ctypes.byref(n3), ctypes.byref(n4), ctypes.byref(s3),
-                ctypes.byref(ms)) if out else (None,) * 6
+                ctypes.byref(pol), ctypes.byref(ms)) if out else (None,) * 7
         return lib.ssd_fwd_autotune(x, FAKE, FAKE, FAKE, FAKE, None, None, Bt, 64, 2, 16, 32, 1, T, cls.SSD_BF16,
                                     y, None, FAKE, ws_bytes, None, reps, *outs)
 
@@ -199,17 +199,23 @@ def test_ssd_plan_query_on_host():
     # 4 x 80 chains: 64 left over after one round, cut into 4 segments
     # (192 pieces of 3 segments fit 512 aggregate slots twice: 2 pieces per segment);
     # a 256-token chunk runs as 128-token sub-chunks
+    # (whole chains walk 64 sub-chunks: non-temporal x and y)
     assert cls.ssd_fwd_plan(4, 8192, 80, 64, 128, 1, 256) == {"nsegs": 4, "nsplit": 64, "agg_pieces": 2,
                                                               "sub_chunk": 128, "s3": "reduce",
+                                                              "cache_policy": "nontemporal",
                                                               "source": "heuristic"}
-    # 64 chains of 512 chunks: every chain cut into 4
+    # 64 chains of 512 chunks: every chain cut into 4 (segments of 128 sub-chunks)
     assert cls.ssd_fwd_plan(1, 65536, 64, 64, 128, 8, 128) == {"nsegs": 4, "nsplit": 64, "agg_pieces": 2,
                                                                "sub_chunk": 128, "s3": "reduce",
+                                                               "cache_policy": "nontemporal",
                                                                "source": "heuristic"}
-    # 192 chains of 16 chunks: a split would not pay, whole chains
+    # 192 chains of 16 chunks: a split would not pay, whole chains, default policy
     assert cls.ssd_fwd_plan(8, 2048, 24, 64, 128, 1, 256) == {"nsegs": 1, "nsplit": 0, "agg_pieces": 0,
                                                               "sub_chunk": 128, "s3": None,
+                                                              "cache_policy": "default",
                                                               "source": "heuristic"}
+    # non-temporal instances exist for 128-token sub-chunks only
+    assert cls.ssd_fwd_plan(1, 8192, 4, 64, 128, 1, 64)["cache_policy"] == "default"
     assert cls.ssd_fwd_plan(1, 1000, 4, 64, 128, 1, 32)["sub_chunk"] == 32
     assert cls.ssd_fwd_plan(1, 256, 2, 16, 16, 1, 32, torch.float32)["source"] == "none"
     assert cls.ssd_fwd_plan(1, 256, 2, 32, 32, 1, 32)["source"] == "none"  # head dim 32: per-head kernel
@@ -217,10 +223,13 @@ def test_ssd_plan_query_on_host():
         cls.ssd_fwd_plan(1, 256, 3, 64, 128, 2, 32)
     lib = cls.load_library()
     n1, n2, n3, n4, s3 = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int()
+    pol = ctypes.c_int()
     assert lib.ssd_fwd_plan(1, 256, 2, 64, 128, 1, 32, 1, None, ctypes.byref(n1), ctypes.byref(n2),
-                            ctypes.byref(n3), ctypes.byref(s3)) == -1
+                            ctypes.byref(n3), ctypes.byref(s3), ctypes.byref(pol)) == -1
     assert lib.ssd_fwd_plan(1, 256, 2, 64, 128, 1, 32, 1, ctypes.byref(n1), ctypes.byref(n2), ctypes.byref(n3),
-                            ctypes.byref(n4), None) == -1
+                            ctypes.byref(n4), None, ctypes.byref(pol)) == -1
+    assert lib.ssd_fwd_plan(1, 256, 2, 64, 128, 1, 32, 1, ctypes.byref(n1), ctypes.byref(n2), ctypes.byref(n3),
+                            ctypes.byref(n4), ctypes.byref(s3), None) == -1
 
 
 def test_linear_scan_typed_rejects_bad_arguments():
@@ -284,7 +293,8 @@ def test_planned_call_validates_the_plan_on_host():
 
     for bad in (cls.plan_request(nsegs=65), cls.PlanRequest(3, 0, 0, 0, 0, 0, 0), cls.PlanRequest(0, 3, 0, 0, 0, 0, 0),
                 cls.PlanRequest(0, 0, -1, 0, 0, 0, 0), cls.PlanRequest(0, 0, 2, -1, 0, 0, 0),
-                cls.PlanRequest(0, 0, 0, 0, 0, 65, 0), cls.PlanRequest(0, 0, 0, 0, 0, 0, 7)):
+                cls.PlanRequest(0, 0, 0, 0, 0, 65, 0), cls.PlanRequest(0, 0, 0, 0, 0, 0, 7),
+                cls.PlanRequest(0, 0, 0, 0, 0, 0, 0, 0, 3), cls.PlanRequest(0, 0, 0, 0, 0, 0, 0, 0, -1)):
         assert call(bad) == -2
         assert lib.ssd_fwd_planned_workspace_size(*shape, ctypes.byref(bad)) == 0
     # a forced plan's workspace: at least ssd_fwd's, more when it splits finer than the tuner would

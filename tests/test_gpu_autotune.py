@@ -54,10 +54,13 @@ def test_autotune_result_plan_and_later_calls(Bt, L, H, G, chunk):
     assert (info["nsegs"] > 1) == (info["s3"] is not None)
     assert (info["agg_pieces"] > 0) == (info["s3"] == "reduce") and info["agg_pieces"] >= 0
     assert info["sub_chunk"] in (min(chunk, 128), 64) and info["sub_chunk"] <= min(chunk, 128)
+    assert info["cache_policy"] in ("default", "nontemporal")
+    assert info["sub_chunk"] == 128 or info["cache_policy"] == "default"
     parity.check_ssd(c, y.float().cpu().numpy(), hf.cpu().numpy(), chunk, "tuned")
     after = cls.ssd_fwd_plan(Bt, L, H, P, S, G, chunk)
     assert after == {"nsegs": info["nsegs"], "nsplit": info["nsplit"], "agg_pieces": info["agg_pieces"],
-                     "sub_chunk": info["sub_chunk"], "s3": info["s3"], "source": "tuned"}
+                     "sub_chunk": info["sub_chunk"], "s3": info["s3"], "cache_policy": info["cache_policy"],
+                     "source": "tuned"}
     y2, hf2 = cls.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=chunk)
     torch.cuda.synchronize()
     assert torch.equal(y2.view(torch.int16), y.view(torch.int16))

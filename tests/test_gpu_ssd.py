@@ -307,6 +307,23 @@ def test_segment_lookback_stress_gives_the_same_bits(seed, nsegs, nsplit, L):
     parity.check_ssd(inp, y1, h1, 128, f"stress {seed}")
 
 
+@pytest.mark.parametrize("plan", [dict(), dict(nsegs=4), dict(nsegs=4, nsplit=3, s3="lookback"),
+                                  dict(nsegs=3, agg_pieces=2)], ids=["heuristic", "split", "lookback", "pieces"])
+def test_cache_policies_give_the_same_bits(plan):
+    """The non-temporal x/y instances differ from the default ones only in
+    the cache policy of two memory operations: y and h_final are equal bit
+    for bit, and both match the oracle."""
+    print(f"[ssd policy] {plan}", flush=True)
+    inp = small_case(11, 2, 5000, 4, 64, 128, 2, torch.bfloat16)
+    outs = {}
+    for pol in ("default", "nontemporal"):
+        outs[pol] = gpu_run(inp, chunk=128, plan=cls.plan_request(cache_policy=pol, **plan))
+    (y0, h0), (y1, h1) = outs["default"], outs["nontemporal"]
+    assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
+    assert np.array_equal(h0.view(np.uint32), h1.view(np.uint32))
+    parity.check_ssd(inp, y1, h1, 128, f"non-temporal {plan}")
+
+
 def test_explicit_workspace_error_word_stays_zero():
     """A caller-owned workspace, reused over shapes and plans (reduce-then-fold
     and look-back, whose claim counters, finish count and epoch must be left
