@@ -71,8 +71,17 @@ def test_autotune_result_plan_and_later_calls(rows, L):
                                      ctypes.c_void_p(typed.data_ptr()), rows, L, cls.SSD_F32, cls.SSD_F32,
                                      ctypes.c_void_p(ws.data_ptr()), ws.numel(),
                                      ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
+        noalloc = torch.empty_like(a)
+        lib.linear_scan_noalloc.argtypes = [ctypes.c_void_p] * 3 + [ctypes.c_int64] * 2 + [ctypes.c_void_p]
+        lib.linear_scan_noalloc.restype = ctypes.c_int
+        if lib.linear_scan_workspace_size(rows, L) <= (1 << 20):
+            assert lib.linear_scan_noalloc(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()),
+                                           ctypes.c_void_p(noalloc.data_ptr()), rows, L,
+                                           ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)) == 0
+        else:
+            noalloc = h
         torch.cuda.synchronize()
-        assert torch.equal(later, h) and torch.equal(typed, h)
+        assert torch.equal(later, h) and torch.equal(typed, h) and torch.equal(noalloc, h)
         # the tuned tile is the one the planned call runs when asked for it
         assert torch.equal(cls.linear_scan_planned(a, b, tile=info["tile"]), h)
         parity.check_scan(w["a"], w["b"], h.cpu().numpy(), label=f"tuned {rows}x{L}")
