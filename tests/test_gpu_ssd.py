@@ -324,6 +324,22 @@ def test_cache_policies_give_the_same_bits(plan):
     parity.check_ssd(inp, y1, h1, 128, f"non-temporal {plan}")
 
 
+@pytest.mark.parametrize("A_value", [0.0, -1e-3])
+@pytest.mark.parametrize("plan", [dict(nsegs=4, s3="reduce"), dict(nsegs=8, s3="lookback"),
+                                  dict(nsegs=3, agg_pieces=2, s3="reduce"), dict(nsegs=16, nsplit=2, s3="lookback")],
+                         ids=["reduce4", "lookback8", "pieces", "lookback16"])
+def test_split_plans_carry_state_without_decay(A_value, plan):
+    """Cut chains with no decay (A = 0: every segment's alpha is exactly 1, so
+    h0 and every earlier token reach the last output) or nearly none (alpha
+    about 0.7 over the sequence): the folds of reduce-then-fold and of the
+    look-back carry the whole history, where strong decay would let a wrong
+    fold hide behind an alpha that underflows to 0."""
+    print(f"[ssd fold] A={A_value} {plan}", flush=True)
+    inp = small_case(170, 2, 64 * 40 + 17, 3, 64, 128, 1, torch.bfloat16)
+    inp["A"] = torch.full_like(inp["A"], A_value)
+    run_and_check(inp, 64, f"fold A={A_value} {plan}", plan=cls.plan_request(**plan))
+
+
 def test_explicit_workspace_error_word_stays_zero():
     """A caller-owned workspace, reused over shapes and plans (reduce-then-fold
     and look-back, whose claim counters, finish count and epoch must be left
