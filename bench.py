@@ -17,7 +17,9 @@ bugs the tests caught": kernels too short for the GPU to boost):
   its own GPU time has run;
 * the K timed steps of the headline run as 15 windows, each bracketed by HIP
   events on the launch stream; the other workloads (the small- and
-  large-model layer shapes, the scans, the decode step) run their own
+  large-model layer shapes, the large layer in heads of dim 128, the large
+  layer forced onto the per-(batch, head) kernel, the scans, the decode
+  step) run their own
   windows of at least 5 ms, interleaved with the headline's: window w of
   every workload runs before window w + 1 of any;
 * inputs and outputs rotate over enough buffer copies that each workload's
@@ -40,7 +42,8 @@ Other modes: ``--scan-ceiling-sweep``, ``--copy-probe`` / ``--record-traffic``
 (HBM traffic counters), ``--no-autotune``, ``--no-cpu-baseline``,
 ``--only-headline`` (the headline workload alone, for counter runs),
 ``--no-side-ssd`` (the headline, the scans and the decode step: a counter run
-that holds one SSD shape), ``--s3-ab`` (the two inter-segment schemes).
+that holds one SSD shape), ``--path chunk`` (the headline workload on the
+per-(batch, head) kernel), ``--s3-ab`` (the two inter-segment schemes).
 
 Prints exactly one JSON line.
 """
@@ -117,6 +120,8 @@ def source_digest(names, read=None):
 
 
 SSD_SOURCES = ["ssd_fused.hpp", "ssd_fused.hip", "common.hpp", "ssd_kernels.hpp", "ssd_dispatch.cpp"]
+# the per-(batch, head) kernel at 256-token chunks (the CB pass and the chunk kernel)
+CHUNK_SOURCES = ["ssd_bf16.hpp", "ssd_bf16_t256.hip", "common.hpp", "ssd_kernels.hpp", "ssd_dispatch.cpp"]
 SCAN_SOURCES = ["linear_scan.hip", "common.hpp"]
 STEP_SOURCES = ["ssd_step.hip", "common.hpp"]
 
@@ -172,6 +177,7 @@ def record_traffic(fetch_csv, write_csv, workload):
         return statistics.mean(f) * sf * 1024, statistics.mean(w) * sw * 1024, len(f)
 
     groups = [("ssd_fwd:" + workload, SSD_SOURCES, ["ssd_cbt_kernel<", "ssd_fused_agg_kernel<", "ssd_fused_kernel<"]),
+              ("ssd_fwd_chunk_kernel:" + workload, CHUNK_SOURCES, ["ssd_cb_kernel<", "ssd_chunk_kernel<"]),
               ("linear_scan:scan", SCAN_SOURCES, ["linear_scan_kernel<false, float, float, false, 2048>"]),
               ("ssd_step:decode_large", STEP_SOURCES, ["ssd_step_kernel"])]
     for key, srcs, pats in groups:
@@ -227,12 +233,18 @@ def _dev():
 
 
 class SsdRunner(Runner):
-    def __init__(self, name):
+    """One ssd_fwd call per step.  path "chunk": the call forced onto the
+    per-(batch, head) kernel through ssd_fwd_planned."""
+
+    def __init__(self, name, path="auto"):
         import torch
         import chunked_linear_scan_amd as cls
         from chunked_linear_scan_amd import workloads
         self.cls = cls
-        self.name = name
+        self.workload = name
+        self.path = path
+        self.name = name + ("" if path == "auto" else ":chunk_kernel")
+        self.plan = cls.plan_request(path=path) if path != "auto" else None
         self.shape, _ = workloads.SSD_WORKLOADS[name]
         self.inp = workloads.ssd_workload(name)
         self.alg_bytes = ssd_alg_bytes(self.inp, self.shape)
@@ -250,14 +262,23 @@ class SsdRunner(Runner):
 
     def step(self, i):
         d = self.sets[i % self.nsets]
-        self.cls.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=self.shape.chunk,
-                         out=d["y"])
+        if self.plan is None:
+            self.cls.ssd_fwd(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=self.shape.chunk,
+                             out=d["y"])
+        else:
+            self.cls.ssd_fwd_planned(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"],
+                                     chunk=self.shape.chunk, plan=self.plan, out=d["y"])
 
     def describe(self):
         s = self.shape
-        return (f"{self.name}: batch {s.batch}, L={s.seqlen}, {s.nheads} heads, P={s.headdim}, S={s.dstate}, "
+        return (f"{self.workload}: batch {s.batch}, L={s.seqlen}, {s.nheads} heads, P={s.headdim}, S={s.dstate}, "
                 f"{s.ngroups} group(s), chunk {s.chunk}, {s.dtype}"
-                + (f", h0 ~ N(0, {s.h0_std}^2)" if s.h0_std > 0 else ""))
+                + (f", h0 ~ N(0, {s.h0_std}^2)" if s.h0_std > 0 else "")
+                + ("" if self.plan is None else ", forced onto the per-(batch, head) kernel"))
+
+    def traffic_key(self):
+        return (("ssd_fwd:" if self.plan is None else "ssd_fwd_chunk_kernel:") + self.workload,
+                SSD_SOURCES if self.plan is None else CHUNK_SOURCES)
 
     def per_launch(self, calls=20):
         """Mean time of each launch of a call: events between the launches
@@ -268,9 +289,12 @@ class SsdRunner(Runner):
         for k in range(calls):
             d = self.sets[k % self.nsets]
             cls.ssd_fwd_planned(d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"], chunk=self.shape.chunk,
-                                out=d["y"], events=evs[k])
+                                plan=self.plan, out=d["y"], events=evs[k])
         torch.cuda.synchronize()
         t = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / calls * 1e3 for j in range(3)]
+        if self.plan is not None:  # one CB pass and the chunk kernel, timed as one
+            return {"cb_pass_and_chunk_kernel_us": round(t[2], 2),
+                    "grid": f"{self.shape.batch * self.shape.nheads} workgroups, one per (batch, head)"}
         plan = cls.ssd_fwd_plan(self.shape.batch, self.shape.seqlen, self.shape.nheads, self.shape.headdim,
                                 self.shape.dstate, self.shape.ngroups, self.shape.chunk, self.inp["x"].dtype)
         return {"cb_pass_us": round(t[0], 2), "aggregate_launch_us": round(t[1], 2),
@@ -574,7 +598,7 @@ def ssd_result(r, st, steps):
            "us_per_call": _us(t), "timing": timing_block(st, steps), "buffer_sets": r.nsets,
            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(gbs / HBM_PEAK_GBS, 4),
-                        "traffic": measured_traffic("ssd_fwd:" + r.name, SSD_SOURCES),
+                        "traffic": measured_traffic(*r.traffic_key()),
                         "kernel": "whole ssd_fwd call", "alg_bytes": r.alg_bytes,
                         "frac_at_median": round(r.alg_bytes / st["median"] / 1e9 / HBM_PEAK_GBS, 4),
                         "mfma": {"alg_flops": r.flops, "achieved_tflops": round(tflops, 1),
@@ -703,7 +727,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="ssd_long", choices=["ssd_small", "ssd_large", "ssd_long", "ssd_tiny"])
+    ap.add_argument("--workload", default="ssd_long",
+                    choices=["ssd_small", "ssd_large", "ssd_long", "ssd_tiny", "ssd_large_p128"])
+    ap.add_argument("--path", default="auto", choices=["auto", "chunk"],
+                    help="SSD path of --workload: auto (what ssd_fwd runs) or chunk (forced onto the "
+                         "per-(batch, head) kernel; counter and trace runs of that kernel)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-autotune", action="store_true",
                     help="skip the autotuner comparison (counter runs: its candidate plans would mix into "
@@ -762,13 +790,15 @@ def main():
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
     clocks_before = None if args.no_clocks else gpu_state()
-    head = SsdRunner(args.workload)
+    head = SsdRunner(args.workload, args.path)
     log(f"headline {head.describe()}, {head.nsets} buffer set(s)")
     side = []
     if not args.only_headline:
-        for name in ("ssd_large", "ssd_small", "ssd_tiny"):
-            if name != args.workload and not args.no_side_ssd:
-                side.append(SsdRunner(name))
+        if not args.no_side_ssd:
+            for name, path in (("ssd_large", "auto"), ("ssd_small", "auto"), ("ssd_tiny", "auto"),
+                               ("ssd_large_p128", "auto"), ("ssd_large", "chunk")):
+                if (name, path) != (args.workload, args.path):
+                    side.append(SsdRunner(name, path))
         side += [ScanRunner("scan"), ScanRunner("scan_ragged"), ScanRunner("scan", "bf16", "f32"),
                  ScanRunner("scan", "bf16", "bf16"), ScanRunner("scan", "f16", "f32"), ScanRunner("scan", "f16", "f16"),
                  HillisSteeleRunner("scan"), Scan3Runner("scan"), MulRunner("scan"), StreamRunner("scan", 2, True),
@@ -855,7 +885,7 @@ def main():
         so["tokens_per_s"] = round(step.shape.batch / stats[step.name]["mean"], 1)
         so["roofline"]["traffic"] = measured_traffic("ssd_step:" + step.name, STEP_SOURCES)
         line["ssd_step"] = so
-    if not args.no_autotune:
+    if not args.no_autotune and args.path == "auto":
         log("autotune comparison")
         line["autotune"] = autotune_compare(head, max(args.steps // 2, NWIN), args.warmup)
         if others:

@@ -317,6 +317,7 @@ size_t ssd_fwd_planned_workspace_size(int64_t batch, int64_t seqlen, int64_t nhe
     SsdLaunchOpts o{};
     if (cls_ssd_check(s) != SSD_OK || !plan_options(plan, &seg, &o)) return 0;
     const size_t need = cls_ssd_plan_bytes(s, o);
+    if (dtype == SSD_BF16 && need == 0) return 0;  // this plan cannot run the shape
     const size_t base = cls_ssd_workspace_bytes(s);
     return need > base ? need : base;
 }
@@ -331,9 +332,15 @@ int ssd_fwd_planned(const void* x, const float* dt, const float* A, const void* 
     cls::SegChoice seg{};
     SsdLaunchOpts o{};
     if (!plan_options(plan, &seg, &o)) return SSD_ERR_SHAPE;
-    const int st = ssd_fwd_validate(s, args, workspace_bytes);
+    // pointers, shape and alignment first, then whether this plan can run the
+    // shape, then the workspace size
+    int st = ssd_fwd_validate(s, args, SIZE_MAX);
     if (st != SSD_OK) return st;
-    if (workspace_bytes < cls_ssd_plan_bytes(s, o)) return SSD_ERR_WORKSPACE;
+    const size_t need = cls_ssd_plan_bytes(s, o);
+    if (dtype == SSD_BF16 && need == 0) return SSD_ERR_UNSUPPORTED;
+    st = ssd_fwd_validate(s, args, workspace_bytes);
+    if (st != SSD_OK) return st;
+    if (workspace_bytes < need) return SSD_ERR_WORKSPACE;
     hipEvent_t ev[4];
     if (events) {
         for (int k = 0; k < 4; ++k) {

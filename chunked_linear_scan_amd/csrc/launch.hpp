@@ -72,7 +72,7 @@ int cls_ssd_check(const SsdShape& s);
 size_t cls_ssd_workspace_bytes(const SsdShape& s);
 int cls_ssd_launch(const SsdShape& s, const SsdArgs& a, const SsdLaunchOpts& o, hipStream_t stream);
 // Workspace bytes of the plan a call with these options runs (0 for paths
-// without a workspace).
+// without a workspace, and for a bf16 plan that cannot run the shape).
 size_t cls_ssd_plan_bytes(const SsdShape& s, const SsdLaunchOpts& o);
 // Times the fused path's candidate segment plans on these arguments, keeps the
 // fastest for the shape and leaves its result in y / h_final (blocking).

@@ -103,7 +103,8 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     // result only by rounding (the chunked form equals the recurrence for every
     // chunk length).  A plan may ask for shorter sub-chunks (64 or 32 tokens).
     chunk = chunk > kFusedMaxChunk ? kFusedMaxChunk : chunk;
-    const int64_t nchains = batch * H;
+    // a head of dim 128 runs as two chains of head dim 64
+    const int64_t nchains = batch * H * (P == 128 ? 2 : 1);
     // the segment plan: forced, else tuned for this shape, else the heuristic
     SegChoice ch{1, 0};
     bool heuristic = true;
@@ -115,10 +116,10 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     }
     if (!heuristic && ch.sub >= 32 && ch.sub < chunk && chunk % ch.sub == 0) chunk = ch.sub;
     const int TT = bf16_tile_tokens(int(chunk));
-    pl.use = dtype == 1 && P == 64 && (S == 64 || S == 128) && ssd_fused_lds_bytes(TT, int(S)) > 0 &&
+    pl.use = dtype == 1 && (P == 64 || P == 128) && (S == 64 || S == 128) && ssd_fused_lds_bytes(TT, int(S)) > 0 &&
              ssd_fused_lds_bytes(TT, int(S)) <= 160 * 1024 && path != 1;
     // the kernel's per-chunk buffer ranges and lane offsets are 32-bit
-    if (H * 64 * 2 * TT >= (int64_t(1) << 31) || G * S * 2 * TT >= (int64_t(1) << 31)) pl.use = false;
+    if (H * P * 2 * TT >= (int64_t(1) << 31) || G * S * 2 * TT >= (int64_t(1) << 31)) pl.use = false;
     if (!pl.use) return pl;
     const int64_t nc = (L + chunk - 1) / chunk;
     // Each workgroup runs one chain (or segment) at a time, one per CU.  The
@@ -233,8 +234,13 @@ extern "C" int cls_ssd_check(const SsdShape& s) {
         if (s.headdim * s.dstate > 16384 || s.headdim % 4 != 0 || s.dstate % 4 != 0) return SSD_ERR_UNSUPPORTED;
         if (cls::ssd_f32_lds_bytes(int(s.headdim), int(s.dstate)) > 160 * 1024) return SSD_ERR_UNSUPPORTED;
     } else {
+        // the per-(batch, head) kernel's tiles must fit LDS, unless the fused
+        // path takes the shape (it runs chunks over 128 tokens as sub-chunks)
         const int TT = cls::bf16_tile_tokens(int(s.chunk));
-        if (!cls::ssd_bf16_supported(TT, int(s.headdim), int(s.dstate))) return SSD_ERR_UNSUPPORTED;
+        if (!cls::ssd_bf16_supported(TT, int(s.headdim), int(s.dstate)) &&
+            !cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk, s.dtype)
+                 .use)
+            return SSD_ERR_UNSUPPORTED;
         if (s.batch * nchunks(s) * s.ngroups > (int64_t(1) << 31)) return SSD_ERR_SHAPE;
     }
     return SSD_OK;
@@ -256,7 +262,7 @@ std::vector<cls::SegChoice> fused_candidates(const SsdShape& s) {
     for (int64_t sub : {base, int64_t(64)}) {
         if (sub != base && !(sub < base && base % sub == 0)) continue;
         const int64_t nc = (s.seqlen + sub - 1) / sub;
-        for (cls::SegChoice c : cls::seg_candidates(s.batch * s.nheads, nc, cls::fused_slots())) {
+        for (cls::SegChoice c : cls::seg_candidates(pl.nchains, nc, cls::fused_slots())) {
             c.sub = sub == base ? 0 : sub;
             for (int nt : {1, 2}) {
                 c.nt = nt;
@@ -299,6 +305,9 @@ extern "C" size_t cls_ssd_plan_bytes(const SsdShape& s, const SsdLaunchOpts& o) 
                                                      s.ngroups, s.chunk, s.dtype, o.force, o.path, o.s3, o.xcds);
     if (pl.use) return pl.bytes;
     const int64_t TT = cls::bf16_tile_tokens(int(s.chunk));
+    // 0: the plan keeps the fused path out and the per-(batch, head) kernel's
+    // tiles do not fit LDS
+    if (!cls::ssd_bf16_supported(int(TT), int(s.headdim), int(s.dstate))) return 0;
     return size_t(s.batch) * size_t(nchunks(s)) * size_t(s.ngroups) * size_t(TT * TT) * 2 + cls::kSsdWsHeader;
 }
 
@@ -367,7 +376,8 @@ static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const SsdLaunchO
         f.err = reinterpret_cast<uint32_t*>(ws);
         f.batch = s.batch;
         f.L = s.seqlen;
-        f.H = int(s.nheads);
+        f.hshift = s.headdim == 128 ? 1 : 0;
+        f.H = int(s.nheads) << f.hshift;
         f.G = int(s.ngroups);
         f.chunk = p.chunk;
         f.nchunks = p.nchunks;

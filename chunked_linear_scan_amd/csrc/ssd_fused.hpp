@@ -1,5 +1,7 @@
 // Fused bf16 SSD forward pass on gfx950 for head dim 64: one workgroup walks
-// a run of chunks of one (batch, head) with the state on chip.
+// a run of chunks of one (batch, head) with the state on chip.  A head of dim
+// 128 runs as two heads of dim 64 (the recurrence is per channel), which share
+// its dt, A and D.
 //
 // Follows "Accelerating Mamba-2 with high-performance forward pass kernels in
 // NVIDIA cuTile" (sections "Mamba-2 architecture", "Kernel 1/2/3"): per chunk
@@ -466,8 +468,9 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
     const int64_t b = chain / p.H;
     const int h = chain % p.H;
     const int g = h / (p.H / p.G);
-    const float A2 = p.A[h] * kLog2e;
-    const float Dh = p.D ? p.D[h] : 0.0f;
+    const int hin = h >> p.hshift;  // the input head (dt, A, D)
+    const float A2 = p.A[hin] * kLog2e;
+    const float Dh = p.D ? p.D[hin] : 0.0f;
     const int64_t L = p.L;
     const int64_t bh = b * p.H + h;
 
@@ -537,7 +540,7 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
         for (int m = 0; m < 4; ++m) xreg[m] = __builtin_amdgcn_raw_buffer_load_b128(rx, int(xoff[m]), 0, kXyPolicy);
         // dt from the CB pass's token-contiguous copy (zeros past the last real row)
         const auto rd = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<float*>(p.dtt + ((b * p.nchunks + c) * p.H + h) * TT), 0, TT * 4, 0x00020000);
+            const_cast<float*>(p.dtt + ((b * p.nchunks + c) * (p.H >> p.hshift) + hin) * TT), 0, TT * 4, 0x00020000);
         dtv = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, int(dtoff), 0, 0));
         if constexpr (OUT) {
             const auto rcb = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(cb_base(c)), 0, TT * TT * 2,

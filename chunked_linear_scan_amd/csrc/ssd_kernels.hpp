@@ -67,6 +67,11 @@ struct SsdFusedParams {
     // segments but the last of every split chain, as agg_d pieces of at most
     // agg_chunks chunks per segment.
     int H, G, chunk, nchunks, seg_chunks, nsegs, nchains, nwhole;
+    // H counts heads of dim 64.  A head of dim 64 << hshift runs as 1 << hshift
+    // adjacent heads of dim 64 (its channels are independent, and x, y, h0 and
+    // h_final hold them at the same addresses either way); head h reads dt, A
+    // and D of head h >> hshift.
+    int hshift;
     int agg_d, agg_chunks;
     int nxcd;  // XCDs the workgroups are dealt across (tile mapping only)
     // Single-pass look-back over the segments of split chains (no aggregate
@@ -83,7 +88,8 @@ struct SsdFusedParams {
     uint32_t stress;     // look-back stress seed (tests only; 0: none)
 };
 
-// Plan of the fused head-dim-64 path for one shape (also sizes its workspace).
+// Plan of the fused path (head dim 64, or 128 as two heads of 64) for one
+// shape (also sizes its workspace).
 constexpr int64_t kFusedMaxChunk = 128;  // longest quadratic block of the fused kernel
 
 // The first bytes of every bf16 SSD workspace: the error word at 0 and the

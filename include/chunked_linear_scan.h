@@ -74,8 +74,11 @@ enum { SSD_F32 = 0, SSD_BF16 = 1, SSD_F16 = 2 };
  * the kernels rely on that to never keep a positive exponent.
  *
  * SSD_BF16 runs the MFMA path (bf16 operands, fp32 accumulation and fp32
- * state); it supports headdim in {16, 32, 64, 128} and dstate in
- * {32, 64, 128, 256} where the chunk's tiles fit the 160 KB of LDS
+ * state).  Head dim 64 or 128 with dstate 64 or 128 runs the fused kernels
+ * at every chunk length (a head of dim 128 as two heads of dim 64, whose
+ * channels are independent); the other shapes with headdim in
+ * {16, 32, 64, 128} and dstate in {32, 64, 128, 256} run the per-(batch,
+ * head) kernel where the chunk's tiles fit the 160 KB of LDS
  * (SSD_ERR_UNSUPPORTED otherwise; ssd_fwd_workspace_size returns 0 then).
  * SSD_F32 runs an fp32 path for any shape with headdim * dstate <= 16384 and
  * headdim, dstate multiples of 4.
@@ -97,7 +100,7 @@ int ssd_fwd(const void* x, const float* dt, const float* A, const void* B,
  * Per-shape autotuning of ssd_fwd ("Accelerating Mamba-2 with high-performance
  * forward pass kernels in NVIDIA cuTile", section "Mamba-2 performance
  * optimization", its autotuner item: a search per input shape, since no one
- * setting suits every shape).  The run-time choices of the bf16 head-dim-64
+ * setting suits every shape).  The run-time choices of the fused bf16
  * path form its plan:
  *   - the segment plan: how many segments a long (batch, head) chain is cut
  *     into, which chains are cut, and, for reduce-then-fold, how many pieces

@@ -1,7 +1,7 @@
 /*
  * chunked_linear_scan — entry point for tests and measurement.
  *
- * ssd_fwd chooses its kernels and, on the fused head-dim-64 bf16 path, its
+ * ssd_fwd chooses its kernels and, on the fused bf16 path, its
  * segment plan by itself (a tuned plan from ssd_fwd_autotune, else a built-in
  * heuristic).  ssd_fwd_planned is ssd_fwd with that choice made explicitly by
  * the caller, per call: parity tests use it to force every plan shape (whole
@@ -24,9 +24,10 @@ extern "C" {
 /* Kernel choice of one call. */
 enum {
     SSD_PATH_AUTO = 0,   /* what ssd_fwd would run                                 */
-    SSD_PATH_CHUNK = 1,  /* the per-(batch, head) chunk kernel (any bf16 shape)    */
-    SSD_PATH_FUSED = 2   /* the fused head-dim-64 kernels (falls back to AUTO where
-                            they do not apply)                                     */
+    SSD_PATH_CHUNK = 1,  /* the per-(batch, head) chunk kernel (bf16 shapes whose
+                            chunk tiles fit LDS; SSD_ERR_UNSUPPORTED otherwise)    */
+    SSD_PATH_FUSED = 2   /* the fused kernels, head dim 64 or 128 (falls back to
+                            AUTO where they do not apply)                          */
 };
 
 /* The inter-segment schemes (SSD_S3_AUTO, SSD_S3_REDUCE, SSD_S3_LOOKBACK) are
@@ -38,7 +39,8 @@ typedef struct {
     int32_t s3;          /* SSD_S3_*                                                 */
     int64_t nsegs;       /* segments per split chain, 1..64; 0: tuned or heuristic   */
     int64_t nsplit;      /* with nsegs: split only the last nsplit (batch, head)
-                            chains, the others run whole; 0: split every chain      */
+                            chains, the others run whole; 0: split every chain
+                            (a head of dim 128 is two chains of dim 64)            */
     int64_t agg_pieces;  /* with nsegs and SSD_S3_REDUCE: aggregate pieces per
                             segment; 0: the heuristic's count                      */
     int32_t xcds;        /* XCDs the workgroups are dealt across (chain mapping

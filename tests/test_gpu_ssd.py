@@ -71,7 +71,7 @@ def test_fp32_chunk_sizes_and_ragged(chunk):
 
 
 @pytest.mark.parametrize("chunk", [16, 32, 64, 128, 256])
-@pytest.mark.parametrize("P,S", [(16, 32), (64, 128), (32, 64), (128, 64), (64, 64)])
+@pytest.mark.parametrize("P,S", [(16, 32), (64, 128), (32, 64), (128, 64), (64, 64), (128, 128), (32, 256)])
 def test_bf16_shapes_chunks_ragged(P, S, chunk):
     if not cls.load_library().ssd_fwd_workspace_size(2, 301, 4, P, S, 2, chunk, cls.SSD_BF16):
         pytest.skip("shape not supported by the bf16 kernels at this chunk")
@@ -200,13 +200,14 @@ def test_one_state_one_channel_matches_linear_scan():
 @pytest.mark.parametrize("plan", [None, {"nsegs": 4, "nsplit": 5}, {"nsegs": 4, "nsplit": 5, "s3": "lookback"},
                                   {"nsegs": 16, "s3": "lookback"}],
                          ids=["default", "split", "lookback", "lookback16"])
-def test_deterministic_100_runs(plan):
+@pytest.mark.parametrize("P", [64, 128])
+def test_deterministic_100_runs(plan, P):
     """100 reruns are bit-identical, with whole chains and with split chains
     (reduce-then-fold: the aggregate launch and the fold at each segment
     start; look-back: segments claimed in whatever order the workgroups run,
     folding whatever their predecessors have published, which must not change
     a bit of the result)."""
-    inp = small_case(9, 2, 1024, 8, 64, 128, 2, torch.bfloat16)
+    inp = small_case(9, 2, 1024, 8, P, 128, 2, torch.bfloat16)
     d = to_dev(inp)
     args = (d["x"], d["dt"], d["A"], d["B"], d["C"], d["D"], d["h0"])
     pr = cls.plan_request(**plan) if plan else None
@@ -221,7 +222,7 @@ def test_deterministic_100_runs(plan):
     parity.check_ssd(inp, y0.float().cpu().numpy(), h0.cpu().numpy(), 256, "determinism")
 
 
-@pytest.mark.parametrize("name", ["ssd_small", "ssd_large", "ssd_long"])
+@pytest.mark.parametrize("name", ["ssd_small", "ssd_large", "ssd_long", "ssd_large_p128"])
 def test_full_workloads_whole(name):
     """The full-size workloads as ssd_fwd runs them by default, every output
     compared (the oracle runs over all (batch, head) sequences in a pool)."""
@@ -276,6 +277,16 @@ def test_chain_mapping_over_xcds(xcds, s3):
     run_and_check(inp, 128, f"xcds={xcds} {s3}", plan=cls.plan_request(nsegs=3, nsplit=7, xcds=xcds, s3=s3))
 
 
+def test_full_workload_on_the_chunk_kernel():
+    """The large-model layer forced onto the per-(batch, head) kernel (the
+    configuration the benchmark times for that kernel); every output
+    compared."""
+    print("[ssd] ssd_large full size, per-(batch, head) kernel", flush=True)
+    inp = workloads.ssd_workload("ssd_large")
+    y, hf = gpu_run(inp, plan=cls.plan_request(path="chunk"))
+    parity.check_ssd_workload("ssd_large", y, hf, label="ssd_large chunk kernel")
+
+
 @pytest.mark.parametrize("name", ["ssd_large", "ssd_long"])
 def test_full_workloads_lookback(name):
     """The two workloads whose plans split chains, with the split chains'
@@ -322,6 +333,53 @@ def test_cache_policies_give_the_same_bits(plan):
     assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
     assert np.array_equal(h0.view(np.uint32), h1.view(np.uint32))
     parity.check_ssd(inp, y1, h1, 128, f"non-temporal {plan}")
+
+
+HEAD128_PLANS = [None, dict(nsegs=3, nsplit=3), dict(nsegs=4, nsplit=5, s3="lookback"),
+                 dict(nsegs=2, s3="reduce", sub_chunk=64), dict(nsegs=3, nsplit=1, s3="lookback", cache_policy="nontemporal")]
+
+
+@pytest.mark.parametrize("chunk", [64, 256])
+@pytest.mark.parametrize("S", [64, 128])
+@pytest.mark.parametrize("plan", HEAD128_PLANS, ids=["heuristic", "split3", "lookback5", "sub64", "lookback1-nt"])
+def test_head_dim_128_on_the_fused_path(plan, S, chunk):
+    """Head dim 128 runs on the fused kernels as two chains of head dim 64
+    that share the head's dt, A and D.  An odd nsplit splits one half of a
+    head into segments and runs the other half whole."""
+    inp = small_case(170 + S + chunk, 2, 64 * 25 + 9, 4, 128, S, 2, torch.bfloat16, dt_shift=-3.0)
+    assert cls.ssd_fwd_plan(2, 64 * 25 + 9, 4, 128, S, 2, chunk)["nsegs"] >= 1
+    run_and_check(inp, chunk, f"P=128 S={S} chunk={chunk} {plan}",
+                  plan=None if plan is None else cls.plan_request(**plan))
+
+
+@pytest.mark.parametrize("plan", HEAD128_PLANS[:3], ids=["heuristic", "split3", "lookback5"])
+def test_head_dim_128_equals_two_heads_of_64(plan):
+    """A head of dim 128 gives, bit for bit, what two heads of dim 64 give
+    when they hold its two halves of x and h0 and both carry its dt, A and D
+    (the same memory for x, y and the states; the same chains and plan)."""
+    print(f"[ssd P=128 as 2x64] {plan}", flush=True)
+    Bt, L, H, S, G = 2, 64 * 20 + 3, 4, 128, 2
+    w = small_case(190, Bt, L, H, 128, S, G, torch.bfloat16, dt_shift=-3.0)
+    n = {"x": w["x"].reshape(Bt, L, 2 * H, 64), "dt": w["dt"].repeat_interleave(2, dim=-1).contiguous(),
+         "A": w["A"].repeat_interleave(2), "B": w["B"], "C": w["C"], "D": w["D"].repeat_interleave(2),
+         "h0": w["h0"].reshape(Bt, 2 * H, 64, S), "chunk": 32}
+    req = None if plan is None else cls.plan_request(**plan)
+    y_w, h_w = gpu_run(w, chunk=128, plan=req)
+    y_n, h_n = gpu_run(n, chunk=128, plan=req)
+    assert np.array_equal(y_w.reshape(y_n.shape).view(np.uint32), y_n.view(np.uint32))
+    assert np.array_equal(h_w.reshape(h_n.shape).view(np.uint32), h_n.view(np.uint32))
+    parity.check_ssd(w, y_w, h_w, 128, f"P=128 {plan}")
+
+
+def test_head_dim_128_chunk_kernel_where_it_fits():
+    """The per-(batch, head) kernel still runs head dim 128 when forced at a
+    chunk whose tiles fit LDS; at 256 tokens with dstate 128 they do not, and
+    the forced plan is rejected before anything runs."""
+    inp = small_case(197, 2, 700, 4, 128, 128, 2, torch.bfloat16)
+    run_and_check(inp, 128, "P=128 chunk kernel forced", plan=cls.plan_request(path="chunk"))
+    with pytest.raises(cls.SSDError) as err:
+        gpu_run(inp, chunk=256, plan=cls.plan_request(path="chunk"))
+    assert err.value.status == -8
 
 
 @pytest.mark.parametrize("A_value", [0.0, -1e-3])
