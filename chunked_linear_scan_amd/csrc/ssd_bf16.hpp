@@ -126,14 +126,65 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cb_kernel(SsdBf16Params p) {
 // ---------------------------------------------------------------------------
 // S1, S2b, S2c, S3, S4 for one (batch, head): chunks in order, state in
 // registers (fp32) and in LDS as the bf16 MFMA operand.
+//
+// One workgroup of four waves per (batch, head); chunks over 128 tokens run as
+// 128-token sub-chunks (or shorter, until the tiles fit LDS).  Where LDS
+// allows few workgroups per CU, each output tile issues all of its C and
+// C B^T loads before its first product and chunk c + 1's dt, X and B rows
+// are loaded while chunk c computes.  The barriers order LDS only
+// (s_waitcnt lgkmcnt(0); s_barrier), so loads stay in flight across them.
+// Eight waves per workgroup measured slower on three of four shapes.
 // ---------------------------------------------------------------------------
+constexpr int kChunkWaves = 4;
+constexpr int kChunkThreads = 64 * kChunkWaves;
+
+__device__ __forceinline__ void chunk_lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Inclusive sum over the workgroup's threads in order (one value each);
+// `scratch` holds kChunkWaves floats of LDS.  Ends with a barrier.
+__device__ __forceinline__ float chunk_inclusive_sum(float v, float* scratch) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const float o = __shfl_up(v, d, 64);
+        if (lane >= d) v += o;
+    }
+    if (lane == 63) scratch[wave] = v;
+    chunk_lds_barrier();
+    float add = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kChunkWaves - 1; ++q)
+        if (q < wave) add += scratch[q];
+    chunk_lds_barrier();
+    return v + add;
+}
+
 template <int TT, int P, int S>
-__global__ __launch_bounds__(kBfThreads) void ssd_chunk_kernel(SsdBf16Params p) {
-    constexpr int XP = TT + 8;         // LDS pitch (elements) of X^T and B^T rows
-    constexpr int HP = S + 8;          // LDS pitch of the bf16 state rows
-    constexpr int NPT = P / 16;        // head-dim tiles
-    constexpr int NST = S / 16;        // state tiles
-    constexpr int KS = (NST + 3) / 4;  // state tiles per wave
+__global__ __launch_bounds__(kChunkThreads) void ssd_chunk_kernel(SsdBf16Params p) {
+    constexpr int NW = kChunkWaves, NT = kChunkThreads;
+    constexpr int XP = TT + 8;            // LDS pitch (elements) of X^T and B^T rows
+    constexpr int HP = S + 8;             // LDS pitch of the bf16 state rows
+    constexpr int NPT = P / 16;           // head-dim tiles
+    constexpr int NST = S / 16;           // state tiles
+    constexpr int KS = (NST + NW - 1) / NW;  // state tiles per wave
+    constexpr int NJB = TT / 32;          // 32-token blocks of a chunk
+    // 8-token x 8-channel items of the X and B transposes, and per thread
+    constexpr int NXQ = (TT / 8) * (P / 8), NBQ = (TT / 8) * (S / 8);
+    constexpr int NXI = (NXQ + NT - 1) / NT, NBI = (NBQ + NT - 1) / NT;
+    // Loads ahead of use.  Where LDS already keeps a CU to at most three of
+    // these workgroups, the registers are better spent holding loads early:
+    // a tile issues all of its loads at once and, with room to spare, the
+    // next chunk's rows are held through this chunk's products (VGPRs per
+    // lane estimated from the state, a tile's loads and accumulators, and the
+    // held rows; spill-free per instance at these bounds).  Where more
+    // workgroups fit, fewer registers per wave (more workgroups per CU) hide
+    // latency better: measured 706 against 1228 us on a head-dim-32 layer.
+    constexpr int kLdsWorkgroups = int((size_t(160) * 1024) / ssd_bf16_lds_bytes(TT, P, S));
+    constexpr int kTileRegs = (KS * NPT + S / 32 + NJB + NPT) * 4;
+    constexpr bool kTileAhead = kLdsWorkgroups <= 3 && kTileRegs <= 192;
+    constexpr bool kAhead = kTileAhead && kTileRegs + 32 * (NXI + NBI) <= 160;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     uint16_t* Xt = reinterpret_cast<uint16_t*>(smem_raw);   // [P][XP]
     uint16_t* Bt = Xt + P * XP;                              // [S][XP]
@@ -141,7 +192,7 @@ __global__ __launch_bounds__(kBfThreads) void ssd_chunk_kernel(SsdBf16Params p) 
     float* Gs = reinterpret_cast<float*>(Hs + P * HP);       // [TT]
     float* dts = Gs + TT;                                    // [TT]
     float* ws = dts + TT;                                    // [TT]
-    float* scratch = ws + TT;                                // [4]
+    float* scratch = ws + TT;                                // [NW]
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kg = lane >> 4;
@@ -153,11 +204,11 @@ __global__ __launch_bounds__(kBfThreads) void ssd_chunk_kernel(SsdBf16Params p) 
     const float Dh = p.D ? p.D[h] : 0.0f;
     const int64_t L = p.L;
 
-    // state h^T tiles owned by this wave: s-tiles st = wave + 4k, all p-tiles
+    // state h^T tiles owned by this wave: s-tiles st = wave + NW k, all p-tiles
     f32x4 hacc[KS][NPT];
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-        const int st = wave + 4 * k;
+        const int st = wave + NW * k;
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) {
             f32x4 v = {0.f, 0.f, 0.f, 0.f};
@@ -175,45 +226,90 @@ __global__ __launch_bounds__(kBfThreads) void ssd_chunk_kernel(SsdBf16Params p) 
         }
     }
 
+    // dt of a chunk (one token per thread); X and B rows of transpose item q
+    // (8 tokens x 8 channels, 8 rows of 16 bytes)
+    auto load_dt = [&](int64_t tok0, int n) { return tid < n ? p.dt[(b * L + tok0 + tid) * p.H + h] : 0.0f; };
+    auto x_row = [&](int64_t tok0, int n, int q, int e) {
+        const int t = 8 * (q / (P / 8)) + e;
+        return (q < NXQ && t < n) ? ldg16(p.x + ((b * L + tok0 + t) * p.H + h) * P + 8 * (q % (P / 8)))
+                                  : u32x4{0, 0, 0, 0};
+    };
+    auto b_row = [&](int64_t tok0, int n, int q, int e) {
+        const int t = 8 * (q / (S / 8)) + e;
+        return (q < NBQ && t < n) ? ldg16(p.B + ((b * L + tok0 + t) * p.G + g) * S + 8 * (q % (S / 8)))
+                                  : u32x4{0, 0, 0, 0};
+    };
+    // X^T [p][t] and B^T [s][t] (bf16) into LDS through an 8x8 register transpose
+    auto store_x = [&](int q, const u32x4 (&r)[8]) {
+        const int tb = q / (P / 8), pb = q % (P / 8);
+        u32x4 o[8];
+        transpose8x8_b16(r, o);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4*>(Xt + (8 * pb + e) * XP + 8 * tb) = o[e];
+    };
+    auto store_b = [&](int q, const u32x4 (&r)[8]) {
+        const int tb = q / (S / 8), sb = q % (S / 8);
+        u32x4 o[8];
+        transpose8x8_b16(r, o);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4*>(Bt + (8 * sb + e) * XP + 8 * tb) = o[e];
+    };
+    // kAhead: the next chunk's dt and rows, loaded during this chunk's products
+    float dt_nx = 0.0f;
+    u32x4 xr[kAhead ? NXI : 1][8], br[kAhead ? NBI : 1][8];
+    auto fetch = [&](int c) {
+        const int64_t tok0 = int64_t(c) * p.chunk;
+        const int n = int((L - tok0 < p.chunk) ? (L - tok0) : p.chunk);
+        dt_nx = load_dt(tok0, n);
+#pragma unroll
+        for (int k = 0; k < NXI; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xr[k][e] = x_row(tok0, n, tid + NT * k, e);
+#pragma unroll
+        for (int k = 0; k < NBI; ++k)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) br[k][e] = b_row(tok0, n, tid + NT * k, e);
+    };
+    if constexpr (kAhead) fetch(0);
+
     for (int c = 0; c < p.nchunks; ++c) {
         const int64_t tok0 = int64_t(c) * p.chunk;
         const int n = int((L - tok0 < p.chunk) ? (L - tok0) : p.chunk);
 
-        // S1: cumulative sum of a_t (log2 units) inside the chunk
-        float dtv = 0.0f;
-        if (tid < n) dtv = p.dt[(b * L + tok0 + tid) * p.H + h];
-        const float G = block_inclusive_sum_256(A2 * dtv, scratch);
+        // S1: cumulative sum of a_t (log2 units) inside the chunk (threads
+        // past the chunk add 0)
+        const float dtv = kAhead ? dt_nx : load_dt(tok0, n);
+        const float G = chunk_inclusive_sum(A2 * dtv, scratch);
         if (tid < TT) {
             Gs[tid] = G;
             dts[tid] = dtv;
         }
 
-        // stage X^T [p][t] and B^T [s][t] (bf16) through an 8x8 register transpose
-        for (int q = tid; q < (TT / 8) * (P / 8); q += kBfThreads) {
-            const int tb = q / (P / 8), pb = q % (P / 8);
-            u32x4 r[8], o[8];
+        if constexpr (kAhead) {
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int t = 8 * tb + e;
-                r[e] = (t < n) ? ldg16(p.x + ((b * L + tok0 + t) * p.H + h) * P + 8 * pb) : u32x4{0, 0, 0, 0};
+            for (int k = 0; k < NXI; ++k)
+                if (tid + NT * k < NXQ) store_x(tid + NT * k, xr[k]);
+#pragma unroll
+            for (int k = 0; k < NBI; ++k)
+                if (tid + NT * k < NBQ) store_b(tid + NT * k, br[k]);
+        } else {
+            // one item at a time: the state holds most of the registers
+            for (int q = tid; q < NXQ; q += NT) {
+                u32x4 r[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) r[e] = x_row(tok0, n, q, e);
+                store_x(q, r);
             }
-            transpose8x8_b16(r, o);
+            for (int q = tid; q < NBQ; q += NT) {
+                u32x4 r[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4*>(Xt + (8 * pb + e) * XP + 8 * tb) = o[e];
-        }
-        for (int q = tid; q < (TT / 8) * (S / 8); q += kBfThreads) {
-            const int tb = q / (S / 8), sb = q % (S / 8);
-            u32x4 r[8], o[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int t = 8 * tb + e;
-                r[e] = (t < n) ? ldg16(p.B + ((b * L + tok0 + t) * p.G + g) * S + 8 * sb) : u32x4{0, 0, 0, 0};
+                for (int e = 0; e < 8; ++e) r[e] = b_row(tok0, n, q, e);
+                store_b(q, r);
             }
-            transpose8x8_b16(r, o);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x4*>(Bt + (8 * sb + e) * XP + 8 * tb) = o[e];
         }
-        __syncthreads();
+        chunk_lds_barrier();
+        if constexpr (kAhead)
+            if (c + 1 < p.nchunks) fetch(c + 1);  // in flight through this chunk's products
         const float Glast = Gs[TT - 1];  // padded positions add 0: G at the last real token
         if (tid < TT) ws[tid] = dts[tid] * fexp2(Glast - Gs[tid]);
 
@@ -221,33 +317,48 @@ __global__ __launch_bounds__(kBfThreads) void ssd_chunk_kernel(SsdBf16Params p) 
         const uint16_t* cbase = p.cb + ((b * p.nchunks + c) * p.G + g) * (TT * TT);
         const uint16_t* Cbase = p.C + ((b * L + tok0) * p.G + g) * S;
         const int ntile = (n + 15) / 16;
-        for (int it = wave; it < ntile; it += 4) {
+        for (int it = wave; it < ntile; it += NW) {
             const int i = 16 * it + l16;
             const bool vi = i < n;
+            const int jb_end = (16 * it + 15) / 32;
+            // C row i and the C B^T row pieces: all issued first (kTileAhead),
+            // else each right before its product
+            auto load_c = [&](int ks) {
+                return vi ? ldg16(Cbase + int64_t(i) * p.G * S + 32 * ks + 8 * kg) : u32x4{0, 0, 0, 0};
+            };
+            auto load_cb = [&](int jb) {
+                return jb <= jb_end ? ldg16(cbase + i * TT + 32 * jb + 8 * kg) : u32x4{0, 0, 0, 0};
+            };
+            u32x4 cf[S / 32], cbw[NJB];
+            if constexpr (kTileAhead) {
+#pragma unroll
+                for (int ks = 0; ks < S / 32; ++ks) cf[ks] = load_c(ks);
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb) cbw[jb] = load_cb(jb);
+            }
             const float gi = Gs[i];
             f32x4 acc[NPT];
 #pragma unroll
             for (int pt = 0; pt < NPT; ++pt) acc[pt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < S / 32; ++ks) {
-                const u32x4 cf = vi ? ldg16(Cbase + int64_t(i) * p.G * S + 32 * ks + 8 * kg) : u32x4{0, 0, 0, 0};
+                const u32x4 cfk = kTileAhead ? cf[ks] : load_c(ks);
 #pragma unroll
                 for (int pt = 0; pt < NPT; ++pt) {
                     const u32x4 hf = *reinterpret_cast<const u32x4*>(Hs + (16 * pt + l16) * HP + 32 * ks + 8 * kg);
-                    acc[pt] = mfma16x16x32(hf, cf, acc[pt]);
+                    acc[pt] = mfma16x16x32(hf, cfk, acc[pt]);
                 }
             }
             const float sc = fexp2(gi);
 #pragma unroll
             for (int pt = 0; pt < NPT; ++pt) acc[pt] *= sc;
-            const int jb_end = (16 * it + 15) / 32;
-            for (int jb = 0; jb <= jb_end; ++jb) {
+            // diagonal-and-below block jb: W = CB . exp2(G_i - G_j) . dt_j on j <= i, D on j = i
+            auto block = [&](int jb, const u32x4& cbj) {
                 const int j0 = 32 * jb + 8 * kg;
-                const u32x4 cbw = ldg16(cbase + i * TT + j0);
                 float wv[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    const uint32_t word = cbw[e >> 1];
+                    const uint32_t word = cbj[e >> 1];
                     const float cbv = (e & 1) ? bf16_hi(word) : bf16_lo(word);
                     const int j = j0 + e;
                     float w = cbv * fexp2(gi - Gs[j]) * dts[j];
@@ -263,6 +374,13 @@ __global__ __launch_bounds__(kBfThreads) void ssd_chunk_kernel(SsdBf16Params p) 
                     const u32x4 xf = *reinterpret_cast<const u32x4*>(Xt + (16 * pt + l16) * XP + 32 * jb + 8 * kg);
                     acc[pt] = mfma16x16x32(xf, wf, acc[pt]);
                 }
+            };
+            if constexpr (kTileAhead) {
+#pragma unroll
+                for (int jb = 0; jb < NJB; ++jb)
+                    if (jb <= jb_end) block(jb, cbw[jb]);
+            } else {
+                for (int jb = 0; jb <= jb_end; ++jb) block(jb, load_cb(jb));
             }
             if (vi) {
                 uint16_t* dst = p.y + ((b * L + tok0 + i) * p.H + h) * P + 4 * kg;
@@ -275,7 +393,7 @@ __global__ __launch_bounds__(kBfThreads) void ssd_chunk_kernel(SsdBf16Params p) 
                 }
             }
         }
-        __syncthreads();
+        chunk_lds_barrier();
 
         // S2c + S3: h^T <- exp(G_last) h^T + (B^T w) X
         const float alpha = fexp2(Glast);
@@ -295,7 +413,7 @@ __global__ __launch_bounds__(kBfThreads) void ssd_chunk_kernel(SsdBf16Params p) 
                 xf[pt] = *reinterpret_cast<const u32x4*>(Xt + (16 * pt + l16) * XP + t0);
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
-                const int st = wave + 4 * k;
+                const int st = wave + NW * k;
                 if (st >= NST) continue;
                 const u32x4 braw = *reinterpret_cast<const u32x4*>(Bt + (16 * st + l16) * XP + t0);
                 u32x4 af;
@@ -308,7 +426,7 @@ __global__ __launch_bounds__(kBfThreads) void ssd_chunk_kernel(SsdBf16Params p) 
         }
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
-            const int st = wave + 4 * k;
+            const int st = wave + NW * k;
             if (st >= NST) continue;
 #pragma unroll
             for (int pt = 0; pt < NPT; ++pt) {
@@ -318,13 +436,13 @@ __global__ __launch_bounds__(kBfThreads) void ssd_chunk_kernel(SsdBf16Params p) 
                 *reinterpret_cast<u32x2*>(Hs + (16 * pt + l16) * HP + 16 * st + 4 * kg) = w;
             }
         }
-        __syncthreads();
+        chunk_lds_barrier();
     }
 
     if (p.h_final) {
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
-            const int st = wave + 4 * k;
+            const int st = wave + NW * k;
             if (st >= NST) continue;
 #pragma unroll
             for (int pt = 0; pt < NPT; ++pt) {
@@ -346,11 +464,10 @@ int launch_ssd_bf16_tpl(const SsdBf16Params& prm, hipStream_t stream) {
                        : -7;
         }) != 0)
         return -7;
-    const dim3 block{uint32_t(kBfThreads), 1u, 1u};
-    const dim3 gcb{cb_grid<TT>(prm), 1u, 1u};
-    hipLaunchKernelGGL((ssd_cb_kernel<TT, S>), gcb, block, 0, stream, prm);
-    const dim3 gmain{uint32_t(prm.batch * prm.H), 1u, 1u};
-    hipLaunchKernelGGL((ssd_chunk_kernel<TT, P, S>), gmain, block, lds, stream, prm);
+    const dim3 gcb{cb_grid<TT>(prm), 1u, 1u}, bcb{uint32_t(kBfThreads), 1u, 1u};
+    hipLaunchKernelGGL((ssd_cb_kernel<TT, S>), gcb, bcb, 0, stream, prm);
+    const dim3 gmain{uint32_t(prm.batch * prm.H), 1u, 1u}, bmain{uint32_t(kChunkThreads), 1u, 1u};
+    hipLaunchKernelGGL((ssd_chunk_kernel<TT, P, S>), gmain, bmain, lds, stream, prm);
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

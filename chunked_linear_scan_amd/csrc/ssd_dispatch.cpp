@@ -24,6 +24,18 @@ bool ssd_bf16_supported(int TT, int P, int S) {
     return p_ok && s_ok && ssd_bf16_lds_fits(TT, P, S);
 }
 
+// The per-(batch, head) kernel's tile: the chunk (at least 32 tokens), run as
+// sub-chunks of at most kChunkMaxTile tokens and halved until its LDS fits.
+// Sub-chunks change the result only by rounding: the chunked form equals the
+// recurrence for every chunk length.  0: no tile fits (head dim or state size
+// outside the kernel's set).
+int chunk_kernel_tile(int64_t chunk, int P, int S) {
+    int tt = bf16_tile_tokens(int(chunk));
+    if (tt > kChunkMaxTile) tt = kChunkMaxTile;
+    while (tt > 32 && !ssd_bf16_lds_fits(tt, P, S)) tt /= 2;
+    return ssd_bf16_supported(tt, P, S) ? tt : 0;
+}
+
 int ssd_bf16_launch(int TT, int P, int S, const SsdBf16Params& prm, hipStream_t stream) {
     switch (TT) {
         case 32: return ssd_bf16_launch_t32(P, S, prm, stream);
@@ -218,6 +230,26 @@ bool valid_chunk(int64_t c) { return c == 16 || c == 32 || c == 64 || c == 128 |
 
 int64_t nchunks(const SsdShape& s) { return (s.seqlen + s.chunk - 1) / s.chunk; }
 
+// The per-(batch, head) kernel's sub-chunk (tile TT, tokens per sub-chunk) and
+// its workspace: C B^T per (batch, sub-chunk, group); 0 when it has no tile.
+struct ChunkTile {
+    int TT, chunk;
+    int64_t nchunks;
+};
+
+ChunkTile chunk_kernel_plan(const SsdShape& s) {
+    const int tt = cls::chunk_kernel_tile(s.chunk, int(s.headdim), int(s.dstate));
+    const int sub = tt < s.chunk ? tt : int(s.chunk);
+    return ChunkTile{tt, sub, tt ? (s.seqlen + sub - 1) / sub : 0};
+}
+
+size_t chunk_kernel_ws_bytes(const SsdShape& s) {
+    const ChunkTile t = chunk_kernel_plan(s);
+    if (t.TT == 0) return 0;
+    return size_t(s.batch) * size_t(t.nchunks) * size_t(s.ngroups) * size_t(t.TT) * size_t(t.TT) * 2 +
+           cls::kSsdWsHeader;
+}
+
 }  // namespace
 
 extern "C" int cls_ssd_check(const SsdShape& s) {
@@ -234,14 +266,12 @@ extern "C" int cls_ssd_check(const SsdShape& s) {
         if (s.headdim * s.dstate > 16384 || s.headdim % 4 != 0 || s.dstate % 4 != 0) return SSD_ERR_UNSUPPORTED;
         if (cls::ssd_f32_lds_bytes(int(s.headdim), int(s.dstate)) > 160 * 1024) return SSD_ERR_UNSUPPORTED;
     } else {
-        // the per-(batch, head) kernel's tiles must fit LDS, unless the fused
-        // path takes the shape (it runs chunks over 128 tokens as sub-chunks)
-        const int TT = cls::bf16_tile_tokens(int(s.chunk));
-        if (!cls::ssd_bf16_supported(TT, int(s.headdim), int(s.dstate)) &&
+        if (cls::chunk_kernel_tile(s.chunk, int(s.headdim), int(s.dstate)) == 0 &&
             !cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk, s.dtype)
                  .use)
             return SSD_ERR_UNSUPPORTED;
-        if (s.batch * nchunks(s) * s.ngroups > (int64_t(1) << 31)) return SSD_ERR_SHAPE;
+        // (batch, sub-chunk, group) blocks of either path, sub-chunks of at least 16 tokens
+        if (s.batch * ((s.seqlen + 15) / 16) * s.ngroups > (int64_t(1) << 31)) return SSD_ERR_SHAPE;
     }
     return SSD_OK;
 }
@@ -295,8 +325,7 @@ extern "C" size_t cls_ssd_workspace_bytes(const SsdShape& s) {
         }
         return bytes;
     }
-    const int64_t TT = cls::bf16_tile_tokens(int(s.chunk));
-    return size_t(s.batch) * size_t(nchunks(s)) * size_t(s.ngroups) * size_t(TT * TT) * 2 + cls::kSsdWsHeader;
+    return chunk_kernel_ws_bytes(s);
 }
 
 extern "C" size_t cls_ssd_plan_bytes(const SsdShape& s, const SsdLaunchOpts& o) {
@@ -304,11 +333,9 @@ extern "C" size_t cls_ssd_plan_bytes(const SsdShape& s, const SsdLaunchOpts& o) 
     const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
                                                      s.ngroups, s.chunk, s.dtype, o.force, o.path, o.s3, o.xcds);
     if (pl.use) return pl.bytes;
-    const int64_t TT = cls::bf16_tile_tokens(int(s.chunk));
-    // 0: the plan keeps the fused path out and the per-(batch, head) kernel's
-    // tiles do not fit LDS
-    if (!cls::ssd_bf16_supported(int(TT), int(s.headdim), int(s.dstate))) return 0;
-    return size_t(s.batch) * size_t(nchunks(s)) * size_t(s.ngroups) * size_t(TT * TT) * 2 + cls::kSsdWsHeader;
+    // 0: the plan keeps the fused path out and the per-(batch, head) kernel
+    // has no tile for the shape
+    return chunk_kernel_ws_bytes(s);
 }
 
 static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const SsdLaunchOpts& o, hipStream_t stream) {
@@ -399,9 +426,12 @@ static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const SsdLaunchO
         if (st == -8) return SSD_ERR_UNSUPPORTED;
         return st == 0 ? SSD_OK : SSD_ERR_HIP;
     }
-    const int TT = cls::bf16_tile_tokens(int(s.chunk));
+    const ChunkTile t = chunk_kernel_plan(s);
+    if (t.TT == 0) return SSD_ERR_UNSUPPORTED;
+    p.chunk = t.chunk;
+    p.nchunks = int(t.nchunks);
     ev_pre();
-    const int st = cls::ssd_bf16_launch(TT, int(s.headdim), int(s.dstate), p, stream);
+    const int st = cls::ssd_bf16_launch(t.TT, int(s.headdim), int(s.dstate), p, stream);
     ev_post();
     if (st == -8) return SSD_ERR_UNSUPPORTED;
     return st == 0 ? SSD_OK : SSD_ERR_HIP;

@@ -125,6 +125,8 @@ constexpr bool ssd_bf16_lds_fits(int TT, int P, int S) {
 }
 
 bool ssd_bf16_supported(int TT, int P, int S);
+constexpr int kChunkMaxTile = 128;  // longest sub-chunk of the per-(batch, head) kernel
+int chunk_kernel_tile(int64_t chunk, int P, int S);
 
 size_t ssd_fused_lds_bytes(int TT, int S);
 int ssd_fused_state_floats(int S);  // floats of one [64, S] state

@@ -74,12 +74,14 @@ enum { SSD_F32 = 0, SSD_BF16 = 1, SSD_F16 = 2 };
  * the kernels rely on that to never keep a positive exponent.
  *
  * SSD_BF16 runs the MFMA path (bf16 operands, fp32 accumulation and fp32
- * state).  Head dim 64 or 128 with dstate 64 or 128 runs the fused kernels
- * at every chunk length (a head of dim 128 as two heads of dim 64, whose
- * channels are independent); the other shapes with headdim in
- * {16, 32, 64, 128} and dstate in {32, 64, 128, 256} run the per-(batch,
- * head) kernel where the chunk's tiles fit the 160 KB of LDS
- * (SSD_ERR_UNSUPPORTED otherwise; ssd_fwd_workspace_size returns 0 then).
+ * state) for headdim in {16, 32, 64, 128} and dstate in {32, 64, 128, 256},
+ * at every chunk length (SSD_ERR_UNSUPPORTED otherwise;
+ * ssd_fwd_workspace_size returns 0 then).  Head dim 64 or 128 with dstate 64
+ * or 128 runs the fused kernels (a head of dim 128 as two heads of dim 64,
+ * whose channels are independent); the other shapes run the per-(batch,
+ * head) kernel.  Both run a chunk longer than their tiles (128 tokens, or
+ * less where the per-(batch, head) kernel's tiles would overflow LDS) as
+ * sub-chunks, which changes the result only by rounding.
  * SSD_F32 runs an fp32 path for any shape with headdim * dstate <= 16384 and
  * headdim, dstate multiples of 4.
  *

@@ -24,8 +24,7 @@ extern "C" {
 /* Kernel choice of one call. */
 enum {
     SSD_PATH_AUTO = 0,   /* what ssd_fwd would run                                 */
-    SSD_PATH_CHUNK = 1,  /* the per-(batch, head) chunk kernel (bf16 shapes whose
-                            chunk tiles fit LDS; SSD_ERR_UNSUPPORTED otherwise)    */
+    SSD_PATH_CHUNK = 1,  /* the per-(batch, head) chunk kernel (any bf16 shape)    */
     SSD_PATH_FUSED = 2   /* the fused kernels, head dim 64 or 128 (falls back to
                             AUTO where they do not apply)                          */
 };

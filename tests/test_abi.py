@@ -133,27 +133,35 @@ def test_ssd_workspace_size_zero_for_invalid_shapes():
 
 def test_head_dim_128_takes_the_fused_path():
     """Head dim 128 with dstate 64 or 128 runs the fused kernels (a head as
-    two chains of head dim 64), so every chunk length is supported; where the
-    per-(batch, head) kernel's 256-token tiles do not fit LDS, a plan that
-    forces that kernel is rejected before anything runs."""
-    lib = cls.load_library()
+    two chains of head dim 64) at every chunk length."""
     for S in (64, 128):
         for chunk in (16, 32, 64, 128, 256):
-            assert lib.ssd_fwd_workspace_size(2, 1000, 4, 128, S, 2, chunk, cls.SSD_BF16) > 0
             p = cls.ssd_fwd_plan(2, 1000, 4, 128, S, 2, chunk)
             assert p["source"] == "heuristic" and p["nsegs"] >= 1
-    shape = (2, 1000, 4, 128, 128, 2, 256, cls.SSD_BF16)
-    chunk_path = cls.plan_request(path="chunk")
-    assert lib.ssd_fwd_planned_workspace_size(*shape, ctypes.byref(chunk_path)) == 0
-    st = lib.ssd_fwd_planned(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, *shape, FAKE, None, FAKE, 1 << 34, None,
-                             ctypes.byref(chunk_path), None)
-    assert st == -8
-    # the per-(batch, head) kernel still runs head dim 128 where its tiles fit
-    assert lib.ssd_fwd_planned_workspace_size(2, 1000, 4, 128, 128, 2, 128, cls.SSD_BF16,
-                                              ctypes.byref(chunk_path)) > 0
-    # outside the fused set (dstate 256) the 256-token tiles do not fit
-    assert lib.ssd_fwd_workspace_size(2, 1000, 4, 128, 256, 2, 256, cls.SSD_BF16) == 0
     assert cls.ssd_fwd_plan(2, 1000, 4, 128, 256, 2, 64)["source"] == "none"
+
+
+def test_every_head_dim_and_state_size_of_the_set_is_supported():
+    """bf16: every head dim in {16, 32, 64, 128} and state size in {32, 64,
+    128, 256} runs at every chunk length, on the fused kernels or on the
+    per-(batch, head) kernel (which runs a chunk whose tiles would overflow LDS
+    as sub-chunks); a forced per-(batch, head) plan runs too.  Outside the set
+    the shape is rejected before anything runs."""
+    lib = cls.load_library()
+    chunk_path = cls.plan_request(path="chunk")
+    for P in (16, 32, 64, 128):
+        for S in (32, 64, 128, 256):
+            for chunk in (16, 32, 64, 128, 256):
+                shape = (2, 1000, 4, P, S, 2, chunk, cls.SSD_BF16)
+                assert lib.ssd_fwd_workspace_size(*shape) > 0, shape
+                assert lib.ssd_fwd_planned_workspace_size(*shape, ctypes.byref(chunk_path)) > 0, shape
+    for P, S in ((48, 64), (64, 96), (256, 64)):
+        shape = (2, 1000, 4, P, S, 2, 64, cls.SSD_BF16)
+        assert lib.ssd_fwd_workspace_size(*shape) == 0
+        assert lib.ssd_fwd_planned_workspace_size(*shape, ctypes.byref(chunk_path)) == 0
+        st = lib.ssd_fwd_planned(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, *shape, FAKE, None, FAKE, 1 << 34, None,
+                                 ctypes.byref(chunk_path), None)
+        assert st == -8
 
 
 def test_ssd_step_rejects_bad_arguments():

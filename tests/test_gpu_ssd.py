@@ -371,15 +371,14 @@ def test_head_dim_128_equals_two_heads_of_64(plan):
     parity.check_ssd(w, y_w, h_w, 128, f"P=128 {plan}")
 
 
-def test_head_dim_128_chunk_kernel_where_it_fits():
-    """The per-(batch, head) kernel still runs head dim 128 when forced at a
-    chunk whose tiles fit LDS; at 256 tokens with dstate 128 they do not, and
-    the forced plan is rejected before anything runs."""
-    inp = small_case(197, 2, 700, 4, 128, 128, 2, torch.bfloat16)
-    run_and_check(inp, 128, "P=128 chunk kernel forced", plan=cls.plan_request(path="chunk"))
-    with pytest.raises(cls.SSDError) as err:
-        gpu_run(inp, chunk=256, plan=cls.plan_request(path="chunk"))
-    assert err.value.status == -8
+@pytest.mark.parametrize("P,S,chunk", [(128, 128, 128), (128, 128, 256), (128, 256, 256), (64, 256, 256),
+                                     (16, 256, 128)])
+def test_chunk_kernel_sub_chunks(P, S, chunk):
+    """The per-(batch, head) kernel forced on shapes whose chunk tiles would
+    overflow LDS: it runs them as sub-chunks of 128 or 64 tokens (only the
+    rounding changes)."""
+    inp = small_case(197 + P + S + chunk, 2, 700, 4, P, S, 2, torch.bfloat16)
+    run_and_check(inp, chunk, f"chunk kernel forced P={P} S={S} chunk={chunk}", plan=cls.plan_request(path="chunk"))
 
 
 @pytest.mark.parametrize("A_value", [0.0, -1e-3])
