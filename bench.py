@@ -14,7 +14,9 @@ Timing protocol ("Selective-scan CUDA kernels", section "Results": median of
 bugs the tests caught": kernels too short for the GPU to boost):
 
 * every workload is warmed up with W steps and then until at least 50 ms of
-  its own GPU time has run;
+  its own GPU time has run, and each of its timed windows is preceded by
+  about 1 ms of its own untimed calls (the clocks settle after a
+  latency-bound workload such as the tiny fp32 one);
 * the K timed steps of the headline run as 15 windows, each bracketed by HIP
   events on the launch stream; the other workloads (the small- and
   large-model layer shapes, the large layer in heads of dim 128, the large
@@ -67,6 +69,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 METRIC = "SSD fwd tokens/sec (B·L) + % of HBM/MFMA roofline; linear-scan GB/s"
 NWIN = 15                      # timed windows per workload
 MIN_WINDOW_S = 5e-3            # each window of a side workload lasts at least this long
+LEAD_S = 1e-3                  # untimed calls of a workload right before each of its windows
 WARM_S = 50e-3                 # GPU time each workload runs before its first window
 
 
@@ -120,8 +123,8 @@ def source_digest(names, read=None):
 
 
 SSD_SOURCES = ["ssd_fused.hpp", "ssd_fused.hip", "common.hpp", "ssd_kernels.hpp", "ssd_dispatch.cpp"]
-# the per-(batch, head) kernel at 256-token chunks (the CB pass and the chunk kernel)
-CHUNK_SOURCES = ["ssd_bf16.hpp", "ssd_bf16_t256.hip", "common.hpp", "ssd_kernels.hpp", "ssd_dispatch.cpp"]
+# the per-(batch, head) kernel at 128-token sub-chunks (the CB pass and the chunk kernel)
+CHUNK_SOURCES = ["ssd_bf16.hpp", "ssd_bf16_t128.hip", "common.hpp", "ssd_kernels.hpp", "ssd_dispatch.cpp"]
 SCAN_SOURCES = ["linear_scan.hip", "common.hpp"]
 STEP_SOURCES = ["ssd_step.hip", "common.hpp"]
 
@@ -447,14 +450,17 @@ def split_steps(k, nwin):
     return [base + (1 if w < extra else 0) for w in range(nwin)]
 
 
-def timed_windows(runners, plan):
+def timed_windows(runners, plan, lead=None):
     """Interleaved windows: window w of every runner before window w + 1 of
-    any.  plan[name] = steps per window (list of NWIN).  Returns per runner the
-    seconds of each window."""
+    any.  plan[name] = steps per window (list of NWIN); lead[name] = untimed
+    steps right before each of its windows (the clocks settle on this
+    workload after the one before it).  Returns per runner the seconds of
+    each window."""
     import torch
     stream = torch.cuda.current_stream()
     out = {r.name: [] for r in runners}
     offs = {r.name: 0 for r in runners}
+    lead = lead or {}
     torch.cuda.synchronize()
     for w in range(NWIN):
         for r in runners:
@@ -462,6 +468,9 @@ def timed_windows(runners, plan):
             if n == 0:
                 out[r.name].append(0.0)
                 continue
+            for i in range(lead.get(r.name, 0)):
+                r.step(offs[r.name] + i)
+            offs[r.name] += lead.get(r.name, 0)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record(stream)
             for i in range(n):
@@ -795,8 +804,8 @@ def main():
     side = []
     if not args.only_headline:
         if not args.no_side_ssd:
-            for name, path in (("ssd_large", "auto"), ("ssd_small", "auto"), ("ssd_tiny", "auto"),
-                               ("ssd_large_p128", "auto"), ("ssd_large", "chunk")):
+            for name, path in (("ssd_large", "auto"), ("ssd_large_p128", "auto"), ("ssd_small", "auto"),
+                               ("ssd_large", "chunk"), ("ssd_tiny", "auto")):
                 if (name, path) != (args.workload, args.path):
                     side.append(SsdRunner(name, path))
         side += [ScanRunner("scan"), ScanRunner("scan_ragged"), ScanRunner("scan", "bf16", "f32"),
@@ -805,16 +814,18 @@ def main():
                  StreamRunner("scan", 4, True), StreamRunner("scan", 2, False), StepRunner("decode_large")]
     runners = [head] + side
     plan = {head.name: split_steps(args.steps, NWIN)}
+    lead = {}
     warm_s = {}
     for r in runners:
         warm_s[r.name], est = warm(r, args.warmup)
+        lead[r.name] = max(1, min(200, math.ceil(LEAD_S / max(est, 1e-7))))
         if r is not head:
             n = max(1, min(2000, math.ceil(MIN_WINDOW_S / max(est, 1e-7))))
             plan[r.name] = [n] * NWIN
         log(f"warmed {r.name}: {warm_s[r.name] * 1e3:.1f} ms, ~{est * 1e6:.1f} us/step")
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    win = timed_windows(runners, plan)
+    win = timed_windows(runners, plan, lead)
     t_wall = time.perf_counter() - t_wall
     stats = {r.name: summarize(win[r.name], plan[r.name]) for r in runners}
     clocks_after = None if args.no_clocks else gpu_state()
@@ -838,7 +849,8 @@ def main():
         "data": "synthetic (seeded; shapes and value distributions of the named workload)",
         "config": {"workload": head.describe(), "global_batch": head.shape.batch, "seq_len": head.shape.seqlen,
                    "parallelism": "single GPU", "buffer_sets": head.nsets},
-        "timing": dict(res["timing"], warmup_gpu_ms=round(warm_s[head.name] * 1e3, 1)),
+        "timing": dict(res["timing"], warmup_gpu_ms=round(warm_s[head.name] * 1e3, 1),
+                       untimed_lead_steps_per_window=lead[head.name]),
         "roofline": res["roofline"],
         "clocks": {"before": clocks_before, "after": clocks_after},
     }
@@ -852,6 +864,7 @@ def main():
             o = step_result(r, st, plan[r.name])
         else:
             o = scan_result(r, st, plan[r.name])
+        o["timing"]["untimed_lead_steps_per_window"] = lead[r.name]
         others[r.name] = o
     if others:
         line["workloads"] = {k: v for k, v in others.items() if k.startswith("ssd_") and k != "decode_large"}
