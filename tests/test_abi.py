@@ -155,6 +155,12 @@ def test_every_head_dim_and_state_size_of_the_set_is_supported():
                 shape = (2, 1000, 4, P, S, 2, chunk, cls.SSD_BF16)
                 assert lib.ssd_fwd_workspace_size(*shape) > 0, shape
                 assert lib.ssd_fwd_planned_workspace_size(*shape, ctypes.byref(chunk_path)) > 0, shape
+    # the per-(batch, head) kernel's workspace is C B^T per (batch, sub-chunk,
+    # group): 256-token chunks run as 128-token sub-chunks, and as 64-token
+    # ones where the 128-token tiles overflow LDS (P = 128, S = 256)
+    assert lib.ssd_fwd_workspace_size(2, 1000, 4, 32, 64, 2, 256, cls.SSD_BF16) == 2 * 8 * 2 * 128 * 128 * 2 + 1024
+    assert lib.ssd_fwd_workspace_size(2, 1000, 4, 128, 256, 2, 256, cls.SSD_BF16) == 2 * 16 * 2 * 64 * 64 * 2 + 1024
+    assert lib.ssd_fwd_workspace_size(2, 1000, 4, 16, 32, 2, 16, cls.SSD_BF16) == 2 * 63 * 2 * 32 * 32 * 2 + 1024
     for P, S in ((48, 64), (64, 96), (256, 64)):
         shape = (2, 1000, 4, P, S, 2, 64, cls.SSD_BF16)
         assert lib.ssd_fwd_workspace_size(*shape) == 0

@@ -71,10 +71,13 @@ def test_fp32_chunk_sizes_and_ragged(chunk):
 
 
 @pytest.mark.parametrize("chunk", [16, 32, 64, 128, 256])
-@pytest.mark.parametrize("P,S", [(16, 32), (64, 128), (32, 64), (128, 64), (64, 64), (128, 128), (32, 256)])
+@pytest.mark.parametrize("P", [16, 32, 64, 128])
+@pytest.mark.parametrize("S", [32, 64, 128, 256])
 def test_bf16_shapes_chunks_ragged(P, S, chunk):
-    if not cls.load_library().ssd_fwd_workspace_size(2, 301, 4, P, S, 2, chunk, cls.SSD_BF16):
-        pytest.skip("shape not supported by the bf16 kernels at this chunk")
+    """Every head dim and state size of the bf16 set at every chunk length, on
+    a ragged length (fused kernels for P in {64, 128} with S in {64, 128}, the
+    per-(batch, head) kernel otherwise)."""
+    assert cls.load_library().ssd_fwd_workspace_size(2, 301, 4, P, S, 2, chunk, cls.SSD_BF16) > 0
     inp = small_case(2, 2, 301, 4, P, S, 2, torch.bfloat16)
     y, _ = run_and_check(inp, chunk, f"bf16 P={P} S={S} chunk={chunk}")
 
