@@ -14,6 +14,8 @@ Workloads (synthetic; each is named by what it is and its sizes):
   bf16, slower decay (dt shift -4) and a nonzero initial state ~ N(0, 0.1^2)
 * ``ssd_large_p128`` the large layer's 5120 inner channels as heads of dim 128:
   batch 4, L=8192, 40 heads, P=128, S=128, 1 group, chunk 256, bf16
+* ``ssd_context_512k`` a half-million-token context: batch 1, L=524288, 8 heads,
+  P=64, S=128, 2 groups, chunk 128, bf16, dt shift -4, h0 ~ N(0, 0.1^2)
 * ``decode_large`` one decode token (``ssd_step``) for 64 sequences of the
   large-model layer's heads: batch 64, 80 heads, P=64, S=128, 1 group, bf16,
   state ~ N(0, 0.5^2)
@@ -58,6 +60,8 @@ SSD_WORKLOADS = {
     "ssd_long": (SSDShape(1, 65536, 64, 64, 128, 8, 128, "bf16", dt_shift=-4.0, h0_std=0.1), 4),
     # the large layer's inner width (40 x 128 = 80 x 64 channels) in heads of dim 128
     "ssd_large_p128": (SSDShape(4, 8192, 40, 128, 128, 1, 256, "bf16"), 5),
+    # a half-million-token context (4096 chunks per chain, chains cut into many segments)
+    "ssd_context_512k": (SSDShape(1, 524288, 8, 64, 128, 2, 128, "bf16", dt_shift=-4.0, h0_std=0.1), 6),
 }
 
 SCAN_WORKLOADS = {

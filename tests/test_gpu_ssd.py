@@ -280,6 +280,19 @@ def test_chain_mapping_over_xcds(xcds, s3):
     run_and_check(inp, 128, f"xcds={xcds} {s3}", plan=cls.plan_request(nsegs=3, nsplit=7, xcds=xcds, s3=s3))
 
 
+@pytest.mark.parametrize("plan", [None, dict(s3="lookback"), dict(nsegs=64, s3="lookback", stress_seed=11)],
+                         ids=["heuristic", "lookback", "lookback64-stress"])
+def test_half_million_token_context(plan):
+    """524288 tokens per sequence (4096 chunks): the heuristic cuts the 8
+    chains into 32 segments each; the look-back plans fold up to 63
+    predecessors.  Every output compared."""
+    print(f"[ssd] ssd_context_512k {plan}", flush=True)
+    inp = workloads.ssd_workload("ssd_context_512k")
+    y, hf = gpu_run(inp, plan=None if plan is None else cls.plan_request(**plan))
+    assert np.isfinite(y).all()
+    parity.check_ssd_workload("ssd_context_512k", y, hf, label=f"ssd_context_512k {plan}")
+
+
 def test_full_workload_on_the_chunk_kernel():
     """The large-model layer forced onto the per-(batch, head) kernel (the
     configuration the benchmark times for that kernel); every output
