@@ -96,6 +96,20 @@ def test_bf16_edge_lengths():
         run_and_check(inp, 256, f"bf16 L={L}")
 
 
+@pytest.mark.parametrize("P,S", [(32, 64), (16, 256), (128, 256)])
+def test_chunk_kernel_edge_lengths_and_optional_arguments(P, S):
+    """The per-(batch, head) kernel at lengths around its sub-chunk and block
+    boundaries (a 256-token chunk runs as 128- or 64-token sub-chunks), and
+    without D, h0 or the final state."""
+    for L in (1, 2, 31, 33, 63, 65, 127, 129, 255, 257, 385):
+        inp = small_case(7 + L + P, 1, L, 2, P, S, 1, torch.bfloat16)
+        run_and_check(inp, 256, f"chunk kernel P={P} S={S} L={L}")
+    inp = small_case(8 + P, 2, 300, 4, P, S, 2, torch.bfloat16, h0=False, D=False)
+    y, hf = gpu_run(inp, chunk=256, want_final=False)
+    assert hf is None
+    parity.check_ssd(inp, y, None, 256, f"chunk kernel P={P} S={S}: no D, no h0, no final state")
+
+
 @pytest.mark.parametrize("chunk", [32, 64, 128, 256])
 def test_whole_chains_many_chunks(chunk):
     """Every (batch, head) chain in one workgroup (one segment), so a
