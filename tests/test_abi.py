@@ -115,7 +115,10 @@ def test_ssd_rejects_bad_arguments():
     assert call(x=None) == -1
     assert call(y=None) == -1
     assert call(Bt=0) == -2
+    assert call(L=0) == -2  # an empty sequence is rejected, not run
     assert call(L=-5) == -2
+    assert call(H=0) == -2
+    assert call(P=0) == -2
     assert call(H=3, G=2) == -2
     assert call(dt=7) == -3
     assert call(T=48) == -4
