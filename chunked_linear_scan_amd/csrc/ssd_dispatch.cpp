@@ -116,7 +116,7 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     // chunk length).  A plan may ask for shorter sub-chunks (64 or 32 tokens).
     chunk = chunk > kFusedMaxChunk ? kFusedMaxChunk : chunk;
     // a head of dim 128 runs as two chains of head dim 64
-    const int64_t nchains = batch * H * (P == 128 ? 2 : 1);
+    const int64_t nchains = (batch * H) << fused_head_shift(P);
     // the segment plan: forced, else tuned for this shape, else the heuristic
     SegChoice ch{1, 0};
     bool heuristic = true;
@@ -270,8 +270,9 @@ extern "C" int cls_ssd_check(const SsdShape& s) {
             !cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate, s.ngroups, s.chunk, s.dtype)
                  .use)
             return SSD_ERR_UNSUPPORTED;
-        // (batch, sub-chunk, group) blocks of either path, sub-chunks of at least 16 tokens
-        if (s.batch * ((s.seqlen + 15) / 16) * s.ngroups > (int64_t(1) << 31)) return SSD_ERR_SHAPE;
+        // (batch, sub-chunk, group) blocks of either path, sub-chunks of at least
+        // 16 tokens: their count and the sub-chunk count stay below 2^31
+        if (s.batch * ((s.seqlen + 15) / 16) * s.ngroups >= (int64_t(1) << 31)) return SSD_ERR_SHAPE;
     }
     return SSD_OK;
 }
@@ -403,7 +404,7 @@ static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const SsdLaunchO
         f.err = reinterpret_cast<uint32_t*>(ws);
         f.batch = s.batch;
         f.L = s.seqlen;
-        f.hshift = s.headdim == 128 ? 1 : 0;
+        f.hshift = cls::fused_head_shift(s.headdim);
         f.H = int(s.nheads) << f.hshift;
         f.G = int(s.ngroups);
         f.chunk = p.chunk;

@@ -1,4 +1,4 @@
-// Launchers of the fused head-dim-64 SSD kernel (see ssd_fused.hpp) and of
+// Launchers of the fused SSD kernels (see ssd_fused.hpp) and of
 // the CB pass that precedes it.
 #include "device_once.hpp"
 #include "ssd_bf16.hpp"

@@ -88,6 +88,10 @@ struct SsdFusedParams {
     uint32_t stress;     // look-back stress seed (tests only; 0: none)
 };
 
+// A head of dim 64 << fused_head_shift(P) runs on the fused path as that
+// many adjacent chains of head dim 64 (P = 64 or 128).
+constexpr int fused_head_shift(int64_t P) { return P == 128 ? 1 : 0; }
+
 // Plan of the fused path (head dim 64, or 128 as two heads of 64) for one
 // shape (also sizes its workspace).
 constexpr int64_t kFusedMaxChunk = 128;  // longest quadratic block of the fused kernel
