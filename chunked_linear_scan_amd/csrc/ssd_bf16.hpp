@@ -200,8 +200,10 @@ __global__ __launch_bounds__(kChunkThreads) void ssd_chunk_kernel(SsdBf16Params 
     const int64_t b = bh / p.H;
     const int h = int(bh % p.H);
     const int g = h / (p.H / p.G);
-    const float A2 = p.A[h] * kLog2e;
-    const float Dh = p.D ? p.D[h] : 0.0f;
+    const int hin = h >> p.hshift;  // the input head (dt, A, D)
+    const int Hin = p.H >> p.hshift;
+    const float A2 = p.A[hin] * kLog2e;
+    const float Dh = p.D ? p.D[hin] : 0.0f;
     const int64_t L = p.L;
 
     // state h^T tiles owned by this wave: s-tiles st = wave + NW k, all p-tiles
@@ -228,7 +230,7 @@ __global__ __launch_bounds__(kChunkThreads) void ssd_chunk_kernel(SsdBf16Params 
 
     // dt of a chunk (one token per thread); X and B rows of transpose item q
     // (8 tokens x 8 channels, 8 rows of 16 bytes)
-    auto load_dt = [&](int64_t tok0, int n) { return tid < n ? p.dt[(b * L + tok0 + tid) * p.H + h] : 0.0f; };
+    auto load_dt = [&](int64_t tok0, int n) { return tid < n ? p.dt[(b * L + tok0 + tid) * Hin + hin] : 0.0f; };
     auto x_row = [&](int64_t tok0, int n, int q, int e) {
         const int t = 8 * (q / (P / 8)) + e;
         return (q < NXQ && t < n) ? ldg16(p.x + ((b * L + tok0 + t) * p.H + h) * P + 8 * (q % (P / 8)))

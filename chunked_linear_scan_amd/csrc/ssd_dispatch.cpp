@@ -24,6 +24,20 @@ bool ssd_bf16_supported(int TT, int P, int S) {
     return p_ok && s_ok && ssd_bf16_lds_fits(TT, P, S);
 }
 
+// The per-(batch, head) kernel's head split: a head of dim P runs as
+// 1 << split heads of dim P >> split (bit-identical results; every split
+// head recomputes the head's diagonal weights).  Head dim 128 halves (the
+// weights are shared by many columns; measured 2156 against 2425 us on a
+// 4 x 8192, 40-head, state-256 layer), and a grid of fewer than 128
+// workgroups splits further down to head dim 16 (32 heads of a 65536-token
+// sequence: 5739 against 7307 us).  Grids of 192 and more workgroups of head
+// dim 64 or less run unsplit: splitting them measured 19-100 % slower.
+int chunk_kernel_split(int64_t batch, int64_t H, int64_t P) {
+    int split = P == 128 ? 1 : 0;
+    while ((batch * H << split) < 128 && (P >> split) > 16) ++split;
+    return split;
+}
+
 // The per-(batch, head) kernel's tile: the chunk (at least 32 tokens), run as
 // sub-chunks of at most kChunkMaxTile tokens and halved until its LDS fits.
 // Sub-chunks change the result only by rounding: the chunked form equals the
@@ -431,8 +445,10 @@ static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const SsdLaunchO
     if (t.TT == 0) return SSD_ERR_UNSUPPORTED;
     p.chunk = t.chunk;
     p.nchunks = int(t.nchunks);
+    p.hshift = cls::chunk_kernel_split(s.batch, s.nheads, s.headdim);
+    p.H = int(s.nheads) << p.hshift;
     ev_pre();
-    const int st = cls::ssd_bf16_launch(t.TT, int(s.headdim), int(s.dstate), p, stream);
+    const int st = cls::ssd_bf16_launch(t.TT, int(s.headdim) >> p.hshift, int(s.dstate), p, stream);
     ev_post();
     if (st == -8) return SSD_ERR_UNSUPPORTED;
     return st == 0 ? SSD_OK : SSD_ERR_HIP;

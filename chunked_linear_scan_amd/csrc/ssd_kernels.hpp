@@ -43,6 +43,11 @@ struct SsdBf16Params {
                          // past the sequence end, or null
     int64_t batch, L;
     int H, G, chunk, nchunks;
+    // per-(batch, head) kernel: H counts heads of dim P >> hshift; a head of
+    // dim P runs as 1 << hshift adjacent heads (its channels are independent,
+    // and x, y, h0 and h_final hold them at the same addresses), and head h
+    // reads dt, A and D of head h >> hshift
+    int hshift;
 };
 
 struct SsdFusedParams {

@@ -401,6 +401,27 @@ def test_head_dim_128_equals_two_heads_of_64(plan):
     parity.check_ssd(w, y_w, h_w, 128, f"P=128 {plan}")
 
 
+@pytest.mark.parametrize("P,S,Bt,H,narrow", [(128, 32, 2, 6, 64), (64, 256, 1, 4, 16)])
+def test_chunk_kernel_head_split_equals_narrow_heads(P, S, Bt, H, narrow):
+    """The per-(batch, head) kernel runs a head of dim 128, and the heads of a
+    grid under 128 workgroups, as several narrower heads that share the head's
+    dt, A and D.  Bit for bit, that is what narrower heads carrying the head's
+    column blocks and its dt, A and D give (the same sub-chunk tile)."""
+    k = P // narrow
+    L, G, chunk = 64 * 12 + 5, 2 if H % 2 == 0 else 1, 128
+    print(f"[ssd split] P={P} S={S} H={H} -> {k} x {narrow}", flush=True)
+    w = small_case(200 + P + S, Bt, L, H, P, S, G, torch.bfloat16, dt_shift=-3.0)
+    n = {"x": w["x"].reshape(Bt, L, k * H, narrow), "dt": w["dt"].repeat_interleave(k, dim=-1).contiguous(),
+         "A": w["A"].repeat_interleave(k), "B": w["B"], "C": w["C"], "D": w["D"].repeat_interleave(k),
+         "h0": w["h0"].reshape(Bt, k * H, narrow, S), "chunk": 32}
+    req = cls.plan_request(path="chunk")
+    y_w, h_w = gpu_run(w, chunk=chunk, plan=req)
+    y_n, h_n = gpu_run(n, chunk=chunk, plan=req)
+    assert np.array_equal(y_w.reshape(y_n.shape).view(np.uint32), y_n.view(np.uint32))
+    assert np.array_equal(h_w.reshape(h_n.shape).view(np.uint32), h_n.view(np.uint32))
+    parity.check_ssd(w, y_w, h_w, chunk, f"split P={P} S={S}")
+
+
 @pytest.mark.parametrize("P,S,chunk", [(128, 128, 128), (128, 128, 256), (128, 256, 256), (64, 256, 256),
                                      (16, 256, 128)])
 def test_chunk_kernel_sub_chunks(P, S, chunk):
