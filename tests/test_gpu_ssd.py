@@ -468,6 +468,29 @@ def test_explicit_workspace_error_word_stays_zero():
     assert cls.workspace_errors([ws]) == 0
 
 
+def test_binding_rejects_bad_tensors_before_any_launch():
+    """The binding checks device, dtype, shape and layout of every tensor
+    before the library is called."""
+    inp = to_dev(small_case(3, 1, 64, 2, 64, 128, 1, torch.bfloat16))
+    args = [inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], inp["h0"]]
+    bad = []
+    a = list(args); a[0] = inp["x"].transpose(1, 2)  # non-contiguous x
+    bad.append((a, ValueError))
+    a = list(args); a[1] = inp["dt"].to(torch.float16)  # wrong dt dtype
+    bad.append((a, TypeError))
+    a = list(args); a[4] = inp["C"][:, :32]  # C of another length
+    bad.append((a, ValueError))
+    a = list(args); a[2] = inp["A"].cpu()  # A on the host
+    bad.append((a, ValueError))
+    a = list(args); a[3] = inp["B"].float()  # B and x of different dtypes
+    bad.append((a, TypeError))
+    for a, err in bad:
+        with pytest.raises(err):
+            cls.ssd_fwd(*a, chunk=32)
+    with pytest.raises(ValueError):
+        cls.linear_scan(torch.ones(4, 100, device="cuda").t(), torch.ones(100, 4, device="cuda"))
+
+
 def test_planned_call_rejects_bad_plans():
     inp = small_case(3, 1, 64, 2, 64, 128, 1, torch.bfloat16)
     d = to_dev(inp)
