@@ -127,8 +127,9 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cb_kernel(SsdBf16Params p) {
 // S1, S2b, S2c, S3, S4 for one (batch, head): chunks in order, state in
 // registers (fp32) and in LDS as the bf16 MFMA operand.
 //
-// One workgroup of four waves per (batch, head); chunks over 128 tokens run as
-// 128-token sub-chunks (or shorter, until the tiles fit LDS).  Where LDS
+// One workgroup of four waves per (batch, head), or per (batch, column block
+// of a head) where heads are split (SsdBf16Params.hshift); chunks over 128
+// tokens run as 128-token sub-chunks (or shorter, until the tiles fit LDS).  Where LDS
 // allows few workgroups per CU, each output tile issues all of its C and
 // C B^T loads before its first product and chunk c + 1's dt, X and B rows
 // are loaded while chunk c computes.  The barriers order LDS only

@@ -35,6 +35,8 @@ bool ssd_bf16_supported(int TT, int P, int S) {
 int chunk_kernel_split(int64_t batch, int64_t H, int64_t P) {
     int split = P == 128 ? 1 : 0;
     while ((batch * H << split) < 128 && (P >> split) > 16) ++split;
+    // the grid (batch * H << split workgroups) and the head count stay in 31 bits
+    while (split > 0 && (batch * H << split) >= (int64_t(1) << 31)) --split;
     return split;
 }
 
