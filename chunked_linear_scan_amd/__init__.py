@@ -33,7 +33,8 @@ class PlanRequest(ctypes.Structure):
     """``ssd_plan_request`` of include/chunked_linear_scan_testing.h."""
     _fields_ = [("path", ctypes.c_int32), ("s3", ctypes.c_int32), ("nsegs", ctypes.c_int64),
                 ("nsplit", ctypes.c_int64), ("agg_pieces", ctypes.c_int64), ("xcds", ctypes.c_int32),
-                ("sub_chunk", ctypes.c_int32), ("stress_seed", ctypes.c_uint32), ("cache_policy", ctypes.c_int32)]
+                ("sub_chunk", ctypes.c_int32), ("stress_seed", ctypes.c_uint32), ("cache_policy", ctypes.c_int32),
+                ("c_source", ctypes.c_int32)]
 
 
 PATH = {"auto": 0, "chunk": 1, "fused": 2}
@@ -41,6 +42,7 @@ S3 = {"auto": 0, "reduce": 1, "lookback": 2}
 _S3_NAME = {0: None, 1: "reduce", 2: "lookback"}
 CACHE = {"auto": 0, "default": 1, "nontemporal": 2}
 _CACHE_NAME = {0: None, 1: "default", 2: "nontemporal"}
+CSRC = {"auto": 0, "copy": 1, "rows": 2}  # where the fused state term reads C
 
 
 class SSDError(RuntimeError):
@@ -345,10 +347,11 @@ def ssd_fwd(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, want_final_state:
 
 
 def plan_request(path="auto", s3="auto", nsegs=0, nsplit=0, agg_pieces=0, xcds=0, sub_chunk=0,
-                 stress_seed=0, cache_policy="auto") -> PlanRequest:
+                 stress_seed=0, cache_policy="auto", c_source="auto") -> PlanRequest:
     """An explicit plan for ``ssd_fwd_planned`` (see the testing header)."""
     return PlanRequest(PATH[path], S3[s3 or "auto"], int(nsegs), int(nsplit), int(agg_pieces), int(xcds),
-                       int(sub_chunk), int(stress_seed), CACHE[cache_policy or "auto"])
+                       int(sub_chunk), int(stress_seed), CACHE[cache_policy or "auto"],
+                       CSRC[c_source or "auto"])
 
 
 def ssd_fwd_planned(x, dt, A, B, C, D=None, h0=None, chunk: int = 256, plan: PlanRequest | None = None,

@@ -294,11 +294,13 @@ static bool plan_options(const ssd_plan_request* plan, cls::SegChoice* seg, SsdL
     if (plan->xcds < 0 || plan->xcds > 64) return false;
     if (plan->sub_chunk != 0 && plan->sub_chunk != 32 && plan->sub_chunk != 64) return false;
     if (plan->cache_policy < 0 || plan->cache_policy > 2) return false;
+    if (plan->c_source < SSD_CSRC_AUTO || plan->c_source > SSD_CSRC_ROWS) return false;
     o->path = plan->path;
     o->s3 = plan->s3;
     o->xcds = plan->xcds;
     o->stress = plan->stress_seed;
     o->policy = plan->cache_policy;
+    o->csrc = plan->c_source;
     if (plan->nsegs > 0) {
         *seg = cls::SegChoice{plan->nsegs, plan->nsplit, plan->agg_pieces};
         seg->s3 = plan->s3;

@@ -33,6 +33,7 @@ struct SsdLaunchOpts {
     hipEvent_t* ev = nullptr;              // four events to record, or null
     uint32_t stress = 0;                   // look-back stress seed of the segment look-back (0: none)
     int policy = 0;                        // x/y cache policy: 0 the plan's, 1 default, 2 non-temporal
+    int csrc = 0;                          // C source of the state term: 0 the plan's, 1 copy, 2 C rows
 };
 
 struct SsdArgs {

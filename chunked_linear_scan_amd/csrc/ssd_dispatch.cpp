@@ -96,7 +96,7 @@ bool tuned_choice(const TuneKey& k, SegChoice* out) {
 // segments.  Plans of more than four rounds of workgroups are left out.
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
                             int64_t chunk, int dtype, const SegChoice* force, int path, int s3, int xcds,
-                            int policy = 0);
+                            int policy = 0, int csrc = 0);
 
 // Passed as `force`: the built-in heuristic, ignoring any tuned plan (the
 // autotuner's incumbent).
@@ -122,9 +122,11 @@ std::vector<SegChoice> seg_candidates(int64_t nchains, int64_t nc, int64_t slots
 // force: null (a tuned choice for this shape, else the heuristic), or the
 // segment plan to use.  path: SSD_PATH_* of the call (SSD_PATH_CHUNK keeps
 // the fused path out).  policy: the call's x/y cache policy (0: the plan's).
+// csrc: where the state term reads C (0: the heuristic's choice, 1: the CB
+// pass's copy, 2: the C rows).
 SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int64_t S, int64_t G,
                             int64_t chunk, int dtype, const SegChoice* force, int path, int s3, int xcds,
-                            int policy) {
+                            int policy, int csrc) {
     SsdFusedPlan pl{};
     // The kernel's quadratic block is at most 128 tokens: a longer chunk is run
     // as sub-chunks of 128 with the state passed between them, which changes the
@@ -200,6 +202,13 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     const int64_t run = (nchains - nsplit) > 0 ? nc : k;  // longest walk of a workgroup
     const int want_nt = policy > 0 ? policy : (!heuristic && ch.nt > 0 ? ch.nt : (run >= 32 ? 2 : 1));
     pl.nt = want_nt == 2 && TT == 128;
+    // The state term's C operand: the CB pass's fragment-major copy (one write
+    // and one read of C per group), or the C rows read by every head's state
+    // loaders (16 rows of 64 bytes per load instead of 1 KB in lane order, more
+    // work for the texture path).  Measured on one MI355X: with 8 chains per
+    // group the rows are 1.4 % faster per call, with 24 the two are even, with
+    // 80 the copy is 4 % faster.
+    pl.cdirect = csrc > 0 ? csrc == 2 : nchains <= 8 * batch * G;
     const int64_t npieces = pl.lookback ? 0 : nsplit * (nsegs - 1) * agg_d;
     if (ntiles >= (int64_t(1) << 24)) {
         pl.use = false;
@@ -228,7 +237,7 @@ SsdFusedPlan ssd_fused_plan(int64_t batch, int64_t L, int64_t H, int64_t P, int6
     pl.cb_off = pl.alpha_off + up(nseg * 4);
     pl.bt_off = pl.cb_off + up(size_t(batch) * size_t(nc) * size_t(G) * size_t(TT) * TT * 2);
     pl.cf_off = pl.bt_off + up(size_t(batch) * size_t(nc) * size_t(G) * size_t(S) * TT * 2);
-    pl.dtt_off = pl.cf_off + up(size_t(batch) * size_t(nc) * size_t(G) * size_t(S) * TT * 2);
+    pl.dtt_off = pl.cf_off + (pl.cdirect ? 0 : up(size_t(batch) * size_t(nc) * size_t(G) * size_t(S) * TT * 2));
     pl.bytes = pl.dtt_off + size_t(batch) * size_t(nc) * size_t(H) * TT * 4;
     return pl;
 }
@@ -348,7 +357,8 @@ extern "C" size_t cls_ssd_workspace_bytes(const SsdShape& s) {
 extern "C" size_t cls_ssd_plan_bytes(const SsdShape& s, const SsdLaunchOpts& o) {
     if (s.dtype == SSD_F32) return 0;
     const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
-                                                     s.ngroups, s.chunk, s.dtype, o.force, o.path, o.s3, o.xcds);
+                                                     s.ngroups, s.chunk, s.dtype, o.force, o.path, o.s3, o.xcds,
+                                                     o.policy, o.csrc);
     if (pl.use) return pl.bytes;
     // 0: the plan keeps the fused path out and the per-(batch, head) kernel
     // has no tile for the shape
@@ -393,14 +403,14 @@ static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const SsdLaunchO
     p.nchunks = int(nchunks(s));
     const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
                                                      s.ngroups, s.chunk, s.dtype, force, o.path, o.s3, o.xcds,
-                                                     o.policy);
+                                                     o.policy, o.csrc);
     if (pl.use) {
         p.chunk = pl.chunk;
         p.nchunks = int((s.seqlen + pl.chunk - 1) / pl.chunk);
         char* ws = static_cast<char*>(a.workspace);
         p.cb = reinterpret_cast<uint16_t*>(ws + pl.cb_off);
         p.bt = reinterpret_cast<uint16_t*>(ws + pl.bt_off);
-        p.cf = reinterpret_cast<uint16_t*>(ws + pl.cf_off);
+        p.cf = pl.cdirect ? nullptr : reinterpret_cast<uint16_t*>(ws + pl.cf_off);
         p.dtt = reinterpret_cast<float*>(ws + pl.dtt_off);
         cls::SsdFusedParams f{};
         f.x = p.x;

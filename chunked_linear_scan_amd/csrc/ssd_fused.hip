@@ -10,7 +10,7 @@ namespace cls {
 // then one per (batch, chunk) that rewrites dt head-major (cbt_dt_transpose).
 // Writes CB[i][j] = sum_s C[i][s] B[j][s] for the 32-token blocks with
 // block(j) <= block(i) (the only ones the fused kernel reads), B^T[s][t], and
-// a copy of the chunk's C rows, all three fragment-major: the MFMA operand
+// (unless p.cf is null) a copy of the chunk's C rows, all three fragment-major: the MFMA operand
 // fragment (16-row tile m, 32-column block k) holds row 16 m + l of the
 // operand, columns 32 k + 8 g .. + 7, in lane l + 16 g, and is stored as 64
 // lanes x 16 bytes at fragment index m * (columns / 32) + k.  A wave of the
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cbt_kernel(SsdBf16Params p) {
         *reinterpret_cast<u32x4*>(sB + (q / CPR) * Lay::BP + 8 * (q % CPR)) = bq[k];
     }
     // the C fragments, as loaded (rows past the chunk's end are zeros)
-    if (has_tiles) {
+    if (has_tiles && p.cf) {
         uint16_t* cfo = p.cf + bcg * (int64_t(TT) * S);
 #pragma unroll
         for (int side = 0; side < 2; ++side) {

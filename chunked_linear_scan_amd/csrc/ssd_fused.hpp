@@ -650,18 +650,33 @@ __device__ __forceinline__ void ssd_fused_body(const SsdFusedParams& p) {
     // fragments loaded straight from global memory.  The loaders compute it
     // while the compute waves run the chunk's block loop; the compute waves add
     // it, decayed to each row, once their block loop is done.
-    // C fragments from the CB pass's fragment-major copy of the chunk's C rows
-    // (fragment (tile, 32-state step) = 64 lanes x 16 bytes; rows past a ragged
-    // end are zeros there)
+    // C fragments (fragment (tile, 32-state step): lane l16 + 16 kg holds row
+    // l16 of the tile, states 32 step + 8 kg ..), from the CB pass's
+    // fragment-major copy of the chunk's C rows (1 KB in lane order), or, when
+    // there is no copy (p.cf null), from the C rows themselves (16 rows of 64
+    // bytes) through a range that ends at the chunk's last real row.  Rows
+    // past a ragged end are zeros either way.  Byte offset of fragment (it2,
+    // ks): cf_lane + it2 * cf_it + ks * cf_ks.
+    const bool c_copy = p.cf != nullptr;
+    const uint32_t crow = uint32_t(p.G * S * 2);  // bytes between consecutive tokens of C
+    const uint32_t cf_lane = !lblk ? kNoRow
+                             : c_copy ? uint32_t((2 * lw * KS * 64 + lane) * 16)
+                                      : uint32_t(32 * lw + (lane & 15)) * crow + uint32_t((lane >> 4) * 16);
+    const uint32_t cf_it = c_copy ? uint32_t(KS * 1024) : 16 * crow;
+    const uint32_t cf_ks = c_copy ? 1024u : 64u;
     auto issue_cf = [&](int c) {
-        const auto rc = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint16_t*>(p.cf + (bcg0 + int64_t(c) * p.G) * (int64_t(TT) * S)), 0, TT * S * 2, 0x00020000);
+        const auto rc =
+            c_copy ? __builtin_amdgcn_make_buffer_rsrc(
+                         const_cast<uint16_t*>(p.cf + (bcg0 + int64_t(c) * p.G) * (int64_t(TT) * S)), 0, TT * S * 2,
+                         0x00020000)
+                   : __builtin_amdgcn_make_buffer_rsrc(
+                         const_cast<uint16_t*>(p.C + ((b * L + int64_t(c) * p.chunk) * p.G + g) * S), 0,
+                         int(uint32_t(chunk_rows(c)) * crow), 0x00020000);
 #pragma unroll
         for (int it2 = 0; it2 < 2; ++it2)
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
-                cfr[it2][ks] = __builtin_amdgcn_raw_buffer_load_b128(
-                    rc, lblk ? int((((2 * lw + it2) * KS + ks) * 64 + lane) * 16) : int(kNoRow), 0, 0);
+                cfr[it2][ks] = __builtin_amdgcn_raw_buffer_load_b128(rc, int(cf_lane + it2 * cf_it + ks * cf_ks), 0, 0);
     };
     // The outputs of a chunk, staged in LDS by the compute waves, are stored by
     // the loader waves during the next chunk, as whole 128-byte rows: 16-byte

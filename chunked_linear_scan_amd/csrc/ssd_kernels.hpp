@@ -114,6 +114,7 @@ struct SsdFusedPlan {
     int agg_d, agg_chunks, npieces;                     // aggregate pieces (see SsdFusedParams)
     bool lookback;                                      // split chains: single-pass look-back
     bool nt;                                            // non-temporal x loads and y stores
+    bool cdirect;                                       // state term reads the C rows (no C copy)
     int nranges;                                        // look-back claim ranges
     size_t payload_off, cb_off, bt_off, cf_off, dtt_off, bytes;
     size_t status_off, segpay_off, alpha_off;           // look-back status words and payloads

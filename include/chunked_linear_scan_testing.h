@@ -29,6 +29,18 @@ enum {
                             AUTO where they do not apply)                          */
 };
 
+/* Where the fused path's state term y = C h^T reads C ("Accelerating Mamba-2
+ * with high-performance forward pass kernels in NVIDIA cuTile", section
+ * "Kernel 3: compute_out").  The values are the same either way, and so is
+ * every bit of y and h_final. */
+enum {
+    SSD_CSRC_AUTO = 0,  /* the plan's choice: the C rows when a group has at most
+                           8 chains of head dim 64, else the copy              */
+    SSD_CSRC_COPY = 1,  /* a fragment-major copy of C that the CB pass writes
+                           into the workspace                                 */
+    SSD_CSRC_ROWS = 2   /* the C rows of the input (no copy in the workspace)  */
+};
+
 /* The inter-segment schemes (SSD_S3_AUTO, SSD_S3_REDUCE, SSD_S3_LOOKBACK) are
  * declared in chunked_linear_scan.h ("Selective-scan CUDA kernels", section
  * "The five kernels", levels 2 and 3). */
@@ -54,6 +66,7 @@ typedef struct {
                             kernels", section "Correctness")                      */
     int32_t cache_policy; /* SSD_CACHE_*: the x/y cache policy (128-token sub-chunks
                             only); 0: the plan's choice                            */
+    int32_t c_source;     /* SSD_CSRC_*: where the fused path's state term reads C */
 } ssd_plan_request;
 
 /*

@@ -128,6 +128,20 @@ def test_ssd_rejects_bad_arguments():
     assert call(P=24) in (-8, -2)
 
 
+def test_ssd_plan_request_c_source_is_validated():
+    """c_source takes SSD_CSRC_AUTO, _COPY or _ROWS; any other value is
+    refused before anything is sized or launched."""
+    lib = cls.load_library()
+    shape = (1, 1000, 8, 64, 128, 1, 128, cls.SSD_BF16)
+    base = lib.ssd_fwd_workspace_size(*shape)
+    for src in ("auto", "copy", "rows"):
+        assert lib.ssd_fwd_planned_workspace_size(*shape, ctypes.byref(cls.plan_request(c_source=src))) >= base > 0
+    for bad_value in (-1, 3):
+        bad = cls.plan_request()
+        bad.c_source = bad_value
+        assert lib.ssd_fwd_planned_workspace_size(*shape, ctypes.byref(bad)) == 0
+
+
 def test_ssd_workspace_size_zero_for_invalid_shapes():
     lib = cls.load_library()
     assert lib.ssd_fwd_workspace_size(1, 64, 3, 16, 32, 2, 32, 1) == 0

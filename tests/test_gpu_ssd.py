@@ -365,6 +365,32 @@ def test_cache_policies_give_the_same_bits(plan):
     parity.check_ssd(inp, y1, h1, 128, f"non-temporal {plan}")
 
 
+C_SOURCE_CASES = [
+    # (seed, Bt, L, H, P, S, G, chunk, plan)
+    (12, 2, 5000, 4, 64, 128, 2, 128, dict()),
+    (13, 2, 5000, 4, 64, 128, 2, 128, dict(nsegs=4, nsplit=3, s3="lookback")),
+    (14, 1, 3001, 6, 128, 64, 3, 64, dict(nsegs=3)),
+    (15, 2, 777, 8, 64, 64, 1, 32, dict(nsegs=2, agg_pieces=3)),
+    (16, 1, 2049, 16, 64, 128, 1, 256, dict(nsegs=3, sub_chunk=32)),
+]
+
+
+@pytest.mark.parametrize("case", C_SOURCE_CASES, ids=["heuristic", "lookback", "p128-sub64", "ragged-pieces",
+                                                      "sub32"])
+def test_c_sources_give_the_same_bits(case):
+    """The state term reads C from the CB pass's fragment-major copy or from
+    the C rows themselves: the same values in the same MFMA lanes, so y and
+    h_final are equal bit for bit, and both match the oracle."""
+    seed, Bt, L, H, P, S, G, chunk, plan = case
+    print(f"[ssd c-source] {case}", flush=True)
+    inp = small_case(seed, Bt, L, H, P, S, G, torch.bfloat16)
+    outs = {src: gpu_run(inp, chunk=chunk, plan=cls.plan_request(c_source=src, **plan)) for src in ("copy", "rows")}
+    (y0, h0), (y1, h1) = outs["copy"], outs["rows"]
+    assert np.array_equal(y0.view(np.uint32), y1.view(np.uint32))
+    assert np.array_equal(h0.view(np.uint32), h1.view(np.uint32))
+    parity.check_ssd(inp, y1, h1, chunk, f"C rows {case}")
+
+
 HEAD128_PLANS = [None, dict(nsegs=3, nsplit=3), dict(nsegs=4, nsplit=5, s3="lookback"),
                  dict(nsegs=2, s3="reduce", sub_chunk=64), dict(nsegs=3, nsplit=1, s3="lookback", cache_policy="nontemporal")]
 
