@@ -165,21 +165,17 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cbt_kernel(SsdBf16Params p) {
             }
         }
     }
-    // B^T from the staged rows: thread u transposes the 8 x 8 block (tokens
-    // 8 tg .., states 8 sg ..); its 8 rows are 8 consecutive lanes of one
-    // fragment, 128 contiguous bytes
+    // B^T from the staged rows, one whole fragment per wave and store (1 KB in
+    // lane order): fragment (16-state tile m, 32-token block k) gives lane
+    // l16 + 16 kg state 16 m + l16 of tokens 32 k + 8 kg .. + 7, gathered by two
+    // transposed LDS reads of 4 tokens each (lane l16 addresses token row
+    // l16 / 4, states 4 (l16 % 4) .. + 3 of the 4 x 16 block)
     uint16_t* bt = p.bt + bcg * (int64_t(S) * TT);
-    for (int u = tid; u < (TT / 8) * (S / 8); u += kBfThreads) {
-        const int tg = u % (TT / 8), sg = u / (TT / 8);
-        u32x4 rows[8], cols[8];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) rows[r] = *reinterpret_cast<const u32x4*>(sB + (8 * tg + r) * Lay::BP + 8 * sg);
-        transpose8x8_b16(rows, cols);
-#pragma unroll
-        for (int cc = 0; cc < 8; ++cc)
-            *reinterpret_cast<u32x4*>(bt +
-                                      (((sg >> 1) * NB + (tg >> 2)) * 64 + 8 * (sg & 1) + cc + 16 * (tg & 3)) * 8) =
-                cols[cc];
+    const unsigned char* sBb = reinterpret_cast<const unsigned char*>(sB);
+    for (int f = wave; f < (S / 16) * NB; f += kBfThreads / 64) {
+        const int m = f / NB, k = f % NB;
+        const uint32_t o1 = uint32_t(((32 * k + 8 * kg + (l16 >> 2)) * Lay::BP + 16 * m + 4 * (l16 & 3)) * 2);
+        *reinterpret_cast<u32x4*>(bt + (int64_t(f) * 64 + lane) * 8) = lds_tr_pair(sBb, o1, o1 + 8 * Lay::BP);
     }
 }
 
