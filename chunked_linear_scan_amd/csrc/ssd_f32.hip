@@ -11,7 +11,9 @@
 // This path exists for fp32 inputs, where bf16 operands would exceed the fp32
 // error budget.  One workgroup owns one (batch, head) and walks its chunks in
 // order with the state in LDS; it is correct for any head dim / state size
-// whose state fits in LDS, and is not the throughput path.
+// whose state fits in LDS, and is not the throughput path.  Where two chunks'
+// operands fit in LDS (small head dims, state sizes and chunks), the next
+// chunk's are loaded while the current one is computed.
 #include "common.hpp"
 #include "device_once.hpp"
 #include "ssd_kernels.hpp"
@@ -19,7 +21,27 @@
 namespace cls {
 
 constexpr int kF32Threads = 256;
+constexpr int kF32Prefetch = 32;  // most floats of a staged chunk one thread holds in flight
 
+// A staged chunk: x [T][P], B [T][S], C [T][S] and dt [T], zero past the last
+// real token.
+__host__ __device__ constexpr int f32_stage_floats(int P, int S, int T) { return T * (P + 2 * S + 1); }
+
+size_t ssd_f32_lds_bytes(int P, int S) {
+    return sizeof(float) * (size_t(P) * (S + 1) + 3 * 256 + 16 * S + 16 * 256 + 32 * P + 32 * S + 4);
+}
+
+// Chunks are staged when two of them fit in LDS beside the working tiles and a
+// thread's share fits its prefetch registers: then a chunk's operands arrive in
+// one load round trip, issued while the previous chunk is computed, instead of
+// one round trip per phase of the chunk (the shapes where the walk over the
+// chunks is latency-bound).
+static bool f32_staged(int P, int S, int T) {
+    const int sf = f32_stage_floats(P, S, T);
+    return sf <= kF32Threads * kF32Prefetch && ssd_f32_lds_bytes(P, S) + 2 * sizeof(float) * sf <= 160 * 1024;
+}
+
+template <bool STAGED>
 __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
     extern __shared__ float smem[];
     const int P = p.P, S = p.S, T = p.chunk;
@@ -33,6 +55,7 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
     float* Xs = Wb + 16 * 256;               // [32][P]
     float* Bs = Xs + 32 * P;                 // [32][S]
     float* scratch = Bs + 32 * S;            // [4]
+    float* Stg = scratch + 4;                // STAGED: [2][stage floats], chunk c in half c & 1
 
     const int tid = threadIdx.x;
     const int64_t bh = blockIdx.x;
@@ -42,23 +65,72 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
     const float Ah = p.A[h];
     const float Dh = p.D ? p.D[h] : 0.0f;
 
-    for (int q = tid; q < P * S; q += kF32Threads) {
-        const int pp = q / S, ss = q % S;
-        Hs[pp * HP + ss] = p.h0 ? p.h0[(bh * P + pp) * S + ss] : 0.0f;
-    }
-    __syncthreads();
-
     const int64_t L = p.L;
     const float* x = static_cast<const float*>(p.x);
     const float* Bm = static_cast<const float*>(p.B);
     const float* Cm = static_cast<const float*>(p.C);
     float* y = static_cast<float*>(p.y);
+    const int SF = f32_stage_floats(P, S, T);
+    const int OFF_B = T * P, OFF_C = T * (P + S), OFF_DT = T * (P + 2 * S);
 
-    for (int64_t tok0 = 0; tok0 < L; tok0 += T) {
+    // this thread's share of the chunk starting at t0, loaded into registers:
+    // 16-byte piece q = tid + 256 k of the staged x, B and C rows, and (tid < T)
+    // dt of token tid
+    const int P4 = P / 4, S4 = S / 4, NX4 = T * P4, NB4 = T * S4;
+    f32x4 pf[kF32Prefetch / 4];
+    float pdt = 0.0f;
+    auto fetch = [&](int64_t t0) {
+        const int n = int((L - t0 < T) ? (L - t0) : T);
+#pragma unroll
+        for (int k = 0; k < kF32Prefetch / 4; ++k) {
+            const int q = tid + kF32Threads * k;
+            const bool isx = q < NX4;
+            const bool isc = !isx && q - NX4 >= NB4;
+            const int idx = isx ? q : q - NX4 - (isc ? NB4 : 0);
+            const int w4 = isx ? P4 : S4;
+            const int row = idx / w4, col = 4 * (idx - row * w4);
+            // the source address, chosen with masks (a select between three
+            // pointers is otherwise compiled as a table in scratch memory)
+            const uint64_t ax = reinterpret_cast<uint64_t>(x + ((b * L + t0 + row) * p.H + h) * P + col);
+            const uint64_t bo = uint64_t(((b * L + t0 + row) * p.G + g) * S + col) * sizeof(float);
+            const uint64_t ab = reinterpret_cast<uint64_t>(Bm) + bo, ac = reinterpret_cast<uint64_t>(Cm) + bo;
+            const uint64_t mx = 0 - uint64_t(isx), mc = 0 - uint64_t(isc), mb = ~(mx | mc);
+            const float* src = reinterpret_cast<const float*>((ax & mx) | (ab & mb) | (ac & mc));
+            pf[k] = (q < NX4 + 2 * NB4 && row < n) ? *reinterpret_cast<const f32x4*>(src) : f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        pdt = tid < n ? p.dt[(b * L + t0 + tid) * p.H + h] : 0.0f;
+    };
+    auto stash = [&](int half) {
+        f32x4* dst = reinterpret_cast<f32x4*>(Stg + half * SF);
+#pragma unroll
+        for (int k = 0; k < kF32Prefetch / 4; ++k) {
+            const int q = tid + kF32Threads * k;
+            if (q < NX4 + 2 * NB4) dst[q] = pf[k];
+        }
+        if (tid < T) Stg[half * SF + OFF_DT + tid] = pdt;
+    };
+
+    for (int q = tid; q < P * S; q += kF32Threads) {
+        const int pp = q / S, ss = q % S;
+        Hs[pp * HP + ss] = p.h0 ? p.h0[(bh * P + pp) * S + ss] : 0.0f;
+    }
+    if constexpr (STAGED) {
+        fetch(0);
+        stash(0);
+    }
+    __syncthreads();
+
+    int ci = 0;
+    for (int64_t tok0 = 0; tok0 < L; tok0 += T, ++ci) {
         const int n = int((L - tok0 < T) ? (L - tok0) : T);
+        const bool more = tok0 + T < L;
+        if constexpr (STAGED) {
+            if (more) fetch(tok0 + T);  // in flight while this chunk is computed
+        }
+        const float* St = Stg + (ci & 1) * SF;  // STAGED: this chunk
         // cumulative sum of a_t inside the chunk (natural-log units)
         float dtv = 0.0f;
-        if (tid < n) dtv = p.dt[((b * L) + tok0 + tid) * p.H + h];
+        if (tid < n) dtv = STAGED ? St[OFF_DT + tid] : p.dt[((b * L) + tok0 + tid) * p.H + h];
         const float G = block_inclusive_sum_256(Ah * dtv, scratch);
         if (tid < T) {
             Gs[tid] = G;
@@ -71,10 +143,14 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
         // outputs, 16 rows at a time
         for (int i0 = 0; i0 < n; i0 += 16) {
             const int nr = (n - i0 < 16) ? (n - i0) : 16;
+            // the 16 C rows (a staged chunk holds zeros past its last real row)
+            const float* Cr = STAGED ? St + OFF_C + i0 * S : Cb;
+            if constexpr (!STAGED) {
 #pragma unroll 4
-            for (int q = tid; q < 16 * S; q += kF32Threads) {
-                const int r = q / S, ss = q % S;
-                Cb[q] = (r < nr) ? Cm[((b * L + tok0 + i0 + r) * p.G + g) * S + ss] : 0.0f;
+                for (int q = tid; q < 16 * S; q += kF32Threads) {
+                    const int r = q / S, ss = q % S;
+                    Cb[q] = (r < nr) ? Cm[((b * L + tok0 + i0 + r) * p.G + g) * S + ss] : 0.0f;
+                }
             }
             __syncthreads();
             const int jmax = i0 + nr;
@@ -82,7 +158,7 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
                 float acc[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r) acc[r] = 0.0f;
-                const float* brow = Bm + ((b * L + tok0 + j) * p.G + g) * S;
+                const float* brow = STAGED ? St + OFF_B + j * S : Bm + ((b * L + tok0 + j) * p.G + g) * S;
                 // eight loads in flight at a time: one at a time, each waited for
                 // before the next, the chunk cost a global-memory latency per item
                 int ss = 0;
@@ -93,12 +169,12 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
 #pragma unroll
                     for (int e = 0; e < 8; ++e)
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) acc[r] = fmaf(Cb[r * S + ss + e], bv[e], acc[r]);
+                        for (int r = 0; r < 16; ++r) acc[r] = fmaf(Cr[r * S + ss + e], bv[e], acc[r]);
                 }
                 for (; ss < S; ++ss) {
                     const float bv = brow[ss];
 #pragma unroll
-                    for (int r = 0; r < 16; ++r) acc[r] = fmaf(Cb[r * S + ss], bv, acc[r]);
+                    for (int r = 0; r < 16; ++r) acc[r] = fmaf(Cr[r * S + ss], bv, acc[r]);
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -114,10 +190,11 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
                 const int r = q / P, pp = q % P;
                 const int i = i0 + r;
                 float s1 = 0.0f;
-                for (int ss = 0; ss < S; ++ss) s1 = fmaf(Cb[r * S + ss], Hs[pp * HP + ss], s1);
+                for (int ss = 0; ss < S; ++ss) s1 = fmaf(Cr[r * S + ss], Hs[pp * HP + ss], s1);
                 float out = expf(Gs[i]) * s1;
-                const float* xc = x + ((b * L + tok0) * p.H + h) * P + pp;  // token j at j * H * P
-                const int64_t xs = int64_t(p.H) * P;
+                // token j of this channel at xc[j * xs]
+                const float* xc = STAGED ? St + pp : x + ((b * L + tok0) * p.H + h) * P + pp;
+                const int64_t xs = STAGED ? int64_t(P) : int64_t(p.H) * P;
                 int j = 0;
                 for (; j + 8 <= i + 1; j += 8) {  // eight loads in flight, as above
                     float xv[8];
@@ -131,6 +208,12 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
             }
             __syncthreads();
         }
+        // the next chunk into the other half (its last reader was the previous
+        // chunk, before this chunk's first barrier); the state jump's barriers
+        // order these writes before the next chunk's reads
+        if constexpr (STAGED) {
+            if (more) stash((ci + 1) & 1);
+        }
 
         // state jump to the next chunk start
         const float alpha = expf(Glast);
@@ -139,12 +222,17 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
 #pragma unroll 4
             for (int q = tid; q < 32 * P; q += kF32Threads) {
                 const int jj = q / P, pp = q % P;
-                Xs[q] = (jj < nj) ? ws[j0 + jj] * x[((b * L + tok0 + j0 + jj) * p.H + h) * P + pp] : 0.0f;
+                const float xv = (jj < nj) ? (STAGED ? St[(j0 + jj) * P + pp]
+                                                     : x[((b * L + tok0 + j0 + jj) * p.H + h) * P + pp])
+                                           : 0.0f;
+                Xs[q] = (jj < nj) ? ws[j0 + jj] * xv : 0.0f;
             }
 #pragma unroll 4
             for (int q = tid; q < 32 * S; q += kF32Threads) {
                 const int jj = q / S, ss = q % S;
-                Bs[q] = (jj < nj) ? Bm[((b * L + tok0 + j0 + jj) * p.G + g) * S + ss] : 0.0f;
+                Bs[q] = (jj < nj) ? (STAGED ? St[OFF_B + (j0 + jj) * S + ss]
+                                            : Bm[((b * L + tok0 + j0 + jj) * p.G + g) * S + ss])
+                                  : 0.0f;
             }
             __syncthreads();
             for (int q = tid; q < P * S; q += kF32Threads) {
@@ -166,23 +254,26 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
     }
 }
 
-size_t ssd_f32_lds_bytes(int P, int S) {
-    return sizeof(float) * (size_t(P) * (S + 1) + 3 * 256 + 16 * S + 16 * 256 + 32 * P + 32 * S + 4);
-}
-
 int ssd_f32_launch(const SsdF32Params& prm, hipStream_t stream) {
-    const size_t lds = ssd_f32_lds_bytes(prm.P, prm.S);
+    const bool staged = f32_staged(prm.P, prm.S, prm.chunk);
+    const size_t lds =
+        ssd_f32_lds_bytes(prm.P, prm.S) + (staged ? 2 * sizeof(float) * f32_stage_floats(prm.P, prm.S, prm.chunk) : 0);
     static DeviceOnce attrs;
     if (run_once_per_device(attrs, [] {
-            return hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_f32_kernel),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess
+            return hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_f32_kernel<false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess &&
+                           hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_f32_kernel<true>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess
                        ? 0
                        : -7;
         }) != 0)
         return -7;
     const dim3 grid{uint32_t(prm.batch * prm.H), 1u, 1u};
     const dim3 block{uint32_t(kF32Threads), 1u, 1u};
-    hipLaunchKernelGGL(ssd_f32_kernel, grid, block, lds, stream, prm);
+    if (staged)
+        hipLaunchKernelGGL(ssd_f32_kernel<true>, grid, block, lds, stream, prm);
+    else
+        hipLaunchKernelGGL(ssd_f32_kernel<false>, grid, block, lds, stream, prm);
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

@@ -51,8 +51,9 @@
 //     at most 2^100 they are split as exp2(GL_i) [CB dt_j exp2(-GL_j)], so only
 //     per-token factors and one per-row scale are needed; stronger decay takes
 //     the element-wise form.
-//   * B^T, CB and a copy of C come fragment-major from the CB pass (a wave's
-//     operand fragment is 1 KB in lane order); the compute waves fetch B^T and
+//   * B^T, CB and (unless C is read from its rows) a copy of C come
+//     fragment-major from the CB pass (a wave's operand fragment is 1 KB in
+//     lane order); the compute waves fetch B^T and
 //     CB fragments a chunk ahead into register rings.  Every ring slot is
 //     refilled at every block (the address, not the load, depends on the
 //     wave's causal extent), so no ring register is merged across branches,

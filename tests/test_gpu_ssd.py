@@ -70,6 +70,16 @@ def test_fp32_chunk_sizes_and_ragged(chunk):
     run_and_check(inp, chunk, f"fp32 chunk={chunk}")
 
 
+@pytest.mark.parametrize("P,S,chunk", [(32, 32, 64), (48, 20, 32), (4, 8, 128), (64, 64, 64), (16, 16, 256)])
+def test_fp32_staged_and_unstaged_chunks(P, S, chunk):
+    """The fp32 kernel stages whole chunks in LDS (the next one loaded while
+    the current one is computed) where two fit, and reads global memory per
+    phase elsewhere (here the last two shapes); both match the oracle,
+    including widths that are not powers of two and a ragged last chunk."""
+    inp = small_case(21, 2, 333, 4, P, S, 2, torch.float32)
+    run_and_check(inp, chunk, f"fp32 P={P} S={S} chunk={chunk}")
+
+
 @pytest.mark.parametrize("chunk", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("P", [16, 32, 64, 128])
 @pytest.mark.parametrize("S", [32, 64, 128, 256])
