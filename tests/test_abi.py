@@ -350,7 +350,8 @@ def test_planned_call_validates_the_plan_on_host():
     for bad in (cls.plan_request(nsegs=65), cls.PlanRequest(3, 0, 0, 0, 0, 0, 0), cls.PlanRequest(0, 3, 0, 0, 0, 0, 0),
                 cls.PlanRequest(0, 0, -1, 0, 0, 0, 0), cls.PlanRequest(0, 0, 2, -1, 0, 0, 0),
                 cls.PlanRequest(0, 0, 0, 0, 0, 65, 0), cls.PlanRequest(0, 0, 0, 0, 0, 0, 7),
-                cls.PlanRequest(0, 0, 0, 0, 0, 0, 0, 0, 3), cls.PlanRequest(0, 0, 0, 0, 0, 0, 0, 0, -1)):
+                cls.PlanRequest(0, 0, 0, 0, 0, 0, 0, 0, 3), cls.PlanRequest(0, 0, 0, 0, 0, 0, 0, 0, -1),
+                cls.PlanRequest(0, 0, 0, 0, 0, 0, 0, 0, 0, 3), cls.PlanRequest(0, 0, 0, 0, 0, 0, 0, 0, 0, -1)):
         assert call(bad) == -2
         assert lib.ssd_fwd_planned_workspace_size(*shape, ctypes.byref(bad)) == 0
     # a forced plan's workspace: at least ssd_fwd's, more when it splits finer than the tuner would
