@@ -16,6 +16,9 @@ Workloads (synthetic; each is named by what it is and its sizes):
   batch 4, L=8192, 40 heads, P=128, S=128, 1 group, chunk 256, bf16
 * ``ssd_context_512k`` a half-million-token context: batch 1, L=524288, 8 heads,
   P=64, S=128, 2 groups, chunk 128, bf16, dt shift -4, h0 ~ N(0, 0.1^2)
+* ``ssd_long_s256`` a long context at state size 256 (the per-(batch, head)
+  kernel's shape): batch 1, L=32768, 8 heads, P=64, S=256, 2 groups, chunk 128,
+  bf16, dt shift -4, h0 ~ N(0, 0.1^2)
 * ``decode_large`` one decode token (``ssd_step``) for 64 sequences of the
   large-model layer's heads: batch 64, 80 heads, P=64, S=128, 1 group, bf16,
   state ~ N(0, 0.5^2)
@@ -62,6 +65,8 @@ SSD_WORKLOADS = {
     "ssd_large_p128": (SSDShape(4, 8192, 40, 128, 128, 1, 256, "bf16"), 5),
     # a half-million-token context (4096 chunks per chain, chains cut into many segments)
     "ssd_context_512k": (SSDShape(1, 524288, 8, 64, 128, 2, 128, "bf16", dt_shift=-4.0, h0_std=0.1), 6),
+    # a long context at state size 256 (per-(batch, head) kernel, heads split into narrower ones)
+    "ssd_long_s256": (SSDShape(1, 32768, 8, 64, 256, 2, 128, "bf16", dt_shift=-4.0, h0_std=0.1), 7),
 }
 
 SCAN_WORKLOADS = {

@@ -317,6 +317,17 @@ def test_half_million_token_context(plan):
     parity.check_ssd_workload("ssd_context_512k", y, hf, label=f"ssd_context_512k {plan}")
 
 
+def test_long_context_state_size_256():
+    """32768 tokens at state size 256 (256 sub-chunks per chain): the
+    per-(batch, head) kernel with its heads split into chains of head dim 16,
+    every output and the final state compared."""
+    print("[ssd] ssd_long_s256 full size, whole outputs", flush=True)
+    inp = workloads.ssd_workload("ssd_long_s256")
+    y, hf = gpu_run(inp)
+    assert np.isfinite(y).all()
+    parity.check_ssd_workload("ssd_long_s256", y, hf, label="ssd_long_s256")
+
+
 def test_full_workload_on_the_chunk_kernel():
     """The large-model layer forced onto the per-(batch, head) kernel (the
     configuration the benchmark times for that kernel); every output
