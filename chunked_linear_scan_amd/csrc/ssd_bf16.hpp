@@ -135,6 +135,13 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cb_kernel(SsdBf16Params p) {
 // are loaded while chunk c computes.  The barriers order LDS only
 // (s_waitcnt lgkmcnt(0); s_barrier), so loads stay in flight across them.
 // Eight waves per workgroup measured slower on three of four shapes.
+//
+// Where the chains are too few to fill the CUs they are cut into segments
+// (SsdBf16Params.nsegs): an aggregate launch (AGG) runs every segment but a
+// chain's last from a zero state without outputs and writes its state and
+// log2 decay; the output launch runs one workgroup per segment, which starts
+// from h0 folded with its predecessors' aggregates in segment order
+// (h <- exp2(decay) h + state).
 // ---------------------------------------------------------------------------
 constexpr int kChunkWaves = 4;
 constexpr int kChunkThreads = 64 * kChunkWaves;
@@ -162,7 +169,7 @@ __device__ __forceinline__ float chunk_inclusive_sum(float v, float* scratch) {
     return v + add;
 }
 
-template <int TT, int P, int S>
+template <int TT, int P, int S, bool AGG>
 __global__ __launch_bounds__(kChunkThreads) void ssd_chunk_kernel(SsdBf16Params p) {
     constexpr int NW = kChunkWaves, NT = kChunkThreads;
     constexpr int XP = TT + 8;            // LDS pitch (elements) of X^T and B^T rows
@@ -195,9 +202,16 @@ __global__ __launch_bounds__(kChunkThreads) void ssd_chunk_kernel(SsdBf16Params 
     float* ws = dts + TT;                                    // [TT]
     float* scratch = ws + TT;                                // [NW]
 
+    static_assert(size_t(KS) * NPT * NT * 4 == chunk_state_floats(P, S), "segment state layout");
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kg = lane >> 4;
-    const int64_t bh = blockIdx.x;
+    // workgroup = (chain, segment), segments of a chain adjacent
+    const int nsegs = p.nsegs > 1 ? p.nsegs : 1;
+    const int per_chain = AGG ? nsegs - 1 : nsegs;
+    const int64_t bh = int64_t(blockIdx.x) / per_chain;
+    const int seg = int(int64_t(blockIdx.x) % per_chain);
+    const int c_begin = nsegs > 1 ? seg * p.seg_chunks : 0;
+    const int c_end = (nsegs > 1 && c_begin + p.seg_chunks < p.nchunks) ? c_begin + p.seg_chunks : p.nchunks;
     const int64_t b = bh / p.H;
     const int h = int(bh % p.H);
     const int g = h / (p.H / p.G);
@@ -207,7 +221,10 @@ __global__ __launch_bounds__(kChunkThreads) void ssd_chunk_kernel(SsdBf16Params 
     const float Dh = p.D ? p.D[hin] : 0.0f;
     const int64_t L = p.L;
 
-    // state h^T tiles owned by this wave: s-tiles st = wave + NW k, all p-tiles
+    // state h^T tiles owned by this wave: s-tiles st = wave + NW k, all p-tiles.
+    // Segment state fragment (k, pt) of this thread at f32x4 index
+    // ((slot * KS + k) * NPT + pt) * NT + tid, slot = chain * (nsegs - 1) + segment.
+    const f32x4* seg_state = reinterpret_cast<const f32x4*>(p.seg_state);
     f32x4 hacc[KS][NPT];
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
@@ -215,9 +232,18 @@ __global__ __launch_bounds__(kChunkThreads) void ssd_chunk_kernel(SsdBf16Params 
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) {
             f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (st < NST && p.h0) {
-                const float* src = p.h0 + (bh * P + 16 * pt + l16) * S + 16 * st + 4 * kg;
-                v = *reinterpret_cast<const f32x4*>(src);
+            if (!AGG && st < NST) {
+                if (p.h0) {
+                    const float* src = p.h0 + (bh * P + 16 * pt + l16) * S + 16 * st + 4 * kg;
+                    v = *reinterpret_cast<const f32x4*>(src);
+                }
+                // the earlier segments' aggregates, in order
+                for (int k2 = 0; k2 < seg; ++k2) {
+                    const int64_t slot = bh * (nsegs - 1) + k2;
+                    const float a = fexp2(p.seg_decay[slot]);
+                    const f32x4 sv = seg_state[((slot * KS + k) * NPT + pt) * NT + tid];
+                    v = v * a + sv;
+                }
             }
             hacc[k][pt] = v;
             if (st < NST) {
@@ -273,9 +299,10 @@ __global__ __launch_bounds__(kChunkThreads) void ssd_chunk_kernel(SsdBf16Params 
 #pragma unroll
             for (int e = 0; e < 8; ++e) br[k][e] = b_row(tok0, n, tid + NT * k, e);
     };
-    if constexpr (kAhead) fetch(0);
+    if constexpr (kAhead) fetch(c_begin);
 
-    for (int c = 0; c < p.nchunks; ++c) {
+    float sumG = 0.0f;  // log2 decay of the chunks so far (AGG)
+    for (int c = c_begin; c < c_end; ++c) {
         const int64_t tok0 = int64_t(c) * p.chunk;
         const int n = int((L - tok0 < p.chunk) ? (L - tok0) : p.chunk);
 
@@ -312,14 +339,15 @@ __global__ __launch_bounds__(kChunkThreads) void ssd_chunk_kernel(SsdBf16Params 
         }
         chunk_lds_barrier();
         if constexpr (kAhead)
-            if (c + 1 < p.nchunks) fetch(c + 1);  // in flight through this chunk's products
+            if (c + 1 < c_end) fetch(c + 1);  // in flight through this chunk's products
         const float Glast = Gs[TT - 1];  // padded positions add 0: G at the last real token
+        sumG += Glast;
         if (tid < TT) ws[tid] = dts[tid] * fexp2(Glast - Gs[tid]);
 
         // S2b + S4: y^T tiles, 16 tokens per tile, tiles spread over the waves
         const uint16_t* cbase = p.cb + ((b * p.nchunks + c) * p.G + g) * (TT * TT);
         const uint16_t* Cbase = p.C + ((b * L + tok0) * p.G + g) * S;
-        const int ntile = (n + 15) / 16;
+        const int ntile = AGG ? 0 : (n + 15) / 16;  // the aggregate launch has no outputs
         for (int it = wave; it < ntile; it += NW) {
             const int i = 16 * it + l16;
             const bool vi = i < n;
@@ -442,7 +470,17 @@ __global__ __launch_bounds__(kChunkThreads) void ssd_chunk_kernel(SsdBf16Params 
         chunk_lds_barrier();
     }
 
-    if (p.h_final) {
+    if constexpr (AGG) {
+        const int64_t slot = bh * (nsegs - 1) + seg;
+        f32x4* out = reinterpret_cast<f32x4*>(p.seg_state);
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            if (wave + NW * k >= NST) continue;
+#pragma unroll
+            for (int pt = 0; pt < NPT; ++pt) out[((slot * KS + k) * NPT + pt) * NT + tid] = hacc[k][pt];
+        }
+        if (tid == 0) p.seg_decay[slot] = sumG;
+    } else if (p.h_final && seg == nsegs - 1) {
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
             const int st = wave + NW * k;
@@ -461,16 +499,24 @@ int launch_ssd_bf16_tpl(const SsdBf16Params& prm, hipStream_t stream) {
     const size_t lds = ssd_bf16_lds_bytes(TT, P, S);
     static DeviceOnce attrs;
     if (run_once_per_device(attrs, [lds] {
-            return hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_chunk_kernel<TT, P, S>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) == hipSuccess
+            return hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_chunk_kernel<TT, P, S, false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) == hipSuccess &&
+                           hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_chunk_kernel<TT, P, S, true>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) == hipSuccess
                        ? 0
                        : -7;
         }) != 0)
         return -7;
+    const int64_t nsegs = prm.nsegs > 1 ? prm.nsegs : 1;
     const dim3 gcb{cb_grid<TT>(prm), 1u, 1u}, bcb{uint32_t(kBfThreads), 1u, 1u};
     hipLaunchKernelGGL((ssd_cb_kernel<TT, S>), gcb, bcb, 0, stream, prm);
-    const dim3 gmain{uint32_t(prm.batch * prm.H), 1u, 1u}, bmain{uint32_t(kChunkThreads), 1u, 1u};
-    hipLaunchKernelGGL((ssd_chunk_kernel<TT, P, S>), gmain, bmain, lds, stream, prm);
+    const dim3 bmain{uint32_t(kChunkThreads), 1u, 1u};
+    if (nsegs > 1) {
+        const dim3 gagg{uint32_t(prm.batch * prm.H * (nsegs - 1)), 1u, 1u};
+        hipLaunchKernelGGL((ssd_chunk_kernel<TT, P, S, true>), gagg, bmain, lds, stream, prm);
+    }
+    const dim3 gmain{uint32_t(prm.batch * prm.H * nsegs), 1u, 1u};
+    hipLaunchKernelGGL((ssd_chunk_kernel<TT, P, S, false>), gmain, bmain, lds, stream, prm);
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

@@ -28,13 +28,12 @@ bool ssd_bf16_supported(int TT, int P, int S) {
 // 1 << split heads of dim P >> split (bit-identical results; every split
 // head recomputes the head's diagonal weights).  Head dim 128 halves (the
 // weights are shared by many columns; measured 2156 against 2425 us on a
-// 4 x 8192, 40-head, state-256 layer), and a grid of fewer than 128
-// workgroups splits further down to head dim 16 (32 heads of a 65536-token
-// sequence: 5739 against 7307 us).  Grids of 192 and more workgroups of head
-// dim 64 or less run unsplit: splitting them measured 19-100 % slower.
+// 4 x 8192, 40-head, state-256 layer).  Few chains are cut into segments
+// instead of narrower heads (chunk_kernel_segs): 32 heads of a 65536-token
+// sequence at state size 256 took 5731 us split into 128 heads of dim 16 and
+// 1601 us as 32 heads in 8 segments.
 int chunk_kernel_split(int64_t batch, int64_t H, int64_t P) {
     int split = P == 128 ? 1 : 0;
-    while ((batch * H << split) < 128 && (P >> split) > 16) ++split;
     // the grid (batch * H << split workgroups) and the head count stay in 31 bits
     while (split > 0 && (batch * H << split) >= (int64_t(1) << 31)) --split;
     return split;
@@ -255,24 +254,59 @@ bool valid_chunk(int64_t c) { return c == 16 || c == 32 || c == 64 || c == 128 |
 
 int64_t nchunks(const SsdShape& s) { return (s.seqlen + s.chunk - 1) / s.chunk; }
 
-// The per-(batch, head) kernel's sub-chunk (tile TT, tokens per sub-chunk) and
-// its workspace: C B^T per (batch, sub-chunk, group); 0 when it has no tile.
+// Segments of the per-(batch, head) kernel's chains.  Where the chains fill
+// at most half of the 256 CUs, each is cut so that about one workgroup per
+// CU runs, in segments of at least 8 sub-chunks (shorter ones would spend
+// more on the aggregate launch and the fold than the parallelism buys).
+// want > 0: that many segments (a plan request), at most one per sub-chunk.
+int64_t chunk_kernel_segs(int64_t chains, int64_t nc, int64_t want) {
+    int64_t n = want > 0 ? want : (chains <= 128 ? 256 / chains : 1);
+    if (want <= 0 && n > nc / 8) n = nc / 8;
+    if (n > 64) n = 64;
+    if (n > nc) n = nc;
+    if (n < 1 || chains * n >= (int64_t(1) << 31)) n = 1;  // the grid stays in 31 bits
+    const int64_t k = (nc + n - 1) / n;
+    return (nc + k - 1) / k;  // every segment holds at least one sub-chunk
+}
+
+// The per-(batch, head) kernel's plan: sub-chunk (tile TT, tokens per
+// sub-chunk), head split, segments, and its workspace: C B^T per (batch,
+// sub-chunk, group), then (segments) the aggregate states and decays.  TT = 0
+// when it has no tile.
 struct ChunkTile {
     int TT, chunk;
     int64_t nchunks;
+    int split, nsegs, seg_chunks;
+    size_t state_off, decay_off, bytes;
 };
 
-ChunkTile chunk_kernel_plan(const SsdShape& s) {
-    const int tt = cls::chunk_kernel_tile(s.chunk, int(s.headdim), int(s.dstate));
-    const int sub = tt < s.chunk ? tt : int(s.chunk);
-    return ChunkTile{tt, sub, tt ? (s.seqlen + sub - 1) / sub : 0};
+ChunkTile chunk_kernel_plan(const SsdShape& s, int64_t want_segs = 0) {
+    ChunkTile t{};
+    t.TT = cls::chunk_kernel_tile(s.chunk, int(s.headdim), int(s.dstate));
+    if (t.TT == 0) return t;
+    t.chunk = t.TT < s.chunk ? t.TT : int(s.chunk);
+    t.nchunks = (s.seqlen + t.chunk - 1) / t.chunk;
+    t.split = cls::chunk_kernel_split(s.batch, s.nheads, s.headdim);
+    const int64_t chains = (s.batch * s.nheads) << t.split;
+    t.nsegs = int(chunk_kernel_segs(chains, t.nchunks, want_segs));
+    t.seg_chunks = int((t.nchunks + t.nsegs - 1) / t.nsegs);
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    const size_t cb = size_t(s.batch) * size_t(t.nchunks) * size_t(s.ngroups) * size_t(t.TT) * size_t(t.TT) * 2;
+    const size_t nagg = size_t(chains) * size_t(t.nsegs - 1);
+    t.state_off = cls::kSsdWsHeader + up(cb);
+    t.decay_off = t.state_off + up(nagg * cls::chunk_state_floats(int(s.headdim >> t.split), int(s.dstate)) * 4);
+    t.bytes = t.nsegs > 1 ? t.decay_off + nagg * 4 : cls::kSsdWsHeader + cb;
+    return t;
 }
 
-size_t chunk_kernel_ws_bytes(const SsdShape& s) {
-    const ChunkTile t = chunk_kernel_plan(s);
-    if (t.TT == 0) return 0;
-    return size_t(s.batch) * size_t(t.nchunks) * size_t(s.ngroups) * size_t(t.TT) * size_t(t.TT) * 2 +
-           cls::kSsdWsHeader;
+// the segment count a plan request asks for (0: the heuristic's)
+int64_t chunk_kernel_want(const cls::SegChoice* force) {
+    return (force && force != &cls::kUseHeuristic) ? force->nsegs : 0;
+}
+
+size_t chunk_kernel_ws_bytes(const SsdShape& s, int64_t want_segs = 0) {
+    const ChunkTile t = chunk_kernel_plan(s, want_segs);
+    return t.TT == 0 ? 0 : t.bytes;
 }
 
 }  // namespace
@@ -362,7 +396,7 @@ extern "C" size_t cls_ssd_plan_bytes(const SsdShape& s, const SsdLaunchOpts& o) 
     if (pl.use) return pl.bytes;
     // 0: the plan keeps the fused path out and the per-(batch, head) kernel
     // has no tile for the shape
-    return chunk_kernel_ws_bytes(s);
+    return chunk_kernel_ws_bytes(s, chunk_kernel_want(o.force));
 }
 
 static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const SsdLaunchOpts& o, hipStream_t stream) {
@@ -453,12 +487,18 @@ static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const SsdLaunchO
         if (st == -8) return SSD_ERR_UNSUPPORTED;
         return st == 0 ? SSD_OK : SSD_ERR_HIP;
     }
-    const ChunkTile t = chunk_kernel_plan(s);
+    const ChunkTile t = chunk_kernel_plan(s, chunk_kernel_want(force));
     if (t.TT == 0) return SSD_ERR_UNSUPPORTED;
     p.chunk = t.chunk;
     p.nchunks = int(t.nchunks);
-    p.hshift = cls::chunk_kernel_split(s.batch, s.nheads, s.headdim);
+    p.hshift = t.split;
     p.H = int(s.nheads) << p.hshift;
+    p.nsegs = t.nsegs;
+    p.seg_chunks = t.seg_chunks;
+    if (t.nsegs > 1) {
+        p.seg_state = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + t.state_off);
+        p.seg_decay = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + t.decay_off);
+    }
     ev_pre();
     const int st = cls::ssd_bf16_launch(t.TT, int(s.headdim) >> p.hshift, int(s.dstate), p, stream);
     ev_post();

@@ -48,6 +48,14 @@ struct SsdBf16Params {
     // and x, y, h0 and h_final hold them at the same addresses), and head h
     // reads dt, A and D of head h >> hshift
     int hshift;
+    // per-(batch, head) kernel: each chain cut into nsegs segments of
+    // seg_chunks sub-chunks (nsegs <= 1: whole chains).  The aggregate launch
+    // writes the state of every segment but a chain's last, from a zero start,
+    // and its log2 decay; a segment's workgroup folds its predecessors' into
+    // its start state (reduce-then-fold).
+    int nsegs, seg_chunks;
+    float* seg_state;  // [chains][nsegs - 1][chunk_state_floats(P >> hshift, S)]
+    float* seg_decay;  // [chains][nsegs - 1]
 };
 
 struct SsdFusedParams {
@@ -137,6 +145,9 @@ constexpr bool ssd_bf16_lds_fits(int TT, int P, int S) {
 bool ssd_bf16_supported(int TT, int P, int S);
 constexpr int kChunkMaxTile = 128;  // longest sub-chunk of the per-(batch, head) kernel
 int chunk_kernel_tile(int64_t chunk, int P, int S);
+// floats of one segment state of the per-(batch, head) kernel (head dim P):
+// its four waves' fp32 state fragments, state tiles wave, wave + 4, ..
+constexpr size_t chunk_state_floats(int P, int S) { return size_t((S / 16 + 3) / 4) * (P / 16) * 256 * 4; }
 
 size_t ssd_fused_lds_bytes(int TT, int S);
 int ssd_fused_state_floats(int S);  // floats of one [64, S] state

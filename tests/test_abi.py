@@ -174,10 +174,26 @@ def test_every_head_dim_and_state_size_of_the_set_is_supported():
                 assert lib.ssd_fwd_planned_workspace_size(*shape, ctypes.byref(chunk_path)) > 0, shape
     # the per-(batch, head) kernel's workspace is C B^T per (batch, sub-chunk,
     # group): 256-token chunks run as 128-token sub-chunks, and as 64-token
-    # ones where the 128-token tiles overflow LDS (P = 128, S = 256)
+    # ones where the 128-token tiles overflow LDS (P = 128, S = 256).  Chains
+    # cut into segments add, per chain and segment but the last, the segment's
+    # fp32 state (a multiple of 4 state tiles of 16 x 16, one per wave) and its
+    # decay.
+    up = lambda v: (v + 255) // 256 * 256
     assert lib.ssd_fwd_workspace_size(2, 1000, 4, 32, 64, 2, 256, cls.SSD_BF16) == 2 * 8 * 2 * 128 * 128 * 2 + 1024
-    assert lib.ssd_fwd_workspace_size(2, 1000, 4, 128, 256, 2, 256, cls.SSD_BF16) == 2 * 16 * 2 * 64 * 64 * 2 + 1024
-    assert lib.ssd_fwd_workspace_size(2, 1000, 4, 16, 32, 2, 16, cls.SSD_BF16) == 2 * 63 * 2 * 32 * 32 * 2 + 1024
+    # head dim 128 runs as 16 chains of head dim 64 (8 heads x 2), 16 sub-chunks
+    # of 64 tokens in 2 segments: 16 aggregates of 4 x 4 tiles
+    cb = 2 * 16 * 2 * 64 * 64 * 2
+    assert lib.ssd_fwd_workspace_size(2, 1000, 4, 128, 256, 2, 256, cls.SSD_BF16) == \
+        1024 + up(cb) + up(16 * 16 * 256 * 16) + 16 * 4
+    # 8 chains of head dim 16, 63 sub-chunks of 16 tokens in 7 segments of 9:
+    # 48 aggregates of 1 x 1 tiles
+    cb = 2 * 63 * 2 * 32 * 32 * 2
+    assert lib.ssd_fwd_workspace_size(2, 1000, 4, 16, 32, 2, 16, cls.SSD_BF16) == \
+        1024 + up(cb) + up(48 * 1 * 256 * 16) + 48 * 4
+    # a plan request of whole chains needs no more than ssd_fwd's workspace
+    one = cls.plan_request(path="chunk", nsegs=1)
+    assert lib.ssd_fwd_planned_workspace_size(2, 1000, 4, 16, 32, 2, 16, cls.SSD_BF16, ctypes.byref(one)) == \
+        lib.ssd_fwd_workspace_size(2, 1000, 4, 16, 32, 2, 16, cls.SSD_BF16)
     for P, S in ((48, 64), (64, 96), (256, 64)):
         shape = (2, 1000, 4, P, S, 2, 64, cls.SSD_BF16)
         assert lib.ssd_fwd_workspace_size(*shape) == 0

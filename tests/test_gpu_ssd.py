@@ -225,8 +225,8 @@ def test_one_state_one_channel_matches_linear_scan():
 
 
 @pytest.mark.parametrize("plan", [None, {"nsegs": 4, "nsplit": 5}, {"nsegs": 4, "nsplit": 5, "s3": "lookback"},
-                                  {"nsegs": 16, "s3": "lookback"}],
-                         ids=["default", "split", "lookback", "lookback16"])
+                                  {"nsegs": 16, "s3": "lookback"}, {"path": "chunk", "nsegs": 3}],
+                         ids=["default", "split", "lookback", "lookback16", "chunk-kernel-segments"])
 @pytest.mark.parametrize("P", [64, 128])
 def test_deterministic_100_runs(plan, P):
     """100 reruns are bit-identical, with whole chains and with split chains
@@ -326,6 +326,19 @@ def test_long_context_state_size_256():
     y, hf = gpu_run(inp)
     assert np.isfinite(y).all()
     parity.check_ssd_workload("ssd_long_s256", y, hf, label="ssd_long_s256")
+
+
+@pytest.mark.parametrize("P,S,L,H,G,chunk,nsegs", [
+    (32, 64, 3000, 3, 1, 64, 2), (32, 64, 3000, 3, 1, 64, 5), (64, 256, 2000, 2, 2, 128, 3),
+    (16, 32, 1500, 4, 2, 32, 64), (128, 128, 999, 2, 1, 256, 7), (64, 128, 700, 2, 2, 16, 4)])
+def test_chunk_kernel_segments_forced(P, S, L, H, G, chunk, nsegs):
+    """The per-(batch, head) kernel with its chains cut into segments
+    (reduce-then-fold: the aggregate launch, then each segment's start state
+    folded from h0 and its predecessors' aggregates), including one segment
+    per sub-chunk, a ragged last segment and chunk 16; against the oracle."""
+    print(f"[ssd chunk segments] P={P} S={S} L={L} chunk={chunk} nsegs={nsegs}", flush=True)
+    inp = small_case(31, 2, L, H, P, S, G, torch.bfloat16)
+    run_and_check(inp, chunk, f"chunk kernel, {nsegs} segments", plan=cls.plan_request(path="chunk", nsegs=nsegs))
 
 
 def test_full_workload_on_the_chunk_kernel():
@@ -450,10 +463,10 @@ def test_head_dim_128_equals_two_heads_of_64(plan):
 
 @pytest.mark.parametrize("P,S,Bt,H,narrow", [(128, 32, 2, 6, 64), (64, 256, 1, 4, 16)])
 def test_chunk_kernel_head_split_equals_narrow_heads(P, S, Bt, H, narrow):
-    """The per-(batch, head) kernel runs a head of dim 128, and the heads of a
-    grid under 128 workgroups, as several narrower heads that share the head's
-    dt, A and D.  Bit for bit, that is what narrower heads carrying the head's
-    column blocks and its dt, A and D give (the same sub-chunk tile)."""
+    """A head's channels are independent: the per-(batch, head) kernel runs a
+    head of dim 128 as two heads of 64 that share its dt, A and D, and bit
+    for bit a head gives what narrower heads carrying its column blocks and
+    its dt, A and D give (the same sub-chunk tile and whole chains)."""
     k = P // narrow
     L, G, chunk = 64 * 12 + 5, 2 if H % 2 == 0 else 1, 128
     print(f"[ssd split] P={P} S={S} H={H} -> {k} x {narrow}", flush=True)
