@@ -173,18 +173,22 @@ def record_traffic(fetch_csv, write_csv, workload):
             db = json.load(f)
 
     def per_kernel(pat):
-        f = [v for (k, g), vs in fe.items() if pat in k for v in vs]
-        w = [v for (k, g), vs in wr.items() if pat in k for v in vs]
+        # pat: a substring of the kernel name, or "a|b": both substrings
+        pats = pat.split("|")
+        f = [v for (k, g), vs in fe.items() if all(q in k for q in pats) for v in vs]
+        w = [v for (k, g), vs in wr.items() if all(q in k for q in pats) for v in vs]
         if not f or not w:
             return None
         return statistics.mean(f) * sf * 1024, statistics.mean(w) * sw * 1024, len(f)
 
     groups = [("ssd_fwd:" + workload, SSD_SOURCES, ["ssd_cbt_kernel<", "ssd_fused_agg_kernel<", "ssd_fused_kernel<"]),
-              ("ssd_fwd_chunk_kernel:" + workload, CHUNK_SOURCES, ["ssd_cb_kernel<", "ssd_chunk_kernel<"]),
+              ("ssd_fwd_chunk_kernel:" + workload, CHUNK_SOURCES,
+               ["ssd_cb_kernel<", "ssd_chunk_kernel<|false>", "ssd_chunk_kernel<|true>"]),
               ("linear_scan:scan", SCAN_SOURCES, ["linear_scan_kernel<false, float, float, false, 2048>"]),
               ("ssd_step:decode_large", STEP_SOURCES, ["ssd_step_kernel"])]
     for key, srcs, pats in groups:
-        parts = {p.rstrip("<"): per_kernel(p) for p in pats}
+        names = {"ssd_chunk_kernel<|false>": "ssd_chunk_kernel", "ssd_chunk_kernel<|true>": "ssd_chunk_kernel (aggregate)"}
+        parts = {names.get(p, p.rstrip("<")): per_kernel(p) for p in pats}
         parts = {k: v for k, v in parts.items() if v is not None}
         if not parts:
             continue
@@ -249,6 +253,9 @@ class SsdRunner(Runner):
         self.name = name + ("" if path == "auto" else ":chunk_kernel")
         self.plan = cls.plan_request(path=path) if path != "auto" else None
         self.shape, _ = workloads.SSD_WORKLOADS[name]
+        # the call runs the per-(batch, head) kernel: forced, or a shape outside the fused set
+        self.chunk_path = self.plan is not None or not (
+            self.shape.dtype == "bf16" and self.shape.headdim in (64, 128) and self.shape.dstate in (64, 128))
         self.inp = workloads.ssd_workload(name)
         self.alg_bytes = ssd_alg_bytes(self.inp, self.shape)
         self.flops = ssd_alg_flops(self.shape)
@@ -280,8 +287,8 @@ class SsdRunner(Runner):
                 + ("" if self.plan is None else ", forced onto the per-(batch, head) kernel"))
 
     def traffic_key(self):
-        return (("ssd_fwd:" if self.plan is None else "ssd_fwd_chunk_kernel:") + self.workload,
-                SSD_SOURCES if self.plan is None else CHUNK_SOURCES)
+        return (("ssd_fwd_chunk_kernel:" if self.chunk_path else "ssd_fwd:") + self.workload,
+                CHUNK_SOURCES if self.chunk_path else SSD_SOURCES)
 
     def per_launch(self, calls=20):
         """Mean time of each launch of a call: events between the launches
@@ -295,9 +302,10 @@ class SsdRunner(Runner):
                                 plan=self.plan, out=d["y"], events=evs[k])
         torch.cuda.synchronize()
         t = [sum(e[j].elapsed_time(e[j + 1]) for e in evs) / calls * 1e3 for j in range(3)]
-        if self.plan is not None:  # one CB pass and the chunk kernel, timed as one
+        if self.chunk_path:  # the CB pass and the chunk kernel's launches, timed as one
             return {"cb_pass_and_chunk_kernel_us": round(t[2], 2),
-                    "grid": f"{self.shape.batch * self.shape.nheads} workgroups, one per (batch, head)"}
+                    "grid": "one workgroup per (batch, head) chain, or per segment of a chain where the "
+                            "chains fill at most half of the CUs (then after an aggregate launch)"}
         plan = cls.ssd_fwd_plan(self.shape.batch, self.shape.seqlen, self.shape.nheads, self.shape.headdim,
                                 self.shape.dstate, self.shape.ngroups, self.shape.chunk, self.inp["x"].dtype)
         return {"cb_pass_us": round(t[0], 2), "aggregate_launch_us": round(t[1], 2),
@@ -737,7 +745,7 @@ def main():
     ap.add_argument("--steps", type=int, default=300)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="ssd_long",
-                    choices=["ssd_small", "ssd_large", "ssd_long", "ssd_tiny", "ssd_large_p128"])
+                    choices=["ssd_small", "ssd_large", "ssd_long", "ssd_tiny", "ssd_large_p128", "ssd_long_s256"])
     ap.add_argument("--path", default="auto", choices=["auto", "chunk"],
                     help="SSD path of --workload: auto (what ssd_fwd runs) or chunk (forced onto the "
                          "per-(batch, head) kernel; counter and trace runs of that kernel)")
@@ -805,7 +813,7 @@ def main():
     if not args.only_headline:
         if not args.no_side_ssd:
             for name, path in (("ssd_large", "auto"), ("ssd_large_p128", "auto"), ("ssd_small", "auto"),
-                               ("ssd_large", "chunk"), ("ssd_tiny", "auto")):
+                               ("ssd_large", "chunk"), ("ssd_long_s256", "auto"), ("ssd_tiny", "auto")):
                 if (name, path) != (args.workload, args.path):
                     side.append(SsdRunner(name, path))
         side += [ScanRunner("scan"), ScanRunner("scan_ragged"), ScanRunner("scan", "bf16", "f32"),
