@@ -341,6 +341,18 @@ def test_chunk_kernel_segments_forced(P, S, L, H, G, chunk, nsegs):
     run_and_check(inp, chunk, f"chunk kernel, {nsegs} segments", plan=cls.plan_request(path="chunk", nsegs=nsegs))
 
 
+@pytest.mark.parametrize("want_final", [True, False])
+def test_chunk_kernel_segments_without_h0_and_d(want_final):
+    """Segments with no initial state and no skip term (the first segment
+    starts from zero, the fold adds nothing for it), with and without the
+    final state."""
+    print(f"[ssd chunk segments] no h0, no D, want_final={want_final}", flush=True)
+    inp = small_case(33, 1, 2500, 2, 32, 256, 1, torch.bfloat16, h0=False, D=False)
+    y, hf = run_and_check(inp, 128, "chunk kernel, 4 segments, no h0/D",
+                          plan=cls.plan_request(path="chunk", nsegs=4), want_final=want_final)
+    assert (hf is None) == (not want_final)
+
+
 def test_full_workload_on_the_chunk_kernel():
     """The large-model layer forced onto the per-(batch, head) kernel (the
     configuration the benchmark times for that kernel); every output
