@@ -20,8 +20,9 @@ bugs the tests caught": kernels too short for the GPU to boost):
 * the K timed steps of the headline run as 15 windows, each bracketed by HIP
   events on the launch stream; the other workloads (the small- and
   large-model layer shapes, the large layer in heads of dim 128, the large
-  layer forced onto the per-(batch, head) kernel, the scans, the decode
-  step) run their own
+  layer forced onto the per-(batch, head) kernel, a long context at state
+  size 256 (the per-(batch, head) kernel in segments), the tiny fp32 one,
+  the scans, the decode step) run their own
   windows of at least 5 ms, interleaved with the headline's: window w of
   every workload runs before window w + 1 of any;
 * inputs and outputs rotate over enough buffer copies that each workload's
