@@ -310,6 +310,30 @@ int64_t chunk_kernel_want(const cls::SegChoice* force) {
     return (force && force != &cls::kUseHeuristic) ? force->nsegs : 0;
 }
 
+// The fp32 kernel's segments (the same rule; at most two workgroups per CU,
+// which is what its registers allow) and their workspace: per chain and
+// segment but the last, the [P][S] state and the decay.
+struct F32Plan {
+    int nsegs, seg_chunks;
+    size_t state_off, decay_off, bytes;
+};
+
+F32Plan f32_plan(const SsdShape& s, int64_t want_segs = 0) {
+    F32Plan f{};
+    const int64_t chains = s.batch * s.nheads;
+    const int64_t nc = (s.seqlen + s.chunk - 1) / s.chunk;
+    int64_t per_cu = int64_t(160 * 1024) / int64_t(cls::ssd_f32_launch_lds(int(s.headdim), int(s.dstate), int(s.chunk)));
+    per_cu = per_cu < 1 ? 1 : (per_cu > 2 ? 2 : per_cu);
+    f.nsegs = int(chunk_kernel_segs(chains, nc, want_segs, per_cu));
+    f.seg_chunks = int((nc + f.nsegs - 1) / f.nsegs);
+    auto up = [](size_t v) { return (v + 255) / 256 * 256; };
+    const size_t nagg = size_t(chains) * size_t(f.nsegs - 1);
+    f.state_off = cls::kSsdWsHeader;
+    f.decay_off = f.state_off + up(nagg * size_t(s.headdim) * size_t(s.dstate) * 4);
+    f.bytes = f.nsegs > 1 ? f.decay_off + nagg * 4 : 0;
+    return f;
+}
+
 size_t chunk_kernel_ws_bytes(const SsdShape& s, int64_t want_segs = 0) {
     const ChunkTile t = chunk_kernel_plan(s, want_segs);
     return t.TT == 0 ? 0 : t.bytes;
@@ -379,7 +403,7 @@ std::vector<cls::SegChoice> fused_candidates(const SsdShape& s) {
 // The workspace fits every plan the autotuner may choose, so a buffer sized
 // before tuning stays large enough after it.
 extern "C" size_t cls_ssd_workspace_bytes(const SsdShape& s) {
-    if (s.dtype == SSD_F32) return 0;
+    if (s.dtype == SSD_F32) return f32_plan(s).bytes;
     const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
                                                      s.ngroups, s.chunk, s.dtype);
     if (pl.use) {
@@ -395,7 +419,7 @@ extern "C" size_t cls_ssd_workspace_bytes(const SsdShape& s) {
 }
 
 extern "C" size_t cls_ssd_plan_bytes(const SsdShape& s, const SsdLaunchOpts& o) {
-    if (s.dtype == SSD_F32) return 0;
+    if (s.dtype == SSD_F32) return f32_plan(s, chunk_kernel_want(o.force)).bytes;
     const cls::SsdFusedPlan pl = cls::ssd_fused_plan(s.batch, s.seqlen, s.nheads, s.headdim, s.dstate,
                                                      s.ngroups, s.chunk, s.dtype, o.force, o.path, o.s3, o.xcds,
                                                      o.policy, o.csrc);
@@ -419,6 +443,13 @@ static int ssd_launch_plan(const SsdShape& s, const SsdArgs& a, const SsdLaunchO
     if (s.dtype == SSD_F32) {
         cls::SsdF32Params p{a.x, a.dt, a.A, a.B, a.C, a.D, a.h0, a.y, a.h_final, s.batch, s.seqlen,
                             int(s.nheads), int(s.headdim), int(s.dstate), int(s.ngroups), int(s.chunk)};
+        const F32Plan fp = f32_plan(s, chunk_kernel_want(force));
+        p.nsegs = fp.nsegs;
+        p.seg_chunks = fp.seg_chunks;
+        if (fp.nsegs > 1) {
+            p.seg_state = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + fp.state_off);
+            p.seg_decay = reinterpret_cast<float*>(static_cast<char*>(a.workspace) + fp.decay_off);
+        }
         ev_pre();
         const int st = cls::ssd_f32_launch(p, stream);
         ev_post();

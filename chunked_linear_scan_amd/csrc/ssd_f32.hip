@@ -41,7 +41,7 @@ static bool f32_staged(int P, int S, int T) {
     return sf <= kF32Threads * kF32Prefetch && ssd_f32_lds_bytes(P, S) + 2 * sizeof(float) * sf <= 160 * 1024;
 }
 
-template <bool STAGED>
+template <bool STAGED, bool AGG>
 __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
     extern __shared__ float smem[];
     const int P = p.P, S = p.S, T = p.chunk;
@@ -58,7 +58,14 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
     float* Stg = scratch + 4;                // STAGED: [2][stage floats], chunk c in half c & 1
 
     const int tid = threadIdx.x;
-    const int64_t bh = blockIdx.x;
+    // workgroup = (chain, segment), segments of a chain adjacent
+    const int nsegs = p.nsegs > 1 ? p.nsegs : 1;
+    const int per_chain = AGG ? nsegs - 1 : nsegs;
+    const int64_t bh = int64_t(blockIdx.x) / per_chain;
+    const int seg = int(int64_t(blockIdx.x) % per_chain);
+    const int64_t tok_begin = nsegs > 1 ? int64_t(seg) * p.seg_chunks * T : 0;
+    const int64_t tok_end =
+        (nsegs > 1 && tok_begin + int64_t(p.seg_chunks) * T < p.L) ? tok_begin + int64_t(p.seg_chunks) * T : p.L;
     const int64_t b = bh / p.H;
     const int h = int(bh % p.H);
     const int g = h / (p.H / p.G);
@@ -110,20 +117,30 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
         if (tid < T) Stg[half * SF + OFF_DT + tid] = pdt;
     };
 
+    // start state: zero (aggregate launch), else h0 folded with the earlier
+    // segments' aggregates in order
     for (int q = tid; q < P * S; q += kF32Threads) {
         const int pp = q / S, ss = q % S;
-        Hs[pp * HP + ss] = p.h0 ? p.h0[(bh * P + pp) * S + ss] : 0.0f;
+        float v = (!AGG && p.h0) ? p.h0[(bh * P + pp) * S + ss] : 0.0f;
+        if constexpr (!AGG) {
+            for (int k = 0; k < seg; ++k) {
+                const int64_t slot = bh * (nsegs - 1) + k;
+                v = v * expf(p.seg_decay[slot]) + p.seg_state[slot * P * S + q];
+            }
+        }
+        Hs[pp * HP + ss] = v;
     }
     if constexpr (STAGED) {
-        fetch(0);
+        fetch(tok_begin);
         stash(0);
     }
     __syncthreads();
 
     int ci = 0;
-    for (int64_t tok0 = 0; tok0 < L; tok0 += T, ++ci) {
-        const int n = int((L - tok0 < T) ? (L - tok0) : T);
-        const bool more = tok0 + T < L;
+    float sumG = 0.0f;  // natural-log decay of the chunks so far (aggregate launch)
+    for (int64_t tok0 = tok_begin; tok0 < tok_end; tok0 += T, ++ci) {
+        const int n = int((tok_end - tok0 < T) ? (tok_end - tok0) : T);
+        const bool more = tok0 + T < tok_end;
         if constexpr (STAGED) {
             if (more) fetch(tok0 + T);  // in flight while this chunk is computed
         }
@@ -138,10 +155,11 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
         }
         __syncthreads();
         const float Glast = Gs[n - 1];
+        sumG += Glast;
         if (tid < n) ws[tid] = dts[tid] * expf(Glast - Gs[tid]);
 
-        // outputs, 16 rows at a time
-        for (int i0 = 0; i0 < n; i0 += 16) {
+        // outputs, 16 rows at a time (none in the aggregate launch)
+        for (int i0 = 0; !AGG && i0 < n; i0 += 16) {
             const int nr = (n - i0 < 16) ? (n - i0) : 16;
             // the 16 C rows (a staged chunk holds zeros past its last real row)
             const float* Cr = STAGED ? St + OFF_C + i0 * S : Cb;
@@ -246,7 +264,11 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
         }
     }
 
-    if (p.h_final) {
+    if constexpr (AGG) {
+        const int64_t slot = bh * (nsegs - 1) + seg;
+        for (int q = tid; q < P * S; q += kF32Threads) p.seg_state[slot * P * S + q] = Hs[(q / S) * HP + q % S];
+        if (tid == 0) p.seg_decay[slot] = sumG;
+    } else if (p.h_final && seg == nsegs - 1) {
         for (int q = tid; q < P * S; q += kF32Threads) {
             const int pp = q / S, ss = q % S;
             p.h_final[(bh * P + pp) * S + ss] = Hs[pp * HP + ss];
@@ -254,26 +276,39 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
     }
 }
 
+size_t ssd_f32_launch_lds(int P, int S, int T) {
+    return ssd_f32_lds_bytes(P, S) + (f32_staged(P, S, T) ? 2 * sizeof(float) * f32_stage_floats(P, S, T) : 0);
+}
+
 int ssd_f32_launch(const SsdF32Params& prm, hipStream_t stream) {
     const bool staged = f32_staged(prm.P, prm.S, prm.chunk);
-    const size_t lds =
-        ssd_f32_lds_bytes(prm.P, prm.S) + (staged ? 2 * sizeof(float) * f32_stage_floats(prm.P, prm.S, prm.chunk) : 0);
+    const size_t lds = ssd_f32_launch_lds(prm.P, prm.S, prm.chunk);
     static DeviceOnce attrs;
     if (run_once_per_device(attrs, [] {
-            return hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_f32_kernel<false>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess &&
-                           hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_f32_kernel<true>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess
-                       ? 0
-                       : -7;
+            const void* fns[] = {reinterpret_cast<const void*>(ssd_f32_kernel<false, false>),
+                                 reinterpret_cast<const void*>(ssd_f32_kernel<true, false>),
+                                 reinterpret_cast<const void*>(ssd_f32_kernel<false, true>),
+                                 reinterpret_cast<const void*>(ssd_f32_kernel<true, true>)};
+            for (const void* f : fns)
+                if (hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+                    return -7;
+            return 0;
         }) != 0)
         return -7;
-    const dim3 grid{uint32_t(prm.batch * prm.H), 1u, 1u};
+    const int64_t nsegs = prm.nsegs > 1 ? prm.nsegs : 1;
     const dim3 block{uint32_t(kF32Threads), 1u, 1u};
+    if (nsegs > 1) {
+        const dim3 gagg{uint32_t(prm.batch * prm.H * (nsegs - 1)), 1u, 1u};
+        if (staged)
+            hipLaunchKernelGGL((ssd_f32_kernel<true, true>), gagg, block, lds, stream, prm);
+        else
+            hipLaunchKernelGGL((ssd_f32_kernel<false, true>), gagg, block, lds, stream, prm);
+    }
+    const dim3 grid{uint32_t(prm.batch * prm.H * nsegs), 1u, 1u};
     if (staged)
-        hipLaunchKernelGGL(ssd_f32_kernel<true>, grid, block, lds, stream, prm);
+        hipLaunchKernelGGL((ssd_f32_kernel<true, false>), grid, block, lds, stream, prm);
     else
-        hipLaunchKernelGGL(ssd_f32_kernel<false>, grid, block, lds, stream, prm);
+        hipLaunchKernelGGL((ssd_f32_kernel<false, false>), grid, block, lds, stream, prm);
     return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

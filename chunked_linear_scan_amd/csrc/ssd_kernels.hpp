@@ -21,9 +21,17 @@ struct SsdF32Params {
     float* h_final;
     int64_t batch, L;
     int H, P, S, G, chunk;
+    // chains cut into nsegs segments of seg_chunks chunks (nsegs <= 1: whole
+    // chains), as for the per-(batch, head) bf16 kernel: the aggregate launch
+    // writes every segment's state but a chain's last ([P][S], from a zero
+    // start) and its natural-log decay; each segment folds its predecessors'.
+    int nsegs, seg_chunks;
+    float* seg_state;  // [chains][nsegs - 1][P][S]
+    float* seg_decay;  // [chains][nsegs - 1]
 };
 
 size_t ssd_f32_lds_bytes(int P, int S);
+size_t ssd_f32_launch_lds(int P, int S, int T);  // LDS of one workgroup as launched (staged chunks included)
 int ssd_f32_launch(const SsdF32Params& prm, hipStream_t stream);
 
 struct SsdBf16Params {

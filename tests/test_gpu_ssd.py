@@ -80,6 +80,23 @@ def test_fp32_staged_and_unstaged_chunks(P, S, chunk):
     run_and_check(inp, chunk, f"fp32 P={P} S={S} chunk={chunk}")
 
 
+@pytest.mark.parametrize("P,S,chunk,nsegs,h0", [(16, 16, 32, 3, True), (32, 32, 64, 6, True), (64, 64, 64, 2, True),
+                                                (16, 16, 16, 64, False), (48, 20, 32, 4, False)])
+def test_fp32_segments(P, S, chunk, nsegs, h0):
+    """The fp32 kernel with its chains cut into segments (an aggregate
+    launch, then each segment folds its predecessors' states into its start
+    state), staged and unstaged chunks, with and without h0; against the
+    oracle at the fp32 tolerance, and equal on 20 reruns."""
+    print(f"[ssd fp32 segments] P={P} S={S} chunk={chunk} nsegs={nsegs} h0={h0}", flush=True)
+    inp = small_case(41, 2, 777, 3, P, S, 1, torch.float32, h0=h0)
+    plan = cls.plan_request(nsegs=nsegs)
+    y, hf = run_and_check(inp, chunk, f"fp32, {nsegs} segments", plan=plan)
+    for _ in range(20):
+        y2, h2 = gpu_run(inp, chunk=chunk, plan=plan)
+        assert np.array_equal(y.view(np.uint32), y2.view(np.uint32))
+        assert np.array_equal(hf.view(np.uint32), h2.view(np.uint32))
+
+
 @pytest.mark.parametrize("chunk", [16, 32, 64, 128, 256])
 @pytest.mark.parametrize("P", [16, 32, 64, 128])
 @pytest.mark.parametrize("S", [32, 64, 128, 256])
