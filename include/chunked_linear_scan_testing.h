@@ -49,9 +49,9 @@ typedef struct {
     int32_t path;        /* SSD_PATH_*                                               */
     int32_t s3;          /* SSD_S3_*                                                 */
     int64_t nsegs;       /* segments per split chain, 1..64; 0: tuned or heuristic
-                            (the per-(batch, head) kernel cuts every chain into
-                            nsegs segments, at most one per sub-chunk; nsplit and
-                            agg_pieces do not apply to it)                         */
+                            (the per-(batch, head) and fp32 kernels cut every
+                            chain into nsegs segments, at most one per sub-chunk;
+                            nsplit and agg_pieces do not apply to them)            */
     int64_t nsplit;      /* with nsegs: split only the last nsplit (batch, head)
                             chains, the others run whole; 0: split every chain
                             (a head of dim 128 is two chains of dim 64)            */

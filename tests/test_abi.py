@@ -128,6 +128,23 @@ def test_ssd_rejects_bad_arguments():
     assert call(P=24) in (-8, -2)
 
 
+def test_fp32_workspace_holds_segment_states_only_when_chains_are_cut():
+    """The fp32 path needs no workspace for whole chains; cut into segments,
+    it holds per chain and segment but the last a [P][S] fp32 state and a
+    decay, after the 1 KB header."""
+    lib = cls.load_library()
+    up = lambda v: (v + 255) // 256 * 256
+    # 2 chains of 8 chunks: no segments (at least 8 chunks each)
+    assert lib.ssd_fwd_workspace_size(1, 256, 2, 16, 16, 1, 32, cls.SSD_F32) == 0
+    # 64 chains of 64 chunks, P = S = 16: 8 segments of 8 chunks
+    assert lib.ssd_fwd_workspace_size(2, 4096, 32, 16, 16, 2, 64, cls.SSD_F32) == \
+        1024 + up(64 * 7 * 16 * 16 * 4) + 64 * 7 * 4
+    # a plan request of 3 segments on the first shape
+    three = cls.plan_request(nsegs=3)
+    assert lib.ssd_fwd_planned_workspace_size(1, 256, 2, 16, 16, 1, 32, cls.SSD_F32, ctypes.byref(three)) == \
+        1024 + up(2 * 2 * 16 * 16 * 4) + 2 * 2 * 4
+
+
 def test_ssd_plan_request_c_source_is_validated():
     """c_source takes SSD_CSRC_AUTO, _COPY or _ROWS; any other value is
     refused before anything is sized or launched."""
