@@ -65,7 +65,7 @@ SSD_WORKLOADS = {
     "ssd_large_p128": (SSDShape(4, 8192, 40, 128, 128, 1, 256, "bf16"), 5),
     # a half-million-token context (4096 chunks per chain, chains cut into many segments)
     "ssd_context_512k": (SSDShape(1, 524288, 8, 64, 128, 2, 128, "bf16", dt_shift=-4.0, h0_std=0.1), 6),
-    # a long context at state size 256 (per-(batch, head) kernel, heads split into narrower ones)
+    # a long context at state size 256 (per-(batch, head) kernel, each chain cut into segments)
     "ssd_long_s256": (SSDShape(1, 32768, 8, 64, 256, 2, 128, "bf16", dt_shift=-4.0, h0_std=0.1), 7),
 }
 

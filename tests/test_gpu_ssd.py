@@ -336,7 +336,7 @@ def test_half_million_token_context(plan):
 
 def test_long_context_state_size_256():
     """32768 tokens at state size 256 (256 sub-chunks per chain): the
-    per-(batch, head) kernel with its heads split into chains of head dim 16,
+    per-(batch, head) kernel with each of its 8 chains cut into 32 segments,
     every output and the final state compared."""
     print("[ssd] ssd_long_s256 full size, whole outputs", flush=True)
     inp = workloads.ssd_workload("ssd_long_s256")
