@@ -779,7 +779,7 @@ def main():
         record_traffic(args.record_traffic[0], args.record_traffic[1], args.workload)
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): this build runs on a single GPU; "
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}): the kernels run on a single GPU; "
               f"run it with --gpus 1", file=sys.stderr)
         sys.exit(2)
     if args.steps < NWIN:
