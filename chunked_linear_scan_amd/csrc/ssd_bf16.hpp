@@ -46,25 +46,32 @@ __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
 
 // ---------------------------------------------------------------------------
 // S2a: CB[b, c, g][i][j] = sum_s C[i][s] B[j][s] for the 32-token blocks with
-// block(j) <= block(i), and, when p.bt is set, B^T[b, c, g][s][t] (the
-// token-contiguous copy of B that the fused kernel reads as an MFMA operand).
-// Padded rows and columns (token >= chunk length) are written as zeros.
-// One workgroup per (batch, chunk, group, 32-row block ib): wave w computes
-// the 16-row tile 2 ib + (w & 1) against the 16-column tiles (w >> 1) + 2 q.
+// block(j) <= block(i), row-major [TT][TT] bf16.  Padded rows and columns
+// (token >= chunk length) are written as zeros.  One workgroup (four waves)
+// per (batch, chunk, group): the chunk's B rows are staged in LDS once, and
+// wave w takes the 16-row tiles in pairs (w + 4 k, NIT - 1 - w - 4 k), so every
+// wave has the same share of the triangle (with fewer tiles than 8, one tile
+// per wave).  A tile's C rows stay in registers.
 // ---------------------------------------------------------------------------
 template <int TT>
 inline uint32_t cb_grid(const SsdBf16Params& prm) {
-    return uint32_t(prm.batch * prm.nchunks * prm.G * (TT / 32));
+    return uint32_t(prm.batch * prm.nchunks * prm.G);
 }
+
+// LDS of the CB pass: the chunk's B rows at a pitch of S + 8 bf16
+constexpr size_t ssd_cb_lds_bytes(int TT, int S) { return size_t(TT) * (S + 8) * 2; }
 
 template <int TT, int S>
 __global__ __launch_bounds__(kBfThreads) void ssd_cb_kernel(SsdBf16Params p) {
     constexpr int KS = S / 32;
-    constexpr int NIB = TT / 32;
+    constexpr int NIT = TT / 16;
+    constexpr int BP = S + 8;
+    constexpr int CPR = S / 8;  // 16-byte pieces per row
+    extern __shared__ __attribute__((aligned(16))) unsigned char cb_sm[];
+    uint16_t* sB = reinterpret_cast<uint16_t*>(cb_sm);  // [TT][BP]
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, kg = lane >> 4;
-    const int ib = int(blockIdx.x % NIB);
-    const int64_t bcg = blockIdx.x / NIB;
+    const int64_t bcg = blockIdx.x;
     const int g = int(bcg % p.G);
     const int64_t c = (bcg / p.G) % p.nchunks;
     const int64_t b = bcg / (int64_t(p.G) * p.nchunks);
@@ -75,50 +82,36 @@ __global__ __launch_bounds__(kBfThreads) void ssd_cb_kernel(SsdBf16Params p) {
     const uint16_t* Cbase = p.C + ((b * p.L + tok0) * p.G + g) * S;
     const uint16_t* Bbase = p.B + ((b * p.L + tok0) * p.G + g) * S;
 
-    const int it = 2 * ib + (wave & 1);
-    const int i = 16 * it + l16;
-    u32x4 cf[KS];
+    for (int q = tid; q < TT * CPR; q += kBfThreads) {
+        const int r = q / CPR, c8 = q % CPR;
+        const u32x4 v = r < n ? ldg16(Bbase + r * rowstride + 8 * c8) : u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(sB + r * BP + 8 * c8) = v;
+    }
+    __syncthreads();
+
+    constexpr int NTW = NIT >= 8 ? NIT / 4 : 1;  // row tiles per wave
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-        cf[ks] = (i < n) ? ldg16(Cbase + i * rowstride + 32 * ks + 8 * kg) : u32x4{0, 0, 0, 0};
-    auto load_b = [&](int jt, u32x4 (&dst)[KS]) {
-        const int j = 16 * jt + l16;
+    for (int k = 0; k < NTW; ++k) {
+        const int w4 = wave + 4 * (k >> 1);
+        const int it = NIT < 8 ? wave : ((k & 1) ? NIT - 1 - w4 : w4);
+        if (it >= NIT) continue;
+        const int i = 16 * it + l16;
+        u32x4 cf[KS];
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
-            dst[ks] = (j < n) ? ldg16(Bbase + j * rowstride + 32 * ks + 8 * kg) : u32x4{0, 0, 0, 0};
-    };
-    u32x4 bcur[KS], bnxt[KS];
-    int jt = wave >> 1;
-    load_b(jt, bcur);
-    for (int q = 0; q <= ib; ++q) {
-        if (q < ib) load_b(jt + 2, bnxt);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            cf[ks] = (i < n) ? ldg16(Cbase + i * rowstride + 32 * ks + 8 * kg) : u32x4{0, 0, 0, 0};
+        const int ntj = 2 * (it >> 1) + 2;  // the column tiles of the blocks <= block(it)
+        for (int jt = 0; jt < ntj; ++jt) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) acc = mfma16x16x32(bcur[ks], cf[ks], acc);
-        // lane holds CB[i][16 jt + 4 kg + r], r = 0..3
-        u32x2 v;
-        v[0] = pack_bf16x2(acc[0], acc[1]);
-        v[1] = pack_bf16x2(acc[2], acc[3]);
-        *reinterpret_cast<u32x2*>(out + i * TT + 16 * jt + 4 * kg) = v;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) bcur[ks] = bnxt[ks];
-        jt += 2;
-    }
-    if (p.bt) {
-        // B^T[s][t] for the block's 32 tokens: thread item (s, 8-token group)
-        uint16_t* bt = p.bt + bcg * (int64_t(S) * TT);
-        for (int u = tid; u < S * 4; u += kBfThreads) {
-            const int s = u % S;
-            const int t0 = 32 * ib + 8 * (u / S);
-            uint32_t w[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int ta = t0 + 2 * e, tb = ta + 1;
-                const uint32_t lo = ta < n ? Bbase[ta * rowstride + s] : 0u;
-                const uint32_t hi = tb < n ? Bbase[tb * rowstride + s] : 0u;
-                w[e] = lo | (hi << 16);
-            }
-            *reinterpret_cast<u32x4*>(bt + s * TT + t0) = u32x4{w[0], w[1], w[2], w[3]};
+            for (int ks = 0; ks < KS; ++ks)
+                acc = mfma16x16x32(*reinterpret_cast<const u32x4*>(sB + (16 * jt + l16) * BP + 32 * ks + 8 * kg),
+                                   cf[ks], acc);
+            // lane holds CB[i][16 jt + 4 kg + r], r = 0..3
+            u32x2 v;
+            v[0] = pack_bf16x2(acc[0], acc[1]);
+            v[1] = pack_bf16x2(acc[2], acc[3]);
+            *reinterpret_cast<u32x2*>(out + i * TT + 16 * jt + 4 * kg) = v;
         }
     }
 }
@@ -497,19 +490,22 @@ __global__ __launch_bounds__(kChunkThreads) void ssd_chunk_kernel(SsdBf16Params 
 template <int TT, int P, int S>
 int launch_ssd_bf16_tpl(const SsdBf16Params& prm, hipStream_t stream) {
     const size_t lds = ssd_bf16_lds_bytes(TT, P, S);
+    constexpr size_t cb_lds = ssd_cb_lds_bytes(TT, S);
     static DeviceOnce attrs;
     if (run_once_per_device(attrs, [lds] {
             return hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_chunk_kernel<TT, P, S, false>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) == hipSuccess &&
                            hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_chunk_kernel<TT, P, S, true>),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) == hipSuccess
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, int(lds)) == hipSuccess &&
+                           hipFuncSetAttribute(reinterpret_cast<const void*>(ssd_cb_kernel<TT, S>),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, int(cb_lds)) == hipSuccess
                        ? 0
                        : -7;
         }) != 0)
         return -7;
     const int64_t nsegs = prm.nsegs > 1 ? prm.nsegs : 1;
     const dim3 gcb{cb_grid<TT>(prm), 1u, 1u}, bcb{uint32_t(kBfThreads), 1u, 1u};
-    hipLaunchKernelGGL((ssd_cb_kernel<TT, S>), gcb, bcb, 0, stream, prm);
+    hipLaunchKernelGGL((ssd_cb_kernel<TT, S>), gcb, bcb, cb_lds, stream, prm);
     const dim3 bmain{uint32_t(kChunkThreads), 1u, 1u};
     if (nsegs > 1) {
         const dim3 gagg{uint32_t(prm.batch * prm.H * (nsegs - 1)), 1u, 1u};
