@@ -225,20 +225,38 @@ __global__ __launch_bounds__(kChunkThreads) void ssd_chunk_kernel(SsdBf16Params 
 #pragma unroll
         for (int pt = 0; pt < NPT; ++pt) {
             f32x4 v = {0.f, 0.f, 0.f, 0.f};
-            if (!AGG && st < NST) {
-                if (p.h0) {
-                    const float* src = p.h0 + (bh * P + 16 * pt + l16) * S + 16 * st + 4 * kg;
-                    v = *reinterpret_cast<const f32x4*>(src);
-                }
-                // the earlier segments' aggregates, in order
-                for (int k2 = 0; k2 < seg; ++k2) {
-                    const int64_t slot = bh * (nsegs - 1) + k2;
-                    const float a = fexp2(p.seg_decay[slot]);
-                    const f32x4 sv = seg_state[((slot * KS + k) * NPT + pt) * NT + tid];
-                    v = v * a + sv;
-                }
+            if (!AGG && st < NST && p.h0) {
+                const float* src = p.h0 + (bh * P + 16 * pt + l16) * S + 16 * st + 4 * kg;
+                v = *reinterpret_cast<const f32x4*>(src);
             }
             hacc[k][pt] = v;
+        }
+    }
+    // the earlier segments' aggregates, in order; each segment's fragments are
+    // loaded together, so a segment costs one memory latency, not one per fragment
+    if constexpr (!AGG) {
+        for (int k2 = 0; k2 < seg; ++k2) {
+            const int64_t slot = bh * (nsegs - 1) + k2;
+            const float a = fexp2(p.seg_decay[slot]);
+            f32x4 sv[KS][NPT];
+#pragma unroll
+            for (int k = 0; k < KS; ++k)
+#pragma unroll
+                for (int pt = 0; pt < NPT; ++pt)
+                    sv[k][pt] = wave + NW * k < NST ? seg_state[((slot * KS + k) * NPT + pt) * NT + tid]
+                                                    : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k = 0; k < KS; ++k)
+#pragma unroll
+                for (int pt = 0; pt < NPT; ++pt) hacc[k][pt] = hacc[k][pt] * a + sv[k][pt];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+        const int st = wave + NW * k;
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) {
+            const f32x4 v = hacc[k][pt];
             if (st < NST) {
                 u32x2 w;
                 w[0] = pack_bf16x2(v[0], v[1]);
