@@ -118,17 +118,23 @@ __global__ __launch_bounds__(kF32Threads) void ssd_f32_kernel(SsdF32Params p) {
     };
 
     // start state: zero (aggregate launch), else h0 folded with the earlier
-    // segments' aggregates in order
+    // segments' aggregates in order (segment by segment, each thread over its
+    // own elements, so a segment's loads are in flight together)
     for (int q = tid; q < P * S; q += kF32Threads) {
         const int pp = q / S, ss = q % S;
-        float v = (!AGG && p.h0) ? p.h0[(bh * P + pp) * S + ss] : 0.0f;
-        if constexpr (!AGG) {
-            for (int k = 0; k < seg; ++k) {
-                const int64_t slot = bh * (nsegs - 1) + k;
-                v = v * expf(p.seg_decay[slot]) + p.seg_state[slot * P * S + q];
+        Hs[pp * HP + ss] = (!AGG && p.h0) ? p.h0[(bh * P + pp) * S + ss] : 0.0f;
+    }
+    if constexpr (!AGG) {
+        for (int k = 0; k < seg; ++k) {
+            const int64_t slot = bh * (nsegs - 1) + k;
+            const float a = expf(p.seg_decay[slot]);
+            const float* sv = p.seg_state + slot * P * S;
+#pragma unroll 4
+            for (int q = tid; q < P * S; q += kF32Threads) {
+                float& hq = Hs[(q / S) * HP + q % S];
+                hq = hq * a + sv[q];
             }
         }
-        Hs[pp * HP + ss] = v;
     }
     if constexpr (STAGED) {
         fetch(tok_begin);
